@@ -1,0 +1,352 @@
+"""Float64 CPU oracle for the DeepSeek Sparse Attention (DSA) hot path.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module. The HIP library
+never calls it, and it shares no code with the HIP library. It is written
+from the definitions in the pages and is slow on purpose: each step is the
+plain formula with numpy primitives (matmul, sort), and there is no blocking,
+fusion or reordering beyond what that formula states.
+
+Sources (page title · section):
+  [P3]  "DeepSeek3.2: Onboard sparse attention" · Background. DSA adds two
+        parts to MLA: an indexer, whose index score is a parametric
+        query-key product, and a non-parametric top-k that picks, for each
+        query, the keys and values it attends to.
+  [P3n] same page · "What this PR does", item 1. The naive implementation
+        takes the top-k indices as an index mask and adds it to the regular
+        attention mask of dot-product attention. Training only.
+  [P3c] same page · item 2. The 671B indexer config is 64 index heads of
+        dim 128, top-k 2048.
+  [P2f] "Support Ring Attention with DeepSeek DSA Sparse Indexer" · "Forward
+        Flow". The index mask is [batch, S, S] and shared by all heads. It is
+        combined with the causal condition (a query sees keys at or before
+        its own position, the diagonal included), and the kept logits are the
+        query-key products multiplied by a softmax scale.
+  [P2b] same page · "Backward Flow". dQ = dP K, dK = dP^T Q and dV = P^T dO,
+        each masked the same way.
+  [P2t] same page · "Tests". The index mask is threaded with and without
+        segment IDs.
+
+The indexer formula is not printed on the pages. It is the standard one of
+the method: I[t,s] = sum_j w[t,j] * ReLU(q_idx[t,j,:] . k_idx[s,:]), with a
+per-token, per-index-head weight w and one index key per token shared by all
+index heads. The readings of what the pages leave open are:
+  * valid(t) = { s <= t : seg[s] == seg[t] }. The causal condition includes
+    the diagonal; without segment IDs there is one segment. Selection is
+    segment-aware.
+  * The selection takes n = min(K, |valid(t)|) keys. The order is: larger
+    score first, then smaller s first among equal scores. -0 and +0 are equal.
+  * Index lists are ascending and padded with -1 to K entries.
+  * A row with no kept key has O = 0, LSE = -inf and zero gradients.
+  * The selection key of a bf16 score buffer is the score rounded to bf16
+    (round to nearest, ties to even).
+
+Parity status: every function here is pinned by the tests in
+``tests/test_oracle_pins.py``. The pins are brute force on tiny inputs,
+library routines (torch float64 SDPA and autograd), closed forms,
+invariants, and hand-computed fixtures under ``tests/golden/``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ----------------------------------------------------------------------------
+# validity: causal (diagonal included) and same segment          [P2f], [P2t]
+# ----------------------------------------------------------------------------
+def valid_row(seg_b, S: int, t: int) -> np.ndarray:
+    """Boolean [S]: True for keys s that query t may attend to.
+
+    s <= t (causal with the diagonal, [P2f]) and, when segment IDs are given,
+    seg[s] equal to seg[t] ([P2t]).
+    """
+    ok = np.zeros(S, dtype=bool)
+    ok[: t + 1] = True
+    if seg_b is not None:
+        ok &= np.asarray(seg_b) == seg_b[t]
+    return ok
+
+
+# ----------------------------------------------------------------------------
+# a1: indexer scores                                              [P3], [P3c]
+# ----------------------------------------------------------------------------
+def index_scores(q_idx, k_idx, w, seg, rows) -> np.ndarray:
+    """Indexer scores for the given query rows, in float64.
+
+    q_idx [B,S,Hi,Di], k_idx [B,S,Di], w [B,S,Hi] (any float dtype; used at
+    their exact values). seg [B,S] int or None. rows: 1-D array of query
+    positions t. Returns [B, len(rows), S] float64, where entry (b, r, s) is
+    I[b, t=rows[r], s] for s in valid(t) and -inf elsewhere.
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    k_idx = np.asarray(k_idx, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, S, Hi, Di = q_idx.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((B, rows.size, S), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            # per index head j: the query-key product of head j with every key
+            prod = q_idx[b, t] @ k_idx[b].T                  # [Hi, S]
+            score = w[b, t] @ np.maximum(prod, 0.0)          # sum_j w_j ReLU(.)
+            ok = valid_row(seg_b, S, int(t))
+            out[b, r, ok] = score[ok]
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even).
+
+    bfloat16 keeps 8 significant bits. Write x = m * 2**e with 0.5 <= |m| < 1.
+    Then m * 2**8 rounded to the nearest integer, with ties to even, gives
+    the kept significand. Values at and below bf16's smallest normal are not
+    produced by this workload. Infinities and zeros pass through unchanged.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(x[fin])
+    out[fin] = np.ldexp(np.rint(m * 256.0), e - 8)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a2: top-k selection                                                   [P3]
+# ----------------------------------------------------------------------------
+def topk_row(keys, valid, K: int) -> np.ndarray:
+    """Selected key positions of one query row, ascending.
+
+    keys: float [S] selection keys (the scores); valid: bool [S].
+    n = min(K, |valid|) keys are taken. A larger key comes first. Among
+    equal keys the smaller position comes first.
+    """
+    cand = np.nonzero(valid)[0]
+    n = min(int(K), cand.size)
+    kv = np.asarray(keys, dtype=np.float64)[cand]
+    order = np.lexsort((cand, -kv))     # primary: descending key; then ascending s
+    return np.sort(cand[order[:n]])
+
+
+def topk(scores, seg, rows, K: int, S: int) -> np.ndarray:
+    """Top-k index lists [B, len(rows), K] int32, ascending, padded with -1.
+
+    ``scores`` is [B, len(rows), S] (the selection keys of those rows).
+    Validity is recomputed from causality and segments, so entries outside
+    valid(t) are never read.
+    """
+    scores = np.asarray(scores)
+    B = scores.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((B, rows.size, K), -1, dtype=np.int32)
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            sel = topk_row(scores[b, r], valid_row(seg_b, S, int(t)), K)
+            out[b, r, : sel.size] = sel
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a2/a3: selection bitmask and tile classes                     [P2f], [P3n]
+# ----------------------------------------------------------------------------
+def selection_matrix(idx, S: int) -> np.ndarray:
+    """Boolean [B, S, S]: M[b,t,s] is True when s is in row t's index list."""
+    idx = np.asarray(idx)
+    B, n_rows, _ = idx.shape
+    M = np.zeros((B, n_rows, S), dtype=bool)
+    for b in range(B):
+        for t in range(n_rows):
+            sel = idx[b, t]
+            M[b, t, sel[sel >= 0]] = True
+    return M
+
+
+def pack_bits(M) -> np.ndarray:
+    """Pack a boolean [B, S, S] matrix into u64 words [B, S, ceil(S/64)].
+
+    Bit (s % 64) of word s // 64 is M[b, t, s].
+    """
+    M = np.asarray(M, dtype=bool)
+    B, R, S = M.shape
+    W = (S + 63) // 64
+    out = np.zeros((B, R, W), dtype=np.uint64)
+    for s in range(S):
+        out[:, :, s // 64] |= M[:, :, s].astype(np.uint64) << np.uint64(s % 64)
+    return out
+
+
+def tile_classes(M, TQ: int, TK: int) -> np.ndarray:
+    """Tile class [B, ceil(S/TQ), ceil(S/TK)] uint8 of a selection matrix.
+
+    0 = no selected pair in the tile, 2 = every in-range pair (t < S, s < S)
+    selected, 1 = otherwise.
+    """
+    M = np.asarray(M, dtype=bool)
+    B, S, _ = M.shape
+    nq, nk = (S + TQ - 1) // TQ, (S + TK - 1) // TK
+    out = np.zeros((B, nq, nk), dtype=np.uint8)
+    for b in range(B):
+        for i in range(nq):
+            for j in range(nk):
+                blk = M[b, i * TQ:(i + 1) * TQ, j * TK:(j + 1) * TK]
+                out[b, i, j] = 2 if blk.all() else (1 if blk.any() else 0)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# a4: sparse attention forward                      [P3n], [P2f]
+# ----------------------------------------------------------------------------
+def _kept(idx_row, seg_b, S: int, t: int) -> np.ndarray:
+    """Keys kept for query t: its index list, intersected again with causal and
+    segment validity (the index mask is added to the regular mask, [P3n])."""
+    sel = np.asarray(idx_row)
+    sel = sel[sel >= 0]
+    ok = valid_row(seg_b, S, t)
+    return np.unique(sel[ok[sel]])
+
+
+def attention_fwd(q, k, v, idx, seg, scale: float, rows):
+    """Masked softmax attention for the given query rows, in float64.
+
+    q,k [B,S,H,Dqk], v [B,S,H,Dv]. idx [B, len(rows), K] holds the index
+    lists of those rows. Returns O [B, len(rows), H, Dv] and LSE
+    [B, H, len(rows)] (natural log). A row with no kept key gives O = 0 and
+    LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, H, _ = q.shape
+    Dv = v.shape[-1]
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.zeros((B, rows.size, H, Dv))
+    L = np.full((B, H, rows.size), NEG_INF)
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            ks = _kept(idx[b, r], seg_b, S, int(t))
+            if ks.size == 0:
+                continue
+            for h in range(H):
+                logit = scale * (k[b, ks, h] @ q[b, t, h])       # [n]
+                m = logit.max()
+                e = np.exp(logit - m)
+                Z = e.sum()
+                O[b, r, h] = (e / Z) @ v[b, ks, h]
+                L[b, h, r] = m + np.log(Z)
+    return O, L
+
+
+# ----------------------------------------------------------------------------
+# a5-a7: backward                                                  [P2b]
+# ----------------------------------------------------------------------------
+def attention_bwd(q, k, v, dout, idx, seg, scale: float):
+    """Gradients of sum(O * dout) w.r.t. q, k, v for all rows, in float64.
+
+    idx [B, S, K] holds every row's index list. Returns dq, dk, dv in the
+    shapes of q, k, v.
+
+    Per kept pair (t, s) and head h:
+      P = softmax over kept s of scale * q_t . k_s
+      D(t) = sum_e dO(t,e) O(t,e)
+      dP(t,s) = dO(t) . v(s)
+      dS = P * (dP - D)
+      dq(t) = scale * sum_s dS k(s)
+      dk(s) = scale * sum_t dS q(t)
+      dv(s) = sum_t P dO(t)
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, H, _ = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for t in range(S):
+            ks = _kept(idx[b, t], seg_b, S, t)
+            if ks.size == 0:
+                continue
+            for h in range(H):
+                logit = scale * (k[b, ks, h] @ q[b, t, h])
+                e = np.exp(logit - logit.max())
+                P = e / e.sum()                                  # [n]
+                O = P @ v[b, ks, h]                              # [Dv]
+                D = dout[b, t, h] @ O
+                dP = v[b, ks, h] @ dout[b, t, h]                 # [n]
+                dS = P * (dP - D)
+                dq[b, t, h] = scale * (dS @ k[b, ks, h])
+                dk[b, ks, h] += scale * np.outer(dS, q[b, t, h])
+                dv[b, ks, h] += np.outer(P, dout[b, t, h])
+    return dq, dk, dv
+
+
+def attention_bwd_rows(q, k, v, dout, idx_rows, seg, scale: float, rows):
+    """dq for the given query rows only: [B, len(rows), H, Dqk].
+
+    It is the same formula as ``attention_bwd``. dq(t) needs only row t's
+    kept set, so a sample of rows can be checked at any size.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, H, Dqk = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((B, rows.size, H, Dqk))
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            ks = _kept(idx_rows[b, r], seg_b, S, int(t))
+            if ks.size == 0:
+                continue
+            for h in range(H):
+                logit = scale * (k[b, ks, h] @ q[b, t, h])
+                e = np.exp(logit - logit.max())
+                P = e / e.sum()
+                O = P @ v[b, ks, h]
+                D = dout[b, t, h] @ O
+                dS = P * (v[b, ks, h] @ dout[b, t, h] - D)
+                dq[b, r, h] = scale * (dS @ k[b, ks, h])
+    return dq
+
+
+def attention_bwd_keys(q, k, v, dout, idx, seg, scale: float, keys, heads):
+    """dk, dv of the given (key s, head h) pairs only.
+
+    idx [B, S, K] holds every row's index list, because the queries that
+    keep key s can sit anywhere at or after s. Returns dk [B, n, Dqk] and
+    dv [B, n, Dv], where n = len(keys) and pair i is (keys[i], heads[i]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    keys = np.asarray(keys, dtype=np.int64)
+    heads = np.asarray(heads, dtype=np.int64)
+    dk = np.zeros((B, keys.size, Dqk))
+    dv = np.zeros((B, keys.size, Dv))
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for i, (s, h) in enumerate(zip(keys, heads)):
+            for t in range(int(s), S):
+                ks = _kept(idx[b, t], seg_b, S, t)
+                pos = np.searchsorted(ks, s)
+                if pos >= ks.size or ks[pos] != s:
+                    continue
+                logit = scale * (k[b, ks, h] @ q[b, t, h])
+                e = np.exp(logit - logit.max())
+                P = e / e.sum()
+                O = P @ v[b, ks, h]
+                D = dout[b, t, h] @ O
+                dS = P[pos] * (v[b, s, h] @ dout[b, t, h] - D)
+                dk[b, i] += scale * dS * q[b, t, h]
+                dv[b, i] += P[pos] * dout[b, t, h]
+    return dk, dv

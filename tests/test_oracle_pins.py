@@ -1,0 +1,515 @@
+"""Pins of the float64 oracle to things other than itself (CPU only).
+
+Each pin comes from the mathematics or from an independent routine:
+  * hand-computed fixtures (tests/golden/*.json, each citing its page);
+  * brute-force scalar loops (math.fsum / math.exp) on tiny inputs;
+  * library routines: torch float64 scaled_dot_product_attention, logsumexp
+    and autograd, numpy argmax, torch's float32->bfloat16 rounding;
+  * closed forms and invariants: top-k >= |valid| gives dense causal
+    attention, K = 1 gives the argmax key's value, constant v passes through,
+    ReLU(x) + ReLU(-x) = |x|, linearity in w, the gradient sum rules;
+  * a complete property check of the top-k rule (every kept key beats every
+    dropped key, ties resolved by position).
+The last block plants plausible mistakes in copies of the oracle and shows
+that a pin catches each one.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as ref
+from sparse_attention_06_amd import inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    table = {"ln3": math.log(3.0), "ln4": math.log(4.0), "0.75ln3": 0.75 * math.log(3.0)}
+    return table[x] if isinstance(x, str) else float(x)
+
+
+def _tiny(B=2, S=9, Hi=3, Di=5, H=2, Dqk=4, Dv=3, seed=0, seg=True):
+    rng = np.random.default_rng(seed)
+    d = dict(
+        q_idx=rng.standard_normal((B, S, Hi, Di)),
+        k_idx=rng.standard_normal((B, S, Di)),
+        w=rng.standard_normal((B, S, Hi)),
+        q=rng.standard_normal((B, S, H, Dqk)),
+        k=rng.standard_normal((B, S, H, Dqk)),
+        v=rng.standard_normal((B, S, H, Dv)),
+        dout=rng.standard_normal((B, S, H, Dv)),
+    )
+    d["seg"] = np.array([[1] * 4 + [2] * (S - 4)] + [[5] * S] * (B - 1), dtype=np.int32) if seg else None
+    return d
+
+
+# ---------------------------------------------------------------- indexer pins
+def test_indexer_hand_fixture():
+    g = _load("indexer_hand.json")
+    q = np.array(g["q_idx"], float)
+    k = np.array(g["k_idx"], float)
+    w = np.array(g["w"], float)
+    rows = np.arange(g["S"])
+    for seg, key in ((None, "expected"), (np.array(g["seg"]), "expected_seg")):
+        got = ref.index_scores(q, k, w, seg, rows)
+        exp = np.array([[[(-np.inf if x is None else x) for x in r] for r in b] for b in g[key]])
+        np.testing.assert_array_equal(got, exp)
+
+
+def _brute_scores(q_idx, k_idx, w, seg, b, t):
+    B, S, Hi, Di = q_idx.shape
+    out = []
+    for s in range(S):
+        ok = s <= t and (seg is None or seg[b][s] == seg[b][t])
+        if not ok:
+            out.append(-math.inf)
+            continue
+        terms = []
+        for j in range(Hi):
+            dot = math.fsum(q_idx[b, t, j, d] * k_idx[b, s, d] for d in range(Di))
+            terms.append(w[b, t, j] * max(dot, 0.0))
+        out.append(math.fsum(terms))
+    return out
+
+
+@pytest.mark.parametrize("seg", [False, True])
+def test_indexer_brute_force(seg):
+    d = _tiny(seg=seg)
+    B, S = d["q_idx"].shape[:2]
+    got = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], d["seg"], np.arange(S))
+    for b in range(B):
+        for t in range(S):
+            np.testing.assert_allclose(got[b, t], _brute_scores(d["q_idx"], d["k_idx"], d["w"], d["seg"], b, t),
+                                       rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_relu_and_linearity_invariants():
+    d = _tiny(seg=False)
+    S = d["q_idx"].shape[1]
+    rows = np.arange(S)
+    I_pos = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], None, rows)
+    I_neg = ref.index_scores(-d["q_idx"], d["k_idx"], d["w"], None, rows)
+    absdot = np.abs(np.einsum("btjd,bsd->btjs", d["q_idx"], d["k_idx"]))
+    expect = np.einsum("btj,btjs->bts", d["w"], absdot)
+    causal = np.tril(np.ones((S, S), bool))
+    np.testing.assert_allclose((I_pos + I_neg)[:, causal], expect[:, causal], rtol=1e-12, atol=1e-12)
+    I_scaled = ref.index_scores(d["q_idx"], d["k_idx"], -2.5 * d["w"], None, rows)
+    np.testing.assert_allclose(I_scaled[:, causal], -2.5 * I_pos[:, causal], rtol=1e-12)
+    # Hi = 1, w = 1 and non-negative inputs: the score is the plain product
+    qn, kn = np.abs(d["q_idx"][:, :, :1]), np.abs(d["k_idx"])
+    I1 = ref.index_scores(qn, kn, np.ones_like(d["w"][:, :, :1]), None, rows)
+    np.testing.assert_allclose(I1[:, causal], np.einsum("btd,bsd->bts", qn[:, :, 0], kn)[:, causal], rtol=1e-12)
+
+
+def test_indexer_head_chunking_is_exact_sum():
+    # the score summed over two halves of the index heads equals the full sum
+    d = _tiny(Hi=6, seg=True)
+    S = d["q_idx"].shape[1]
+    rows = np.arange(S)
+    full = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], d["seg"], rows)
+    a = ref.index_scores(d["q_idx"][:, :, :3], d["k_idx"], d["w"][:, :, :3], d["seg"], rows)
+    b = ref.index_scores(d["q_idx"][:, :, 3:], d["k_idx"], d["w"][:, :, 3:], d["seg"], rows)
+    fin = np.isfinite(full)
+    np.testing.assert_allclose(full[fin], (a + b)[fin], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(fin, np.isfinite(a))
+
+
+def test_bf16_round_matches_torch_rne():
+    rng = np.random.default_rng(3)
+    x32 = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 0.07,
+                          rng.standard_normal(2000).astype(np.float32) * 1e3,
+                          np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf], np.float32)])
+    # exact halfway cases between neighbouring bf16 values
+    base = np.array([1.0, 1.0078125, 3.0, -5.0], np.float32).view(np.uint32)
+    halves = (base + np.uint32(0x8000)).view(np.float32)
+    x32 = np.concatenate([x32, halves])
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = ref.bf16_round(x32.astype(np.float64))
+    np.testing.assert_array_equal(got, want)
+
+
+# ----------------------------------------------------------------- top-k pins
+def test_topk_tie_fixture():
+    g = _load("topk_ties.json")
+    for c in g["cases"]:
+        keys = np.array(c["keys"], float)
+        S = keys.size
+        got = ref.topk(keys[None, None, :], None, [c["t"]], c["K"], S)[0, 0]
+        assert got.tolist() == c["expected"], c["why"]
+    # the hand fixture's index lists
+    gi = _load("indexer_hand.json")
+    q, k, w = (np.array(gi[n], float) for n in ("q_idx", "k_idx", "w"))
+    rows = np.arange(gi["S"])
+    sc = ref.index_scores(q, k, w, None, rows)
+    for kk in (1, 2):
+        got = ref.topk(sc, None, rows, kk, gi["S"])
+        assert got.tolist() == gi["topk"][f"K={kk}"]
+    seg = np.array(gi["seg"])
+    sc = ref.index_scores(q, k, w, seg, rows)
+    assert ref.topk(sc, seg, rows, 2, gi["S"]).tolist() == gi["topk_seg"]["K=2"]
+
+
+def _check_topk_properties(keys, valid, K, sel):
+    """Complete specification of the selection rule for one row."""
+    sel = np.asarray(sel)
+    kept = sel[sel >= 0]
+    cand = np.nonzero(valid)[0]
+    n = min(K, cand.size)
+    assert kept.size == n
+    assert np.all(sel[n:] == -1)
+    assert np.all(np.diff(kept) > 0)                       # ascending, distinct
+    assert np.all(valid[kept])
+    dropped = np.setdiff1d(cand, kept)
+    for s in kept:                                         # every kept key beats every dropped key
+        for u in dropped:
+            assert keys[s] > keys[u] or (keys[s] == keys[u] and s < u)
+
+
+def test_topk_complete_property_random_rows():
+    rng = np.random.default_rng(7)
+    for trial in range(300):
+        S = int(rng.integers(1, 40))
+        t = int(rng.integers(0, S))
+        K = int(rng.integers(1, 45))
+        # few distinct values so that ties are common; some signed zeros
+        keys = rng.integers(-3, 4, size=S).astype(float) * 0.5
+        keys[rng.random(S) < 0.1] = -0.0
+        seg = rng.integers(0, 2, size=S) if trial % 2 else None
+        valid = ref.valid_row(seg, S, t)
+        sel = ref.topk(keys[None, None], None if seg is None else seg[None], [t], K, S)[0, 0]
+        _check_topk_properties(keys, valid, K, sel)
+
+
+def test_topk_special_cases():
+    rng = np.random.default_rng(11)
+    S = 50
+    keys = rng.standard_normal(S)
+    for t in (0, 7, 49):
+        valid = ref.valid_row(None, S, t)
+        # K >= |valid|: every valid key
+        assert ref.topk_row(keys, valid, S + 3).tolist() == list(range(t + 1))
+        # K = 1: numpy argmax (first occurrence on ties)
+        assert ref.topk_row(keys, valid, 1).tolist() == [int(np.argmax(keys[: t + 1]))]
+        # all keys equal: the n lowest positions
+        assert ref.topk_row(np.zeros(S), valid, 5).tolist() == list(range(min(5, t + 1)))
+    # distinct keys: the set equals the set of the n largest by a full sort
+    for K in (1, 3, 17, 40):
+        want = set(np.argsort(-keys[:45])[:K].tolist())
+        assert set(ref.topk_row(keys, ref.valid_row(None, S, 44), K).tolist()) == want
+
+
+# ----------------------------------------------------------- bitmask / tiles
+def test_pack_bits_and_tile_classes_brute():
+    rng = np.random.default_rng(5)
+    B, S = 2, 131
+    M = rng.random((B, S, S)) < 0.3
+    M[:, :40, :30] = True               # a region of full tiles
+    M[:, 100:, 64:] = False             # a region of empty tiles
+    bits = ref.pack_bits(M)
+    for b in range(B):
+        for t in range(S):
+            for s in range(S):
+                assert bool((int(bits[b, t, s // 64]) >> (s % 64)) & 1) == M[b, t, s]
+    TQ, TK = 16, 8
+    cls = ref.tile_classes(M, TQ, TK)
+    for b, i, j in itertools.product(range(B), range(cls.shape[1]), range(cls.shape[2])):
+        vals = [M[b, t, s] for t in range(i * TQ, min(S, (i + 1) * TQ)) for s in range(j * TK, min(S, (j + 1) * TK))]
+        want = 2 if all(vals) else (1 if any(vals) else 0)
+        assert cls[b, i, j] == want
+    idx = np.full((B, S, S), -1, np.int32)
+    for b in range(B):
+        for t in range(S):
+            nz = np.nonzero(M[b, t])[0]
+            idx[b, t, : nz.size] = nz
+    assert np.array_equal(ref.selection_matrix(idx, S), M)
+
+
+# --------------------------------------------------------- attention fwd pins
+def test_attention_hand_fixture():
+    g = _load("attention_hand.json")
+    q = np.array([_num(x) for x in g["q"]]).reshape(1, 2, 1, 1)
+    k = np.array([_num(x) for x in g["k"]]).reshape(1, 2, 1, 1)
+    v = np.array([_num(x) for x in g["v"]]).reshape(1, 2, 1, 1)
+    dout = np.array([_num(x) for x in g["dout"]]).reshape(1, 2, 1, 1)
+    idx = np.array(g["idx"], np.int32)[None]
+    O, L = ref.attention_fwd(q, k, v, idx, None, g["scale"], [0, 1])
+    np.testing.assert_allclose(O[0, :, 0, 0], [_num(x) for x in g["O"]], rtol=1e-14)
+    np.testing.assert_allclose(L[0, 0], [_num(x) for x in g["LSE"]], rtol=1e-14, atol=1e-15)
+    dq, dk, dv = ref.attention_bwd(q, k, v, dout, idx, None, g["scale"])
+    np.testing.assert_allclose(dq[0, :, 0, 0], [_num(x) for x in g["dq"]], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dk[0, :, 0, 0], [_num(x) for x in g["dk"]], rtol=1e-14)
+    np.testing.assert_allclose(dv[0, :, 0, 0], [_num(x) for x in g["dv"]], rtol=1e-14)
+
+
+def _all_valid_idx(seg, B, S, K):
+    idx = np.full((B, S, K), -1, np.int32)
+    for b in range(B):
+        for t in range(S):
+            v = np.nonzero(ref.valid_row(None if seg is None else seg[b], S, t))[0][:K]
+            idx[b, t, : v.size] = v
+    return idx
+
+
+@pytest.mark.parametrize("seg", [False, True])
+def test_attention_topk_ge_S_is_dense_causal_sdpa(seg):
+    d = _tiny(S=11, H=3, Dqk=6, Dv=5, seg=seg)
+    q, k, v, sg = d["q"], d["k"], d["v"], d["seg"]
+    B, S, H, Dqk = q.shape
+    scale = 0.37
+    # index lists from the oracle's own indexer + top-k with K >= S
+    rows = np.arange(S)
+    sc = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], sg, rows)
+    idx = ref.topk(sc, sg, rows, S + 2, S)
+    O, L = ref.attention_fwd(q, k, v, idx, sg, scale, rows)
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+    mask = torch.tril(torch.ones(S, S, dtype=torch.bool)).expand(B, 1, S, S).clone()
+    if sg is not None:
+        ts = torch.from_numpy(sg)
+        mask &= (ts[:, None, :, None] == ts[:, None, None, :])
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    np.testing.assert_allclose(O, want.permute(0, 2, 1, 3).numpy(), rtol=1e-12, atol=1e-12)
+    logits = (tq @ tk.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
+    np.testing.assert_allclose(L, lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_k1_and_constant_v():
+    d = _tiny(S=10, seg=False)
+    q, k, v = d["q"], d["k"], d["v"]
+    B, S, H, _ = q.shape
+    rows = np.arange(S)
+    sc = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], None, rows)
+    idx = ref.topk(sc, None, rows, 1, S)
+    O, L = ref.attention_fwd(q, k, v, idx, None, 0.5, rows)
+    for b in range(B):
+        for t in range(S):
+            s = int(np.argmax(sc[b, t, : t + 1]))
+            np.testing.assert_allclose(O[b, t], v[b, s], rtol=1e-14)
+            np.testing.assert_allclose(L[b, :, t], 0.5 * np.einsum("hd,hd->h", q[b, t], k[b, s]), rtol=1e-12)
+    vc = np.broadcast_to(np.arange(1, 4, dtype=float), v.shape).copy()
+    idx = ref.topk(sc, None, rows, 4, S)
+    O, _ = ref.attention_fwd(q, k, vc, idx, None, 0.5, rows)
+    np.testing.assert_allclose(O, vc, rtol=1e-13)
+
+
+def test_attention_brute_force_scalar():
+    d = _tiny(S=9, seg=True)
+    q, k, v, sg = d["q"], d["k"], d["v"], d["seg"]
+    B, S, H, Dqk = q.shape
+    rows = np.arange(S)
+    sc = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], sg, rows)
+    idx = ref.topk(sc, sg, rows, 3, S)
+    O, L = ref.attention_fwd(q, k, v, idx, sg, 0.8, rows)
+    for b, t, h in itertools.product(range(B), range(S), range(H)):
+        ks = [int(s) for s in idx[b, t] if s >= 0]
+        lg = [0.8 * math.fsum(q[b, t, h, i] * k[b, s, h, i] for i in range(Dqk)) for s in ks]
+        m = max(lg)
+        e = [math.exp(x - m) for x in lg]
+        Z = math.fsum(e)
+        for c in range(v.shape[-1]):
+            assert abs(math.fsum(e[i] / Z * v[b, s, h, c] for i, s in enumerate(ks)) - O[b, t, h, c]) < 1e-12
+        assert abs(m + math.log(Z) - L[b, h, t]) < 1e-12
+
+
+def test_attention_packing_invariance():
+    # two documents packed in one row give the same outputs as run alone
+    d = _tiny(B=1, S=12, seg=False)
+    S1 = 5
+    seg = np.array([[1] * S1 + [2] * (12 - S1)], np.int32)
+    rows = np.arange(12)
+    sc = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], seg, rows)
+    idx = ref.topk(sc, seg, rows, 3, 12)
+    O, L = ref.attention_fwd(d["q"], d["k"], d["v"], idx, seg, 0.6, rows)
+    sl = slice(S1, 12)
+    rows2 = np.arange(12 - S1)
+    sc2 = ref.index_scores(d["q_idx"][:, sl], d["k_idx"][:, sl], d["w"][:, sl], None, rows2)
+    idx2 = ref.topk(sc2, None, rows2, 3, 12 - S1)
+    O2, L2 = ref.attention_fwd(d["q"][:, sl], d["k"][:, sl], d["v"][:, sl], idx2, None, 0.6, rows2)
+    np.testing.assert_allclose(O[:, sl], O2, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(L[:, :, sl], L2, rtol=1e-13)
+
+
+def test_attention_empty_row():
+    d = _tiny(B=1, S=4, seg=False)
+    idx = np.full((1, 4, 2), -1, np.int32)
+    idx[0, 2, 0] = 3          # a future key: dropped by the causal condition
+    O, L = ref.attention_fwd(d["q"], d["k"], d["v"], idx, None, 1.0, np.arange(4))
+    assert np.all(O == 0) and np.all(L == -np.inf)
+    dq, dk, dv = ref.attention_bwd(d["q"], d["k"], d["v"], d["dout"], idx, None, 1.0)
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+# --------------------------------------------------------- attention bwd pins
+def _random_sets(B, S, K, seg, seed):
+    return inputs.random_index_sets(B, S, K, seg, seed)
+
+
+@pytest.mark.parametrize("seg", [False, True])
+def test_attention_bwd_torch_autograd(seg):
+    d = _tiny(S=10, H=2, Dqk=5, Dv=4, seg=seg)
+    q, k, v, dout, sg = d["q"], d["k"], d["v"], d["dout"], d["seg"]
+    B, S, H, _ = q.shape
+    idx = _random_sets(B, S, 4, sg, seed=1)
+    scale = 0.45
+    dq, dk, dv = ref.attention_bwd(q, k, v, dout, idx, sg, scale)
+    M = torch.from_numpy(ref.selection_matrix(idx, S))[:, None]              # [B,1,S,S]
+    tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3).clone().requires_grad_(True) for x in (q, k, v))
+    logits = (tq @ tk.transpose(-1, -2)) * scale
+    P = torch.softmax(logits.masked_fill(~M, -math.inf), dim=-1)
+    O = P @ tv
+    (O * torch.from_numpy(dout).permute(0, 2, 1, 3)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_attention_bwd_finite_differences():
+    d = _tiny(B=1, S=6, H=1, Dqk=3, Dv=2, seg=False)
+    q, k, v, dout = d["q"], d["k"], d["v"], d["dout"]
+    S = q.shape[1]
+    idx = _random_sets(1, S, 3, None, seed=2)
+    scale = 0.9
+    rows = np.arange(S)
+    dq, dk, dv = ref.attention_bwd(q, k, v, dout, idx, None, scale)
+
+    def f(q_, k_, v_):
+        O, _ = ref.attention_fwd(q_, k_, v_, idx, None, scale, rows)
+        return float(np.sum(O * dout))
+
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for pos in itertools.product(*(range(n) for n in x.shape)):
+            xp, xm = x.copy(), x.copy()
+            xp[pos] += h
+            xm[pos] -= h
+            args = {"q": q, "k": k, "v": v}
+            num = (f(**{**{a + "_": b for a, b in args.items()}, name + "_": xp})
+                   - f(**{**{a + "_": b for a, b in args.items()}, name + "_": xm})) / (2 * h)
+            assert abs(num - g[pos]) < 1e-7, (name, pos, num, g[pos])
+
+
+def test_attention_bwd_sum_rules_and_row_key_variants():
+    d = _tiny(B=2, S=12, H=2, seg=True)
+    q, k, v, dout, sg = d["q"], d["k"], d["v"], d["dout"], d["seg"]
+    B, S, H, _ = q.shape
+    idx = _random_sets(B, S, 5, sg, seed=3)
+    dq, dk, dv = ref.attention_bwd(q, k, v, dout, idx, sg, 0.7)
+    # sum_s dS(t, s) = 0 for every non-empty row, hence sum_s dk(s) = 0
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    # sum_s P(t, s) = 1, hence sum_s dv(s) = sum_t dO(t)
+    np.testing.assert_allclose(dv.sum(axis=1), dout.sum(axis=1), rtol=1e-12, atol=1e-12)
+    rows = np.array([0, 3, 11])
+    np.testing.assert_allclose(ref.attention_bwd_rows(q, k, v, dout, idx[:, rows], sg, 0.7, rows), dq[:, rows],
+                               rtol=1e-13, atol=1e-14)
+    keys, heads = np.array([0, 4, 7, 11]), np.array([1, 0, 1, 0])
+    dk_s, dv_s = ref.attention_bwd_keys(q, k, v, dout, idx, sg, 0.7, keys, heads)
+    np.testing.assert_allclose(dk_s, dk[:, keys, heads], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dv_s, dv[:, keys, heads], rtol=1e-13, atol=1e-14)
+
+
+# -------------------------------------------------- planted mistakes are caught
+def test_planted_mistakes_fail_a_pin(monkeypatch):
+    """Copies of oracle steps with one plausible mistake each; a pin must fail."""
+    g = _load("indexer_hand.json")
+    q, k, w = (np.array(g[n], float) for n in ("q_idx", "k_idx", "w"))
+    expect = np.array([[[(-np.inf if x is None else x) for x in r] for r in b] for b in g["expected"]])
+
+    def scores_no_relu(q_idx, k_idx, w_, rows):
+        out = np.full((1, 3, 3), -np.inf)
+        for t in rows:
+            out[0, t, : t + 1] = (w_[0, t] @ (q_idx[0, t] @ k_idx[0].T))[: t + 1]
+        return out
+
+    def scores_w_inside(q_idx, k_idx, w_, rows):
+        out = np.full((1, 3, 3), -np.inf)
+        for t in rows:
+            out[0, t, : t + 1] = np.maximum(w_[0, t][:, None] * (q_idx[0, t] @ k_idx[0].T), 0).sum(0)[: t + 1]
+        return out
+
+    def scores_strict_causal(q_idx, k_idx, w_, rows):
+        out = ref.index_scores(q_idx, k_idx, w_, None, rows)
+        for t in rows:
+            out[0, t, t] = -np.inf
+        return out
+
+    for bad in (scores_no_relu, scores_w_inside, scores_strict_causal):
+        assert not np.array_equal(bad(q, k, w, range(3)), expect), bad.__name__
+
+    # wrong tie order (larger position first) breaks the tie fixture
+    def topk_row_bad(keys, valid, K):
+        cand = np.nonzero(valid)[0]
+        order = np.lexsort((-cand, -np.asarray(keys)[cand]))
+        return np.sort(cand[order[: min(K, cand.size)]])
+
+    monkeypatch.setattr(ref, "topk_row", topk_row_bad)
+    with pytest.raises(AssertionError):
+        test_topk_tie_fixture()
+    monkeypatch.undo()
+
+    # a transposed softmax scale (dividing instead of multiplying) breaks SDPA parity
+    orig = ref.attention_fwd
+
+    def fwd_bad(q_, k_, v_, idx, seg, scale, rows):
+        return orig(q_, k_, v_, idx, seg, 1.0 / scale, rows)
+
+    monkeypatch.setattr(ref, "attention_fwd", fwd_bad)
+    with pytest.raises(AssertionError):
+        test_attention_topk_ge_S_is_dense_causal_sdpa(False)
+    monkeypatch.undo()
+
+    # a dropped D term in the backward (dS = P * dP) breaks the autograd pin
+    def bwd_bad(q_, k_, v_, dout, idx, seg, scale):
+        B, S, H, _ = q_.shape
+        dq, dk, dv = np.zeros_like(q_), np.zeros_like(k_), np.zeros_like(v_)
+        for b in range(B):
+            for t in range(S):
+                ks = ref._kept(idx[b, t], None if seg is None else seg[b], S, t)
+                for h in range(H):
+                    lg = scale * (k_[b, ks, h] @ q_[b, t, h])
+                    P = np.exp(lg - lg.max())
+                    P /= P.sum()
+                    dS = P * (v_[b, ks, h] @ dout[b, t, h])
+                    dq[b, t, h] = scale * (dS @ k_[b, ks, h])
+                    dk[b, ks, h] += scale * np.outer(dS, q_[b, t, h])
+                    dv[b, ks, h] += np.outer(P, dout[b, t, h])
+        return dq, dk, dv
+
+    monkeypatch.setattr(ref, "attention_bwd", bwd_bad)
+    with pytest.raises(AssertionError):
+        test_attention_bwd_torch_autograd(False)
+    monkeypatch.undo()
+
+
+# ------------------------------------------------------------- input recipe
+def test_inputs_deterministic_and_distribution():
+    cfg = inputs.CONFIGS["c2"].replace(B=1, S=256)
+    a = inputs.make(cfg)
+    b = inputs.make(cfg)
+    for n in ("q", "k", "v", "q_idx", "k_idx", "w", "dout"):
+        assert torch.equal(a[n], b[n]), n
+        assert a[n].dtype == torch.bfloat16
+    assert abs(a["q"].float().std().item() - 192 ** -0.5) < 0.01
+    assert abs(a["w"].float().std().item() - 64 ** -0.5) < 0.01
+    assert abs(a["dout"].float().std().item() - 1.0) < 0.05
+    seg = inputs.segment_ids(4, 8192, 64, 4096, 0)
+    for row in seg:
+        assert row[0] == 1 and np.all(np.diff(row) >= 0) and np.all(np.diff(row) <= 1)
+        _, counts = np.unique(row, return_counts=True)
+        assert np.all(counts[:-1] >= 64) and np.all(counts[:-1] <= 4096)
+    sets = inputs.random_index_sets(2, 50, 8, seg[:2, :50], 0)
+    for b in range(2):
+        for t in range(50):
+            row = sets[b, t]
+            kept = row[row >= 0]
+            assert np.all(np.diff(kept) > 0) and np.all(kept <= t)
+            assert np.all(seg[b, kept] == seg[b, t])
