@@ -1,0 +1,201 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) hot path on MI355X (gfx950).
+ *
+ * The path has three steps, each a call below:
+ *   1. dsa_index_scores   lightning-indexer scores per (query, key)
+ *   2. dsa_topk           per-query top-k selection, emitted as index lists and
+ *                         as the attention mask (selection bits + tile classes)
+ *   3. dsa_sparse_attn_fwd / dsa_sparse_attn_bwd
+ *                         flash attention restricted to the selected keys
+ *                         (forward; dQ/dK/dV backward)
+ * dsa_build_mask turns index lists that come from elsewhere into the same mask.
+ *
+ * Sources (page title, section):
+ *   "DeepSeek3.2: Onboard sparse attention", Background: an indexer computes a
+ *     parametric index score as a query-key product, and a non-parametric top-k
+ *     picks the keys and values each query attends to. Section "What this PR
+ *     does", item 1: the top-k indices become an index mask that is added to
+ *     the ordinary attention mask. Training only. Item 2: the 671B config uses
+ *     64 index heads of dim 128 and top-k 2048.
+ *   "Support Ring Attention with DeepSeek DSA Sparse Indexer", Forward Flow:
+ *     the index mask is [batch, S, S] and shared by all heads. It is combined
+ *     with the causal condition (diagonal included), and logits are scaled
+ *     query-key products on kept entries. Backward Flow: dQ = dP K,
+ *     dK = dP^T Q, dV = P^T dO on the same mask. Tests: the mask is threaded
+ *     with and without segment IDs.
+ *   "Integrate DeepSeek Sparse Attention with Tokamax Flash Attention",
+ *     Description: flash attention takes a 3-D dynamic index mask in place of
+ *     additive masking.
+ *
+ * Definitions used by every call:
+ *   valid(t) = { s : s <= t and (seg == NULL or seg[b,s] == seg[b,t]) }
+ *   I[b,t,s] = sum_j w[b,t,j] * max(0, sum_d q_idx[b,t,j,d] * k_idx[b,s,d])
+ *   T(b,t)   = the n = min(K, |valid(t)|) keys of valid(t) with the largest
+ *              scores; equal scores go to the smaller s; -0 == +0
+ *   attention of query t, head h, over T(t):
+ *              P = softmax_s(scale * q[b,t,h] . k[b,s,h]),  O = sum_s P v[b,s,h]
+ *              LSE = log(sum_s exp(scale * q . k))   (natural log, float32)
+ *   A row with T(t) empty gives O = 0, LSE = -inf and zero gradients.
+ *
+ * Conventions:
+ *   - Every tensor is caller-owned DEVICE memory, contiguous row-major in the
+ *     layout given next to it, and at least 16-byte aligned. The library never
+ *     allocates and keeps no state besides a per-thread error string.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Every call only
+ *     enqueues work on it and returns; nothing waits. A kernel fault shows up
+ *     at the caller's next synchronisation.
+ *   - Return value: DSA_OK, or an error code with no work enqueued. Arguments
+ *     are checked on the host before any launch: NULL pointers, sizes < 1,
+ *     misaligned pointers, unsupported dtype or dims, row ranges outside [0,S),
+ *     ld < S, workspace too small. A failed launch returns DSA_ERR_HIP.
+ *     dsa_last_error() then gives the detail.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - bf16 tensors hold bfloat16 bit patterns. Every product is accumulated in
+ *     float32, and stores round to nearest even.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* NULL pointer, size < 1, bad range, misalignment */
+  DSA_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype/dim combination) */
+  DSA_ERR_WORKSPACE = 3,   /* workspace smaller than dsa_bwd_workspace_bytes() */
+  DSA_ERR_HIP = 4          /* a HIP launch failed */
+} dsa_status;
+
+typedef enum { DSA_BF16 = 0, DSA_FP32 = 1 } dsa_dtype;
+
+/* Tile of the attention kernels. The tile-class map of the mask is laid out on
+ * this grid: one class per (128 queries) x (64 keys). */
+#define DSA_TILE_Q 128
+#define DSA_TILE_K 64
+
+/* Tile classes stored in the mask. */
+#define DSA_TILE_EMPTY 0 /* no selected (t, s) in the tile */
+#define DSA_TILE_PARTIAL 1
+#define DSA_TILE_FULL 2 /* every (t, s) with t < S selected; keys all < S */
+
+/* ---------------------------------------------------------------------------
+ * Size of the attention mask buffer for B x S, in bytes. Layout:
+ *   sel_bits  uint64 [B][S][W], W = ceil(S/64). Bit (s % 64) of word s/64 of
+ *             row (b,t) is 1 iff s is in T(b,t). Bits beyond S are 0.
+ *   tile_cls  uint8  [B][ceil(S/DSA_TILE_Q)][ceil(S/DSA_TILE_K)], starting at
+ *             byte B*S*W*8. Class of each tile of the selection matrix.
+ * Produced only by dsa_topk or dsa_build_mask. Every set bit lies in valid(t),
+ * so the mask already combines index, causal and segment conditions.
+ * ------------------------------------------------------------------------- */
+size_t dsa_mask_bytes(int B, int S);
+
+/* ---------------------------------------------------------------------------
+ * dsa_index_scores -- indexer scores I[b,t,s] for the query rows
+ * t in [row0, row0 + nrows).
+ * Source: "DeepSeek3.2: Onboard sparse attention", Background (the index score
+ * is a query-key product of the indexer) and item 2 (64 x 128 index heads).
+ *   q_idx   [B,S,Hi,Di]  in_dtype   index queries (after any RoPE)
+ *   k_idx   [B,S,Di]     in_dtype   index keys, one per token, shared by heads
+ *   w       [B,S,Hi]     in_dtype   per-token, per-index-head weights
+ *   seg     [B,S] int32 or NULL     segment IDs (NULL = one segment)
+ *   scores  [B,nrows,ld] score_dtype   out: row r holds query t = row0 + r.
+ *           Entry s is written with I[b,t,s] for every s in valid(t); entries
+ *           outside valid(t) are left unspecified.
+ * in_dtype DSA_BF16 or DSA_FP32; score_dtype DSA_FP32 or DSA_BF16 (bf16 is
+ * the float32 score rounded to nearest even). Any Hi, Di >= 1 are accepted.
+ * bf16 inputs with Hi in {32, 64} and Di in {64, 128} take the MFMA kernel;
+ * the rest take a plain kernel.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
+                            const int32_t* seg, int B, int S, int Hi, int Di,
+                            dsa_dtype in_dtype, int row0, int nrows, void* scores,
+                            dsa_dtype score_dtype, int64_t ld, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dsa_topk -- top-k selection of the rows t in [row0, row0 + nrows).
+ * Source: "DeepSeek3.2: Onboard sparse attention", Background and item 1
+ * (select the top-k keys of each query; get the top-k indices and the index
+ * mask); "Support Ring Attention with DeepSeek DSA Sparse Indexer", Forward
+ * Flow (mask [batch, S, S] combined with causal).
+ *   scores  [B,nrows,ld] score_dtype, as written by dsa_index_scores. Only the
+ *           entries in valid(t) are read.
+ *   seg     [B,S] int32 or NULL (must match the one given to the indexer)
+ *   idx     [B,S,K] int32  out: rows t of the slab get T(b,t) ascending,
+ *           then -1 up to K entries. Other rows are untouched.
+ *   mask    dsa_mask_bytes(B,S) bytes  out: sel_bits rows of the slab and the
+ *           tile classes of the query tiles inside the slab.
+ * K >= 1 (K >= S gives dense causal attention). row0 must be a multiple of
+ * DSA_TILE_Q, and row0 + nrows must be a multiple of DSA_TILE_Q or equal S, so
+ * that every query tile's class is built from rows of one call. Scores must be
+ * finite; NaN gives an unspecified selection.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld,
+                    const int32_t* seg, int B, int S, int K, int row0, int nrows,
+                    int32_t* idx, void* mask, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dsa_build_mask -- attention mask from index lists given by the caller.
+ * Source: same passages as dsa_topk (index mask shared by all heads, combined
+ * with the causal and segment conditions).
+ *   idx   [B,S,K] int32: entries < 0 or >= S are ignored, as are entries
+ *         outside valid(t) (so the mask equals idx AND causal AND segment).
+ *         Duplicates are harmless.
+ *   seg   [B,S] int32 or NULL
+ *   mask  dsa_mask_bytes(B,S) bytes  out: all of it.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_build_mask(const int32_t* idx, const int32_t* seg, int B, int S, int K,
+                          void* mask, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dsa_sparse_attn_fwd -- attention of every query over its selected keys.
+ * Source: "Support Ring Attention with DeepSeek DSA Sparse Indexer", Forward
+ * Flow (logits are the query-key products times scale on kept entries);
+ * "Integrate DeepSeek Sparse Attention with Tokamax Flash Attention",
+ * Description (flash attention with a dynamic 3-D index mask).
+ *   q, k  [B,S,H,Dqk] dtype;  v [B,S,H,Dv] dtype
+ *   mask  from dsa_topk / dsa_build_mask for the same B, S
+ *   o     [B,S,H,Dv] dtype  out
+ *   lse   [B,H,S] float32   out (natural log; -inf for an empty row)
+ * dtype DSA_BF16 or DSA_FP32. bf16 with (Dqk, Dv) = (192, 128) takes the MFMA
+ * kernel; other dims up to 256 take a plain kernel.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
+                               int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                               dsa_dtype dtype, void* o, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dsa_sparse_attn_bwd -- gradients of sum(O * dout) w.r.t. q, k, v.
+ * Source: "Support Ring Attention with DeepSeek DSA Sparse Indexer", Backward
+ * Flow (dQ = dP K, dK = dP^T Q, dV = P^T dO, each on the kept entries).
+ *   q, k, v, o, dout  as in the forward (o and lse from dsa_sparse_attn_fwd)
+ *   lse       [B,H,S] float32
+ *   mask      the forward's mask
+ *   dq, dk    [B,S,H,Dqk] dtype out;  dv [B,S,H,Dv] dtype out
+ *   workspace device scratch of at least dsa_bwd_workspace_bytes() bytes
+ *             (holds D = rowsum(dout * o) as float32 [B,H,S]).
+ * Deterministic: no atomics; dK/dV run key-major and dQ query-major.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, const void* mask,
+                               int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                               dsa_dtype dtype, void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv);
+
+/* Human-readable name of a status code. Static storage. */
+const char* dsa_status_string(dsa_status s);
+/* Detail of the last non-OK return on this thread ("" if none). */
+const char* dsa_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

@@ -1,0 +1,231 @@
+// C ABI of the DSA hot path: host-side argument checks, then kernel launches.
+// Every check runs before any HIP call, so the error paths can be exercised on
+// a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dsa.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dsa_status ok() {
+  g_err[0] = '\0';
+  return DSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQ(cond, code, ...)                 \
+  do {                                       \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQ_PTR(p)                                                                   \
+  do {                                                                               \
+    REQ((p) != nullptr, DSA_ERR_INVALID_ARG, "%s must not be NULL", #p);             \
+    REQ(aligned16(p), DSA_ERR_INVALID_ARG, "%s must be 16-byte aligned", #p);        \
+  } while (0)
+
+dsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(dsa_dtype d) { return d == DSA_BF16 || d == DSA_FP32; }
+
+uint64_t* bits_of(void* mask) { return (uint64_t*)mask; }
+uint8_t* cls_of(void* mask, int B, int S) { return (uint8_t*)mask + dsa::bits_bytes(B, S); }
+
+// largest S: a build-mask row (S/64 words) must fit one workgroup's 64 KB of
+// dynamic LDS, with room to spare
+constexpr int kMaxS = 1 << 18;
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_mask_bytes(int B, int S) {
+  if (B < 1 || S < 1) return 0;
+  return dsa::bits_bytes(B, S) + (size_t)B * dsa::n_qtiles(S) * dsa::n_ktiles(S);
+}
+
+size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv) {
+  (void)Dqk;
+  (void)Dv;
+  if (B < 1 || S < 1 || H < 1) return 0;
+  return (size_t)B * H * S * sizeof(float);
+}
+
+const char* dsa_status_string(dsa_status s) {
+  switch (s) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+int dsa_version(void) { return 100; }  // 0.1.0
+
+dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
+                            const int32_t* seg, int B, int S, int Hi, int Di,
+                            dsa_dtype in_dtype, int row0, int nrows, void* scores,
+                            dsa_dtype score_dtype, int64_t ld, void* stream) {
+  REQ_PTR(q_idx);
+  REQ_PTR(k_idx);
+  REQ_PTR(w);
+  REQ_PTR(scores);
+  REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
+  REQ(B >= 1 && S >= 1 && Hi >= 1 && Di >= 1, DSA_ERR_INVALID_ARG,
+      "sizes must be >= 1 (B=%d S=%d Hi=%d Di=%d)", B, S, Hi, Di);
+  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
+      "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
+  REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld < S=%d", (long long)ld, S);
+  REQ(dtype_ok(in_dtype) && dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  const bool in_bf16 = in_dtype == DSA_BF16, out_bf16 = score_dtype == DSA_BF16;
+  REQ(!in_bf16 || Di % 8 == 0, DSA_ERR_UNSUPPORTED, "bf16 index dim must be a multiple of 8");
+  hipStream_t st = (hipStream_t)stream;
+  if (in_bf16 && (Hi == 32 || Hi == 64) && (Di == 64 || Di == 128))
+    return hip_status(dsa::launch_index_scores_mfma(q_idx, k_idx, w, seg, B, S, Hi, Di, row0, nrows,
+                                                    scores, out_bf16, ld, st),
+                      "dsa_index_scores");
+  REQ((size_t)(Hi * Di + Hi) * 4 <= 65536, DSA_ERR_UNSUPPORTED,
+      "Hi*Di=%d too large for the plain indexer kernel", Hi * Di);
+  return hip_status(dsa::launch_index_scores_plain(q_idx, k_idx, w, seg, B, S, Hi, Di, in_bf16, row0,
+                                                   nrows, scores, out_bf16, ld, st),
+                    "dsa_index_scores");
+}
+
+dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* seg,
+                    int B, int S, int K, int row0, int nrows, int32_t* idx, void* mask,
+                    void* stream) {
+  REQ_PTR(scores);
+  REQ_PTR(idx);
+  REQ_PTR(mask);
+  REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
+  REQ(B >= 1 && S >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d K=%d)", B, S, K);
+  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
+      "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
+  REQ(row0 % DSA_TILE_Q == 0 && ((row0 + nrows) % DSA_TILE_Q == 0 || row0 + nrows == S),
+      DSA_ERR_INVALID_ARG, "row slab [%d, %d) must start and end on a %d-row query tile (or at S)",
+      row0, row0 + nrows, DSA_TILE_Q);
+  REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld < S=%d", (long long)ld, S);
+  REQ(dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown score dtype");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dsa::launch_topk(scores, score_dtype == DSA_BF16, ld, seg, B, S, K, row0, nrows, idx,
+                                  bits_of(mask), st);
+  if (e != hipSuccess) return hip_status(e, "dsa_topk");
+  const int qt0 = row0 / DSA_TILE_Q, qt1 = (row0 + nrows + DSA_TILE_Q - 1) / DSA_TILE_Q;
+  return hip_status(dsa::launch_tile_classes(bits_of(mask), B, S, qt0, qt1, cls_of(mask, B, S), st),
+                    "dsa_topk tile classes");
+}
+
+dsa_status dsa_build_mask(const int32_t* idx, const int32_t* seg, int B, int S, int K, void* mask,
+                          void* stream) {
+  REQ_PTR(idx);
+  REQ_PTR(mask);
+  REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
+  REQ(B >= 1 && S >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d K=%d)", B, S, K);
+  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dsa::launch_build_bits(idx, seg, B, S, K, bits_of(mask), st);
+  if (e != hipSuccess) return hip_status(e, "dsa_build_mask");
+  return hip_status(dsa::launch_tile_classes(bits_of(mask), B, S, 0, dsa::n_qtiles(S),
+                                             cls_of(mask, B, S), st),
+                    "dsa_build_mask tile classes");
+}
+
+static dsa_status check_attn(int B, int S, int H, int Dqk, int Dv, float scale, dsa_dtype dtype) {
+  REQ(B >= 1 && S >= 1 && H >= 1 && Dqk >= 1 && Dv >= 1, DSA_ERR_INVALID_ARG,
+      "sizes must be >= 1 (B=%d S=%d H=%d Dqk=%d Dv=%d)", B, S, H, Dqk, Dv);
+  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(dtype_ok(dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  REQ(scale == scale && scale > 0.f, DSA_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  REQ(Dqk <= 256 && Dv <= 256, DSA_ERR_UNSUPPORTED, "head dims above 256 (Dqk=%d Dv=%d)", Dqk, Dv);
+  REQ(dtype != DSA_BF16 || (Dqk % 8 == 0 && Dv % 8 == 0), DSA_ERR_UNSUPPORTED,
+      "bf16 head dims must be multiples of 8");
+  return DSA_OK;
+}
+
+static bool attn_mfma(int Dqk, int Dv, dsa_dtype dtype) {
+  return dtype == DSA_BF16 && Dqk == 192 && Dv == 128;
+}
+
+dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
+                               int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                               dsa_dtype dtype, void* o, float* lse, void* stream) {
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(v);
+  REQ_PTR(mask);
+  REQ_PTR(o);
+  REQ_PTR(lse);
+  dsa_status s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
+  if (s != DSA_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  void* m = const_cast<void*>(mask);
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_fwd_mfma(q, k, v, bits_of(m), cls_of(m, B, S), B, S, H,
+                                                softmax_scale, o, lse, st),
+                      "dsa_sparse_attn_fwd");
+  return hip_status(dsa::launch_attn_fwd_plain(q, k, v, bits_of(m), B, S, H, Dqk, Dv, softmax_scale,
+                                               dtype == DSA_BF16, o, lse, st),
+                    "dsa_sparse_attn_fwd");
+}
+
+dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                               const void* dout, const float* lse, const void* mask, int B, int S,
+                               int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype,
+                               void* dq, void* dk, void* dv, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(v);
+  REQ_PTR(o);
+  REQ_PTR(dout);
+  REQ_PTR(lse);
+  REQ_PTR(mask);
+  REQ_PTR(dq);
+  REQ_PTR(dk);
+  REQ_PTR(dv);
+  REQ_PTR(workspace);
+  dsa_status s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
+  if (s != DSA_OK) return s;
+  const size_t need = dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv);
+  REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  void* m = const_cast<void*>(mask);
+  float* D = (float*)workspace;
+  const bool bf16 = dtype == DSA_BF16;
+  hipError_t e = dsa::launch_bwd_rowdot(o, dout, B, S, H, Dv, bf16, D, st);
+  if (e != hipSuccess) return hip_status(e, "dsa_sparse_attn_bwd rowdot");
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_bwd_mfma(q, k, v, dout, lse, D, bits_of(m), cls_of(m, B, S), B,
+                                                S, H, softmax_scale, dq, dk, dv, st),
+                      "dsa_sparse_attn_bwd");
+  return hip_status(dsa::launch_attn_bwd_plain(q, k, v, dout, lse, D, bits_of(m), B, S, H, Dqk, Dv,
+                                               softmax_scale, bf16, dq, dk, dv, st),
+                    "dsa_sparse_attn_bwd");
+}
+
+}  // extern "C"

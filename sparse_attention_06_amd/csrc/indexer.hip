@@ -1,0 +1,204 @@
+// Lightning-indexer scores (gfx950).
+//
+// I[b,t,s] = sum_j w[b,t,j] * max(0, q_idx[b,t,j,:] . k_idx[b,s,:]) for s in
+// valid(t) (causal with the diagonal, same segment). Source: "DeepSeek3.2:
+// Onboard sparse attention", Background (the indexer's parametric query-key
+// product) and "What this PR does", item 2 (64 index heads x 128).
+//
+// MFMA kernel: per query t, the product of its index heads with a tile of 32
+// keys is a [Hi x 32] GEMM with K = Di. Heads go on the MFMA row dimension and
+// keys on the column dimension. Each lane then owns one key column and 16
+// head rows per 32-head block, so the ReLU and the w-weighted sum over heads
+// are in-lane float32 FMAs, with one exchange between the two lane halves.
+// q_idx[t] (Hi x Di bf16, 16 KB at 64 x 128) stays in VGPRs as MFMA A
+// fragments for the whole key loop. The 32-key k_idx tile is staged through
+// LDS once per workgroup (4 waves = 4 consecutive queries) and double buffered.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsa {
+
+template <int HB, int KS, typename OutT>
+__global__ __launch_bounds__(256) void index_scores_mfma_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
+    const uint16_t* __restrict__ w, const int32_t* __restrict__ seg, int B, int S, int row0,
+    int nrows, OutT* __restrict__ scores, int64_t ld) {
+  constexpr int Hi = HB * 32, Di = KS * 16;
+  constexpr int TILE = 32;
+  constexpr int ROWB = Di * 2 + 16;          // padded LDS row: conflict-free b128 reads
+  constexpr int CPR = Di * 2 / 16;           // 16-byte chunks per key row
+  constexpr int CPT = (TILE * CPR + 255) / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][TILE * ROWB];
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int nrb = (nrows + 3) / 4;
+  const int rb = nrb - 1 - (int)(blockIdx.x / B);  // longest rows first
+  const int b = blockIdx.x % B;
+  const int r = rb * 4 + wid;
+  const bool active = r < nrows;
+  const int t = row0 + r;
+  const int t_last = row0 + min(nrows - 1, rb * 4 + 3);
+  const int nkt = t_last / TILE + 1;
+
+  u32x4 afrag[HB][KS];
+  float wreg[HB][16];
+  int seg_t = 0;
+  if (active) {
+    const uint16_t* qrow = q_idx + ((size_t)b * S + t) * Hi * Di;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        afrag[hb][ks] = *(const u32x4*)(qrow + (size_t)(hb * 32 + col) * Di + ks * 16 + 8 * half);
+    const uint16_t* wrow = w + ((size_t)b * S + t) * Hi;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) wreg[hb][rr] = bf2f(wrow[hb * 32 + acc_row(rr, half)]);
+    if (seg) seg_t = seg[(size_t)b * S + t];
+  }
+
+  u32x4 pre[CPT];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = threadIdx.x + c * 256;
+      const int row = ci / CPR, cc = ci % CPR;
+      const int s = kt * TILE + row;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (ci < TILE * CPR && s < S) z = *(const u32x4*)(k_idx + ((size_t)b * S + s) * Di + cc * 8);
+      pre[c] = z;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ci = threadIdx.x + c * 256;
+      if (ci < TILE * CPR) {
+        const int row = ci / CPR, cc = ci % CPR;
+        *(u32x4*)(&lds[buf][row * ROWB + cc * 16]) = pre[c];
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  OutT* out_row = scores + ((size_t)b * nrows + r) * ld;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) gload(kt + 1);
+    const int s0 = kt * TILE;
+    if (active && s0 <= t) {
+      const int s = s0 + col;
+      bool ok = s <= t;
+      if (seg && ok) ok = seg[(size_t)b * S + s] == seg_t;
+      if (__ballot(ok)) {
+        f32x16 acc[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4 bq = *(const u32x4*)(&lds[buf][col * ROWB + (ks * 16 + 8 * half) * 2]);
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(afrag[hb][ks], bq, acc[hb]);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) part = fmaf(wreg[hb][rr], fmaxf(acc[hb][rr], 0.f), part);
+        part += __shfl_xor(part, 32);
+        if (half == 0 && ok) Elem<OutT>::store(out_row + s, part);
+      }
+    }
+    if (kt + 1 < nkt) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// Plain kernel for any (Hi, Di) and fp32 or bf16 inputs: one thread per key s,
+// the query's Hi x Di index vectors staged in LDS as float32.
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(256) void index_scores_plain_kernel(
+    const InT* __restrict__ q_idx, const InT* __restrict__ k_idx, const InT* __restrict__ w,
+    const int32_t* __restrict__ seg, int B, int S, int Hi, int Di, int row0, int nrows,
+    OutT* __restrict__ scores, int64_t ld) {
+  extern __shared__ float smem[];  // Hi*Di query values, then Hi weights
+  const int nkb = (S + 255) / 256;
+  const int r = blockIdx.x / nkb, kb = blockIdx.x % nkb, b = blockIdx.y;
+  const int t = row0 + r;
+  const int s = kb * 256 + threadIdx.x;
+  if (kb * 256 > t) return;  // whole block in the future (uniform)
+  float* qs = smem;
+  float* ws = smem + Hi * Di;
+  const InT* qrow = q_idx + ((size_t)b * S + t) * Hi * Di;
+  for (int i = threadIdx.x; i < Hi * Di; i += 256) qs[i] = Elem<InT>::load(qrow + i);
+  for (int i = threadIdx.x; i < Hi; i += 256) ws[i] = Elem<InT>::load(w + ((size_t)b * S + t) * Hi + i);
+  __syncthreads();
+  if (s > t) return;
+  if (seg && seg[(size_t)b * S + s] != seg[(size_t)b * S + t]) return;
+  const InT* krow = k_idx + ((size_t)b * S + s) * Di;
+  float part = 0.f;
+  for (int j = 0; j < Hi; ++j) {
+    float dot = 0.f;
+    for (int d = 0; d < Di; ++d) dot = fmaf(qs[j * Di + d], Elem<InT>::load(krow + d), dot);
+    part = fmaf(ws[j], fmaxf(dot, 0.f), part);
+  }
+  Elem<OutT>::store(scores + ((size_t)b * nrows + r) * ld + s, part);
+}
+
+template <int HB, int KS>
+static hipError_t launch_mfma_t(const void* q_idx, const void* k_idx, const void* w,
+                                const int32_t* seg, int B, int S, int row0, int nrows,
+                                void* scores, bool out_bf16, int64_t ld, hipStream_t st) {
+  const int nrb = (nrows + 3) / 4;
+  dim3 grid((unsigned)(nrb * B)), block(256);
+  if (out_bf16)
+    hipLaunchKernelGGL((index_scores_mfma_kernel<HB, KS, uint16_t>), grid, block, 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w, seg, B,
+                       S, row0, nrows, (uint16_t*)scores, ld);
+  else
+    hipLaunchKernelGGL((index_scores_mfma_kernel<HB, KS, float>), grid, block, 0, st,
+                       (const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w, seg, B,
+                       S, row0, nrows, (float*)scores, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_index_scores_mfma(const void* q_idx, const void* k_idx, const void* w,
+                                    const int32_t* seg, int B, int S, int Hi, int Di, int row0,
+                                    int nrows, void* scores, bool out_bf16, int64_t ld,
+                                    hipStream_t st) {
+  if (Hi == 64 && Di == 128)
+    return launch_mfma_t<2, 8>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+  if (Hi == 32 && Di == 128)
+    return launch_mfma_t<1, 8>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+  if (Hi == 64 && Di == 64)
+    return launch_mfma_t<2, 4>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+  if (Hi == 32 && Di == 64)
+    return launch_mfma_t<1, 4>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const void* w,
+                                     const int32_t* seg, int B, int S, int Hi, int Di,
+                                     bool in_bf16, int row0, int nrows, void* scores,
+                                     bool out_bf16, int64_t ld, hipStream_t st) {
+  dim3 grid((unsigned)(((S + 255) / 256) * nrows), (unsigned)B), block(256);
+  const size_t shm = (size_t)(Hi * Di + Hi) * sizeof(float);
+#define DSA_IDX_PLAIN(IT, OT)                                                               \
+  hipLaunchKernelGGL((index_scores_plain_kernel<IT, OT>), grid, block, shm, st, (const IT*)q_idx, \
+                     (const IT*)k_idx, (const IT*)w, seg, B, S, Hi, Di, row0, nrows, (OT*)scores, ld)
+  if (in_bf16) {
+    if (out_bf16) DSA_IDX_PLAIN(uint16_t, uint16_t); else DSA_IDX_PLAIN(uint16_t, float);
+  } else {
+    if (out_bf16) DSA_IDX_PLAIN(float, uint16_t); else DSA_IDX_PLAIN(float, float);
+  }
+#undef DSA_IDX_PLAIN
+  return hipGetLastError();
+}
+
+}  // namespace dsa

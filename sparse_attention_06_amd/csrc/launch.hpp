@@ -1,0 +1,53 @@
+// Internal launchers of the DSA kernels. The public ABI (dsa.h) validates its
+// arguments on the host and then calls these; each returns the launch's
+// hipError_t (hipSuccess when nothing had to be launched).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// scores: in_bf16 selects bf16 vs fp32 inputs, out_bf16 the score storage.
+hipError_t launch_index_scores_mfma(const void* q_idx, const void* k_idx, const void* w,
+                                    const int32_t* seg, int B, int S, int Hi, int Di, int row0,
+                                    int nrows, void* scores, bool out_bf16, int64_t ld,
+                                    hipStream_t st);
+hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const void* w,
+                                     const int32_t* seg, int B, int S, int Hi, int Di,
+                                     bool in_bf16, int row0, int nrows, void* scores,
+                                     bool out_bf16, int64_t ld, hipStream_t st);
+
+hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
+                       int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
+                       hipStream_t st);
+hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int K,
+                             uint64_t* bits, hipStream_t st);
+hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int qt0, int qt1,
+                               uint8_t* cls, hipStream_t st);
+
+hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, const uint64_t* bits,
+                                const uint8_t* cls, int B, int S, int H, float scale, void* o,
+                                float* lse, hipStream_t st);
+hipError_t launch_attn_fwd_plain(const void* q, const void* k, const void* v, const uint64_t* bits,
+                                 int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
+                                 void* o, float* lse, hipStream_t st);
+
+hipError_t launch_bwd_rowdot(const void* o, const void* dout, int B, int S, int H, int Dv,
+                             bool bf16, float* D, hipStream_t st);
+hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* D, const uint64_t* bits,
+                                const uint8_t* cls, int B, int S, int H, float scale, void* dq,
+                                void* dk, void* dv, hipStream_t st);
+hipError_t launch_attn_bwd_plain(const void* q, const void* k, const void* v, const void* dout,
+                                 const float* lse, const float* D, const uint64_t* bits, int B,
+                                 int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dq,
+                                 void* dk, void* dv, hipStream_t st);
+
+// layout helpers shared by the host side
+inline int mask_words(int S) { return (S + 63) / 64; }
+inline int n_qtiles(int S) { return (S + 127) / 128; }
+inline int n_ktiles(int S) { return (S + 63) / 64; }
+inline size_t bits_bytes(int B, int S) { return (size_t)B * S * mask_words(S) * 8; }
+
+}  // namespace dsa

@@ -1,0 +1,334 @@
+// Per-query top-k selection, selection bitmask and tile classes (gfx950).
+//
+// Source: "DeepSeek3.2: Onboard sparse attention", Background (the top-k is a
+// non-parametric choice of the keys each query attends to) and "What this PR
+// does", item 1 (top-k indices and an index mask); "Support Ring Attention
+// with DeepSeek DSA Sparse Indexer", Forward Flow (the index mask is
+// [batch, S, S], shared by all heads, tiled into partial-mask blocks).
+//
+// Selection rule: n = min(K, |valid(t)|) keys. Larger scores win. Among equal
+// scores the smaller key position wins, and -0 equals +0.
+//
+// One workgroup (4 waves) per query row:
+//   * |valid| <= K: every valid key is taken and the scores are never read.
+//   * otherwise the K-th largest key T is found exactly:
+//       1. min/max of the row's valid scores;
+//       2. a 2048-bin histogram that is linear in the score value. Bins are
+//          monotone in the value, so equal scores share a bin. Scores of a row
+//          are spread out, so few lanes collide on one LDS counter. The bin
+//          holding the K-th largest score is then a contiguous range of the
+//          order-preserving u32 keys [klo, khi];
+//       3. radix passes over (key - klo) >> shift with at most 2048 bins each,
+//          until the range is a single key T.
+//     Then c_gt = #{key > T} and c_eq = K - c_gt ties at T are taken,
+//     lowest positions first.
+//   * compaction walks the row in 64-key words, one word per wave step:
+//     ballot gives the word's selection bits (the bitmask word itself),
+//     and mbcnt over the ballots gives each selected lane its ascending slot
+//     in the index list. A first walk counts per wave; a second one writes.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsa {
+
+constexpr int kNB = 2048;  // histogram bins
+
+template <typename ST> struct ScoreLoad;
+template <> struct ScoreLoad<float> {
+  __device__ static __forceinline__ float get(const float* p, int s) { return p[s]; }
+};
+template <> struct ScoreLoad<uint16_t> {
+  __device__ static __forceinline__ float get(const uint16_t* p, int s) { return bf2f(p[s]); }
+};
+
+struct TopkShared {
+  uint32_t hist[kNB];
+  uint32_t red_u[8];
+  float red_f[8];
+  uint32_t found_bin, found_above;
+  uint32_t wave_gt[4], wave_eq[4];
+};
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, TopkShared& sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  x = wave_sum(x);
+  if (lane == 0) sh.red_u[wid] = x;
+  __syncthreads();
+  const uint32_t r = sh.red_u[0] + sh.red_u[1] + sh.red_u[2] + sh.red_u[3];
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ void block_minmax(float& mn, float& mx, TopkShared& sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) { sh.red_f[wid] = mn; sh.red_f[4 + wid] = mx; }
+  __syncthreads();
+  mn = fminf(fminf(sh.red_f[0], sh.red_f[1]), fminf(sh.red_f[2], sh.red_f[3]));
+  mx = fmaxf(fmaxf(sh.red_f[4], sh.red_f[5]), fmaxf(sh.red_f[6], sh.red_f[7]));
+  __syncthreads();
+}
+__device__ __forceinline__ void block_uminmax(uint32_t& mn, uint32_t& mx, TopkShared& sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if (lane == 0) { sh.red_u[wid] = mn; sh.red_u[4 + wid] = mx; }
+  __syncthreads();
+  mn = min(min(sh.red_u[0], sh.red_u[1]), min(sh.red_u[2], sh.red_u[3]));
+  mx = max(max(sh.red_u[4], sh.red_u[5]), max(sh.red_u[6], sh.red_u[7]));
+  __syncthreads();
+}
+
+// Given the histogram in sh.hist[0..kNB), find the largest bin b with
+// count(bins >= b) >= need. Writes b and count(bins > b) to sh. Needs
+// count(all bins) >= need >= 1.
+__device__ void find_bin(TopkShared& sh, uint32_t need) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // thread i owns bins [8i, 8i+8); scan in descending bin order: thread order
+  // reversed, so thread j = 255 - i covers the j-th chunk from the top
+  const int j = 255 - tid;
+  uint32_t c[8];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { c[i] = sh.hist[8 * tid + i]; tot += c[i]; }
+  // inclusive prefix over j (descending bins) within the wave: lanes ordered by j
+  // j = 255 - tid, so within a wave, lower j is higher lane. Use a suffix scan
+  // over lanes: incl = sum of tot over lanes >= this lane.
+  uint32_t incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(incl, o);
+    if (lane + o < 64) incl += y;
+  }
+  if (lane == 0) sh.red_u[wid] = incl;  // wave total
+  __syncthreads();
+  // waves with larger wid hold higher bins
+  uint32_t above_waves = 0;
+  for (int w2 = wid + 1; w2 < 4; ++w2) above_waves += sh.red_u[w2];
+  __syncthreads();
+  uint32_t running = above_waves + incl - tot;  // count of bins above this thread's chunk
+  (void)j;
+#pragma unroll
+  for (int i = 7; i >= 0; --i) {
+    if (running < need && running + c[i] >= need) {
+      sh.found_bin = 8 * tid + i;
+      sh.found_above = running;
+    }
+    running += c[i];
+  }
+  __syncthreads();
+}
+
+template <typename ST>
+__global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                   const int32_t* __restrict__ seg, int B, int S,
+                                                   int K, int row0, int nrows,
+                                                   int32_t* __restrict__ idx,
+                                                   uint64_t* __restrict__ bits) {
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.x % B;
+  const int r = nrows - 1 - (int)(blockIdx.x / B);  // longest rows first
+  const int t = row0 + r;
+  const int W = (S + 63) / 64;
+  const ST* row = scores + ((size_t)b * nrows + r) * ld;
+  const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
+  const int seg_t = seg ? segb[t] : 0;
+  const int L = t + 1;
+  const int nw = (L + 63) / 64;
+
+  auto is_valid = [&](int s) -> bool { return s < L && (!segb || segb[s] == seg_t); };
+
+  uint32_t n_valid = (uint32_t)L;
+  if (segb) {
+    uint32_t c = 0;
+    for (int s = tid; s < L; s += 256) c += (segb[s] == seg_t);
+    n_valid = block_sum(c, sh);
+  }
+  const bool take_all = n_valid <= (uint32_t)K;
+  uint32_t T = 0, c_eq = 0;
+  if (!take_all) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int s = tid; s < L; s += 256)
+      if (is_valid(s)) {
+        const float v = ScoreLoad<ST>::get(row, s);
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+    block_minmax(mn, mx, sh);
+    uint32_t need = (uint32_t)K;
+    uint32_t klo, khi;
+    if (!(mx > mn)) {
+      klo = khi = fkey(mx);
+    } else {
+      const float inv = (float)kNB / (mx - mn);
+      for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
+      __syncthreads();
+      for (int s = tid; s < L; s += 256)
+        if (is_valid(s)) {
+          const float v = ScoreLoad<ST>::get(row, s);
+          const int bin = (int)fminf(fmaxf((v - mn) * inv, 0.f), (float)(kNB - 1));
+          atomicAdd(&sh.hist[bin], 1u);
+        }
+      __syncthreads();
+      find_bin(sh, need);
+      const int bstar = (int)sh.found_bin;
+      need -= sh.found_above;
+      klo = 0xffffffffu;
+      khi = 0u;
+      for (int s = tid; s < L; s += 256)
+        if (is_valid(s)) {
+          const float v = ScoreLoad<ST>::get(row, s);
+          const int bin = (int)fminf(fmaxf((v - mn) * inv, 0.f), (float)(kNB - 1));
+          if (bin == bstar) {
+            const uint32_t kk = fkey(v);
+            klo = min(klo, kk);
+            khi = max(khi, kk);
+          }
+        }
+      block_uminmax(klo, khi, sh);
+    }
+    // radix refinement on the key interval [klo, khi]
+    while (klo != khi) {
+      const uint32_t span = khi - klo;
+      const int nbits = 32 - __clz(span);
+      const int shift = nbits > 11 ? nbits - 11 : 0;
+      for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
+      __syncthreads();
+      for (int s = tid; s < L; s += 256)
+        if (is_valid(s)) {
+          const uint32_t kk = fkey(ScoreLoad<ST>::get(row, s));
+          if (kk >= klo && kk <= khi) atomicAdd(&sh.hist[(kk - klo) >> shift], 1u);
+        }
+      __syncthreads();
+      find_bin(sh, need);
+      need -= sh.found_above;
+      const uint32_t nlo = klo + (sh.found_bin << shift);
+      const uint32_t nhi = shift == 0 ? nlo : min(khi, nlo + ((1u << shift) - 1u));
+      klo = nlo;
+      khi = nhi;
+    }
+    T = klo;
+    c_eq = need;
+  }
+
+  // ---- compaction: ascending index list and bitmask words
+  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
+  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
+  const int wpw = (nw + 3) / 4;
+  const int wa = wid * wpw, wb = min(nw, wa + wpw);
+  auto classify = [&](int s, bool& gt, bool& eq) {
+    const bool v = is_valid(s);
+    if (take_all) {
+      gt = v;
+      eq = false;
+    } else {
+      const uint32_t kk = v ? fkey(ScoreLoad<ST>::get(row, s)) : 0u;
+      gt = v && kk > T;
+      eq = v && kk == T;
+    }
+  };
+  uint32_t my_gt = 0, my_eq = 0;
+  for (int w = wa; w < wb; ++w) {
+    bool gt, eq;
+    classify(64 * w + lane, gt, eq);
+    my_gt += __popcll(__ballot(gt));
+    my_eq += __popcll(__ballot(eq));
+  }
+  if (lane == 0) { sh.wave_gt[wid] = my_gt; sh.wave_eq[wid] = my_eq; }
+  __syncthreads();
+  uint32_t eq_before = 0, sel_before = 0;
+  for (int w2 = 0; w2 < wid; ++w2) {
+    const uint32_t take_eq = eq_before >= c_eq ? 0u : min(sh.wave_eq[w2], c_eq - eq_before);
+    sel_before += sh.wave_gt[w2] + take_eq;
+    eq_before += sh.wave_eq[w2];
+  }
+  for (int w = wa; w < wb; ++w) {
+    const int s = 64 * w + lane;
+    bool gt, eq;
+    classify(s, gt, eq);
+    const uint64_t eqm = __ballot(eq);
+    const uint32_t eq_rank = eq_before + lanes_below(eqm);
+    const bool sel = gt || (eq && eq_rank < c_eq);
+    const uint64_t selm = __ballot(sel);
+    const uint32_t pos = sel_before + lanes_below(selm);
+    if (sel && pos < (uint32_t)K) idx_row[pos] = s;
+    if (lane == 0) bits_row[w] = selm;
+    eq_before += __popcll(eqm);
+    sel_before += __popcll(selm);
+  }
+  for (int w = nw + tid; w < W; w += 256) bits_row[w] = 0ull;
+  const int n = take_all ? (int)n_valid : K;
+  for (int i = n + tid; i < K; i += 256) idx_row[i] = -1;
+}
+
+// Bits of caller-given index lists: one workgroup per row, the row's words
+// assembled in LDS with atomic ORs, then written out whole.
+__global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ seg, int B,
+                                                         int S, int K, uint64_t* __restrict__ bits) {
+  extern __shared__ unsigned long long words[];
+  const int W = (S + 63) / 64;
+  const int b = blockIdx.x % B, t = blockIdx.x / B;
+  for (int w = threadIdx.x; w < W; w += 256) words[w] = 0ull;
+  __syncthreads();
+  const int32_t* row = idx + ((size_t)b * S + t) * K;
+  const int seg_t = seg ? seg[(size_t)b * S + t] : 0;
+  for (int i = threadIdx.x; i < K; i += 256) {
+    const int s = row[i];
+    if (s >= 0 && s <= t && (!seg || seg[(size_t)b * S + s] == seg_t))
+      atomicOr(&words[s >> 6], 1ull << (s & 63));
+  }
+  __syncthreads();
+  uint64_t* out = bits + ((size_t)b * S + t) * W;
+  for (int w = threadIdx.x; w < W; w += 256) out[w] = words[w];
+}
+
+// Tile classes of query tiles [qt0, qt1): thread per key tile (one mask word).
+__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int B,
+                                                         int S, int qt0, uint8_t* __restrict__ cls) {
+  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int kt = blockIdx.x * 256 + threadIdx.x;
+  const int qt = qt0 + blockIdx.y, b = blockIdx.z;
+  if (kt >= NK) return;
+  const int t0 = qt * 128, t1 = min(S, t0 + 128);
+  uint64_t o = 0ull, a = ~0ull;
+  for (int t = t0; t < t1; ++t) {
+    const uint64_t w = bits[((size_t)b * S + t) * W + kt];
+    o |= w;
+    a &= w;
+  }
+  const bool keys_in_range = (kt + 1) * 64 <= S;
+  cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
+}
+
+hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
+                       int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
+                       hipStream_t st) {
+  dim3 grid((unsigned)((size_t)nrows * B)), block(256);
+  if (score_bf16)
+    hipLaunchKernelGGL(topk_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)scores, ld, seg,
+                       B, S, K, row0, nrows, idx, bits);
+  else
+    hipLaunchKernelGGL(topk_kernel<float>, grid, block, 0, st, (const float*)scores, ld, seg, B, S,
+                       K, row0, nrows, idx, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int K,
+                             uint64_t* bits, hipStream_t st) {
+  const size_t shm = (size_t)mask_words(S) * 8;
+  hipLaunchKernelGGL(build_bits_kernel, dim3((unsigned)((size_t)B * S)), dim3(256), shm, st, idx,
+                     seg, B, S, K, bits);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int qt0, int qt1, uint8_t* cls,
+                               hipStream_t st) {
+  if (qt1 <= qt0) return hipSuccess;
+  dim3 grid((unsigned)((n_ktiles(S) + 255) / 256), (unsigned)(qt1 - qt0), (unsigned)B);
+  hipLaunchKernelGGL(tile_class_kernel, grid, dim3(256), 0, st, bits, B, S, qt0, cls);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

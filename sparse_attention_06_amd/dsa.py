@@ -1,0 +1,153 @@
+"""ctypes binding of libdsa.so (declared in include/dsa.h).
+
+Argument marshalling only. Each function passes tensor data pointers, sizes
+and torch's current HIP stream to the C entry point of the same name, and
+raises DSAError on a non-OK status. Every step of the computation runs in the
+library's HIP kernels, so a missing library is an error: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+DSA_BF16, DSA_FP32 = 0, 1
+TILE_Q, TILE_K = 128, 64
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
+          4: "DSA_ERR_HIP"}
+
+EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
+           "dsa_sparse_attn_bwd", "dsa_mask_bytes", "dsa_bwd_workspace_bytes",
+           "dsa_status_string", "dsa_last_error", "dsa_version")
+
+
+class DSAError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str):
+        super().__init__(f"{fn}: {STATUS.get(code, code)}: {detail}")
+        self.code = code
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdsa.so once. Raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_06_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.dsa_index_scores.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32, i64, vp]
+        L.dsa_topk.argtypes = [vp, i32, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.dsa_build_mask.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+        L.dsa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
+        L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                          vp, vp, vp, vp, sz, vp]
+        for f in ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
+                  "dsa_sparse_attn_bwd"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dsa_mask_bytes.argtypes = [i32, i32]
+        L.dsa_mask_bytes.restype = sz
+        L.dsa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.dsa_bwd_workspace_bytes.restype = sz
+        L.dsa_status_string.argtypes = [i32]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_last_error.argtypes = []
+        L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_version.argtypes = []
+        L.dsa_version.restype = ctypes.c_int
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise DSAError(fn, code, lib().dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdsa must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ sizes
+def dsa_mask_bytes(B: int, S: int) -> int:
+    return int(lib().dsa_mask_bytes(B, S))
+
+
+def dsa_bwd_workspace_bytes(B: int, S: int, H: int, Dqk: int, Dv: int) -> int:
+    return int(lib().dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv))
+
+
+def mask_views(mask: torch.Tensor, B: int, S: int):
+    """(sel_bits int64 [B,S,W], tile_cls uint8 [B,NQ,NK]) views of a mask buffer."""
+    W = (S + 63) // 64
+    nq, nk = (S + TILE_Q - 1) // TILE_Q, (S + TILE_K - 1) // TILE_K
+    nb = B * S * W * 8
+    bits = mask[:nb].view(torch.int64).view(B, S, W)
+    cls = mask[nb:nb + B * nq * nk].view(B, nq, nk)
+    return bits, cls
+
+
+# ------------------------------------------------------------------ calls
+def dsa_index_scores(q_idx, k_idx, w, seg, row0: int, nrows: int, scores, stream=None) -> None:
+    B, S, Hi, Di = q_idx.shape
+    ld = scores.shape[-1]
+    _check("dsa_index_scores", lib().dsa_index_scores(
+        _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(seg), B, S, Hi, Di, _dt(q_idx), row0, nrows,
+        _ptr(scores), _dt(scores), ld, _stream(stream)))
+
+
+def dsa_topk(scores, seg, B: int, S: int, K: int, row0: int, nrows: int, idx, mask, stream=None) -> None:
+    ld = scores.shape[-1]
+    _check("dsa_topk", lib().dsa_topk(
+        _ptr(scores), _dt(scores), ld, _ptr(seg), B, S, K, row0, nrows, _ptr(idx), _ptr(mask),
+        _stream(stream)))
+
+
+def dsa_build_mask(idx, seg, mask, stream=None) -> None:
+    B, S, K = idx.shape
+    _check("dsa_build_mask", lib().dsa_build_mask(_ptr(idx), _ptr(seg), B, S, K, _ptr(mask),
+                                                  _stream(stream)))
+
+
+def dsa_sparse_attn_fwd(q, k, v, mask, softmax_scale: float, o, lse, stream=None) -> None:
+    B, S, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    _check("dsa_sparse_attn_fwd", lib().dsa_sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(mask), B, S, H, Dqk, Dv, float(softmax_scale), _dt(q),
+        _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, dk, dv, workspace,
+                        stream=None) -> None:
+    B, S, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    _check("dsa_sparse_attn_bwd", lib().dsa_sparse_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
+        float(softmax_scale), _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))

@@ -1,0 +1,271 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Sizes here are ones the oracle finishes in seconds, spanning several tiles
+and a ragged tail. The full-size workloads are in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (check_close, compare_topk_rows, f64)
+from oracle import dsa_oracle as ref
+from sparse_attention_06_amd import dsa, inputs
+from sparse_attention_06_amd.pipeline import DSAPath
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def _cfg(**kw):
+    base = inputs.CONFIGS["c2"].replace(B=2, S=333, H=3, K=64, backward=True)
+    return base.replace(**kw)
+
+
+def _seg_np(x):
+    return None if x["seg"] is None else x["seg"].cpu().numpy()
+
+
+def _seg_dev(x):
+    return None if x["seg"] is None else x["seg"].to(DEV).contiguous()
+
+
+def _make(cfg, device=DEV):
+    x = inputs.make(cfg, device="cpu")
+    return x, {k: (None if v is None else v.to(device).contiguous()) for k, v in x.items()}
+
+
+# ------------------------------------------------------------------ indexer
+@pytest.mark.parametrize("segments", [None, (40, 150)])
+@pytest.mark.parametrize("score_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("HiDi", [(64, 128), (32, 64)])
+def test_indexer_mfma_parity(segments, score_dtype, HiDi):
+    Hi, Di = HiDi
+    cfg = _cfg(Hi=Hi, Di=Di, segments=segments)
+    x, d = _make(cfg)
+    S = cfg.S
+    sc = torch.full((cfg.B, S, S), float("nan"), dtype=score_dtype, device=DEV)
+    dsa.dsa_index_scores(d["q_idx"], d["k_idx"], d["w"], _seg_dev(x), 0, S, sc)
+    torch.cuda.synchronize()
+    rows = np.arange(S)
+    want = ref.index_scores(f64(x["q_idx"]), f64(x["k_idx"]), f64(x["w"]), _seg_np(x), rows)
+    got = f64(sc)
+    fin = np.isfinite(want)
+    assert np.all(np.isfinite(got[fin]))
+    rowmax = np.abs(np.where(fin, want, 0)).max(axis=-1, keepdims=True)
+    err = np.abs(np.where(fin, got - want, 0))
+    if score_dtype == torch.float32:
+        assert np.all(err <= 1e-5 * rowmax + 1e-7), err.max()
+    else:
+        # one bf16 rounding of the float32 score: within one bf16 ulp of the exact value
+        ulp = np.ldexp(1.0, np.frexp(np.abs(np.where(fin, want, 1.0)))[1] - 8)
+        assert np.all(err <= ulp + 1e-6 * rowmax), err.max()
+
+
+@pytest.mark.parametrize("dtype,Hi,Di", [("fp32", 4, 32), ("bf16", 48, 40), ("fp32", 64, 128)])
+def test_indexer_plain_parity(dtype, Hi, Di):
+    cfg = _cfg(Hi=Hi, Di=Di, dtype=dtype, scaled=dtype == "bf16", S=200)
+    x, d = _make(cfg)
+    S = cfg.S
+    sc = torch.zeros((cfg.B, S, S), dtype=torch.float32, device=DEV)
+    dsa.dsa_index_scores(d["q_idx"], d["k_idx"], d["w"], None, 0, S, sc)
+    torch.cuda.synchronize()
+    want = ref.index_scores(f64(x["q_idx"]), f64(x["k_idx"]), f64(x["w"]), None, np.arange(S))
+    fin = np.isfinite(want)
+    rowmax = np.abs(np.where(fin, want, 0)).max(axis=-1, keepdims=True)
+    err = np.abs(np.where(fin, f64(sc) - want, 0))
+    assert np.all(err <= 1e-5 * rowmax + 1e-6), err.max()
+
+
+def test_indexer_slabs_match_whole_call():
+    cfg = _cfg(segments=(30, 120))
+    x, d = _make(cfg)
+    S = cfg.S
+    whole = torch.zeros((cfg.B, S, S), device=DEV)
+    dsa.dsa_index_scores(d["q_idx"], d["k_idx"], d["w"], _seg_dev(x), 0, S, whole)
+    buf = torch.zeros(cfg.B * 128 * S, device=DEV)
+    valid = torch.from_numpy(np.stack([np.stack([ref.valid_row(_seg_np(x)[b], S, t) for t in range(S)])
+                                       for b in range(cfg.B)])).to(DEV)
+    for row0 in range(0, S, 128):
+        n = min(128, S - row0)
+        part = buf[: cfg.B * n * S].view(cfg.B, n, S)      # [B, nrows, ld] for this slab
+        dsa.dsa_index_scores(d["q_idx"], d["k_idx"], d["w"], _seg_dev(x), row0, n, part)
+        v = valid[:, row0:row0 + n]
+        assert torch.equal(part[v], whole[:, row0:row0 + n][v])
+
+
+# ------------------------------------------------------------------ top-k
+def _mask_ref(idx_np, S):
+    M = ref.selection_matrix(idx_np, S)
+    return ref.pack_bits(M).view(np.int64), ref.tile_classes(M, 128, 64)
+
+
+@pytest.mark.parametrize("S,K,segments,score_dtype", [
+    (700, 64, None, torch.float32), (700, 64, (50, 300), torch.float32),
+    (300, 512, None, torch.float32), (513, 1, None, torch.float32),
+    (700, 100, None, torch.bfloat16), (1000, 200, (64, 500), torch.bfloat16)])
+def test_topk_exact_on_gpu_scores(S, K, segments, score_dtype):
+    """Given identical keys the selection is unique: GPU == oracle bit for bit."""
+    cfg = _cfg(S=S, K=K, segments=segments)
+    x, d = _make(cfg)
+    B = cfg.B
+    sc = torch.zeros((B, S, S), dtype=score_dtype, device=DEV)
+    idx = torch.empty((B, S, K), dtype=torch.int32, device=DEV)
+    mask = torch.empty(dsa.dsa_mask_bytes(B, S), dtype=torch.uint8, device=DEV)
+    dsa.dsa_index_scores(d["q_idx"], d["k_idx"], d["w"], _seg_dev(x), 0, S, sc)
+    dsa.dsa_topk(sc, _seg_dev(x), B, S, K, 0, S, idx, mask)
+    torch.cuda.synchronize()
+    keys = f64(sc)
+    want = ref.topk(keys, _seg_np(x), np.arange(S), K, S)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    bits, cls = dsa.mask_views(mask, B, S)
+    wb, wc = _mask_ref(want, S)
+    assert np.array_equal(bits.cpu().numpy(), wb)
+    assert np.array_equal(cls.cpu().numpy(), wc)
+
+
+def test_topk_ties_and_signed_zeros():
+    """Crafted scores with heavy ties, -0/+0, and slab calls."""
+    B, S, K = 2, 640, 37
+    g = torch.Generator().manual_seed(5)
+    vals = (torch.randint(-4, 5, (B, S, S), generator=g).float() * 0.25)
+    vals[torch.rand((B, S, S), generator=g) < 0.05] = -0.0
+    vals[:, 200:300] = 0.0                         # whole rows of zeros
+    sc = vals.to(DEV)
+    idx = torch.full((B, S, K), -7, dtype=torch.int32, device=DEV)
+    mask = torch.zeros(dsa.dsa_mask_bytes(B, S), dtype=torch.uint8, device=DEV)
+    for row0 in range(0, S, 256):
+        n = min(256, S - row0)
+        dsa.dsa_topk(sc[:, row0:row0 + n].contiguous(), None, B, S, K, row0, n, idx, mask)
+    torch.cuda.synchronize()
+    want = ref.topk(vals.double().numpy(), None, np.arange(S), K, S)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    bits, cls = dsa.mask_views(mask, B, S)
+    wb, wc = _mask_ref(want, S)
+    assert np.array_equal(bits.cpu().numpy(), wb)
+    assert np.array_equal(cls.cpu().numpy(), wc)
+
+
+@pytest.mark.parametrize("segments", [None, (40, 200)])
+def test_topk_vs_oracle_scores(segments):
+    """End to end selection against the oracle's own scores and sets."""
+    cfg = _cfg(S=600, K=128, segments=segments)
+    x, d = _make(cfg)
+    S, B, K = cfg.S, cfg.B, cfg.K
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, K, cfg.H, cfg.Dqk, cfg.Dv)
+    path.select(d["q_idx"], d["k_idx"], d["w"], _seg_dev(x))
+    torch.cuda.synchronize()
+    rows = np.arange(S)
+    rs = ref.index_scores(f64(x["q_idx"]), f64(x["k_idx"]), f64(x["w"]), _seg_np(x), rows)
+    ri = ref.topk(rs, _seg_np(x), rows, K, S)
+    dec = compare_topk_rows(rs, f64(path.scores), path.idx.cpu().numpy(), ri, _seg_np(x), rows, S, K)
+    assert len(dec) >= 0.9 * B * S
+
+
+# --------------------------------------------------------------- attention
+def _sets(cfg, x):
+    return inputs.random_index_sets(cfg.B, cfg.S, cfg.K, _seg_np(x), seed=cfg.seed + 1)
+
+
+@pytest.mark.parametrize("S,K,segments", [(333, 64, None), (333, 64, (40, 150)), (200, 256, None),
+                                          (130, 1, None)])
+def test_build_mask_and_attention_fwd_mfma(S, K, segments):
+    cfg = _cfg(S=S, K=K, segments=segments)
+    x, d = _make(cfg)
+    B = cfg.B
+    sets = _sets(cfg, x)
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, K, cfg.H, cfg.Dqk, cfg.Dv)
+    path.build_mask(torch.from_numpy(sets).to(DEV), _seg_dev(x))
+    path.forward(d["q"], d["k"], d["v"], cfg.softmax_scale)
+    torch.cuda.synchronize()
+    bits, cls = dsa.mask_views(path.mask, B, S)
+    wb, wc = _mask_ref(sets, S)
+    assert np.array_equal(bits.cpu().numpy(), wb)
+    assert np.array_equal(cls.cpu().numpy(), wc)
+    O, L = ref.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), sets, _seg_np(x), cfg.softmax_scale,
+                             np.arange(S))
+    check_close("O", f64(path.o), O, bf16=True)
+    np.testing.assert_allclose(path.lse.cpu().numpy(), L, rtol=0, atol=1e-4)
+
+
+@pytest.mark.parametrize("dtype,Dqk,Dv", [("fp32", 64, 64), ("bf16", 64, 64), ("bf16", 128, 96)])
+def test_attention_fwd_plain(dtype, Dqk, Dv):
+    cfg = _cfg(S=200, K=32, Dqk=Dqk, Dv=Dv, dtype=dtype, scaled=dtype == "bf16", segments=(30, 90))
+    x, d = _make(cfg)
+    B, S = cfg.B, cfg.S
+    sets = _sets(cfg, x)
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, cfg.K, cfg.H, Dqk, Dv, dtype=cfg.torch_dtype())
+    path.build_mask(torch.from_numpy(sets).to(DEV), _seg_dev(x))
+    path.forward(d["q"], d["k"], d["v"], cfg.softmax_scale)
+    torch.cuda.synchronize()
+    O, L = ref.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), sets, _seg_np(x), cfg.softmax_scale,
+                             np.arange(S))
+    check_close("O", f64(path.o), O, bf16=dtype == "bf16")
+    np.testing.assert_allclose(path.lse.cpu().numpy(), L, rtol=0, atol=1e-4)
+
+
+def test_attention_negative_control():
+    """A single flipped index per row in the oracle's sets must fail the check."""
+    cfg = _cfg(S=256, K=16, H=2)
+    x, d = _make(cfg)
+    B, S = cfg.B, cfg.S
+    sets = _sets(cfg, x)
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, cfg.K, cfg.H, cfg.Dqk, cfg.Dv)
+    path.build_mask(torch.from_numpy(sets).to(DEV), None)
+    path.forward(d["q"], d["k"], d["v"], cfg.softmax_scale)
+    torch.cuda.synchronize()
+    bad = sets.copy()
+    rows = np.arange(100, S)
+    for b in range(B):
+        for t in rows:
+            kept = bad[b, t][bad[b, t] >= 0]
+            free = np.setdiff1d(np.arange(t + 1), kept)
+            bad[b, t, 0] = free[0]
+            bad[b, t] = np.sort(bad[b, t])
+    O_bad, _ = ref.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), bad[:, rows], None,
+                                 cfg.softmax_scale, rows)
+    with pytest.raises(AssertionError):
+        check_close("O", f64(path.o)[:, rows], O_bad, bf16=True)
+
+
+@pytest.mark.parametrize("S,K,segments,dtype,dims", [
+    (333, 64, None, "bf16", (192, 128)), (333, 48, (40, 150), "bf16", (192, 128)),
+    (150, 256, None, "bf16", (192, 128)), (200, 32, (30, 90), "fp32", (64, 64)),
+    (200, 32, None, "bf16", (64, 64))])
+def test_attention_bwd(S, K, segments, dtype, dims):
+    Dqk, Dv = dims
+    cfg = _cfg(S=S, K=K, segments=segments, dtype=dtype, scaled=dtype == "bf16", Dqk=Dqk, Dv=Dv, H=2)
+    x, d = _make(cfg)
+    B = cfg.B
+    sets = _sets(cfg, x)
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, K, cfg.H, Dqk, Dv, dtype=cfg.torch_dtype(), backward=True)
+    path.build_mask(torch.from_numpy(sets).to(DEV), _seg_dev(x))
+    path.forward(d["q"], d["k"], d["v"], cfg.softmax_scale)
+    path.backward(d["q"], d["k"], d["v"], d["dout"], cfg.softmax_scale)
+    torch.cuda.synchronize()
+    dq, dk, dv = ref.attention_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"]), sets,
+                                   _seg_np(x), cfg.softmax_scale)
+    bf = dtype == "bf16"
+    check_close("dq", f64(path.dq), dq, bf16=bf, rel=2e-2)
+    check_close("dk", f64(path.dk), dk, bf16=bf, rel=2e-2)
+    check_close("dv", f64(path.dv), dv, bf16=bf, rel=2e-2)
+
+
+def test_end_to_end_tiny_fp32():
+    """The 128-token fp32 workload: indexer, top-k and forward against the oracle."""
+    cfg = inputs.CONFIGS["c1"]
+    x, d = _make(cfg)
+    B, S, K = cfg.B, cfg.S, cfg.K
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, K, cfg.H, cfg.Dqk, cfg.Dv, dtype=torch.float32)
+    path.step(d, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    rows = np.arange(S)
+    rs = ref.index_scores(f64(x["q_idx"]), f64(x["k_idx"]), f64(x["w"]), None, rows)
+    ri = ref.topk(rs, None, rows, K, S)
+    dec = compare_topk_rows(rs, f64(path.scores), path.idx.cpu().numpy(), ri, None, rows, S, K)
+    assert len(dec) >= 0.9 * S
+    O, L = ref.attention_fwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), ri, None, cfg.softmax_scale, rows)
+    rr = np.array([r for _, r in dec])
+    check_close("O", f64(path.o)[:, rr], O[:, rr], bf16=False)
+    np.testing.assert_allclose(path.lse.cpu().numpy()[:, :, rr], L[:, :, rr], rtol=0, atol=1e-5)
