@@ -1,0 +1,231 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--no-cpu]
+
+One step is the whole path over one batch of seeded synthetic input: indexer
+scores -> top-k (index lists, mask bits, tile classes) -> sparse attention
+forward -> backward (dQ, then dK/dV). Inputs are resident in HBM before the
+timed region. Default workload: the 2B-model training shape (batch 12,
+seq 4096, 16 heads of 192/128, indexer 64 x 128, top-k 2048, bf16).
+
+Prints one JSON line. `value` is useful TFLOP/s of the whole step:
+indexer pairs x Hi x 2 Di, plus selected pairs x H x 6 (Dqk + Dv) for
+forward + backward. `indexer_topk_ms` is the selection half of the metric.
+Per-kernel times come from HIP events recorded on the launch stream around
+each C-ABI call (each is one kernel, except dsa_topk, which is the top-k
+kernel plus the small tile-class kernel).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DSA fwd+bwd useful TFLOP/s and indexer+top-k ms at S=4K/32K/128K, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def valid_counts(cfg, seg_np):
+    """|valid(t)| per (b, t): causal with the diagonal, same segment."""
+    B, S = cfg.B, cfg.S
+    if seg_np is None:
+        return np.broadcast_to(np.arange(1, S + 1, dtype=np.int64), (B, S))
+    out = np.empty((B, S), np.int64)
+    for b in range(B):
+        row = seg_np[b]
+        starts = np.r_[0, np.nonzero(np.diff(row))[0] + 1]
+        start_of = np.repeat(starts, np.diff(np.r_[starts, S]))
+        out[b] = np.arange(S) - start_of + 1
+    return out
+
+
+def work(cfg, seg_np):
+    nv = valid_counts(cfg, seg_np)
+    sel = np.minimum(nv, cfg.K)
+    pairs, selected = int(nv.sum()), int(sel.sum())
+    sb = 2 if cfg.score_dtype == "bf16" else 4
+    W = (cfg.S + 63) // 64
+    topk_bytes = int(nv[nv > cfg.K].sum()) * sb + cfg.B * cfg.S * cfg.K * 4 + cfg.B * cfg.S * W * 8
+    return {
+        "pairs": pairs, "selected": selected,
+        "indexer": pairs * cfg.Hi * 2 * cfg.Di,
+        "fwd": selected * cfg.H * 2 * (cfg.Dqk + cfg.Dv),
+        "bwd": selected * cfg.H * 4 * (cfg.Dqk + cfg.Dv),
+        "bwd_dq": selected * cfg.H * 2 * cfg.Dqk,
+        "topk_bytes": topk_bytes,
+    }
+
+
+def cpu_baseline(cfg, x_cpu, budget_s=15.0, max_rows=4096):
+    """The float64 oracle on a bounded row sample of the same workload."""
+    from oracle import dsa_oracle as ref
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    f64 = lambda t: t.float().double().numpy()  # noqa: E731
+    q_idx, k_idx, w = f64(x_cpu["q_idx"]), f64(x_cpu["k_idx"]), f64(x_cpu["w"])
+    q, k, v = f64(x_cpu["q"]), f64(x_cpu["k"]), f64(x_cpu["v"])
+    dout = f64(x_cpu["dout"]) if cfg.backward else None
+    seg = None if x_cpu["seg"] is None else x_cpu["seg"].numpy()
+    rng = np.random.default_rng(1234)
+    rows_all = rng.permutation(cfg.S)[:max_rows]
+    flops, done = 0, 0
+    t0 = time.perf_counter()
+    for t in rows_all:
+        rows = np.array([t])
+        sc = ref.index_scores(q_idx[:1], k_idx[:1], w[:1], None if seg is None else seg[:1], rows)
+        idx = ref.topk(sc, None if seg is None else seg[:1], rows, cfg.K, cfg.S)
+        ref.attention_fwd(q[:1], k[:1], v[:1], idx, None if seg is None else seg[:1], cfg.softmax_scale, rows)
+        if cfg.backward:
+            ref.attention_bwd(q[:1], k[:1], v[:1], dout[:1], idx, None if seg is None else seg[:1],
+                              cfg.softmax_scale, rows=rows)
+        nv = int(np.isfinite(sc).sum())
+        n = int((idx >= 0).sum())
+        flops += nv * cfg.Hi * 2 * cfg.Di + n * cfg.H * (6 if cfg.backward else 2) * (cfg.Dqk + cfg.Dv)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} random query rows of batch row 0 (indexer, top-k, forward"
+                      f"{', backward' if cfg.backward else ''}), {dt:.1f} s, float64 numpy",
+            "seconds": dt, "rows": done}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_06_amd import dsa, inputs
+    from sparse_attention_06_amd.pipeline import DSAPath
+
+    cfg = inputs.CONFIGS[args.config]
+    dsa.lib()
+    dev = "cuda"
+    log(f"config {cfg.name}: generating inputs on the GPU")
+    x = inputs.make(cfg, device=dev)
+    seg_np = None if x["seg"] is None else x["seg"].cpu().numpy()
+    sdt = torch.bfloat16 if cfg.score_dtype == "bf16" else torch.float32
+    path = DSAPath(cfg.B, cfg.S, cfg.Hi, cfg.Di, cfg.K, cfg.H, cfg.Dqk, cfg.Dv, dtype=cfg.torch_dtype(),
+                   score_dtype=sdt, backward=cfg.backward, device=dev)
+    scale = cfg.softmax_scale
+    seg = x["seg"]
+    stream = torch.cuda.current_stream()
+
+    calls = ["index_scores", "topk", "attn_fwd"] + (["attn_bwd_dq", "attn_bwd_dkdv"] if cfg.backward else [])
+
+    def step(evs=None):
+        def mark(i):
+            if evs is not None:
+                evs[i].record(stream)
+        mark(0)
+        dsa.dsa_index_scores(x["q_idx"], x["k_idx"], x["w"], seg, 0, cfg.S, path.scores)
+        mark(1)
+        dsa.dsa_topk(path.scores, seg, cfg.B, cfg.S, cfg.K, 0, cfg.S, path.idx, path.mask)
+        mark(2)
+        dsa.dsa_sparse_attn_fwd(x["q"], x["k"], x["v"], path.mask, scale, path.o, path.lse)
+        mark(3)
+        if cfg.backward:
+            dsa.dsa_sparse_attn_bwd_dq(x["q"], x["k"], x["v"], path.o, x["dout"], path.lse, path.mask, scale,
+                                       path.dq, path.ws)
+            mark(4)
+            dsa.dsa_sparse_attn_bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], path.lse, path.mask, scale,
+                                         path.dk, path.dv, path.ws)
+            mark(5)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / args.steps
+    per = {c: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
+           for j, c in enumerate(calls)}
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{c} {v:.3f}" for c, v in per.items()))
+
+    wk = work(cfg, seg_np)
+    useful = wk["indexer"] + wk["fwd"] + (wk["bwd"] if cfg.backward else 0)
+    value = useful / (ms * 1e-3) / 1e12
+    kern = {
+        "index_scores": ("mfma", wk["indexer"]),
+        "topk": ("hbm", wk["topk_bytes"]),
+        "attn_fwd": ("mfma", wk["fwd"]),
+        "attn_bwd_dq": ("mfma", wk["bwd_dq"]),
+        "attn_bwd_dkdv": ("mfma", wk["bwd"]),
+    }
+    kernels = {}
+    for c in calls:
+        bound, amount = kern[c]
+        t = per[c] * 1e-3
+        if bound == "mfma":
+            ach = amount / t / 1e12
+            kernels[c] = {"ms": per[c], "bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
+                          "frac": ach / PEAK_BF16_TFLOPS, "algorithmic": amount}
+        else:
+            ach = amount / t / 1e9
+            kernels[c] = {"ms": per[c], "bound": "hbm", "achieved": ach, "unit": "GB/s",
+                          "frac": ach / PEAK_HBM_GBS, "algorithmic": amount}
+    dom = max(calls, key=lambda c: per[c])
+    kd = kernels[dom]
+    roofline = {"bound": kd["bound"], "achieved": kd["achieved"],
+                "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS, "unit": kd["unit"],
+                "frac": kd["frac"], "traffic": None, "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the float64 oracle on a row sample (cpu baseline)")
+        x_cpu = {k: (None if v is None else v.cpu()) for k, v in x.items()}
+        cpu = cpu_baseline(cfg, x_cpu)
+        log(f"cpu baseline: {cpu['value']:.3e} TFLOP/s over {cpu['rows']} rows")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "fp32", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "S": cfg.S, "index_heads": cfg.Hi, "index_dim": cfg.Di,
+                   "topk": cfg.K, "heads": cfg.H, "dqk": cfg.Dqk, "dv": cfg.Dv, "score_dtype": cfg.score_dtype,
+                   "segments": cfg.segments is not None, "passes": "+".join(calls)},
+        "indexer_topk_ms": per["index_scores"] + per["topk"],
+        "attention_useful_tflops": (wk["fwd"] + (wk["bwd"] if cfg.backward else 0)) /
+                                   (sum(per[c] for c in calls if c.startswith("attn")) * 1e-3) / 1e12,
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -171,20 +171,39 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
 /* ---------------------------------------------------------------------------
  * dsa_sparse_attn_bwd -- gradients of sum(O * dout) w.r.t. q, k, v.
  * Source: "Support Ring Attention with DeepSeek DSA Sparse Indexer", Backward
- * Flow (dQ = dP K, dK = dP^T Q, dV = P^T dO, each on the kept entries).
+ * Flow (dQ = dP K, dK = dP^T Q, dV = P^T dO, each on the kept entries; dK/dV
+ * run key-major).
  *   q, k, v, o, dout  as in the forward (o and lse from dsa_sparse_attn_fwd)
  *   lse       [B,H,S] float32
  *   mask      the forward's mask
  *   dq, dk    [B,S,H,Dqk] dtype out;  dv [B,S,H,Dv] dtype out
- *   workspace device scratch of at least dsa_bwd_workspace_bytes() bytes
- *             (holds D = rowsum(dout * o) as float32 [B,H,S]).
- * Deterministic: no atomics; dK/dV run key-major and dQ query-major.
+ *   workspace device scratch of at least dsa_bwd_workspace_bytes() bytes; it
+ *             receives D = rowsum(dout * o) as float32 [B,H,S].
+ * Same as dsa_sparse_attn_bwd_dq followed by dsa_sparse_attn_bwd_dkdv on the
+ * same stream. Deterministic: no atomics.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                                const void* dout, const float* lse, const void* mask,
                                int B, int S, int H, int Dqk, int Dv, float softmax_scale,
                                dsa_dtype dtype, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two halves of dsa_sparse_attn_bwd, one kernel each, for callers that
+ * schedule them separately (say dK/dV on another stream after an event):
+ *   _dq    query-major. Computes D into the workspace, then dq.
+ *   _dkdv  key-major. Reads D from the workspace, so it must be ordered after
+ *          _dq on the same workspace. Writes dk and dv.
+ * Arguments as in dsa_sparse_attn_bwd. */
+dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, const void* mask,
+                                  int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                                  dsa_dtype dtype, void* dq, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v,
+                                    const void* dout, const float* lse, const void* mask,
+                                    int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                                    dsa_dtype dtype, void* dk, void* dv, const void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv);
 

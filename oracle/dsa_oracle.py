@@ -243,11 +243,12 @@ def attention_fwd(q, k, v, idx, seg, scale: float, rows):
 # ----------------------------------------------------------------------------
 # a5-a7: backward                                                  [P2b]
 # ----------------------------------------------------------------------------
-def attention_bwd(q, k, v, dout, idx, seg, scale: float):
-    """Gradients of sum(O * dout) w.r.t. q, k, v for all rows, in float64.
+def attention_bwd(q, k, v, dout, idx, seg, scale: float, rows=None):
+    """Gradients of sum(O * dout) w.r.t. q, k, v, in float64.
 
-    idx [B, S, K] holds every row's index list. Returns dq, dk, dv in the
-    shapes of q, k, v.
+    idx [B, S, K] holds every row's index list. With ``rows`` given, idx is
+    [B, len(rows), K] for those rows, and only their terms are summed (a row
+    sample of the same sums). Returns dq, dk, dv in the shapes of q, k, v.
 
     Per kept pair (t, s) and head h:
       P = softmax over kept s of scale * q_t . k_s
@@ -263,13 +264,15 @@ def attention_bwd(q, k, v, dout, idx, seg, scale: float):
     v = np.asarray(v, dtype=np.float64)
     dout = np.asarray(dout, dtype=np.float64)
     B, S, H, _ = q.shape
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for b in range(B):
         seg_b = None if seg is None else np.asarray(seg)[b]
-        for t in range(S):
-            ks = _kept(idx[b, t], seg_b, S, t)
+        for r, t in enumerate(rows):
+            t = int(t)
+            ks = _kept(idx[b, r], seg_b, S, t)
             if ks.size == 0:
                 continue
             for h in range(H):

@@ -193,39 +193,83 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
                     "dsa_sparse_attn_fwd");
 }
 
+static dsa_status check_bwd_common(const void* q, const void* k, const void* v, const void* dout,
+                                   const float* lse, const void* mask, int B, int S, int H, int Dqk,
+                                   int Dv, float scale, dsa_dtype dtype, const void* workspace,
+                                   size_t workspace_bytes) {
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(v);
+  REQ_PTR(dout);
+  REQ_PTR(lse);
+  REQ_PTR(mask);
+  REQ_PTR(workspace);
+  dsa_status s = check_attn(B, S, H, Dqk, Dv, scale, dtype);
+  if (s != DSA_OK) return s;
+  const size_t need = dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv);
+  REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
+  return DSA_OK;
+}
+
+dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, const void* mask, int B, int S,
+                                  int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype,
+                                  void* dq, void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
+                                  workspace, workspace_bytes);
+  if (s != DSA_OK) return s;
+  REQ_PTR(o);
+  REQ_PTR(dq);
+  hipStream_t st = (hipStream_t)stream;
+  void* m = const_cast<void*>(mask);
+  float* D = (float*)workspace;
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_bwd_dq_mfma(q, k, v, o, dout, lse, D, bits_of(m), cls_of(m, B, S),
+                                                   B, S, H, softmax_scale, dq, st),
+                      "dsa_sparse_attn_bwd_dq");
+  return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, o, dout, lse, D, bits_of(m), B, S, H, Dqk, Dv,
+                                                  softmax_scale, dtype == DSA_BF16, dq, st),
+                    "dsa_sparse_attn_bwd_dq");
+}
+
+dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                                    const float* lse, const void* mask, int B, int S, int H, int Dqk,
+                                    int Dv, float softmax_scale, dsa_dtype dtype, void* dk, void* dv,
+                                    const void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
+                                  workspace, workspace_bytes);
+  if (s != DSA_OK) return s;
+  REQ_PTR(dk);
+  REQ_PTR(dv);
+  hipStream_t st = (hipStream_t)stream;
+  void* m = const_cast<void*>(mask);
+  const float* D = (const float*)workspace;
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, lse, D, bits_of(m), cls_of(m, B, S),
+                                                     B, S, H, softmax_scale, dk, dv, st),
+                      "dsa_sparse_attn_bwd_dkdv");
+  return hip_status(dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, D, bits_of(m), B, S, H, Dqk, Dv,
+                                                    softmax_scale, dtype == DSA_BF16, dk, dv, st),
+                    "dsa_sparse_attn_bwd_dkdv");
+}
+
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                                const void* dout, const float* lse, const void* mask, int B, int S,
                                int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype,
                                void* dq, void* dk, void* dv, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  REQ_PTR(q);
-  REQ_PTR(k);
-  REQ_PTR(v);
+  dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
+                                  workspace, workspace_bytes);
+  if (s != DSA_OK) return s;
   REQ_PTR(o);
-  REQ_PTR(dout);
-  REQ_PTR(lse);
-  REQ_PTR(mask);
   REQ_PTR(dq);
   REQ_PTR(dk);
   REQ_PTR(dv);
-  REQ_PTR(workspace);
-  dsa_status s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
+  s = dsa_sparse_attn_bwd_dq(q, k, v, o, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dq,
+                             workspace, workspace_bytes, stream);
   if (s != DSA_OK) return s;
-  const size_t need = dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv);
-  REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
-  hipStream_t st = (hipStream_t)stream;
-  void* m = const_cast<void*>(mask);
-  float* D = (float*)workspace;
-  const bool bf16 = dtype == DSA_BF16;
-  hipError_t e = dsa::launch_bwd_rowdot(o, dout, B, S, H, Dv, bf16, D, st);
-  if (e != hipSuccess) return hip_status(e, "dsa_sparse_attn_bwd rowdot");
-  if (attn_mfma(Dqk, Dv, dtype))
-    return hip_status(dsa::launch_attn_bwd_mfma(q, k, v, dout, lse, D, bits_of(m), cls_of(m, B, S), B,
-                                                S, H, softmax_scale, dq, dk, dv, st),
-                      "dsa_sparse_attn_bwd");
-  return hip_status(dsa::launch_attn_bwd_plain(q, k, v, dout, lse, D, bits_of(m), B, S, H, Dqk, Dv,
-                                               softmax_scale, bf16, dq, dk, dv, st),
-                    "dsa_sparse_attn_bwd");
+  return dsa_sparse_attn_bwd_dkdv(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dk,
+                                  dv, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

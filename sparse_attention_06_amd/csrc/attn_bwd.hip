@@ -4,7 +4,8 @@
 // Flow: the forward runs query-major while dK/dV run key-major. Each uses the
 // same index mask, dQ = dP K, dK = dP^T Q and dV = P^T dO.
 //
-//   D(t)   = sum_e dO(t,e) O(t,e)                       (rowdot kernel)
+//   D(t)   = sum_e dO(t,e) O(t,e)       (computed by the query-major kernel,
+//                                         which runs first and stores it)
 //   P      = exp(scale q.k - LSE(t)) on kept (t, s)
 //   dP     = dO(t) . v(s),   dS = P (dP - D(t))
 //   dV(s) += P dO(t),        dK(s) += scale dS q(t)      (key-major kernel)
@@ -30,23 +31,6 @@ constexpr int KROW = DQK * 2 + 16;
 constexpr int VROW = DV * 2 + 16;
 constexpr int KTROW = TK * 2 + 16;     // K^T rows (64 keys)
 }  // namespace bwd
-
-template <typename T>
-__global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                     int B, int S, int H, int Dv, float* __restrict__ D) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const size_t row = (size_t)blockIdx.x * 4 + wid;  // (b, t, h)
-  if (row >= (size_t)B * S * H) return;
-  float acc = 0.f;
-  for (int e = lane; e < Dv; e += 64) acc = fmaf(Elem<T>::load(o + row * Dv + e), Elem<T>::load(dout + row * Dv + e), acc);
-  acc = wave_sumf(acc);
-  if (lane == 0) {
-    const int h = (int)(row % H);
-    const int t = (int)((row / H) % S);
-    const int b = (int)(row / ((size_t)H * S));
-    D[((size_t)b * H + h) * S + t] = acc;
-  }
-}
 
 // transpose-store 8 bf16 values (one 16-byte chunk of row `qi`, columns
 // c0..c0+7) into a [col][query] LDS array with row pitch `pitch` bytes.
@@ -234,9 +218,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ D,
-    const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
-    float scale, float scale_log2, uint16_t* __restrict__ dq) {
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+    float* __restrict__ D, const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B,
+    int S, int H, float scale, float scale_log2, uint16_t* __restrict__ dq) {
   using namespace bwd;
   __shared__ __attribute__((aligned(16))) unsigned char smK[TK * KROW];
   __shared__ __attribute__((aligned(16))) unsigned char smKT[DQK * KTROW];
@@ -266,7 +250,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     of[ks] = z;
   }
   const float Lq = qvalid ? lse[((size_t)b * H + h) * S + tq] * 1.4426950408889634f : INFINITY;
-  const float Dq = qvalid ? D[((size_t)b * H + h) * S + tq] : 0.f;
+  // D(t) = dO(t) . O(t): this lane holds half of dO(t) as MFMA fragments; the
+  // matching half of O(t) is read here and the halves are summed across lanes
+  float Dq = 0.f;
+  if (qvalid) {
+    const uint16_t* orow = o + ((size_t)b * S + tq) * rs_v + (size_t)h * DV;
+#pragma unroll
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      const u32x4 ov = *(const u32x4*)(orow + ks * 16 + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wo = ov[e >> 1], wd = of[ks][e >> 1];
+        const uint16_t xo = (e & 1) ? (uint16_t)(wo >> 16) : (uint16_t)(wo & 0xffffu);
+        const uint16_t xd = (e & 1) ? (uint16_t)(wd >> 16) : (uint16_t)(wd & 0xffffu);
+        Dq = fmaf(bf2f(xo), bf2f(xd), Dq);
+      }
+    }
+  }
+  Dq += __shfl_xor(Dq, 32);
+  if (qvalid && half == 0) D[((size_t)b * H + h) * S + tq] = Dq;
   f32x16 dqacc[DQK / 32];
 #pragma unroll
   for (int i = 0; i < DQK / 32; ++i)
@@ -373,9 +375,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ D, const uint64_t* __restrict__ bits, int B,
-    int S, int H, int Dqk, int Dv, float scale, T* __restrict__ dq) {
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
+    const T* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ D,
+    const uint64_t* __restrict__ bits, int B, int S, int H, int Dqk, int Dv, float scale,
+    T* __restrict__ dq) {
   __shared__ float qs[4][256], os[4][256], dss[4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const size_t row = (size_t)blockIdx.x * 4 + wid;
@@ -388,7 +391,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
   for (int d = lane; d < Dv; d += 64) os[wid][d] = Elem<T>::load(dout + row * Dv + d);
   __builtin_amdgcn_wave_barrier();
   const float L = lse[((size_t)b * H + h) * S + t];
-  const float Dt = D[((size_t)b * H + h) * S + t];
+  float Dt = 0.f;
+  for (int e = lane; e < Dv; e += 64) Dt = fmaf(Elem<T>::load(o + row * Dv + e), os[wid][e], Dt);
+  Dt = wave_sumf(Dt);
+  if (lane == 0) D[((size_t)b * H + h) * S + t] = Dt;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const uint64_t* brow = bits + ((size_t)b * S + t) * W;
   for (int w = 0; w <= t / 64; ++w) {
@@ -478,55 +484,57 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_plain_kernel(
   }
 }
 
-hipError_t launch_bwd_rowdot(const void* o, const void* dout, int B, int S, int H, int Dv, bool bf16,
-                             float* D, hipStream_t st) {
-  const size_t nblk = ((size_t)B * S * H + 3) / 4;
-  if (bf16)
-    hipLaunchKernelGGL(rowdot_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
-                       (const uint16_t*)o, (const uint16_t*)dout, B, S, H, Dv, D);
-  else
-    hipLaunchKernelGGL(rowdot_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st, (const float*)o,
-                       (const float*)dout, B, S, H, Dv, D);
+hipError_t launch_attn_bwd_dq_mfma(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, float* D, const uint64_t* bits,
+                                   const uint8_t* cls, int B, int S, int H, float scale, void* dq,
+                                   hipStream_t st) {
+  const size_t nq = (size_t)n_qtiles(S) * B * H;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(256), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse,
+                     D, bits, cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dq);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* D, const uint64_t* bits,
-                                const uint8_t* cls, int B, int S, int H, float scale, void* dq,
-                                void* dk, void* dv, hipStream_t st) {
-  const float sl2 = scale * 1.4426950408889634f;
+hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout,
+                                     const float* lse, const float* D, const uint64_t* bits,
+                                     const uint8_t* cls, int B, int S, int H, float scale, void* dk,
+                                     void* dv, hipStream_t st) {
   const size_t nkv = (size_t)((S + 127) / 128) * B * H;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, D, bits, cls, B,
-                     S, H, scale, sl2, (uint16_t*)dk, (uint16_t*)dv);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t nq = (size_t)n_qtiles(S) * B * H;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(256), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, D, bits, cls, B,
-                     S, H, scale, sl2, (uint16_t*)dq);
+                     S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_plain(const void* q, const void* k, const void* v, const void* dout,
-                                 const float* lse, const float* D, const uint64_t* bits, int B,
-                                 int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dq,
-                                 void* dk, void* dv, hipStream_t st) {
+hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dout, const float* lse, float* D, const uint64_t* bits,
+                                    int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
+                                    void* dq, hipStream_t st) {
   const size_t nblk = ((size_t)B * S * H + 3) / 4;
-#define DSA_BWD_PLAIN(T)                                                                             \
-  hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<T>, dim3((unsigned)nblk), dim3(256), 0, st, (const T*)q, \
-                     (const T*)k, (const T*)v, (const T*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale,   \
-                     (T*)dq);                                                                        \
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;                                 \
-  hipLaunchKernelGGL(attn_bwd_dkdv_plain_kernel<T>, dim3((unsigned)nblk), dim3(256), 0, st,           \
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)dout, lse, D, bits, B, S, H, Dqk, \
-                     Dv, scale, (T*)dk, (T*)dv)
-  if (bf16) {
-    DSA_BWD_PLAIN(uint16_t);
-  } else {
-    DSA_BWD_PLAIN(float);
-  }
-#undef DSA_BWD_PLAIN
+  if (bf16)
+    hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                       (const uint16_t*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale, (uint16_t*)dq);
+  else
+    hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
+                       (const float*)q, (const float*)k, (const float*)v, (const float*)o,
+                       (const float*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale, (float*)dq);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* v, const void* dout,
+                                      const float* lse, const float* D, const uint64_t* bits, int B,
+                                      int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dk,
+                                      void* dv, hipStream_t st) {
+  const size_t nblk = ((size_t)B * S * H + 3) / 4;
+  if (bf16)
+    hipLaunchKernelGGL(attn_bwd_dkdv_plain_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
+                       lse, D, bits, B, S, H, Dqk, Dv, scale, (uint16_t*)dk, (uint16_t*)dv);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkdv_plain_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
+                       (const float*)q, (const float*)k, (const float*)v, (const float*)dout, lse, D,
+                       bits, B, S, H, Dqk, Dv, scale, (float*)dk, (float*)dv);
   return hipGetLastError();
 }
 

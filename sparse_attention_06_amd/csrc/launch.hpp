@@ -33,16 +33,24 @@ hipError_t launch_attn_fwd_plain(const void* q, const void* k, const void* v, co
                                  int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
                                  void* o, float* lse, hipStream_t st);
 
-hipError_t launch_bwd_rowdot(const void* o, const void* dout, int B, int S, int H, int Dv,
-                             bool bf16, float* D, hipStream_t st);
-hipError_t launch_attn_bwd_mfma(const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* D, const uint64_t* bits,
-                                const uint8_t* cls, int B, int S, int H, float scale, void* dq,
-                                void* dk, void* dv, hipStream_t st);
-hipError_t launch_attn_bwd_plain(const void* q, const void* k, const void* v, const void* dout,
-                                 const float* lse, const float* D, const uint64_t* bits, int B,
-                                 int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dq,
-                                 void* dk, void* dv, hipStream_t st);
+// backward, query-major: writes D = rowsum(dout * o) [B,H,S] and dq
+hipError_t launch_attn_bwd_dq_mfma(const void* q, const void* k, const void* v, const void* o,
+                                   const void* dout, const float* lse, float* D, const uint64_t* bits,
+                                   const uint8_t* cls, int B, int S, int H, float scale, void* dq,
+                                   hipStream_t st);
+hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dout, const float* lse, float* D, const uint64_t* bits,
+                                    int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
+                                    void* dq, hipStream_t st);
+// backward, key-major: reads D, writes dk and dv
+hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout,
+                                     const float* lse, const float* D, const uint64_t* bits,
+                                     const uint8_t* cls, int B, int S, int H, float scale, void* dk,
+                                     void* dv, hipStream_t st);
+hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* v, const void* dout,
+                                      const float* lse, const float* D, const uint64_t* bits, int B,
+                                      int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dk,
+                                      void* dv, hipStream_t st);
 
 // layout helpers shared by the host side
 inline int mask_words(int S) { return (S + 63) / 64; }
