@@ -15,9 +15,12 @@
 //   in-lane, with one exchange between lane halves. Q stays in VGPRs.
 //   O^T += V^T P^T: the probabilities go straight from the S^T accumulator
 //   into the B operand. The key order inside each 16-wide k step is permuted
-//   to match the accumulator layout, and V^T is read from LDS with the same
-//   permutation.
-// exp2 with the scale folded in (scale * log2 e).
+//   to match the accumulator layout. V^T comes from the natural V tile in LDS
+//   through the gfx950 transposing LDS read, with the same permutation.
+// K/V tiles are double buffered in LDS. The next non-empty tile's global loads
+// are issued before the current tile is computed. exp2 is the hardware
+// v_exp_f32, with the scale folded in (scale * log2 e). O is rescaled only when
+// a running max moves.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,9 +28,11 @@ namespace dsa {
 
 namespace fwd {
 constexpr int DQK = 192, DV = 128, TK = 64;
-constexpr int KS = DQK / 16;         // k steps of S^T
-constexpr int KROW = DQK * 2 + 16;   // bytes per K row in LDS (padded)
-constexpr int VTROW = TK * 2 + 16;   // bytes per V^T row (64 keys) in LDS (padded)
+constexpr int KS = DQK / 16;   // k steps of S^T
+constexpr int KP = DQK + 8;    // LDS pitch (elements) of a K row: 400 B, conflict-free b128 reads
+constexpr int VP = DV + 8;     // LDS pitch of a V row: 272 B
+constexpr int KCH = TK * DQK / 8 / 256;  // 16-byte chunks per thread per K tile (6)
+constexpr int VCH = TK * DV / 8 / 256;   // ... per V tile (4)
 }  // namespace fwd
 
 __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
@@ -35,8 +40,10 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
     float scale_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace fwd;
-  __shared__ __attribute__((aligned(16))) unsigned char smK[TK * KROW];
-  __shared__ __attribute__((aligned(16))) unsigned char smVT[DV * VTROW];
+  // double-buffered natural-layout K and V tiles; V^T fragments come from
+  // ds_read_b64_tr_b16 on the V tile, so no transposed copy is stored
+  __shared__ __attribute__((aligned(16))) uint16_t smK[2][TK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t smV[2][TK * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -47,6 +54,8 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
   const int tq = qt * 128 + wid * 32 + col;  // this lane's query
   const bool qvalid = tq < S;
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;  // token strides
+  const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
+  const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
 
   u32x4 qf[KS];
 #pragma unroll
@@ -66,112 +75,125 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
   const int kt_last = min(S - 1, qt * 128 + 127) / TK;
   const uint8_t* cls_row = cls + ((size_t)b * NQ + qt) * NK;
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
+  auto next_tile = [&](int kt) {
+    int n = kt + 1;
+    while (n <= kt_last && cls_row[n] == 0) ++n;
+    return n;
+  };
 
-  for (int kt = 0; kt <= kt_last; ++kt) {
-    const int c = cls_row[kt];
-    if (c == 0) continue;  // uniform over the workgroup
-    __syncthreads();       // previous tile's LDS reads are done
-    // K tile [64][192] -> LDS rows
+  u32x4 pk[KCH], pv[VCH];
+  auto gload = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int ci = tid + i * 256;
-      const int row = ci / 24, cc = ci % 24;
-      const int s = kt * TK + row;
+    for (int i = 0; i < KCH; ++i) {
+      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24, s = kt * TK + row;
       u32x4 z = {0u, 0u, 0u, 0u};
-      if (s < S) z = *(const u32x4*)(k + ((size_t)b * S + s) * rs_qk + (size_t)h * DQK + cc * 8);
-      *(u32x4*)(smK + row * KROW + cc * 16) = z;
+      if (s < S) z = *(const u32x4*)(kbase + (size_t)s * rs_qk + cc * 8);
+      pk[i] = z;
     }
-    // V tile [64][128] -> LDS transposed V^T[e][key], two keys per 32-bit store
-    {
-      const int kp = tid & 31, ec = tid >> 5;  // keys 2kp, 2kp+1; e = 16 ec .. 16 ec + 15
-      const int s0 = kt * TK + 2 * kp;
-      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = a0, b0 = a0, b1 = a0;
-      if (s0 < S) {
-        const uint16_t* p = v + ((size_t)b * S + s0) * rs_v + (size_t)h * DV + ec * 16;
-        a0 = *(const u32x4*)p;
-        a1 = *(const u32x4*)(p + 8);
-      }
-      if (s0 + 1 < S) {
-        const uint16_t* p = v + ((size_t)b * S + s0 + 1) * rs_v + (size_t)h * DV + ec * 16;
-        b0 = *(const u32x4*)p;
-        b1 = *(const u32x4*)(p + 8);
-      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const uint32_t wa = e < 8 ? a0[(e & 7) >> 1] : a1[(e & 7) >> 1];
-        const uint32_t wb = e < 8 ? b0[(e & 7) >> 1] : b1[(e & 7) >> 1];
-        const uint32_t lo = (e & 1) ? (wa >> 16) : (wa & 0xffffu);
-        const uint32_t hi = (e & 1) ? (wb >> 16) : (wb & 0xffffu);
-        *(uint32_t*)(smVT + (ec * 16 + e) * VTROW + kp * 4) = lo | (hi << 16);
-      }
+    for (int i = 0; i < VCH; ++i) {
+      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16, s = kt * TK + row;
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (s < S) z = *(const u32x4*)(vbase + (size_t)s * rs_v + cc * 8);
+      pv[i] = z;
     }
-    __syncthreads();
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24;
+      *(u32x4*)(&smK[buf][row * KP + cc * 8]) = pk[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16;
+      *(u32x4*)(&smV[buf][row * VP + cc * 8]) = pv[i];
+    }
+  };
+
+  int kt = next_tile(-1);
+  if (kt <= kt_last) gload(kt);
+  int buf = 0;
+  while (kt <= kt_last) {
+    const int c = cls_row[kt];
+    lstore(buf);
+    __syncthreads();  // tile kt visible; the other buffer is free (read two tiles ago)
+    const int kn = next_tile(kt);
+    if (kn <= kt_last) gload(kn);  // in flight while this tile is computed
 
     uint64_t mw = ~0ull;
+    bool work = true;
     if (c == 1) {
       mw = qvalid ? bits_q[kt] : 0ull;
-      if (__ballot(mw != 0ull) == 0ull) continue;  // no selected key for this wave
+      work = __ballot(mw != 0ull) != 0ull;  // some query of this wave keeps a key here
     }
-
-    f32x16 sacc[2];
+    if (work) {
+      const uint16_t* sK = smK[buf];
+      const uint16_t* sV = smV[buf];
+      f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 a = *(const u32x4*)(smK + (kb * 32 + col) * KROW + (ks * 16 + 8 * half) * 2);
-        sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
-      }
-
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb][r] * scale_log2;
-        if (c == 1 && !((mw >> (kb * 32 + acc_row(r, half))) & 1ull)) x = -INFINITY;
-        sacc[kb][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m - m_use);
-    m = m_new;
-    l *= alpha;
-#pragma unroll
-    for (int eb = 0; eb < 4; ++eb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
-
-    u32x4 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
-        float pv[8];
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) {
-          pv[c8] = exp2f(sacc[kb][8 * p2 + c8] - m_use);
-          l += pv[c8];
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 a = *(const u32x4*)(sK + (kb * 32 + col) * KP + ks * 16 + 8 * half);
+          sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
         }
-        pb[kb][p2] = u32x4{pack_bf2(pv[0], pv[1]), pack_bf2(pv[2], pv[3]), pack_bf2(pv[4], pv[5]),
-                           pack_bf2(pv[6], pv[7])};
-      }
+
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int eb = 0; eb < 4; ++eb)
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sacc[kb][r] * scale_log2;
+          if (c == 1 && !((mw >> (kb * 32 + acc_row(r, half))) & 1ull)) x = -INFINITY;
+          sacc[kb][r] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      if (__ballot(m_new != m)) {  // rescale only when some running max moved
+        const float alpha = fast_exp2(m - m_use);
+        l *= alpha;
+#pragma unroll
+        for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
+      }
+      m = m_new;
+
+      u32x4 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
-          const unsigned char* base = smVT + (eb * 32 + col) * VTROW + (kb * 32 + 16 * p2 + 4 * half) * 2;
-          const u32x2 lo = *(const u32x2*)base;
-          const u32x2 hi = *(const u32x2*)(base + 16);
-          oacc[eb] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kb][p2], oacc[eb]);
+          float pv8[8];
+#pragma unroll
+          for (int c8 = 0; c8 < 8; ++c8) {
+            pv8[c8] = fast_exp2(sacc[kb][8 * p2 + c8] - m_use);
+            l += pv8[c8];
+          }
+          pb[kb][p2] = u32x4{pack_bf2(pv8[0], pv8[1]), pack_bf2(pv8[2], pv8[3]), pack_bf2(pv8[4], pv8[5]),
+                             pack_bf2(pv8[6], pv8[7])};
         }
+      // O^T[e, q] += V^T[e, key] P^T[key, q]; V^T fragments read transposed from the V tile,
+      // keys permuted inside each 16-key step to match the S^T accumulator rows
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+          const int r0 = kb * 32 + 16 * p2 + 4 * half;
+#pragma unroll
+          for (int eb = 0; eb < 4; ++eb)
+            oacc[eb] = mfma32(lds_tr_frag(sV, VP, r0, r0 + 8, eb * 32), pb[kb][p2], oacc[eb]);
+        }
+    }
+    buf ^= 1;
+    kt = kn;
   }
 
   const float l_tot = l + __shfl_xor(l, 32);
@@ -183,9 +205,9 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int e = eb * 32 + 8 * g + 4 * half;
-        u32x2 pk = {pack_bf2(oacc[eb][4 * g] * inv, oacc[eb][4 * g + 1] * inv),
-                    pack_bf2(oacc[eb][4 * g + 2] * inv, oacc[eb][4 * g + 3] * inv)};
-        *(u32x2*)(orow + e) = pk;
+        u32x2 pk2 = {pack_bf2(oacc[eb][4 * g] * inv, oacc[eb][4 * g + 1] * inv),
+                     pack_bf2(oacc[eb][4 * g + 2] * inv, oacc[eb][4 * g + 3] * inv)};
+        *(u32x2*)(orow + e) = pk2;
       }
     if (half == 0)
       lse[((size_t)b * H + h) * S + tq] =

@@ -51,6 +51,27 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 // row of accumulator register r for lane-half h (h = lane / 32)
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
+// A-operand fragment of v_mfma_f32_32x32x16_bf16 read *transposed* from a
+// natural row-major LDS tile X[k][m] (m contiguous, `pitch` elements per row)
+// with ds_read_b64_tr_b16. Lane l receives A[m][k] = X[k][m] for
+// m = mbase + l%32 and the eight k rows {kr0..kr0+3, kr1..kr1+3}, where kr0/kr1
+// are this lane-half's rows (they may differ between halves). Within each
+// 16-lane group, the instruction hands lane i element (i%4) of the 4-element
+// chunk of source lane (i/4 + 4*slot). So source lane j points at row
+// kr + j/4, columns m0 + 4*(j%4) .. +3, and lane i gets column m0 + i.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+__device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* X, int pitch, int kr0, int kr1, int mbase) {
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int m0 = mbase + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(X + (kr0 + (j >> 2)) * pitch + m0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(X + (kr1 + (j >> 2)) * pitch + m0));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
