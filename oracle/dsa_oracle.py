@@ -72,6 +72,19 @@ def valid_row(seg_b, S: int, t: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # a1: indexer scores                                              [P3], [P3c]
 # ----------------------------------------------------------------------------
+def index_scores_row(q_t, w_t, k_b, valid) -> np.ndarray:
+    """Scores of one query over all keys: [S] float64, -inf outside ``valid``.
+
+    q_t [Hi, Di] (the query's index vectors), w_t [Hi], k_b [S, Di] (the batch
+    row's index keys), valid bool [S].
+    """
+    prod = np.asarray(q_t, np.float64) @ np.asarray(k_b, np.float64).T   # [Hi, S]: head j . key s
+    score = np.asarray(w_t, np.float64) @ np.maximum(prod, 0.0)          # sum_j w_j ReLU(.)
+    out = np.full(score.shape, NEG_INF)
+    out[valid] = score[valid]
+    return out
+
+
 def index_scores(q_idx, k_idx, w, seg, rows) -> np.ndarray:
     """Indexer scores for the given query rows, in float64.
 
@@ -89,11 +102,7 @@ def index_scores(q_idx, k_idx, w, seg, rows) -> np.ndarray:
     for b in range(B):
         seg_b = None if seg is None else np.asarray(seg)[b]
         for r, t in enumerate(rows):
-            # per index head j: the query-key product of head j with every key
-            prod = q_idx[b, t] @ k_idx[b].T                  # [Hi, S]
-            score = w[b, t] @ np.maximum(prod, 0.0)          # sum_j w_j ReLU(.)
-            ok = valid_row(seg_b, S, int(t))
-            out[b, r, ok] = score[ok]
+            out[b, r] = index_scores_row(q_idx[b, t], w[b, t], k_idx[b], valid_row(seg_b, S, int(t)))
     return out
 
 
@@ -208,6 +217,25 @@ def _kept(idx_row, seg_b, S: int, t: int) -> np.ndarray:
     return np.unique(sel[ok[sel]])
 
 
+def attention_fwd_row(q_t, k_sel, v_sel, scale: float):
+    """Softmax attention of one query over its kept keys, all heads.
+
+    q_t [H, Dqk]; k_sel [n, H, Dqk], v_sel [n, H, Dv] are the kept keys'
+    rows (n >= 1). Returns O [H, Dv] and LSE [H] (natural log).
+    """
+    H = q_t.shape[0]
+    O = np.zeros((H, v_sel.shape[-1]))
+    L = np.zeros(H)
+    for h in range(H):
+        logit = scale * (k_sel[:, h] @ q_t[h])       # [n]
+        m = logit.max()
+        e = np.exp(logit - m)
+        Z = e.sum()
+        O[h] = (e / Z) @ v_sel[:, h]
+        L[h] = m + np.log(Z)
+    return O, L
+
+
 def attention_fwd(q, k, v, idx, seg, scale: float, rows):
     """Masked softmax attention for the given query rows, in float64.
 
@@ -230,34 +258,47 @@ def attention_fwd(q, k, v, idx, seg, scale: float, rows):
             ks = _kept(idx[b, r], seg_b, S, int(t))
             if ks.size == 0:
                 continue
-            for h in range(H):
-                logit = scale * (k[b, ks, h] @ q[b, t, h])       # [n]
-                m = logit.max()
-                e = np.exp(logit - m)
-                Z = e.sum()
-                O[b, r, h] = (e / Z) @ v[b, ks, h]
-                L[b, h, r] = m + np.log(Z)
+            O[b, r], L[b, :, r] = attention_fwd_row(q[b, t], k[b, ks], v[b, ks], scale)
     return O, L
 
 
 # ----------------------------------------------------------------------------
 # a5-a7: backward                                                  [P2b]
 # ----------------------------------------------------------------------------
+def attention_bwd_row(q_t, k_sel, v_sel, dout_t, scale: float):
+    """One query row's terms of the backward, all heads.
+
+    q_t [H, Dqk], dout_t [H, Dv]; k_sel [n, H, Dqk], v_sel [n, H, Dv] are the
+    kept keys' rows. Returns dq_t [H, Dqk] and this row's contributions
+    dk_sel [n, H, Dqk], dv_sel [n, H, Dv] to the kept keys' gradients:
+      P = softmax over kept s of scale * q_t . k_s
+      D = sum_e dO(t,e) O(t,e),  dP(s) = dO(t) . v(s),  dS = P * (dP - D)
+      dq(t) = scale * sum_s dS k(s),  dk(s) += scale * dS q(t),  dv(s) += P dO(t)
+    """
+    H = q_t.shape[0]
+    dq_t = np.zeros_like(q_t)
+    dk_sel = np.zeros_like(k_sel)
+    dv_sel = np.zeros_like(v_sel)
+    for h in range(H):
+        logit = scale * (k_sel[:, h] @ q_t[h])
+        e = np.exp(logit - logit.max())
+        P = e / e.sum()                                  # [n]
+        O = P @ v_sel[:, h]                              # [Dv]
+        D = dout_t[h] @ O
+        dP = v_sel[:, h] @ dout_t[h]                     # [n]
+        dS = P * (dP - D)
+        dq_t[h] = scale * (dS @ k_sel[:, h])
+        dk_sel[:, h] = scale * np.outer(dS, q_t[h])
+        dv_sel[:, h] = np.outer(P, dout_t[h])
+    return dq_t, dk_sel, dv_sel
+
+
 def attention_bwd(q, k, v, dout, idx, seg, scale: float, rows=None):
     """Gradients of sum(O * dout) w.r.t. q, k, v, in float64.
 
     idx [B, S, K] holds every row's index list. With ``rows`` given, idx is
     [B, len(rows), K] for those rows, and only their terms are summed (a row
     sample of the same sums). Returns dq, dk, dv in the shapes of q, k, v.
-
-    Per kept pair (t, s) and head h:
-      P = softmax over kept s of scale * q_t . k_s
-      D(t) = sum_e dO(t,e) O(t,e)
-      dP(t,s) = dO(t) . v(s)
-      dS = P * (dP - D)
-      dq(t) = scale * sum_s dS k(s)
-      dk(s) = scale * sum_t dS q(t)
-      dv(s) = sum_t P dO(t)
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -275,17 +316,9 @@ def attention_bwd(q, k, v, dout, idx, seg, scale: float, rows=None):
             ks = _kept(idx[b, r], seg_b, S, t)
             if ks.size == 0:
                 continue
-            for h in range(H):
-                logit = scale * (k[b, ks, h] @ q[b, t, h])
-                e = np.exp(logit - logit.max())
-                P = e / e.sum()                                  # [n]
-                O = P @ v[b, ks, h]                              # [Dv]
-                D = dout[b, t, h] @ O
-                dP = v[b, ks, h] @ dout[b, t, h]                 # [n]
-                dS = P * (dP - D)
-                dq[b, t, h] = scale * (dS @ k[b, ks, h])
-                dk[b, ks, h] += scale * np.outer(dS, q[b, t, h])
-                dv[b, ks, h] += np.outer(P, dout[b, t, h])
+            dq[b, t], dk_sel, dv_sel = attention_bwd_row(q[b, t], k[b, ks], v[b, ks], dout[b, t], scale)
+            dk[b, ks] += dk_sel
+            dv[b, ks] += dv_sel
     return dq, dk, dv
 
 

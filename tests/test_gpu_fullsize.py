@@ -1,0 +1,214 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+Each workload runs once on the GPU (indexer over all rows, top-k, forward,
+and backward where the workload has one). The float64 oracle then checks a
+seeded sample of query rows: the first and last 8, the rows around t = K,
+and random ones. A row needs only its own index vectors, the batch row's index
+keys, and the K/V rows of its kept keys, so the oracle handles any S.
+Properties that hold at any size cover the rest: every index list and mask
+row agrees with the scores, and the key-gradient sum rules hold
+(sum_s dK(s) = 0, sum_s dV(s) = sum_t dO(t)).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import BF16_ATOL, BF16_REL, check_undecidable_row, row_decision
+from oracle import dsa_oracle as ref
+from sparse_attention_06_amd import dsa, inputs
+from sparse_attention_06_amd.pipeline import DSAPath
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def _rows(S, K, seed, n_rand=12):
+    rng = np.random.default_rng(seed)
+    r = set(range(8)) | set(range(S - 8, S)) | {K - 2, K - 1, K, K + 1}
+    r |= set(rng.integers(0, S, n_rand).tolist())
+    return np.array(sorted(t for t in r if 0 <= t < S))
+
+
+def _f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def _check_rel(name, got, want):
+    err = np.abs(got - want).max()
+    scale = np.abs(want).max()
+    assert err <= BF16_ATOL, f"{name}: max-abs {err:.3e}"
+    assert err <= BF16_REL * scale + 1e-5, f"{name}: max-abs {err:.3e} vs max|ref| {scale:.3e}"
+
+
+class Run:
+    """One full-size execution of the path and its host-side samples."""
+
+    def __init__(self, key, batches=(0,)):
+        cfg = inputs.CONFIGS[key]
+        self.cfg = cfg
+        self.x = inputs.make(cfg, device=DEV)
+        sdt = torch.bfloat16 if cfg.score_dtype == "bf16" else torch.float32
+        self.path = DSAPath(cfg.B, cfg.S, cfg.Hi, cfg.Di, cfg.K, cfg.H, cfg.Dqk, cfg.Dv, score_dtype=sdt,
+                            backward=cfg.backward, device=DEV)
+        self.path.step(self.x, cfg.softmax_scale, backward=cfg.backward)
+        torch.cuda.synchronize()
+        self.seg = None if self.x["seg"] is None else self.x["seg"].cpu().numpy()
+        self.batches = [b for b in batches if b < cfg.B]
+        self.rows = _rows(cfg.S, cfg.K, seed=7)
+        self._sample()
+
+    def _sample(self):
+        cfg, x, p = self.cfg, self.x, self.path
+        self.samples = []
+        for b in self.batches:
+            k_b = _f64(x["k_idx"][b])
+            seg_b = None if self.seg is None else self.seg[b]
+            for t in self.rows:
+                t = int(t)
+                valid = ref.valid_row(seg_b, cfg.S, t)
+                rs = ref.index_scores_row(_f64(x["q_idx"][b, t]), _f64(x["w"][b, t]), k_b, valid)
+                keys = ref.bf16_round(rs) if cfg.score_dtype == "bf16" else rs
+                sel = ref.topk_row(keys, valid, cfg.K)
+                want_idx = np.full(cfg.K, -1, np.int32)
+                want_idx[: sel.size] = sel
+                self.samples.append(dict(b=b, t=t, valid=valid, ref_scores=rs, keys=keys, want_idx=want_idx,
+                                         gpu_scores=_f64(p.scores[b, t]), gpu_idx=p.idx[b, t].cpu().numpy()))
+
+    def gather(self, b, sel, name):
+        return _f64(self.x[name][b, torch.from_numpy(sel).to(DEV)])
+
+
+CASES = {"c2": dict(batches=(0, 11)), "c4": dict(batches=(0, 3)), "c3": {}, "c5": {}}
+
+
+@pytest.mark.parametrize("key", list(CASES))
+def test_fullsize(key):
+    """One workload at full size: every check below on the same run."""
+    torch.cuda.empty_cache()
+    r = Run(key, **CASES[key])
+    check_scores_and_selection(r)
+    check_mask_matches_index_lists(r)
+    check_forward_rows(r)
+    if r.cfg.backward:
+        check_backward(r)
+        check_key_gradients_on_given_sets(r)
+    del r
+    torch.cuda.empty_cache()
+
+
+def check_scores_and_selection(r):
+    cfg = r.cfg
+    n_dec = 0
+    for sm in r.samples:
+        fin = sm["valid"]
+        err = np.abs(sm["gpu_scores"][fin] - sm["ref_scores"][fin])
+        rowmax = np.abs(sm["ref_scores"][fin]).max()
+        if cfg.score_dtype == "bf16":
+            ulp = np.ldexp(1.0, np.frexp(np.abs(sm["ref_scores"][fin]))[1] - 8)
+            assert np.all(err <= ulp + 1e-6 * rowmax), (sm["b"], sm["t"])
+        else:
+            assert np.all(err <= 1e-5 * rowmax + 1e-7), (sm["b"], sm["t"], err.max())
+        # selection on the GPU's own keys is unique: exact
+        own = ref.topk_row(sm["gpu_scores"], fin, cfg.K)
+        assert np.array_equal(sm["gpu_idx"][: own.size], own) and np.all(sm["gpu_idx"][own.size:] == -1)
+        dec, k_n, k_n1, tau = row_decision(sm["keys"], sm["gpu_scores"], fin, cfg.K)
+        if dec:
+            assert np.array_equal(sm["gpu_idx"], sm["want_idx"]), (sm["b"], sm["t"])
+            n_dec += 1
+        else:
+            check_undecidable_row(sm["keys"], fin, sm["gpu_idx"], cfg.K, k_n, k_n1, tau)
+    assert n_dec >= 0.75 * len(r.samples)
+
+
+def check_mask_matches_index_lists(r):
+    cfg = r.cfg
+    bits, cls = dsa.mask_views(r.path.mask, cfg.B, cfg.S)
+    W = bits.shape[-1]
+    for sm in r.samples:
+        row = bits[sm["b"], sm["t"]].cpu().numpy().view(np.uint64)
+        want = np.zeros(W, np.uint64)
+        kept = sm["gpu_idx"][sm["gpu_idx"] >= 0]
+        for s in kept:
+            want[s // 64] |= np.uint64(1) << np.uint64(s % 64)
+        assert np.array_equal(row, want), (sm["b"], sm["t"])
+    # tile classes of two query tiles recomputed from their mask rows
+    for qt in (0, (cfg.S - 1) // 128):
+        b = r.batches[0]
+        t0, t1 = qt * 128, min(cfg.S, qt * 128 + 128)
+        blk = bits[b, t0:t1].cpu().numpy().view(np.uint64)
+        o = np.bitwise_or.reduce(blk, axis=0)
+        a = np.bitwise_and.reduce(blk, axis=0)
+        in_range = (np.arange(W) + 1) * 64 <= cfg.S
+        want = np.where(o == 0, 0, np.where(in_range & (a == np.uint64(0xFFFFFFFFFFFFFFFF)), 2, 1))
+        assert np.array_equal(cls[b, qt].cpu().numpy(), want.astype(np.uint8))
+
+
+def check_forward_rows(r):
+    cfg = r.cfg
+    for sm in r.samples:
+        sel = sm["gpu_idx"][sm["gpu_idx"] >= 0].astype(np.int64)
+        # the GPU's own index list equals the oracle's on decidable rows (checked above);
+        # here the oracle attends over the oracle's list
+        want_sel = sm["want_idx"][sm["want_idx"] >= 0].astype(np.int64)
+        if not np.array_equal(sel, want_sel):
+            continue
+        b, t = sm["b"], sm["t"]
+        O, L = ref.attention_fwd_row(_f64(r.x["q"][b, t]), r.gather(b, want_sel, "k"), r.gather(b, want_sel, "v"),
+                                     cfg.softmax_scale)
+        _check_rel(f"O[{b},{t}]", _f64(r.path.o[b, t]), O)
+        np.testing.assert_allclose(r.path.lse[b, :, t].cpu().numpy(), L, rtol=0, atol=1e-4)
+
+
+def check_backward(r):
+    cfg = r.cfg
+    for sm in r.samples:
+        sel = sm["gpu_idx"][sm["gpu_idx"] >= 0].astype(np.int64)
+        want_sel = sm["want_idx"][sm["want_idx"] >= 0].astype(np.int64)
+        if not np.array_equal(sel, want_sel):
+            continue
+        b, t = sm["b"], sm["t"]
+        dq_t, _, _ = ref.attention_bwd_row(_f64(r.x["q"][b, t]), r.gather(b, want_sel, "k"),
+                                           r.gather(b, want_sel, "v"), _f64(r.x["dout"][b, t]), cfg.softmax_scale)
+        _check_rel(f"dq[{b},{t}]", _f64(r.path.dq[b, t]), dq_t)
+    # key-gradient sum rules over every key: every row keeps at least one key
+    dk = r.path.dk.float().sum(dim=1)                    # [B, H, Dqk]
+    dk_abs = r.path.dk.float().abs().sum(dim=1)
+    assert torch.all(dk.abs() <= 1e-2 * dk_abs + 1e-3)
+    dv = r.path.dv.float().sum(dim=1)
+    do = r.x["dout"].float().sum(dim=1)
+    dv_abs = r.path.dv.float().abs().sum(dim=1)
+    assert torch.all((dv - do).abs() <= 1e-2 * dv_abs + 1e-2)
+
+
+def check_key_gradients_on_given_sets(r):
+    """dK/dV of sampled keys, with the mask built from seeded random index
+    sets, so that the oracle knows every query's list."""
+    cfg = r.cfg
+    seg = r.seg
+    b = r.batches[-1]
+    sets = inputs.random_index_sets(cfg.B, cfg.S, cfg.K, seg, seed=3)
+    path = r.path
+    path.build_mask(torch.from_numpy(sets).to(DEV), r.x["seg"])
+    path.forward(r.x["q"], r.x["k"], r.x["v"], cfg.softmax_scale)
+    path.backward(r.x["q"], r.x["k"], r.x["v"], r.x["dout"], cfg.softmax_scale)
+    torch.cuda.synchronize()
+    S = cfg.S
+    for s, h in ((S - 1, 0), (S - 40, cfg.H - 1), (S - 700, 3)):
+        dk = np.zeros(cfg.Dqk)
+        dv = np.zeros(cfg.Dv)
+        for t in range(s, S):
+            row = sets[b, t]
+            kept = row[row >= 0].astype(np.int64)
+            pos = np.searchsorted(kept, s)
+            if pos >= kept.size or kept[pos] != s:
+                continue
+            q_t = _f64(r.x["q"][b, t, h:h + 1])
+            _, dk_sel, dv_sel = ref.attention_bwd_row(q_t, r.gather(b, kept, "k")[:, h:h + 1],
+                                                      r.gather(b, kept, "v")[:, h:h + 1],
+                                                      _f64(r.x["dout"][b, t, h:h + 1]), cfg.softmax_scale)
+            dk += dk_sel[pos, 0]
+            dv += dv_sel[pos, 0]
+        _check_rel(f"dk[{b},{s},{h}]", _f64(path.dk[b, s, h]), dk)
+        _check_rel(f"dv[{b},{s},{h}]", _f64(path.dv[b, s, h]), dv)
