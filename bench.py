@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
@@ -155,6 +157,16 @@ def main():
             dsa.dsa_sparse_attn_bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], path.lse, path.mask, scale,
                                          path.dk, path.dv, path.ws)
             mark(5)
+
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
 
     for i in range(args.warmup):
         step()

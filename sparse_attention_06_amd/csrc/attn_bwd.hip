@@ -59,8 +59,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int nkb = (S + 127) / 128;
-  const int kblk = (int)(blockIdx.x % nkb);
-  const int bh = (int)(blockIdx.x / nkb);
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s key blocks share an XCD
+  const int kblk = L % nkb;
+  const int bh = L / nkb;
   const int b = bh / H, h = bh % H;
   const int kb0 = kblk * 128;
   const int s0 = kb0 + wid * 32;  // this wave's first key
@@ -182,7 +183,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int ks = 0; ks < DV / 16; ++ks)
         dpacc = mfma32(*(const u32x4*)(sO + col * OP + ks * 16 + 8 * half), vf[ks], dpacc);
-      const uint64_t* mwv = smW[buf][kt_w - kt_lo];
+      // this lane's bit of query qi's word: one 32-bit half, constant bit offset
+      const uint32_t* mw32 = (const uint32_t*)smW[buf][kt_w - kt_lo] + (bitpos >> 5);
+      const int bsh = bitpos & 31;
       // dV^T[e, s] += dO^T[e, q] P[q, s];  dK^T[d, s] += Q^T[d, q] dS[q, s]
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
         for (int c8 = 0; c8 < 8; ++c8) {
           const int r = 8 * p2 + c8;
           const int qi = acc_row(r, half);
-          const bool keep = cw == 2 ? (q0 + qi < S) : (((mwv[qi] >> bitpos) & 1ull) != 0ull);
+          const bool keep = (mw32[2 * qi] >> bsh) & 1u;  // FULL tiles have every in-range bit set
           const float pr = keep ? fast_exp2(sacc[r] * scale_log2 - smL[buf][qi]) : 0.f;
           p[c8] = pr;
           ds[c8] = pr * (dpacc[r] - smD[buf][qi]);
@@ -248,8 +251,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
-  const int qt = NQ - 1 - (int)(blockIdx.x / (B * H));
-  const int bh = blockIdx.x % (B * H);
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s query tiles share an XCD
+  const int bh = L / NQ;
+  const int qt = NQ - 1 - L % NQ;
   const int b = bh / H, h = bh % H;
   const int tq = qt * 128 + wid * 32 + col;
   const bool qvalid = tq < S;
@@ -345,12 +349,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
     const int kn = next_tile(kt);
     if (kn <= kt_last) gload(kn);
 
-    uint64_t mw = ~0ull;
+    uint64_t mw = qvalid ? ~0ull : 0ull;
     bool work = true;
     if (c == 1) {
       mw = qvalid ? bits_q[kt] : 0ull;
       work = __ballot(mw != 0ull) != 0ull;
     }
+    // this lane's keys are kb*32 + 8i + 4*half + r: pre-shift the word by 4*half
+    const uint32_t w0 = (uint32_t)(mw >> (4 * half)), w1 = (uint32_t)(mw >> (32 + 4 * half));
     if (work) {
       const uint16_t* sK = smK[buf];
       const uint16_t* sV = smV[buf];
@@ -378,8 +384,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
           for (int c8 = 0; c8 < 8; ++c8) {
             const int r = 8 * p2 + c8;
-            const int key = kb * 32 + acc_row(r, half);
-            const bool keep = c == 2 ? qvalid : (((mw >> key) & 1ull) != 0ull);
+            const bool keep = ((kb ? w1 : w0) >> (8 * (r >> 2) + (r & 3))) & 1u;
             const float pr = keep ? fast_exp2(sacc[kb][r] * scale_log2 - Lq) : 0.f;
             dsv[c8] = pr * (dpacc[kb][r] - Dq);
           }

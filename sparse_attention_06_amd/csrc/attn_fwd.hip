@@ -20,7 +20,7 @@
 // K/V tiles are double buffered in LDS. The next non-empty tile's global loads
 // are issued before the current tile is computed. exp2 is the hardware
 // v_exp_f32, with the scale folded in (scale * log2 e). O is rescaled only when
-// a running max moves.
+// a tile max passes the reference max by more than 2^8.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,6 +35,81 @@ constexpr int KCH = TK * DQK / 8 / 256;  // 16-byte chunks per thread per K tile
 constexpr int VCH = TK * DV / 8 / 256;   // ... per V tile (4)
 }  // namespace fwd
 
+// One 64-key tile of the online softmax for a wave's 32 queries. Keys whose
+// selection bit is clear drop out (FULL tiles pass all-ones words). This
+// lane's keys are kb*32 + 8i + 4*half + r (i, r in 0..3); its query word is
+// passed pre-shifted by 4*half and split into halves, so each bit sits at the
+// constant position 8i + r of word kb.
+__device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV, const u32x4 (&qf)[fwd::KS],
+                                         uint32_t w0, uint32_t w1, float scale_log2, float& m, float& l,
+                                         f32x16 (&oacc)[4]) {
+  using namespace fwd;
+  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
+  f32x16 sacc[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x4 a = *(const u32x4*)(sK + (kb * 32 + col) * KP + ks * 16 + 8 * half);
+      sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
+    }
+
+  float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = sacc[kb][r] * scale_log2;
+      const uint32_t w = kb ? w1 : w0;
+      if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) x = -INFINITY;
+      sacc[kb][r] = x;
+      tm[r & 3] = fmaxf(tm[r & 3], x);
+    }
+  float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  // Lazy rescaling: probabilities are taken relative to a reference max m that
+  // only moves when the tile max exceeds it by more than 8 (log2 units), so
+  // p <= 2^8. O and l share the reference, so the result is unchanged; the
+  // O rescale (64 accumulator multiplies) becomes rare.
+  const bool bump = tmax > m + 8.f;
+  if (__ballot(bump)) {
+    const float m_new = bump ? tmax : m;
+    const float alpha = bump ? fast_exp2(m - m_new) : 1.f;  // m = -inf on a first bump: alpha = 0
+    l *= alpha;
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
+    m = m_new;
+  }
+  const float m_use = m == -INFINITY ? 0.f : m;
+
+  // O^T[e, q] += V^T[e, key] P^T[key, q]; V^T fragments read transposed from the V tile,
+  // keys permuted inside each 16-key step to match the S^T accumulator rows
+  float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      float pv8[8];
+#pragma unroll
+      for (int c8 = 0; c8 < 8; ++c8) {
+        pv8[c8] = fast_exp2(sacc[kb][8 * p2 + c8] - m_use);
+        ls[c8 & 3] += pv8[c8];
+      }
+      const u32x4 pb = u32x4{pack_bf2(pv8[0], pv8[1]), pack_bf2(pv8[2], pv8[3]), pack_bf2(pv8[4], pv8[5]),
+                             pack_bf2(pv8[6], pv8[7])};
+      const int r0 = kb * 32 + 16 * p2 + 4 * half;
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb) oacc[eb] = mfma32(lds_tr_frag(sV, VP, r0, r0 + 8, eb * 32), pb, oacc[eb]);
+    }
+  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+}
+
 __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
@@ -48,8 +123,10 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
-  const int qt = NQ - 1 - (int)(blockIdx.x / (B * H));  // longest tiles first
-  const int bh = blockIdx.x % (B * H);
+  // all query tiles of one (b, h) on one XCD (they share K/V), longest first
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int bh = L / NQ;
+  const int qt = NQ - 1 - L % NQ;
   const int b = bh / H, h = bh % H;
   const int tq = qt * 128 + wid * 32 + col;  // this lane's query
   const bool qvalid = tq < S;
@@ -127,71 +204,9 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
       mw = qvalid ? bits_q[kt] : 0ull;
       work = __ballot(mw != 0ull) != 0ull;  // some query of this wave keeps a key here
     }
-    if (work) {
-      const uint16_t* sK = smK[buf];
-      const uint16_t* sV = smV[buf];
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = *(const u32x4*)(sK + (kb * 32 + col) * KP + ks * 16 + 8 * half);
-          sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
-        }
-
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sacc[kb][r] * scale_log2;
-          if (c == 1 && !((mw >> (kb * 32 + acc_row(r, half))) & 1ull)) x = -INFINITY;
-          sacc[kb][r] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      if (__ballot(m_new != m)) {  // rescale only when some running max moved
-        const float alpha = fast_exp2(m - m_use);
-        l *= alpha;
-#pragma unroll
-        for (int eb = 0; eb < 4; ++eb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
-      }
-      m = m_new;
-
-      u32x4 pb[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int p2 = 0; p2 < 2; ++p2) {
-          float pv8[8];
-#pragma unroll
-          for (int c8 = 0; c8 < 8; ++c8) {
-            pv8[c8] = fast_exp2(sacc[kb][8 * p2 + c8] - m_use);
-            l += pv8[c8];
-          }
-          pb[kb][p2] = u32x4{pack_bf2(pv8[0], pv8[1]), pack_bf2(pv8[2], pv8[3]), pack_bf2(pv8[4], pv8[5]),
-                             pack_bf2(pv8[6], pv8[7])};
-        }
-      // O^T[e, q] += V^T[e, key] P^T[key, q]; V^T fragments read transposed from the V tile,
-      // keys permuted inside each 16-key step to match the S^T accumulator rows
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int p2 = 0; p2 < 2; ++p2) {
-          const int r0 = kb * 32 + 16 * p2 + 4 * half;
-#pragma unroll
-          for (int eb = 0; eb < 4; ++eb)
-            oacc[eb] = mfma32(lds_tr_frag(sV, VP, r0, r0 + 8, eb * 32), pb[kb][p2], oacc[eb]);
-        }
-    }
+    if (work)
+      fwd_tile(smK[buf], smV[buf], qf, (uint32_t)(mw >> (4 * half)), (uint32_t)(mw >> (32 + 4 * half)),
+               scale_log2, m, l, oacc);
     buf ^= 1;
     kt = kn;
   }

@@ -17,16 +17,16 @@ constexpr int kTileK = 64;   // attention tile columns (keys); one u64 mask word
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// float -> bf16 bits, round to nearest even (NaN stays NaN): the IEEE
+// narrowing conversion, which gfx950 does in hardware (v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <typename T> struct Elem;
@@ -71,6 +71,17 @@ __device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* X, int pitch, int k
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroups of a 1-D grid are dealt round-robin to the 8 XCDs, each with
+// its own L2. Remap the block id so that each XCD works through one contiguous
+// range of logical blocks; blocks that share operands (same batch and head)
+// then share an L2. The tail beyond a multiple of 8 keeps its id.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int NX = 8;
+  const int per = nblocks / NX;
+  if (bid >= per * NX) return bid;
+  return (bid % NX) * per + bid / NX;
+}
 
 // ---------------------------------------------------------------- wave helpers
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {

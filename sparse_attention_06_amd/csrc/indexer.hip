@@ -33,8 +33,10 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int nrb = (nrows + 3) / 4;
-  const int rb = nrb - 1 - (int)(blockIdx.x / B);  // longest rows first
-  const int b = blockIdx.x % B;
+  // one batch row's row blocks share an XCD (and its L2 copy of k_idx); longest rows first
+  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int b = L / nrb;
+  const int rb = nrb - 1 - L % nrb;
   const int r = rb * 4 + wid;
   const bool active = r < nrows;
   const int t = row0 + r;
