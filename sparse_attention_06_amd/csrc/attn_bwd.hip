@@ -236,27 +236,43 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ, query-major; also computes D. Workgroup = (b, h, 128 queries), wave =
-// 32 queries. Walks the non-empty 64-key tiles up to the diagonal.
+// dQ, query-major; also computes D. Workgroup = (b, h, 256 queries) with 8
+// waves (two per SIMD) of 32 queries. Walks the non-empty 64-key tiles up to
+// the diagonal; K and V tiles are double buffered in natural layout and filled
+// by direct global->LDS copies. Each tile is processed as two 32-key halves to
+// bound the live accumulators.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
+namespace dqk {
+constexpr int NW = 8, QW = 32 * NW;
+constexpr int KSL = bwd::DQK / 8 + 1, VSL = bwd::DV / 8 + 1;  // 16-byte slots per padded row
+constexpr int KBLK = bwd::TK * KSL / 64, VBLK = bwd::TK * VSL / 64;
+constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;
+static_assert(KSL * 8 == bwd::QP && VSL * 8 == bwd::OP, "pitches");
+}  // namespace dqk
+
+__global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ D, const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B,
     int S, int H, float scale, float scale_log2, uint16_t* __restrict__ dq) {
   using namespace bwd;
-  __shared__ __attribute__((aligned(16))) uint16_t smK[2][TK * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t smV[2][TK * OP];
+  using dqk::NW;
+  using dqk::QW;
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * QP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smV[2][TK * OP];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
-  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s query tiles share an XCD
-  const int bh = L / NQ;
-  const int qt = NQ - 1 - L % NQ;
+  const int NQW = (S + QW - 1) / QW;
+  const int Lb = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s query blocks share an XCD
+  const int bh = Lb / NQW;
+  const int qw = NQW - 1 - Lb % NQW;
   const int b = bh / H, h = bh % H;
-  const int tq = qt * 128 + wid * 32 + col;
+  const int tq = qw * QW + wid * 32 + col;
   const bool qvalid = tq < S;
+  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
+  const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
   const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
   const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
@@ -301,92 +317,76 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqacc[i][j] = 0.f;
 
-  const int kt_last = min(S - 1, qt * 128 + 127) / TK;
-  const uint8_t* cls_row = cls + ((size_t)b * NQ + qt) * NK;
+  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  const uint8_t* cls0 = cls + ((size_t)b * NQ + qt0) * NK;
+  const uint8_t* cls1 = cls + ((size_t)b * NQ + qt1) * NK;
+  const uint8_t* clsw = cls + ((size_t)b * NQ + qt_w) * NK;
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
   auto next_tile = [&](int kt) {
     int n = kt + 1;
-    while (n <= kt_last && cls_row[n] == 0) ++n;
+    while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
     return n;
   };
-  u32x4 pk[KCH], pv[VCH];
-  auto gload = [&](int kt) {
+  auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24, s = kt * TK + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (s < S) z = *(const u32x4*)(kbase + (size_t)s * rs_qk + cc * 8);
-      pk[i] = z;
+    for (int i = 0; i < dqk::KI; ++i) {
+      const int j = wid + i * NW;
+      if (j < dqk::KBLK) {
+        const int slot = j * 64 + lane, row = slot / dqk::KSL, c = min(slot % dqk::KSL, dqk::KSL - 2);
+        const int s = min(kt * TK + row, S - 1);
+        g2lds16(kbase + (size_t)s * rs_qk + c * 8, (char*)smK[buf] + j * 1024);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16, s = kt * TK + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (s < S) z = *(const u32x4*)(vbase + (size_t)s * rs_v + cc * 8);
-      pv[i] = z;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24;
-      *(u32x4*)(&smK[buf][row * QP + cc * 8]) = pk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16;
-      *(u32x4*)(&smV[buf][row * OP + cc * 8]) = pv[i];
+    for (int i = 0; i < dqk::VI; ++i) {
+      const int j = wid + i * NW;
+      if (j < dqk::VBLK) {
+        const int slot = j * 64 + lane, row = slot / dqk::VSL, c = min(slot % dqk::VSL, dqk::VSL - 2);
+        const int s = min(kt * TK + row, S - 1);
+        g2lds16(vbase + (size_t)s * rs_v + c * 8, (char*)smV[buf] + j * 1024);
+      }
     }
   };
 
   int kt = next_tile(-1);
-  if (kt <= kt_last) gload(kt);
+  if (kt <= kt_last) issue(kt, 0);
   int buf = 0;
   while (kt <= kt_last) {
-    const int c = cls_row[kt];
-    lstore(buf);
+    const int c = clsw[kt];
+    uint64_t mw = (qvalid && c == 2) ? ~0ull : 0ull;
+    if (c == 1 && qvalid) mw = bits_q[kt];
+    wait_vmem();
     __syncthreads();
     const int kn = next_tile(kt);
-    if (kn <= kt_last) gload(kn);
+    if (kn <= kt_last) issue(kn, buf ^ 1);
 
-    uint64_t mw = qvalid ? ~0ull : 0ull;
-    bool work = true;
-    if (c == 1) {
-      mw = qvalid ? bits_q[kt] : 0ull;
-      work = __ballot(mw != 0ull) != 0ull;
-    }
-    // this lane's keys are kb*32 + 8i + 4*half + r: pre-shift the word by 4*half
-    const uint32_t w0 = (uint32_t)(mw >> (4 * half)), w1 = (uint32_t)(mw >> (32 + 4 * half));
-    if (work) {
+    if (c != 0 && __ballot(mw != 0ull)) {
       const uint16_t* sK = smK[buf];
       const uint16_t* sV = smV[buf];
-      f32x16 sacc[2], dpacc[2];
+      // this lane's keys are kb*32 + 8i + 4*half + r: pre-shift the word by 4*half
+      const uint64_t mwh = mw >> (4 * half);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t w = (uint32_t)(mwh >> (32 * kb));
+        f32x16 sacc, dpacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { sacc[kb][i] = 0.f; dpacc[kb][i] = 0.f; }
+        for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks)
+        for (int ks = 0; ks < DQK / 16; ++ks)
+          sacc = mfma32(*(const u32x4*)(sK + (kb * 32 + col) * QP + ks * 16 + 8 * half), qf[ks], sacc);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sacc[kb] = mfma32(*(const u32x4*)(sK + (kb * 32 + col) * QP + ks * 16 + 8 * half), qf[ks], sacc[kb]);
-#pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          dpacc[kb] = mfma32(*(const u32x4*)(sV + (kb * 32 + col) * OP + ks * 16 + 8 * half), of[ks], dpacc[kb]);
-      // dQ^T[d, q] += K^T[d, s] dS^T[s, q], keys permuted inside each 16-key step
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int ks = 0; ks < DV / 16; ++ks)
+          dpacc = mfma32(*(const u32x4*)(sV + (kb * 32 + col) * OP + ks * 16 + 8 * half), of[ks], dpacc);
+        // dQ^T[d, q] += K^T[d, s] dS^T[s, q], keys permuted inside each 16-key step
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
           float dsv[8];
 #pragma unroll
           for (int c8 = 0; c8 < 8; ++c8) {
             const int r = 8 * p2 + c8;
-            const bool keep = ((kb ? w1 : w0) >> (8 * (r >> 2) + (r & 3))) & 1u;
-            const float pr = keep ? fast_exp2(sacc[kb][r] * scale_log2 - Lq) : 0.f;
-            dsv[c8] = pr * (dpacc[kb][r] - Dq);
+            const bool keep = (w >> (8 * (r >> 2) + (r & 3))) & 1u;
+            const float pr = keep ? fast_exp2(fmaf(sacc[r], scale_log2, -Lq)) : 0.f;
+            dsv[c8] = pr * (dpacc[r] - Dq);
           }
           const u32x4 db = pack8(dsv);
           const int r0 = kb * 32 + 16 * p2 + 4 * half;
@@ -394,6 +394,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(
           for (int i = 0; i < DQK / 32; ++i)
             dqacc[i] = mfma32(lds_tr_frag(sK, QP, r0, r0 + 8, i * 32), db, dqacc[i]);
         }
+      }
     }
     buf ^= 1;
     kt = kn;
@@ -415,8 +416,8 @@ hipError_t launch_attn_bwd_dq_mfma(const void* q, const void* k, const void* v, 
                                    const void* dout, const float* lse, float* D, const uint64_t* bits,
                                    const uint8_t* cls, int B, int S, int H, float scale, void* dq,
                                    hipStream_t st) {
-  const size_t nq = (size_t)n_qtiles(S) * B * H;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(256), 0, st, (const uint16_t*)q,
+  const size_t nq = (size_t)((S + dqk::QW - 1) / dqk::QW) * B * H;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(dqk::NW * 64), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse,
                      D, bits, cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dq);
   return hipGetLastError();

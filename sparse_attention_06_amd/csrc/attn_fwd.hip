@@ -6,10 +6,11 @@
 // "Integrate DeepSeek Sparse Attention with Tokamax Flash Attention",
 // Description (flash attention driven by a dynamic 3-D index mask).
 //
-// MFMA kernel (bf16, Dqk = 192, Dv = 128). A workgroup is one (b, h, 128-query
-// tile) with 4 waves of 32 queries each. It walks the 64-key tiles up to the
-// diagonal. Tiles of class EMPTY are skipped outright. FULL tiles use no mask.
-// PARTIAL tiles read one u64 selection word per query.
+// MFMA kernel (bf16, Dqk = 192, Dv = 128). A workgroup is one (b, h, 256-query
+// block) with 8 waves (two per SIMD) of 32 queries each. It walks the 64-key
+// tiles up to the diagonal. Tiles that are EMPTY for both of its 128-query
+// tiles are skipped outright. A wave whose tile is EMPTY idles. PARTIAL tiles
+// read one u64 selection word per query.
 //   S^T = K Q^T: keys on MFMA rows, queries on columns, so each lane owns one
 //   query and 32 of the tile's 64 logits. The online-softmax max and sum are
 //   in-lane, with one exchange between lane halves. Q stays in VGPRs.
@@ -17,8 +18,9 @@
 //   into the B operand. The key order inside each 16-wide k step is permuted
 //   to match the accumulator layout. V^T comes from the natural V tile in LDS
 //   through the gfx950 transposing LDS read, with the same permutation.
-// K/V tiles are double buffered in LDS. The next non-empty tile's global loads
-// are issued before the current tile is computed. exp2 is the hardware
+// K/V tiles are double buffered in LDS and filled by direct global->LDS copies
+// (no staging registers). The next non-empty tile's copies are issued before
+// the current tile is computed. exp2 is the hardware
 // v_exp_f32, with the scale folded in (scale * log2 e). O is rescaled only when
 // a tile max passes the reference max by more than 2^8.
 #include "common.hpp"
@@ -28,11 +30,17 @@ namespace dsa {
 
 namespace fwd {
 constexpr int DQK = 192, DV = 128, TK = 64;
-constexpr int KS = DQK / 16;   // k steps of S^T
-constexpr int KP = DQK + 8;    // LDS pitch (elements) of a K row: 400 B, conflict-free b128 reads
-constexpr int VP = DV + 8;     // LDS pitch of a V row: 272 B
-constexpr int KCH = TK * DQK / 8 / 256;  // 16-byte chunks per thread per K tile (6)
-constexpr int VCH = TK * DV / 8 / 256;   // ... per V tile (4)
+constexpr int NW = 8;                // waves per workgroup: 2 per SIMD
+constexpr int QW = 32 * NW;          // queries per workgroup (two 128-query tiles)
+constexpr int KS = DQK / 16;         // k steps of S^T
+constexpr int KSL = DQK / 8 + 1;     // 16-byte slots per LDS K row (one pad slot): 400 B
+constexpr int VSL = DV / 8 + 1;      // ... per V row: 272 B
+constexpr int KP = KSL * 8;          // LDS pitch of a K row (elements)
+constexpr int VP = VSL * 8;          // LDS pitch of a V row
+constexpr int KBLK = TK * KSL / 64;  // 1 KB blocks per K tile (25)
+constexpr int VBLK = TK * VSL / 64;  // ... per V tile (17)
+constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;  // blocks per wave
+static_assert(TK * KSL % 64 == 0 && TK * VSL % 64 == 0, "tiles must be whole 1 KB blocks");
 }  // namespace fwd
 
 // One 64-key tile of the online softmax for a wave's 32 queries. Keys whose
@@ -58,19 +66,20 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV,
       sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
     }
 
+  // masked max over raw logits (the scale is positive, so it commutes with max)
   float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = sacc[kb][r] * scale_log2;
       const uint32_t w = kb ? w1 : w0;
-      if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) x = -INFINITY;
+      const float x = ((w >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[kb][r] : -INFINITY;
       sacc[kb][r] = x;
       tm[r & 3] = fmaxf(tm[r & 3], x);
     }
   float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+
   // Lazy rescaling: probabilities are taken relative to a reference max m that
   // only moves when the tile max exceeds it by more than 8 (log2 units), so
   // p <= 2^8. O and l share the reference, so the result is unchanged; the
@@ -86,7 +95,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV,
       for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
     m = m_new;
   }
-  const float m_use = m == -INFINITY ? 0.f : m;
+  const float neg_m = m == -INFINITY ? 0.f : -m;
 
   // O^T[e, q] += V^T[e, key] P^T[key, q]; V^T fragments read transposed from the V tile,
   // keys permuted inside each 16-key step to match the S^T accumulator rows
@@ -98,7 +107,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV,
       float pv8[8];
 #pragma unroll
       for (int c8 = 0; c8 < 8; ++c8) {
-        pv8[c8] = fast_exp2(sacc[kb][8 * p2 + c8] - m_use);
+        pv8[c8] = fast_exp2(fmaf(sacc[kb][8 * p2 + c8], scale_log2, neg_m));
         ls[c8 & 3] += pv8[c8];
       }
       const u32x4 pb = u32x4{pack_bf2(pv8[0], pv8[1]), pack_bf2(pv8[2], pv8[3]), pack_bf2(pv8[4], pv8[5]),
@@ -110,26 +119,29 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV,
   l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 }
 
-__global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
+__global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
     float scale_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace fwd;
-  // double-buffered natural-layout K and V tiles; V^T fragments come from
-  // ds_read_b64_tr_b16 on the V tile, so no transposed copy is stored
-  __shared__ __attribute__((aligned(16))) uint16_t smK[2][TK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t smV[2][TK * VP];
+  // double-buffered natural-layout K and V tiles, filled by direct global->LDS
+  // copies; V^T fragments come from ds_read_b64_tr_b16 on the V tile
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * KP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smV[2][TK * VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
-  // all query tiles of one (b, h) on one XCD (they share K/V), longest first
-  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-  const int bh = L / NQ;
-  const int qt = NQ - 1 - L % NQ;
+  const int NQW = (S + QW - 1) / QW;
+  // all query blocks of one (b, h) on one XCD (they share K/V), longest first
+  const int Lb = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int bh = Lb / NQW;
+  const int qw = NQW - 1 - Lb % NQW;
   const int b = bh / H, h = bh % H;
-  const int tq = qt * 128 + wid * 32 + col;  // this lane's query
+  const int tq = qw * QW + wid * 32 + col;  // this lane's query
   const bool qvalid = tq < S;
+  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);  // this wave's 128-query tile
+  const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;  // token strides
   const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
   const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
@@ -149,62 +161,51 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[eb][i] = 0.f;
 
-  const int kt_last = min(S - 1, qt * 128 + 127) / TK;
-  const uint8_t* cls_row = cls + ((size_t)b * NQ + qt) * NK;
+  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  const uint8_t* cls0 = cls + ((size_t)b * NQ + qt0) * NK;
+  const uint8_t* cls1 = cls + ((size_t)b * NQ + qt1) * NK;
+  const uint8_t* clsw = cls + ((size_t)b * NQ + qt_w) * NK;
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
   auto next_tile = [&](int kt) {
     int n = kt + 1;
-    while (n <= kt_last && cls_row[n] == 0) ++n;
+    while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
     return n;
   };
-
-  u32x4 pk[KCH], pv[VCH];
-  auto gload = [&](int kt) {
+  // this wave's 1 KB blocks of a tile: block j covers slots 64j .. 64j+63 of the
+  // padded [64 rows][KSL or VSL slots] layout; pad slots copy a harmless chunk
+  auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24, s = kt * TK + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (s < S) z = *(const u32x4*)(kbase + (size_t)s * rs_qk + cc * 8);
-      pk[i] = z;
+    for (int i = 0; i < KI; ++i) {
+      const int j = wid + i * NW;
+      if (j < KBLK) {
+        const int slot = j * 64 + lane, row = slot / KSL, c = min(slot % KSL, KSL - 2);
+        const int s = min(kt * TK + row, S - 1);
+        g2lds16(kbase + (size_t)s * rs_qk + c * 8, (char*)smK[buf] + j * 1024);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16, s = kt * TK + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (s < S) z = *(const u32x4*)(vbase + (size_t)s * rs_v + cc * 8);
-      pv[i] = z;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24;
-      *(u32x4*)(&smK[buf][row * KP + cc * 8]) = pk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16;
-      *(u32x4*)(&smV[buf][row * VP + cc * 8]) = pv[i];
+    for (int i = 0; i < VI; ++i) {
+      const int j = wid + i * NW;
+      if (j < VBLK) {
+        const int slot = j * 64 + lane, row = slot / VSL, c = min(slot % VSL, VSL - 2);
+        const int s = min(kt * TK + row, S - 1);
+        g2lds16(vbase + (size_t)s * rs_v + c * 8, (char*)smV[buf] + j * 1024);
+      }
     }
   };
 
   int kt = next_tile(-1);
-  if (kt <= kt_last) gload(kt);
+  if (kt <= kt_last) issue(kt, 0);
   int buf = 0;
   while (kt <= kt_last) {
-    const int c = cls_row[kt];
-    lstore(buf);
-    __syncthreads();  // tile kt visible; the other buffer is free (read two tiles ago)
+    const int c = clsw[kt];
+    uint64_t mw = (qvalid && c == 2) ? ~0ull : 0ull;
+    if (c == 1 && qvalid) mw = bits_q[kt];
+    wait_vmem();
+    __syncthreads();  // tile kt visible in `buf`; every wave is done with the other buffer
     const int kn = next_tile(kt);
-    if (kn <= kt_last) gload(kn);  // in flight while this tile is computed
-
-    uint64_t mw = ~0ull;
-    bool work = true;
-    if (c == 1) {
-      mw = qvalid ? bits_q[kt] : 0ull;
-      work = __ballot(mw != 0ull) != 0ull;  // some query of this wave keeps a key here
-    }
-    if (work)
+    if (kn <= kt_last) issue(kn, buf ^ 1);  // lands while this tile is computed
+    if (c != 0 && __ballot(mw != 0ull))
       fwd_tile(smK[buf], smV[buf], qf, (uint32_t)(mw >> (4 * half)), (uint32_t)(mw >> (32 + 4 * half)),
                scale_log2, m, l, oacc);
     buf ^= 1;
@@ -295,8 +296,8 @@ __global__ __launch_bounds__(256) void attn_fwd_plain_kernel(
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, const uint64_t* bits,
                                 const uint8_t* cls, int B, int S, int H, float scale, void* o,
                                 float* lse, hipStream_t st) {
-  const size_t nblk = (size_t)n_qtiles(S) * B * H;
-  hipLaunchKernelGGL(attn_fwd_mfma_kernel, dim3((unsigned)nblk), dim3(256), 0, st,
+  const size_t nblk = (size_t)((S + fwd::QW - 1) / fwd::QW) * B * H;
+  hipLaunchKernelGGL(attn_fwd_mfma_kernel, dim3((unsigned)nblk), dim3(fwd::NW * 64), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, bits, cls, B, S, H,
                      scale * 1.4426950408889634f, (uint16_t*)o, lse);
   return hipGetLastError();

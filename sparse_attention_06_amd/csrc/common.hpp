@@ -72,6 +72,16 @@ __device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* X, int pitch, int k
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at lds_base + 16*l, so one wave fills a contiguous 1 KB
+// block. `lds_base` must be wave-uniform. Completion is waited for with
+// wait_vmem() before the barrier that publishes the block.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
+                                   (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Workgroups of a 1-D grid are dealt round-robin to the 8 XCDs, each with
 // its own L2. Remap the block id so that each XCD works through one contiguous
 // range of logical blocks; blocks that share operands (same batch and head)
