@@ -29,8 +29,6 @@ constexpr int QC = 32;              // queries per chunk (key-major kernel)
 constexpr int TK = 64;              // keys per tile (query-major kernel)
 constexpr int QP = DQK + 8;         // LDS pitch (elements) of q / k rows
 constexpr int OP = DV + 8;          // LDS pitch of dO / v rows
-constexpr int QCH = QC * DQK / 8 / 256;  // 16-byte chunks per thread: Q chunk (3)
-constexpr int OCH = QC * DV / 8 / 256;   // dO chunk (2)
 constexpr int KCH = TK * DQK / 8 / 256;  // K tile (6)
 constexpr int VCH = TK * DV / 8 / 256;   // V tile (4)
 }  // namespace bwd
@@ -40,23 +38,44 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV, key-major. Workgroup = (b, h, 128 keys), wave = 32 keys held in
-// registers (K, V fragments and the dK, dV accumulators). Walks the 32-query
-// chunks from the first key to the end, skipping chunks whose tiles are EMPTY.
+// dK / dV, key-major. Workgroup = (b, h, 128 keys) with 8 waves in two roles,
+// two waves per SIMD:
+//   waves 0-3 ("A", 32 keys each, K/V fragments in VGPRs): S = Q K^T,
+//     dP = dO V^T, P, dS, and dV^T += dO^T P. A hands dS to its partner
+//     through LDS.
+//   waves 4-7 ("B", the same 32 keys as wave w-4): dK^T += Q^T dS, one
+//     32-query chunk behind A.
+// So B's MFMAs run while A does its softmax-gradient VALU work, and no MFMA is
+// done twice. Chunks with EMPTY tiles for the workgroup's keys are skipped.
+// Q chunks are triple buffered (B reads the previous one); dO and dS are
+// double buffered. All are filled by direct global->LDS copies.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
+namespace dkv {
+constexpr int NW = 8;
+constexpr int QSL = bwd::DQK / 8 + 1, OSL = bwd::DV / 8 + 1;    // 16-byte slots per padded row
+constexpr int QBLK = (bwd::QC * QSL + 63) / 64;                 // 1 KB blocks per Q chunk (13)
+constexpr int OBLK = (bwd::QC * OSL + 63) / 64;                 // ... per dO chunk (9)
+constexpr int QI = (QBLK + NW - 1) / NW, OI = (OBLK + NW - 1) / NW;
+static_assert(QSL * 8 == bwd::QP && OSL * 8 == bwd::OP, "pitches");
+}  // namespace dkv
+
+__global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ D,
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
     float scale, float scale_log2, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   using namespace bwd;
-  __shared__ __attribute__((aligned(16))) uint16_t smQ[2][QC * QP];
-  __shared__ __attribute__((aligned(16))) uint16_t smO[2][QC * OP];
+  using dkv::NW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smQ[3][dkv::QBLK * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char smO[2][dkv::OBLK * 1024];
+  __shared__ __attribute__((aligned(16))) u32x4 smS[2][4][2][64];  // dS, B-operand layout, per A wave
   __shared__ float smL[2][QC], smD[2][QC];
   __shared__ uint64_t smW[2][2][QC];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
+  const bool roleA = wid < 4;
+  const int kw = wid & 3;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int nkb = (S + 127) / 128;
   const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s key blocks share an XCD
@@ -64,10 +83,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const int bh = L / nkb;
   const int b = bh / H, h = bh % H;
   const int kb0 = kblk * 128;
-  const int s0 = kb0 + wid * 32;  // this wave's first key
+  const int s0 = kb0 + kw * 32;   // this wave pair's first key
   const int sk = s0 + col;        // this lane's key
   const bool kvalid = sk < S;
-  const int kt_w = s0 / 64;       // this wave's 64-key tile
+  const int kt_w = s0 / 64;       // the pair's 64-key tile
   const int kt_lo = kb0 / 64;     // workgroup's first key tile
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
   const uint16_t* qbase = q + (size_t)b * S * rs_qk + (size_t)h * DQK;
@@ -75,30 +94,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
   const float* lrow = lse + ((size_t)b * H + h) * S;
   const float* drow = D + ((size_t)b * H + h) * S;
 
-  u32x4 kf[DQK / 16], vf[DV / 16];
-#pragma unroll
-  for (int ks = 0; ks < DQK / 16; ++ks) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (kvalid) z = *(const u32x4*)(k + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK + ks * 16 + 8 * half);
-    kf[ks] = z;
-  }
-#pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (kvalid) z = *(const u32x4*)(v + ((size_t)b * S + sk) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
-    vf[ks] = z;
-  }
-  f32x16 dkacc[DQK / 32], dvacc[DV / 32];
-#pragma unroll
-  for (int i = 0; i < DQK / 32; ++i)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) dkacc[i][j] = 0.f;
-#pragma unroll
-  for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-    for (int j = 0; j < 16; ++j) dvacc[i][j] = 0.f;
-
-  const int bitpos = sk & 63;
   const int nchunks = (S + QC - 1) / QC;
   auto chunk_cls = [&](int qc, int which) -> int {
     const int kt = kt_lo + which;
@@ -109,26 +104,37 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
     while (n < nchunks && chunk_cls(n, 0) == 0 && chunk_cls(n, 1) == 0) ++n;
     return n;
   };
-
-  u32x4 pq[QCH], po[OCH];
-  float pl = 0.f, pd = 0.f;
-  uint64_t pw = 0ull;
-  auto gload = [&](int qc) {
+  // chunk qc's Q / dO rows into buffers (qb, ob); slots past the chunk copy a harmless chunk
+  auto issue = [&](int qc, int qb, int ob) {
     const int q0 = qc * QC;
 #pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24, t = q0 + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (t < S) z = *(const u32x4*)(qbase + (size_t)t * rs_qk + cc * 8);
-      pq[i] = z;
+    for (int i = 0; i < dkv::QI; ++i) {
+      const int j = wid + i * NW;
+      if (j < dkv::QBLK) {
+        const int slot = j * 64 + lane;
+        const bool in = slot < QC * dkv::QSL;
+        const int row = in ? slot / dkv::QSL : 0, c = in ? min(slot % dkv::QSL, dkv::QSL - 2) : 0;
+        const int t = min(q0 + row, S - 1);
+        g2lds16(qbase + (size_t)t * rs_qk + c * 8, smQ[qb] + j * 1024);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < OCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16, t = q0 + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (t < S) z = *(const u32x4*)(obase + (size_t)t * rs_v + cc * 8);
-      po[i] = z;
+    for (int i = 0; i < dkv::OI; ++i) {
+      const int j = wid + i * NW;
+      if (j < dkv::OBLK) {
+        const int slot = j * 64 + lane;
+        const bool in = slot < QC * dkv::OSL;
+        const int row = in ? slot / dkv::OSL : 0, c = in ? min(slot % dkv::OSL, dkv::OSL - 2) : 0;
+        const int t = min(q0 + row, S - 1);
+        g2lds16(obase + (size_t)t * rs_v + c * 8, smO[ob] + j * 1024);
+      }
     }
+  };
+  // per-query scalars of chunk qc: LSE (log2 units), D, and the two mask words
+  float pl = 0.f, pd = 0.f;
+  uint64_t pw = 0ull;
+  auto load_small = [&](int qc) {
+    const int q0 = qc * QC;
     if (tid < QC) {
       const int t = q0 + tid;
       pl = t < S ? lrow[t] * 1.4426950408889634f : INFINITY;
@@ -139,99 +145,150 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(
       pw = (t < S && kt < NK) ? bits[((size_t)b * S + t) * W + kt] : 0ull;
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < QCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 24, cc = ci % 24;
-      *(u32x4*)(&smQ[buf][row * QP + cc * 8]) = pq[i];
-    }
-#pragma unroll
-    for (int i = 0; i < OCH; ++i) {
-      const int ci = tid + i * 256, row = ci / 16, cc = ci % 16;
-      *(u32x4*)(&smO[buf][row * OP + cc * 8]) = po[i];
-    }
+  auto store_small = [&](int sb) {
     if (tid < QC) {
-      smL[buf][tid] = pl;
-      smD[buf][tid] = pd;
+      smL[sb][tid] = pl;
+      smD[sb][tid] = pd;
     } else if (tid < 3 * QC) {
-      smW[buf][(tid - QC) / QC][(tid - QC) % QC] = pw;
+      smW[sb][(tid - QC) / QC][(tid - QC) % QC] = pw;
     }
   };
+  auto active = [&](int qc) { return chunk_cls(qc, kt_w - kt_lo) != 0 && s0 <= qc * QC + QC - 1; };
 
   int qc = kb0 / QC;
   if (chunk_cls(qc, 0) == 0 && chunk_cls(qc, 1) == 0) qc = next_chunk(qc);
-  if (qc < nchunks) gload(qc);
-  int buf = 0;
-  while (qc < nchunks) {
-    const int q0 = qc * QC;
-    const int cw = chunk_cls(qc, kt_w - kt_lo);
-    lstore(buf);
-    __syncthreads();  // chunk qc visible; the other buffer is free
-    const int qn = next_chunk(qc);
-    if (qn < nchunks) gload(qn);  // in flight while this chunk is computed
+  if (qc < nchunks) {
+    issue(qc, 0, 0);
+    load_small(qc);
+  }
 
-    if (cw != 0 && s0 <= q0 + QC - 1) {
-      const uint16_t* sQ = smQ[buf];
-      const uint16_t* sO = smO[buf];
-      // S = Q K^T and dP = dO V^T: rows = queries, columns = keys (lane's key)
-      f32x16 sacc, dpacc;
+  if (roleA) {
+    u32x4 kf[DQK / 16], vf[DV / 16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+    for (int ks = 0; ks < DQK / 16; ++ks) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (kvalid) z = *(const u32x4*)(k + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK + ks * 16 + 8 * half);
+      kf[ks] = z;
+    }
 #pragma unroll
-      for (int ks = 0; ks < DQK / 16; ++ks)
-        sacc = mfma32(*(const u32x4*)(sQ + col * QP + ks * 16 + 8 * half), kf[ks], sacc);
+    for (int ks = 0; ks < DV / 16; ++ks) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (kvalid) z = *(const u32x4*)(v + ((size_t)b * S + sk) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
+      vf[ks] = z;
+    }
+    f32x16 dvacc[DV / 32];
 #pragma unroll
-      for (int ks = 0; ks < DV / 16; ++ks)
-        dpacc = mfma32(*(const u32x4*)(sO + col * OP + ks * 16 + 8 * half), vf[ks], dpacc);
-      // this lane's bit of query qi's word: one 32-bit half, constant bit offset
-      const uint32_t* mw32 = (const uint32_t*)smW[buf][kt_w - kt_lo] + (bitpos >> 5);
-      const int bsh = bitpos & 31;
-      // dV^T[e, s] += dO^T[e, q] P[q, s];  dK^T[d, s] += Q^T[d, q] dS[q, s]
+    for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dvacc[i][j] = 0.f;
+    const int bitpos = sk & 63;
+    for (int it = 0; qc < nchunks; ++it) {
+      store_small(it & 1);
+      wait_vmem();
+      __syncthreads();  // chunk qc visible in buffers (it%3, it%2)
+      const int qn = next_chunk(qc);
+      if (qn < nchunks) {
+        issue(qn, (it + 1) % 3, (it + 1) & 1);
+        load_small(qn);
+      }
+      if (active(qc)) {
+        const int q0 = qc * QC;
+        const uint16_t* sQ = (const uint16_t*)smQ[it % 3];
+        const uint16_t* sO = (const uint16_t*)smO[it & 1];
+        f32x16 sacc, dpacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < DQK / 16; ++ks)
+          sacc = mfma32(*(const u32x4*)(sQ + col * QP + ks * 16 + 8 * half), kf[ks], sacc);
+#pragma unroll
+        for (int ks = 0; ks < DV / 16; ++ks)
+          dpacc = mfma32(*(const u32x4*)(sO + col * OP + ks * 16 + 8 * half), vf[ks], dpacc);
+        // this lane's bit of query qi's word: one 32-bit half, constant bit offset;
+        // FULL tiles have every in-range bit set
+        const uint32_t* mw32 = (const uint32_t*)smW[it & 1][kt_w - kt_lo] + (bitpos >> 5);
+        const int bsh = bitpos & 31;
+        (void)q0;
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+          float p[8], ds[8];
+#pragma unroll
+          for (int c8 = 0; c8 < 8; ++c8) {
+            const int r = 8 * p2 + c8;
+            const int qi = acc_row(r, half);
+            const bool keep = (mw32[2 * qi] >> bsh) & 1u;
+            const float pr = keep ? fast_exp2(fmaf(sacc[r], scale_log2, -smL[it & 1][qi])) : 0.f;
+            p[c8] = pr;
+            ds[c8] = pr * (dpacc[r] - smD[it & 1][qi]);
+          }
+          smS[it & 1][kw][p2][lane] = pack8(ds);  // to the partner wave, in B-operand layout
+          const u32x4 pb = pack8(p);
+          const int r0 = 16 * p2 + 4 * half;
+#pragma unroll
+          for (int eb = 0; eb < DV / 32; ++eb)
+            dvacc[eb] = mfma32(lds_tr_frag(sO, OP, r0, r0 + 8, eb * 32), pb, dvacc[eb]);
+        }
+      }
+      qc = qn;
+    }
+    __syncthreads();  // matches the partner's final barrier
+    if (kvalid) {
+      uint16_t* dvrow = dv + ((size_t)b * S + sk) * rs_v + (size_t)h * DV;
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int e = i * 32 + 8 * g + 4 * half;
+          *(u32x2*)(dvrow + e) = u32x2{pack_bf2(dvacc[i][4 * g], dvacc[i][4 * g + 1]),
+                                       pack_bf2(dvacc[i][4 * g + 2], dvacc[i][4 * g + 3])};
+        }
+    }
+  } else {
+    f32x16 dkacc[DQK / 32];
+#pragma unroll
+    for (int i = 0; i < DQK / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dkacc[i][j] = 0.f;
+    // dK^T[d, s] += Q^T[d, q] dS[q, s] for the chunk of iteration `it`
+    auto dk_update = [&](int it) {
+      const uint16_t* sQ = (const uint16_t*)smQ[it % 3];
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
-        float p[8], ds[8];
-#pragma unroll
-        for (int c8 = 0; c8 < 8; ++c8) {
-          const int r = 8 * p2 + c8;
-          const int qi = acc_row(r, half);
-          const bool keep = (mw32[2 * qi] >> bsh) & 1u;  // FULL tiles have every in-range bit set
-          const float pr = keep ? fast_exp2(sacc[r] * scale_log2 - smL[buf][qi]) : 0.f;
-          p[c8] = pr;
-          ds[c8] = pr * (dpacc[r] - smD[buf][qi]);
-        }
-        const u32x4 pb = pack8(p), db = pack8(ds);
+        const u32x4 db = smS[it & 1][kw][p2][lane];
         const int r0 = 16 * p2 + 4 * half;
-#pragma unroll
-        for (int eb = 0; eb < DV / 32; ++eb)
-          dvacc[eb] = mfma32(lds_tr_frag(sO, OP, r0, r0 + 8, eb * 32), pb, dvacc[eb]);
 #pragma unroll
         for (int d2 = 0; d2 < DQK / 32; ++d2)
           dkacc[d2] = mfma32(lds_tr_frag(sQ, QP, r0, r0 + 8, d2 * 32), db, dkacc[d2]);
       }
+    };
+    bool prev = false;
+    int it = 0;
+    for (; qc < nchunks; ++it) {
+      store_small(it & 1);
+      wait_vmem();
+      __syncthreads();
+      const int qn = next_chunk(qc);
+      if (qn < nchunks) {
+        issue(qn, (it + 1) % 3, (it + 1) & 1);
+        load_small(qn);
+      }
+      if (prev) dk_update(it - 1);  // the chunk A finished before this barrier
+      prev = active(qc);
+      qc = qn;
     }
-    buf ^= 1;
-    qc = qn;
-  }
-
-  if (kvalid) {
-    uint16_t* dkrow = dk + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK;
-    uint16_t* dvrow = dv + ((size_t)b * S + sk) * rs_v + (size_t)h * DV;
+    __syncthreads();  // A's dS of the last chunk is visible
+    if (prev) dk_update(it - 1);
+    if (kvalid) {
+      uint16_t* dkrow = dk + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK;
 #pragma unroll
-    for (int i = 0; i < DQK / 32; ++i)
+      for (int i = 0; i < DQK / 32; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = i * 32 + 8 * g + 4 * half;
-        *(u32x2*)(dkrow + d) = u32x2{pack_bf2(dkacc[i][4 * g] * scale, dkacc[i][4 * g + 1] * scale),
-                                     pack_bf2(dkacc[i][4 * g + 2] * scale, dkacc[i][4 * g + 3] * scale)};
-      }
-#pragma unroll
-    for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int e = i * 32 + 8 * g + 4 * half;
-        *(u32x2*)(dvrow + e) = u32x2{pack_bf2(dvacc[i][4 * g], dvacc[i][4 * g + 1]),
-                                     pack_bf2(dvacc[i][4 * g + 2], dvacc[i][4 * g + 3])};
-      }
+        for (int g = 0; g < 4; ++g) {
+          const int d = i * 32 + 8 * g + 4 * half;
+          *(u32x2*)(dkrow + d) = u32x2{pack_bf2(dkacc[i][4 * g] * scale, dkacc[i][4 * g + 1] * scale),
+                                       pack_bf2(dkacc[i][4 * g + 2] * scale, dkacc[i][4 * g + 3] * scale)};
+        }
+    }
   }
 }
 
@@ -428,7 +485,7 @@ hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v
                                      const uint8_t* cls, int B, int S, int H, float scale, void* dk,
                                      void* dv, hipStream_t st) {
   const size_t nkv = (size_t)((S + 127) / 128) * B * H;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(256), 0, st, (const uint16_t*)q,
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, D, bits, cls, B,
                      S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv);
   return hipGetLastError();
