@@ -69,8 +69,11 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) unsigned char smQ[3][dkv::QBLK * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char smO[2][dkv::OBLK * 1024];
   __shared__ __attribute__((aligned(16))) u32x4 smS[2][4][2][64];  // dS, B-operand layout, per A wave
-  __shared__ float smL[2][QC], smD[2][QC];
-  __shared__ uint64_t smW[2][2][QC];
+  __shared__ __attribute__((aligned(16))) float smL[2][QC];
+  __shared__ __attribute__((aligned(16))) float smD[2][QC];
+  // mask words of the chunk's queries for the workgroup's two key tiles, split
+  // into 32-bit halves: [buf][tile][half][query]
+  __shared__ __attribute__((aligned(16))) uint32_t smW[2][2][2][QC];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -150,7 +153,9 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       smL[sb][tid] = pl;
       smD[sb][tid] = pd;
     } else if (tid < 3 * QC) {
-      smW[sb][(tid - QC) / QC][(tid - QC) % QC] = pw;
+      const int which = (tid - QC) / QC, qi = (tid - QC) % QC;
+      smW[sb][which][0][qi] = (uint32_t)pw;
+      smW[sb][which][1][qi] = (uint32_t)(pw >> 32);
     }
   };
   auto active = [&](int qc) { return chunk_cls(qc, kt_w - kt_lo) != 0 && s0 <= qc * QC + QC - 1; };
@@ -181,7 +186,6 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     for (int i = 0; i < DV / 32; ++i)
 #pragma unroll
       for (int j = 0; j < 16; ++j) dvacc[i][j] = 0.f;
-    const int bitpos = sk & 63;
     for (int it = 0; qc < nchunks; ++it) {
       store_small(it & 1);
       wait_vmem();
@@ -204,22 +208,38 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
         for (int ks = 0; ks < DV / 16; ++ks)
           dpacc = mfma32(*(const u32x4*)(sO + col * OP + ks * 16 + 8 * half), vf[ks], dpacc);
-        // this lane's bit of query qi's word: one 32-bit half, constant bit offset;
-        // FULL tiles have every in-range bit set
-        const uint32_t* mw32 = (const uint32_t*)smW[it & 1][kt_w - kt_lo] + (bitpos >> 5);
-        const int bsh = bitpos & 31;
+        // per-row scalars of this lane's 16 query rows (rows 8i + 4*half + r are
+        // 4-aligned runs): LSE, D and this wave's 32-bit half of each mask word
+        // (the half is fixed per wave: keys s0..s0+31 sit in one half).
+        // FULL tiles have every in-range bit set.
+        const int bsh = sk & 31;
+        const uint32_t* wrow = smW[it & 1][kt_w - kt_lo][(s0 >> 5) & 1];
         (void)q0;
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
+          float Lr[8], Dr[8];
+          uint32_t Wr[8];
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            const int r0 = 8 * (2 * p2 + i2) + 4 * half;
+            const f32x4 l4 = *(const f32x4*)&smL[it & 1][r0];
+            const f32x4 d4 = *(const f32x4*)&smD[it & 1][r0];
+            const u32x4 w4 = *(const u32x4*)&wrow[r0];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              Lr[4 * i2 + j] = l4[j];
+              Dr[4 * i2 + j] = d4[j];
+              Wr[4 * i2 + j] = w4[j];
+            }
+          }
           float p[8], ds[8];
 #pragma unroll
           for (int c8 = 0; c8 < 8; ++c8) {
             const int r = 8 * p2 + c8;
-            const int qi = acc_row(r, half);
-            const bool keep = (mw32[2 * qi] >> bsh) & 1u;
-            const float pr = keep ? fast_exp2(fmaf(sacc[r], scale_log2, -smL[it & 1][qi])) : 0.f;
+            const bool keep = (Wr[c8] >> bsh) & 1u;
+            const float pr = keep ? fast_exp2(fmaf(sacc[r], scale_log2, -Lr[c8])) : 0.f;
             p[c8] = pr;
-            ds[c8] = pr * (dpacc[r] - smD[it & 1][qi]);
+            ds[c8] = pr * (dpacc[r] - Dr[c8]);
           }
           smS[it & 1][kw][p2][lane] = pack8(ds);  // to the partner wave, in B-operand layout
           const u32x4 pb = pack8(p);
