@@ -68,6 +68,28 @@ def work(cfg, seg_np):
     }
 
 
+KERNEL_SRC = {"index_scores": "indexer.hip", "topk": "topk.hip", "attn_fwd": "attn_fwd.hip",
+              "attn_bwd_dq": "attn_bwd.hip", "attn_bwd_dkdv": "attn_bwd.hip"}
+KERNEL_SYM = {"index_scores": "index_scores_mfma_kernel", "topk": "topk_kernel", "attn_fwd": "attn_fwd_mfma_kernel",
+              "attn_bwd_dq": "attn_bwd_dq_kernel", "attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
+
+
+def measured_traffic(call, workload_key):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when it is missing or the kernel's source changed since."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", f"dsa_step_{workload_key}_hbm_traffic.txt")
+    src = os.path.join(ROOT, "sparse_attention_06_amd", "csrc", KERNEL_SRC[call])
+    if not os.path.exists(prof) or not os.path.exists(src):
+        return None
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(prof):
+        f = line.split()
+        if len(f) == 5 and f[0] == "traffic_bytes" and f[1] == KERNEL_SYM[call] and f[3] == "source_sha":
+            return int(f[2]) if f[4] == sha else None
+    return None
+
+
 def cpu_baseline(cfg, x_cpu, budget_s=15.0, max_rows=4096):
     """The float64 oracle on a bounded row sample of the same workload."""
     from oracle import dsa_oracle as ref
@@ -213,7 +235,7 @@ def main():
     kd = kernels[dom]
     roofline = {"bound": kd["bound"], "achieved": kd["achieved"],
                 "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS, "unit": kd["unit"],
-                "frac": kd["frac"], "traffic": None, "kernel": dom}
+                "frac": kd["frac"], "traffic": measured_traffic(dom, args.config), "kernel": dom}
 
     cpu = None
     if not args.no_cpu:

@@ -24,6 +24,10 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
+# Per-file extras. NaN inputs are outside the library's contract, so the
+# indexer's ReLU (a float max) needs no IEEE NaN canonicalisation; in the
+# attention kernels the same flags cost registers, so they stay off there.
+EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def sources():
@@ -32,7 +36,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *COMMON, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -11,8 +11,12 @@
 // head rows per 32-head block, so the ReLU and the w-weighted sum over heads
 // are in-lane float32 FMAs, with one exchange between the two lane halves.
 // q_idx[t] (Hi x Di bf16, 16 KB at 64 x 128) stays in VGPRs as MFMA A
-// fragments for the whole key loop. The 32-key k_idx tile is staged through
-// LDS once per workgroup (4 waves = 4 consecutive queries) and double buffered.
+// fragments for the whole key loop. A 64-key k_idx tile is copied straight
+// into padded LDS (global_load_lds) once per workgroup (4 waves = 4
+// consecutive queries) and double buffered. The two 32-key column blocks'
+// MFMAs are issued before either epilogue, so one epilogue overlaps the
+// other's MFMAs. Lane half 0 stores the first block's scores, half 1 the
+// second's.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,13 +28,14 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     const uint16_t* __restrict__ w, const int32_t* __restrict__ seg, int B, int S, int row0,
     int nrows, OutT* __restrict__ scores, int64_t ld) {
   constexpr int Hi = HB * 32, Di = KS * 16;
-  constexpr int TILE = 32;
-  constexpr int ROWB = Di * 2 + 16;          // padded LDS row: conflict-free b128 reads
-  constexpr int CPR = Di * 2 / 16;           // 16-byte chunks per key row
-  constexpr int CPT = (TILE * CPR + 255) / 256;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2][TILE * ROWB];
+  constexpr int TILE = 64;                   // keys per iteration: two 32-key MFMA column blocks
+  constexpr int SL = Di / 8 + 1;             // 16-byte slots per padded LDS key row
+  constexpr int ROWE = SL * 8;               // padded row pitch in elements (conflict-free b128 reads)
+  constexpr int NBLK = (TILE * SL + 63) / 64;  // 1 KB blocks per tile
+  constexpr int BI = (NBLK + 3) / 4;           // blocks per wave
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][NBLK * 1024];
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   const int nrb = (nrows + 3) / 4;
   // one batch row's row blocks share an XCD (and its L2 copy of k_idx); longest rows first
@@ -42,6 +47,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   const int t = row0 + r;
   const int t_last = row0 + min(nrows - 1, rb * 4 + 3);
   const int nkt = t_last / TILE + 1;
+  const uint16_t* kb_base = k_idx + (size_t)b * S * Di;
 
   u32x4 afrag[HB][KS];
   float wreg[HB][16];
@@ -61,64 +67,68 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     if (seg) seg_t = seg[(size_t)b * S + t];
   }
 
-  u32x4 pre[CPT];
-  auto gload = [&](int kt) {
+  // this wave's 1 KB blocks of the padded [64 rows][SL slots] tile; slots past
+  // a row's data or the tile copy a harmless chunk
+  auto issue = [&](int kt, int buf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = threadIdx.x + c * 256;
-      const int row = ci / CPR, cc = ci % CPR;
-      const int s = kt * TILE + row;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      if (ci < TILE * CPR && s < S) z = *(const u32x4*)(k_idx + ((size_t)b * S + s) * Di + cc * 8);
-      pre[c] = z;
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ci = threadIdx.x + c * 256;
-      if (ci < TILE * CPR) {
-        const int row = ci / CPR, cc = ci % CPR;
-        *(u32x4*)(&lds[buf][row * ROWB + cc * 16]) = pre[c];
+    for (int i = 0; i < BI; ++i) {
+      const int j = wid + i * 4;
+      if (j < NBLK) {
+        const int slot = j * 64 + lane;
+        const bool in = slot < TILE * SL;
+        const int row = in ? slot / SL : 0, c = in ? min(slot % SL, SL - 2) : 0;
+        const int s = min(kt * TILE + row, S - 1);
+        g2lds16(kb_base + (size_t)s * Di + c * 8, lds[buf] + j * 1024);
       }
     }
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  issue(0, 0);
   OutT* out_row = scores + ((size_t)b * nrows + r) * ld;
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nkt) gload(kt + 1);
+    wait_vmem();
+    __syncthreads();  // tile kt visible; every wave is done with the other buffer
+    if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
     const int s0 = kt * TILE;
     if (active && s0 <= t) {
-      const int s = s0 + col;
-      bool ok = s <= t;
-      if (seg && ok) ok = seg[(size_t)b * S + s] == seg_t;
-      if (__ballot(ok)) {
-        f32x16 acc[HB];
+      const uint16_t* sk = (const uint16_t*)lds[buf];
+      bool ok[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int s = s0 + sb * 32 + col;
+        ok[sb] = s <= t;
+        if (seg && ok[sb]) ok[sb] = seg[(size_t)b * S + s] == seg_t;
+      }
+      // both 32-key column blocks' MFMAs first: the epilogue of one overlaps the other's MFMAs
+      f32x16 acc[2][HB];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+          for (int i = 0; i < 16; ++i) acc[sb][hb][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4 bq = *(const u32x4*)(&lds[buf][col * ROWB + (ks * 16 + 8 * half) * 2]);
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-          for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(afrag[hb][ks], bq, acc[hb]);
+        for (int sb = 0; sb < 2; ++sb) {
+          const u32x4 bq = *(const u32x4*)(sk + (sb * 32 + col) * ROWE + ks * 16 + 8 * half);
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) acc[sb][hb] = mfma32(afrag[hb][ks], bq, acc[sb][hb]);
         }
-        float part = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-          for (int rr = 0; rr < 16; ++rr) part = fmaf(wreg[hb][rr], fmaxf(acc[hb][rr], 0.f), part);
-        part += __shfl_xor(part, 32);
-        if (half == 0 && ok) Elem<OutT>::store(out_row + s, part);
+          for (int rr = 0; rr < 16; ++rr)
+            part[rr & 3] = fmaf(wreg[hb][rr], fmaxf(acc[sb][hb][rr], 0.f), part[rr & 3]);
+        float tot = (part[0] + part[1]) + (part[2] + part[3]);
+        tot += __shfl_xor(tot, 32);
+        if (half == sb && ok[sb]) Elem<OutT>::store(out_row + s0 + sb * 32 + col, tot);
       }
     }
-    if (kt + 1 < nkt) lstore(buf ^ 1);
-    __syncthreads();
   }
 }
 
