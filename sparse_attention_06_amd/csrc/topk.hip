@@ -9,7 +9,8 @@
 // Selection rule: n = min(K, |valid(t)|) keys. Larger scores win. Among equal
 // scores the smaller key position wins, and -0 equals +0.
 //
-// One workgroup (4 waves) per query row:
+// One workgroup (4 waves) per query row. Rows short enough keep their keys in
+// LDS after one coalesced read; longer ones re-read global memory per pass.
 //   * |valid| <= K: every valid key is taken and the scores are never read.
 //   * otherwise the K-th largest key T is found exactly:
 //       1. min/max of the row's valid scores;
@@ -41,12 +42,16 @@ template <> struct ScoreLoad<uint16_t> {
   __device__ static __forceinline__ float get(const uint16_t* p, int s) { return bf2f(p[s]); }
 };
 
+constexpr int kCand = 256;  // candidates ranked directly (one per thread)
+
 struct TopkShared {
   uint32_t hist[kNB];
   uint32_t red_u[8];
   float red_f[8];
   uint32_t found_bin, found_above;
   uint32_t wave_gt[4], wave_eq[4];
+  uint32_t ncand, thresh;
+  uint32_t cand[kCand];
 };
 
 __device__ __forceinline__ uint32_t block_sum(uint32_t x, TopkShared& sh) {
@@ -119,13 +124,24 @@ __device__ void find_bin(TopkShared& sh, uint32_t need) {
   __syncthreads();
 }
 
-template <typename ST>
+// inverse of fkey for a valid (non-zero) key
+__device__ __forceinline__ float kfloat(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// One workgroup per row. All passes work on order-preserving u32 keys, with
+// key 0 marking a position outside valid(t) (every finite score maps above
+// 0x007fffff). With IN_LDS the row's keys are built once from one coalesced
+// read of the scores and every later pass reads LDS; otherwise (rows too long
+// for LDS) each pass recomputes them from global memory.
+template <typename ST, bool IN_LDS>
 __global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores, int64_t ld,
                                                    const int32_t* __restrict__ seg, int B, int S,
                                                    int K, int row0, int nrows,
                                                    int32_t* __restrict__ idx,
                                                    uint64_t* __restrict__ bits) {
   __shared__ TopkShared sh;
+  extern __shared__ uint32_t rowkeys[];  // IN_LDS: keys of positions [0, 64 * nw)
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x % B;
   const int r = nrows - 1 - (int)(blockIdx.x / B);  // longest rows first
@@ -137,8 +153,24 @@ __global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores
   const int L = t + 1;
   const int nw = (L + 63) / 64;
 
-  auto is_valid = [&](int s) -> bool { return s < L && (!segb || segb[s] == seg_t); };
+  auto gkey = [&](int s) -> uint32_t {  // key from global memory (0 if not valid)
+    if (s >= L || (segb && segb[s] != seg_t)) return 0u;
+    return fkey(ScoreLoad<ST>::get(row, s));
+  };
+  auto key = [&](int s) -> uint32_t {
+    if constexpr (IN_LDS) return rowkeys[s];
+    else return gkey(s);
+  };
 
+  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
+  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
+  if (!segb && L <= K) {
+    // causal-only row with at most K keys: every key 0..t, no score read
+    for (int i = tid; i < K; i += 256) idx_row[i] = i < L ? i : -1;
+    for (int w = tid; w < W; w += 256)
+      bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
+    return;
+  }
   uint32_t n_valid = (uint32_t)L;
   if (segb) {
     uint32_t c = 0;
@@ -146,47 +178,91 @@ __global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores
     n_valid = block_sum(c, sh);
   }
   const bool take_all = n_valid <= (uint32_t)K;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if constexpr (IN_LDS) {
+    // take-all rows never read scores: their keys only mark validity
+    for (int s = tid; s < 64 * nw; s += 256) {
+      const uint32_t kk = take_all ? ((s < L && (!segb || segb[s] == seg_t)) ? 1u : 0u) : gkey(s);
+      rowkeys[s] = kk;
+      if (kk) {
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+      }
+    }
+    __syncthreads();  // the row's keys are visible to every wave
+  }
   uint32_t T = 0, c_eq = 0;
   if (!take_all) {
-    float mn = INFINITY, mx = -INFINITY;
-    for (int s = tid; s < L; s += 256)
-      if (is_valid(s)) {
-        const float v = ScoreLoad<ST>::get(row, s);
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+    if constexpr (!IN_LDS) {
+      for (int s = tid; s < L; s += 256) {
+        const uint32_t kk = key(s);
+        if (kk) {
+          kmin = min(kmin, kk);
+          kmax = max(kmax, kk);
+        }
       }
-    block_minmax(mn, mx, sh);
+    }
+    block_uminmax(kmin, kmax, sh);
     uint32_t need = (uint32_t)K;
     uint32_t klo, khi;
-    if (!(mx > mn)) {
-      klo = khi = fkey(mx);
+    if (kmin == kmax) {
+      klo = khi = kmax;
     } else {
+      // value-linear bins: monotone in the score, so equal scores share a bin
+      const float mn = kfloat(kmin), mx = kfloat(kmax);
       const float inv = (float)kNB / (mx - mn);
       for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
       __syncthreads();
-      for (int s = tid; s < L; s += 256)
-        if (is_valid(s)) {
-          const float v = ScoreLoad<ST>::get(row, s);
-          const int bin = (int)fminf(fmaxf((v - mn) * inv, 0.f), (float)(kNB - 1));
+      for (int s = tid; s < L; s += 256) {
+        const uint32_t kk = key(s);
+        if (kk) {
+          const int bin = (int)fminf(fmaxf((kfloat(kk) - mn) * inv, 0.f), (float)(kNB - 1));
           atomicAdd(&sh.hist[bin], 1u);
         }
+      }
       __syncthreads();
       find_bin(sh, need);
       const int bstar = (int)sh.found_bin;
       need -= sh.found_above;
+      // the keys in bin b* form one contiguous key interval; collect them, and
+      // when few, take the need-th largest by direct ranking
+      if (tid == 0) sh.ncand = 0;
+      __syncthreads();
       klo = 0xffffffffu;
       khi = 0u;
-      for (int s = tid; s < L; s += 256)
-        if (is_valid(s)) {
-          const float v = ScoreLoad<ST>::get(row, s);
-          const int bin = (int)fminf(fmaxf((v - mn) * inv, 0.f), (float)(kNB - 1));
+      for (int s = tid; s < L; s += 256) {
+        const uint32_t kk = key(s);
+        if (kk) {
+          const int bin = (int)fminf(fmaxf((kfloat(kk) - mn) * inv, 0.f), (float)(kNB - 1));
           if (bin == bstar) {
-            const uint32_t kk = fkey(v);
             klo = min(klo, kk);
             khi = max(khi, kk);
+            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+            if (slot < (uint32_t)kCand) sh.cand[slot] = kk;
           }
         }
+      }
       block_uminmax(klo, khi, sh);
+      const uint32_t nc = sh.ncand;
+      if (nc <= (uint32_t)kCand) {
+        // candidate i is the threshold when #greater < need <= #greater + #equal
+        if (tid < (int)nc) {
+          const uint32_t ki = sh.cand[tid];
+          uint32_t gt = 0, eq = 0;
+          for (uint32_t j = 0; j < nc; ++j) {
+            const uint32_t kj = sh.cand[j];
+            gt += kj > ki;
+            eq += kj == ki;
+          }
+          if (gt < need && need <= gt + eq) {
+            sh.thresh = ki;  // every thread that writes holds the same key
+            sh.found_above = gt;
+          }
+        }
+        __syncthreads();
+        klo = khi = sh.thresh;
+        need -= sh.found_above;
+      }
     }
     // radix refinement on the key interval [klo, khi]
     while (klo != khi) {
@@ -195,11 +271,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores
       const int shift = nbits > 11 ? nbits - 11 : 0;
       for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
       __syncthreads();
-      for (int s = tid; s < L; s += 256)
-        if (is_valid(s)) {
-          const uint32_t kk = fkey(ScoreLoad<ST>::get(row, s));
-          if (kk >= klo && kk <= khi) atomicAdd(&sh.hist[(kk - klo) >> shift], 1u);
-        }
+      for (int s = tid; s < L; s += 256) {
+        const uint32_t kk = key(s);
+        if (kk >= klo && kk <= khi) atomicAdd(&sh.hist[(kk - klo) >> shift], 1u);
+      }
       __syncthreads();
       find_bin(sh, need);
       need -= sh.found_above;
@@ -213,19 +288,16 @@ __global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores
   }
 
   // ---- compaction: ascending index list and bitmask words
-  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
-  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
   const int wpw = (nw + 3) / 4;
   const int wa = wid * wpw, wb = min(nw, wa + wpw);
   auto classify = [&](int s, bool& gt, bool& eq) {
-    const bool v = is_valid(s);
+    const uint32_t kk = (IN_LDS || s < L) ? key(s) : 0u;
     if (take_all) {
-      gt = v;
+      gt = kk != 0u;
       eq = false;
     } else {
-      const uint32_t kk = v ? fkey(ScoreLoad<ST>::get(row, s)) : 0u;
-      gt = v && kk > T;
-      eq = v && kk == T;
+      gt = kk != 0u && kk > T;
+      eq = kk != 0u && kk == T;
     }
   };
   uint32_t my_gt = 0, my_eq = 0;
@@ -302,17 +374,35 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restr
   cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
 }
 
+// rows whose keys fit this much dynamic LDS keep them there
+constexpr size_t kTopkLdsMax = 128 * 1024;
+
+template <typename ST>
+static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
+                                int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
+  const size_t nrow_all = (size_t)nrows * B;
+  dim3 grid((unsigned)nrow_all), block(256);
+  const size_t shm = (size_t)mask_words(S) * 64 * sizeof(uint32_t);
+  if (shm <= kTopkLdsMax) {
+    if (shm > 64 * 1024) {
+      hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<ST, true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((topk_kernel<ST, true>), grid, block, shm, st, (const ST*)scores, ld, seg, B, S, K,
+                       row0, nrows, idx, bits);
+  } else {
+    hipLaunchKernelGGL((topk_kernel<ST, false>), grid, block, 0, st, (const ST*)scores, ld, seg, B, S, K,
+                       row0, nrows, idx, bits);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
                        int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
                        hipStream_t st) {
-  dim3 grid((unsigned)((size_t)nrows * B)), block(256);
-  if (score_bf16)
-    hipLaunchKernelGGL(topk_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)scores, ld, seg,
-                       B, S, K, row0, nrows, idx, bits);
-  else
-    hipLaunchKernelGGL(topk_kernel<float>, grid, block, 0, st, (const float*)scores, ld, seg, B, S,
-                       K, row0, nrows, idx, bits);
-  return hipGetLastError();
+  return score_bf16 ? launch_topk_t<uint16_t>(scores, ld, seg, B, S, K, row0, nrows, idx, bits, st)
+                    : launch_topk_t<float>(scores, ld, seg, B, S, K, row0, nrows, idx, bits, st);
 }
 
 hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int K,
