@@ -50,10 +50,6 @@ bool dtype_ok(dsa_dtype d) { return d == DSA_BF16 || d == DSA_FP32; }
 uint64_t* bits_of(void* mask) { return (uint64_t*)mask; }
 uint8_t* cls_of(void* mask, int B, int S) { return (uint8_t*)mask + dsa::bits_bytes(B, S); }
 
-// largest S: a build-mask row (S/64 words) must fit one workgroup's 64 KB of
-// dynamic LDS, with room to spare
-constexpr int kMaxS = 1 << 18;
-
 }  // namespace
 
 extern "C" {
@@ -96,7 +92,7 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
   REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
   REQ(B >= 1 && S >= 1 && Hi >= 1 && Di >= 1, DSA_ERR_INVALID_ARG,
       "sizes must be >= 1 (B=%d S=%d Hi=%d Di=%d)", B, S, Hi, Di);
-  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
   REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
       "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
   REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld < S=%d", (long long)ld, S);
@@ -123,7 +119,7 @@ dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, const
   REQ_PTR(mask);
   REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
   REQ(B >= 1 && S >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d K=%d)", B, S, K);
-  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
   REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
       "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
   REQ(row0 % DSA_TILE_Q == 0 && ((row0 + nrows) % DSA_TILE_Q == 0 || row0 + nrows == S),
@@ -146,7 +142,7 @@ dsa_status dsa_build_mask(const int32_t* idx, const int32_t* seg, int B, int S, 
   REQ_PTR(mask);
   REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
   REQ(B >= 1 && S >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d K=%d)", B, S, K);
-  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = dsa::launch_build_bits(idx, seg, B, S, K, bits_of(mask), st);
   if (e != hipSuccess) return hip_status(e, "dsa_build_mask");
@@ -158,7 +154,7 @@ dsa_status dsa_build_mask(const int32_t* idx, const int32_t* seg, int B, int S, 
 static dsa_status check_attn(int B, int S, int H, int Dqk, int Dv, float scale, dsa_dtype dtype) {
   REQ(B >= 1 && S >= 1 && H >= 1 && Dqk >= 1 && Dv >= 1, DSA_ERR_INVALID_ARG,
       "sizes must be >= 1 (B=%d S=%d H=%d Dqk=%d Dv=%d)", B, S, H, Dqk, Dv);
-  REQ(S <= kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, kMaxS);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
   REQ(dtype_ok(dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
   REQ(scale == scale && scale > 0.f, DSA_ERR_INVALID_ARG, "softmax_scale must be > 0");
   REQ(Dqk <= 256 && Dv <= 256, DSA_ERR_UNSUPPORTED, "head dims above 256 (Dqk=%d Dv=%d)", Dqk, Dv);

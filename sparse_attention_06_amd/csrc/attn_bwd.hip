@@ -74,8 +74,11 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   // mask words of the chunk's queries for the workgroup's two key tiles, split
   // into 32-bit halves: [buf][tile][half][query]
   __shared__ __attribute__((aligned(16))) uint32_t smW[2][2][2][QC];
+  // tile classes of the workgroup's two key tiles for every 128-query tile
+  __shared__ uint8_t scls[2][kMaxS / 128];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
   const int half = lane >> 5, col = lane & 31;
   const bool roleA = wid < 4;
   const int kw = wid & 3;
@@ -98,10 +101,12 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   const float* drow = D + ((size_t)b * H + h) * S;
 
   const int nchunks = (S + QC - 1) / QC;
-  auto chunk_cls = [&](int qc, int which) -> int {
-    const int kt = kt_lo + which;
-    return kt < NK ? cls[((size_t)b * NQ + (qc * QC) / 128) * NK + kt] : 0;
-  };
+  for (int i = tid; i < 2 * NQ; i += blockDim.x) {
+    const int which = i / NQ, qt = i % NQ, kt = kt_lo + which;
+    scls[which][qt] = kt < NK ? cls[((size_t)b * NQ + qt) * NK + kt] : 0;
+  }
+  __syncthreads();  // class column staged
+  auto chunk_cls = [&](int qc, int which) -> int { return scls[which][(qc * QC) / 128]; };
   auto next_chunk = [&](int qc) {
     int n = qc + 1;
     while (n < nchunks && chunk_cls(n, 0) == 0 && chunk_cls(n, 1) == 0) ++n;
@@ -337,14 +342,16 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   using dqk::QW;
   __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * QP];
   __shared__ __attribute__((aligned(1024))) uint16_t smV[2][TK * OP];
+  __shared__ uint8_t scls[2][kMaxTiles];  // tile classes of the workgroup's two 128-query tiles
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
-  const int Lb = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s query blocks share an XCD
-  const int bh = Lb / NQW;
-  const int qw = NQW - 1 - Lb % NQW;
+  // the query blocks of a (b, h) on one XCD (they share K/V), costliest first
+  int bh, qw;
+  grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
   const int b = bh / H, h = bh % H;
   const int tq = qw * QW + wid * 32 + col;
   const bool qvalid = tq < S;
@@ -395,9 +402,11 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
     for (int j = 0; j < 16; ++j) dqacc[i][j] = 0.f;
 
   const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
-  const uint8_t* cls0 = cls + ((size_t)b * NQ + qt0) * NK;
-  const uint8_t* cls1 = cls + ((size_t)b * NQ + qt1) * NK;
-  const uint8_t* clsw = cls + ((size_t)b * NQ + qt_w) * NK;
+  stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
+  stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
+  const uint8_t* cls0 = scls[0];
+  const uint8_t* cls1 = scls[1];
+  const uint8_t* clsw = scls[qt_w - qt0];
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
   auto next_tile = [&](int kt) {
     int n = kt + 1;
@@ -425,16 +434,25 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
     }
   };
 
+  // this lane's selection word of tile kt (FULL: all ones; EMPTY: none)
+  auto word = [&](int kt) -> uint64_t {
+    const int c = clsw[kt];
+    if (!qvalid || c == 0) return 0ull;
+    return c == 2 ? ~0ull : bits_q[kt];
+  };
+  __syncthreads();  // class rows staged
   int kt = next_tile(-1);
   if (kt <= kt_last) issue(kt, 0);
+  uint64_t mw = kt <= kt_last ? word(kt) : 0ull;
   int buf = 0;
   while (kt <= kt_last) {
     const int c = clsw[kt];
-    uint64_t mw = (qvalid && c == 2) ? ~0ull : 0ull;
-    if (c == 1 && qvalid) mw = bits_q[kt];
-    wait_vmem();
-    __syncthreads();
     const int kn = next_tile(kt);
+    wait_vmem();
+    __syncthreads();  // tile kt visible in `buf`; every wave is done with the other buffer
+    // the next selection word is loaded before the tile copies are issued, so
+    // that waiting for it does not wait for them
+    const uint64_t mw_n = kn <= kt_last ? word(kn) : 0ull;
     if (kn <= kt_last) issue(kn, buf ^ 1);
 
     if (c != 0 && __ballot(mw != 0ull)) {
@@ -473,6 +491,7 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
         }
       }
     }
+    mw = mw_n;
     buf ^= 1;
     kt = kn;
   }

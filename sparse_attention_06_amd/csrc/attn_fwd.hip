@@ -7,10 +7,11 @@
 // Description (flash attention driven by a dynamic 3-D index mask).
 //
 // MFMA kernel (bf16, Dqk = 192, Dv = 128). A workgroup is one (b, h, 256-query
-// block) with 8 waves (two per SIMD) of 32 queries each. It walks the 64-key
-// tiles up to the diagonal. Tiles that are EMPTY for both of its 128-query
-// tiles are skipped outright. A wave whose tile is EMPTY idles. PARTIAL tiles
-// read one u64 selection word per query.
+// block) with 8 waves of 32 queries each, two waves per SIMD. It walks the
+// 64-key tiles up to the diagonal. Tiles that are EMPTY for both of its
+// 128-query tiles are skipped outright. A wave whose own tile is EMPTY, or
+// whose 32 queries keep no key of the tile, idles on it. PARTIAL tiles read
+// one u64 selection word per query.
 //   S^T = K Q^T: keys on MFMA rows, queries on columns, so each lane owns one
 //   query and 32 of the tile's 64 logits. The online-softmax max and sum are
 //   in-lane, with one exchange between lane halves. Q stays in VGPRs.
@@ -18,11 +19,17 @@
 //   into the B operand. The key order inside each 16-wide k step is permuted
 //   to match the accumulator layout. V^T comes from the natural V tile in LDS
 //   through the gfx950 transposing LDS read, with the same permutation.
-// K/V tiles are double buffered in LDS and filled by direct global->LDS copies
-// (no staging registers). The next non-empty tile's copies are issued before
-// the current tile is computed. exp2 is the hardware
-// v_exp_f32, with the scale folded in (scale * log2 e). O is rescaled only when
-// a tile max passes the reference max by more than 2^8.
+// The tile walk reads the workgroup's tile-class rows from LDS, where they are
+// staged at start. K/V tiles are double buffered and filled by direct
+// global->LDS copies; the next tile's copies are issued right after the
+// barrier and land while the current tile is computed. The per-query
+// selection word of the next tile is loaded before those copies, so waiting
+// for it never waits for them.
+// LDS pitches: K rows 400 B (b128 reads of 16 consecutive rows hit distinct
+// banks), V rows 320 B (the four rows of a transposing read cover all 64
+// banks). exp2 is the hardware v_exp_f32, with the scale folded in
+// (scale * log2 e). O is rescaled only when a tile max passes the reference
+// max by more than 2^8.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,27 +40,26 @@ constexpr int DQK = 192, DV = 128, TK = 64;
 constexpr int NW = 8;                // waves per workgroup: 2 per SIMD
 constexpr int QW = 32 * NW;          // queries per workgroup (two 128-query tiles)
 constexpr int KS = DQK / 16;         // k steps of S^T
+constexpr int NB = 2;                // K/V tile buffers
 constexpr int KSL = DQK / 8 + 1;     // 16-byte slots per LDS K row (one pad slot): 400 B
-constexpr int VSL = DV / 8 + 1;      // ... per V row: 272 B
+constexpr int VSL = DV / 8 + 4;      // ... per V row (four pad slots): 320 B
 constexpr int KP = KSL * 8;          // LDS pitch of a K row (elements)
 constexpr int VP = VSL * 8;          // LDS pitch of a V row
 constexpr int KBLK = TK * KSL / 64;  // 1 KB blocks per K tile (25)
-constexpr int VBLK = TK * VSL / 64;  // ... per V tile (17)
+constexpr int VBLK = TK * VSL / 64;  // ... per V tile (20)
 constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;  // blocks per wave
 static_assert(TK * KSL % 64 == 0 && TK * VSL % 64 == 0, "tiles must be whole 1 KB blocks");
 }  // namespace fwd
 
-// One 64-key tile of the online softmax for a wave's 32 queries. Keys whose
-// selection bit is clear drop out (FULL tiles pass all-ones words). This
-// lane's keys are kb*32 + 8i + 4*half + r (i, r in 0..3); its query word is
-// passed pre-shifted by 4*half and split into halves, so each bit sits at the
-// constant position 8i + r of word kb.
-__device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV, const u32x4 (&qf)[fwd::KS],
-                                         uint32_t w0, uint32_t w1, float scale_log2, float& m, float& l,
-                                         f32x16 (&oacc)[4]) {
+// Scores phase of one 64-key tile for a wave's 32 queries: S^T into sacc,
+// masked (dropped keys become -inf), and the tile max of each query in log2
+// units. This lane's keys are kb*32 + 8i + 4*half + r (i, r in 0..3); with
+// the query word shifted right by 4*half, the bit of accumulator register r of
+// half kb sits at position 32*kb + 8*(r/4) + r%4.
+__device__ __forceinline__ float fwd_scores(const uint16_t* sK, const u32x4 (&qf)[fwd::KS], uint64_t mw,
+                                            bool full, float scale_log2, f32x16 (&sacc)[2]) {
   using namespace fwd;
   const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-  f32x16 sacc[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -65,25 +71,40 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV,
       const u32x4 a = *(const u32x4*)(sK + (kb * 32 + col) * KP + ks * 16 + 8 * half);
       sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
     }
-
-  // masked max over raw logits (the scale is positive, so it commutes with max)
   float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (full) {
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const uint32_t w = kb ? w1 : w0;
-      const float x = ((w >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[kb][r] : -INFINITY;
-      sacc[kb][r] = x;
-      tm[r & 3] = fmaxf(tm[r & 3], x);
+      for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], sacc[kb][r]);
+  } else {
+    const uint64_t mwh = mw >> (4 * half);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint32_t w = (uint32_t)(mwh >> (32 * kb));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // keep ? x : -inf as a bit select on an all-ones / all-zeros field
+        const int keep = __builtin_amdgcn_sbfe((int)w, 8 * (r >> 2) + (r & 3), 1);
+        const float x = __int_as_float((keep & __float_as_int(sacc[kb][r])) | (~keep & (int)0xff800000u));
+        sacc[kb][r] = x;
+        tm[r & 3] = fmaxf(tm[r & 3], x);
+      }
     }
-  float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;
+  }
+  const float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+  return fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;  // scale > 0 commutes with max
+}
 
-  // Lazy rescaling: probabilities are taken relative to a reference max m that
-  // only moves when the tile max exceeds it by more than 8 (log2 units), so
-  // p <= 2^8. O and l share the reference, so the result is unchanged; the
-  // O rescale (64 accumulator multiplies) becomes rare.
+// Update phase: online-softmax step with the masked logits of fwd_scores and
+// the PV MFMAs against the tile's V. Lazy rescaling: probabilities are taken
+// relative to a reference max m that only moves when the tile max exceeds it
+// by more than 8 (log2 units), so p <= 2^8. O and l share the reference, so
+// the result is unchanged; the O rescale (64 accumulator multiplies) is rare.
+__device__ __forceinline__ void fwd_update(const uint16_t* sV, const f32x16 (&sacc)[2], float tmax,
+                                           float scale_log2, float& m, float& l, f32x16 (&oacc)[4]) {
+  using namespace fwd;
+  const int lane = threadIdx.x & 63, half = lane >> 5;
   const bool bump = tmax > m + 8.f;
   if (__ballot(bump)) {
     const float m_new = bump ? tmax : m;
@@ -96,7 +117,6 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* sK, const uint16_t* sV,
     m = m_new;
   }
   const float neg_m = m == -INFINITY ? 0.f : -m;
-
   // O^T[e, q] += V^T[e, key] P^T[key, q]; V^T fragments read transposed from the V tile,
   // keys permuted inside each 16-key step to match the S^T accumulator rows
   float ls[4] = {0.f, 0.f, 0.f, 0.f};
@@ -124,19 +144,18 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
     float scale_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace fwd;
-  // double-buffered natural-layout K and V tiles, filled by direct global->LDS
-  // copies; V^T fragments come from ds_read_b64_tr_b16 on the V tile
-  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * KP];
-  __shared__ __attribute__((aligned(1024))) uint16_t smV[2][TK * VP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[NB][TK * KP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smV[NB][TK * VP];
+  __shared__ uint8_t scls[2][kMaxTiles];  // tile classes of the workgroup's two 128-query tiles
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
-  // all query blocks of one (b, h) on one XCD (they share K/V), longest first
-  const int Lb = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-  const int bh = Lb / NQW;
-  const int qw = NQW - 1 - Lb % NQW;
+  // the query blocks of a (b, h) on one XCD (they share K/V), costliest first
+  int bh, qw;
+  grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
   const int b = bh / H, h = bh % H;
   const int tq = qw * QW + wid * 32 + col;  // this lane's query
   const bool qvalid = tq < S;
@@ -145,6 +164,50 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;  // token strides
   const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
   const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
+
+  // this wave's 1 KB blocks of a tile: block j covers slots 64j .. 64j+63 of the
+  // padded [64 rows][KSL or VSL slots] layout; pad slots copy a harmless chunk.
+  // Row and chunk of each slot are fixed, so byte offsets within the tile's
+  // rows are computed once.
+  uint32_t koff[KI], voff[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int slot = (wid + i * NW) * 64 + lane;
+    koff[i] = (uint32_t)(((slot / KSL) * rs_qk + min(slot % KSL, KSL - 2) * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int slot = (wid + i * NW) * 64 + lane;
+    voff[i] = (uint32_t)(((slot / VSL) * rs_v + min(slot % VSL, DV / 8 - 1) * 8) * 2);
+  }
+  auto issue = [&](int kt, int buf) {
+    const char* kt_base = (const char*)(kbase + (size_t)kt * TK * rs_qk);
+    const char* vt_base = (const char*)(vbase + (size_t)kt * TK * rs_v);
+    const int lim = S - 1 - kt * TK;  // last in-range row of the tile
+    if (lim >= TK - 1) {
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+        if (wid + i * NW < KBLK) g2lds16(kt_base + koff[i], (char*)smK[buf] + (wid + i * NW) * 1024);
+#pragma unroll
+      for (int i = 0; i < VI; ++i)
+        if (wid + i * NW < VBLK) g2lds16(vt_base + voff[i], (char*)smV[buf] + (wid + i * NW) * 1024);
+    } else {  // ragged last tile: rows past S copy row S-1
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+        if (wid + i * NW < KBLK) {
+          const int row = ((wid + i * NW) * 64 + lane) / KSL;
+          const int dr = row - min(row, lim);
+          g2lds16(kt_base + koff[i] - (size_t)dr * rs_qk * 2, (char*)smK[buf] + (wid + i * NW) * 1024);
+        }
+#pragma unroll
+      for (int i = 0; i < VI; ++i)
+        if (wid + i * NW < VBLK) {
+          const int row = ((wid + i * NW) * 64 + lane) / VSL;
+          const int dr = row - min(row, lim);
+          g2lds16(vt_base + voff[i] - (size_t)dr * rs_v * 2, (char*)smV[buf] + (wid + i * NW) * 1024);
+        }
+    }
+  };
 
   u32x4 qf[KS];
 #pragma unroll
@@ -162,52 +225,42 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     for (int i = 0; i < 16; ++i) oacc[eb][i] = 0.f;
 
   const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
-  const uint8_t* cls0 = cls + ((size_t)b * NQ + qt0) * NK;
-  const uint8_t* cls1 = cls + ((size_t)b * NQ + qt1) * NK;
-  const uint8_t* clsw = cls + ((size_t)b * NQ + qt_w) * NK;
+  stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
+  stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
+  const uint8_t* cls0 = scls[0];
+  const uint8_t* cls1 = scls[1];
+  const uint8_t* clsw = scls[qt_w - qt0];
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
   auto next_tile = [&](int kt) {
     int n = kt + 1;
     while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
     return n;
   };
-  // this wave's 1 KB blocks of a tile: block j covers slots 64j .. 64j+63 of the
-  // padded [64 rows][KSL or VSL slots] layout; pad slots copy a harmless chunk
-  auto issue = [&](int kt, int buf) {
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int j = wid + i * NW;
-      if (j < KBLK) {
-        const int slot = j * 64 + lane, row = slot / KSL, c = min(slot % KSL, KSL - 2);
-        const int s = min(kt * TK + row, S - 1);
-        g2lds16(kbase + (size_t)s * rs_qk + c * 8, (char*)smK[buf] + j * 1024);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VI; ++i) {
-      const int j = wid + i * NW;
-      if (j < VBLK) {
-        const int slot = j * 64 + lane, row = slot / VSL, c = min(slot % VSL, VSL - 2);
-        const int s = min(kt * TK + row, S - 1);
-        g2lds16(vbase + (size_t)s * rs_v + c * 8, (char*)smV[buf] + j * 1024);
-      }
-    }
+  // this lane's selection word of tile kt (FULL: all ones; EMPTY: none)
+  auto word = [&](int kt) -> uint64_t {
+    const int c = clsw[kt];
+    if (!qvalid || c == 0) return 0ull;
+    return c == 2 ? ~0ull : bits_q[kt];
   };
 
+  f32x16 sacc[2];
+  __syncthreads();  // class rows staged
   int kt = next_tile(-1);
   if (kt <= kt_last) issue(kt, 0);
+  uint64_t mw = kt <= kt_last ? word(kt) : 0ull;
   int buf = 0;
   while (kt <= kt_last) {
+    const int kn = next_tile(kt);
     const int c = clsw[kt];
-    uint64_t mw = (qvalid && c == 2) ? ~0ull : 0ull;
-    if (c == 1 && qvalid) mw = bits_q[kt];
     wait_vmem();
     __syncthreads();  // tile kt visible in `buf`; every wave is done with the other buffer
-    const int kn = next_tile(kt);
-    if (kn <= kt_last) issue(kn, buf ^ 1);  // lands while this tile is computed
-    if (c != 0 && __ballot(mw != 0ull))
-      fwd_tile(smK[buf], smV[buf], qf, (uint32_t)(mw >> (4 * half)), (uint32_t)(mw >> (32 + 4 * half)),
-               scale_log2, m, l, oacc);
+    const uint64_t mw_n = kn <= kt_last ? word(kn) : 0ull;
+    if (kn <= kt_last) issue(kn, buf ^ 1);
+    if (c != 0 && __ballot(mw != 0ull)) {
+      const float tmax = fwd_scores(smK[buf], qf, mw, c == 2, scale_log2, sacc);
+      fwd_update(smV[buf], sacc, tmax, scale_log2, m, l, oacc);
+    }
+    mw = mw_n;
     buf ^= 1;
     kt = kn;
   }

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.hpp"
+
 namespace dsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -91,6 +93,34 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   const int per = nblocks / NX;
   if (bid >= per * NX) return bid;
   return (bid % NX) * per + bid / NX;
+}
+
+// Order of the query-major attention grids: logical block L -> (bh, qb) with
+// nq query blocks per (batch, head) of decreasing cost (qb = nq-1 first).
+// Blocks are taken in groups of two (batch, head) pairs; within a group the
+// costliest blocks of both pairs come first. The pairs of a group still run
+// together (they share an XCD's L2), and the last blocks dispatched anywhere
+// are short ones, so the causal triangle's long blocks do not end up alone
+// at the tail of the grid.
+__device__ __forceinline__ void grouped_order(int L, int nq, int nbh, int& bh, int& qb) {
+  constexpr int G = 2;
+  const int bh0 = L / (G * nq) * G;
+  const int g = min(G, nbh - bh0);
+  const int r = L - bh0 * nq;
+  qb = nq - 1 - r / g;
+  bh = bh0 + r % g;
+}
+
+// 64-key tiles of the longest sequence: the attention kernels stage a
+// workgroup's tile-class rows (one byte per tile) in LDS at start, so that
+// walking the tiles reads LDS instead of waiting on global loads that would
+// also wait for the tile copies in flight.
+constexpr int kMaxTiles = kMaxS / kTileK;
+
+// n bytes from global memory to LDS, by the whole workgroup; the caller
+// publishes them with a barrier
+__device__ __forceinline__ void stage_bytes(uint8_t* dst, const uint8_t* src, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src[i];
 }
 
 // ---------------------------------------------------------------- wave helpers

@@ -8,6 +8,12 @@
 
 namespace dsa {
 
+// Largest sequence length the library accepts. A build-mask row (S/64 words)
+// must fit one workgroup's 64 KB of dynamic LDS with room to spare, and the
+// attention kernels stage a workgroup's tile-class rows (S/64 bytes each) in
+// LDS.
+constexpr int kMaxS = 1 << 18;
+
 // scores: in_bf16 selects bf16 vs fp32 inputs, out_bf16 the score storage.
 hipError_t launch_index_scores_mfma(const void* q_idx, const void* k_idx, const void* w,
                                     const int32_t* seg, int B, int S, int Hi, int Di, int row0,
