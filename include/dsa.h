@@ -178,7 +178,8 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  *   mask      the forward's mask
  *   dq, dk    [B,S,H,Dqk] dtype out;  dv [B,S,H,Dv] dtype out
  *   workspace device scratch of at least dsa_bwd_workspace_bytes() bytes; it
- *             receives D = rowsum(dout * o) as float32 [B,H,S].
+ *             receives two float32 [B,H,S] arrays: D = rowsum(dout * o), then
+ *             lse * log2(e) (the row's log-sum-exp in base-2 units).
  * Same as dsa_sparse_attn_bwd_dq followed by dsa_sparse_attn_bwd_dkdv on the
  * same stream. Deterministic: no atomics.
  * ------------------------------------------------------------------------- */
@@ -190,9 +191,10 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
 
 /* The two halves of dsa_sparse_attn_bwd, one kernel each, for callers that
  * schedule them separately (say dK/dV on another stream after an event):
- *   _dq    query-major. Computes D into the workspace, then dq.
- *   _dkdv  key-major. Reads D from the workspace, so it must be ordered after
- *          _dq on the same workspace. Writes dk and dv.
+ *   _dq    query-major. Computes D and lse * log2(e) into the workspace,
+ *          then dq.
+ *   _dkdv  key-major. Reads both from the workspace, so it must be ordered
+ *          after _dq on the same workspace. Writes dk and dv.
  * Arguments as in dsa_sparse_attn_bwd. */
 dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
                                   const void* dout, const float* lse, const void* mask,

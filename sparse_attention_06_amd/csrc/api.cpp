@@ -63,7 +63,7 @@ size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv) {
   (void)Dqk;
   (void)Dv;
   if (B < 1 || S < 1 || H < 1) return 0;
-  return (size_t)B * H * S * sizeof(float);
+  return 2 * (size_t)B * H * S * sizeof(float);  // D, then lse * log2(e)
 }
 
 const char* dsa_status_string(dsa_status s) {

@@ -38,44 +38,68 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV, key-major. Workgroup = (b, h, 128 keys) with 8 waves in two roles,
-// two waves per SIMD:
-//   waves 0-3 ("A", 32 keys each, K/V fragments in VGPRs): S = Q K^T,
-//     dP = dO V^T, P, dS, and dV^T += dO^T P. A hands dS to its partner
-//     through LDS.
-//   waves 4-7 ("B", the same 32 keys as wave w-4): dK^T += Q^T dS, one
-//     32-query chunk behind A.
-// So B's MFMAs run while A does its softmax-gradient VALU work, and no MFMA is
-// done twice. Chunks with EMPTY tiles for the workgroup's keys are skipped.
-// Q chunks are triple buffered (B reads the previous one); dO and dS are
-// double buffered. All are filled by direct global->LDS copies.
+// dK / dV, key-major. Workgroup = (b, h, 128 keys) with 8 waves in two roles;
+// wave w and wave w+4 share a SIMD and the same 32 keys:
+//   waves 0-3 ("A", K/V fragments in VGPRs, raised issue priority):
+//     S = Q K^T and dP = dO V^T for a 32-query chunk, then P and
+//     dS = P (dP - D). P and dS go to LDS in MFMA B-operand layout.
+//   waves 4-7 ("B", dV^T and dK^T accumulators): dV^T += dO^T P and
+//     dK^T += Q^T dS, one chunk behind A.
+// Each role issues 20 MFMAs per chunk. A's softmax-gradient VALU work hides
+// under B's MFMAs: A has priority, so its MFMAs issue first after a barrier
+// and B's fill the matrix pipe while A works on P and dS. Chunks with EMPTY
+// tiles for the workgroup's keys are skipped.
+// A chunk's operands -- Q and dO rows, LSE and D, and the 32-bit halves of the
+// mask words of the workgroup's two key tiles -- all reach LDS through direct
+// global->LDS copies. A chunk is only ~1.3k MFMA cycles of work, less than a
+// global load's latency, so copies run two chunks ahead: four chunk buffers
+// (B reads the previous chunk, A the current one, one is in flight, one being
+// issued). Every wave issues exactly four copy instructions per chunk, so a
+// counted vmcnt wait finds the current chunk complete while the next one is
+// still in flight. P and dS are double buffered. The Q and dO tiles use the
+// swizzled padded layout that keeps both the row reads of A and the
+// transposing reads of B free of bank conflicts.
 // ---------------------------------------------------------------------------
 namespace dkv {
 constexpr int NW = 8;
-constexpr int QSL = bwd::DQK / 8 + 1, OSL = bwd::DV / 8 + 1;    // 16-byte slots per padded row
-constexpr int QBLK = (bwd::QC * QSL + 63) / 64;                 // 1 KB blocks per Q chunk (13)
-constexpr int OBLK = (bwd::QC * OSL + 63) / 64;                 // ... per dO chunk (9)
-constexpr int QI = (QBLK + NW - 1) / NW, OI = (OBLK + NW - 1) / NW;
-static_assert(QSL * 8 == bwd::QP && OSL * 8 == bwd::OP, "pitches");
+constexpr int NB = 4;                                          // chunk buffers
+constexpr int QSL = 28, OSL = 20;                              // 16-byte slots per swizzled row
+constexpr int QPX = QSL * 8, OPX = OSL * 8;                    // pitches (elements)
+constexpr int QBLK = bwd::QC * QSL / 64;                       // 1 KB blocks per Q chunk (14)
+constexpr int OBLK = bwd::QC * OSL / 64;                       // ... per dO chunk (10)
+// copy slots of a chunk: k = wid + NW*i, i < NSLOT: [0, QBLK) Q blocks,
+// [QBLK, QBLK+OBLK) dO blocks, then LSE/D, then the two mask-word tiles; the
+// remaining slots repeat Q blocks (same bytes to the same place)
+constexpr int NSLOT = 4;
+constexpr int K_LD = QBLK + OBLK, K_W = K_LD + 1, K_REP = K_W + 2;
+static_assert(bwd::QC * QSL % 64 == 0 && bwd::QC * OSL % 64 == 0, "chunks must be whole 1 KB blocks");
+static_assert(K_REP <= NW * NSLOT && NW * NSLOT - K_REP <= QBLK, "copy slots");
+static_assert(bwd::QC == 32, "one copy instruction moves a chunk's LSE and D, one a mask tile");
 }  // namespace dkv
 
 __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ D,
-    const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
-    float scale, float scale_log2, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    const uint16_t* __restrict__ dout, const float* __restrict__ ws, const uint64_t* __restrict__ bits,
+    const uint8_t* __restrict__ cls, int B, int S, int H, float scale, float scale_log2,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
   using namespace bwd;
   using dkv::NW;
-  __shared__ __attribute__((aligned(1024))) unsigned char smQ[3][dkv::QBLK * 1024];
-  __shared__ __attribute__((aligned(1024))) unsigned char smO[2][dkv::OBLK * 1024];
-  __shared__ __attribute__((aligned(16))) u32x4 smS[2][4][2][64];  // dS, B-operand layout, per A wave
-  __shared__ __attribute__((aligned(16))) float smL[2][QC];
-  __shared__ __attribute__((aligned(16))) float smD[2][QC];
-  // mask words of the chunk's queries for the workgroup's two key tiles, split
-  // into 32-bit halves: [buf][tile][half][query]
-  __shared__ __attribute__((aligned(16))) uint32_t smW[2][2][2][QC];
+  using dkv::NB;
+  __shared__ __attribute__((aligned(1024))) unsigned char smQ[NB][dkv::QBLK * 1024];
+  __shared__ __attribute__((aligned(1024))) unsigned char smO[NB][dkv::OBLK * 1024];
+  // P and dS of each A wave, B-operand layout: [buf][wave][p2][lane]
+  __shared__ __attribute__((aligned(16))) u32x4 smP[2][4][2][64];
+  __shared__ __attribute__((aligned(16))) u32x4 smS[2][4][2][64];
+  // per chunk: LSE in base-2 units of its 32 queries, then D
+  __shared__ __attribute__((aligned(16))) float smLD[NB][2 * QC];
+  // per chunk: 32-bit halves of the mask words of the workgroup's two key
+  // tiles: [buf][tile][half][query]
+  __shared__ __attribute__((aligned(16))) uint32_t smW[NB][2][2][QC];
   // tile classes of the workgroup's two key tiles for every 128-query tile
   __shared__ uint8_t scls[2][kMaxS / 128];
+  // the workgroup's non-empty chunks in order: chunk index | tile0 flag << 14 | tile1 flag << 15
+  __shared__ uint16_t clist[kMaxS / QC];
+  __shared__ int s_nlist;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
@@ -92,13 +116,13 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   const int s0 = kb0 + kw * 32;   // this wave pair's first key
   const int sk = s0 + col;        // this lane's key
   const bool kvalid = sk < S;
-  const int kt_w = s0 / 64;       // the pair's 64-key tile
   const int kt_lo = kb0 / 64;     // workgroup's first key tile
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
   const uint16_t* qbase = q + (size_t)b * S * rs_qk + (size_t)h * DQK;
   const uint16_t* obase = dout + (size_t)b * S * rs_v + (size_t)h * DV;
-  const float* lrow = lse + ((size_t)b * H + h) * S;
-  const float* drow = D + ((size_t)b * H + h) * S;
+  const float* drow = ws + ((size_t)b * H + h) * S;                       // D
+  const float* lrow = ws + (size_t)B * H * S + ((size_t)b * H + h) * S;   // LSE * log2(e)
+  const uint32_t* wbase = (const uint32_t*)bits + (size_t)b * S * W * 2;
 
   const int nchunks = (S + QC - 1) / QC;
   for (int i = tid; i < 2 * NQ; i += blockDim.x) {
@@ -106,73 +130,111 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     scls[which][qt] = kt < NK ? cls[((size_t)b * NQ + qt) * NK + kt] : 0;
   }
   __syncthreads();  // class column staged
-  auto chunk_cls = [&](int qc, int which) -> int { return scls[which][(qc * QC) / 128]; };
-  auto next_chunk = [&](int qc) {
-    int n = qc + 1;
-    while (n < nchunks && chunk_cls(n, 0) == 0 && chunk_cls(n, 1) == 0) ++n;
-    return n;
-  };
-  // chunk qc's Q / dO rows into buffers (qb, ob); slots past the chunk copy a harmless chunk
-  auto issue = [&](int qc, int qb, int ob) {
-    const int q0 = qc * QC;
-#pragma unroll
-    for (int i = 0; i < dkv::QI; ++i) {
-      const int j = wid + i * NW;
-      if (j < dkv::QBLK) {
-        const int slot = j * 64 + lane;
-        const bool in = slot < QC * dkv::QSL;
-        const int row = in ? slot / dkv::QSL : 0, c = in ? min(slot % dkv::QSL, dkv::QSL - 2) : 0;
-        const int t = min(q0 + row, S - 1);
-        g2lds16(qbase + (size_t)t * rs_qk + c * 8, smQ[qb] + j * 1024);
-      }
+  if (wid == 0) {   // compact the non-empty chunks from the diagonal on
+    int cnt = 0;
+    for (int base = kb0 / QC; base < nchunks; base += 64) {
+      const int qc = base + lane;
+      int fl = 0;
+      if (qc < nchunks) fl = (scls[0][qc * QC / 128] != 0) | ((scls[1][qc * QC / 128] != 0) << 1);
+      const uint64_t m = __ballot(fl != 0);
+      if (fl) clist[cnt + lanes_below(m)] = (uint16_t)(qc | (fl << 14));
+      cnt += __popcll(m);
     }
-#pragma unroll
-    for (int i = 0; i < dkv::OI; ++i) {
-      const int j = wid + i * NW;
-      if (j < dkv::OBLK) {
-        const int slot = j * 64 + lane;
-        const bool in = slot < QC * dkv::OSL;
-        const int row = in ? slot / dkv::OSL : 0, c = in ? min(slot % dkv::OSL, dkv::OSL - 2) : 0;
-        const int t = min(q0 + row, S - 1);
-        g2lds16(obase + (size_t)t * rs_v + c * 8, smO[ob] + j * 1024);
-      }
-    }
-  };
-  // per-query scalars of chunk qc: LSE (log2 units), D, and the two mask words
-  float pl = 0.f, pd = 0.f;
-  uint64_t pw = 0ull;
-  auto load_small = [&](int qc) {
-    const int q0 = qc * QC;
-    if (tid < QC) {
-      const int t = q0 + tid;
-      pl = t < S ? lrow[t] * 1.4426950408889634f : INFINITY;
-      pd = t < S ? drow[t] : 0.f;
-    } else if (tid < 3 * QC) {
-      const int qi = (tid - QC) % QC, which = (tid - QC) / QC;
-      const int t = q0 + qi, kt = kt_lo + which;
-      pw = (t < S && kt < NK) ? bits[((size_t)b * S + t) * W + kt] : 0ull;
-    }
-  };
-  auto store_small = [&](int sb) {
-    if (tid < QC) {
-      smL[sb][tid] = pl;
-      smD[sb][tid] = pd;
-    } else if (tid < 3 * QC) {
-      const int which = (tid - QC) / QC, qi = (tid - QC) % QC;
-      smW[sb][which][0][qi] = (uint32_t)pw;
-      smW[sb][which][1][qi] = (uint32_t)(pw >> 32);
-    }
-  };
-  auto active = [&](int qc) { return chunk_cls(qc, kt_w - kt_lo) != 0 && s0 <= qc * QC + QC - 1; };
-
-  int qc = kb0 / QC;
-  if (chunk_cls(qc, 0) == 0 && chunk_cls(qc, 1) == 0) qc = next_chunk(qc);
-  if (qc < nchunks) {
-    issue(qc, 0, 0);
-    load_small(qc);
+    if (lane == 0) s_nlist = cnt;
   }
+  __syncthreads();
+  const int nlist = s_nlist;
+  auto entry = [&](int j) -> int { return j < nlist ? (int)clist[j] : -1; };
+  // this wave pair's keys take part in the chunk: its key tile is non-empty
+  // there and the chunk reaches the pair's first key (causal)
+  auto active = [&](int e) {
+    return ((e >> (14 + (kw >> 1))) & 1) != 0 && s0 <= (e & 0x3FFF) * QC + QC - 1;
+  };
+
+  // source offsets (elements from the chunk's first row) of this lane's Q / dO
+  // slots: swizzled padded rows, pad slots copy the row's last chunk
+  auto slot_src = [&](int kslot, int& row) -> uint32_t {
+    if (kslot < dkv::QBLK || kslot >= dkv::K_REP) {
+      const int j = kslot < dkv::QBLK ? kslot : kslot - dkv::K_REP;
+      const int slot = j * 64 + lane, pc = slot % dkv::QSL;
+      row = slot / dkv::QSL;
+      const int c = pc < DQK / 8 ? swz_chunk(row, pc) : DQK / 8 - 1;
+      return (uint32_t)(row * rs_qk + c * 8);
+    }
+    const int slot = (kslot - dkv::QBLK) * 64 + lane, pc = slot % dkv::OSL;
+    row = slot / dkv::OSL;
+    const int c = pc < DV / 8 ? swz_chunk(row, pc) : DV / 8 - 1;
+    return (uint32_t)(row * rs_v + c * 8);
+  };
+  uint32_t soff[dkv::NSLOT];
+#pragma unroll
+  for (int i = 0; i < dkv::NSLOT; ++i) {
+    int row;
+    soff[i] = slot_src(wid + NW * i, row);
+  }
+  // chunk qc's copies into buffer bi: exactly NSLOT instructions per wave
+  auto issue = [&](int qc, int bi) {
+    const int q0 = qc * QC;
+    const bool ragged = q0 + QC > S;  // rows past S copy row S-1
+#pragma unroll
+    for (int i = 0; i < dkv::NSLOT; ++i) {
+      const int kslot = wid + NW * i;
+      if (kslot < dkv::QBLK || kslot >= dkv::K_REP) {
+        const int j = kslot < dkv::QBLK ? kslot : kslot - dkv::K_REP;
+        uint32_t off = soff[i];
+        if (ragged) {
+          int row;
+          off = slot_src(kslot, row);
+          off -= (uint32_t)((row - min(row, S - 1 - q0)) * rs_qk);
+        }
+        g2lds16_async(qbase + (size_t)q0 * rs_qk + off, smQ[bi] + j * 1024);
+      } else if (kslot < dkv::K_LD) {
+        uint32_t off = soff[i];
+        if (ragged) {
+          int row;
+          off = slot_src(kslot, row);
+          off -= (uint32_t)((row - min(row, S - 1 - q0)) * rs_v);
+        }
+        g2lds16_async(obase + (size_t)q0 * rs_v + off, smO[bi] + (kslot - dkv::QBLK) * 1024);
+      } else if (kslot == dkv::K_LD) {
+        const int t = min(q0 + col, S - 1);
+        g2lds4_async(half ? drow + t : lrow + t, smLD[bi]);
+      } else {
+        const int which = kslot - dkv::K_W;
+        const int t = min(q0 + col, S - 1), kt = min(kt_lo + which, NK - 1);
+        g2lds4_async(wbase + ((size_t)t * W + kt) * 2 + half, smW[bi][which]);
+      }
+    }
+  };
+  // The wave that copies a mask tile clears, once the copy has landed, the
+  // rows of a ragged last chunk that lie past S (they hold row S-1's words).
+  auto fix_ragged = [&](int qc, int bi) {
+    const int q0 = qc * QC;
+    if (q0 + QC <= S) return;
+#pragma unroll
+    for (int i = 0; i < dkv::NSLOT; ++i) {
+      const int kslot = wid + NW * i;
+      if (kslot >= dkv::K_W && kslot < dkv::K_REP && q0 + col >= S) smW[bi][kslot - dkv::K_W][half][col] = 0u;
+    }
+  };
+
+  int e0 = entry(0), e1 = entry(1), e2 = entry(2);  // current, next, and the one after
+  if (e0 >= 0) issue(e0 & 0x3FFF, 0);
+  if (e1 >= 0) issue(e1 & 0x3FFF, 1);
+  // chunk e0 (issued two chunks back) complete, then published; e1's copies
+  // may still be in flight
+  auto publish = [&](int it) {
+    if (e1 >= 0)
+      wait_vmem_n<dkv::NSLOT>();
+    else
+      wait_vmem();
+    fix_ragged(e0 & 0x3FFF, it % NB);
+    lds_barrier();
+  };
 
   if (roleA) {
+    __builtin_amdgcn_s_setprio(1);
+    // K/V fragments of this lane's key
     u32x4 kf[DQK / 16], vf[DV / 16];
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) {
@@ -186,40 +248,40 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       if (kvalid) z = *(const u32x4*)(v + ((size_t)b * S + sk) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
       vf[ks] = z;
     }
-    f32x16 dvacc[DV / 32];
+    wait_vmem();  // once: the loop's waits then only concern chunk copies
+    // byte offsets of this lane's b128 fragment rows in the swizzled Q / dO
+    // chunks, for even and odd k steps (k step ks adds 64 * (ks / 2) bytes)
+    const int u = (col >> 2) & 3;
+    uint32_t qa[2], oa[2];
 #pragma unroll
-    for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dvacc[i][j] = 0.f;
-    for (int it = 0; qc < nchunks; ++it) {
-      store_small(it & 1);
-      wait_vmem();
-      __syncthreads();  // chunk qc visible in buffers (it%3, it%2)
-      const int qn = next_chunk(qc);
-      if (qn < nchunks) {
-        issue(qn, (it + 1) % 3, (it + 1) & 1);
-        load_small(qn);
-      }
-      if (active(qc)) {
-        const int q0 = qc * QC;
-        const uint16_t* sQ = (const uint16_t*)smQ[it % 3];
-        const uint16_t* sO = (const uint16_t*)smO[it & 1];
+    for (int par = 0; par < 2; ++par) {
+      qa[par] = (uint32_t)(col * dkv::QPX * 2 + 16 * ((2 * par + half) ^ u));
+      oa[par] = (uint32_t)(col * dkv::OPX * 2 + 16 * ((2 * par + half) ^ u));
+    }
+    const int bsh = sk & 31;
+    const int wsel = (kw >> 1), hsel = (s0 >> 5) & 1;  // the pair's key tile and word half
+    for (int it = 0; e0 >= 0; ++it) {
+      publish(it);
+      if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
+      const int e3 = entry(it + 3);
+      if (active(e0)) {
+        const int bi = it % NB, qc = e0 & 0x3FFF;
+        const char* sQ = (const char*)smQ[bi];
+        const char* sO = (const char*)smO[bi];
         f32x16 sacc, dpacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
 #pragma unroll
         for (int ks = 0; ks < DQK / 16; ++ks)
-          sacc = mfma32(*(const u32x4*)(sQ + col * QP + ks * 16 + 8 * half), kf[ks], sacc);
+          sacc = mfma32(*(const u32x4*)(sQ + qa[ks & 1] + 64 * (ks >> 1)), kf[ks], sacc);
 #pragma unroll
         for (int ks = 0; ks < DV / 16; ++ks)
-          dpacc = mfma32(*(const u32x4*)(sO + col * OP + ks * 16 + 8 * half), vf[ks], dpacc);
+          dpacc = mfma32(*(const u32x4*)(sO + oa[ks & 1] + 64 * (ks >> 1)), vf[ks], dpacc);
         // per-row scalars of this lane's 16 query rows (rows 8i + 4*half + r are
-        // 4-aligned runs): LSE, D and this wave's 32-bit half of each mask word
-        // (the half is fixed per wave: keys s0..s0+31 sit in one half).
-        // FULL tiles have every in-range bit set.
-        const int bsh = sk & 31;
-        const uint32_t* wrow = smW[it & 1][kt_w - kt_lo][(s0 >> 5) & 1];
-        (void)q0;
+        // 4-aligned runs): base-2 LSE, D and this pair's 32-bit half of each
+        // mask word. FULL tiles have every in-range bit set.
+        const uint32_t* wrow = smW[bi][wsel][hsel];
+        (void)qc;
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
           float Lr[8], Dr[8];
@@ -227,8 +289,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2) {
             const int r0 = 8 * (2 * p2 + i2) + 4 * half;
-            const f32x4 l4 = *(const f32x4*)&smL[it & 1][r0];
-            const f32x4 d4 = *(const f32x4*)&smD[it & 1][r0];
+            const f32x4 l4 = *(const f32x4*)&smLD[bi][r0];
+            const f32x4 d4 = *(const f32x4*)&smLD[bi][QC + r0];
             const u32x4 w4 = *(const u32x4*)&wrow[r0];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -241,77 +303,102 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
           for (int c8 = 0; c8 < 8; ++c8) {
             const int r = 8 * p2 + c8;
-            const bool keep = (Wr[c8] >> bsh) & 1u;
-            const float pr = keep ? fast_exp2(fmaf(sacc[r], scale_log2, -Lr[c8])) : 0.f;
+            // keep ? P : 0 as a bit select on an all-ones / all-zeros field
+            const int keep = __builtin_amdgcn_sbfe((int)Wr[c8], bsh, 1);
+            const float pr =
+                __int_as_float(keep & __float_as_int(fast_exp2(fmaf(sacc[r], scale_log2, -Lr[c8]))));
             p[c8] = pr;
             ds[c8] = pr * (dpacc[r] - Dr[c8]);
           }
-          smS[it & 1][kw][p2][lane] = pack8(ds);  // to the partner wave, in B-operand layout
-          const u32x4 pb = pack8(p);
-          const int r0 = 16 * p2 + 4 * half;
-#pragma unroll
-          for (int eb = 0; eb < DV / 32; ++eb)
-            dvacc[eb] = mfma32(lds_tr_frag(sO, OP, r0, r0 + 8, eb * 32), pb, dvacc[eb]);
+          smP[it & 1][kw][p2][lane] = pack8(p);
+          smS[it & 1][kw][p2][lane] = pack8(ds);
         }
       }
-      qc = qn;
+      e0 = e1;
+      e1 = e2;
+      e2 = e3;
     }
-    __syncthreads();  // matches the partner's final barrier
-    if (kvalid) {
-      uint16_t* dvrow = dv + ((size_t)b * S + sk) * rs_v + (size_t)h * DV;
-#pragma unroll
-      for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int e = i * 32 + 8 * g + 4 * half;
-          *(u32x2*)(dvrow + e) = u32x2{pack_bf2(dvacc[i][4 * g], dvacc[i][4 * g + 1]),
-                                       pack_bf2(dvacc[i][4 * g + 2], dvacc[i][4 * g + 3])};
-        }
-    }
+    lds_barrier();  // matches B's final barrier
   } else {
-    f32x16 dkacc[DQK / 32];
+    f32x16 dkacc[DQK / 32], dvacc[DV / 32];
 #pragma unroll
     for (int i = 0; i < DQK / 32; ++i)
 #pragma unroll
       for (int j = 0; j < 16; ++j) dkacc[i][j] = 0.f;
-    // dK^T[d, s] += Q^T[d, q] dS[q, s] for the chunk of iteration `it`
-    auto dk_update = [&](int it) {
-      const uint16_t* sQ = (const uint16_t*)smQ[it % 3];
+#pragma unroll
+    for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) dvacc[i][j] = 0.f;
+    // byte offsets of this lane's transposing reads in the swizzled Q / dO
+    // chunks: rows r0 + j/4 and r0 + 8 + j/4 (r0 = 16*p2 + 4*half), 4-column
+    // group j%4 of the lane's 16-column half; column block n adds 64*n bytes
+    const int j16 = lane & 15, g = (lane >> 4) & 1;
+    uint32_t qt[2][2], ot[2][2];
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int row = 16 * p2 + 4 * half + 8 * kk + (j16 >> 2);
+        const int chunk = (2 * g + ((j16 & 3) >> 1)) ^ ((row >> 2) & 3);
+        qt[p2][kk] = (uint32_t)(row * dkv::QPX * 2 + 16 * chunk + 8 * (j16 & 1));
+        ot[p2][kk] = (uint32_t)(row * dkv::OPX * 2 + 16 * chunk + 8 * (j16 & 1));
+      }
+    auto tr = [&](const char* base, uint32_t oa_, uint32_t ob_) -> u32x4 {
+      const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + oa_));
+      const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + ob_));
+      const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+      return u32x4{ux[0], ux[1], uy[0], uy[1]};
+    };
+    // dV^T[e, s] += dO^T[e, q] P[q, s] and dK^T[d, s] += Q^T[d, q] dS[q, s] for
+    // the chunk of iteration `it`; the query order inside each 16-query step
+    // matches the A wave's accumulator rows
+    auto update = [&](int it) {
+      const char* sQ = (const char*)smQ[it % NB];
+      const char* sO = (const char*)smO[it % NB];
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
+        const u32x4 pb = smP[it & 1][kw][p2][lane];
         const u32x4 db = smS[it & 1][kw][p2][lane];
-        const int r0 = 16 * p2 + 4 * half;
+#pragma unroll
+        for (int eb = 0; eb < DV / 32; ++eb)
+          dvacc[eb] = mfma32(tr(sO + 64 * eb, ot[p2][0], ot[p2][1]), pb, dvacc[eb]);
 #pragma unroll
         for (int d2 = 0; d2 < DQK / 32; ++d2)
-          dkacc[d2] = mfma32(lds_tr_frag(sQ, QP, r0, r0 + 8, d2 * 32), db, dkacc[d2]);
+          dkacc[d2] = mfma32(tr(sQ + 64 * d2, qt[p2][0], qt[p2][1]), db, dkacc[d2]);
       }
     };
     bool prev = false;
     int it = 0;
-    for (; qc < nchunks; ++it) {
-      store_small(it & 1);
-      wait_vmem();
-      __syncthreads();
-      const int qn = next_chunk(qc);
-      if (qn < nchunks) {
-        issue(qn, (it + 1) % 3, (it + 1) & 1);
-        load_small(qn);
-      }
-      if (prev) dk_update(it - 1);  // the chunk A finished before this barrier
-      prev = active(qc);
-      qc = qn;
+    for (; e0 >= 0; ++it) {
+      publish(it);
+      if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
+      const int e3 = entry(it + 3);
+      if (prev) update(it - 1);  // the chunk A finished before this barrier
+      prev = active(e0);
+      e0 = e1;
+      e1 = e2;
+      e2 = e3;
     }
-    __syncthreads();  // A's dS of the last chunk is visible
-    if (prev) dk_update(it - 1);
+    lds_barrier();  // A's P and dS of the last chunk are visible
+    if (prev) update(it - 1);
     if (kvalid) {
       uint16_t* dkrow = dk + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK;
 #pragma unroll
       for (int i = 0; i < DQK / 32; ++i)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = i * 32 + 8 * g + 4 * half;
-          *(u32x2*)(dkrow + d) = u32x2{pack_bf2(dkacc[i][4 * g] * scale, dkacc[i][4 * g + 1] * scale),
-                                       pack_bf2(dkacc[i][4 * g + 2] * scale, dkacc[i][4 * g + 3] * scale)};
+        for (int gg = 0; gg < 4; ++gg) {
+          const int d = i * 32 + 8 * gg + 4 * half;
+          *(u32x2*)(dkrow + d) = u32x2{pack_bf2(dkacc[i][4 * gg] * scale, dkacc[i][4 * gg + 1] * scale),
+                                       pack_bf2(dkacc[i][4 * gg + 2] * scale, dkacc[i][4 * gg + 3] * scale)};
+        }
+      uint16_t* dvrow = dv + ((size_t)b * S + sk) * rs_v + (size_t)h * DV;
+#pragma unroll
+      for (int i = 0; i < DV / 32; ++i)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          const int e = i * 32 + 8 * gg + 4 * half;
+          *(u32x2*)(dvrow + e) = u32x2{pack_bf2(dvacc[i][4 * gg], dvacc[i][4 * gg + 1]),
+                                       pack_bf2(dvacc[i][4 * gg + 2], dvacc[i][4 * gg + 3])};
         }
     }
   }
@@ -393,7 +480,11 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
     }
   }
   Dq += __shfl_xor(Dq, 32);
-  if (qvalid && half == 0) D[((size_t)b * H + h) * S + tq] = Dq;
+  // the workspace holds D, then the log-sum-exp in base-2 units, for the key-major kernel
+  if (qvalid && half == 0) {
+    D[((size_t)b * H + h) * S + tq] = Dq;
+    D[(size_t)B * H * S + ((size_t)b * H + h) * S + tq] = Lq;
+  }
 
   f32x16 dqacc[DQK / 32];
 #pragma unroll
@@ -523,10 +614,11 @@ hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v
                                      const float* lse, const float* D, const uint64_t* bits,
                                      const uint8_t* cls, int B, int S, int H, float scale, void* dk,
                                      void* dv, hipStream_t st) {
+  (void)lse;  // the dQ kernel left lse * log2(e) in the workspace after D
   const size_t nkv = (size_t)((S + 127) / 128) * B * H;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, D, bits, cls, B,
-                     S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv);
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, D, bits, cls, B, S, H,
+                     scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv);
   return hipGetLastError();
 }
 

@@ -37,7 +37,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
   float Dt = 0.f;
   for (int e = lane; e < Dv; e += 64) Dt = fmaf(Elem<T>::load(o + row * Dv + e), os[wid][e], Dt);
   Dt = wave_sumf(Dt);
-  if (lane == 0) D[((size_t)b * H + h) * S + t] = Dt;
+  if (lane == 0) {
+    D[((size_t)b * H + h) * S + t] = Dt;
+    D[(size_t)B * H * S + ((size_t)b * H + h) * S + t] = L * 1.4426950408889634f;
+  }
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const uint64_t* brow = bits + ((size_t)b * S + t) * W;
   for (int w = 0; w <= t / 64; ++w) {

@@ -72,6 +72,33 @@ __device__ __forceinline__ u32x4 lds_tr_frag(const uint16_t* X, int pitch, int k
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// Tiles whose rows are read both ways -- b128 fragment reads of 16
+// consecutive rows at one chunk, and transposing reads of 4 rows x 4 chunks --
+// are stored with a padded pitch and the low two bits of each 16-byte chunk
+// index XORed with bits 2-3 of the row: chunk c of row r sits at chunk
+// c ^ ((r >> 2) & 3). With a pitch of 20 chunks (128-element rows) or 28
+// chunks (192-element rows), both read patterns touch 16 distinct 4-bank
+// groups of the 64 LDS banks.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// b128 A/B fragment of a swizzled tile: row r, logical chunk c (8 elements)
+__device__ __forceinline__ u32x4 lds_frag_x(const uint16_t* X, int pitch, int r, int c) {
+  return *(const u32x4*)(X + r * pitch + swz_chunk(r, c) * 8);
+}
+
+// lds_tr_frag on a swizzled tile (kr0, kr1 multiples of 4, mbase of 32)
+__device__ __forceinline__ u32x4 lds_tr_frag_x(const uint16_t* X, int pitch, int kr0, int kr1, int mbase) {
+  const int lane = threadIdx.x & 63, j = lane & 15;
+  const int m0 = mbase + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+  const int ra = kr0 + (j >> 2), rb = kr1 + (j >> 2);
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16_ptr)(X + ra * pitch + swz_chunk(ra, m0 >> 3) * 8 + (m0 & 7)));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16_ptr)(X + rb * pitch + swz_chunk(rb, m0 >> 3) * 8 + (m0 & 7)));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
@@ -82,7 +109,49 @@ __device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
                                    (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
 }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// 4 bytes per lane (global_load_lds_dword): lane l's word lands at lds_base + 4*l
+__device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
+                                   (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
+}
+// The same copies issued through inline assembly. The compiler then does not
+// track them as LDS writes, so it inserts no wait for every outstanding load
+// before LDS reads it cannot prove disjoint from them (with dynamically indexed
+// buffers it never can). The caller waits for them explicitly (wait_vmem or
+// wait_vmem_n) before the barrier that publishes them; waits the compiler
+// computes for its own loads stay correct, since loads complete in issue order.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+// M0 (the LDS base of the copy) is saved and restored around it.
+__device__ __forceinline__ void g2lds16_async(const void* gsrc, void* lds_base) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(gsrc), "s"(lds_addr(lds_base)) : "memory");
+}
+__device__ __forceinline__ void g2lds4_async(const void* gsrc, void* lds_base) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+               "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(gsrc), "s"(lds_addr(lds_base)) : "memory");
+}
+// Wait until at most N vector-memory instructions of this wave are in flight
+// (they complete in issue order). Issued through the builtin, so that the
+// compiler's own wait insertion knows the loads before it are complete.
+// Encoding (gfx9): vmcnt in bits 3:0 and 15:14; expcnt (bits 6:4) and lgkmcnt
+// (bits 11:8) left at their maxima.
+template <int N> __device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_vmem() { wait_vmem_n<0>(); }
+// Workgroup barrier that publishes this wave's LDS writes (ds_write; LDS-DMA
+// copies count as vector-memory instructions and are waited for separately)
+// without the wait for every outstanding global load that __syncthreads()'s
+// release fence adds. The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Workgroups of a 1-D grid are dealt round-robin to the 8 XCDs, each with
 // its own L2. Remap the block id so that each XCD works through one contiguous

@@ -38,7 +38,7 @@ def test_sizes_and_strings():
     W = (S + 63) // 64
     assert dsa.dsa_mask_bytes(B, S) == B * S * W * 8 + B * ((S + 127) // 128) * ((S + 63) // 64)
     assert dsa.dsa_mask_bytes(0, 5) == 0
-    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 192, 128) == 2 * 3 * 100 * 4
+    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 192, 128) == 2 * (2 * 3 * 100 * 4)  # D and base-2 LSE
     assert L.dsa_status_string(0) == b"DSA_OK"
     assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
     assert L.dsa_version() >= 100
