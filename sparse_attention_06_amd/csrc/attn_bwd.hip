@@ -51,14 +51,15 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 // tiles for the workgroup's keys are skipped.
 // A chunk's operands -- Q and dO rows, LSE and D, and the 32-bit halves of the
 // mask words of the workgroup's two key tiles -- all reach LDS through direct
-// global->LDS copies. A chunk is only ~1.3k MFMA cycles of work, less than a
-// global load's latency, so copies run two chunks ahead: four chunk buffers
-// (B reads the previous chunk, A the current one, one is in flight, one being
-// issued). Every wave issues exactly four copy instructions per chunk, so a
-// counted vmcnt wait finds the current chunk complete while the next one is
-// still in flight. P and dS are double buffered. The Q and dO tiles use the
-// swizzled padded layout that keeps both the row reads of A and the
-// transposing reads of B free of bank conflicts.
+// global->LDS copies, issued by the B waves only: a wave stalls while the copy
+// path accepts its copies, and A is the critical path. A chunk is only ~1.3k
+// MFMA cycles of work, less than a global load's latency, so copies run two
+// chunks ahead: four chunk buffers (B reads the previous chunk, A the current
+// one, one is in flight, one being issued). Each B wave issues a fixed number
+// of copies per chunk, so a counted vmcnt wait finds the current chunk
+// complete while the next one is still in flight. P and dS are double
+// buffered. The Q and dO tiles use the swizzled padded layout that keeps both
+// the row reads of A and the transposing reads of B free of bank conflicts.
 // ---------------------------------------------------------------------------
 namespace dkv {
 constexpr int NW = 8;
@@ -67,13 +68,13 @@ constexpr int QSL = 28, OSL = 20;                              // 16-byte slots 
 constexpr int QPX = QSL * 8, OPX = OSL * 8;                    // pitches (elements)
 constexpr int QBLK = bwd::QC * QSL / 64;                       // 1 KB blocks per Q chunk (14)
 constexpr int OBLK = bwd::QC * OSL / 64;                       // ... per dO chunk (10)
-// copy slots of a chunk: k = wid + NW*i, i < NSLOT: [0, QBLK) Q blocks,
-// [QBLK, QBLK+OBLK) dO blocks, then LSE/D, then the two mask-word tiles; the
-// remaining slots repeat Q blocks (same bytes to the same place)
-constexpr int NSLOT = 4;
-constexpr int K_LD = QBLK + OBLK, K_W = K_LD + 1, K_REP = K_W + 2;
+// copy slots of a chunk, all issued by the four B waves (slot k by wave
+// k % 4): [0, QBLK) Q blocks, [QBLK, QBLK+OBLK) dO blocks, then LSE/D, then
+// the two mask-word tiles
+constexpr int K_LD = QBLK + OBLK, K_W = K_LD + 1, NCOPY = K_W + 2;  // 27
+constexpr int NSLOT = (NCOPY + 3) / 4;                              // per B wave, at most (7)
 static_assert(bwd::QC * QSL % 64 == 0 && bwd::QC * OSL % 64 == 0, "chunks must be whole 1 KB blocks");
-static_assert(K_REP <= NW * NSLOT && NW * NSLOT - K_REP <= QBLK, "copy slots");
+static_assert(NCOPY % 4 == 3, "B waves 0-2 issue NSLOT copies per chunk, wave 3 one fewer");
 static_assert(bwd::QC == 32, "one copy instruction moves a chunk's LSE and D, one a mask tile");
 }  // namespace dkv
 
@@ -154,9 +155,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   // source offsets (elements from the chunk's first row) of this lane's Q / dO
   // slots: swizzled padded rows, pad slots copy the row's last chunk
   auto slot_src = [&](int kslot, int& row) -> uint32_t {
-    if (kslot < dkv::QBLK || kslot >= dkv::K_REP) {
-      const int j = kslot < dkv::QBLK ? kslot : kslot - dkv::K_REP;
-      const int slot = j * 64 + lane, pc = slot % dkv::QSL;
+    if (kslot < dkv::QBLK) {
+      const int slot = kslot * 64 + lane, pc = slot % dkv::QSL;
       row = slot / dkv::QSL;
       const int c = pc < DQK / 8 ? swz_chunk(row, pc) : DQK / 8 - 1;
       return (uint32_t)(row * rs_qk + c * 8);
@@ -166,28 +166,29 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const int c = pc < DV / 8 ? swz_chunk(row, pc) : DV / 8 - 1;
     return (uint32_t)(row * rs_v + c * 8);
   };
+  // B wave kw issues copy slots kw, kw+4, ...: NSLOT, or NSLOT-1 for kw == 3
   uint32_t soff[dkv::NSLOT];
 #pragma unroll
   for (int i = 0; i < dkv::NSLOT; ++i) {
     int row;
-    soff[i] = slot_src(wid + NW * i, row);
+    const int kslot = kw + 4 * i;
+    soff[i] = kslot < dkv::K_LD ? slot_src(kslot, row) : 0u;
   }
-  // chunk qc's copies into buffer bi: exactly NSLOT instructions per wave
+  // chunk qc's copies into buffer bi (B waves)
   auto issue = [&](int qc, int bi) {
     const int q0 = qc * QC;
     const bool ragged = q0 + QC > S;  // rows past S copy row S-1
 #pragma unroll
     for (int i = 0; i < dkv::NSLOT; ++i) {
-      const int kslot = wid + NW * i;
-      if (kslot < dkv::QBLK || kslot >= dkv::K_REP) {
-        const int j = kslot < dkv::QBLK ? kslot : kslot - dkv::K_REP;
+      const int kslot = kw + 4 * i;
+      if (kslot < dkv::QBLK) {
         uint32_t off = soff[i];
         if (ragged) {
           int row;
           off = slot_src(kslot, row);
           off -= (uint32_t)((row - min(row, S - 1 - q0)) * rs_qk);
         }
-        g2lds16_async(qbase + (size_t)q0 * rs_qk + off, smQ[bi] + j * 1024);
+        g2lds16_async(qbase + (size_t)q0 * rs_qk + off, smQ[bi] + kslot * 1024);
       } else if (kslot < dkv::K_LD) {
         uint32_t off = soff[i];
         if (ragged) {
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       } else if (kslot == dkv::K_LD) {
         const int t = min(q0 + col, S - 1);
         g2lds4_async(half ? drow + t : lrow + t, smLD[bi]);
-      } else {
+      } else if (kslot < dkv::NCOPY) {
         const int which = kslot - dkv::K_W;
         const int t = min(q0 + col, S - 1), kt = min(kt_lo + which, NK - 1);
         g2lds4_async(wbase + ((size_t)t * W + kt) * 2 + half, smW[bi][which]);
@@ -213,21 +214,27 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     if (q0 + QC <= S) return;
 #pragma unroll
     for (int i = 0; i < dkv::NSLOT; ++i) {
-      const int kslot = wid + NW * i;
-      if (kslot >= dkv::K_W && kslot < dkv::K_REP && q0 + col >= S) smW[bi][kslot - dkv::K_W][half][col] = 0u;
+      const int kslot = kw + 4 * i;
+      if (kslot >= dkv::K_W && kslot < dkv::NCOPY && q0 + col >= S) smW[bi][kslot - dkv::K_W][half][col] = 0u;
     }
   };
 
   int e0 = entry(0), e1 = entry(1), e2 = entry(2);  // current, next, and the one after
-  if (e0 >= 0) issue(e0 & 0x3FFF, 0);
-  if (e1 >= 0) issue(e1 & 0x3FFF, 1);
-  // chunk e0 (issued two chunks back) complete, then published; e1's copies
+  if (!roleA) {
+    if (e0 >= 0) issue(e0 & 0x3FFF, 0);
+    if (e1 >= 0) issue(e1 & 0x3FFF, 1);
+  }
+  // B: chunk e0 (issued two chunks back) complete, then published; e1's copies
   // may still be in flight
-  auto publish = [&](int it) {
-    if (e1 >= 0)
-      wait_vmem_n<dkv::NSLOT>();
-    else
+  auto publish_b = [&](int it) {
+    if (e1 >= 0) {
+      if (kw == 3)
+        wait_vmem_n<dkv::NSLOT - 1>();
+      else
+        wait_vmem_n<dkv::NSLOT>();
+    } else {
       wait_vmem();
+    }
     fix_ragged(e0 & 0x3FFF, it % NB);
     lds_barrier();
   };
@@ -261,8 +268,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const int bsh = sk & 31;
     const int wsel = (kw >> 1), hsel = (s0 >> 5) & 1;  // the pair's key tile and word half
     for (int it = 0; e0 >= 0; ++it) {
-      publish(it);
-      if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
+      lds_barrier();  // chunk e0 visible (B waited for its copies); B is done with P/dS buffer it&1
       const int e3 = entry(it + 3);
       if (active(e0)) {
         const int bi = it % NB, qc = e0 & 0x3FFF;
@@ -370,7 +376,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     bool prev = false;
     int it = 0;
     for (; e0 >= 0; ++it) {
-      publish(it);
+      publish_b(it);
       if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
       const int e3 = entry(it + 3);
       if (prev) update(it - 1);  // the chunk A finished before this barrier
