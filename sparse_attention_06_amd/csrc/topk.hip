@@ -334,6 +334,215 @@ __global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores
   for (int i = n + tid; i < K; i += 256) idx_row[i] = -1;
 }
 
+// Rows of at most 64 * 4 * kRegWords keys: the row's keys stay in VGPRs.
+// Wave w holds 64-key words w, w+4, w+8, ... (lane = position in the word), so
+// every pass is register work, and the compaction handles all words in
+// parallel: per-word counts of the "greater" and "tied" keys go to LDS, one
+// wave-wide prefix scan gives every word its first slot, and ballot/mbcnt
+// place the keys inside a word. One workgroup per row, longest rows first.
+constexpr int kRegWords = 16;
+
+template <typename ST>
+__global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                       const int32_t* __restrict__ seg, int B, int S,
+                                                       int K, int row0, int nrows,
+                                                       int32_t* __restrict__ idx,
+                                                       uint64_t* __restrict__ bits) {
+  __shared__ TopkShared sh;
+  __shared__ uint32_t wgt[64], weq[64];  // per 64-key word: keys above T, keys equal to T
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int W = (S + 63) / 64;
+  // row of work item i (longest rows first), and whether it reads scores
+  auto row_of = [&](int i, int& b, int& r) {
+    b = i % B;
+    r = nrows - 1 - i / B;
+  };
+  auto reads_scores = [&](int t) { return seg != nullptr || t + 1 > K; };
+  // raw scores of a row's positions held by this lane (positions >= L are not read)
+  ST raw[kRegWords];
+  auto load_row = [&](int i) {
+    int b, r;
+    row_of(i, b, r);
+    const int t = row0 + r;
+    if (!reads_scores(t)) return;
+    const ST* row = scores + ((size_t)b * nrows + r) * ld;
+#pragma unroll
+    for (int j = 0; j < kRegWords; ++j) {
+      const int s = 64 * (4 * j + wid) + lane;
+      if (s <= t) raw[j] = row[s];
+    }
+  };
+  {
+    const int item = blockIdx.x;
+    int b, r;
+    row_of(item, b, r);
+    const int t = row0 + r;
+    const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
+    const int seg_t = seg ? segb[t] : 0;
+    const int L = t + 1;
+    const int nw = (L + 63) / 64;
+    int32_t* idx_row = idx + ((size_t)b * S + t) * K;
+    uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
+    if (!reads_scores(t)) {
+      // causal-only row with at most K keys: every key 0..t, no score read
+      for (int i = tid; i < K; i += 256) idx_row[i] = i < L ? i : -1;
+      for (int w = tid; w < W; w += 256)
+        bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
+      return;
+    }
+    load_row(item);  // all of the row's score loads in flight at once
+    // keys of the valid positions (0 = not valid); take-all rows only need validity
+    uint32_t nv = 0;
+#pragma unroll
+    for (int j = 0; j < kRegWords; ++j) {
+      const int s = 64 * (4 * j + wid) + lane;
+      nv += __popcll(__ballot(s < L && (!segb || segb[s] == seg_t)));
+    }
+    __syncthreads();  // the previous row is done with the shared state
+    if (lane == 0) sh.red_u[wid] = nv;
+    __syncthreads();
+    const uint32_t n_valid = sh.red_u[0] + sh.red_u[1] + sh.red_u[2] + sh.red_u[3];
+    const bool take_all = n_valid <= (uint32_t)K;
+    uint32_t key[kRegWords];
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegWords; ++j) {
+      const int s = 64 * (4 * j + wid) + lane;
+      const bool valid = s < L && (!segb || segb[s] == seg_t);
+      uint32_t kk = 0u;
+      if (valid) kk = take_all ? 1u : fkey(ScoreLoad<ST>::get(&raw[j], 0));
+      key[j] = kk;
+      if (kk) {
+        kmin = min(kmin, kk);
+        kmax = max(kmax, kk);
+      }
+    }
+    uint32_t T = 0, c_eq = 0;
+    if (!take_all) {
+      __syncthreads();  // red_u is reused
+      block_uminmax(kmin, kmax, sh);
+      uint32_t need = (uint32_t)K;
+      uint32_t klo, khi;
+      if (kmin == kmax) {
+        klo = khi = kmax;
+      } else {
+        // value-linear bins: monotone in the score, so equal scores share a bin
+        const float mn = kfloat(kmin), mx = kfloat(kmax);
+        const float inv = (float)kNB / (mx - mn);
+        for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
+        __syncthreads();
+        auto bin_of = [&](uint32_t kk) {
+          return (int)fminf(fmaxf((kfloat(kk) - mn) * inv, 0.f), (float)(kNB - 1));
+        };
+#pragma unroll
+        for (int j = 0; j < kRegWords; ++j)
+          if (key[j]) atomicAdd(&sh.hist[bin_of(key[j])], 1u);
+        __syncthreads();
+        find_bin(sh, need);
+        const int bstar = (int)sh.found_bin;
+        need -= sh.found_above;
+        if (tid == 0) sh.ncand = 0;
+        __syncthreads();
+        klo = 0xffffffffu;
+        khi = 0u;
+#pragma unroll
+        for (int j = 0; j < kRegWords; ++j)
+          if (key[j] && bin_of(key[j]) == bstar) {
+            klo = min(klo, key[j]);
+            khi = max(khi, key[j]);
+            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+            if (slot < (uint32_t)kCand) sh.cand[slot] = key[j];
+          }
+        block_uminmax(klo, khi, sh);
+        const uint32_t nc = sh.ncand;
+        if (nc <= (uint32_t)kCand) {
+          // candidate i is the threshold when #greater < need <= #greater + #equal
+          if (tid < (int)nc) {
+            const uint32_t ki = sh.cand[tid];
+            uint32_t gt = 0, eq = 0;
+            for (uint32_t jj = 0; jj < nc; ++jj) {
+              const uint32_t kj = sh.cand[jj];
+              gt += kj > ki;
+              eq += kj == ki;
+            }
+            if (gt < need && need <= gt + eq) {
+              sh.thresh = ki;  // every thread that writes holds the same key
+              sh.found_above = gt;
+            }
+          }
+          __syncthreads();
+          klo = khi = sh.thresh;
+          need -= sh.found_above;
+        }
+      }
+      // radix refinement on the key interval [klo, khi] (crowded threshold bins)
+      while (klo != khi) {
+        const uint32_t span = khi - klo;
+        const int nbits = 32 - __clz(span);
+        const int shift = nbits > 11 ? nbits - 11 : 0;
+        for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kRegWords; ++j)
+          if (key[j] >= klo && key[j] <= khi) atomicAdd(&sh.hist[(key[j] - klo) >> shift], 1u);
+        __syncthreads();
+        find_bin(sh, need);
+        need -= sh.found_above;
+        const uint32_t nlo = klo + (sh.found_bin << shift);
+        const uint32_t nhi = shift == 0 ? nlo : min(khi, nlo + ((1u << shift) - 1u));
+        klo = nlo;
+        khi = nhi;
+      }
+      T = klo;
+      c_eq = need;
+    }
+
+    // ---- compaction: per-word counts, one scan, then every word in parallel
+    auto is_gt = [&](uint32_t kk) { return take_all ? kk != 0u : (kk != 0u && kk > T); };
+    auto is_eq = [&](uint32_t kk) { return !take_all && kk != 0u && kk == T; };
+#pragma unroll
+    for (int j = 0; j < kRegWords; ++j) {
+      const uint32_t cg = (uint32_t)__popcll(__ballot(is_gt(key[j])));
+      const uint32_t ce = (uint32_t)__popcll(__ballot(is_eq(key[j])));
+      const int w = 4 * j + wid;
+      if (lane == 0 && w < 64) {
+        wgt[w] = cg;
+        weq[w] = ce;
+      }
+    }
+    __syncthreads();
+    // exclusive prefix over the row's words (lane = word), in every wave
+    const uint32_t g = lane < nw ? wgt[lane] : 0u, e = lane < nw ? weq[lane] : 0u;
+    uint32_t gi = g, ei = e;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t gy = __shfl_up(gi, o), ey = __shfl_up(ei, o);
+      if (lane >= o) {
+        gi += gy;
+        ei += ey;
+      }
+    }
+    const uint32_t gx = gi - g, ex = ei - e;  // keys above T / ties in the words before
+#pragma unroll
+    for (int j = 0; j < kRegWords; ++j) {
+      const int w = 4 * j + wid;
+      if (w >= nw) continue;  // wave-uniform
+      const int s = 64 * w + lane;
+      const uint32_t gb = __builtin_amdgcn_readlane(gx, w), eb = __builtin_amdgcn_readlane(ex, w);
+      const bool gt = is_gt(key[j]), eq = is_eq(key[j]);
+      const uint32_t eq_rank = eb + lanes_below(__ballot(eq));
+      const bool sel = gt || (eq && eq_rank < c_eq);
+      const uint64_t selm = __ballot(sel);
+      const uint32_t pos = gb + min(eb, c_eq) + lanes_below(selm);
+      if (sel && pos < (uint32_t)K) idx_row[pos] = s;
+      if (lane == 0) bits_row[w] = selm;
+    }
+    for (int w = nw + tid; w < W; w += 256) bits_row[w] = 0ull;
+    const int n = take_all ? (int)n_valid : K;
+    for (int i = n + tid; i < K; i += 256) idx_row[i] = -1;
+  }
+}
+
 // Bits of caller-given index lists: one workgroup per row, the row's words
 // assembled in LDS with atomic ORs, then written out whole.
 __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restrict__ idx,
@@ -382,6 +591,11 @@ static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* s
                                 int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
   const size_t nrow_all = (size_t)nrows * B;
   dim3 grid((unsigned)nrow_all), block(256);
+  if (S <= 64 * 4 * kRegWords) {
+    hipLaunchKernelGGL((topk_reg_kernel<ST>), grid, block, 0, st, (const ST*)scores, ld, seg, B, S, K, row0,
+                       nrows, idx, bits);
+    return hipGetLastError();
+  }
   const size_t shm = (size_t)mask_words(S) * 64 * sizeof(uint32_t);
   if (shm <= kTopkLdsMax) {
     if (shm > 64 * 1024) {
