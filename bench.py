@@ -1,6 +1,6 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--no-cpu] [--no-long]
 
 One step is the whole path over one batch of seeded synthetic input: indexer
 scores -> top-k (index lists, mask bits, tile classes) -> sparse attention
@@ -10,7 +10,10 @@ seq 4096, 16 heads of 192/128, indexer 64 x 128, top-k 2048, bf16).
 
 Prints one JSON line. `value` is useful TFLOP/s of the whole step:
 indexer pairs x Hi x 2 Di, plus selected pairs x H x 6 (Dqk + Dv) for
-forward + backward. `indexer_topk_ms` is the selection half of the metric.
+forward + backward. `indexer_topk_ms` is the selection half of the metric;
+`selection` repeats it at the 32K (671B head count) and 128K workloads, where
+indexer and top-k are timed alone (the attention there is forward only and not
+part of the step).
 Per-kernel times come from HIP events recorded on the launch stream around
 each C-ABI call (each is one kernel, except dsa_topk, which is the top-k
 kernel plus the small tile-class kernel).
@@ -128,6 +131,44 @@ def cpu_baseline(cfg, x_cpu, budget_s=15.0, max_rows=4096):
             "seconds": dt, "rows": done}
 
 
+def selection_long(key, reps=2):
+    """Indexer + top-k alone at a long-sequence workload (the metric's 32K and
+    128K points): one warm-up call, then `reps` timed calls of each, with HIP
+    events on the launch stream. Only the selection inputs are generated."""
+    import torch
+    from sparse_attention_06_amd import dsa, inputs
+    cfg = inputs.CONFIGS[key]
+    x = inputs.make_index_inputs(cfg, device="cuda")
+    sdt = torch.bfloat16 if cfg.score_dtype == "bf16" else torch.float32
+    scores = torch.empty((cfg.B, cfg.S, cfg.S), dtype=sdt, device="cuda")
+    idx = torch.empty((cfg.B, cfg.S, cfg.K), dtype=torch.int32, device="cuda")
+    mask = torch.empty(dsa.dsa_mask_bytes(cfg.B, cfg.S), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    t_idx, t_top = [], []
+    for i in range(reps + 1):
+        ev[0].record(stream)
+        dsa.dsa_index_scores(x["q_idx"], x["k_idx"], x["w"], x["seg"], 0, cfg.S, scores)
+        ev[1].record(stream)
+        dsa.dsa_topk(scores, x["seg"], cfg.B, cfg.S, cfg.K, 0, cfg.S, idx, mask)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i:
+            t_idx.append(ev[0].elapsed_time(ev[1]))
+            t_top.append(ev[1].elapsed_time(ev[2]))
+    wk = work(cfg, None if x["seg"] is None else x["seg"].cpu().numpy())
+    mi, mt = float(np.mean(t_idx)), float(np.mean(t_top))
+    del scores, idx, mask, x
+    torch.cuda.empty_cache()
+    ach_i = wk["indexer"] / (mi * 1e-3) / 1e12
+    ach_t = wk["topk_bytes"] / (mt * 1e-3) / 1e9
+    return {"workload": cfg.name, "S": cfg.S, "index_scores_ms": mi, "topk_ms": mt, "indexer_topk_ms": mi + mt,
+            "index_scores": {"achieved": ach_i, "unit": "TFLOP/s", "frac": ach_i / PEAK_BF16_TFLOPS,
+                             "algorithmic": wk["indexer"]},
+            "topk": {"achieved": ach_t, "unit": "GB/s", "frac": ach_t / PEAK_HBM_GBS,
+                     "algorithmic": wk["topk_bytes"]}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +176,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip timing indexer + top-k at the 32K and 128K workloads")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -237,6 +280,18 @@ def main():
                 "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS, "unit": kd["unit"],
                 "frac": kd["frac"], "traffic": measured_traffic(dom, args.config), "kernel": dom}
 
+    # the metric's other sequence lengths: indexer + top-k alone at 32K and 128K
+    selection = {f"S{cfg.S}": {"workload": cfg.name, "S": cfg.S, "index_scores_ms": per["index_scores"],
+                               "topk_ms": per["topk"], "indexer_topk_ms": per["index_scores"] + per["topk"]}}
+    if not args.no_long:
+        del path
+        torch.cuda.empty_cache()
+        for key in ("c3", "c5"):
+            log(f"indexer + top-k at {inputs.CONFIGS[key].name}")
+            r = selection_long(key)
+            selection[f"S{r['S']}"] = r
+            log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms")
+
     cpu = None
     if not args.no_cpu:
         log("timing the float64 oracle on a row sample (cpu baseline)")
@@ -252,6 +307,7 @@ def main():
                    "topk": cfg.K, "heads": cfg.H, "dqk": cfg.Dqk, "dv": cfg.Dv, "score_dtype": cfg.score_dtype,
                    "segments": cfg.segments is not None, "passes": "+".join(calls)},
         "indexer_topk_ms": per["index_scores"] + per["topk"],
+        "selection": selection,
         "attention_useful_tflops": (wk["fwd"] + (wk["bwd"] if cfg.backward else 0)) /
                                    (sum(per[c] for c in calls if c.startswith("attn")) * 1e-3) / 1e12,
         "kernels": kernels,

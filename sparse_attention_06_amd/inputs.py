@@ -143,6 +143,25 @@ def make(cfg: Config, device="cpu", with_dout: Optional[bool] = None) -> dict:
     return out
 
 
+def make_index_inputs(cfg: Config, device="cpu") -> dict:
+    """Only the indexer's inputs (q_idx, k_idx, w, seg) of a configuration:
+    the same tensors, drawn from the same streams, as ``make`` returns."""
+    dt = cfg.torch_dtype()
+    B, S = cfg.B, cfg.S
+    sig = float(cfg.Di) ** -0.5 if cfg.scaled else 1.0
+    out = {
+        "q_idx": normal((B, S, cfg.Hi, cfg.Di), sig, cfg.seed, "q_idx", dt, device),
+        "k_idx": normal((B, S, cfg.Di), sig, cfg.seed, "k_idx", dt, device),
+        "w": normal((B, S, cfg.Hi), float(cfg.Hi) ** -0.5, cfg.seed, "w", dt, device),
+    }
+    if cfg.segments is not None:
+        seg = segment_ids(B, S, cfg.segments[0], cfg.segments[1], cfg.seed)
+        out["seg"] = torch.from_numpy(seg).to(device)
+    else:
+        out["seg"] = None
+    return out
+
+
 def random_index_sets(B: int, S: int, K: int, seg: Optional[np.ndarray], seed: int,
                       rows: Optional[np.ndarray] = None) -> np.ndarray:
     """Uniformly random key sets, one per query row, as a sparsity pattern.
