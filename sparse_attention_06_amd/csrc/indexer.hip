@@ -34,14 +34,20 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   constexpr int NBLK = (TILE * SL + 63) / 64;  // 1 KB blocks per tile
   constexpr int BI = (NBLK + 3) / 4;           // blocks per wave
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][NBLK * 1024];
+  __shared__ int32_t lseg[2][TILE];            // segment IDs of the tile's keys (when given)
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int nrb = (nrows + 3) / 4;
-  // one batch row's row blocks share an XCD (and its L2 copy of k_idx); longest rows first
-  const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);
-  const int b = L / nrb;
-  const int rb = nrb - 1 - L % nrb;
+  // Row blocks longest first, the batch index fastest. Blocks are dealt to
+  // the 8 XCDs round-robin in dispatch order, so every XCD gets an equal share
+  // of long and short rows (a contiguous split per XCD leaves one XCD with all
+  // of a batch's longest rows), and the row blocks that run together on an
+  // XCD stream the same k_idx tiles, once, through its L2.
+  const int L = (int)blockIdx.x;
+  const int b = L % B;
+  const int rb = nrb - 1 - L / B;
   const int r = rb * 4 + wid;
   const bool active = r < nrows;
   const int t = row0 + r;
@@ -68,7 +74,9 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   }
 
   // this wave's 1 KB blocks of the padded [64 rows][SL slots] tile; slots past
-  // a row's data or the tile copy a harmless chunk
+  // a row's data or the tile copy a harmless chunk. Wave 1 also copies the
+  // tile's segment IDs. Copies go through the untracked asm path; each wave
+  // waits for its own before the barrier that publishes the tile.
   auto issue = [&](int kt, int buf) {
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -78,17 +86,18 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
         const bool in = slot < TILE * SL;
         const int row = in ? slot / SL : 0, c = in ? min(slot % SL, SL - 2) : 0;
         const int s = min(kt * TILE + row, S - 1);
-        g2lds16(kb_base + (size_t)s * Di + c * 8, lds[buf] + j * 1024);
+        g2lds16_async(kb_base + (size_t)s * Di + c * 8, lds[buf] + j * 1024);
       }
     }
+    if (seg && wid == 1) g2lds4_async(seg + (size_t)b * S + min(kt * TILE + lane, S - 1), lseg[buf]);
   };
-
+  wait_vmem();  // this wave's query fragments and weights are in
   issue(0, 0);
   OutT* out_row = scores + ((size_t)b * nrows + r) * ld;
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     wait_vmem();
-    __syncthreads();  // tile kt visible; every wave is done with the other buffer
+    lds_barrier();  // tile kt visible; every wave is done with the other buffer
     if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
     const int s0 = kt * TILE;
     if (active && s0 <= t) {
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
       for (int sb = 0; sb < 2; ++sb) {
         const int s = s0 + sb * 32 + col;
         ok[sb] = s <= t;
-        if (seg && ok[sb]) ok[sb] = seg[(size_t)b * S + s] == seg_t;
+        if (seg && ok[sb]) ok[sb] = lseg[buf][sb * 32 + col] == seg_t;
       }
       // both 32-key column blocks' MFMAs first: the epilogue of one overlaps the other's MFMAs
       f32x16 acc[2][HB];
