@@ -54,25 +54,6 @@ struct TopkShared {
   uint32_t cand[kCand];
 };
 
-__device__ __forceinline__ uint32_t block_sum(uint32_t x, TopkShared& sh) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  x = wave_sum(x);
-  if (lane == 0) sh.red_u[wid] = x;
-  __syncthreads();
-  const uint32_t r = sh.red_u[0] + sh.red_u[1] + sh.red_u[2] + sh.red_u[3];
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ void block_minmax(float& mn, float& mx, TopkShared& sh) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  mn = wave_min(mn);
-  mx = wave_max(mx);
-  if (lane == 0) { sh.red_f[wid] = mn; sh.red_f[4 + wid] = mx; }
-  __syncthreads();
-  mn = fminf(fminf(sh.red_f[0], sh.red_f[1]), fminf(sh.red_f[2], sh.red_f[3]));
-  mx = fmaxf(fmaxf(sh.red_f[4], sh.red_f[5]), fmaxf(sh.red_f[6], sh.red_f[7]));
-  __syncthreads();
-}
 __device__ __forceinline__ void block_uminmax(uint32_t& mn, uint32_t& mx, TopkShared& sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   mn = wave_umin(mn);
@@ -129,211 +110,6 @@ __device__ __forceinline__ float kfloat(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// One workgroup per row. All passes work on order-preserving u32 keys, with
-// key 0 marking a position outside valid(t) (every finite score maps above
-// 0x007fffff). With IN_LDS the row's keys are built once from one coalesced
-// read of the scores and every later pass reads LDS; otherwise (rows too long
-// for LDS) each pass recomputes them from global memory.
-template <typename ST, bool IN_LDS>
-__global__ __launch_bounds__(256) void topk_kernel(const ST* __restrict__ scores, int64_t ld,
-                                                   const int32_t* __restrict__ seg, int B, int S,
-                                                   int K, int row0, int nrows,
-                                                   int32_t* __restrict__ idx,
-                                                   uint64_t* __restrict__ bits) {
-  __shared__ TopkShared sh;
-  extern __shared__ uint32_t rowkeys[];  // IN_LDS: keys of positions [0, 64 * nw)
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int b = blockIdx.x % B;
-  const int r = nrows - 1 - (int)(blockIdx.x / B);  // longest rows first
-  const int t = row0 + r;
-  const int W = (S + 63) / 64;
-  const ST* row = scores + ((size_t)b * nrows + r) * ld;
-  const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
-  const int seg_t = seg ? segb[t] : 0;
-  const int L = t + 1;
-  const int nw = (L + 63) / 64;
-
-  auto gkey = [&](int s) -> uint32_t {  // key from global memory (0 if not valid)
-    if (s >= L || (segb && segb[s] != seg_t)) return 0u;
-    return fkey(ScoreLoad<ST>::get(row, s));
-  };
-  auto key = [&](int s) -> uint32_t {
-    if constexpr (IN_LDS) return rowkeys[s];
-    else return gkey(s);
-  };
-
-  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
-  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
-  if (!segb && L <= K) {
-    // causal-only row with at most K keys: every key 0..t, no score read
-    for (int i = tid; i < K; i += 256) idx_row[i] = i < L ? i : -1;
-    for (int w = tid; w < W; w += 256)
-      bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
-    return;
-  }
-  uint32_t n_valid = (uint32_t)L;
-  if (segb) {
-    uint32_t c = 0;
-    for (int s = tid; s < L; s += 256) c += (segb[s] == seg_t);
-    n_valid = block_sum(c, sh);
-  }
-  const bool take_all = n_valid <= (uint32_t)K;
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  if constexpr (IN_LDS) {
-    // take-all rows never read scores: their keys only mark validity
-    for (int s = tid; s < 64 * nw; s += 256) {
-      const uint32_t kk = take_all ? ((s < L && (!segb || segb[s] == seg_t)) ? 1u : 0u) : gkey(s);
-      rowkeys[s] = kk;
-      if (kk) {
-        kmin = min(kmin, kk);
-        kmax = max(kmax, kk);
-      }
-    }
-    __syncthreads();  // the row's keys are visible to every wave
-  }
-  uint32_t T = 0, c_eq = 0;
-  if (!take_all) {
-    if constexpr (!IN_LDS) {
-      for (int s = tid; s < L; s += 256) {
-        const uint32_t kk = key(s);
-        if (kk) {
-          kmin = min(kmin, kk);
-          kmax = max(kmax, kk);
-        }
-      }
-    }
-    block_uminmax(kmin, kmax, sh);
-    uint32_t need = (uint32_t)K;
-    uint32_t klo, khi;
-    if (kmin == kmax) {
-      klo = khi = kmax;
-    } else {
-      // value-linear bins: monotone in the score, so equal scores share a bin
-      const float mn = kfloat(kmin), mx = kfloat(kmax);
-      const float inv = (float)kNB / (mx - mn);
-      for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
-      __syncthreads();
-      for (int s = tid; s < L; s += 256) {
-        const uint32_t kk = key(s);
-        if (kk) {
-          const int bin = (int)fminf(fmaxf((kfloat(kk) - mn) * inv, 0.f), (float)(kNB - 1));
-          atomicAdd(&sh.hist[bin], 1u);
-        }
-      }
-      __syncthreads();
-      find_bin(sh, need);
-      const int bstar = (int)sh.found_bin;
-      need -= sh.found_above;
-      // the keys in bin b* form one contiguous key interval; collect them, and
-      // when few, take the need-th largest by direct ranking
-      if (tid == 0) sh.ncand = 0;
-      __syncthreads();
-      klo = 0xffffffffu;
-      khi = 0u;
-      for (int s = tid; s < L; s += 256) {
-        const uint32_t kk = key(s);
-        if (kk) {
-          const int bin = (int)fminf(fmaxf((kfloat(kk) - mn) * inv, 0.f), (float)(kNB - 1));
-          if (bin == bstar) {
-            klo = min(klo, kk);
-            khi = max(khi, kk);
-            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-            if (slot < (uint32_t)kCand) sh.cand[slot] = kk;
-          }
-        }
-      }
-      block_uminmax(klo, khi, sh);
-      const uint32_t nc = sh.ncand;
-      if (nc <= (uint32_t)kCand) {
-        // candidate i is the threshold when #greater < need <= #greater + #equal
-        if (tid < (int)nc) {
-          const uint32_t ki = sh.cand[tid];
-          uint32_t gt = 0, eq = 0;
-          for (uint32_t j = 0; j < nc; ++j) {
-            const uint32_t kj = sh.cand[j];
-            gt += kj > ki;
-            eq += kj == ki;
-          }
-          if (gt < need && need <= gt + eq) {
-            sh.thresh = ki;  // every thread that writes holds the same key
-            sh.found_above = gt;
-          }
-        }
-        __syncthreads();
-        klo = khi = sh.thresh;
-        need -= sh.found_above;
-      }
-    }
-    // radix refinement on the key interval [klo, khi]
-    while (klo != khi) {
-      const uint32_t span = khi - klo;
-      const int nbits = 32 - __clz(span);
-      const int shift = nbits > 11 ? nbits - 11 : 0;
-      for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
-      __syncthreads();
-      for (int s = tid; s < L; s += 256) {
-        const uint32_t kk = key(s);
-        if (kk >= klo && kk <= khi) atomicAdd(&sh.hist[(kk - klo) >> shift], 1u);
-      }
-      __syncthreads();
-      find_bin(sh, need);
-      need -= sh.found_above;
-      const uint32_t nlo = klo + (sh.found_bin << shift);
-      const uint32_t nhi = shift == 0 ? nlo : min(khi, nlo + ((1u << shift) - 1u));
-      klo = nlo;
-      khi = nhi;
-    }
-    T = klo;
-    c_eq = need;
-  }
-
-  // ---- compaction: ascending index list and bitmask words
-  const int wpw = (nw + 3) / 4;
-  const int wa = wid * wpw, wb = min(nw, wa + wpw);
-  auto classify = [&](int s, bool& gt, bool& eq) {
-    const uint32_t kk = (IN_LDS || s < L) ? key(s) : 0u;
-    if (take_all) {
-      gt = kk != 0u;
-      eq = false;
-    } else {
-      gt = kk != 0u && kk > T;
-      eq = kk != 0u && kk == T;
-    }
-  };
-  uint32_t my_gt = 0, my_eq = 0;
-  for (int w = wa; w < wb; ++w) {
-    bool gt, eq;
-    classify(64 * w + lane, gt, eq);
-    my_gt += __popcll(__ballot(gt));
-    my_eq += __popcll(__ballot(eq));
-  }
-  if (lane == 0) { sh.wave_gt[wid] = my_gt; sh.wave_eq[wid] = my_eq; }
-  __syncthreads();
-  uint32_t eq_before = 0, sel_before = 0;
-  for (int w2 = 0; w2 < wid; ++w2) {
-    const uint32_t take_eq = eq_before >= c_eq ? 0u : min(sh.wave_eq[w2], c_eq - eq_before);
-    sel_before += sh.wave_gt[w2] + take_eq;
-    eq_before += sh.wave_eq[w2];
-  }
-  for (int w = wa; w < wb; ++w) {
-    const int s = 64 * w + lane;
-    bool gt, eq;
-    classify(s, gt, eq);
-    const uint64_t eqm = __ballot(eq);
-    const uint32_t eq_rank = eq_before + lanes_below(eqm);
-    const bool sel = gt || (eq && eq_rank < c_eq);
-    const uint64_t selm = __ballot(sel);
-    const uint32_t pos = sel_before + lanes_below(selm);
-    if (sel && pos < (uint32_t)K) idx_row[pos] = s;
-    if (lane == 0) bits_row[w] = selm;
-    eq_before += __popcll(eqm);
-    sel_before += __popcll(selm);
-  }
-  for (int w = nw + tid; w < W; w += 256) bits_row[w] = 0ull;
-  const int n = take_all ? (int)n_valid : K;
-  for (int i = n + tid; i < K; i += 256) idx_row[i] = -1;
-}
-
 // Rows of at most 64 * 4 * kRegWords keys: the row's keys stay in VGPRs.
 // Wave w holds 64-key words w, w+4, w+8, ... (lane = position in the word), so
 // every pass is register work, and the compaction handles all words in
@@ -345,7 +121,7 @@ constexpr int kRegWords = 16;
 template <typename ST>
 __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ scores, int64_t ld,
                                                        const int32_t* __restrict__ seg, int B, int S,
-                                                       int K, int row0, int nrows,
+                                                       int K, int row0, int nrows, int rbeg, int rcount,
                                                        int32_t* __restrict__ idx,
                                                        uint64_t* __restrict__ bits) {
   __shared__ TopkShared sh;
@@ -355,7 +131,7 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
   // row of work item i (longest rows first), and whether it reads scores
   auto row_of = [&](int i, int& b, int& r) {
     b = i % B;
-    r = nrows - 1 - i / B;
+    r = rbeg + rcount - 1 - i / B;
   };
   auto reads_scores = [&](int t) { return seg != nullptr || t + 1 > K; };
   // raw scores of a row's positions held by this lane (positions >= L are not read)
@@ -543,6 +319,389 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
   }
 }
 
+// ---- rows longer than 64 * 4 * kRegWords keys: one workgroup per row
+//
+// The row's scores are either copied once into LDS (global_load_lds, one
+// coalesced read) or, for rows too long for LDS, read from global memory in
+// every pass (the later passes then hit the caches). Wave w walks one
+// contiguous range of the row's 64-key words in order, lane = key position in
+// the word, so every count it needs is a running scalar: no per-word arrays.
+//   1. The histogram's value range comes from a strided sample of 1024 valid
+//      scores. Values outside it go to the edge bins, so the bins stay
+//      monotone in the value (equal scores share a bin) and the result stays
+//      exact; a badly placed range only makes step 3 take its slow branch.
+//   2. A 2048-bin histogram over the sampled range locates the bin b* of the
+//      K-th largest score.
+//   3. One pass counts, per wave, the keys in bins above b*, and collects the
+//      keys of bin b* (key and position). The K-th largest key T is found by
+//      ranking them directly; the candidates above or at T are then added to
+//      their waves' counts. A crowded b* (more candidates than the list
+//      holds) falls back to radix passes over the key interval of b*, and one
+//      more pass counts each wave's keys above and at T.
+//   4. An exclusive prefix over the waves' counts gives each wave its first
+//      slot; the last pass walks the words in order and writes the ascending
+//      index list (ties at T from the lowest positions) and, 64 words per
+//      store, the mask words.
+constexpr int kMaxLW = 16;        // most waves per workgroup
+constexpr int kLCand = 256;       // candidates ranked directly (one per thread)
+constexpr int kSample = 1024;     // scores sampled for the histogram range
+
+struct LongShared {
+  uint32_t hist[kNB + 1];         // + a bin that invalid positions count into
+  uint32_t cand_key[kLCand];
+  uint32_t cand_pos[kLCand];
+  uint32_t red_u[2 * kMaxLW];
+  float red_f[2 * kMaxLW];
+  uint32_t wave_g[kMaxLW], wave_e[kMaxLW];
+  uint32_t found_bin, found_above, ncand, thresh, thresh_above;
+};
+
+template <int NW> __device__ __forceinline__ void block_minmax_f(float& mn, float& mx, float* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  if (lane == 0) { red[wid] = mn; red[NW + wid] = mx; }
+  __syncthreads();
+  mn = red[0];
+  mx = red[NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) { mn = fminf(mn, red[i]); mx = fmaxf(mx, red[NW + i]); }
+  __syncthreads();
+}
+template <int NW> __device__ __forceinline__ void block_minmax_u(uint32_t& mn, uint32_t& mx, uint32_t* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  mn = wave_umin(mn);
+  mx = wave_umax(mx);
+  if (lane == 0) { red[wid] = mn; red[NW + wid] = mx; }
+  __syncthreads();
+  mn = red[0];
+  mx = red[NW];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) { mn = min(mn, red[i]); mx = max(mx, red[NW + i]); }
+  __syncthreads();
+}
+
+// Largest bin b of hist[0..kNB) with count(bins >= b) >= need, for NT threads;
+// writes b and count(bins > b). Needs count(all bins) >= need >= 1.
+template <int NT>
+__device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t& found_bin,
+                           uint32_t& found_above) {
+  constexpr int PER = kNB / NT, NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t c[PER];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) { c[i] = hist[PER * tid + i]; tot += c[i]; }
+  // suffix sum over the lanes at or above this one (they hold higher bins)
+  uint32_t incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(incl, o);
+    if (lane + o < 64) incl += y;
+  }
+  if (lane == 0) red[wid] = incl;  // wave total
+  __syncthreads();
+  uint32_t running = incl - tot;  // keys in bins above this thread's chunk
+  for (int w2 = wid + 1; w2 < NW; ++w2) running += red[w2];
+  __syncthreads();
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    if (running < need && running + c[i] >= need) {
+      found_bin = PER * tid + i;
+      found_above = running;
+    }
+    running += c[i];
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
+
+template <typename ST, bool IN_LDS, bool SEG, int NW>
+__global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                            const int32_t* __restrict__ seg, int B, int S,
+                                                            int K, int row0, int nrows, int rbeg, int rcount,
+                                                            int nw_max, int32_t* __restrict__ idx,
+                                                            uint64_t* __restrict__ bits) {
+  constexpr int NT = 64 * NW;
+  constexpr int kU = 8;  // words per step: all of their reads issued first
+  __shared__ LongShared sh;
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  uint64_t* segw = (uint64_t*)dyn;  // per word: same-segment positions <= t
+  unsigned char* rawl = (unsigned char*)(dyn + (SEG ? 2 * nw_max : 0));  // the row's scores
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x % B;
+  const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
+  const int t = row0 + r;
+  const int W = (S + 63) / 64;
+  const int L = t + 1, nw = (L + 63) / 64;
+  const ST* row = scores + ((size_t)b * nrows + r) * ld;
+  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
+  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
+  // this wave's words [wa, wb)
+  const int nwp = (nw + NW - 1) / NW;
+  const int wa = min(nw, wid * nwp), wb = min(nw, wa + nwp);
+
+  if (!SEG && L <= K) {
+    // causal-only row with at most K keys: every key 0..t, no score read
+    for (int i = tid; i < K; i += NT) idx_row[i] = i < L ? i : -1;
+    for (int w = tid; w < W; w += NT)
+      bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
+    return;
+  }
+  uint32_t n_valid = (uint32_t)L;
+  if (SEG) {
+    const int32_t* segb = seg + (size_t)b * S;
+    const int seg_t = segb[t];
+    uint32_t c = 0;
+    for (int w = wa; w < wb; ++w) {
+      const int s = 64 * w + lane;
+      const uint64_t m = __ballot(s < L && segb[s] == seg_t);
+      if (lane == 0) segw[w] = m;
+      c += popc64(m);
+    }
+    if (lane == 0) sh.red_u[wid] = c;
+    __syncthreads();
+    n_valid = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) n_valid += sh.red_u[i];
+    __syncthreads();
+  }
+  // is this lane's position in word w valid (w < nw)
+  auto valid = [&](int w) -> bool {
+    if (SEG) return (segw[w] >> lane) & 1ull;
+    return 64 * w + lane < L;
+  };
+  const bool take_all = n_valid <= (uint32_t)K;
+
+  // the row's bytes start `off` bytes into the first copied dword
+  const uintptr_t rs = (uintptr_t)row;
+  const int off = (int)(rs & 3);
+  if (IN_LDS && !take_all) {
+    const uintptr_t ra = rs - off;
+    const uintptr_t last = (rs + (uintptr_t)L * sizeof(ST) - 1) & ~(uintptr_t)3;
+    const int nchunk = (off + L * (int)sizeof(ST) + 255) / 256;
+    for (int c = wid; c < nchunk; c += NW) {
+      uintptr_t src = ra + 256 * (uintptr_t)c + 4 * lane;
+      src = src > last ? last : src;  // past the row's end: a duplicate of its last dword
+      g2lds4((const void*)src, rawl + 256 * c);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  auto score = [&](int s) -> float {
+    if constexpr (IN_LDS) {
+      if constexpr (sizeof(ST) == 4) return *(const float*)(rawl + off + 4 * s);
+      else return bf2f(*(const uint16_t*)(rawl + off + 2 * s));
+    } else {
+      return ScoreLoad<ST>::get(row, s);
+    }
+  };
+  // scores of words w0 .. w0 + kU - 1 (those below wb), every read issued
+  // before any use: in LDS the copy's tail is padded, so positions past t in
+  // the row's last word are read (and dropped); global memory is not read there
+  auto load_words = [&](int w0, float (&x)[kU]) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int w = w0 + u, s = 64 * w + lane;
+      x[u] = 0.f;
+      if (w < wb) {  // wave-uniform
+        if (IN_LDS) x[u] = score(s);
+        else if (s < L) x[u] = score(s);
+      }
+    }
+  };
+
+  uint32_t T = 0, c_eq = 0;
+  float Tf = 0.f;
+  if (!take_all) {
+    // 1. histogram range from a strided sample of valid scores
+    float mn = INFINITY, mx = -INFINITY;
+    for (int i = tid; i < kSample; i += NT) {
+      const int s = (int)(((int64_t)i * L) / kSample);
+      const bool v = SEG ? ((segw[s >> 6] >> (s & 63)) & 1ull) : true;
+      if (v) {
+        const float x = score(s);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+    }
+    block_minmax_f<NW>(mn, mx, sh.red_f);
+    if (!(mn <= mx)) {  // no valid key sampled: the whole row
+      for (int w = wa; w < wb; ++w)
+        if (valid(w)) {
+          const float x = score(64 * w + lane);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+      block_minmax_f<NW>(mn, mx, sh.red_f);
+    }
+    // a single sampled value: a huge scale puts it in bin 0, larger scores in the top bin
+    const float inv = mx > mn ? (float)kNB / (mx - mn) : 1e30f;
+    auto bin_of = [&](float x) -> int { return (int)fminf(fmaxf((x - mn) * inv, 0.f), (float)(kNB - 1)); };
+    // 2. histogram
+    for (int i = tid; i <= kNB; i += NT) sh.hist[i] = 0;
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+    for (int w0 = wa; w0 < wb; w0 += kU) {
+      float x[kU];
+      load_words(w0, x);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int w = w0 + u;
+        if (w < wb) atomicAdd(&sh.hist[valid(w) ? bin_of(x[u]) : kNB], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin_n<NT>(sh.hist, (uint32_t)K, sh.red_u, sh.found_bin, sh.found_above);
+    const int bstar = (int)sh.found_bin;
+    uint32_t need = (uint32_t)K - sh.found_above;
+    // 3. this wave's keys in bins above b*, and the keys of b*
+    uint32_t klo = 0xffffffffu, khi = 0u, gw = 0u;
+    for (int w0 = wa; w0 < wb; w0 += kU) {
+      float x[kU];
+      load_words(w0, x);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int w = w0 + u;
+        if (w >= wb) break;  // wave-uniform
+        const int bn = valid(w) ? bin_of(x[u]) : -1;
+        gw += popc64(__ballot(bn > bstar));
+        if (bn == bstar) {
+          const uint32_t k = fkey(x[u]);
+          klo = min(klo, k);
+          khi = max(khi, k);
+          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+          if (slot < (uint32_t)kLCand) {
+            sh.cand_key[slot] = k;
+            sh.cand_pos[slot] = (uint32_t)(64 * w + lane);
+          }
+        }
+      }
+    }
+    if (lane == 0) {
+      sh.wave_g[wid] = gw;
+      sh.wave_e[wid] = 0u;
+    }
+    block_minmax_u<NW>(klo, khi, sh.red_u);  // its barrier also publishes the candidates
+    const uint32_t nc = sh.ncand;
+    if (nc <= (uint32_t)kLCand) {
+      // candidate i is T when #greater < need <= #greater + #equal
+      if (tid < (int)nc) {
+        const uint32_t ki = sh.cand_key[tid];
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t j = 0; j < nc; ++j) {
+          const uint32_t kj = sh.cand_key[j];
+          gt += kj > ki;
+          eq += kj == ki;
+        }
+        if (gt < need && need <= gt + eq) {
+          sh.thresh = ki;  // every thread that writes holds the same key
+          sh.thresh_above = gt;
+        }
+      }
+      __syncthreads();
+      T = sh.thresh;
+      c_eq = need - sh.thresh_above;
+      if (tid < (int)nc) {
+        const uint32_t k = sh.cand_key[tid], wi = (sh.cand_pos[tid] >> 6) / (uint32_t)nwp;
+        if (k > T) atomicAdd(&sh.wave_g[wi], 1u);
+        else if (k == T) atomicAdd(&sh.wave_e[wi], 1u);
+      }
+    } else {
+      // crowded b*: radix passes over its key interval [klo, khi]
+      while (klo != khi) {
+        const uint32_t span = khi - klo;
+        const int nbits = 32 - __clz(span);
+        const int shift = nbits > 11 ? nbits - 11 : 0;
+        for (int i = tid; i < kNB; i += NT) sh.hist[i] = 0;
+        __syncthreads();
+        for (int w = wa; w < wb; ++w)
+          if (valid(w)) {
+            const uint32_t k = fkey(score(64 * w + lane));
+            if (k >= klo && k <= khi) atomicAdd(&sh.hist[(k - klo) >> shift], 1u);
+          }
+        __syncthreads();
+        find_bin_n<NT>(sh.hist, need, sh.red_u, sh.found_bin, sh.found_above);
+        need -= sh.found_above;
+        const uint32_t nlo = klo + (sh.found_bin << shift);
+        const uint32_t nhi = shift == 0 ? nlo : min(khi, nlo + ((1u << shift) - 1u));
+        klo = nlo;
+        khi = nhi;
+      }
+      T = klo;
+      c_eq = need;
+      uint32_t g2 = 0, e2 = 0;
+      for (int w = wa; w < wb; ++w) {
+        const bool v = valid(w);
+        const uint32_t k = v ? fkey(score(64 * w + lane)) : 0u;
+        g2 += popc64(__ballot(v && k > T));
+        e2 += popc64(__ballot(v && k == T));
+      }
+      if (lane == 0) {
+        sh.wave_g[wid] = g2;
+        sh.wave_e[wid] = e2;
+      }
+    }
+    Tf = kfloat(T);
+  } else {
+    uint32_t g2 = 0;
+    for (int w = wa; w < wb; ++w) g2 += popc64(__ballot(valid(w)));
+    if (lane == 0) {
+      sh.wave_g[wid] = g2;
+      sh.wave_e[wid] = 0u;
+    }
+  }
+  __syncthreads();
+
+  // 4. this wave's first slot, then its words in order
+  uint32_t gb = 0, eb = 0;
+  for (int w2 = 0; w2 < wid; ++w2) {
+    gb += sh.wave_g[w2];
+    eb += sh.wave_e[w2];
+  }
+  gb = __builtin_amdgcn_readfirstlane(gb);
+  eb = __builtin_amdgcn_readfirstlane(eb);
+  uint32_t mlo = 0, mhi = 0;  // lane j: mask word wa + 64 * (k / 64) + j
+  for (int w0 = wa; w0 < wb; w0 += kU) {
+    float x[kU];
+    if (take_all) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) x[u] = 0.f;
+    } else {
+      load_words(w0, x);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int w = w0 + u;
+      if (w >= wb) break;  // wave-uniform
+      const bool v = valid(w);
+      const bool gt = v && (take_all || x[u] > Tf);
+      const bool eq = v && !take_all && x[u] == Tf;
+      const uint64_t eqm = __ballot(eq);
+      const bool sel = gt || (eq && eb + lanes_below(eqm) < c_eq);
+      const uint64_t selm = __ballot(sel);
+      const uint32_t pos = gb + min(eb, c_eq) + lanes_below(selm);
+      if (sel && pos < (uint32_t)K) idx_row[pos] = 64 * w + lane;
+      gb += popc64(__ballot(gt));
+      eb += popc64(eqm);
+      const int j = (w - wa) & 63;
+      if (lane == j) {
+        mlo = (uint32_t)selm;
+        mhi = (uint32_t)(selm >> 32);
+      }
+      if (j == 63 || w == wb - 1) {  // wave-uniform: store the collected mask words
+        if (lane <= j) bits_row[w - j + lane] = ((uint64_t)mhi << 32) | mlo;
+      }
+    }
+  }
+  for (int w = nw + tid; w < W; w += NT) bits_row[w] = 0ull;
+  const int n = take_all ? (int)n_valid : K;
+  for (int i = n + tid; i < K; i += NT) idx_row[i] = -1;
+}
+
 // Bits of caller-given index lists: one workgroup per row, the row's words
 // assembled in LDS with atomic ORs, then written out whole.
 __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restrict__ idx,
@@ -583,33 +742,62 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restr
   cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
 }
 
-// rows whose keys fit this much dynamic LDS keep them there
-constexpr size_t kTopkLdsMax = 128 * 1024;
+template <typename ST, bool IN_LDS, bool SEG, int NW>
+static hipError_t launch_long_t(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
+                                int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
+                                hipStream_t st) {
+  const int Lmax = row0 + rbeg + rcount;  // longest row of the range
+  const int nw_max = (Lmax + 63) / 64;
+  size_t shm = SEG ? (size_t)nw_max * 8 : 0;
+  // a bf16 row may start 2 bytes into its first copied dword; reads run to the end of the last word
+  if (IN_LDS) shm += ((size_t)Lmax * sizeof(ST) + (sizeof(ST) == 2 ? 2 : 0) + 255) / 256 * 256 + 256;
+  if (shm + sizeof(LongShared) > 160 * 1024) return hipErrorInvalidValue;
+  const void* fn = (const void*)topk_long_kernel<ST, IN_LDS, SEG, NW>;
+  if (shm > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((topk_long_kernel<ST, IN_LDS, SEG, NW>), dim3((unsigned)((size_t)rcount * B)),
+                     dim3(64 * NW), shm, st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max,
+                     idx, bits);
+  return hipGetLastError();
+}
+// rows in LDS with up to 64 KB of scores: 8 waves, two workgroups per CU;
+// longer rows: 16 waves, one workgroup per CU
+template <typename ST, bool IN_LDS, int NW>
+static hipError_t launch_long(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
+                              int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
+                              hipStream_t st) {
+  return seg ? launch_long_t<ST, IN_LDS, true, NW>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx,
+                                                   bits, st)
+             : launch_long_t<ST, IN_LDS, false, NW>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx,
+                                                    bits, st);
+}
 
+// Rows are routed by length L = t + 1 (longest first): up to 64 * 4 *
+// kRegWords keys in VGPRs; up to 64 KB of scores in LDS (two workgroups per
+// CU); up to 128 KB in LDS (one per CU); longer rows read global memory.
 template <typename ST>
 static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
                                 int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
-  const size_t nrow_all = (size_t)nrows * B;
-  dim3 grid((unsigned)nrow_all), block(256);
-  if (S <= 64 * 4 * kRegWords) {
-    hipLaunchKernelGGL((topk_reg_kernel<ST>), grid, block, 0, st, (const ST*)scores, ld, seg, B, S, K, row0,
-                       nrows, idx, bits);
-    return hipGetLastError();
+  const ST* sc = (const ST*)scores;
+  const int l_reg = 64 * 4 * kRegWords;
+  const int l_small = (int)(64 * 1024 / sizeof(ST)), l_big = 2 * l_small;
+  auto upto = [&](int l) { return max(0, min(nrows, l - row0)); };  // rows with L <= l
+  const int n_reg = upto(l_reg), n_small = upto(l_small), n_big = upto(l_big);
+  hipError_t e = hipSuccess;
+  if (nrows > n_big)
+    e = launch_long<ST, false, 16>(sc, ld, seg, B, S, K, row0, nrows, n_big, nrows - n_big, idx, bits, st);
+  if (e == hipSuccess && n_big > n_small)
+    e = launch_long<ST, true, 16>(sc, ld, seg, B, S, K, row0, nrows, n_small, n_big - n_small, idx, bits, st);
+  if (e == hipSuccess && n_small > n_reg)
+    e = launch_long<ST, true, 8>(sc, ld, seg, B, S, K, row0, nrows, n_reg, n_small - n_reg, idx, bits, st);
+  if (e == hipSuccess && n_reg > 0) {
+    hipLaunchKernelGGL((topk_reg_kernel<ST>), dim3((unsigned)((size_t)n_reg * B)), dim3(256), 0, st, sc, ld,
+                       seg, B, S, K, row0, nrows, 0, n_reg, idx, bits);
+    e = hipGetLastError();
   }
-  const size_t shm = (size_t)mask_words(S) * 64 * sizeof(uint32_t);
-  if (shm <= kTopkLdsMax) {
-    if (shm > 64 * 1024) {
-      hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<ST, true>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL((topk_kernel<ST, true>), grid, block, shm, st, (const ST*)scores, ld, seg, B, S, K,
-                       row0, nrows, idx, bits);
-  } else {
-    hipLaunchKernelGGL((topk_kernel<ST, false>), grid, block, 0, st, (const ST*)scores, ld, seg, B, S, K,
-                       row0, nrows, idx, bits);
-  }
-  return hipGetLastError();
+  return e;
 }
 
 hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,

@@ -163,6 +163,60 @@ def test_topk_vs_oracle_scores(segments):
     assert len(dec) >= 0.9 * B * S
 
 
+def _long_rows(B, n, S, row0, dtype, seed):
+    """Scores of n slab rows with the structures the selection must handle:
+    value ties, signed zeros, far outliers (outside a sampled value range),
+    a single repeated value with a few larger ones, and constant rows."""
+    g = torch.Generator().manual_seed(seed)
+    v = torch.randn((B, n, S), generator=g)
+    for r in range(n):
+        kind = (row0 + r) % 5
+        if kind == 0:
+            v[:, r] = torch.round(v[:, r] * 64) / 64
+        elif kind == 1:
+            v[:, r][torch.rand((B, S), generator=g) < 0.05] = -0.0
+            v[:, r][torch.rand((B, S), generator=g) < 0.05] = 0.0
+        elif kind == 2:
+            v[:, r] = 0.5
+            pos = torch.randint(0, row0 + r + 1, (B, 12), generator=g)
+            v[:, r].scatter_(1, pos, 100.0)
+        elif kind == 3:
+            pos = torch.randint(0, row0 + r + 1, (B, 40), generator=g)
+            v[:, r].scatter_(1, pos, torch.where(torch.rand((B, 40), generator=g) < 0.5, 1e30, -1e30))
+        else:
+            v[:, r] = -1.25
+    return v.to(dtype)
+
+
+@pytest.mark.parametrize("score_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("segments", [None, (3000, 20000)])
+def test_topk_long_rows(score_dtype, segments):
+    """Rows longer than 4096 keys on both sides of every length at which the
+    selection changes kernels (scores in VGPRs / 64 KB and 128 KB of scores
+    in LDS / read from global memory), as slab calls of whole query tiles:
+    bit-exact index lists and mask rows."""
+    B, K = 2, 300
+    if score_dtype == torch.float32:   # lengths 4096, 16384, 32768
+        S, slabs = 33000, [(3968, 256), (16256, 256), (32640, 256), (32896, 104)]
+    else:                              # lengths 4096, 32768, 65536
+        S, slabs = 66000, [(3968, 256), (32640, 256), (65408, 256), (65920, 80)]
+    seg = None if segments is None else inputs.segment_ids(B, S, segments[0], segments[1], seed=3)
+    seg_dev = None if seg is None else torch.from_numpy(seg).to(DEV).contiguous()
+    idx = torch.full((B, S, K), -7, dtype=torch.int32, device=DEV)
+    mask = torch.zeros(dsa.dsa_mask_bytes(B, S), dtype=torch.uint8, device=DEV)
+    bits, _ = dsa.mask_views(mask, B, S)
+    for i, (row0, n) in enumerate(slabs):
+        sc = _long_rows(B, n, S, row0, score_dtype, seed=100 + i)
+        dsa.dsa_topk(sc.to(DEV).contiguous(), seg_dev, B, S, K, row0, n, idx, mask)
+        torch.cuda.synchronize()
+        want = ref.topk(sc.double().numpy(), seg, np.arange(row0, row0 + n), K, S)
+        del sc
+        got = idx[:, row0:row0 + n].cpu().numpy()
+        assert np.array_equal(got, want), row0
+        wb = ref.pack_bits(ref.selection_matrix(want, S)).view(np.int64)
+        assert np.array_equal(bits[:, row0:row0 + n].cpu().numpy(), wb), row0
+
+
 # --------------------------------------------------------------- attention
 def _sets(cfg, x):
     return inputs.random_index_sets(cfg.B, cfg.S, cfg.K, _seg_np(x), seed=cfg.seed + 1)
