@@ -65,15 +65,19 @@ def work(cfg, seg_np):
         "pairs": pairs, "selected": selected,
         "indexer": pairs * cfg.Hi * 2 * cfg.Di,
         "fwd": selected * cfg.H * 2 * (cfg.Dqk + cfg.Dv),
+        # backward: dP = dO V^T, dV = P^T dO, dK = dS^T Q (the dK/dV kernel) and
+        # dQ = dS K (the dQ kernel); recomputing S = Q K^T (both kernels) and dP
+        # (the dQ kernel) is not counted
         "bwd": selected * cfg.H * 4 * (cfg.Dqk + cfg.Dv),
         "bwd_dq": selected * cfg.H * 2 * cfg.Dqk,
+        "bwd_dkdv": selected * cfg.H * 2 * (cfg.Dqk + 2 * cfg.Dv),
         "topk_bytes": topk_bytes,
     }
 
 
 KERNEL_SRC = {"index_scores": "indexer.hip", "topk": "topk.hip", "attn_fwd": "attn_fwd.hip",
               "attn_bwd_dq": "attn_bwd.hip", "attn_bwd_dkdv": "attn_bwd.hip"}
-KERNEL_SYM = {"index_scores": "index_scores_mfma_kernel", "topk": "topk_kernel", "attn_fwd": "attn_fwd_mfma_kernel",
+KERNEL_SYM = {"index_scores": "index_scores_mfma_kernel", "topk": "topk_reg_kernel", "attn_fwd": "attn_fwd_mfma_kernel",
               "attn_bwd_dq": "attn_bwd_dq_kernel", "attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
 
@@ -178,6 +182,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-long", action="store_true",
                     help="skip timing indexer + top-k at the 32K and 128K workloads")
+    ap.add_argument("--long-only", action="store_true",
+                    help="only time indexer + top-k at the 32K and 128K workloads (one JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
@@ -192,6 +198,25 @@ def main():
     cfg = inputs.CONFIGS[args.config]
     dsa.lib()
     dev = "cuda"
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
+
+    if args.long_only:
+        selection = {}
+        for key in ("c3", "c5"):
+            log(f"indexer + top-k at {inputs.CONFIGS[key].name}")
+            r = selection_long(key)
+            selection[f"S{r['S']}"] = r
+            log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms")
+        print(json.dumps({"metric": "indexer + top-k ms", "selection": selection}), flush=True)
+        return
     log(f"config {cfg.name}: generating inputs on the GPU")
     x = inputs.make(cfg, device=dev)
     seg_np = None if x["seg"] is None else x["seg"].cpu().numpy()
@@ -223,16 +248,6 @@ def main():
                                          path.dk, path.dv, path.ws)
             mark(5)
 
-    if args.copy_mib:
-        n = args.copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {n} bytes read, {n} bytes written")
-        del src, dst
-
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -260,7 +275,7 @@ def main():
         "topk": ("hbm", wk["topk_bytes"]),
         "attn_fwd": ("mfma", wk["fwd"]),
         "attn_bwd_dq": ("mfma", wk["bwd_dq"]),
-        "attn_bwd_dkdv": ("mfma", wk["bwd"]),
+        "attn_bwd_dkdv": ("mfma", wk["bwd_dkdv"]),
     }
     kernels = {}
     for c in calls:

@@ -9,24 +9,18 @@
 // Selection rule: n = min(K, |valid(t)|) keys. Larger scores win. Among equal
 // scores the smaller key position wins, and -0 equals +0.
 //
-// One workgroup (4 waves) per query row. Rows short enough keep their keys in
-// LDS after one coalesced read; longer ones re-read global memory per pass.
-//   * |valid| <= K: every valid key is taken and the scores are never read.
-//   * otherwise the K-th largest key T is found exactly:
-//       1. min/max of the row's valid scores;
-//       2. a 2048-bin histogram that is linear in the score value. Bins are
-//          monotone in the value, so equal scores share a bin. Scores of a row
-//          are spread out, so few lanes collide on one LDS counter. The bin
-//          holding the K-th largest score is then a contiguous range of the
-//          order-preserving u32 keys [klo, khi];
-//       3. radix passes over (key - klo) >> shift with at most 2048 bins each,
-//          until the range is a single key T.
-//     Then c_gt = #{key > T} and c_eq = K - c_gt ties at T are taken,
-//     lowest positions first.
-//   * compaction walks the row in 64-key words, one word per wave step:
-//     ballot gives the word's selection bits (the bitmask word itself),
-//     and mbcnt over the ballots gives each selected lane its ascending slot
-//     in the index list. A first walk counts per wave; a second one writes.
+// One workgroup per query row, three kernels by row length L = t + 1:
+//   * L <= 4096: the row's keys in VGPRs (topk_reg_kernel);
+//   * longer rows: one read of the row that lists only the keys above a
+//     sampled lower bound of the threshold (topk_stash_kernel);
+//   * rows that list falls short for, and any row when K is too large for
+//     the list: a multi-pass kernel that re-reads the row (topk_long_kernel).
+// All of them find the K-th largest key T exactly, through a 2048-bin
+// histogram that is monotone in the score (equal scores share a bin) and
+// then the keys of T's bin; c_gt = #{key > T} and c_eq = K - c_gt ties at T
+// are taken, lowest positions first. |valid| <= K takes every valid key; a
+// causal-only row with L <= K never reads its scores. Each kernel emits the
+// ascending index list and the row's u64 mask words together.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -319,13 +313,11 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
   }
 }
 
-// ---- rows longer than 64 * 4 * kRegWords keys: one workgroup per row
-//
-// The row's scores are either copied once into LDS (global_load_lds, one
-// coalesced read) or, for rows too long for LDS, read from global memory in
-// every pass (the later passes then hit the caches). Wave w walks one
-// contiguous range of the row's 64-key words in order, lane = key position in
-// the word, so every count it needs is a running scalar: no per-word arrays.
+// ---- multi-pass selection of a long row (any K; the rows the single-read
+// kernel below leaves): one workgroup per row, the row's scores read from
+// global memory in every pass. Wave w walks one contiguous range of the row's
+// 64-key words in order, lane = key position in the word, so every count it
+// needs is a running scalar: no per-word arrays.
 //   1. The histogram's value range comes from a strided sample of 1024 valid
 //      scores. Values outside it go to the edge bins, so the bins stay
 //      monotone in the value (equal scores share a bin) and the result stays
@@ -343,6 +335,7 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
 //      index list (ties at T from the lowest positions) and, 64 words per
 //      store, the mask words.
 constexpr int kMaxLW = 16;        // most waves per workgroup
+constexpr int kRetry = -2;        // first index slot of a row left to the multi-pass kernel
 constexpr int kLCand = 256;       // candidates ranked directly (one per thread)
 constexpr int kSample = 1024;     // scores sampled for the histogram range
 
@@ -385,7 +378,7 @@ template <int NW> __device__ __forceinline__ void block_minmax_u(uint32_t& mn, u
 // writes b and count(bins > b). Needs count(all bins) >= need >= 1.
 template <int NT>
 __device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t& found_bin,
-                           uint32_t& found_above) {
+                           uint32_t& found_above, uint32_t* total = nullptr) {
   constexpr int PER = kNB / NT, NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t c[PER];
@@ -403,6 +396,11 @@ __device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, u
   __syncthreads();
   uint32_t running = incl - tot;  // keys in bins above this thread's chunk
   for (int w2 = wid + 1; w2 < NW; ++w2) running += red[w2];
+  if (total) {
+    uint32_t all = 0;
+    for (int w2 = 0; w2 < NW; ++w2) all += red[w2];
+    *total = all;
+  }
   __syncthreads();
 #pragma unroll
   for (int i = PER - 1; i >= 0; --i) {
@@ -417,18 +415,17 @@ __device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, u
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
-template <typename ST, bool IN_LDS, bool SEG, int NW>
+template <typename ST, bool SEG, int NW>
 __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ seg, int B, int S,
                                                             int K, int row0, int nrows, int rbeg, int rcount,
-                                                            int nw_max, int32_t* __restrict__ idx,
+                                                            int nw_max, bool retry_only, int32_t* __restrict__ idx,
                                                             uint64_t* __restrict__ bits) {
   constexpr int NT = 64 * NW;
   constexpr int kU = 8;  // words per step: all of their reads issued first
   __shared__ LongShared sh;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   uint64_t* segw = (uint64_t*)dyn;  // per word: same-segment positions <= t
-  unsigned char* rawl = (unsigned char*)(dyn + (SEG ? 2 * nw_max : 0));  // the row's scores
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -443,6 +440,7 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   // this wave's words [wa, wb)
   const int nwp = (nw + NW - 1) / NW;
   const int wa = min(nw, wid * nwp), wb = min(nw, wa + nwp);
+  if (retry_only && idx_row[0] != kRetry) return;  // uniform: the row is done
 
   if (!SEG && L <= K) {
     // causal-only row with at most K keys: every key 0..t, no score read
@@ -476,41 +474,15 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   };
   const bool take_all = n_valid <= (uint32_t)K;
 
-  // the row's bytes start `off` bytes into the first copied dword
-  const uintptr_t rs = (uintptr_t)row;
-  const int off = (int)(rs & 3);
-  if (IN_LDS && !take_all) {
-    const uintptr_t ra = rs - off;
-    const uintptr_t last = (rs + (uintptr_t)L * sizeof(ST) - 1) & ~(uintptr_t)3;
-    const int nchunk = (off + L * (int)sizeof(ST) + 255) / 256;
-    for (int c = wid; c < nchunk; c += NW) {
-      uintptr_t src = ra + 256 * (uintptr_t)c + 4 * lane;
-      src = src > last ? last : src;  // past the row's end: a duplicate of its last dword
-      g2lds4((const void*)src, rawl + 256 * c);
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-  auto score = [&](int s) -> float {
-    if constexpr (IN_LDS) {
-      if constexpr (sizeof(ST) == 4) return *(const float*)(rawl + off + 4 * s);
-      else return bf2f(*(const uint16_t*)(rawl + off + 2 * s));
-    } else {
-      return ScoreLoad<ST>::get(row, s);
-    }
-  };
+  auto score = [&](int s) -> float { return ScoreLoad<ST>::get(row, s); };
   // scores of words w0 .. w0 + kU - 1 (those below wb), every read issued
-  // before any use: in LDS the copy's tail is padded, so positions past t in
-  // the row's last word are read (and dropped); global memory is not read there
+  // before any use; positions past t are not read
   auto load_words = [&](int w0, float (&x)[kU]) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int w = w0 + u, s = 64 * w + lane;
       x[u] = 0.f;
-      if (w < wb) {  // wave-uniform
-        if (IN_LDS) x[u] = score(s);
-        else if (s < L) x[u] = score(s);
-      }
+      if (w < wb && s < L) x[u] = score(s);
     }
   };
 
@@ -702,6 +674,406 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   for (int i = n + tid; i < K; i += NT) idx_row[i] = -1;
 }
 
+// ---- rows longer than 64 * 4 * kRegWords keys, read once
+//
+// A strided sample of the row (32 runs of 64 consecutive keys) gives a lower
+// bound lo on the threshold, chosen so that about 2K of the row's keys are at
+// or above it. One pass over the row (16-byte loads, every score read once)
+// lists each valid key >= lo as (position << 11 | bin), with a 2048-bin
+// histogram over [lo, sampled max]; every other key costs two compares. Any
+// lo for which at least K keys are listed gives the exact result: every key
+// in a bin above the K-th largest's bin is listed, and so are the largest
+// keys of that bin. The K-th largest key T is then found by ranking the
+// listed keys of its bin (their scores re-read by position), ties at T are
+// ordered by position, and the selected positions are set in a per-word LDS
+// mask that is turned into the index list and the mask words, one word per
+// thread. A row whose list comes out short, or longer than the LDS list
+// holds, is marked with -2 in its first index slot and left to the
+// multi-pass kernel.
+//
+// In the pass, each lane holds kSU 16-byte blocks per stage in VGPRs, with the
+// next two stages in flight. Each wave lists into its own region of the list,
+// at slots from a wave-wide prefix of the lanes' counts: no atomics on the
+// list, and no waits inside the pass.
+constexpr int kStash = 6144;     // listed keys
+constexpr int kChunks = 32;      // sample: runs of 64 consecutive keys
+constexpr int kSB = 256;         // sample histogram bins
+constexpr int kSU = 2;           // 16-byte blocks per lane and stage (two stages in flight)
+constexpr uint32_t kHole = 0xffffffffu;  // a list slot whose key is not valid (other segment)
+
+struct StashShared {
+  uint32_t hist[kNB];
+  uint32_t shist[kSB];
+  uint32_t cand_key[kLCand];
+  uint32_t cand_pos[kLCand];
+  uint32_t red_u[2 * kMaxLW];
+  float red_f[2 * kMaxLW];
+  uint32_t wave_g[kMaxLW];   // per wave: listed keys, then selected keys of a word chunk
+  uint32_t samp_n[kMaxLW];   // per wave: valid sampled scores
+  uint32_t found_bin, found_above, ncand, thresh, thresh_above;
+};
+
+// order-preserving 16-bit key of a bfloat16 score (its bits); -0 maps like +0
+__device__ __forceinline__ uint32_t bkey16(uint32_t h) {
+  h &= 0xffffu;
+  if (h == 0x8000u) h = 0u;
+  return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
+}
+
+// dynamic LDS of topk_stash_kernel: the list, the selection mask, the
+// segment-validity words
+static size_t stash_lds_bytes(int nw_max, bool seg) {
+  return (size_t)kStash * 4 + (size_t)nw_max * (seg ? 16 : 8);
+}
+
+template <typename ST, bool SEG, int NW>
+__global__ __launch_bounds__(64 * NW) void topk_stash_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                             const int32_t* __restrict__ seg, int B, int S, int K,
+                                                             int row0, int nrows, int rbeg, int rcount, int nw_max,
+                                                             int32_t* __restrict__ idx,
+                                                             uint64_t* __restrict__ bits) {
+  constexpr int NT = 64 * NW;
+  constexpr int EPB = 16 / (int)sizeof(ST);  // scores per 16-byte block
+  constexpr int CPW = kChunks / NW;          // sample runs per wave
+  constexpr int kCapW = kStash / NW;         // list entries per wave
+  constexpr int kSPT = kStash / NT;          // list slots per thread
+  __shared__ StashShared sh;
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  uint32_t* stash = dyn;                         // the list
+  uint64_t* selw = (uint64_t*)(dyn + kStash);    // per word: the selected positions
+  uint64_t* segw = selw + nw_max;                // per word: same-segment positions <= t
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.x % B;
+  const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
+  const int t = row0 + r;
+  const int W = (S + 63) / 64;
+  const int L = t + 1, nw = (L + 63) / 64;
+  const ST* row = scores + ((size_t)b * nrows + r) * ld;
+  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
+  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
+
+  if (!SEG && L <= K) {
+    // causal-only row with at most K keys: every key 0..t, no score read
+    for (int i = tid; i < K; i += NT) idx_row[i] = i < L ? i : -1;
+    for (int w = tid; w < W; w += NT)
+      bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
+    return;
+  }
+  uint32_t n_valid = (uint32_t)L;
+  if (SEG) {
+    const int32_t* segb = seg + (size_t)b * S;
+    const int seg_t = segb[t];
+    uint32_t c = 0;
+    for (int w = wid; w < nw; w += NW) {
+      const int s = 64 * w + lane;
+      const uint64_t m = __ballot(s < L && segb[s] == seg_t);
+      if (lane == 0) segw[w] = m;
+      c += popc64(m);
+    }
+    if (lane == 0) sh.red_u[wid] = c;
+    __syncthreads();
+    n_valid = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) n_valid += sh.red_u[i];
+    __syncthreads();
+  }
+  auto valid_pos = [&](int p) -> bool {  // 0 <= p < L
+    if (SEG) return (segw[p >> 6] >> (p & 63)) & 1ull;
+    return true;
+  };
+  const bool take_all = n_valid <= (uint32_t)K;
+
+  // The sample's loads are issued first, then the first stage of the pass,
+  // which reads the 16-byte blocks [ra, ra + 16 * nblk) and stays in flight
+  // during the sample.
+  const uintptr_t rs = (uintptr_t)row, ra = rs & ~(uintptr_t)15;
+  const int nblk = (int)((rs + (uintptr_t)L * sizeof(ST) - ra + 15) / 16);
+  const int p_ra = -(int)((rs - ra) / sizeof(ST));  // position of the first block's first score
+  // derived from the row pointer, so the loads stay global (flat loads would
+  // also count against the LDS wait counter)
+  const u32x4* blk = (const u32x4*)((const char*)row - (rs - ra));
+  auto load_stage = [&](int i0, u32x4 (&v)[kSU]) {
+#pragma unroll
+    for (int u = 0; u < kSU; ++u) {
+      const int i = i0 + u * NT;
+      if (i < nblk) v[u] = blk[i];
+    }
+  };
+  float sx[CPW];
+  bool sv[CPW];
+  u32x4 vcur[kSU], vnxt[kSU];  // stages st + 1 and st + 2 while stage st is scanned
+  if (!take_all) {
+    // sample: run c starts at c * (L - 64) / (kChunks - 1)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int c = wid + NW * j;
+      const int p = (int)(((int64_t)c * (L - 64)) / (kChunks - 1)) + lane;
+      sv[j] = valid_pos(p);
+      sx[j] = sv[j] ? ScoreLoad<ST>::get(row, p) : 0.f;
+    }
+    load_stage(tid, vcur);
+    load_stage(tid + kSU * NT, vnxt);
+  }
+
+  bool fail = false;
+  if (take_all) {
+    for (int w = tid; w < nw; w += NT) selw[w] = segw[w];
+  } else {
+    for (int w = tid; w < nw; w += NT) selw[w] = 0ull;
+    for (int i = tid; i < kNB; i += NT) sh.hist[i] = 0;
+    for (int i = tid; i < kSB; i += NT) sh.shist[i] = 0;
+    if (tid == 0) sh.ncand = 0;
+    float mn = INFINITY, mx = -INFINITY;
+    uint32_t nvs = 0;
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      if (sv[j]) {
+        mn = fminf(mn, sx[j]);
+        mx = fmaxf(mx, sx[j]);
+      }
+      nvs += popc64(__ballot(sv[j]));
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+      sh.red_f[wid] = mn;
+      sh.red_f[NW + wid] = mx;
+      sh.samp_n[wid] = nvs;
+    }
+    __syncthreads();
+    nvs = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      mn = fminf(mn, sh.red_f[i]);
+      mx = fmaxf(mx, sh.red_f[NW + i]);
+      nvs += sh.samp_n[i];
+    }
+    float lo = mn;
+    if (nvs < 64) {
+      fail = true;  // uniform: too few valid keys sampled
+    } else if (mx > mn) {
+      // lo: the lower edge of the sample-histogram bin holding the ks-th
+      // largest sample, ks sized so that about 2K of the row's valid keys
+      // lie at or above it
+      const float inv_s = (float)kSB / (mx - mn);
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+        if (sv[j]) atomicAdd(&sh.shist[(int)fminf(fmaxf((sx[j] - mn) * inv_s, 0.f), (float)(kSB - 1))], 1u);
+      __syncthreads();
+      if (wid == 0) {
+        const uint32_t ks =
+            (uint32_t)min((uint64_t)nvs, max((uint64_t)1, ((uint64_t)nvs * 2 * K + n_valid - 1) / n_valid));
+        constexpr int PER = kSB / 64;
+        uint32_t c[PER], tot = 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          c[i] = sh.shist[PER * lane + i];
+          tot += c[i];
+        }
+        uint32_t incl = tot;  // samples in the bins of this lane and the lanes above
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_down(incl, o);
+          if (lane + o < 64) incl += y;
+        }
+        uint32_t running = incl - tot;
+#pragma unroll
+        for (int i = PER - 1; i >= 0; --i) {
+          if (running < ks && running + c[i] >= ks) sh.found_bin = PER * lane + i;
+          running += c[i];
+        }
+      }
+      __syncthreads();
+      lo = mn + (float)sh.found_bin / inv_s;
+    }
+    if (!fail) {
+      // bins: fp32 scores, linear in the value over [lo, max]; bf16 scores,
+      // one bin per value from the largest bf16 value below lo (exact while
+      // the listed values span fewer than 2047 of them)
+      const float inv = mx > lo ? (float)kNB / (mx - lo) : 1e30f;
+      const uint32_t klo16 = bkey16(__float_as_uint(lo) >> 16);
+      const uint32_t kb16 = klo16 > 0 ? klo16 - 1 : 0;
+      auto bin_of = [&](float x) -> int {
+        if constexpr (sizeof(ST) == 2) return (int)min(bkey16(__float_as_uint(x) >> 16) - kb16, (uint32_t)(kNB - 1));
+        else return (int)fminf(fmaxf((x - lo) * inv, 0.f), (float)(kNB - 1));
+      };
+      // the pass: list this wave's valid scores >= lo in its region of the list
+      uint32_t* wst = stash + wid * kCapW;
+      uint32_t listed = 0;  // this wave's slots so far (uniform)
+      const int nstage = (nblk + kSU * NT - 1) / (kSU * NT);
+      for (int st = 0; st < nstage; ++st) {
+        const int i0 = tid + st * kSU * NT;
+        u32x4 v[kSU];
+#pragma unroll
+        for (int u = 0; u < kSU; ++u) {
+          v[u] = vcur[u];
+          vcur[u] = vnxt[u];
+        }
+        load_stage(i0 + 2 * kSU * NT, vnxt);  // two stages ahead
+        uint32_t msk = 0;  // bit u * EPB + e: score e of block u is listed
+#pragma unroll
+        for (int u = 0; u < kSU; ++u) {
+          const int i = i0 + u * NT;
+          const uint32_t pb = (uint32_t)(p_ra + i * EPB);
+#pragma unroll
+          for (int e = 0; e < EPB; ++e) {
+            float x;
+            if constexpr (sizeof(ST) == 4) x = __uint_as_float(v[u][e]);
+            else x = __uint_as_float((e & 1) ? (v[u][e >> 1] & 0xffff0000u) : (v[u][e >> 1] << 16));
+            if (i < nblk && pb + e < (uint32_t)L && x >= lo) msk |= 1u << (u * EPB + e);
+          }
+        }
+        const uint32_t cnt = __popc(msk);
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(incl, o);
+          if (lane >= o) incl += y;
+        }
+        uint32_t slot = listed + incl - cnt;
+        // the listed scores, in a static walk over the stage (each write is
+        // masked to the lanes that list that score)
+#pragma unroll
+        for (int u = 0; u < kSU; ++u) {
+#pragma unroll
+          for (int e = 0; e < EPB; ++e) {
+            if ((msk >> (u * EPB + e)) & 1u) {
+              float x;
+              if constexpr (sizeof(ST) == 4) x = __uint_as_float(v[u][e]);
+              else x = __uint_as_float((e & 1) ? (v[u][e >> 1] & 0xffff0000u) : (v[u][e >> 1] << 16));
+              const int p = p_ra + (i0 + u * NT) * EPB + e;
+              uint32_t ent = kHole;
+              if (valid_pos(p)) {
+                const int bn = bin_of(x);
+                atomicAdd(&sh.hist[bn], 1u);
+                ent = ((uint32_t)p << 11) | (uint32_t)bn;
+              }
+              if (slot < (uint32_t)kCapW) wst[slot] = ent;
+              ++slot;
+            }
+          }
+        }
+        listed += __builtin_amdgcn_readlane(incl, 63);
+      }
+      if (lane == 0) sh.wave_g[wid] = listed;
+      __syncthreads();  // the list and its histogram are complete
+      bool over = false;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) over |= sh.wave_g[w2] > (uint32_t)kCapW;
+      // this thread's list slots j = tid + NT * q (slot j % kCapW of wave j / kCapW)
+      uint32_t ent[kSPT];
+#pragma unroll
+      for (int q = 0; q < kSPT; ++q) {
+        const int j = tid + NT * q;
+        ent[q] = !over && (uint32_t)(j % kCapW) < sh.wave_g[j / kCapW] ? stash[j] : kHole;
+      }
+      uint32_t nst = 0;  // valid listed keys: the histogram's total
+      find_bin_n<NT>(sh.hist, (uint32_t)K, sh.red_u, sh.found_bin, sh.found_above, &nst);
+      if (over || nst < (uint32_t)K) {
+        fail = true;
+      } else {
+        const uint32_t bstar = sh.found_bin;
+        const uint32_t need = (uint32_t)K - sh.found_above;
+#pragma unroll
+        for (int q = 0; q < kSPT; ++q) {
+          if (ent[q] == kHole) continue;
+          const uint32_t bn = ent[q] & (kNB - 1), p = ent[q] >> 11;
+          if (bn == bstar) {
+            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+            if (slot < (uint32_t)kLCand) sh.cand_pos[slot] = p;
+          } else if (bn > bstar) {
+            atomicOr((unsigned long long*)&selw[p >> 6], 1ull << (p & 63));
+          }
+        }
+        __syncthreads();
+        const uint32_t nc = sh.ncand;
+        if (nc > (uint32_t)kLCand) {
+          fail = true;
+        } else if (sizeof(ST) == 2 && bstar < (uint32_t)(kNB - 1)) {
+          // bf16, exact bin: every candidate equals T; the need lowest positions are taken
+          if (tid < (int)nc) {
+            const uint32_t p = sh.cand_pos[tid];
+            bool sel = true;
+            if (need < nc) {
+              uint32_t below = 0;
+              for (uint32_t j = 0; j < nc; ++j) below += sh.cand_pos[j] < p;
+              sel = below < need;
+            }
+            if (sel) atomicOr((unsigned long long*)&selw[p >> 6], 1ull << (p & 63));
+          }
+        } else {
+          if (tid < (int)nc) sh.cand_key[tid] = fkey(ScoreLoad<ST>::get(row, (int)sh.cand_pos[tid]));
+          __syncthreads();
+          // candidate i is T when #greater < need <= #greater + #equal
+          if (tid < (int)nc) {
+            const uint32_t ki = sh.cand_key[tid];
+            uint32_t gt = 0, eq = 0;
+            for (uint32_t j = 0; j < nc; ++j) {
+              const uint32_t kj = sh.cand_key[j];
+              gt += kj > ki;
+              eq += kj == ki;
+            }
+            if (gt < need && need <= gt + eq) {
+              sh.thresh = ki;  // every thread that writes holds the same key
+              sh.thresh_above = gt;
+            }
+          }
+          __syncthreads();
+          const uint32_t T = sh.thresh, c_eq = need - sh.thresh_above;
+          if (tid < (int)nc) {
+            const uint32_t k = sh.cand_key[tid], p = sh.cand_pos[tid];
+            bool sel = k > T;
+            if (k == T) {  // ties at T: the lowest positions
+              uint32_t below = 0;
+              for (uint32_t j = 0; j < nc; ++j) below += sh.cand_key[j] == T && sh.cand_pos[j] < p;
+              sel = below < c_eq;
+            }
+            if (sel) atomicOr((unsigned long long*)&selw[p >> 6], 1ull << (p & 63));
+          }
+        }
+      }
+    }
+  }
+  if (fail) {  // uniform
+    if (tid == 0) idx_row[0] = kRetry;
+    return;
+  }
+  __syncthreads();
+
+  // ordered output, one mask word per thread: an exclusive scan of the
+  // words' counts gives each word its first slot
+  uint32_t base = 0;  // selected keys in the words before this chunk
+  for (int c0 = 0; c0 < nw; c0 += NT) {
+    const int w = c0 + tid;
+    const uint64_t m = w < nw ? selw[w] : 0ull;
+    const uint32_t cnt = popc64(m);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) sh.wave_g[wid] = incl;
+    __syncthreads();
+    uint32_t pos = base + incl - cnt, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const uint32_t c = sh.wave_g[w2];
+      if (w2 < wid) pos += c;
+      tot += c;
+    }
+    __syncthreads();
+    if (w < nw) bits_row[w] = m;
+    for (uint64_t mm = m; mm; mm &= mm - 1) idx_row[pos++] = 64 * w + __builtin_ctzll(mm);
+    base += tot;
+  }
+  for (int w = nw + tid; w < W; w += NT) bits_row[w] = 0ull;
+  const int n = take_all ? (int)n_valid : K;
+  for (int i = n + tid; i < K; i += NT) idx_row[i] = -1;
+}
+
 // Bits of caller-given index lists: one workgroup per row, the row's words
 // assembled in LDS with atomic ORs, then written out whole.
 __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restrict__ idx,
@@ -742,56 +1114,63 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restr
   cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
 }
 
-template <typename ST, bool IN_LDS, bool SEG, int NW>
-static hipError_t launch_long_t(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
-                                int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
-                                hipStream_t st) {
-  const int Lmax = row0 + rbeg + rcount;  // longest row of the range
-  const int nw_max = (Lmax + 63) / 64;
-  size_t shm = SEG ? (size_t)nw_max * 8 : 0;
-  // a bf16 row may start 2 bytes into its first copied dword; reads run to the end of the last word
-  if (IN_LDS) shm += ((size_t)Lmax * sizeof(ST) + (sizeof(ST) == 2 ? 2 : 0) + 255) / 256 * 256 + 256;
+template <typename ST, bool SEG, int NW>
+static hipError_t launch_multipass(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
+                                   int row0, int nrows, int rbeg, int rcount, bool retry_only, int32_t* idx,
+                                   uint64_t* bits, hipStream_t st) {
+  const int nw_max = (row0 + rbeg + rcount + 63) / 64;  // words of the range's longest row
+  const size_t shm = SEG ? (size_t)nw_max * 8 : 0;
   if (shm + sizeof(LongShared) > 160 * 1024) return hipErrorInvalidValue;
-  const void* fn = (const void*)topk_long_kernel<ST, IN_LDS, SEG, NW>;
+  const void* fn = (const void*)topk_long_kernel<ST, SEG, NW>;
   if (shm > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((topk_long_kernel<ST, IN_LDS, SEG, NW>), dim3((unsigned)((size_t)rcount * B)),
-                     dim3(64 * NW), shm, st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max,
-                     idx, bits);
+  hipLaunchKernelGGL((topk_long_kernel<ST, SEG, NW>), dim3((unsigned)((size_t)rcount * B)), dim3(64 * NW),
+                     shm, st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max, retry_only, idx, bits);
   return hipGetLastError();
 }
-// rows in LDS with up to 64 KB of scores: 8 waves, two workgroups per CU;
-// longer rows: 16 waves, one workgroup per CU
-template <typename ST, bool IN_LDS, int NW>
-static hipError_t launch_long(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
-                              int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
-                              hipStream_t st) {
-  return seg ? launch_long_t<ST, IN_LDS, true, NW>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx,
-                                                   bits, st)
-             : launch_long_t<ST, IN_LDS, false, NW>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx,
-                                                    bits, st);
+template <typename ST, bool SEG, int NW>
+static hipError_t launch_stash(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K, int row0,
+                               int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits, hipStream_t st) {
+  const int nw_max = (row0 + rbeg + rcount + 63) / 64;
+  const size_t shm = stash_lds_bytes(nw_max, SEG);
+  if (shm + sizeof(StashShared) > 160 * 1024) return hipErrorInvalidValue;
+  const void* fn = (const void*)topk_stash_kernel<ST, SEG, NW>;
+  if (shm > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((topk_stash_kernel<ST, SEG, NW>), dim3((unsigned)((size_t)rcount * B)), dim3(64 * NW), shm,
+                     st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max, idx, bits);
+  return hipGetLastError();
+}
+// rows [rbeg, rbeg + rcount) of the slab, all longer than 64 * 4 * kRegWords keys
+template <typename ST, bool SEG>
+static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K, int row0,
+                                   int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits, hipStream_t st) {
+  if (2 * K > kStash)  // the listed keys could not hold the selection: multi-pass only
+    return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, false, idx, bits, st);
+  hipError_t e = launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
+  if (e != hipSuccess) return e;
+  // rows the single pass left (marked in their first index slot)
+  return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, true, idx, bits, st);
 }
 
 // Rows are routed by length L = t + 1 (longest first): up to 64 * 4 *
-// kRegWords keys in VGPRs; up to 64 KB of scores in LDS (two workgroups per
-// CU); up to 128 KB in LDS (one per CU); longer rows read global memory.
+// kRegWords keys in VGPRs; longer rows are read once into a short list of
+// their largest keys, with the multi-pass kernel behind for rows where the
+// list misses.
 template <typename ST>
 static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
                                 int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
   const ST* sc = (const ST*)scores;
   const int l_reg = 64 * 4 * kRegWords;
-  const int l_small = (int)(64 * 1024 / sizeof(ST)), l_big = 2 * l_small;
-  auto upto = [&](int l) { return max(0, min(nrows, l - row0)); };  // rows with L <= l
-  const int n_reg = upto(l_reg), n_small = upto(l_small), n_big = upto(l_big);
+  const int n_reg = max(0, min(nrows, l_reg - row0));  // rows with L <= l_reg
   hipError_t e = hipSuccess;
-  if (nrows > n_big)
-    e = launch_long<ST, false, 16>(sc, ld, seg, B, S, K, row0, nrows, n_big, nrows - n_big, idx, bits, st);
-  if (e == hipSuccess && n_big > n_small)
-    e = launch_long<ST, true, 16>(sc, ld, seg, B, S, K, row0, nrows, n_small, n_big - n_small, idx, bits, st);
-  if (e == hipSuccess && n_small > n_reg)
-    e = launch_long<ST, true, 8>(sc, ld, seg, B, S, K, row0, nrows, n_reg, n_small - n_reg, idx, bits, st);
+  if (nrows > n_reg)
+    e = seg ? launch_long_rows<ST, true>(sc, ld, seg, B, S, K, row0, nrows, n_reg, nrows - n_reg, idx, bits, st)
+            : launch_long_rows<ST, false>(sc, ld, seg, B, S, K, row0, nrows, n_reg, nrows - n_reg, idx, bits, st);
   if (e == hipSuccess && n_reg > 0) {
     hipLaunchKernelGGL((topk_reg_kernel<ST>), dim3((unsigned)((size_t)n_reg * B)), dim3(256), 0, st, sc, ld,
                        seg, B, S, K, row0, nrows, 0, n_reg, idx, bits);
