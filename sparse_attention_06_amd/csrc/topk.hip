@@ -335,7 +335,6 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
 //      index list (ties at T from the lowest positions) and, 64 words per
 //      store, the mask words.
 constexpr int kMaxLW = 16;        // most waves per workgroup
-constexpr int kRetry = -2;        // first index slot of a row left to the multi-pass kernel
 constexpr int kLCand = 256;       // candidates ranked directly (one per thread)
 constexpr int kSample = 1024;     // scores sampled for the histogram range
 
@@ -415,32 +414,22 @@ __device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, u
 
 __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popcll(m); }
 
+// One row t of one batch row: scores `row` (positions 0..t), segment IDs
+// `segb` of that batch row (SEG), outputs idx_row / bits_row. sh and segw
+// (one u64 per 64-key word, SEG) are the workgroup's LDS.
 template <typename ST, bool SEG, int NW>
-__global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict__ scores, int64_t ld,
-                                                            const int32_t* __restrict__ seg, int B, int S,
-                                                            int K, int row0, int nrows, int rbeg, int rcount,
-                                                            int nw_max, bool retry_only, int32_t* __restrict__ idx,
-                                                            uint64_t* __restrict__ bits) {
+__device__ void multipass_row(const ST* __restrict__ row, const int32_t* __restrict__ segb, int S, int K, int t,
+                              int32_t* __restrict__ idx_row, uint64_t* __restrict__ bits_row, LongShared& sh,
+                              uint64_t* segw) {
   constexpr int NT = 64 * NW;
   constexpr int kU = 8;  // words per step: all of their reads issued first
-  __shared__ LongShared sh;
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-  uint64_t* segw = (uint64_t*)dyn;  // per word: same-segment positions <= t
-
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x % B;
-  const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
-  const int t = row0 + r;
   const int W = (S + 63) / 64;
   const int L = t + 1, nw = (L + 63) / 64;
-  const ST* row = scores + ((size_t)b * nrows + r) * ld;
-  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
-  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
   // this wave's words [wa, wb)
   const int nwp = (nw + NW - 1) / NW;
   const int wa = min(nw, wid * nwp), wb = min(nw, wa + nwp);
-  if (retry_only && idx_row[0] != kRetry) return;  // uniform: the row is done
 
   if (!SEG && L <= K) {
     // causal-only row with at most K keys: every key 0..t, no score read
@@ -451,7 +440,6 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   }
   uint32_t n_valid = (uint32_t)L;
   if (SEG) {
-    const int32_t* segb = seg + (size_t)b * S;
     const int seg_t = segb[t];
     uint32_t c = 0;
     for (int w = wa; w < wb; ++w) {
@@ -674,6 +662,21 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   for (int i = n + tid; i < K; i += NT) idx_row[i] = -1;
 }
 
+template <typename ST, bool SEG, int NW>
+__global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                            const int32_t* __restrict__ seg, int B, int S,
+                                                            int K, int row0, int nrows, int rbeg, int rcount,
+                                                            int32_t* __restrict__ idx, uint64_t* __restrict__ bits) {
+  __shared__ LongShared sh;
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  const int b = blockIdx.x % B;
+  const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
+  const int t = row0 + r;
+  multipass_row<ST, SEG, NW>(scores + ((size_t)b * nrows + r) * ld, SEG ? seg + (size_t)b * S : nullptr, S, K, t,
+                             idx + ((size_t)b * S + t) * K, bits + ((size_t)b * S + t) * ((S + 63) / 64), sh,
+                             (uint64_t*)dyn);
+}
+
 // ---- rows longer than 64 * 4 * kRegWords keys, read once
 //
 // A strided sample of the row (32 runs of 64 consecutive keys) gives a lower
@@ -688,8 +691,7 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
 // ordered by position, and the selected positions are set in a per-word LDS
 // mask that is turned into the index list and the mask words, one word per
 // thread. A row whose list comes out short, or longer than the LDS list
-// holds, is marked with -2 in its first index slot and left to the
-// multi-pass kernel.
+// holds, is finished by the multi-pass selection in the same workgroup.
 //
 // In the pass, each lane holds kSU 16-byte blocks per stage in VGPRs, with the
 // next two stages in flight. Each wave lists into its own region of the list,
@@ -1036,8 +1038,11 @@ __global__ __launch_bounds__(64 * NW) void topk_stash_kernel(const ST* __restric
       }
     }
   }
-  if (fail) {  // uniform
-    if (tid == 0) idx_row[0] = kRetry;
+  if (fail) {  // uniform: the multi-pass selection, its state in the list's LDS
+    static_assert(sizeof(LongShared) <= kStash * 4, "multi-pass state must fit the list");
+    __syncthreads();
+    multipass_row<ST, SEG, NW>(row, SEG ? seg + (size_t)b * S : nullptr, S, K, t, idx_row, bits_row,
+                               *reinterpret_cast<LongShared*>(stash), segw);
     return;
   }
   __syncthreads();
@@ -1116,8 +1121,8 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restr
 
 template <typename ST, bool SEG, int NW>
 static hipError_t launch_multipass(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
-                                   int row0, int nrows, int rbeg, int rcount, bool retry_only, int32_t* idx,
-                                   uint64_t* bits, hipStream_t st) {
+                                   int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
+                                   hipStream_t st) {
   const int nw_max = (row0 + rbeg + rcount + 63) / 64;  // words of the range's longest row
   const size_t shm = SEG ? (size_t)nw_max * 8 : 0;
   if (shm + sizeof(LongShared) > 160 * 1024) return hipErrorInvalidValue;
@@ -1127,7 +1132,7 @@ static hipError_t launch_multipass(const ST* scores, int64_t ld, const int32_t* 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((topk_long_kernel<ST, SEG, NW>), dim3((unsigned)((size_t)rcount * B)), dim3(64 * NW),
-                     shm, st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max, retry_only, idx, bits);
+                     shm, st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits);
   return hipGetLastError();
 }
 template <typename ST, bool SEG, int NW>
@@ -1150,17 +1155,14 @@ template <typename ST, bool SEG>
 static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K, int row0,
                                    int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits, hipStream_t st) {
   if (2 * K > kStash)  // the listed keys could not hold the selection: multi-pass only
-    return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, false, idx, bits, st);
-  hipError_t e = launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
-  if (e != hipSuccess) return e;
-  // rows the single pass left (marked in their first index slot)
-  return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, true, idx, bits, st);
+    return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
+  return launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
 }
 
 // Rows are routed by length L = t + 1 (longest first): up to 64 * 4 *
 // kRegWords keys in VGPRs; longer rows are read once into a short list of
-// their largest keys, with the multi-pass kernel behind for rows where the
-// list misses.
+// their largest keys, with the multi-pass selection behind for rows where
+// the list misses.
 template <typename ST>
 static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
                                 int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
