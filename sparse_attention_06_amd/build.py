@@ -27,7 +27,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # Per-file extras. NaN inputs are outside the library's contract, so the
 # indexer's ReLU (a float max) needs no IEEE NaN canonicalisation; in the
 # attention kernels the same flags cost registers, so they stay off there.
-EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+# The indexer also keeps its MFMA accumulators in architectural VGPRs (its
+# register budget allows it), so its epilogue needs no v_accvgpr_read moves;
+# the attention kernels already get that form from the compiler.
+EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():
