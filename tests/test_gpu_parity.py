@@ -189,16 +189,19 @@ def _long_rows(B, n, S, row0, dtype, seed):
 
 
 @pytest.mark.parametrize("score_dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("segments", [None, (3000, 20000)])
-def test_topk_long_rows(score_dtype, segments):
-    """Rows longer than 4096 keys on both sides of every length at which the
-    selection changes kernels (scores in VGPRs / 64 KB and 128 KB of scores
-    in LDS / read from global memory), as slab calls of whole query tiles:
-    bit-exact index lists and mask rows."""
-    B, K = 2, 300
-    if score_dtype == torch.float32:   # lengths 4096, 16384, 32768
+@pytest.mark.parametrize("segments,K", [(None, 300), ((3000, 20000), 300), (None, 3500)])
+def test_topk_long_rows(score_dtype, segments, K):
+    """Rows on both sides of 4096 keys (scores in VGPRs / longer rows read
+    once into a list of their largest keys, with the multi-pass selection
+    behind it; K = 3500 is too large for the list, so long rows go straight to
+    the multi-pass kernel), as slab calls of whole query tiles, with ties,
+    signed zeros, outliers and constant rows: bit-exact index lists and mask
+    rows."""
+    B = 2
+    # slabs across 4096 keys, at 16K / 32K / 64K, and the ragged end at S
+    if score_dtype == torch.float32:
         S, slabs = 33000, [(3968, 256), (16256, 256), (32640, 256), (32896, 104)]
-    else:                              # lengths 4096, 32768, 65536
+    else:
         S, slabs = 66000, [(3968, 256), (32640, 256), (65408, 256), (65920, 80)]
     seg = None if segments is None else inputs.segment_ids(B, S, segments[0], segments[1], seed=3)
     seg_dev = None if seg is None else torch.from_numpy(seg).to(DEV).contiguous()
