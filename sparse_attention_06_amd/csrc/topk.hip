@@ -1101,22 +1101,38 @@ __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restri
   for (int w = threadIdx.x; w < W; w += 256) out[w] = words[w];
 }
 
-// Tile classes of query tiles [qt0, qt1): thread per key tile (one mask word).
-__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int B,
-                                                         int S, int qt0, uint8_t* __restrict__ cls) {
+// Tile classes of query tiles [qt0, qt1): a workgroup per (query tile, 64
+// key tiles). Lane = key tile (one mask word per row), wave w takes rows
+// t0 + 32w .. t0 + 32w + 31 of the query tile, and the four waves' OR and AND
+// of their words are combined in LDS.
+__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int B, int S,
+                                                         int qt0, uint8_t* __restrict__ cls) {
+  __shared__ uint64_t s_or[4][64], s_and[4][64];
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
-  const int kt = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int kt = blockIdx.x * 64 + lane;
   const int qt = qt0 + blockIdx.y, b = blockIdx.z;
-  if (kt >= NK) return;
   const int t0 = qt * 128, t1 = min(S, t0 + 128);
+  const int ta = t0 + 32 * wv, tb = min(t1, ta + 32);
   uint64_t o = 0ull, a = ~0ull;
-  for (int t = t0; t < t1; ++t) {
-    const uint64_t w = bits[((size_t)b * S + t) * W + kt];
-    o |= w;
-    a &= w;
+  if (kt < NK) {
+    const uint64_t* col = bits + ((size_t)b * S) * W + kt;
+#pragma unroll 8
+    for (int t = ta; t < tb; ++t) {
+      const uint64_t w = col[(size_t)t * W];
+      o |= w;
+      a &= w;
+    }
   }
-  const bool keys_in_range = (kt + 1) * 64 <= S;
-  cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
+  s_or[wv][lane] = o;
+  s_and[wv][lane] = a;
+  __syncthreads();
+  if (wv == 0 && kt < NK) {
+    o = s_or[0][lane] | s_or[1][lane] | s_or[2][lane] | s_or[3][lane];
+    a = s_and[0][lane] & s_and[1][lane] & s_and[2][lane] & s_and[3][lane];
+    const bool keys_in_range = (kt + 1) * 64 <= S;
+    cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
+  }
 }
 
 template <typename ST, bool SEG, int NW>
@@ -1199,7 +1215,7 @@ hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int 
 hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int qt0, int qt1, uint8_t* cls,
                                hipStream_t st) {
   if (qt1 <= qt0) return hipSuccess;
-  dim3 grid((unsigned)((n_ktiles(S) + 255) / 256), (unsigned)(qt1 - qt0), (unsigned)B);
+  dim3 grid((unsigned)((n_ktiles(S) + 63) / 64), (unsigned)(qt1 - qt0), (unsigned)B);
   hipLaunchKernelGGL(tile_class_kernel, grid, dim3(256), 0, st, bits, B, S, qt0, cls);
   return hipGetLastError();
 }
