@@ -130,6 +130,22 @@ __device__ __forceinline__ void g2lds16_async(const void* gsrc, void* lds_base) 
                "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(save) : "v"(gsrc), "s"(lds_addr(lds_base)) : "memory");
 }
+// A wave-uniform pointer moved to SGPRs (read from the first active lane).
+template <typename T> __device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return (T*)(uintptr_t)((hi << 32) | lo);
+}
+// The same 16-byte copy from a wave-uniform base (SGPR pair) plus a per-lane
+// 32-bit byte offset: no 64-bit address arithmetic per lane. `gbase` must be
+// wave-uniform and held in SGPRs (see uniform_ptr).
+__device__ __forceinline__ void g2lds16_async_off(const void* gbase, uint32_t off, void* lds_base) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(off), "s"(gbase), "s"(lds_addr(lds_base)) : "memory");
+}
 __device__ __forceinline__ void g2lds4_async(const void* gsrc, void* lds_base) {
   uint32_t save;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"

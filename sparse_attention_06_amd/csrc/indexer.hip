@@ -28,13 +28,14 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     const uint16_t* __restrict__ w, const int32_t* __restrict__ seg, int B, int S, int row0,
     int nrows, OutT* __restrict__ scores, int64_t ld) {
   constexpr int Hi = HB * 32, Di = KS * 16;
-  constexpr int TILE = 64;                   // keys per iteration: two 32-key MFMA column blocks
+  constexpr int TILE = 128;                  // keys per iteration: four 32-key MFMA column blocks
   constexpr int SL = Di / 8 + 1;             // 16-byte slots per padded LDS key row
   constexpr int ROWE = SL * 8;               // padded row pitch in elements (conflict-free b128 reads)
   constexpr int NBLK = (TILE * SL + 63) / 64;  // 1 KB blocks per tile
   constexpr int BI = (NBLK + 3) / 4;           // blocks per wave
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][NBLK * 1024];
   __shared__ int32_t lseg[2][TILE];            // segment IDs of the tile's keys (when given)
+  static_assert((Di * 2 & (Di * 2 - 1)) == 0, "key rows are a power-of-two number of bytes");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   const int t = row0 + r;
   const int t_last = row0 + min(nrows - 1, rb * 4 + 3);
   const int nkt = t_last / TILE + 1;
-  const uint16_t* kb_base = k_idx + (size_t)b * S * Di;
+  const uint16_t* kb_base = uniform_ptr(k_idx + (size_t)b * S * Di);
 
   u32x4 afrag[HB][KS];
   float wreg[HB][16];
@@ -71,73 +72,120 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) wreg[hb][rr] = bf2f(wrow[hb * 32 + acc_row(rr, half)]);
     if (seg) seg_t = seg[(size_t)b * S + t];
+  } else {
+    // a row past the range runs the workgroup's MFMAs on zeros and stores nothing
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) afrag[hb][ks] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) wreg[hb][rr] = 0.f;
+    }
   }
 
-  // this wave's 1 KB blocks of the padded [64 rows][SL slots] tile; slots past
-  // a row's data or the tile copy a harmless chunk. Wave 1 also copies the
-  // tile's segment IDs. Copies go through the untracked asm path; each wave
-  // waits for its own before the barrier that publishes the tile.
-  auto issue = [&](int kt, int buf) {
+  // this wave's 1 KB blocks of the padded [TILE rows][SL slots] tile; slots
+  // past a row's data or the tile copy a harmless chunk. Waves 1 and 2 also
+  // copy the tile's segment IDs. Copies go through the untracked asm path;
+  // each wave waits for its own before the barrier that publishes the tile. A
+  // tile inside the sequence is copied from a scalar base plus fixed lane
+  // offsets; the last, partial one clamps its rows to S - 1.
+  uint32_t coff[BI];
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int j = wid + i * 4;
-      if (j < NBLK) {
-        const int slot = j * 64 + lane;
-        const bool in = slot < TILE * SL;
-        const int row = in ? slot / SL : 0, c = in ? min(slot % SL, SL - 2) : 0;
-        const int s = min(kt * TILE + row, S - 1);
-        g2lds16_async(kb_base + (size_t)s * Di + c * 8, lds[buf] + j * 1024);
-      }
+  for (int i = 0; i < BI; ++i) {
+    const int slot = (wid + i * 4) * 64 + lane;
+    const bool in = slot < TILE * SL;
+    const int row = in ? slot / SL : 0, c = in ? min(slot % SL, SL - 2) : 0;
+    coff[i] = (uint32_t)((row * Di + c * 8) * 2);
+  }
+  auto issue = [&](int kt, int buf) {
+    if ((kt + 1) * TILE <= S) {
+      const uint16_t* tb = kb_base + (size_t)kt * TILE * Di;
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+        if (wid + i * 4 < NBLK) g2lds16_async_off(tb, coff[i], lds[buf] + (wid + i * 4) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BI; ++i)
+        if (wid + i * 4 < NBLK) {
+          const int row = (int)(coff[i] / (Di * 2));
+          const int s = min(kt * TILE + row, S - 1);
+          const uint32_t c_bytes = coff[i] % (Di * 2);
+          g2lds16_async((const char*)(kb_base + (size_t)s * Di) + c_bytes, lds[buf] + (wid + i * 4) * 1024);
+        }
     }
-    if (seg && wid == 1) g2lds4_async(seg + (size_t)b * S + min(kt * TILE + lane, S - 1), lseg[buf]);
+    if (seg && (wid == 1 || wid == 2)) {
+      const int h = wid - 1;
+      g2lds4_async(seg + (size_t)b * S + min(kt * TILE + 64 * h + lane, S - 1), lseg[buf] + 64 * h);
+    }
   };
+  // [Hi x 32] scores of the 32-key column block sb of the tile in buffer buf
+  auto mfma_block = [&](int buf, int sb, f32x16 (&acc)[HB]) {
+    const uint16_t* sk = (const uint16_t*)lds[buf] + (sb * 32 + col) * ROWE + 8 * half;
+    u32x4 bq[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bq[ks] = *(const u32x4*)(sk + ks * 16);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[hb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma32(afrag[hb][ks], bq[ks], acc[hb]);
+  };
+  // w-weighted ReLU sum over the heads for key col; both lane halves end
+  // with the total
+  auto head_sum = [&](const f32x16 (&acc)[HB]) -> float {
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        part[rr & 3] = fmaf(wreg[hb][rr], fmaxf(acc[hb][rr], 0.f), part[rr & 3]);
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    return tot + __shfl_xor(tot, 32);
+  };
+
+  // Software pipeline over 32-key blocks: the MFMAs of one block run while
+  // the previous block's sums are formed, across the tile barrier. Lane l
+  // stores keys 128*kt + l (half 0 from block 0, half 1 from block 1) and
+  // 128*kt + 64 + l (blocks 2 and 3). The second store comes after the
+  // barrier and the first half a tile before the next one, so the wait for
+  // the next tile's copies does not wait for a store issued just before it.
+  OutT* out_row = scores + ((size_t)b * nrows + r) * ld;
+  f32x16 accA[HB], accB[HB];
   wait_vmem();  // this wave's query fragments and weights are in
   issue(0, 0);
-  OutT* out_row = scores + ((size_t)b * nrows + r) * ld;
+  wait_vmem();
+  lds_barrier();
+  if (nkt > 1) issue(1, 1);
+  mfma_block(0, 0, accA);
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
-    wait_vmem();
-    lds_barrier();  // tile kt visible; every wave is done with the other buffer
-    if (kt + 1 < nkt) issue(kt + 1, buf ^ 1);
-    const int s0 = kt * TILE;
-    if (active && s0 <= t) {
-      const uint16_t* sk = (const uint16_t*)lds[buf];
-      bool ok[2];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int s = s0 + sb * 32 + col;
-        ok[sb] = s <= t;
-        if (seg && ok[sb]) ok[sb] = lseg[buf][sb * 32 + col] == seg_t;
-      }
-      // both 32-key column blocks' MFMAs first: the epilogue of one overlaps the other's MFMAs
-      f32x16 acc[2][HB];
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[sb][hb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          const u32x4 bq = *(const u32x4*)(sk + (sb * 32 + col) * ROWE + ks * 16 + 8 * half);
-#pragma unroll
-          for (int hb = 0; hb < HB; ++hb) acc[sb][hb] = mfma32(afrag[hb][ks], bq, acc[sb][hb]);
-        }
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            part[rr & 3] = fmaf(wreg[hb][rr], fmaxf(acc[sb][hb][rr], 0.f), part[rr & 3]);
-        float tot = (part[0] + part[1]) + (part[2] + part[3]);
-        tot += __shfl_xor(tot, 32);
-        if (half == sb && ok[sb]) Elem<OutT>::store(out_row + s0 + sb * 32 + col, tot);
-      }
+    const int s_lo = kt * TILE + lane, s_hi = s_lo + 64;
+    bool ok_lo = active && s_lo <= t, ok_hi = active && s_hi <= t;
+    if (seg) {
+      ok_lo = ok_lo && lseg[buf][lane] == seg_t;
+      ok_hi = ok_hi && lseg[buf][64 + lane] == seg_t;
     }
+    mfma_block(buf, 1, accB);
+    const float t0 = head_sum(accA);
+    mfma_block(buf, 2, accA);
+    const float t1 = head_sum(accB);
+    if (ok_lo) Elem<OutT>::store(out_row + s_lo, half ? t1 : t0);
+    mfma_block(buf, 3, accB);
+    const float t2 = head_sum(accA);
+    float t3;
+    if (kt + 1 < nkt) {
+      wait_vmem();
+      lds_barrier();  // tile kt+1 visible; every wave is done with tile kt
+      if (kt + 2 < nkt) issue(kt + 2, buf);
+      mfma_block(buf ^ 1, 0, accA);
+      t3 = head_sum(accB);
+    } else {
+      t3 = head_sum(accB);
+    }
+    if (ok_hi) Elem<OutT>::store(out_row + s_hi, half ? t3 : t2);
   }
 }
 
