@@ -227,7 +227,7 @@ def main():
     seg = x["seg"]
     stream = torch.cuda.current_stream()
 
-    calls = ["index_scores", "topk", "attn_fwd"] + (["attn_bwd_dq", "attn_bwd_dkdv"] if cfg.backward else [])
+    calls = ["index_scores", "topk", "attn_fwd"] + (["attn_bwd_dkdv", "attn_bwd_dq"] if cfg.backward else [])
 
     def step(evs=None):
         def mark(i):
@@ -241,11 +241,11 @@ def main():
         dsa.dsa_sparse_attn_fwd(x["q"], x["k"], x["v"], path.mask, scale, path.o, path.lse)
         mark(3)
         if cfg.backward:
-            dsa.dsa_sparse_attn_bwd_dq(x["q"], x["k"], x["v"], path.o, x["dout"], path.lse, path.mask, scale,
-                                       path.dq, path.ws)
-            mark(4)
-            dsa.dsa_sparse_attn_bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], path.lse, path.mask, scale,
+            dsa.dsa_sparse_attn_bwd_dkdv(x["q"], x["k"], x["v"], path.o, x["dout"], path.lse, path.mask, scale,
                                          path.dk, path.dv, path.ws)
+            mark(4)
+            dsa.dsa_sparse_attn_bwd_dq(x["q"], x["k"], x["v"], x["dout"], path.lse, path.mask, scale,
+                                       path.dq, path.ws)
             mark(5)
 
     for i in range(args.warmup):

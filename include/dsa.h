@@ -179,8 +179,12 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  *   dq, dk    [B,S,H,Dqk] dtype out;  dv [B,S,H,Dv] dtype out
  *   workspace device scratch of at least dsa_bwd_workspace_bytes() bytes; it
  *             receives two float32 [B,H,S] arrays: D = rowsum(dout * o), then
- *             lse * log2(e) (the row's log-sum-exp in base-2 units).
- * Same as dsa_sparse_attn_bwd_dq followed by dsa_sparse_attn_bwd_dkdv on the
+ *             lse * log2(e) (the row's log-sum-exp in base-2 units). With the
+ *             bf16 MFMA path (Dqk = 192, Dv = 128) it also holds, from the
+ *             next 256-byte boundary, the dS tiles that the key-major kernel
+ *             hands to the dQ kernel: 2 bytes per causal (query, key) pair of
+ *             every (b, h), rounded to 32 x 64 blocks (about B*H*S*S bytes).
+ * Same as dsa_sparse_attn_bwd_dkdv followed by dsa_sparse_attn_bwd_dq on the
  * same stream. Deterministic: no atomics.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -189,23 +193,23 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
                                dsa_dtype dtype, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two halves of dsa_sparse_attn_bwd, one kernel each, for callers that
- * schedule them separately (say dK/dV on another stream after an event):
- *   _dq    query-major. Computes D and lse * log2(e) into the workspace,
- *          then dq.
- *   _dkdv  key-major. Reads both from the workspace, so it must be ordered
- *          after _dq on the same workspace. Writes dk and dv.
+/* The two halves of dsa_sparse_attn_bwd, for callers that schedule them
+ * separately:
+ *   _dkdv  key-major. Computes D and lse * log2(e) into the workspace, then
+ *          dk and dv; on the MFMA path it also leaves dS there.
+ *   _dq    query-major. Reads the workspace, so it must be ordered after
+ *          _dkdv on the same workspace. Writes dq.
  * Arguments as in dsa_sparse_attn_bwd. */
-dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
-                                  const void* dout, const float* lse, const void* mask,
-                                  int B, int S, int H, int Dqk, int Dv, float softmax_scale,
-                                  dsa_dtype dtype, void* dq, void* workspace,
-                                  size_t workspace_bytes, void* stream);
-dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v,
+dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
                                     const void* dout, const float* lse, const void* mask,
                                     int B, int S, int H, int Dqk, int Dv, float softmax_scale,
-                                    dsa_dtype dtype, void* dk, void* dv, const void* workspace,
+                                    dsa_dtype dtype, void* dk, void* dv, void* workspace,
                                     size_t workspace_bytes, void* stream);
+dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v,
+                                  const void* dout, const float* lse, const void* mask,
+                                  int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                                  dsa_dtype dtype, void* dq, const void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv);
 

@@ -59,11 +59,17 @@ size_t dsa_mask_bytes(int B, int S) {
   return dsa::bits_bytes(B, S) + (size_t)B * dsa::n_qtiles(S) * dsa::n_ktiles(S);
 }
 
+// D, then lse * log2(e) (float32 [B,H,S] each); for the MFMA head dims, the
+// dS^T fragments after them, from a 256-byte boundary
+static size_t bwd_frag_offset(int B, int S, int H) {
+  return (2 * (size_t)B * H * S * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv) {
-  (void)Dqk;
-  (void)Dv;
   if (B < 1 || S < 1 || H < 1) return 0;
-  return 2 * (size_t)B * H * S * sizeof(float);  // D, then lse * log2(e)
+  if (Dqk == 192 && Dv == 128)
+    return bwd_frag_offset(B, S, H) + (size_t)B * H * dsa::dsf_tile_base((S + 31) / 32) * 4096;
+  return 2 * (size_t)B * H * S * sizeof(float);
 }
 
 const char* dsa_status_string(dsa_status s) {
@@ -207,46 +213,50 @@ static dsa_status check_bwd_common(const void* q, const void* k, const void* v, 
   return DSA_OK;
 }
 
-dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
-                                  const void* dout, const float* lse, const void* mask, int B, int S,
-                                  int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype,
-                                  void* dq, void* workspace, size_t workspace_bytes, void* stream) {
+dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dout, const float* lse, const void* mask, int B, int S,
+                                    int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype, void* dk,
+                                    void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
                                   workspace, workspace_bytes);
   if (s != DSA_OK) return s;
   REQ_PTR(o);
-  REQ_PTR(dq);
-  hipStream_t st = (hipStream_t)stream;
-  void* m = const_cast<void*>(mask);
-  float* D = (float*)workspace;
-  if (attn_mfma(Dqk, Dv, dtype))
-    return hip_status(dsa::launch_attn_bwd_dq_mfma(q, k, v, o, dout, lse, D, bits_of(m), cls_of(m, B, S),
-                                                   B, S, H, softmax_scale, dq, st),
-                      "dsa_sparse_attn_bwd_dq");
-  return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, o, dout, lse, D, bits_of(m), B, S, H, Dqk, Dv,
-                                                  softmax_scale, dtype == DSA_BF16, dq, st),
-                    "dsa_sparse_attn_bwd_dq");
-}
-
-dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                                    const float* lse, const void* mask, int B, int S, int H, int Dqk,
-                                    int Dv, float softmax_scale, dsa_dtype dtype, void* dk, void* dv,
-                                    const void* workspace, size_t workspace_bytes, void* stream) {
-  dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
-                                  workspace, workspace_bytes);
-  if (s != DSA_OK) return s;
   REQ_PTR(dk);
   REQ_PTR(dv);
   hipStream_t st = (hipStream_t)stream;
   void* m = const_cast<void*>(mask);
-  const float* D = (const float*)workspace;
+  float* ws = (float*)workspace;
+  s = hip_status(dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, dtype == DSA_BF16, ws, st),
+                 "dsa_sparse_attn_bwd_dkdv");
+  if (s != DSA_OK) return s;
   if (attn_mfma(Dqk, Dv, dtype))
-    return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, lse, D, bits_of(m), cls_of(m, B, S),
-                                                     B, S, H, softmax_scale, dk, dv, st),
+    return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
+                                                     softmax_scale, dk, dv,
+                                                     (char*)workspace + bwd_frag_offset(B, S, H), st),
                       "dsa_sparse_attn_bwd_dkdv");
-  return hip_status(dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, D, bits_of(m), B, S, H, Dqk, Dv,
+  return hip_status(dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, H, Dqk, Dv,
                                                     softmax_scale, dtype == DSA_BF16, dk, dv, st),
                     "dsa_sparse_attn_bwd_dkdv");
+}
+
+dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const void* mask, int B, int S, int H, int Dqk,
+                                  int Dv, float softmax_scale, dsa_dtype dtype, void* dq,
+                                  const void* workspace, size_t workspace_bytes, void* stream) {
+  dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
+                                  workspace, workspace_bytes);
+  if (s != DSA_OK) return s;
+  REQ_PTR(dq);
+  hipStream_t st = (hipStream_t)stream;
+  void* m = const_cast<void*>(mask);
+  const float* ws = (const float*)workspace;
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_bwd_dq_mfma(k, (const char*)workspace + bwd_frag_offset(B, S, H),
+                                                   cls_of(m, B, S), B, S, H, softmax_scale, dq, st),
+                      "dsa_sparse_attn_bwd_dq");
+  return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, H, Dqk, Dv,
+                                                  softmax_scale, dtype == DSA_BF16, dq, st),
+                    "dsa_sparse_attn_bwd_dq");
 }
 
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -261,11 +271,11 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
   REQ_PTR(dq);
   REQ_PTR(dk);
   REQ_PTR(dv);
-  s = dsa_sparse_attn_bwd_dq(q, k, v, o, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dq,
-                             workspace, workspace_bytes, stream);
+  s = dsa_sparse_attn_bwd_dkdv(q, k, v, o, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dk,
+                               dv, workspace, workspace_bytes, stream);
   if (s != DSA_OK) return s;
-  return dsa_sparse_attn_bwd_dkdv(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dk,
-                                  dv, workspace, workspace_bytes, stream);
+  return dsa_sparse_attn_bwd_dq(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dq,
+                                workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

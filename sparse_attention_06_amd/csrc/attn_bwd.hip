@@ -73,6 +73,7 @@ constexpr int OBLK = bwd::QC * OSL / 64;                       // ... per dO chu
 // the two mask-word tiles
 constexpr int K_LD = QBLK + OBLK, K_W = K_LD + 1, NCOPY = K_W + 2;  // 27
 constexpr int NSLOT = (NCOPY + 3) / 4;                              // per B wave, at most (7)
+constexpr int TP = 40;  // pitch (elements) of the dS tile: 80-byte rows spread 16 rows over all 64 banks
 static_assert(bwd::QC * QSL % 64 == 0 && bwd::QC * OSL % 64 == 0, "chunks must be whole 1 KB blocks");
 static_assert(NCOPY % 4 == 3, "B waves 0-2 issue NSLOT copies per chunk, wave 3 one fewer");
 static_assert(bwd::QC == 32, "one copy instruction moves a chunk's LSE and D, one a mask tile");
@@ -82,15 +83,17 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws, const uint64_t* __restrict__ bits,
     const uint8_t* __restrict__ cls, int B, int S, int H, float scale, float scale_log2,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv) {
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, u32x4* __restrict__ dsf) {
   using namespace bwd;
   using dkv::NW;
   using dkv::NB;
   __shared__ __attribute__((aligned(1024))) unsigned char smQ[NB][dkv::QBLK * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char smO[NB][dkv::OBLK * 1024];
-  // P and dS of each A wave, B-operand layout: [buf][wave][p2][lane]
+  // P of each A wave, B-operand layout: [buf][wave][p2][lane]
   __shared__ __attribute__((aligned(16))) u32x4 smP[2][4][2][64];
-  __shared__ __attribute__((aligned(16))) u32x4 smS[2][4][2][64];
+  // dS of each A wave as a row-major [32 keys][32 queries] tile (pitch
+  // dkv::TP): B reads its rows for dK, A reads it transposed for dQ
+  __shared__ __attribute__((aligned(16))) uint16_t smT[2][4][32 * dkv::TP];
   // per chunk: LSE in base-2 units of its 32 queries, then D
   __shared__ __attribute__((aligned(16))) float smLD[NB][2 * QC];
   // per chunk: 32-bit halves of the mask words of the workgroup's two key
@@ -287,7 +290,6 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         // 4-aligned runs): base-2 LSE, D and this pair's 32-bit half of each
         // mask word. FULL tiles have every in-range bit set.
         const uint32_t* wrow = smW[bi][wsel][hsel];
-        (void)qc;
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
           float Lr[8], Dr[8];
@@ -317,8 +319,13 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
             ds[c8] = pr * (dpacc[r] - Dr[c8]);
           }
           smP[it & 1][kw][p2][lane] = pack8(p);
-          smS[it & 1][kw][p2][lane] = pack8(ds);
+          // this lane's key row, queries 16*p2 + 4*half + 0..3 and 16*p2 + 8 + 4*half + 0..3
+          const u32x4 dsp = pack8(ds);
+          uint16_t* trow = smT[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
+          *(u32x2*)trow = u32x2{dsp[0], dsp[1]};
+          *(u32x2*)(trow + 8) = u32x2{dsp[2], dsp[3]};
         }
+        (void)qc;
       }
       e0 = e1;
       e1 = e2;
@@ -355,6 +362,24 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
       return u32x4{ux[0], ux[1], uy[0], uy[1]};
     };
+    // dS^T fragments of the chunk B last updated, for the dQ kernel: lane
+    // (half, col) holds query col and keys 16*p2 + 4*half + {0..3, 8..11} of
+    // this pair, the order in which the dQ kernel reads the matching K^T rows.
+    // They are stored right after the next barrier, before that iteration's
+    // copies, so the counted wait for a chunk's copies stays exact: copies
+    // complete in order, so while one of them is in flight, all copies issued
+    // after it are too.
+    u32x4 fhold[2];
+    int qhold = -1;
+    auto store_frags = [&]() {
+      if (qhold >= 0) {
+        u32x4* fr = dsf + (((size_t)bh * dsf_tile_base(nchunks) + dsf_tile_base(qhold) + kt_lo + (kw >> 1)) * 4 +
+                           2 * (kw & 1)) * 64 + lane;
+        fr[0] = fhold[0];
+        fr[64] = fhold[1];
+        qhold = -1;
+      }
+    };
     // dV^T[e, s] += dO^T[e, q] P[q, s] and dK^T[d, s] += Q^T[d, q] dS[q, s] for
     // the chunk of iteration `it`; the query order inside each 16-query step
     // matches the A wave's accumulator rows
@@ -364,7 +389,9 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
         const u32x4 pb = smP[it & 1][kw][p2][lane];
-        const u32x4 db = smS[it & 1][kw][p2][lane];
+        const uint16_t* trow = smT[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
+        const u32x2 d0 = *(const u32x2*)trow, d1 = *(const u32x2*)(trow + 8);
+        const u32x4 db = u32x4{d0[0], d0[1], d1[0], d1[1]};
 #pragma unroll
         for (int eb = 0; eb < DV / 32; ++eb)
           dvacc[eb] = mfma32(tr(sO + 64 * eb, ot[p2][0], ot[p2][1]), pb, dvacc[eb]);
@@ -372,21 +399,35 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         for (int d2 = 0; d2 < DQK / 32; ++d2)
           dkacc[d2] = mfma32(tr(sQ + 64 * d2, qt[p2][0], qt[p2][1]), db, dkacc[d2]);
       }
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2)
+        fhold[p2] = lds_tr_frag(smT[it & 1][kw], dkv::TP, 16 * p2 + 4 * half, 16 * p2 + 4 * half + 8, 0);
     };
     bool prev = false;
+    int qprev = 0;
     int it = 0;
     for (; e0 >= 0; ++it) {
       publish_b(it);
+      store_frags();
       if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
       const int e3 = entry(it + 3);
-      if (prev) update(it - 1);  // the chunk A finished before this barrier
+      if (prev) {  // the chunk A finished before this barrier
+        update(it - 1);
+        qhold = qprev;
+      }
       prev = active(e0);
+      qprev = e0 & 0x3FFF;
       e0 = e1;
       e1 = e2;
       e2 = e3;
     }
     lds_barrier();  // A's P and dS of the last chunk are visible
-    if (prev) update(it - 1);
+    store_frags();
+    if (prev) {
+      update(it - 1);
+      qhold = qprev;
+      store_frags();
+    }
     if (kvalid) {
       uint16_t* dkrow = dk + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK;
 #pragma unroll
@@ -411,86 +452,58 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ, query-major; also computes D. Workgroup = (b, h, 256 queries) with 8
-// waves (two per SIMD) of 32 queries. Walks the non-empty 64-key tiles up to
-// the diagonal; K and V tiles are double buffered in natural layout and filled
-// by direct global->LDS copies. Each tile is processed as two 32-key halves to
-// bound the live accumulators.
+// dQ, query-major, from the dS^T fragments the key-major kernel stored:
+// dQ^T[d, q] = scale * sum_s K^T[d, s] dS^T[s, q]. Workgroup = (b, h, 256
+// queries), 8 waves (two per SIMD) of one 32-query chunk each. It walks the
+// non-empty 64-key tiles up to the diagonal. K tiles are double buffered in
+// natural layout and read transposed; each wave's 4 KB of fragments per tile
+// go to a private three-slot LDS ring, two tiles ahead (they stream from
+// HBM). Every copy is a direct global->LDS copy issued through the untracked
+// asm path, and each wave issues exactly four fragment copies per tile
+// (harmless ones where it has nothing to take), so one counted wait covers
+// both. A wave takes a tile only where the key-major kernel wrote it: its own
+// 128-query tile is non-empty there, and only the 32-key halves that start at
+// or before its last query (causal).
 // ---------------------------------------------------------------------------
 namespace dqk {
 constexpr int NW = 8, QW = 32 * NW;
-constexpr int KSL = bwd::DQK / 8 + 1, VSL = bwd::DV / 8 + 1;  // 16-byte slots per padded row
-constexpr int KBLK = bwd::TK * KSL / 64, VBLK = bwd::TK * VSL / 64;
-constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;
-static_assert(KSL * 8 == bwd::QP && VSL * 8 == bwd::OP, "pitches");
+constexpr int KSL = bwd::DQK / 8 + 1;  // 16-byte slots per padded K row
+constexpr int KBLK = bwd::TK * KSL / 64;
+constexpr int KI = (KBLK + NW - 1) / NW;
+constexpr int NF = 3;  // fragment ring slots
+static_assert(KSL * 8 == bwd::QP, "pitch");
 }  // namespace dqk
 
 __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
-    float* __restrict__ D, const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B,
-    int S, int H, float scale, float scale_log2, uint16_t* __restrict__ dq) {
+    const uint16_t* __restrict__ k, const u32x4* __restrict__ dsf, const uint8_t* __restrict__ cls, int B,
+    int S, int H, float scale, uint16_t* __restrict__ dq) {
   using namespace bwd;
   using dqk::NW;
   using dqk::QW;
   __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * QP];
-  __shared__ __attribute__((aligned(1024))) uint16_t smV[2][TK * OP];
+  __shared__ __attribute__((aligned(1024))) u32x4 smF[dqk::NF][NW][4][64];
   __shared__ uint8_t scls[2][kMaxTiles];  // tile classes of the workgroup's two 128-query tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
   const int half = lane >> 5, col = lane & 31;
-  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
   const int NQW = (S + QW - 1) / QW;
-  // the query blocks of a (b, h) on one XCD (they share K/V), costliest first
+  const int nchunks = (S + QC - 1) / QC;
+  // the query blocks of a (b, h) on one XCD (they share K), costliest first
   int bh, qw;
   grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
   const int b = bh / H, h = bh % H;
-  const int tq = qw * QW + wid * 32 + col;
-  const bool qvalid = tq < S;
-  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
+  const int qc = qw * NW + wid;  // this wave's chunk
+  const bool wvalid = qc < nchunks;
+  const int tq = qc * QC + col;
+  const int qt_w = min(NQ - 1, qc * QC / 128);
   const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
-  const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
-  const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
-  const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
-
-  u32x4 qf[DQK / 16], of[DV / 16];
-#pragma unroll
-  for (int ks = 0; ks < DQK / 16; ++ks) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (qvalid) z = *(const u32x4*)(q + ((size_t)b * S + tq) * rs_qk + (size_t)h * DQK + ks * 16 + 8 * half);
-    qf[ks] = z;
-  }
-#pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    if (qvalid) z = *(const u32x4*)(dout + ((size_t)b * S + tq) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
-    of[ks] = z;
-  }
-  const float Lq = qvalid ? lse[((size_t)b * H + h) * S + tq] * 1.4426950408889634f : INFINITY;
-  // D(t) = dO(t) . O(t): this lane holds half of dO(t) as MFMA fragments; the
-  // matching half of O(t) is read here and the halves are summed across lanes
-  float Dq = 0.f;
-  if (qvalid) {
-    const uint16_t* orow = o + ((size_t)b * S + tq) * rs_v + (size_t)h * DV;
-#pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks) {
-      const u32x4 ov = *(const u32x4*)(orow + ks * 16 + 8 * half);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t wo = ov[e >> 1], wd = of[ks][e >> 1];
-        const uint16_t xo = (e & 1) ? (uint16_t)(wo >> 16) : (uint16_t)(wo & 0xffffu);
-        const uint16_t xd = (e & 1) ? (uint16_t)(wd >> 16) : (uint16_t)(wd & 0xffffu);
-        Dq = fmaf(bf2f(xo), bf2f(xd), Dq);
-      }
-    }
-  }
-  Dq += __shfl_xor(Dq, 32);
-  // the workspace holds D, then the log-sum-exp in base-2 units, for the key-major kernel
-  if (qvalid && half == 0) {
-    D[((size_t)b * H + h) * S + tq] = Dq;
-    D[(size_t)B * H * S + ((size_t)b * H + h) * S + tq] = Lq;
-  }
+  const size_t rs_qk = (size_t)H * DQK;
+  const uint16_t* kbase = uniform_ptr(k + (size_t)b * S * rs_qk + (size_t)h * DQK);
+  // this (b, h)'s fragment tiles, and this chunk's: key tile kt at + 256 * kt (u32x4 units)
+  const u32x4* fbh = uniform_ptr(dsf + (size_t)bh * dsf_tile_base(nchunks) * 256);
+  const u32x4* fch = uniform_ptr(fbh + dsf_tile_base(wvalid ? qc : 0) * 256);
 
   f32x16 dqacc[DQK / 32];
 #pragma unroll
@@ -504,95 +517,86 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   const uint8_t* cls0 = scls[0];
   const uint8_t* cls1 = scls[1];
   const uint8_t* clsw = scls[qt_w - qt0];
-  const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
   auto next_tile = [&](int kt) {
     int n = kt + 1;
     while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
     return n;
   };
-  auto issue = [&](int kt, int buf) {
+  // this wave's 1 KB blocks of a K tile: byte offsets within the tile's rows
+  uint32_t koff[dqk::KI];
+  int krow[dqk::KI];
 #pragma unroll
-    for (int i = 0; i < dqk::KI; ++i) {
-      const int j = wid + i * NW;
-      if (j < dqk::KBLK) {
-        const int slot = j * 64 + lane, row = slot / dqk::KSL, c = min(slot % dqk::KSL, dqk::KSL - 2);
-        const int s = min(kt * TK + row, S - 1);
-        g2lds16(kbase + (size_t)s * rs_qk + c * 8, (char*)smK[buf] + j * 1024);
-      }
-    }
+  for (int i = 0; i < dqk::KI; ++i) {
+    const int slot = (wid + i * NW) * 64 + lane;
+    krow[i] = slot / dqk::KSL;
+    koff[i] = (uint32_t)((krow[i] * rs_qk + min(slot % dqk::KSL, dqk::KSL - 2) * 8) * 2);
+  }
+  auto issue_k = [&](int kt, int buf) {
+    const uint16_t* tb = kbase + (size_t)kt * TK * rs_qk;
+    const int lim = S - 1 - kt * TK;  // last in-range row of the tile
 #pragma unroll
-    for (int i = 0; i < dqk::VI; ++i) {
-      const int j = wid + i * NW;
-      if (j < dqk::VBLK) {
-        const int slot = j * 64 + lane, row = slot / dqk::VSL, c = min(slot % dqk::VSL, dqk::VSL - 2);
-        const int s = min(kt * TK + row, S - 1);
-        g2lds16(vbase + (size_t)s * rs_v + c * 8, (char*)smV[buf] + j * 1024);
+    for (int i = 0; i < dqk::KI; ++i)
+      if (wid + i * NW < dqk::KBLK) {
+        const int dr = krow[i] - min(krow[i], lim);  // rows past S copy row S-1
+        g2lds16_async_off(tb, koff[i] - (uint32_t)(dr * rs_qk * 2), (char*)smK[buf] + (wid + i * NW) * 1024);
       }
+  };
+  // 32-key halves of tile kt this wave takes: 0, 1 or 2 (causal at 32 keys)
+  auto halves = [&](int kt) -> int {
+    if (kt > kt_last || !wvalid || clsw[kt] == 0) return 0;
+    return max(0, min(2, qc - 2 * kt + 1));
+  };
+  // the four fragment blocks of tile kt into ring slot f; k steps the wave
+  // does not take copy this (b, h)'s first block instead
+  auto issue_f = [&](int kt, int nh, int f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4* src = (j < 2 * nh) ? fch + 256 * kt + 64 * j : fbh;
+      g2lds16_async_off(src, (uint32_t)lane * 16u, &smF[f][wid][j][0]);
     }
   };
 
-  // this lane's selection word of tile kt (FULL: all ones; EMPTY: none)
-  auto word = [&](int kt) -> uint64_t {
-    const int c = clsw[kt];
-    if (!qvalid || c == 0) return 0ull;
-    return c == 2 ? ~0ull : bits_q[kt];
-  };
   __syncthreads();  // class rows staged
   int kt = next_tile(-1);
-  if (kt <= kt_last) issue(kt, 0);
-  uint64_t mw = kt <= kt_last ? word(kt) : 0ull;
-  int buf = 0;
+  int kn = next_tile(kt);
+  int nh = halves(kt), nh1 = halves(kn);
+  if (kt <= kt_last) issue_k(kt, 0);
+  issue_f(kt, nh, 0);
+  issue_f(kn, nh1, 1);
+  int buf = 0, fs = 0;
   while (kt <= kt_last) {
-    const int c = clsw[kt];
-    const int kn = next_tile(kt);
-    wait_vmem();
-    __syncthreads();  // tile kt visible in `buf`; every wave is done with the other buffer
-    // the next selection word is loaded before the tile copies are issued, so
-    // that waiting for it does not wait for them
-    const uint64_t mw_n = kn <= kt_last ? word(kn) : 0ull;
-    if (kn <= kt_last) issue(kn, buf ^ 1);
-
-    if (c != 0 && __ballot(mw != 0ull)) {
-      const uint16_t* sK = smK[buf];
-      const uint16_t* sV = smV[buf];
-      // this lane's keys are kb*32 + 8i + 4*half + r: pre-shift the word by 4*half
-      const uint64_t mwh = mw >> (4 * half);
+    const int kn2 = next_tile(kn);
+    const int nh2 = halves(kn2);
+    wait_vmem_n<4>();  // K tile kt and its fragments are in; tile kn's fragments may still fly
+    __syncthreads();   // tile kt visible in `buf`; every wave is done with the other buffer
+    if (kn <= kt_last) issue_k(kn, buf ^ 1);
+    issue_f(kn2, nh2, fs == 0 ? 2 : fs - 1);
+    const uint16_t* sK = smK[buf];
+    // dQ^T[d, q] += K^T[d, s] dS^T[s, q]; the fragment of k step (kb, p2)
+    // holds keys kb*32 + 16*p2 + 4*half + {0..3, 8..11}
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t w = (uint32_t)(mwh >> (32 * kb));
-        f32x16 sacc, dpacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
-#pragma unroll
-        for (int ks = 0; ks < DQK / 16; ++ks)
-          sacc = mfma32(*(const u32x4*)(sK + (kb * 32 + col) * QP + ks * 16 + 8 * half), qf[ks], sacc);
-#pragma unroll
-        for (int ks = 0; ks < DV / 16; ++ks)
-          dpacc = mfma32(*(const u32x4*)(sV + (kb * 32 + col) * OP + ks * 16 + 8 * half), of[ks], dpacc);
-        // dQ^T[d, q] += K^T[d, s] dS^T[s, q], keys permuted inside each 16-key step
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb < nh) {
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
-          float dsv[8];
-#pragma unroll
-          for (int c8 = 0; c8 < 8; ++c8) {
-            const int r = 8 * p2 + c8;
-            const bool keep = (w >> (8 * (r >> 2) + (r & 3))) & 1u;
-            const float pr = keep ? fast_exp2(fmaf(sacc[r], scale_log2, -Lq)) : 0.f;
-            dsv[c8] = pr * (dpacc[r] - Dq);
-          }
-          const u32x4 db = pack8(dsv);
           const int r0 = kb * 32 + 16 * p2 + 4 * half;
+          const u32x4 db = smF[fs][wid][2 * kb + p2][lane];
+          u32x4 ka[DQK / 32];
 #pragma unroll
-          for (int i = 0; i < DQK / 32; ++i)
-            dqacc[i] = mfma32(lds_tr_frag(sK, QP, r0, r0 + 8, i * 32), db, dqacc[i]);
+          for (int i = 0; i < DQK / 32; ++i) ka[i] = lds_tr_frag(sK, QP, r0, r0 + 8, i * 32);
+#pragma unroll
+          for (int i = 0; i < DQK / 32; ++i) dqacc[i] = mfma32(ka[i], db, dqacc[i]);
         }
       }
-    }
-    mw = mw_n;
+    nh = nh1;
+    nh1 = nh2;
     buf ^= 1;
+    fs = fs == 2 ? 0 : fs + 1;
     kt = kn;
+    kn = kn2;
   }
-  if (qvalid) {
+  wait_vmem();  // no copy outlives the workgroup
+  if (wvalid && tq < S) {
     uint16_t* dqrow = dq + ((size_t)b * S + tq) * rs_qk + (size_t)h * DQK;
 #pragma unroll
     for (int i = 0; i < DQK / 32; ++i)
@@ -605,26 +609,21 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   }
 }
 
-hipError_t launch_attn_bwd_dq_mfma(const void* q, const void* k, const void* v, const void* o,
-                                   const void* dout, const float* lse, float* D, const uint64_t* bits,
-                                   const uint8_t* cls, int B, int S, int H, float scale, void* dq,
-                                   hipStream_t st) {
+hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int H,
+                                   float scale, void* dq, hipStream_t st) {
   const size_t nq = (size_t)((S + dqk::QW - 1) / dqk::QW) * B * H;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(dqk::NW * 64), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse,
-                     D, bits, cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dq);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(dqk::NW * 64), 0, st, (const uint16_t*)k,
+                     (const u32x4*)dsf, cls, B, S, H, scale, (uint16_t*)dq);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout,
-                                     const float* lse, const float* D, const uint64_t* bits,
-                                     const uint8_t* cls, int B, int S, int H, float scale, void* dk,
-                                     void* dv, hipStream_t st) {
-  (void)lse;  // the dQ kernel left lse * log2(e) in the workspace after D
+                                     const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
+                                     int H, float scale, void* dk, void* dv, void* dsf, hipStream_t st) {
   const size_t nkv = (size_t)((S + 127) / 128) * B * H;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, D, bits, cls, B, S, H,
-                     scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv);
+                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits, cls, B, S, H,
+                     scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv, (u32x4*)dsf);
   return hipGetLastError();
 }
 

@@ -3,12 +3,65 @@
 //
 // Source: "Support Ring Attention with DeepSeek DSA Sparse Indexer", Backward
 // Flow (dQ = dP K, dK = dP^T Q, dV = P^T dO on the kept entries; dK/dV
-// key-major). D(t) = dO(t) . O(t) is computed by the query-major kernel, which
-// runs first and stores it for the key-major one.
+// key-major). D(t) = dO(t) . O(t) and the base-2 log-sum-exp are computed
+// first, by attn_bwd_prep_kernel, into the backward workspace.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dsa {
+
+// ---------------------------------------------------------------------------
+// Backward prologue: D(b,h,t) = sum_e dO(b,t,h,e) O(b,t,h,e) and
+// lse(b,h,t) * log2(e), as two float32 [B,H,S] arrays at the workspace start.
+// 16 lanes per (b, t, h) row, 8 elements per lane per pass.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                            const float* __restrict__ lse, int B, int S, int H,
+                                                            int Dv, float* __restrict__ ws) {
+  const int sub = threadIdx.x & 15;
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b, t, h) flattened
+  const bool valid = row < (size_t)B * S * H;
+  float acc = 0.f;
+  if (valid) {
+    const T* orow = o + row * Dv;
+    const T* drow = dout + row * Dv;
+    for (int e0 = sub * 8; e0 < Dv; e0 += 128) {
+      if (sizeof(T) == 2 && e0 + 8 <= Dv && (Dv & 7) == 0) {
+        const u32x4 a = *(const u32x4*)(orow + e0), g = *(const u32x4*)(drow + e0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = fmaf(__uint_as_float(a[j] << 16), __uint_as_float(g[j] << 16), acc);
+          acc = fmaf(__uint_as_float(a[j] & 0xffff0000u), __uint_as_float(g[j] & 0xffff0000u), acc);
+        }
+      } else {
+        for (int e = e0; e < min(Dv, e0 + 8); ++e) acc = fmaf(Elem<T>::load(orow + e), Elem<T>::load(drow + e), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m, 16);
+  if (valid && sub == 0) {
+    const int h = (int)(row % H);
+    const int t = (int)((row / H) % S);
+    const int b = (int)(row / ((size_t)H * S));
+    const size_t i = ((size_t)b * H + h) * S + t;
+    ws[i] = acc;
+    ws[(size_t)B * H * S + i] = lse[i] * 1.4426950408889634f;
+  }
+}
+
+hipError_t launch_attn_bwd_prep(const void* o, const void* dout, const float* lse, int B, int S, int H, int Dv,
+                                bool bf16, float* ws, hipStream_t st) {
+  const size_t nblk = ((size_t)B * S * H + 15) / 16;
+  if (bf16)
+    hipLaunchKernelGGL(attn_bwd_prep_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st, (const uint16_t*)o,
+                       (const uint16_t*)dout, lse, B, S, H, Dv, ws);
+  else
+    hipLaunchKernelGGL(attn_bwd_prep_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st, (const float*)o,
+                       (const float*)dout, lse, B, S, H, Dv, ws);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Plain kernels (any dims <= 256, fp32 or bf16).
@@ -18,8 +71,8 @@ namespace dsa {
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ o,
-    const T* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ D,
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ D,
     const uint64_t* __restrict__ bits, int B, int S, int H, int Dqk, int Dv, float scale,
     T* __restrict__ dq) {
   __shared__ float qs[4][256], os[4][256], dss[4][64];
@@ -34,13 +87,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
   for (int d = lane; d < Dv; d += 64) os[wid][d] = Elem<T>::load(dout + row * Dv + d);
   __builtin_amdgcn_wave_barrier();
   const float L = lse[((size_t)b * H + h) * S + t];
-  float Dt = 0.f;
-  for (int e = lane; e < Dv; e += 64) Dt = fmaf(Elem<T>::load(o + row * Dv + e), os[wid][e], Dt);
-  Dt = wave_sumf(Dt);
-  if (lane == 0) {
-    D[((size_t)b * H + h) * S + t] = Dt;
-    D[(size_t)B * H * S + ((size_t)b * H + h) * S + t] = L * 1.4426950408889634f;
-  }
+  const float Dt = D[((size_t)b * H + h) * S + t];
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const uint64_t* brow = bits + ((size_t)b * S + t) * W;
   for (int w = 0; w <= t / 64; ++w) {
@@ -130,18 +177,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_plain_kernel(
   }
 }
 
-hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v, const void* o,
-                                    const void* dout, const float* lse, float* D, const uint64_t* bits,
+hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,
+                                    const void* dout, const float* lse, const float* D, const uint64_t* bits,
                                     int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
                                     void* dq, hipStream_t st) {
   const size_t nblk = ((size_t)B * S * H + 3) / 4;
   if (bf16)
     hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                        (const uint16_t*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale, (uint16_t*)dq);
   else
     hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
-                       (const float*)q, (const float*)k, (const float*)v, (const float*)o,
+                       (const float*)q, (const float*)k, (const float*)v,
                        (const float*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale, (float*)dq);
   return hipGetLastError();
 }

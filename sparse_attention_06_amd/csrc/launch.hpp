@@ -39,24 +39,35 @@ hipError_t launch_attn_fwd_plain(const void* q, const void* k, const void* v, co
                                  int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
                                  void* o, float* lse, hipStream_t st);
 
-// backward, query-major: writes D = rowsum(dout * o) [B,H,S] and dq
-hipError_t launch_attn_bwd_dq_mfma(const void* q, const void* k, const void* v, const void* o,
-                                   const void* dout, const float* lse, float* D, const uint64_t* bits,
-                                   const uint8_t* cls, int B, int S, int H, float scale, void* dq,
-                                   hipStream_t st);
-hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v, const void* o,
-                                    const void* dout, const float* lse, float* D, const uint64_t* bits,
-                                    int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
-                                    void* dq, hipStream_t st);
-// backward, key-major: reads D, writes dk and dv
+// backward prologue: D = rowsum(dout * o) and lse * log2(e), two float32
+// [B,H,S] arrays at the start of the workspace
+hipError_t launch_attn_bwd_prep(const void* o, const void* dout, const float* lse, int B, int S, int H, int Dv,
+                                bool bf16, float* ws, hipStream_t st);
+// backward, key-major: reads D and the base-2 LSE from ws, writes dk and dv
+// and the dS^T fragments (dsf) for the dQ kernel
 hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout,
-                                     const float* lse, const float* D, const uint64_t* bits,
-                                     const uint8_t* cls, int B, int S, int H, float scale, void* dk,
-                                     void* dv, hipStream_t st);
+                                     const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
+                                     int H, float scale, void* dk, void* dv, void* dsf, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* v, const void* dout,
                                       const float* lse, const float* D, const uint64_t* bits, int B,
                                       int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dk,
                                       void* dv, hipStream_t st);
+// backward, query-major: dq from the dS^T fragments of the key-major kernel
+hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int H,
+                                   float scale, void* dq, hipStream_t st);
+hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,
+                                    const void* dout, const float* lse, const float* D, const uint64_t* bits,
+                                    int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
+                                    void* dq, hipStream_t st);
+
+// dS^T fragments that the key-major backward kernel leaves for the dQ kernel:
+// per (b, h), 32-query chunk qc holds key tiles 0 .. qc/2 (the causal ones),
+// each as four 1 KB MFMA B-operand blocks (one per 16-key step). This is the
+// first tile of chunk qc; dsf_tile_base(number of chunks) is the count per (b, h).
+__host__ __device__ inline size_t dsf_tile_base(int qc) {
+  const size_t m = (size_t)(qc >> 1);
+  return (qc & 1) ? (m + 1) * (m + 1) : m * (m + 1);
+}
 
 // layout helpers shared by the host side
 inline int mask_words(int S) { return (S + 63) / 64; }

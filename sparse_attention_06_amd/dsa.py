@@ -50,10 +50,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
         L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                           vp, vp, vp, vp, sz, vp]
-        L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                             i32, vp, vp, sz, vp]
-        L.dsa_sparse_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
-                                               vp, vp, vp, sz, vp]
+        L.dsa_sparse_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                               i32, vp, vp, vp, sz, vp]
+        L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                             vp, vp, sz, vp]
         for f in ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
                   "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv"):
             getattr(L, f).restype = ctypes.c_int
@@ -157,21 +157,24 @@ def dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, d
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def dsa_sparse_attn_bwd_dq(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, workspace,
-                           stream=None) -> None:
-    B, S, H, Dqk = q.shape
-    Dv = v.shape[-1]
-    _check("dsa_sparse_attn_bwd_dq", lib().dsa_sparse_attn_bwd_dq(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
-        float(softmax_scale), _dt(q), _ptr(dq), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
-
-
-def dsa_sparse_attn_bwd_dkdv(q, k, v, dout, lse, mask, softmax_scale: float, dk, dv, workspace,
+def dsa_sparse_attn_bwd_dkdv(q, k, v, o, dout, lse, mask, softmax_scale: float, dk, dv, workspace,
                              stream=None) -> None:
+    """Key-major half: D and base-2 LSE into the workspace, then dk, dv (and,
+    on the MFMA path, the dS tiles for dsa_sparse_attn_bwd_dq)."""
     B, S, H, Dqk = q.shape
     Dv = v.shape[-1]
     _check("dsa_sparse_attn_bwd_dkdv", lib().dsa_sparse_attn_bwd_dkdv(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
         float(softmax_scale), _dt(q), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dsa_sparse_attn_bwd_dq(q, k, v, dout, lse, mask, softmax_scale: float, dq, workspace,
+                           stream=None) -> None:
+    """Query-major half; runs after dsa_sparse_attn_bwd_dkdv on the same workspace."""
+    B, S, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    _check("dsa_sparse_attn_bwd_dq", lib().dsa_sparse_attn_bwd_dq(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
+        float(softmax_scale), _dt(q), _ptr(dq), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))

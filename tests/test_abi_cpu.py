@@ -38,7 +38,12 @@ def test_sizes_and_strings():
     W = (S + 63) // 64
     assert dsa.dsa_mask_bytes(B, S) == B * S * W * 8 + B * ((S + 127) // 128) * ((S + 63) // 64)
     assert dsa.dsa_mask_bytes(0, 5) == 0
-    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 192, 128) == 2 * (2 * 3 * 100 * 4)  # D and base-2 LSE
+    # D and base-2 LSE; for the MFMA dims also the dS tiles, from a 256-byte
+    # boundary: each 32-query chunk c of a (b, h) holds key tiles 0..c//2, 4 KB each
+    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 64, 64) == 2 * (2 * 3 * 100 * 4)
+    tiles = sum(c // 2 + 1 for c in range((100 + 31) // 32))
+    off = -(-(2 * 2 * 3 * 100 * 4) // 256) * 256
+    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 192, 128) == off + 2 * 3 * tiles * 4096
     assert L.dsa_status_string(0) == b"DSA_OK"
     assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
     assert L.dsa_version() >= 100
