@@ -72,12 +72,16 @@ def work(cfg, seg_np):
         "bwd_dq": selected * cfg.H * 2 * cfg.Dqk,
         "bwd_dkdv": selected * cfg.H * 2 * (cfg.Dqk + 2 * cfg.Dv),
         "topk_bytes": topk_bytes,
+        # backward prologue: O and dO rows read, D and base-2 LSE written
+        "bwd_prep_bytes": cfg.B * cfg.S * cfg.H * (2 * cfg.Dv * (2 if cfg.dtype == "bf16" else 4) + 8),
     }
 
 
 KERNEL_SRC = {"index_scores": "indexer.hip", "topk": "topk.hip", "attn_fwd": "attn_fwd.hip",
+              "attn_bwd_prep": "attn_bwd_plain.hip",
               "attn_bwd_dq": "attn_bwd.hip", "attn_bwd_dkdv": "attn_bwd.hip"}
 KERNEL_SYM = {"index_scores": "index_scores_mfma_kernel", "topk": "topk_reg_kernel", "attn_fwd": "attn_fwd_mfma_kernel",
+              "attn_bwd_prep": "attn_bwd_prep_kernel",
               "attn_bwd_dq": "attn_bwd_dq_kernel", "attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
 
@@ -227,7 +231,8 @@ def main():
     seg = x["seg"]
     stream = torch.cuda.current_stream()
 
-    calls = ["index_scores", "topk", "attn_fwd"] + (["attn_bwd_dkdv", "attn_bwd_dq"] if cfg.backward else [])
+    calls = ["index_scores", "topk", "attn_fwd"] + (["attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq"]
+                                                    if cfg.backward else [])
 
     def step(evs=None):
         def mark(i):
@@ -241,12 +246,14 @@ def main():
         dsa.dsa_sparse_attn_fwd(x["q"], x["k"], x["v"], path.mask, scale, path.o, path.lse)
         mark(3)
         if cfg.backward:
-            dsa.dsa_sparse_attn_bwd_dkdv(x["q"], x["k"], x["v"], path.o, x["dout"], path.lse, path.mask, scale,
-                                         path.dk, path.dv, path.ws)
+            dsa.dsa_sparse_attn_bwd_prep(path.o, x["dout"], path.lse, cfg.Dqk, path.ws)
             mark(4)
+            dsa.dsa_sparse_attn_bwd_dkdv(x["q"], x["k"], x["v"], x["dout"], path.lse, path.mask, scale,
+                                         path.dk, path.dv, path.ws)
+            mark(5)
             dsa.dsa_sparse_attn_bwd_dq(x["q"], x["k"], x["v"], x["dout"], path.lse, path.mask, scale,
                                        path.dq, path.ws)
-            mark(5)
+            mark(6)
 
     for i in range(args.warmup):
         step()
@@ -274,6 +281,7 @@ def main():
         "index_scores": ("mfma", wk["indexer"]),
         "topk": ("hbm", wk["topk_bytes"]),
         "attn_fwd": ("mfma", wk["fwd"]),
+        "attn_bwd_prep": ("hbm", wk["bwd_prep_bytes"]),
         "attn_bwd_dq": ("mfma", wk["bwd_dq"]),
         "attn_bwd_dkdv": ("mfma", wk["bwd_dkdv"]),
     }

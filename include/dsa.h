@@ -184,8 +184,8 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  *             next 256-byte boundary, the dS tiles that the key-major kernel
  *             hands to the dQ kernel: 2 bytes per causal (query, key) pair of
  *             every (b, h), rounded to 32 x 64 blocks (about B*H*S*S bytes).
- * Same as dsa_sparse_attn_bwd_dkdv followed by dsa_sparse_attn_bwd_dq on the
- * same stream. Deterministic: no atomics.
+ * Same as dsa_sparse_attn_bwd_prep, _dkdv and _dq in that order on the same
+ * stream. Deterministic: no atomics.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                                const void* dout, const float* lse, const void* mask,
@@ -193,14 +193,19 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
                                dsa_dtype dtype, void* dq, void* dk, void* dv,
                                void* workspace, size_t workspace_bytes, void* stream);
 
-/* The two halves of dsa_sparse_attn_bwd, for callers that schedule them
- * separately:
- *   _dkdv  key-major. Computes D and lse * log2(e) into the workspace, then
- *          dk and dv; on the MFMA path it also leaves dS there.
- *   _dq    query-major. Reads the workspace, so it must be ordered after
- *          _dkdv on the same workspace. Writes dq.
- * Arguments as in dsa_sparse_attn_bwd. */
-dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
+/* The three parts of dsa_sparse_attn_bwd, for callers that schedule them
+ * separately, in this order on one workspace:
+ *   _prep  D = rowsum(dout * o) and lse * log2(e) into the workspace
+ *          (Backward Flow's per-row term of dS = P (dP - D)).
+ *   _dkdv  key-major. Reads both; writes dk and dv, and on the MFMA path
+ *          also leaves dS in the workspace.
+ *   _dq    query-major. Reads the workspace; writes dq.
+ * Arguments as in dsa_sparse_attn_bwd; each returns DSA_ERR_WORKSPACE for a
+ * workspace below dsa_bwd_workspace_bytes(). */
+dsa_status dsa_sparse_attn_bwd_prep(const void* o, const void* dout, const float* lse,
+                                    int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v,
                                     const void* dout, const float* lse, const void* mask,
                                     int B, int S, int H, int Dqk, int Dv, float softmax_scale,
                                     dsa_dtype dtype, void* dk, void* dv, void* workspace,

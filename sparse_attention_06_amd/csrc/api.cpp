@@ -213,22 +213,34 @@ static dsa_status check_bwd_common(const void* q, const void* k, const void* v, 
   return DSA_OK;
 }
 
-dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o,
-                                    const void* dout, const float* lse, const void* mask, int B, int S,
-                                    int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype, void* dk,
-                                    void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+dsa_status dsa_sparse_attn_bwd_prep(const void* o, const void* dout, const float* lse, int B, int S, int H,
+                                    int Dqk, int Dv, dsa_dtype dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  REQ_PTR(o);
+  REQ_PTR(dout);
+  REQ_PTR(lse);
+  REQ_PTR(workspace);
+  dsa_status s = check_attn(B, S, H, Dqk, Dv, 1.f, dtype);
+  if (s != DSA_OK) return s;
+  const size_t need = dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv);
+  REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
+  return hip_status(dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, dtype == DSA_BF16, (float*)workspace,
+                                              (hipStream_t)stream),
+                    "dsa_sparse_attn_bwd_prep");
+}
+
+dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                                    const float* lse, const void* mask, int B, int S, int H, int Dqk,
+                                    int Dv, float softmax_scale, dsa_dtype dtype, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
   dsa_status s = check_bwd_common(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype,
                                   workspace, workspace_bytes);
   if (s != DSA_OK) return s;
-  REQ_PTR(o);
   REQ_PTR(dk);
   REQ_PTR(dv);
   hipStream_t st = (hipStream_t)stream;
   void* m = const_cast<void*>(mask);
-  float* ws = (float*)workspace;
-  s = hip_status(dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, dtype == DSA_BF16, ws, st),
-                 "dsa_sparse_attn_bwd_dkdv");
-  if (s != DSA_OK) return s;
+  const float* ws = (const float*)workspace;
   if (attn_mfma(Dqk, Dv, dtype))
     return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
                                                      softmax_scale, dk, dv,
@@ -271,8 +283,10 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
   REQ_PTR(dq);
   REQ_PTR(dk);
   REQ_PTR(dv);
-  s = dsa_sparse_attn_bwd_dkdv(q, k, v, o, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dk,
-                               dv, workspace, workspace_bytes, stream);
+  s = dsa_sparse_attn_bwd_prep(o, dout, lse, B, S, H, Dqk, Dv, dtype, workspace, workspace_bytes, stream);
+  if (s != DSA_OK) return s;
+  s = dsa_sparse_attn_bwd_dkdv(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dk, dv,
+                               workspace, workspace_bytes, stream);
   if (s != DSA_OK) return s;
   return dsa_sparse_attn_bwd_dq(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dq,
                                 workspace, workspace_bytes, stream);

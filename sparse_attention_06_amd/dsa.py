@@ -22,7 +22,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
           4: "DSA_ERR_HIP"}
 
 EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
-           "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes",
+           "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -50,12 +50,14 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
         L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                           vp, vp, vp, vp, sz, vp]
-        L.dsa_sparse_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
-                                               i32, vp, vp, vp, sz, vp]
+        L.dsa_sparse_attn_bwd_prep.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.dsa_sparse_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                               vp, vp, vp, sz, vp]
         L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, sz, vp]
         for f in ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
-                  "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv"):
+                  "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq",
+                  "dsa_sparse_attn_bwd_dkdv"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_mask_bytes.argtypes = [i32, i32]
         L.dsa_mask_bytes.restype = sz
@@ -157,14 +159,22 @@ def dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, d
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def dsa_sparse_attn_bwd_dkdv(q, k, v, o, dout, lse, mask, softmax_scale: float, dk, dv, workspace,
+def dsa_sparse_attn_bwd_prep(o, dout, lse, Dqk: int, workspace, stream=None) -> None:
+    """D and base-2 LSE into the workspace (first part of the backward)."""
+    B, S, H, Dv = o.shape
+    _check("dsa_sparse_attn_bwd_prep", lib().dsa_sparse_attn_bwd_prep(
+        _ptr(o), _ptr(dout), _ptr(lse), B, S, H, Dqk, Dv, _dt(o), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dsa_sparse_attn_bwd_dkdv(q, k, v, dout, lse, mask, softmax_scale: float, dk, dv, workspace,
                              stream=None) -> None:
-    """Key-major half: D and base-2 LSE into the workspace, then dk, dv (and,
-    on the MFMA path, the dS tiles for dsa_sparse_attn_bwd_dq)."""
+    """Key-major part: dk, dv (and, on the MFMA path, the dS tiles for
+    dsa_sparse_attn_bwd_dq); runs after dsa_sparse_attn_bwd_prep."""
     B, S, H, Dqk = q.shape
     Dv = v.shape[-1]
     _check("dsa_sparse_attn_bwd_dkdv", lib().dsa_sparse_attn_bwd_dkdv(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
         float(softmax_scale), _dt(q), _ptr(dk), _ptr(dv), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
