@@ -728,8 +728,14 @@ static size_t stash_lds_bytes(int nw_max, bool seg) {
   return (size_t)kStash * 4 + (size_t)nw_max * (seg ? 16 : 8);
 }
 
+// fp32 rows without segments are held to 64 VGPRs, so that four workgroups
+// (eight waves per SIMD) share a CU: 10% faster at 32K. The bf16 and
+// segment-aware instances gain nothing or spill at that budget.
+template <typename ST, bool SEG>
+constexpr int stash_waves_per_simd() { return (sizeof(ST) == 4 && !SEG) ? 8 : 1; }
+
 template <typename ST, bool SEG, int NW>
-__global__ __launch_bounds__(64 * NW) void topk_stash_kernel(const ST* __restrict__ scores, int64_t ld,
+__global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void topk_stash_kernel(const ST* __restrict__ scores, int64_t ld,
                                                              const int32_t* __restrict__ seg, int B, int S, int K,
                                                              int row0, int nrows, int rbeg, int rcount, int nw_max,
                                                              int32_t* __restrict__ idx,
