@@ -101,6 +101,20 @@ __device__ __forceinline__ u32x4 lds_tr_frag_x(const uint16_t* X, int pitch, int
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: four row shifts
+// give each 16-lane row its own prefix, then row 0's total is broadcast into
+// rows 1 and 3, and rows 0-1's total into rows 2 and 3. Lanes read zero past a
+// row's edge. No LDS round trip (a __shfl_up scan is six ds_bpermute waits).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Asynchronous global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
 // lane l's bytes land at lds_base + 16*l, so one wave fills a contiguous 1 KB
 // block. `lds_base` must be wave-uniform. Completion is waited for with

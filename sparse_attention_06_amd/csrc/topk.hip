@@ -74,12 +74,8 @@ __device__ void find_bin(TopkShared& sh, uint32_t need) {
   // inclusive prefix over j (descending bins) within the wave: lanes ordered by j
   // j = 255 - tid, so within a wave, lower j is higher lane. Use a suffix scan
   // over lanes: incl = sum of tot over lanes >= this lane.
-  uint32_t incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_down(incl, o);
-    if (lane + o < 64) incl += y;
-  }
+  const uint32_t pre = wave_incl_scan(tot);
+  const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + tot;
   if (lane == 0) sh.red_u[wid] = incl;  // wave total
   __syncthreads();
   // waves with larger wid hold higher bins
@@ -283,15 +279,7 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
     __syncthreads();
     // exclusive prefix over the row's words (lane = word), in every wave
     const uint32_t g = lane < nw ? wgt[lane] : 0u, e = lane < nw ? weq[lane] : 0u;
-    uint32_t gi = g, ei = e;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t gy = __shfl_up(gi, o), ey = __shfl_up(ei, o);
-      if (lane >= o) {
-        gi += gy;
-        ei += ey;
-      }
-    }
+    const uint32_t gi = wave_incl_scan(g), ei = wave_incl_scan(e);
     const uint32_t gx = gi - g, ex = ei - e;  // keys above T / ties in the words before
 #pragma unroll
     for (int j = 0; j < kRegWords; ++j) {
@@ -385,12 +373,8 @@ __device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, u
 #pragma unroll
   for (int i = 0; i < PER; ++i) { c[i] = hist[PER * tid + i]; tot += c[i]; }
   // suffix sum over the lanes at or above this one (they hold higher bins)
-  uint32_t incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_down(incl, o);
-    if (lane + o < 64) incl += y;
-  }
+  const uint32_t pre = wave_incl_scan(tot);
+  const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + tot;
   if (lane == 0) red[wid] = incl;  // wave total
   __syncthreads();
   uint32_t running = incl - tot;  // keys in bins above this thread's chunk
@@ -880,12 +864,9 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
           c[i] = sh.shist[PER * lane + i];
           tot += c[i];
         }
-        uint32_t incl = tot;  // samples in the bins of this lane and the lanes above
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_down(incl, o);
-          if (lane + o < 64) incl += y;
-        }
+        // samples in the bins of this lane and the lanes above
+        const uint32_t pre = wave_incl_scan(tot);
+        const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + tot;
         uint32_t running = incl - tot;
 #pragma unroll
         for (int i = PER - 1; i >= 0; --i) {
@@ -934,12 +915,7 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
           }
         }
         const uint32_t cnt = __popc(msk);
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(incl, o);
-          if (lane >= o) incl += y;
-        }
+        const uint32_t incl = wave_incl_scan(cnt);
         uint32_t slot = listed + incl - cnt;
         // the listed scores, in a static walk over the stage (each write is
         // masked to the lanes that list that score)
@@ -1060,12 +1036,7 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
     const int w = c0 + tid;
     const uint64_t m = w < nw ? selw[w] : 0ull;
     const uint32_t cnt = popc64(m);
-    uint32_t incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_scan(cnt);
     if (lane == 63) sh.wave_g[wid] = incl;
     __syncthreads();
     uint32_t pos = base + incl - cnt, tot = 0;
