@@ -227,35 +227,47 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// Wave reductions with DPP (no LDS round trips): the row shifts and row
+// broadcasts of wave_incl_scan, with lanes past a row's edge or outside the
+// row mask reading the identity; lane 63 ends with the whole wave's result,
+// which every lane then reads.
+template <int CTRL, int RMASK>
+__device__ __forceinline__ int dpp_or(int identity, int x) {
+  return __builtin_amdgcn_update_dpp(identity, x, CTRL, RMASK, 0xf, false);
+}
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_bits(int x, int identity, Op op) {
+  x = op(x, dpp_or<0x111, 0xf>(identity, x));
+  x = op(x, dpp_or<0x112, 0xf>(identity, x));
+  x = op(x, dpp_or<0x114, 0xf>(identity, x));
+  x = op(x, dpp_or<0x118, 0xf>(identity, x));
+  x = op(x, dpp_or<0x142, 0xa>(identity, x));
+  x = op(x, dpp_or<0x143, 0xc>(identity, x));
+  return __builtin_amdgcn_readlane(x, 63);
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  return __int_as_float(wave_reduce_bits(__float_as_int(x), __float_as_int(-INFINITY), [](int a, int b) {
+    return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
+  }));
 }
 __device__ __forceinline__ float wave_min(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o));
-  return x;
+  return __int_as_float(wave_reduce_bits(__float_as_int(x), __float_as_int(INFINITY), [](int a, int b) {
+    return __float_as_int(fminf(__int_as_float(a), __int_as_float(b)));
+  }));
 }
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return (uint32_t)wave_reduce_bits((int)x, 0, [](int a, int b) { return (int)((uint32_t)a + (uint32_t)b); });
 }
 __device__ __forceinline__ float wave_sumf(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return __int_as_float(wave_reduce_bits(__float_as_int(x), 0, [](int a, int b) {
+    return __float_as_int(__int_as_float(a) + __int_as_float(b));
+  }));
 }
 __device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  return (uint32_t)wave_reduce_bits((int)x, -1, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
 }
 __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
+  return (uint32_t)wave_reduce_bits((int)x, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
 }
 
 // order-preserving map float -> u32 (larger float => larger key; -0 == +0)
