@@ -93,7 +93,7 @@ __device__ __forceinline__ float fwd_scores(const uint16_t* sK, const u32x4 (&qf
     }
   }
   const float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-  return fmaxf(tmax, __shfl_xor(tmax, 32)) * scale_log2;  // scale > 0 commutes with max
+  return half_max(tmax) * scale_log2;  // scale > 0 commutes with max
 }
 
 // Update phase: online-softmax step with the masked logits of fwd_scores and
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     kt = kn;
   }
 
-  const float l_tot = l + __shfl_xor(l, 32);
+  const float l_tot = half_sum(l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qvalid) {
     uint16_t* orow = o + ((size_t)b * S + tq) * rs_v + (size_t)h * DV;

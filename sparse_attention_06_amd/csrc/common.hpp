@@ -227,6 +227,19 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
+// x(l) + x(l ^ 32) and max(x(l), x(l ^ 32)) in every lane through
+// v_permlane32_swap, which trades the upper half of its first operand with the
+// lower half of its second: with both operands x, the first result holds the
+// lower half's values in both halves and the second the upper half's.
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Wave reductions with DPP (no LDS round trips): the row shifts and row
 // broadcasts of wave_incl_scan, with lanes past a row's edge or outside the
 // row mask reading the identity; lane 63 ends with the whole wave's result,

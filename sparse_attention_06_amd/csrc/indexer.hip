@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
       for (int rr = 0; rr < 16; ++rr)
         part[rr & 3] = fmaf(wreg[hb][rr], fmaxf(acc[hb][rr], 0.f), part[rr & 3]);
     const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-    return tot + __shfl_xor(tot, 32);
+    return half_sum(tot);
   };
 
   // Software pipeline over 32-key blocks: the MFMAs of one block run while
