@@ -706,10 +706,15 @@ __device__ __forceinline__ uint32_t bkey16(uint32_t h) {
   return (h & 0x8000u) ? (~h & 0xffffu) : (h | 0x8000u);
 }
 
-// dynamic LDS of topk_stash_kernel: the list, the selection mask, the
-// segment-validity words
+// dynamic LDS of topk_stash_kernel: the list, which the selection mask
+// reuses once the list has been read into registers, then the
+// segment-validity words. Sharing keeps a 128K row's workgroup at 36 KB of
+// LDS, four per CU.
+static size_t stash_list_bytes(int nw_max) {
+  return (size_t)nw_max * 8 > (size_t)kStash * 4 ? (size_t)nw_max * 8 : (size_t)kStash * 4;
+}
 static size_t stash_lds_bytes(int nw_max, bool seg) {
-  return (size_t)kStash * 4 + (size_t)nw_max * (seg ? 16 : 8);
+  return stash_list_bytes(nw_max) + (seg ? (size_t)nw_max * 8 : 0);
 }
 
 // fp32 rows without segments are held to 64 VGPRs, so that four workgroups
@@ -732,8 +737,9 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   __shared__ StashShared sh;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   uint32_t* stash = dyn;                         // the list
-  uint64_t* selw = (uint64_t*)(dyn + kStash);    // per word: the selected positions
-  uint64_t* segw = selw + nw_max;                // per word: same-segment positions <= t
+  uint64_t* selw = (uint64_t*)dyn;               // per word: the selected positions (after the list)
+  // per word: same-segment positions <= t
+  uint64_t* segw = (uint64_t*)(dyn + (nw_max * 2 > kStash ? nw_max * 2 : kStash));
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -813,7 +819,6 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   if (take_all) {
     for (int w = tid; w < nw; w += NT) selw[w] = segw[w];
   } else {
-    for (int w = tid; w < nw; w += NT) selw[w] = 0ull;
     for (int i = tid; i < kNB; i += NT) sh.hist[i] = 0;
     for (int i = tid; i < kSB; i += NT) sh.shist[i] = 0;
     if (tid == 0) sh.ncand = 0;
@@ -958,6 +963,10 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
       if (over || nst < (uint32_t)K) {
         fail = true;
       } else {
+        // every thread holds its list slots (find_bin_n passed barriers since):
+        // the mask takes over the list's LDS
+        for (int w = tid; w < nw; w += NT) selw[w] = 0ull;
+        __syncthreads();
         const uint32_t bstar = sh.found_bin;
         const uint32_t need = (uint32_t)K - sh.found_above;
 #pragma unroll
