@@ -309,6 +309,38 @@ def test_attention_bwd(S, K, segments, dtype, dims):
     check_close("dv", f64(path.dv), dv, bf16=bf, rel=2e-2)
 
 
+@pytest.mark.parametrize("S,K,segments", [(777, 48, (10, 100)), (640, 2048, None)])
+def test_attention_bwd_parts_on_poisoned_workspace(S, K, segments):
+    """prep, dK/dV and dQ called one by one on a workspace full of 0xFF bytes
+    (NaN as fp32 and bf16) give what the whole call gives, and match the
+    oracle: dQ reads only the dS tiles dK/dV wrote (short segments leave many
+    tiles EMPTY; K >= S makes every causal tile FULL)."""
+    cfg = _cfg(S=S, K=K, segments=segments, dtype="bf16", scaled=True, Dqk=192, Dv=128, H=2)
+    x, d = _make(cfg)
+    B = cfg.B
+    sets = _sets(cfg, x)
+    path = DSAPath(B, S, cfg.Hi, cfg.Di, K, cfg.H, 192, 128, dtype=cfg.torch_dtype(), backward=True)
+    path.build_mask(torch.from_numpy(sets).to(DEV), _seg_dev(x))
+    path.forward(d["q"], d["k"], d["v"], cfg.softmax_scale)
+    path.backward(d["q"], d["k"], d["v"], d["dout"], cfg.softmax_scale)
+    whole = [t.clone() for t in (path.dq, path.dk, path.dv)]
+    ws = torch.full_like(path.ws, 0xFF)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in whole)
+    dsa.dsa_sparse_attn_bwd_prep(path.o, d["dout"], path.lse, 192, ws)
+    dsa.dsa_sparse_attn_bwd_dkdv(d["q"], d["k"], d["v"], d["dout"], path.lse, path.mask, cfg.softmax_scale,
+                                 dk, dv, ws)
+    dsa.dsa_sparse_attn_bwd_dq(d["q"], d["k"], d["v"], d["dout"], path.lse, path.mask, cfg.softmax_scale,
+                               dq, ws)
+    torch.cuda.synchronize()
+    for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), whole):
+        assert torch.equal(got, want), name
+    rdq, rdk, rdv = ref.attention_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"]), sets,
+                                      _seg_np(x), cfg.softmax_scale)
+    check_close("dq", f64(dq), rdq, bf16=True, rel=2e-2)
+    check_close("dk", f64(dk), rdk, bf16=True, rel=2e-2)
+    check_close("dv", f64(dv), rdv, bf16=True, rel=2e-2)
+
+
 def test_end_to_end_tiny_fp32():
     """The 128-token fp32 workload: indexer, top-k and forward against the oracle."""
     cfg = inputs.CONFIGS["c1"]
