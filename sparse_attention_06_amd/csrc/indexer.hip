@@ -11,12 +11,13 @@
 // head rows per 32-head block, so the ReLU and the w-weighted sum over heads
 // are in-lane float32 FMAs, with one exchange between the two lane halves.
 // q_idx[t] (Hi x Di bf16, 16 KB at 64 x 128) stays in VGPRs as MFMA A
-// fragments for the whole key loop. A 64-key k_idx tile is copied straight
+// fragments for the whole key loop. A 128-key k_idx tile is copied straight
 // into padded LDS (global_load_lds) once per workgroup (4 waves = 4
-// consecutive queries) and double buffered. The two 32-key column blocks'
-// MFMAs are issued before either epilogue, so one epilogue overlaps the
-// other's MFMAs. Lane half 0 stores the first block's scores, half 1 the
-// second's.
+// consecutive queries) and double buffered. The tile is four 32-key column
+// blocks, software-pipelined: the MFMAs of one block run while the previous
+// block's ReLU and weighted sums are formed, across the tile barrier too.
+// Lane l stores key 128*kt + l from blocks 0/1 and 128*kt + 64 + l from
+// blocks 2/3.
 #include "common.hpp"
 #include "launch.hpp"
 
