@@ -4,20 +4,23 @@
 // Flow: the forward runs query-major while dK/dV run key-major. Each uses the
 // same index mask, dQ = dP K, dK = dP^T Q and dV = P^T dO.
 //
-//   D(t)   = sum_e dO(t,e) O(t,e)       (computed by the query-major kernel,
-//                                         which runs first and stores it)
+//   D(t)   = sum_e dO(t,e) O(t,e)       (a prologue kernel stores it, with the
+//                                         base-2 LSE, in the workspace)
 //   P      = exp(scale q.k - LSE(t)) on kept (t, s)
 //   dP     = dO(t) . v(s),   dS = P (dP - D(t))
 //   dV(s) += P dO(t),        dK(s) += scale dS q(t)      (key-major kernel)
 //   dQ(t)  = scale sum_s dS k(s)                         (query-major kernel)
-// Both MFMA kernels recompute P from LSE. Neither uses atomics, so the result
-// is deterministic. The key-major kernel reads the same row-major selection
-// words as the forward. A lane owns one key, so the bit it needs sits at a
-// fixed position of each query's word, and no transposed copy of the mask is
-// needed. Operands that the MFMAs need transposed (Q^T and dO^T for dK/dV, K^T
-// for dQ) come from the natural LDS tiles through ds_read_b64_tr_b16. Tiles
-// are double buffered, and the next tile's global loads are issued before the
-// current tile is computed.
+// The key-major kernel runs first: it recomputes P from LSE, forms dS, and
+// also stores dS^T in the workspace as MFMA B-operand fragments, which the
+// query-major kernel then contracts with K; nothing is recomputed there.
+// Neither uses atomics, so the result is deterministic. The key-major kernel
+// reads the same row-major selection words as the forward. A lane owns one
+// key, so the bit it needs sits at a fixed position of each query's word, and
+// no transposed copy of the mask is needed. Operands that the MFMAs need
+// transposed (Q^T and dO^T for dK/dV, dS^T and K^T for dQ) come from natural
+// row-major LDS tiles through ds_read_b64_tr_b16. Tiles are double (or more)
+// buffered, and later tiles' copies are issued before the current tile is
+// computed.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -42,9 +45,11 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 // wave w and wave w+4 share a SIMD and the same 32 keys:
 //   waves 0-3 ("A", K/V fragments in VGPRs, raised issue priority):
 //     S = Q K^T and dP = dO V^T for a 32-query chunk, then P and
-//     dS = P (dP - D). P and dS go to LDS in MFMA B-operand layout.
+//     dS = P (dP - D). P goes to LDS in MFMA B-operand layout, dS as a
+//     row-major [32 keys][32 queries] tile.
 //   waves 4-7 ("B", dV^T and dK^T accumulators): dV^T += dO^T P and
-//     dK^T += Q^T dS, one chunk behind A.
+//     dK^T += Q^T dS, one chunk behind A; they also read the dS tile
+//     transposed and store it as the dQ kernel's fragments.
 // Each role issues 20 MFMAs per chunk. A's softmax-gradient VALU work hides
 // under B's MFMAs: A has priority, so its MFMAs issue first after a barrier
 // and B's fill the matrix pipe while A works on P and dS. Chunks with EMPTY
