@@ -30,10 +30,7 @@ namespace bwd {
 constexpr int DQK = 192, DV = 128;
 constexpr int QC = 32;              // queries per chunk (key-major kernel)
 constexpr int TK = 64;              // keys per tile (query-major kernel)
-constexpr int QP = DQK + 8;         // LDS pitch (elements) of q / k rows
-constexpr int OP = DV + 8;          // LDS pitch of dO / v rows
-constexpr int KCH = TK * DQK / 8 / 256;  // K tile (6)
-constexpr int VCH = TK * DV / 8 / 256;   // V tile (4)
+constexpr int QP = DQK + 8;         // LDS pitch (elements) of K rows (query-major kernel)
 }  // namespace bwd
 
 __device__ __forceinline__ u32x4 pack8(const float* x) {

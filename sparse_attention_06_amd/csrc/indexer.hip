@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
 template <typename InT, typename OutT>
 __global__ __launch_bounds__(256) void index_scores_plain_kernel(
     const InT* __restrict__ q_idx, const InT* __restrict__ k_idx, const InT* __restrict__ w,
-    const int32_t* __restrict__ seg, int B, int S, int Hi, int Di, int row0, int nrows,
+    const int32_t* __restrict__ seg, int S, int Hi, int Di, int row0, int nrows,
     OutT* __restrict__ scores, int64_t ld) {
   extern __shared__ float smem[];  // Hi*Di query values, then Hi weights
   const int nkb = (S + 255) / 256;
@@ -261,7 +261,7 @@ hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const
   const size_t shm = (size_t)(Hi * Di + Hi) * sizeof(float);
 #define DSA_IDX_PLAIN(IT, OT)                                                               \
   hipLaunchKernelGGL((index_scores_plain_kernel<IT, OT>), grid, block, shm, st, (const IT*)q_idx, \
-                     (const IT*)k_idx, (const IT*)w, seg, B, S, Hi, Di, row0, nrows, (OT*)scores, ld)
+                     (const IT*)k_idx, (const IT*)w, seg, S, Hi, Di, row0, nrows, (OT*)scores, ld)
   if (in_bf16) {
     if (out_bf16) DSA_IDX_PLAIN(uint16_t, uint16_t); else DSA_IDX_PLAIN(uint16_t, float);
   } else {

@@ -1091,8 +1091,8 @@ __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restri
 // key tiles). Lane = key tile (one mask word per row), wave w takes rows
 // t0 + 32w .. t0 + 32w + 31 of the query tile, and the four waves' OR and AND
 // of their words are combined in LDS.
-__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int B, int S,
-                                                         int qt0, uint8_t* __restrict__ cls) {
+__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int S, int qt0,
+                                                         uint8_t* __restrict__ cls) {
   __shared__ uint64_t s_or[4][64], s_and[4][64];
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -1202,7 +1202,7 @@ hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int qt0, int 
                                hipStream_t st) {
   if (qt1 <= qt0) return hipSuccess;
   dim3 grid((unsigned)((n_ktiles(S) + 63) / 64), (unsigned)(qt1 - qt0), (unsigned)B);
-  hipLaunchKernelGGL(tile_class_kernel, grid, dim3(256), 0, st, bits, B, S, qt0, cls);
+  hipLaunchKernelGGL(tile_class_kernel, grid, dim3(256), 0, st, bits, S, qt0, cls);
   return hipGetLastError();
 }
 
