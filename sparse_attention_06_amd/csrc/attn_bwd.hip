@@ -14,11 +14,10 @@
 // also stores dS^T in the workspace as MFMA B-operand fragments, which the
 // query-major kernel then contracts with K; nothing is recomputed there.
 // Neither uses atomics, so the result is deterministic. The key-major kernel
-// reads the same row-major selection words as the forward. A lane owns one
-// key, so the bit it needs sits at a fixed position of each query's word, and
-// no transposed copy of the mask is needed. Operands that the MFMAs need
-// transposed (Q^T and dO^T for dK/dV, dS^T and K^T for dQ) come from natural
-// row-major LDS tiles through ds_read_b64_tr_b16. Tiles are double (or more)
+// reads the same row-major selection words as the forward: a lane owns one
+// query and 16 keys of its word, so no transposed copy of the mask is needed.
+// Operands that the MFMAs need transposed (Q^T, dO^T, P and dS for dK/dV, K^T
+// for dQ) come from natural row-major LDS tiles through ds_read_b64_tr_b16. Tiles are double (or more)
 // buffered, and later tiles' copies are issued before the current tile is
 // computed.
 #include "common.hpp"
@@ -41,12 +40,14 @@ __device__ __forceinline__ u32x4 pack8(const float* x) {
 // dK / dV, key-major. Workgroup = (b, h, 128 keys) with 8 waves in two roles;
 // wave w and wave w+4 share a SIMD and the same 32 keys:
 //   waves 0-3 ("A", K/V fragments in VGPRs, raised issue priority):
-//     S = Q K^T and dP = dO V^T for a 32-query chunk, then P and
-//     dS = P (dP - D). P goes to LDS in MFMA B-operand layout, dS as a
-//     row-major [32 keys][32 queries] tile.
+//     S^T = K Q^T and dP^T = V dO^T for a 32-query chunk, then P and
+//     dS = P (dP - D). In the transposed orientation a lane holds one query
+//     (so one LSE, one D and one mask word per lane) and 16 keys, which is
+//     exactly the dQ kernel's B-operand fragment of dS^T: A stores it to the
+//     workspace straight from registers. P and dS also go to LDS as
+//     row-major [32 queries][32 keys] tiles.
 //   waves 4-7 ("B", dV^T and dK^T accumulators): dV^T += dO^T P and
-//     dK^T += Q^T dS, one chunk behind A; they also read the dS tile
-//     transposed and store it as the dQ kernel's fragments.
+//     dK^T += Q^T dS, one chunk behind A, with P and dS read transposed.
 // Each role issues 20 MFMAs per chunk. A's softmax-gradient VALU work hides
 // under B's MFMAs: A has priority, so its MFMAs issue first after a barrier
 // and B's fill the matrix pipe while A works on P and dS. Chunks with EMPTY
@@ -91,10 +92,9 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   using dkv::NB;
   __shared__ __attribute__((aligned(1024))) unsigned char smQ[NB][dkv::QBLK * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char smO[NB][dkv::OBLK * 1024];
-  // P of each A wave, B-operand layout: [buf][wave][p2][lane]
-  __shared__ __attribute__((aligned(16))) u32x4 smP[2][4][2][64];
-  // dS of each A wave as a row-major [32 keys][32 queries] tile (pitch
-  // dkv::TP): B reads its rows for dK, A reads it transposed for dQ
+  // P and dS of each A wave as row-major [32 queries][32 keys] tiles (pitch
+  // dkv::TP), which B reads transposed as MFMA B operands
+  __shared__ __attribute__((aligned(16))) uint16_t smP[2][4][32 * dkv::TP];
   __shared__ __attribute__((aligned(16))) uint16_t smT[2][4][32 * dkv::TP];
   // per chunk: LSE in base-2 units of its 32 queries, then D
   __shared__ __attribute__((aligned(16))) float smLD[NB][2 * QC];
@@ -183,6 +183,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   auto issue = [&](int qc, int bi) {
     const int q0 = qc * QC;
     const bool ragged = q0 + QC > S;  // rows past S copy row S-1
+    const uint16_t* qsrc = uniform_ptr(qbase + (size_t)q0 * rs_qk);
+    const uint16_t* osrc = uniform_ptr(obase + (size_t)q0 * rs_v);
 #pragma unroll
     for (int i = 0; i < dkv::NSLOT; ++i) {
       const int kslot = kw + 4 * i;
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
           off = slot_src(kslot, row);
           off -= (uint32_t)((row - min(row, S - 1 - q0)) * rs_qk);
         }
-        g2lds16_async(qbase + (size_t)q0 * rs_qk + off, smQ[bi] + kslot * 1024);
+        g2lds16_async_off(qsrc, 2 * off, smQ[bi] + kslot * 1024);
       } else if (kslot < dkv::K_LD) {
         uint32_t off = soff[i];
         if (ragged) {
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
           off = slot_src(kslot, row);
           off -= (uint32_t)((row - min(row, S - 1 - q0)) * rs_v);
         }
-        g2lds16_async(obase + (size_t)q0 * rs_v + off, smO[bi] + (kslot - dkv::QBLK) * 1024);
+        g2lds16_async_off(osrc, 2 * off, smO[bi] + (kslot - dkv::QBLK) * 1024);
       } else if (kslot == dkv::K_LD) {
         const int t = min(q0 + col, S - 1);
         g2lds4_async(half ? drow + t : lrow + t, smLD[bi]);
@@ -270,7 +272,6 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       qa[par] = (uint32_t)(col * dkv::QPX * 2 + 16 * ((2 * par + half) ^ u));
       oa[par] = (uint32_t)(col * dkv::OPX * 2 + 16 * ((2 * par + half) ^ u));
     }
-    const int bsh = sk & 31;
     const int wsel = (kw >> 1), hsel = (s0 >> 5) & 1;  // the pair's key tile and word half
     for (int it = 0; e0 >= 0; ++it) {
       lds_barrier();  // chunk e0 visible (B waited for its copies); B is done with P/dS buffer it&1
@@ -282,52 +283,46 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         f32x16 sacc, dpacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+        // transposed scores: S^T = K Q^T and dP^T = V dO^T, so lane (half, col)
+        // holds query col and keys 8i + 4*half + r (i, r = 0..3) of the pair
 #pragma unroll
         for (int ks = 0; ks < DQK / 16; ++ks)
-          sacc = mfma32(*(const u32x4*)(sQ + qa[ks & 1] + 64 * (ks >> 1)), kf[ks], sacc);
+          sacc = mfma32(kf[ks], *(const u32x4*)(sQ + qa[ks & 1] + 64 * (ks >> 1)), sacc);
 #pragma unroll
         for (int ks = 0; ks < DV / 16; ++ks)
-          dpacc = mfma32(*(const u32x4*)(sO + oa[ks & 1] + 64 * (ks >> 1)), vf[ks], dpacc);
-        // per-row scalars of this lane's 16 query rows (rows 8i + 4*half + r are
-        // 4-aligned runs): base-2 LSE, D and this pair's 32-bit half of each
-        // mask word. FULL tiles have every in-range bit set.
-        const uint32_t* wrow = smW[bi][wsel][hsel];
+          dpacc = mfma32(vf[ks], *(const u32x4*)(sO + oa[ks & 1] + 64 * (ks >> 1)), dpacc);
+        // the lane's query: base-2 LSE, D and the pair's 32-bit half of its mask
+        // word, shifted so that key 8i + 4*half + r sits at bit 8i + r. FULL
+        // tiles have every in-range bit set.
+        const float Lq = smLD[bi][col], Dq = smLD[bi][QC + col];
+        const uint32_t Wq = smW[bi][wsel][hsel][col] >> (4 * half);
+        u32x4* fr = dsf + (((size_t)bh * dsf_tile_base(nchunks) + dsf_tile_base(qc) + kt_lo + (kw >> 1)) * 4 +
+                           2 * (kw & 1)) * 64 + lane;
 #pragma unroll
         for (int p2 = 0; p2 < 2; ++p2) {
-          float Lr[8], Dr[8];
-          uint32_t Wr[8];
-#pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2) {
-            const int r0 = 8 * (2 * p2 + i2) + 4 * half;
-            const f32x4 l4 = *(const f32x4*)&smLD[bi][r0];
-            const f32x4 d4 = *(const f32x4*)&smLD[bi][QC + r0];
-            const u32x4 w4 = *(const u32x4*)&wrow[r0];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              Lr[4 * i2 + j] = l4[j];
-              Dr[4 * i2 + j] = d4[j];
-              Wr[4 * i2 + j] = w4[j];
-            }
-          }
           float p[8], ds[8];
 #pragma unroll
           for (int c8 = 0; c8 < 8; ++c8) {
             const int r = 8 * p2 + c8;
             // keep ? P : 0 as a bit select on an all-ones / all-zeros field
-            const int keep = __builtin_amdgcn_sbfe((int)Wr[c8], bsh, 1);
+            const int keep = __builtin_amdgcn_sbfe((int)Wq, 8 * (r >> 2) + (r & 3), 1);
             const float pr =
-                __int_as_float(keep & __float_as_int(fast_exp2(fmaf(sacc[r], scale_log2, -Lr[c8]))));
+                __int_as_float(keep & __float_as_int(fast_exp2(fmaf(sacc[r], scale_log2, -Lq))));
             p[c8] = pr;
-            ds[c8] = pr * (dpacc[r] - Dr[c8]);
+            ds[c8] = pr * (dpacc[r] - Dq);
           }
-          smP[it & 1][kw][p2][lane] = pack8(p);
-          // this lane's key row, queries 16*p2 + 4*half + 0..3 and 16*p2 + 8 + 4*half + 0..3
-          const u32x4 dsp = pack8(ds);
+          // keys 16*p2 + 4*half + 0..3 and 16*p2 + 8 + 4*half + 0..3 of query
+          // col: a row segment of the [query][key] P and dS tiles, and, for dS,
+          // exactly the dQ kernel's B-operand fragment for this 16-key step
+          const u32x4 pp = pack8(p), dsp = pack8(ds);
+          uint16_t* prow = smP[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
           uint16_t* trow = smT[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
+          *(u32x2*)prow = u32x2{pp[0], pp[1]};
+          *(u32x2*)(prow + 8) = u32x2{pp[2], pp[3]};
           *(u32x2*)trow = u32x2{dsp[0], dsp[1]};
           *(u32x2*)(trow + 8) = u32x2{dsp[2], dsp[3]};
+          fr[64 * p2] = dsp;
         }
-        (void)qc;
       }
       e0 = e1;
       e1 = e2;
@@ -364,24 +359,6 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
       return u32x4{ux[0], ux[1], uy[0], uy[1]};
     };
-    // dS^T fragments of the chunk B last updated, for the dQ kernel: lane
-    // (half, col) holds query col and keys 16*p2 + 4*half + {0..3, 8..11} of
-    // this pair, the order in which the dQ kernel reads the matching K^T rows.
-    // They are stored right after the next barrier, before that iteration's
-    // copies, so the counted wait for a chunk's copies stays exact: copies
-    // complete in order, so while one of them is in flight, all copies issued
-    // after it are too.
-    u32x4 fhold[2];
-    int qhold = -1;
-    auto store_frags = [&]() {
-      if (qhold >= 0) {
-        u32x4* fr = dsf + (((size_t)bh * dsf_tile_base(nchunks) + dsf_tile_base(qhold) + kt_lo + (kw >> 1)) * 4 +
-                           2 * (kw & 1)) * 64 + lane;
-        fr[0] = fhold[0];
-        fr[64] = fhold[1];
-        qhold = -1;
-      }
-    };
     // dV^T[e, s] += dO^T[e, q] P[q, s] and dK^T[d, s] += Q^T[d, q] dS[q, s] for
     // the chunk of iteration `it`; the query order inside each 16-query step
     // matches the A wave's accumulator rows
@@ -390,10 +367,9 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       const char* sO = (const char*)smO[it % NB];
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
-        const u32x4 pb = smP[it & 1][kw][p2][lane];
-        const uint16_t* trow = smT[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
-        const u32x2 d0 = *(const u32x2*)trow, d1 = *(const u32x2*)(trow + 8);
-        const u32x4 db = u32x4{d0[0], d0[1], d1[0], d1[1]};
+        // lane (half, col): key col, queries 16*p2 + 4*half + {0..3, 8..11}
+        const u32x4 pb = lds_tr_frag(smP[it & 1][kw], dkv::TP, 16 * p2 + 4 * half, 16 * p2 + 4 * half + 8, 0);
+        const u32x4 db = lds_tr_frag(smT[it & 1][kw], dkv::TP, 16 * p2 + 4 * half, 16 * p2 + 4 * half + 8, 0);
 #pragma unroll
         for (int eb = 0; eb < DV / 32; ++eb)
           dvacc[eb] = mfma32(tr(sO + 64 * eb, ot[p2][0], ot[p2][1]), pb, dvacc[eb]);
@@ -401,35 +377,21 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         for (int d2 = 0; d2 < DQK / 32; ++d2)
           dkacc[d2] = mfma32(tr(sQ + 64 * d2, qt[p2][0], qt[p2][1]), db, dkacc[d2]);
       }
-#pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2)
-        fhold[p2] = lds_tr_frag(smT[it & 1][kw], dkv::TP, 16 * p2 + 4 * half, 16 * p2 + 4 * half + 8, 0);
     };
     bool prev = false;
-    int qprev = 0;
     int it = 0;
     for (; e0 >= 0; ++it) {
       publish_b(it);
-      store_frags();
       if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
       const int e3 = entry(it + 3);
-      if (prev) {  // the chunk A finished before this barrier
-        update(it - 1);
-        qhold = qprev;
-      }
+      if (prev) update(it - 1);  // the chunk A finished before this barrier
       prev = active(e0);
-      qprev = e0 & 0x3FFF;
       e0 = e1;
       e1 = e2;
       e2 = e3;
     }
     lds_barrier();  // A's P and dS of the last chunk are visible
-    store_frags();
-    if (prev) {
-      update(it - 1);
-      qhold = qprev;
-      store_frags();
-    }
+    if (prev) update(it - 1);
     if (kvalid) {
       uint16_t* dkrow = dk + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK;
 #pragma unroll
