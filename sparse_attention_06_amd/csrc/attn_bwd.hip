@@ -321,7 +321,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
           *(u32x2*)(prow + 8) = u32x2{pp[2], pp[3]};
           *(u32x2*)trow = u32x2{dsp[0], dsp[1]};
           *(u32x2*)(trow + 8) = u32x2{dsp[2], dsp[3]};
-          fr[64 * p2] = dsp;
+          __builtin_nontemporal_store(dsp, fr + 64 * p2);  // streamed: read once, by the dQ kernel
         }
       }
       e0 = e1;
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4* src = (j < 2 * nh) ? fch + 256 * kt + 64 * j : fbh;
-      g2lds16_async_off(src, (uint32_t)lane * 16u, &smF[f][wid][j][0]);
+      g2lds16_async_off_nt(src, (uint32_t)lane * 16u, &smF[f][wid][j][0]);
     }
   };
 
