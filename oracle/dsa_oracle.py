@@ -26,6 +26,9 @@ Sources (page title · section):
         each masked the same way.
   [P2t] same page · "Tests". The index mask is threaded with and without
         segment IDs.
+  [P3r] "DeepSeek3.2: Onboard sparse attention" · "What this PR does",
+        item 4. The original indexer runs on quantized fp8 inputs (the fp8
+        indexer section at the end states the readings of that format).
 
 The indexer formula is not printed on the pages. It is the standard one of
 the method: I[t,s] = sum_j w[t,j] * ReLU(q_idx[t,j,:] . k_idx[s,:]), with a
@@ -386,3 +389,125 @@ def attention_bwd_keys(q, k, v, dout, idx, seg, scale: float, keys, heads):
                 dk[b, i] += scale * dS * q[b, t, h]
                 dv[b, i] += P[pos] * dout[b, t, h]
     return dk, dv
+
+
+# ----------------------------------------------------------------------------
+# next row: fp8 indexer                                                [P3r]
+# ----------------------------------------------------------------------------
+# [P3r] "DeepSeek3.2: Onboard sparse attention" · "What this PR does", item 4:
+# the original torch reference runs its indexer through quantization and fp8
+# kernels (activation quantization, an fp8 GEMM and an fp8 index kernel). The
+# page gives no format. Readings taken here:
+#   * OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent (bias 7) and 3 mantissa
+#     bits; no infinities; largest finite magnitude 448; smallest normal 2**-6;
+#     subnormals are multiples of 2**-9.
+#   * One float32 scale per quantized row: per (token, index head) for q_idx,
+#     per token for k_idx. scale = amax / 448 in float32, the row is divided by
+#     it in float32 and rounded to the nearest e4m3 value, ties to even. An
+#     all-zero row gets scale 0 and zero codes.
+#   * The scores are the indexer formula on the dequantized values
+#     code * scale; w keeps its own precision.
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_round(x) -> np.ndarray:
+    """Round values to the nearest OCP E4M3 value, ties to even, float64 out.
+
+    Normal range (|x| >= 2**-6): write |x| = m * 2**e with 0.5 <= m < 1; the
+    format keeps 4 significant bits, so m * 2**4 is rounded to an integer
+    (ties to even) and scaled back. Below 2**-6 the grid is uniform with step
+    2**-9. Magnitudes that round past 448 are outside the format; the
+    quantizer below never produces them, and they raise here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    out = np.zeros_like(a)
+    sub = a < 2.0 ** -6
+    out[sub] = np.rint(a[sub] * 512.0) / 512.0
+    nrm = ~sub & (a > 0)
+    m, e = np.frexp(a[nrm])
+    out[nrm] = np.ldexp(np.rint(m * 16.0), e - 4)
+    if np.any(out > FP8_MAX):
+        raise ValueError("value outside the e4m3 range")
+    return np.copysign(out, x)
+
+
+def fp8_e4m3_encode(v) -> np.ndarray:
+    """uint8 codes of values already on the E4M3 grid (bit layout s eeee mmm)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    code = np.zeros(a.shape, dtype=np.int64)
+    sub = (a < 2.0 ** -6) & (a > 0)
+    code[sub] = np.rint(a[sub] * 512.0).astype(np.int64)           # exponent field 0
+    nrm = a >= 2.0 ** -6
+    m, e = np.frexp(a[nrm])                                         # a = m 2**e, m in [0.5, 1)
+    frac = np.rint(m * 16.0).astype(np.int64) - 8                   # 3 mantissa bits
+    code[nrm] = ((e - 1 + 7) << 3) | frac
+    code |= np.signbit(v).astype(np.int64) << 7
+    return code.astype(np.uint8)
+
+
+def fp8_e4m3_decode(code) -> np.ndarray:
+    """float64 values of uint8 E4M3 codes (the NaN codes 0x7f / 0xff excluded)."""
+    c = np.asarray(code, dtype=np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where(c >> 7, -mag, mag)
+
+
+def quantize_fp8_rows(x):
+    """Quantize the last axis of x to E4M3 with one float32 scale per row.
+
+    Returns (codes uint8, same shape as x; scale float32, x.shape[:-1]). The
+    arithmetic is float32, as the readings above state: amax, scale =
+    amax / 448 and x / scale are each rounded to float32 before the final
+    rounding to E4M3.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    scale = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x32 / safe[..., None]).astype(np.float32)
+    y = np.where(scale[..., None] > 0, y, np.float32(0.0))
+    codes = fp8_e4m3_encode(fp8_e4m3_round(y.astype(np.float64)))
+    return codes, scale
+
+
+def index_scores_fp8(q8, q_scale, k8, k_scale, w, seg, rows) -> np.ndarray:
+    """Indexer scores of fp8 inputs for the given query rows, in float64.
+
+    q8 [B,S,Hi,Di] and k8 [B,S,Di] are E4M3 codes, q_scale [B,S,Hi] and
+    k_scale [B,S] their float32 scales, w [B,S,Hi]. The scores are the
+    indexer formula on the dequantized values (index_scores above).
+    """
+    q = fp8_e4m3_decode(q8) * np.asarray(q_scale, np.float64)[..., None]
+    k = fp8_e4m3_decode(k8) * np.asarray(k_scale, np.float64)[..., None]
+    return index_scores(q, k, w, seg, rows)
+
+
+def index_scores_fp8_bound(q8, q_scale, k8, k_scale, w, rows, rel: float) -> np.ndarray:
+    """Elementwise error bound [B, len(rows), S] for a kernel that forms each
+    head's dot product q8 . k8 with an absolute error of at most
+    rel * Di * max_d |q8_d| * max_d |k8_d| (in code units), and everything
+    after it in float32:
+        bound = sum_j |w_j| q_scale_j k_scale * rel * Di * max|q8_j| * max|k8|
+              + 1e-6 * sum_j |w_j q_scale_j k_scale| * |q8_j| . |k8|.
+    The second term covers float32 rounding of the products and the head sum.
+    """
+    qv = np.abs(fp8_e4m3_decode(q8))                      # [B,S,Hi,Di]
+    kv = np.abs(fp8_e4m3_decode(k8))                      # [B,S,Di]
+    w = np.abs(np.asarray(w, np.float64))
+    qs = np.asarray(q_scale, np.float64)
+    ks = np.asarray(k_scale, np.float64)
+    B, S, Hi, Di = qv.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, rows.size, S))
+    for b in range(B):
+        kmax = kv[b].max(axis=-1) * ks[b]                 # [S]
+        for r, t in enumerate(rows):
+            wq = w[b, t] * qs[b, t]                       # [Hi]
+            mq = qv[b, t].max(axis=-1)                    # [Hi]
+            dot_abs = qv[b, t] @ kv[b].T                  # [Hi, S]
+            out[b, r] = rel * Di * (wq * mq).sum() * kmax + 1e-6 * (wq @ dot_abs) * ks[b]
+    return out

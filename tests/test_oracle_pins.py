@@ -513,3 +513,132 @@ def test_inputs_deterministic_and_distribution():
             kept = row[row >= 0]
             assert np.all(np.diff(kept) > 0) and np.all(kept <= t)
             assert np.all(seg[b, kept] == seg[b, t])
+
+
+# ------------------------------------------------------------ fp8 indexer pins
+def _torch_e4m3(x32):
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn)
+
+
+def test_fp8_round_encode_decode_match_torch():
+    # library pin: torch's float32 -> float8_e4m3fn conversion (round to nearest even)
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(50000) * 60.0, rng.standard_normal(20000) * 0.01,
+                        rng.uniform(-448.0, 448.0, 20000)]).astype(np.float32)
+    x = np.clip(x, -448.0, 448.0)
+    t = _torch_e4m3(x)
+    np.testing.assert_array_equal(ref.fp8_e4m3_round(x), t.float().numpy())
+    np.testing.assert_array_equal(ref.fp8_e4m3_encode(ref.fp8_e4m3_round(x)), t.view(torch.uint8).numpy())
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    dec = ref.fp8_e4m3_decode(codes)
+    np.testing.assert_array_equal(dec, torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy())
+    np.testing.assert_array_equal(ref.fp8_e4m3_encode(dec), codes)
+    # hand cases: ties go to the even mantissa; the subnormal grid is 2**-9
+    hand = {1.0625: 1.0, 1.1875: 1.25, 2.0 ** -10: 0.0, 3 * 2.0 ** -10: 2.0 ** -8, 0.3: 0.3125,
+            447.0: 448.0, -240.0: -240.0, 2.0 ** -6: 2.0 ** -6}
+    for a, b in hand.items():
+        assert ref.fp8_e4m3_round(np.array([a]))[0] == b, a
+    with pytest.raises(ValueError):
+        ref.fp8_e4m3_round(np.array([470.0]))
+
+
+def test_fp8_quantize_rows_properties():
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((6, 5, 128)) * np.exp(rng.uniform(-3, 3, (6, 5, 1)))).astype(np.float32)
+    x[2, 3] = 0.0                                       # an all-zero row
+    codes, scale = ref.quantize_fp8_rows(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32 and scale.shape == (6, 5)
+    amax = np.abs(x).max(-1)
+    np.testing.assert_array_equal(scale, (amax / np.float32(448.0)).astype(np.float32))
+    assert scale[2, 3] == 0 and not codes[2, 3].any()
+    dec = ref.fp8_e4m3_decode(codes)
+    # the row's largest magnitude lands on (or next to) the format's largest value
+    top = np.abs(dec).max(-1)
+    assert np.all((top[scale > 0] >= 416.0) & (top[scale > 0] <= 448.0))
+    # each code is the nearest e4m3 value to x / scale: half a step of relative error at most
+    y = x / np.where(scale > 0, scale, 1)[..., None]
+    err = np.abs(dec - y)
+    step = np.where(np.abs(y) >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -6))) - 3), 2.0 ** -9)
+    assert np.all(err <= step / 2 + 1e-9)
+    # torch's conversion of the same float32 quotients gives the same codes
+    yq = (x / np.where(scale > 0, scale, np.float32(1))[..., None]).astype(np.float32)
+    yq[2, 3] = 0
+    np.testing.assert_array_equal(codes, _torch_e4m3(yq).view(torch.uint8).numpy())
+
+
+def test_fp8_indexer_brute_force_and_exact_values():
+    rng = np.random.default_rng(13)
+    B, S, Hi, Di = 2, 9, 3, 8
+    q = rng.standard_normal((B, S, Hi, Di)).astype(np.float32)
+    k = rng.standard_normal((B, S, Di)).astype(np.float32)
+    w = rng.standard_normal((B, S, Hi))
+    seg = np.array([[1] * 4 + [2] * 5, [3] * 9], dtype=np.int32)
+    q8, qs = ref.quantize_fp8_rows(q)
+    k8, ks = ref.quantize_fp8_rows(k)
+    got = ref.index_scores_fp8(q8, qs, k8, ks, w, seg, np.arange(S))
+    qd, kd = ref.fp8_e4m3_decode(q8), ref.fp8_e4m3_decode(k8)
+    for b in range(B):
+        for t in range(S):
+            for s in range(S):
+                if s > t or seg[b, s] != seg[b, t]:
+                    assert got[b, t, s] == -np.inf
+                    continue
+                terms = []
+                for j in range(Hi):
+                    dot = math.fsum(float(qd[b, t, j, d]) * float(qs[b, t, j]) * float(kd[b, s, d]) * float(ks[b, s])
+                                    for d in range(Di))
+                    terms.append(w[b, t, j] * max(dot, 0.0))
+                assert abs(got[b, t, s] - math.fsum(terms)) <= 1e-12 * (1 + abs(got[b, t, s]))
+    # values on the e4m3 grid with unit scales: the pinned float64 indexer on the same numbers
+    qe = rng.integers(-16, 17, (B, S, Hi, Di)).astype(np.float64) / 4
+    ke = rng.integers(-16, 17, (B, S, Di)).astype(np.float64) / 8
+    got = ref.index_scores_fp8(ref.fp8_e4m3_encode(qe), np.ones((B, S, Hi), np.float32),
+                               ref.fp8_e4m3_encode(ke), np.ones((B, S), np.float32), w, None, np.arange(S))
+    np.testing.assert_array_equal(got, ref.index_scores(qe, ke, w, None, np.arange(S)))
+    # a positive key scale scales the key's scores (a power of two: exact in float32)
+    ks2 = ks.copy()
+    ks2[:, 4] *= np.float32(4.0)
+    g1 = ref.index_scores_fp8(q8, qs, k8, ks, w, None, np.arange(S))
+    g3 = ref.index_scores_fp8(q8, qs, k8, ks2, w, None, np.arange(S))
+    np.testing.assert_allclose(g3[:, 4:, 4], 4.0 * g1[:, 4:, 4], rtol=1e-12)
+    bound = ref.index_scores_fp8_bound(q8, qs, k8, ks, w, np.arange(S), rel=2.0 ** -12)
+    assert bound.shape == (B, S, S) and np.all(bound > 0)
+    assert not ref.index_scores_fp8_bound(q8, qs, k8, ks, 0 * w, np.arange(S), rel=2.0 ** -12).any()
+
+
+def test_fp8_planted_mistakes_fail_a_pin(monkeypatch):
+    # the other common e4m3 flavour (exponent bias 8, as in the FNUZ variant) breaks the torch pin
+    def decode_bias8(code):
+        c = np.asarray(code, dtype=np.int64)
+        e, m = (c >> 3) & 15, c & 7
+        mag = np.where(e == 0, m / 8.0 * 2.0 ** -7, (1.0 + m / 8.0) * np.exp2(e - 8.0))
+        return np.where(c >> 7, -mag, mag)
+
+    monkeypatch.setattr(ref, "fp8_e4m3_decode", decode_bias8)
+    with pytest.raises(AssertionError):
+        test_fp8_round_encode_decode_match_torch()
+    monkeypatch.undo()
+
+    # rounding half away from zero instead of to even breaks the hand cases
+    def round_away(x):
+        x = np.asarray(x, dtype=np.float64)
+        a = np.abs(x)
+        m, e = np.frexp(a)
+        out = np.where(a < 2.0 ** -6, np.floor(a * 512.0 + 0.5) / 512.0, np.ldexp(np.floor(m * 16.0 + 0.5), e - 4))
+        return np.copysign(out, x)
+
+    monkeypatch.setattr(ref, "fp8_e4m3_round", round_away)
+    with pytest.raises(AssertionError):
+        test_fp8_round_encode_decode_match_torch()
+    monkeypatch.undo()
+
+    # a dropped key scale breaks the brute-force pin
+    orig = ref.index_scores_fp8
+
+    def no_kscale(q8, qs, k8, ks, w, seg, rows):
+        return orig(q8, qs, k8, np.ones_like(ks), w, seg, rows)
+
+    monkeypatch.setattr(ref, "index_scores_fp8", no_kscale)
+    with pytest.raises(AssertionError):
+        test_fp8_indexer_brute_force_and_exact_values()
+    monkeypatch.undo()
