@@ -117,6 +117,40 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
                             dsa_dtype score_dtype, int64_t ld, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dsa_quant_fp8_rows -- quantize rows to OCP FP8 E4M3 with one scale per row.
+ * Source: "DeepSeek3.2: Onboard sparse attention", What this PR does, item 4
+ * (the original indexer's inputs are quantized to fp8). The page names no
+ * format; the one used here: scale = amax(|row|) / 448 in float32, code =
+ * round-to-nearest-even(x / scale) (float32 division), scale 0 and zero codes
+ * for an all-zero row.
+ *   x       [nrows, D] x_dtype (DSA_BF16 or DSA_FP32), rows contiguous
+ *   codes   [nrows, D] uint8     out: E4M3 codes (s eeee mmm, bias 7)
+ *   scale   [nrows]    float32   out
+ * D in {64, 128, 256, 512}. For the fp8 indexer below, q_idx [B,S,Hi,Di] is
+ * B*S*Hi rows of Di and k_idx [B,S,Di] is B*S rows of Di.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_quant_fp8_rows(const void* x, dsa_dtype x_dtype, int64_t nrows, int D,
+                              uint8_t* codes, float* scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * dsa_index_scores_fp8 -- indexer scores from fp8 index queries and keys.
+ * Source: as dsa_index_scores, with the fp8 inputs of item 4 of the same page.
+ *   q8      [B,S,Hi,Di] uint8 E4M3   q_scale [B,S,Hi] float32  (q = q8 * q_scale)
+ *   k8      [B,S,Di]    uint8 E4M3   k_scale [B,S]    float32  (k = k8 * k_scale)
+ *   w       [B,S,Hi]    bf16
+ *   seg, row0, nrows, scores, score_dtype, ld: as dsa_index_scores.
+ * I[b,t,s] = sum_j w[t,j] max(0, q[t,j,:] . k[s,:]) on the dequantized values.
+ * Scales must be finite and >= 0. Hi in {32, 64}, Di in {64, 128}. The code
+ * products are summed by fp8 MFMAs, whose internal accumulation is coarser
+ * than float32: each head's dot product carries an absolute error of a few
+ * 2^-14 of the largest code product in it (scaled by q_scale * k_scale).
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                                const float* k_scale, const void* w, const int32_t* seg, int B,
+                                int S, int Hi, int Di, int row0, int nrows, void* scores,
+                                dsa_dtype score_dtype, int64_t ld, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dsa_topk -- top-k selection of the rows t in [row0, row0 + nrows).
  * Source: "DeepSeek3.2: Onboard sparse attention", Background and item 1
  * (select the top-k keys of each query; get the top-k indices and the index

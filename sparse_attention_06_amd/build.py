@@ -30,7 +30,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # The indexer also keeps its MFMA accumulators in architectural VGPRs (its
 # register budget allows it), so its epilogue needs no v_accvgpr_read moves;
 # the attention kernels already get that form from the compiler.
-EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"indexer.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "indexer_fp8.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

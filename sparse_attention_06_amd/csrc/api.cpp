@@ -117,6 +117,47 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
                     "dsa_index_scores");
 }
 
+dsa_status dsa_quant_fp8_rows(const void* x, dsa_dtype x_dtype, int64_t nrows, int D, uint8_t* codes,
+                              float* scale, void* stream) {
+  REQ_PTR(x);
+  REQ_PTR(codes);
+  REQ_PTR(scale);
+  REQ(dtype_ok(x_dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  REQ(nrows >= 1, DSA_ERR_INVALID_ARG, "nrows=%lld must be >= 1", (long long)nrows);
+  REQ(D == 64 || D == 128 || D == 256 || D == 512, DSA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256, 512}", D);
+  // one wave per row, 256-thread blocks: the grid's thread count must stay below 2^32
+  REQ(nrows <= ((int64_t)1 << 26), DSA_ERR_UNSUPPORTED, "nrows=%lld exceeds 2^26", (long long)nrows);
+  return hip_status(dsa::launch_quant_fp8_rows(x, x_dtype == DSA_BF16, nrows, D, codes, scale,
+                                               (hipStream_t)stream),
+                    "dsa_quant_fp8_rows");
+}
+
+dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
+                                const float* k_scale, const void* w, const int32_t* seg, int B, int S,
+                                int Hi, int Di, int row0, int nrows, void* scores, dsa_dtype score_dtype,
+                                int64_t ld, void* stream) {
+  REQ_PTR(q8);
+  REQ_PTR(q_scale);
+  REQ_PTR(k8);
+  REQ_PTR(k_scale);
+  REQ_PTR(w);
+  REQ_PTR(scores);
+  REQ(aligned16(q8) && aligned16(k8), DSA_ERR_INVALID_ARG, "q8 and k8 must be 16-byte aligned");
+  REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
+  REQ(B >= 1 && S >= 1 && Hi >= 1 && Di >= 1, DSA_ERR_INVALID_ARG,
+      "sizes must be >= 1 (B=%d S=%d Hi=%d Di=%d)", B, S, Hi, Di);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
+  REQ((Hi == 32 || Hi == 64) && (Di == 64 || Di == 128), DSA_ERR_UNSUPPORTED,
+      "fp8 indexer needs Hi in {32, 64} and Di in {64, 128} (Hi=%d Di=%d)", Hi, Di);
+  REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
+      "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
+  REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld < S=%d", (long long)ld, S);
+  REQ(dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown score dtype");
+  return hip_status(dsa::launch_index_scores_fp8(q8, q_scale, k8, k_scale, w, seg, B, S, Hi, Di, row0, nrows,
+                                                 scores, score_dtype == DSA_BF16, ld, (hipStream_t)stream),
+                    "dsa_index_scores_fp8");
+}
+
 dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* seg,
                     int B, int S, int K, int row0, int nrows, int32_t* idx, void* mask,
                     void* stream) {

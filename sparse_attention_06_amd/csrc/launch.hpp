@@ -24,6 +24,11 @@ hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const
                                      bool in_bf16, int row0, int nrows, void* scores,
                                      bool out_bf16, int64_t ld, hipStream_t st);
 
+hipError_t launch_index_scores_fp8(const void* q8, const float* qs, const void* k8, const float* ks,
+                                   const void* w, const int32_t* seg, int B, int S, int Hi, int Di, int row0,
+                                   int nrows, void* scores, bool out_bf16, int64_t ld, hipStream_t st);
+hipError_t launch_quant_fp8_rows(const void* x, bool in_bf16, int64_t nrows, int D, uint8_t* codes,
+                                 float* scale, hipStream_t st);
 hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
                        int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
                        hipStream_t st);

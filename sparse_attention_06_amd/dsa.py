@@ -21,7 +21,7 @@ TILE_Q, TILE_K = 128, 64
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
           4: "DSA_ERR_HIP"}
 
-EXPORTS = ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
+EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
@@ -45,6 +45,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         L.dsa_index_scores.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32, i64, vp]
+        L.dsa_index_scores_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i64, vp]
+        L.dsa_quant_fp8_rows.argtypes = [vp, i32, i64, i32, vp, vp, vp]
         L.dsa_topk.argtypes = [vp, i32, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.dsa_build_mask.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.dsa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
@@ -55,7 +57,7 @@ def lib() -> ctypes.CDLL:
                                                vp, vp, vp, sz, vp]
         L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, sz, vp]
-        for f in ("dsa_index_scores", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
+        for f in ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
                   "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq",
                   "dsa_sparse_attn_bwd_dkdv"):
             getattr(L, f).restype = ctypes.c_int
@@ -125,6 +127,23 @@ def dsa_index_scores(q_idx, k_idx, w, seg, row0: int, nrows: int, scores, stream
     ld = scores.shape[-1]
     _check("dsa_index_scores", lib().dsa_index_scores(
         _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(seg), B, S, Hi, Di, _dt(q_idx), row0, nrows,
+        _ptr(scores), _dt(scores), ld, _stream(stream)))
+
+
+def dsa_quant_fp8_rows(x, codes, scale, stream=None) -> None:
+    """Quantize the last axis of x (bf16 or fp32) to E4M3 codes (uint8, same
+    shape) with one float32 scale per row (x.shape[:-1])."""
+    D = x.shape[-1]
+    nrows = x.numel() // D
+    _check("dsa_quant_fp8_rows", lib().dsa_quant_fp8_rows(
+        _ptr(x), _dt(x), nrows, D, _ptr(codes), _ptr(scale), _stream(stream)))
+
+
+def dsa_index_scores_fp8(q8, q_scale, k8, k_scale, w, seg, row0: int, nrows: int, scores, stream=None) -> None:
+    B, S, Hi, Di = q8.shape
+    ld = scores.shape[-1]
+    _check("dsa_index_scores_fp8", lib().dsa_index_scores_fp8(
+        _ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(w), _ptr(seg), B, S, Hi, Di, row0, nrows,
         _ptr(scores), _dt(scores), ld, _stream(stream)))
 
 

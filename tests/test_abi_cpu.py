@@ -68,6 +68,33 @@ def test_index_scores_rejects(kw, code):
     assert dsa.lib().dsa_last_error()
 
 
+def _fp8_call(**kw):
+    a = dict(q8=P, qs=P, k8=P, ks=P, w=P, seg=NUL, B=1, S=128, Hi=64, Di=128, row0=0, nrows=128,
+             scores=P, sdt=1, ld=128, st=S_)
+    a.update(kw)
+    return dsa.lib().dsa_index_scores_fp8(a["q8"], a["qs"], a["k8"], a["ks"], a["w"], a["seg"], a["B"], a["S"],
+                                          a["Hi"], a["Di"], a["row0"], a["nrows"], a["scores"], a["sdt"],
+                                          a["ld"], a["st"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q8=NUL), 1), (dict(ks=NUL), 1), (dict(k8=MIS), 1), (dict(B=0), 1), (dict(row0=100, nrows=100), 1),
+    (dict(ld=100), 1), (dict(sdt=5), 1), (dict(Di=96), 2), (dict(Hi=48), 2), (dict(Hi=128), 2),
+])
+def test_index_scores_fp8_rejects(kw, code):
+    assert _fp8_call(**kw) == code
+    assert dsa.lib().dsa_last_error()
+
+
+def test_quant_fp8_rejects():
+    L = dsa.lib()
+    assert L.dsa_quant_fp8_rows(NUL, 0, 4, 128, P, P, S_) == 1
+    assert L.dsa_quant_fp8_rows(P, 0, 0, 128, P, P, S_) == 1
+    assert L.dsa_quant_fp8_rows(P, 3, 4, 128, P, P, S_) == 1
+    assert L.dsa_quant_fp8_rows(P, 0, 4, 96, P, P, S_) == 2
+    assert L.dsa_quant_fp8_rows(P, 0, (1 << 26) + 1, 128, P, P, S_) == 2
+
+
 def test_topk_rejects():
     L = dsa.lib()
     # row slab not on a 128-row tile
