@@ -123,3 +123,32 @@ def test_indexer_fp8_full_length_sampled_rows():
     bound = ref.index_scores_fp8_bound(q8h, qsh, k8.numpy(), ks.numpy(), w64, rows, REL)
     worst = _check(np.concatenate(got, axis=1), want, bound)
     print(f"fp8 indexer S={S}: max err / bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("segments", [None, (40, 150)])
+def test_fp8_selection_end_to_end(segments):
+    """fp8 indexer, then the top-k on its scores, against the oracle's top-k on
+    the oracle's fp8 scores: exact index lists on decidable rows, the near-tie
+    rule on the rest, and the selection mask equal to the index lists."""
+    from gpu_util import compare_topk_rows
+    cfg = inputs.CONFIGS["c2"].replace(B=2, S=333, K=64, segments=segments)
+    x, q8, qs, k8, ks = _fp8_inputs(cfg)
+    S, K = cfg.S, cfg.K
+    seg_np = None if x["seg"] is None else x["seg"].numpy()
+    seg_d = None if x["seg"] is None else x["seg"].to(DEV).contiguous()
+    sc = torch.empty((cfg.B, S, S), dtype=torch.float32, device=DEV)
+    idx = torch.empty((cfg.B, S, K), dtype=torch.int32, device=DEV)
+    mask = torch.empty(dsa.dsa_mask_bytes(cfg.B, S), dtype=torch.uint8, device=DEV)
+    dsa.dsa_index_scores_fp8(q8.to(DEV), qs.to(DEV), k8.to(DEV), ks.to(DEV), x["w"].to(DEV), seg_d, 0, S, sc)
+    dsa.dsa_topk(sc, seg_d, cfg.B, S, K, 0, S, idx, mask)
+    torch.cuda.synchronize()
+    rows = np.arange(S)
+    rs = ref.index_scores_fp8(q8.numpy(), qs.numpy(), k8.numpy(), ks.numpy(), f64(x["w"]), seg_np, rows)
+    ri = ref.topk(rs, seg_np, rows, K, S)
+    gi = idx.cpu().numpy()
+    dec = compare_topk_rows(rs, f64(sc), gi, ri, seg_np, rows, S, K)
+    assert len(dec) >= 0.9 * cfg.B * S, len(dec)
+    bits, _ = dsa.mask_views(mask, cfg.B, S)
+    want_bits = ref.pack_bits(ref.selection_matrix(gi, S))
+    np.testing.assert_array_equal(bits.cpu().numpy().view(np.uint64), want_bits)
+    print(f"fp8 selection seg={segments}: {len(dec)} of {cfg.B * S} rows decidable and exact")
