@@ -29,6 +29,8 @@ Sources (page title · section):
   [P3r] "DeepSeek3.2: Onboard sparse attention" · "What this PR does",
         item 4. The original indexer runs on quantized fp8 inputs (the fp8
         indexer section at the end states the readings of that format).
+  [P3o] same page · item 1, Indexer: partial RoPE on the indexer's q and k,
+        concatenated layout (the RoPE section at the end states the readings).
 
 The indexer formula is not printed on the pages. It is the standard one of
 the method: I[t,s] = sum_j w[t,j] * ReLU(q_idx[t,j,:] . k_idx[s,:]), with a
@@ -511,3 +513,42 @@ def index_scores_fp8_bound(q8, q_scale, k8, k_scale, w, rows, rel: float) -> np.
             dot_abs = qv[b, t] @ kv[b].T                  # [Hi, S]
             out[b, r] = rel * Di * (wq * mq).sum() * kmax + 1e-6 * (wq @ dot_abs) * ks[b]
     return out
+
+
+# ----------------------------------------------------------------------------
+# next row: indexer RoPE (partial, concatenated layout)                 [P3o]
+# ----------------------------------------------------------------------------
+# [P3o] "DeepSeek3.2: Onboard sparse attention" · "What this PR does", item 1,
+# Indexer: the indexer applies partial RoPE to its q and k, with the same
+# YaRN frequencies as MLA, in the concatenated layout rather than the
+# interleaved one. Readings taken here:
+#   * "partial": the first rope_dim dims of every index head vector (q_idx per
+#     head, k_idx) are rotated, the rest pass through;
+#   * "concatenated": dim i pairs with dim i + rope_dim/2 (not 2i with 2i+1);
+#   * the frequencies arrive as tables cos[p, i], sin[p, i] (p a position,
+#     i < rope_dim/2), so the YaRN construction stays with the caller; the
+#     position of token t is pos[b, t] (t itself when no positions are given);
+#   * the rotated vectors are bf16, like the inputs. Each output element is
+#     float32(float32(x_a c) - float32(x_b s)) or float32(float32(x_b c) +
+#     float32(x_a s)) rounded to bf16 (nearest, ties to even): the products
+#     and the sum are each rounded to float32, with no fused multiply-add.
+def rope_rotate(x, cos_t, sin_t, pos, rope_dim: int) -> np.ndarray:
+    """Partial concatenated-layout RoPE of x [B, S, ..., D] (bf16 values as
+    float, or float32). cos_t, sin_t [P, rope_dim/2] float32; pos [B, S] int
+    or None. Returns float64 values on the bf16 grid, same shape as x."""
+    x32 = np.asarray(x, dtype=np.float32)
+    B, S = x32.shape[:2]
+    h = rope_dim // 2
+    p = np.broadcast_to(np.arange(S), (B, S)) if pos is None else np.asarray(pos)
+    c = np.asarray(cos_t, np.float32)[p]                  # [B, S, h]
+    s = np.asarray(sin_t, np.float32)[p]
+    extra = x32.ndim - 3                                  # head axes between S and D
+    c = c.reshape(c.shape[:2] + (1,) * extra + (h,))
+    s = s.reshape(s.shape[:2] + (1,) * extra + (h,))
+    a, b = x32[..., :h], x32[..., h:rope_dim]
+    ya = (a * c).astype(np.float32) - (b * s).astype(np.float32)
+    yb = (b * c).astype(np.float32) + (a * s).astype(np.float32)
+    out = x32.astype(np.float64).copy()
+    out[..., :h] = ya.astype(np.float32)
+    out[..., h:rope_dim] = yb.astype(np.float32)
+    return bf16_round(out)

@@ -642,3 +642,94 @@ def test_fp8_planted_mistakes_fail_a_pin(monkeypatch):
     with pytest.raises(AssertionError):
         test_fp8_indexer_brute_force_and_exact_values()
     monkeypatch.undo()
+
+
+# ------------------------------------------------------------------ RoPE pins
+def _rope_tables(P, h, base=10000.0):
+    inv = base ** (-np.arange(h) / h)
+    ang = np.arange(P)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32), ang
+
+
+def _bf16(x):
+    return ref.bf16_round(np.asarray(x, np.float64)).astype(np.float32)
+
+
+def test_rope_identity_and_passthrough():
+    rng = np.random.default_rng(21)
+    x = _bf16(rng.standard_normal((2, 6, 3, 32)))
+    h = 8
+    out = ref.rope_rotate(x, np.ones((6, h), np.float32), np.zeros((6, h), np.float32), None, 2 * h)
+    np.testing.assert_array_equal(out, x)                 # angle 0: identity, bit for bit
+    c, s, _ = _rope_tables(6, h)
+    out = ref.rope_rotate(x, c, s, None, 2 * h)
+    np.testing.assert_array_equal(out[..., 2 * h:], x[..., 2 * h:])   # dims past rope_dim untouched
+    np.testing.assert_array_equal(out[:, 0], x[:, 0])     # position 0 has angle 0
+
+
+def test_rope_is_complex_rotation():
+    # textbook form: (x_i + i x_{i+h}) * exp(i theta_i(p)); the oracle's float32
+    # steps and bf16 output may differ from it by one bf16 step at most
+    rng = np.random.default_rng(22)
+    B, S, H, D, rd = 2, 50, 4, 128, 64
+    h = rd // 2
+    x = _bf16(rng.standard_normal((B, S, H, D)))
+    c, s, ang = _rope_tables(S, h)
+    got = ref.rope_rotate(x, c, s, None, rd)
+    z = (x[..., :h].astype(np.float64) + 1j * x[..., h:rd]) * np.exp(1j * ang)[None, :, None, :]
+    want = np.concatenate([z.real, z.imag], axis=-1)
+    diff = np.abs(got[..., :rd] - want)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 1e-30))) - 7)
+    assert np.all(diff <= ulp * 1.01 + 1e-12)
+    assert np.mean(diff > ulp * 0.51) < 0.01             # almost everywhere the nearest bf16 value
+    # rotation keeps the norm of every pair (up to bf16 rounding)
+    n0 = np.hypot(x[..., :h], x[..., h:rd])
+    n1 = np.hypot(got[..., :h], got[..., h:rd])
+    assert np.allclose(n0, n1, rtol=2 ** -7, atol=1e-6)
+
+
+def test_rope_relative_position_and_positions_argument():
+    rng = np.random.default_rng(23)
+    D, rd, S = 64, 64, 40
+    h = rd // 2
+    q = _bf16(rng.standard_normal((1, S, D)))
+    k = _bf16(rng.standard_normal((1, S, D)))
+    c, s, _ = _rope_tables(S, h)
+    # all tokens share q's and k's vectors: <R(a)q, R(b)k> depends on a - b only
+    qq = np.broadcast_to(q[:, :1], q.shape).copy()
+    kk = np.broadcast_to(k[:, :1], k.shape).copy()
+    rq = ref.rope_rotate(qq, c, s, None, rd)[0]
+    rk = ref.rope_rotate(kk, c, s, None, rd)[0]
+    d = {}
+    for a in range(S):
+        for b in range(a + 1):
+            d.setdefault(a - b, []).append(float(rq[a] @ rk[b]))
+    for v in d.values():
+        assert max(v) - min(v) <= 0.05 * (1 + abs(np.mean(v)))
+    # explicit positions select table rows
+    pos = rng.integers(0, S, (1, S)).astype(np.int32)
+    a = ref.rope_rotate(q, c, s, pos, rd)
+    b = ref.rope_rotate(q, c[pos[0]], s[pos[0]], None, rd)   # row t reads table row pos[t] ... as position t
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rope_planted_mistakes_fail_a_pin(monkeypatch):
+    orig = ref.rope_rotate
+
+    def interleaved(x, cos_t, sin_t, pos, rope_dim):
+        x = np.asarray(x, np.float32)
+        perm = np.arange(x.shape[-1])
+        h = rope_dim // 2
+        perm[:rope_dim] = np.concatenate([np.arange(0, rope_dim, 2), np.arange(1, rope_dim, 2)])
+        y = orig(x[..., perm], cos_t, sin_t, pos, rope_dim)
+        inv = np.argsort(perm)
+        return y[..., inv]
+
+    def wrong_sign(x, cos_t, sin_t, pos, rope_dim):
+        return orig(x, cos_t, -np.asarray(sin_t), pos, rope_dim)
+
+    for bad in (interleaved, wrong_sign):
+        monkeypatch.setattr(ref, "rope_rotate", bad)
+        with pytest.raises(AssertionError):
+            test_rope_is_complex_rotation()
+        monkeypatch.undo()
