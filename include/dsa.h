@@ -151,6 +151,27 @@ dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const u
                                 dsa_dtype score_dtype, int64_t ld, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * dsa_indexer_rope -- partial RoPE of indexer inputs, concatenated layout.
+ * Source: "DeepSeek3.2: Onboard sparse attention", What this PR does, item 1,
+ * Indexer (partial RoPE on the indexer's q and k with the YaRN frequencies of
+ * MLA, concatenated rather than interleaved layout).
+ *   x       [B,S,nh,D] bf16   vectors to rotate (q_idx: nh = Hi; k_idx: nh = 1)
+ *   cos_t, sin_t [P, rope_dim/2] float32   the frequency tables, row p for
+ *           position p (the caller builds them, YaRN included)
+ *   pos     [B,S] int32 or NULL   position of each token (NULL: token index t,
+ *           which needs P >= S); positions outside [0, P) are clamped
+ *   out     [B,S,nh,D] bf16   out; may be x itself (in place)
+ * The first rope_dim dims rotate with dim i paired with i + rope_dim/2:
+ *   y_i = x_i c_i - x_{i+h} s_i,  y_{i+h} = x_{i+h} c_i + x_i s_i  (h = rope_dim/2),
+ * each product and sum rounded to float32 (no fused multiply-add), the result
+ * rounded to bf16 (nearest, ties to even); the other dims are copied.
+ * D % 8 == 0; rope_dim % 16 == 0 and 16 <= rope_dim <= D.
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_indexer_rope(const void* x, int B, int S, int nh, int D, int rope_dim,
+                            const float* cos_t, const float* sin_t, int P, const int32_t* pos,
+                            void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dsa_topk -- top-k selection of the rows t in [row0, row0 + nrows).
  * Source: "DeepSeek3.2: Onboard sparse attention", Background and item 1
  * (select the top-k keys of each query; get the top-k indices and the index

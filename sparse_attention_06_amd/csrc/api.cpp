@@ -158,6 +158,26 @@ dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const u
                     "dsa_index_scores_fp8");
 }
 
+dsa_status dsa_indexer_rope(const void* x, int B, int S, int nh, int D, int rope_dim, const float* cos_t,
+                            const float* sin_t, int P, const int32_t* pos, void* out, void* stream) {
+  REQ_PTR(x);
+  REQ_PTR(cos_t);
+  REQ_PTR(sin_t);
+  REQ_PTR(out);
+  REQ(aligned16(x) && aligned16(out) && aligned16(cos_t) && aligned16(sin_t), DSA_ERR_INVALID_ARG,
+      "x, out and the tables must be 16-byte aligned");
+  REQ(pos == nullptr || aligned16(pos), DSA_ERR_INVALID_ARG, "pos must be 16-byte aligned");
+  REQ(B >= 1 && S >= 1 && nh >= 1 && D >= 1 && P >= 1, DSA_ERR_INVALID_ARG,
+      "sizes must be >= 1 (B=%d S=%d nh=%d D=%d P=%d)", B, S, nh, D, P);
+  REQ(D % 8 == 0 && rope_dim % 16 == 0 && rope_dim >= 16 && rope_dim <= D, DSA_ERR_UNSUPPORTED,
+      "need D %% 8 == 0 and rope_dim %% 16 == 0 in [16, D] (D=%d rope_dim=%d)", D, rope_dim);
+  REQ(pos != nullptr || P >= S, DSA_ERR_INVALID_ARG, "without positions the tables need P >= S (P=%d S=%d)", P, S);
+  REQ((int64_t)B * S * nh * (D / 8) < ((int64_t)1 << 32) - 256, DSA_ERR_UNSUPPORTED, "too many vectors");
+  return hip_status(dsa::launch_rope_rows(x, B, S, nh, D, rope_dim, P, cos_t, sin_t, pos, out,
+                                          (hipStream_t)stream),
+                    "dsa_indexer_rope");
+}
+
 dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* seg,
                     int B, int S, int K, int row0, int nrows, int32_t* idx, void* mask,
                     void* stream) {

@@ -29,6 +29,8 @@ hipError_t launch_index_scores_fp8(const void* q8, const float* qs, const void* 
                                    int nrows, void* scores, bool out_bf16, int64_t ld, hipStream_t st);
 hipError_t launch_quant_fp8_rows(const void* x, bool in_bf16, int64_t nrows, int D, uint8_t* codes,
                                  float* scale, hipStream_t st);
+hipError_t launch_rope_rows(const void* x, int B, int S, int nh, int D, int rope_dim, int P, const float* cos_t,
+                            const float* sin_t, const int32_t* pos, void* out, hipStream_t st);
 hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
                        int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
                        hipStream_t st);

@@ -21,7 +21,7 @@ TILE_Q, TILE_K = 128, 64
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "DSA_ERR_WORKSPACE",
           4: "DSA_ERR_HIP"}
 
-EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
+EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
@@ -47,6 +47,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_index_scores.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, i32, i64, vp]
         L.dsa_index_scores_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, i64, vp]
         L.dsa_quant_fp8_rows.argtypes = [vp, i32, i64, i32, vp, vp, vp]
+        L.dsa_indexer_rope.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp]
         L.dsa_topk.argtypes = [vp, i32, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.dsa_build_mask.argtypes = [vp, vp, i32, i32, i32, vp, vp]
         L.dsa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
@@ -57,7 +58,7 @@ def lib() -> ctypes.CDLL:
                                                vp, vp, vp, sz, vp]
         L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, sz, vp]
-        for f in ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
+        for f in ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
                   "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq",
                   "dsa_sparse_attn_bwd_dkdv"):
             getattr(L, f).restype = ctypes.c_int
@@ -137,6 +138,18 @@ def dsa_quant_fp8_rows(x, codes, scale, stream=None) -> None:
     nrows = x.numel() // D
     _check("dsa_quant_fp8_rows", lib().dsa_quant_fp8_rows(
         _ptr(x), _dt(x), nrows, D, _ptr(codes), _ptr(scale), _stream(stream)))
+
+
+def dsa_indexer_rope(x, rope_dim: int, cos_t, sin_t, pos=None, out=None, stream=None) -> None:
+    """Partial concatenated-layout RoPE of x [B,S,nh,D] or [B,S,D] (bf16) into
+    out (default: in place). cos_t, sin_t [P, rope_dim/2] float32."""
+    B, S = x.shape[:2]
+    nh = x.shape[2] if x.dim() == 4 else 1
+    D = x.shape[-1]
+    out = x if out is None else out
+    _check("dsa_indexer_rope", lib().dsa_indexer_rope(
+        _ptr(x), B, S, nh, D, rope_dim, _ptr(cos_t), _ptr(sin_t), cos_t.shape[0], _ptr(pos), _ptr(out),
+        _stream(stream)))
 
 
 def dsa_index_scores_fp8(q8, q_scale, k8, k_scale, w, seg, row0: int, nrows: int, scores, stream=None) -> None:

@@ -95,6 +95,18 @@ def test_quant_fp8_rejects():
     assert L.dsa_quant_fp8_rows(P, 0, (1 << 26) + 1, 128, P, P, S_) == 2
 
 
+def test_indexer_rope_rejects():
+    L = dsa.lib()
+    ok = (P, 2, 64, 4, 128, 64, P, P, 64, NUL, P, S_)
+    assert L.dsa_indexer_rope(NUL, *ok[1:]) == 1
+    assert L.dsa_indexer_rope(MIS, *ok[1:]) == 1
+    assert L.dsa_indexer_rope(*ok[:8], 32, NUL, P, S_) == 1          # P < S without positions
+    assert L.dsa_indexer_rope(*ok[:5], 40, *ok[6:]) == 2             # rope_dim % 16
+    assert L.dsa_indexer_rope(*ok[:5], 144, *ok[6:]) == 2            # rope_dim > D
+    assert L.dsa_indexer_rope(*ok[:4], 100, 64, *ok[6:]) == 2        # D % 8
+    assert dsa.lib().dsa_last_error()
+
+
 def test_topk_rejects():
     L = dsa.lib()
     # row slab not on a 128-row tile
