@@ -180,9 +180,26 @@ def selection_long(key, reps=2):
         torch.cuda.synchronize()
         if i:
             t_fp8.append(ev[0].elapsed_time(ev[1]))
+    # partial RoPE (rope_dim 64) of q_idx and k_idx in place, after the timings above
+    h = 32
+    ang = torch.arange(cfg.S, device="cuda", dtype=torch.float64)[:, None] * \
+        (10000.0 ** (-torch.arange(h, device="cuda", dtype=torch.float64) / h))[None, :]
+    ct, st = torch.cos(ang).float().contiguous(), torch.sin(ang).float().contiguous()
+    t_rope = []
+    for i in range(reps + 1):
+        ev[0].record(stream)
+        dsa.dsa_indexer_rope(x["q_idx"], 64, ct, st)
+        dsa.dsa_indexer_rope(x["k_idx"], 64, ct, st)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i:
+            t_rope.append(ev[0].elapsed_time(ev[1]))
+    # in place only the rotated dims move: bf16 read + write of 64 of every Di
+    rope_bytes = 2 * (x["q_idx"].numel() + x["k_idx"].numel()) * 2 * 64 // cfg.Di
     wk = work(cfg, None if x["seg"] is None else x["seg"].cpu().numpy())
     mi, mt = float(np.mean(t_idx)), float(np.mean(t_top))
     m8 = float(np.mean(t_fp8))
+    mr = float(np.mean(t_rope))
     del scores, idx, mask, x, q8, qs, k8, ks
     torch.cuda.empty_cache()
     ach_i = wk["indexer"] / (mi * 1e-3) / 1e12
@@ -196,7 +213,11 @@ def selection_long(key, reps=2):
             # fp8 inputs (not the metric's bf16 workload): the indexer alone and with the same top-k
             "index_scores_fp8_ms": m8, "indexer_fp8_topk_ms": m8 + mt,
             "index_scores_fp8": {"achieved": ach_8, "unit": "TFLOP/s", "frac": ach_8 / PEAK_FP8_TFLOPS,
-                                 "algorithmic": wk["indexer"]}}
+                                 "algorithmic": wk["indexer"]},
+            # input preparation before the indexer (not part of the metric): RoPE of q_idx and k_idx
+            "rope_ms": mr, "rope": {"achieved": rope_bytes / (mr * 1e-3) / 1e9, "unit": "GB/s",
+                                    "frac": rope_bytes / (mr * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                    "algorithmic": rope_bytes}}
 
 
 def main():
@@ -241,7 +262,7 @@ def main():
             r = selection_long(key)
             selection[f"S{r['S']}"] = r
             log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms, "
-                f"fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms")
+                f"fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms, rope {r['rope_ms']:.3f} ms")
         print(json.dumps({"metric": "indexer + top-k ms", "selection": selection}), flush=True)
         return
     log(f"config {cfg.name}: generating inputs on the GPU")
@@ -337,7 +358,7 @@ def main():
             r = selection_long(key)
             selection[f"S{r['S']}"] = r
             log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms, "
-                f"fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms")
+                f"fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms, rope {r['rope_ms']:.3f} ms")
 
     cpu = None
     if not args.no_cpu:

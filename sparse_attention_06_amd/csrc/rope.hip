@@ -9,10 +9,10 @@
 // each product and each sum rounded to float32 (no fused multiply-add), the
 // result rounded to bf16. The other dims are copied.
 //
-// One thread per 8-element chunk of a vector: a chunk in the first half of the
-// rotated part computes itself and its partner chunk h dims later; a chunk in
-// the second half has nothing to do; the rest are copies. 16-byte loads and
-// stores; HBM-bound.
+// One thread per work item of a vector: item j < h/8 rotates the 8-element
+// chunk at 8j together with its partner chunk h dims later; when the output is
+// a separate buffer, the remaining items copy the chunks past the rotated part
+// (in place there is nothing to copy). 16-byte loads and stores; HBM-bound.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,19 +24,21 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const uint16_t* x, int64
                                                         const float* __restrict__ st,
                                                         const int32_t* __restrict__ pos,
                                                         uint16_t* out) {
-  const int cpv = D / 8;  // chunks per vector
+  const int nrot = h / 8;                             // rotating items per vector
+  const int ipv = nrot + (x != out ? (D - 2 * h) / 8 : 0);  // items per vector
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= nvec * cpv) return;
-  const int64_t v = gid / cpv;
-  const int c0 = (int)(gid % cpv) * 8;
+  if (gid >= nvec * ipv) return;
+  const int64_t v = gid / ipv;
+  const int j = (int)(gid % ipv);
   const int64_t tok = v / nh;  // b * S + t
   const uint16_t* xv = x + v * D;
   uint16_t* ov = out + v * D;
-  if (c0 >= 2 * h) {  // past the rotated part: copy
-    *(u32x4*)(ov + c0) = *(const u32x4*)(xv + c0);
+  if (j >= nrot) {  // past the rotated part: copy
+    const int c = 2 * h + 8 * (j - nrot);
+    *(u32x4*)(ov + c) = *(const u32x4*)(xv + c);
     return;
   }
-  if (c0 >= h) return;  // second half of the rotated part: done by its partner
+  const int c0 = 8 * j;
   // positions outside the tables are clamped to them (an out-of-range
   // position gives a wrong rotation, never an out-of-bounds read)
   const int p = min(max(pos ? pos[tok] : (int)(tok % S), 0), P - 1);
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256) void rope_rows_kernel(const uint16_t* x, int64
 hipError_t launch_rope_rows(const void* x, int B, int S, int nh, int D, int rope_dim, int P, const float* cos_t,
                             const float* sin_t, const int32_t* pos, void* out, hipStream_t st) {
   const int64_t nvec = (int64_t)B * S * nh;
-  const int64_t nthr = nvec * (D / 8);
+  const int64_t nthr = nvec * (rope_dim / 16 + (x != out ? (D - rope_dim) / 8 : 0));
   const dim3 grid((unsigned)((nthr + 255) / 256)), block(256);
   hipLaunchKernelGGL(rope_rows_kernel, grid, block, 0, st, (const uint16_t*)x, nvec, nh, S, D, rope_dim / 2, P,
                      cos_t, sin_t, pos, (uint16_t*)out);
