@@ -502,7 +502,8 @@ def index_scores_fp8_bound(q8, q_scale, k8, k_scale, w, rows, rel: float) -> np.
     w = np.abs(np.asarray(w, np.float64))
     qs = np.asarray(q_scale, np.float64)
     ks = np.asarray(k_scale, np.float64)
-    B, S, Hi, Di = qv.shape
+    B, _, Hi, Di = qv.shape
+    S = kv.shape[1]
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((B, rows.size, S))
     for b in range(B):
@@ -552,3 +553,27 @@ def rope_rotate(x, cos_t, sin_t, pos, rope_dim: int) -> np.ndarray:
     out[..., :h] = ya.astype(np.float32)
     out[..., h:rope_dim] = yb.astype(np.float32)
     return bf16_round(out)
+
+
+def index_scores_fp8_rows(q8_rows, q_scale_rows, k8, k_scale, w_rows, seg, rows) -> np.ndarray:
+    """index_scores_fp8 for long sequences: the query side is given only for
+    the requested rows (q8_rows [B, R, Hi, Di], q_scale_rows [B, R, Hi],
+    w_rows [B, R, Hi], R = len(rows)); keys for every position."""
+    q = fp8_e4m3_decode(q8_rows) * np.asarray(q_scale_rows, np.float64)[..., None]
+    k = fp8_e4m3_decode(k8) * np.asarray(k_scale, np.float64)[..., None]
+    w_rows = np.asarray(w_rows, np.float64)
+    B, S = k.shape[:2]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((B, rows.size, S), NEG_INF)
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            out[b, r] = index_scores_row(q[b, r], w_rows[b, r], k[b], valid_row(seg_b, S, int(t)))
+    return out
+
+
+def index_scores_fp8_bound_rows(q8_rows, q_scale_rows, k8, k_scale, w_rows, rel: float) -> np.ndarray:
+    """index_scores_fp8_bound with the query side given only for the rows
+    (same layout as index_scores_fp8_rows)."""
+    R = np.asarray(q8_rows).shape[1]
+    return index_scores_fp8_bound(q8_rows, q_scale_rows, k8, k_scale, w_rows, np.arange(R), rel)

@@ -92,35 +92,39 @@ def test_indexer_fp8_parity(segments, score_dtype, HiDi):
     print(f"fp8 indexer Hi={Hi} Di={Di} seg={segments} {score_dtype}: max err / bound {ratio:.3f}")
 
 
-def test_indexer_fp8_full_length_sampled_rows():
-    """S = 32768, 64 x 128 index heads: slabs of rows at the start, middle and
-    end of the sequence against the oracle (only those rows' q_idx are
-    quantized and uploaded; every key is)."""
-    cfg = inputs.CONFIGS["c3"]
+@pytest.mark.parametrize("key", ["c3", "c5"])
+def test_indexer_fp8_full_length_sampled_rows(key):
+    """S = 32768 (fp32 scores) and 131072 (bf16 scores), 64 x 128 index heads:
+    slabs of rows at the start, middle and end of the sequence against the
+    oracle (only those rows' q_idx are quantized and uploaded; every key is)."""
+    cfg = inputs.CONFIGS[key]
+    sdt = torch.bfloat16 if cfg.score_dtype == "bf16" else torch.float32
     x = inputs.make_index_inputs(cfg, device="cpu")
     S, Hi, Di = cfg.S, cfg.Hi, cfg.Di
     k8, ks = _quant_host(x["k_idx"])
     q8_d = torch.zeros((1, S, Hi, Di), dtype=torch.uint8, device=DEV)
     qs_d = torch.zeros((1, S, Hi), dtype=torch.float32, device=DEV)
     k8_d, ks_d, w_d = k8.to(DEV), ks.to(DEV), x["w"].to(DEV)
-    slabs = (0, 13, 16380, S - 4)
+    slabs = (0, 13, S // 2 - 4, S - 4)
     nrows = 4
-    got = []
-    q8h = np.zeros((1, S, Hi, Di), np.uint8)
-    qsh = np.zeros((1, S, Hi), np.float32)
+    got, q8s, qss = [], [], []
     for row0 in slabs:
         q8r, qsr = _quant_host(x["q_idx"][:, row0:row0 + nrows])
-        q8h[:, row0:row0 + nrows], qsh[:, row0:row0 + nrows] = q8r.numpy(), qsr.numpy()
+        q8s.append(q8r.numpy())
+        qss.append(qsr.numpy())
         q8_d[:, row0:row0 + nrows] = q8r.to(DEV)
         qs_d[:, row0:row0 + nrows] = qsr.to(DEV)
-        sc = torch.full((1, nrows, S), float("nan"), device=DEV)
+        sc = torch.full((1, nrows, S), float("nan"), dtype=sdt, device=DEV)
         dsa.dsa_index_scores_fp8(q8_d, qs_d, k8_d, ks_d, w_d, None, row0, nrows, sc)
         torch.cuda.synchronize()
         got.append(f64(sc))
     rows = np.concatenate([np.arange(r, r + nrows) for r in slabs])
-    w64 = f64(x["w"])
-    want = ref.index_scores_fp8(q8h, qsh, k8.numpy(), ks.numpy(), w64, None, rows)
-    bound = ref.index_scores_fp8_bound(q8h, qsh, k8.numpy(), ks.numpy(), w64, rows, REL)
+    q8h, qsh = np.concatenate(q8s, axis=1), np.concatenate(qss, axis=1)
+    w_rows = f64(x["w"])[:, rows]
+    want = ref.index_scores_fp8_rows(q8h, qsh, k8.numpy(), ks.numpy(), w_rows, None, rows)
+    bound = ref.index_scores_fp8_bound_rows(q8h, qsh, k8.numpy(), ks.numpy(), w_rows, REL)
+    if sdt == torch.bfloat16:
+        bound = bound + np.abs(np.where(np.isfinite(want), want, 0)) * 2.0 ** -8
     worst = _check(np.concatenate(got, axis=1), want, bound)
     print(f"fp8 indexer S={S}: max err / bound {worst:.3f}")
 

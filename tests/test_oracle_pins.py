@@ -733,3 +733,19 @@ def test_rope_planted_mistakes_fail_a_pin(monkeypatch):
         with pytest.raises(AssertionError):
             test_rope_is_complex_rotation()
         monkeypatch.undo()
+
+
+def test_fp8_row_restricted_helpers_match_full_functions():
+    rng = np.random.default_rng(14)
+    B, S, Hi, Di = 2, 11, 3, 16
+    q8, qs = ref.quantize_fp8_rows(rng.standard_normal((B, S, Hi, Di)).astype(np.float32))
+    k8, ks = ref.quantize_fp8_rows(rng.standard_normal((B, S, Di)).astype(np.float32))
+    w = rng.standard_normal((B, S, Hi))
+    seg = np.array([[1] * 5 + [2] * 6, [4] * 11], dtype=np.int32)
+    rows = np.array([0, 4, 5, 10])
+    full = ref.index_scores_fp8(q8, qs, k8, ks, w, seg, rows)
+    part = ref.index_scores_fp8_rows(q8[:, rows], qs[:, rows], k8, ks, w[:, rows], seg, rows)
+    np.testing.assert_array_equal(full, part)
+    bf = ref.index_scores_fp8_bound(q8, qs, k8, ks, w, rows, 2.0 ** -17)
+    bp = ref.index_scores_fp8_bound_rows(q8[:, rows], qs[:, rows], k8, ks, w[:, rows], 2.0 ** -17)
+    np.testing.assert_array_equal(bf, bp)
