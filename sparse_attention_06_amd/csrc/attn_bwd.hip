@@ -273,8 +273,19 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       oa[par] = (uint32_t)(col * dkv::OPX * 2 + 16 * ((2 * par + half) ^ u));
     }
     const int wsel = (kw >> 1), hsel = (s0 >> 5) & 1;  // the pair's key tile and word half
+    // a chunk's dS^T fragments are stored right after the next barrier, while
+    // the wave waits for its first LDS reads, not at the end of the chunk,
+    // where the wave is on the way to the barrier
+    u32x4 pend[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+    u32x4* pfr = dsf;
+    bool have = false;
     for (int it = 0; e0 >= 0; ++it) {
       lds_barrier();  // chunk e0 visible (B waited for its copies); B is done with P/dS buffer it&1
+      if (have) {  // streamed: read once, by the dQ kernel
+        __builtin_nontemporal_store(pend[0], pfr);
+        __builtin_nontemporal_store(pend[1], pfr + 64);
+        have = false;
+      }
       const int e3 = entry(it + 3);
       if (active(e0)) {
         const int bi = it % NB, qc = e0 & 0x3FFF;
@@ -321,12 +332,18 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
           *(u32x2*)(prow + 8) = u32x2{pp[2], pp[3]};
           *(u32x2*)trow = u32x2{dsp[0], dsp[1]};
           *(u32x2*)(trow + 8) = u32x2{dsp[2], dsp[3]};
-          __builtin_nontemporal_store(dsp, fr + 64 * p2);  // streamed: read once, by the dQ kernel
+          pend[p2] = dsp;
+          pfr = fr;
+          have = true;
         }
       }
       e0 = e1;
       e1 = e2;
       e2 = e3;
+    }
+    if (have) {
+      __builtin_nontemporal_store(pend[0], pfr);
+      __builtin_nontemporal_store(pend[1], pfr + 64);
     }
     lds_barrier();  // matches B's final barrier
   } else {

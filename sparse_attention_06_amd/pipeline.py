@@ -49,6 +49,16 @@ class DSAPath:
             dsa.dsa_index_scores(q_idx, k_idx, w, seg, row0, n, sc)
             dsa.dsa_topk(sc, seg, self.B, self.S, self.K, row0, n, self.idx, self.mask)
 
+    def select_fp8(self, q8, q_scale, k8, k_scale, w, seg=None):
+        """select() on fp8 (E4M3) index queries and keys with their row scales
+        (see dsa_quant_fp8_rows / dsa_index_scores_fp8)."""
+        for row0 in range(0, self.S, self.slab):
+            n = min(self.slab, self.S - row0)
+            sc = self.scores if n == self.slab else \
+                self.scores.view(-1)[: self.B * n * self.S].view(self.B, n, self.S)
+            dsa.dsa_index_scores_fp8(q8, q_scale, k8, k_scale, w, seg, row0, n, sc)
+            dsa.dsa_topk(sc, seg, self.B, self.S, self.K, row0, n, self.idx, self.mask)
+
     def build_mask(self, idx, seg=None):
         dsa.dsa_build_mask(idx, seg, self.mask)
 

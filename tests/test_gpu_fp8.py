@@ -156,3 +156,22 @@ def test_fp8_selection_end_to_end(segments):
     want_bits = ref.pack_bits(ref.selection_matrix(gi, S))
     np.testing.assert_array_equal(bits.cpu().numpy().view(np.uint64), want_bits)
     print(f"fp8 selection seg={segments}: {len(dec)} of {cfg.B * S} rows decidable and exact")
+
+
+def test_path_select_fp8_matches_direct_calls():
+    """DSAPath.select_fp8 (slabbed) gives the same index lists and mask as one
+    direct fp8 indexer + top-k call on the whole sequence."""
+    from sparse_attention_06_amd.pipeline import DSAPath
+    cfg = inputs.CONFIGS["c2"].replace(B=2, S=333, K=64)
+    x, q8, qs, k8, ks = _fp8_inputs(cfg)
+    d = [t.to(DEV) for t in (q8, qs, k8, ks, x["w"])]
+    path = DSAPath(cfg.B, cfg.S, cfg.Hi, cfg.Di, cfg.K, cfg.H, cfg.Dqk, cfg.Dv)
+    path.select_fp8(*d)
+    sc = torch.empty((cfg.B, cfg.S, cfg.S), device=DEV)
+    idx = torch.empty((cfg.B, cfg.S, cfg.K), dtype=torch.int32, device=DEV)
+    mask = torch.empty(dsa.dsa_mask_bytes(cfg.B, cfg.S), dtype=torch.uint8, device=DEV)
+    dsa.dsa_index_scores_fp8(*d, None, 0, cfg.S, sc)
+    dsa.dsa_topk(sc, None, cfg.B, cfg.S, cfg.K, 0, cfg.S, idx, mask)
+    torch.cuda.synchronize()
+    assert torch.equal(path.idx, idx)
+    assert torch.equal(path.mask, mask)
