@@ -142,8 +142,9 @@ dsa_status dsa_quant_fp8_rows(const void* x, dsa_dtype x_dtype, int64_t nrows, i
  * I[b,t,s] = sum_j w[t,j] max(0, q[t,j,:] . k[s,:]) on the dequantized values.
  * Scales must be finite and >= 0. Hi in {32, 64}, Di in {64, 128}. The code
  * products are summed by fp8 MFMAs, whose internal accumulation is coarser
- * than float32: each head's dot product carries an absolute error of a few
- * 2^-14 of the largest code product in it (scaled by q_scale * k_scale).
+ * than float32: a 64-wide partial sum was measured off by up to 2^-12.9 of the
+ * largest code product in it, so a head's dot product carries an absolute
+ * error of about 2^-12 of its largest code product (times q_scale * k_scale).
  * ------------------------------------------------------------------------- */
 dsa_status dsa_index_scores_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                                 const float* k_scale, const void* w, const int32_t* seg, int B,
