@@ -126,7 +126,7 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
  *   x       [nrows, D] x_dtype (DSA_BF16 or DSA_FP32), rows contiguous
  *   codes   [nrows, D] uint8     out: E4M3 codes (s eeee mmm, bias 7)
  *   scale   [nrows]    float32   out
- * D in {64, 128, 256, 512}. For the fp8 indexer below, q_idx [B,S,Hi,Di] is
+ * D in {64, 128, 256, 512}; x and codes 16-byte aligned. For the fp8 indexer below, q_idx [B,S,Hi,Di] is
  * B*S*Hi rows of Di and k_idx [B,S,Di] is B*S rows of Di.
  * ------------------------------------------------------------------------- */
 dsa_status dsa_quant_fp8_rows(const void* x, dsa_dtype x_dtype, int64_t nrows, int D,

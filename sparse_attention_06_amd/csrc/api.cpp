@@ -123,6 +123,8 @@ dsa_status dsa_quant_fp8_rows(const void* x, dsa_dtype x_dtype, int64_t nrows, i
   REQ_PTR(codes);
   REQ_PTR(scale);
   REQ(dtype_ok(x_dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  REQ(aligned16(x) && aligned16(codes) && ((uintptr_t)scale & 3) == 0, DSA_ERR_INVALID_ARG,
+      "x and codes must be 16-byte aligned, scale 4-byte aligned");
   REQ(nrows >= 1, DSA_ERR_INVALID_ARG, "nrows=%lld must be >= 1", (long long)nrows);
   REQ(D == 64 || D == 128 || D == 256 || D == 512, DSA_ERR_UNSUPPORTED, "D=%d not in {64, 128, 256, 512}", D);
   // one wave per row, 256-thread blocks: the grid's thread count must stay below 2^32

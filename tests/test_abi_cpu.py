@@ -92,6 +92,8 @@ def test_quant_fp8_rejects():
     assert L.dsa_quant_fp8_rows(P, 0, 0, 128, P, P, S_) == 1
     assert L.dsa_quant_fp8_rows(P, 3, 4, 128, P, P, S_) == 1
     assert L.dsa_quant_fp8_rows(P, 0, 4, 96, P, P, S_) == 2
+    assert L.dsa_quant_fp8_rows(MIS, 0, 4, 128, P, P, S_) == 1
+    assert L.dsa_quant_fp8_rows(P, 0, 4, 128, MIS, P, S_) == 1
     assert L.dsa_quant_fp8_rows(P, 0, (1 << 26) + 1, 128, P, P, S_) == 2
 
 
