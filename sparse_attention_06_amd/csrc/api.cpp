@@ -110,8 +110,10 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
     return hip_status(dsa::launch_index_scores_mfma(q_idx, k_idx, w, seg, B, S, Hi, Di, row0, nrows,
                                                     scores, out_bf16, ld, st),
                       "dsa_index_scores");
-  REQ((size_t)(Hi * Di + Hi) * 4 <= 65536, DSA_ERR_UNSUPPORTED,
-      "Hi*Di=%d too large for the plain indexer kernel", Hi * Di);
+  // the plain kernel stages the query's Hi x Di values and Hi weights as
+  // float32 in 64 KB of LDS; the product is formed in 64 bits
+  REQ(((int64_t)Hi * Di + Hi) * 4 <= 65536, DSA_ERR_UNSUPPORTED,
+      "Hi*Di=%lld too large for the plain indexer kernel", (long long)Hi * Di);
   return hip_status(dsa::launch_index_scores_plain(q_idx, k_idx, w, seg, B, S, Hi, Di, in_bf16, row0,
                                                    nrows, scores, out_bf16, ld, st),
                     "dsa_index_scores");

@@ -258,7 +258,7 @@ hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const
                                      bool in_bf16, int row0, int nrows, void* scores,
                                      bool out_bf16, int64_t ld, hipStream_t st) {
   dim3 grid((unsigned)(((S + 255) / 256) * nrows), (unsigned)B), block(256);
-  const size_t shm = (size_t)(Hi * Di + Hi) * sizeof(float);
+  const size_t shm = ((size_t)Hi * Di + Hi) * sizeof(float);  // the caller bounds it to 64 KB
 #define DSA_IDX_PLAIN(IT, OT)                                                               \
   hipLaunchKernelGGL((index_scores_plain_kernel<IT, OT>), grid, block, shm, st, (const IT*)q_idx, \
                      (const IT*)k_idx, (const IT*)w, seg, S, Hi, Di, row0, nrows, (OT*)scores, ld)

@@ -64,16 +64,14 @@ __device__ __forceinline__ void block_uminmax(uint32_t& mn, uint32_t& mx, TopkSh
 // count(all bins) >= need >= 1.
 __device__ void find_bin(TopkShared& sh, uint32_t need) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // thread i owns bins [8i, 8i+8); scan in descending bin order: thread order
-  // reversed, so thread j = 255 - i covers the j-th chunk from the top
-  const int j = 255 - tid;
+  // thread i owns bins [8i, 8i+8); the scan runs in descending bin order, so
+  // thread 255 - i covers the i-th chunk from the top
   uint32_t c[8];
   uint32_t tot = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { c[i] = sh.hist[8 * tid + i]; tot += c[i]; }
-  // inclusive prefix over j (descending bins) within the wave: lanes ordered by j
-  // j = 255 - tid, so within a wave, lower j is higher lane. Use a suffix scan
-  // over lanes: incl = sum of tot over lanes >= this lane.
+  // inclusive prefix in descending bin order within the wave, i.e. a suffix
+  // scan over lanes: incl = sum of tot over lanes >= this lane.
   const uint32_t pre = wave_incl_scan(tot);
   const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + tot;
   if (lane == 0) sh.red_u[wid] = incl;  // wave total
@@ -83,7 +81,6 @@ __device__ void find_bin(TopkShared& sh, uint32_t need) {
   for (int w2 = wid + 1; w2 < 4; ++w2) above_waves += sh.red_u[w2];
   __syncthreads();
   uint32_t running = above_waves + incl - tot;  // count of bins above this thread's chunk
-  (void)j;
 #pragma unroll
   for (int i = 7; i >= 0; --i) {
     if (running < need && running + c[i] >= need) {

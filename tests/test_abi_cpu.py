@@ -61,7 +61,10 @@ def _idx_call(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q_idx=NUL), 1), (dict(k_idx=MIS), 1), (dict(B=0), 1), (dict(S=-1), 1),
     (dict(row0=100, nrows=100), 1), (dict(ld=100), 1), (dict(dt=7), 1), (dict(seg=MIS), 1),
-    (dict(Di=12), 2), (dict(Hi=4096, Di=64, dt=1), 2), (dict(S=(1 << 18) + 1, nrows=1, ld=(1 << 18) + 1), 2),
+    (dict(Di=12), 2), (dict(Hi=4096, Di=64, dt=1), 2),
+    # Hi * Di wraps a 32-bit int to a small value: still rejected (64-bit product)
+    (dict(Hi=65536, Di=65535, dt=1), 2), (dict(Hi=65536, Di=65536, dt=1), 2),
+    (dict(S=(1 << 18) + 1, nrows=1, ld=(1 << 18) + 1), 2),
 ])
 def test_index_scores_rejects(kw, code):
     assert _idx_call(**kw) == code

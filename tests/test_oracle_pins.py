@@ -749,3 +749,92 @@ def test_fp8_row_restricted_helpers_match_full_functions():
     bf = ref.index_scores_fp8_bound(q8, qs, k8, ks, w, rows, 2.0 ** -17)
     bp = ref.index_scores_fp8_bound_rows(q8[:, rows], qs[:, rows], k8, ks, w[:, rows], 2.0 ** -17)
     np.testing.assert_array_equal(bf, bp)
+
+
+# ------------------------------------------------ fp8 score error bound pins
+# The fp8 indexer's parity tolerance is oracle.index_scores_fp8_bound. It is
+# pinned here against an emulation of a coarse accumulator, written out
+# independently of the bound: each head's dot product of codes is summed in
+# 64-wide blocks, and every block's exact partial sum is rounded to a grid of
+# 2^-13 of the largest code product inside that block, in the direction that
+# moves the score furthest (towards sign(w_j)). That is the accumulation a
+# K = 64 fp8 MFMA with ~13 fractional bits relative to its largest product
+# would perform; everything after the dot product is exact here.
+def _fp8_coarse_scores(q8, qs, k8, ks, w, rows, grid_rel=2.0 ** -13, block=64):
+    qd, kd = ref.fp8_e4m3_decode(q8), ref.fp8_e4m3_decode(k8)   # code values
+    B, S, Hi, Di = qd.shape
+    out = np.full((B, len(rows), S), -np.inf)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            for s in range(t + 1):
+                total = 0.0
+                for j in range(Hi):
+                    dot = 0.0
+                    for d0 in range(0, Di, block):
+                        prod = qd[b, t, j, d0:d0 + block] * kd[b, s, d0:d0 + block]
+                        part = math.fsum(prod.tolist())
+                        u = grid_rel * np.abs(prod).max()
+                        if u > 0:
+                            part = u * (math.ceil(part / u) if w[b, t, j] > 0 else math.floor(part / u))
+                        dot += part
+                    total += w[b, t, j] * float(qs[b, t, j]) * float(ks[b, s]) * max(dot, 0.0)
+                out[b, r, s] = total
+    return out
+
+
+def _fp8_bound_case(seed=31, B=1, S=12, Hi=64, Di=128):
+    """Codes whose largest |q8| and |k8| sit at the same dim of both 64-wide
+    blocks (so a block's largest product is max|q8| * max|k8|), most head
+    dot products positive, and key scales spread over 2^-4 .. 2^4."""
+    rng = np.random.default_rng(seed)
+    q = np.abs(rng.standard_normal((B, S, Hi, Di))).astype(np.float32) * 0.5
+    k = np.abs(rng.standard_normal((B, S, Di))).astype(np.float32) * 0.5
+    q[..., 3] = q[..., 67] = 4.0
+    k[..., 3] = k[..., 67] = 4.0
+    q *= np.where(rng.random((B, S, Hi, Di)) < 0.2, -1, 1).astype(np.float32)
+    q8, qs = ref.quantize_fp8_rows(q)
+    k8, ks = ref.quantize_fp8_rows(k)
+    ks = (ks * np.exp2(rng.uniform(-4, 4, ks.shape))).astype(np.float32)
+    w = rng.standard_normal((B, S, Hi))
+    return q8, qs, k8, ks, w
+
+
+def test_fp8_bound_covers_coarse_accumulation_and_is_tight():
+    q8, qs, k8, ks, w = _fp8_bound_case()
+    rows = np.arange(q8.shape[1])
+    exact = ref.index_scores_fp8(q8, qs, k8, ks, w, None, rows)
+    coarse = _fp8_coarse_scores(q8, qs, k8, ks, w, rows)
+    fin = np.isfinite(exact)
+    err = np.zeros_like(exact)
+    err[fin] = np.abs(coarse[fin] - exact[fin])
+    assert err.max() > 0
+    # the bound the GPU tests use covers the emulated accumulator everywhere
+    bound = ref.index_scores_fp8_bound(q8, qs, k8, ks, w, rows, rel=2.0 ** -17)
+    assert np.all(err <= np.where(fin, bound, 0)), float((err / np.maximum(bound, 1e-300)).max())
+    # and is not loose by an order of magnitude: an 8x tighter one is exceeded
+    tight = ref.index_scores_fp8_bound(q8, qs, k8, ks, w, rows, rel=2.0 ** -20)
+    assert np.any(err > np.where(fin, tight, np.inf))
+
+
+def test_fp8_bound_planted_mistakes_fail_a_pin(monkeypatch):
+    orig = ref.index_scores_fp8_bound
+
+    def no_di(q8, q_scale, k8, k_scale, w, rows, rel):   # Di factor dropped
+        return orig(q8, q_scale, k8, k_scale, w, rows, rel / np.asarray(q8).shape[-1])
+
+    def no_kscale(q8, q_scale, k8, k_scale, w, rows, rel):   # k_scale dropped from the first term
+        full = orig(q8, q_scale, k8, k_scale, w, rows, rel)
+        small = orig(q8, q_scale, k8, k_scale, w, rows, 0.0)
+        return small + (full - small) / np.asarray(k_scale, np.float64)[:, None, :]
+
+    def head_max(q8, q_scale, k8, k_scale, w, rows, rel):    # max over heads instead of a sum
+        Hi = np.asarray(q8).shape[2]
+        per = [orig(q8[:, :, j:j + 1], q_scale[:, :, j:j + 1], k8, k_scale, w[:, :, j:j + 1], rows, rel)
+               for j in range(Hi)]
+        return np.max(per, axis=0)
+
+    for bad in (no_di, no_kscale, head_max):
+        monkeypatch.setattr(ref, "index_scores_fp8_bound", bad)
+        with pytest.raises(AssertionError):
+            test_fp8_bound_covers_coarse_accumulation_and_is_tight()
+        monkeypatch.undo()
