@@ -1,22 +1,30 @@
 """Benchmark of the DSA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--no-cpu] [--no-long]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2] [--no-cpu]
+                    [--no-long] [--no-c4] [--no-c1] [--long-only] [--copy-mib N]
 
 One step is the whole path over one batch of seeded synthetic input: indexer
 scores -> top-k (index lists, mask bits, tile classes) -> sparse attention
-forward -> backward (dQ, then dK/dV). Inputs are resident in HBM before the
-timed region. Default workload: the 2B-model training shape (batch 12,
+forward -> backward (D prologue, dK/dV, dQ). Inputs are resident in HBM before
+the timed region. Default workload: the 2B-model training shape (batch 12,
 seq 4096, 16 heads of 192/128, indexer 64 x 128, top-k 2048, bf16).
+
+Before each timed step a 512 MB scratch buffer is overwritten, so every step
+starts with cold caches (the scores of a step are up to 0.8 GB, comparable to
+the chip's last-level cache). Each C-ABI call is bracketed by HIP events on
+the launch stream; ms_per_step is the mean of the per-step spans (the scrub
+itself is outside them), with the median and min next to it.
 
 Prints one JSON line. `value` is useful TFLOP/s of the whole step:
 indexer pairs x Hi x 2 Di, plus selected pairs x H x 6 (Dqk + Dv) for
-forward + backward. `indexer_topk_ms` is the selection half of the metric;
-`selection` repeats it at the 32K (671B head count) and 128K workloads, where
-indexer and top-k are timed alone (the attention there is forward only and not
-part of the step).
-Per-kernel times come from HIP events recorded on the launch stream around
-each C-ABI call (each is one kernel, except dsa_topk, which is the top-k
-kernel plus the small tile-class kernel).
+forward + backward. `indexer_topk_ms` is the selection half of the metric.
+The same line also carries:
+  * "c4": the packed-document fwd+bwd workload (B 4, S 8192, 32 heads);
+  * "selection": indexer + top-k at the 32K and 128K workloads, with the
+    attention forward there (useful and executed-tile TFLOP/s);
+  * "c1": the tiny fp32 workload's latency in microseconds;
+  * "roofline" for the dominant kernel, and "cpu_baseline" (the float64
+    oracle on a bounded row sample).
 """
 from __future__ import annotations
 
@@ -105,11 +113,23 @@ def measured_traffic(call, workload_key):
 def cpu_baseline(cfg, x_cpu, budget_s=15.0, max_rows=4096):
     """The float64 oracle on a bounded row sample of the same workload."""
     from oracle import dsa_oracle as ref
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] + [1])
+        blas = ",".join(sorted({str(p.get("internal_api", "?")) for p in info})) or "unknown"
     except Exception:  # pragma: no cover
         threads = 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     f64 = lambda t: t.float().double().numpy()  # noqa: E731
     q_idx, k_idx, w = f64(x_cpu["q_idx"]), f64(x_cpu["k_idx"]), f64(x_cpu["w"])
     q, k, v = f64(x_cpu["q"]), f64(x_cpu["k"]), f64(x_cpu["v"])
@@ -137,13 +157,29 @@ def cpu_baseline(cfg, x_cpu, budget_s=15.0, max_rows=4096):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{done} random query rows of batch row 0 (indexer, top-k, forward"
                       f"{', backward' if cfg.backward else ''}), {dt:.1f} s, float64 numpy",
-            "seconds": dt, "rows": done}
+            "seconds": dt, "rows": done, "host_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model, "blas": blas, "blas_threads": int(threads)}
 
 
-def selection_long(key, reps=2):
-    """Indexer + top-k alone at a long-sequence workload (the metric's 32K and
-    128K points): one warm-up call, then `reps` timed calls of each, with HIP
-    events on the launch stream. Only the selection inputs are generated."""
+def executed_tile_pairs(cls_np, S):
+    """(query, key) pairs of the non-EMPTY 128 x 64 tiles of a tile-class map
+    [B, NQ, NK] (ragged edge tiles counted at their real size): the pairs the
+    attention kernels run MFMAs on."""
+    nq, nk = cls_np.shape[1:]
+    rows = np.minimum(128, S - 128 * np.arange(nq))
+    cols = np.minimum(64, S - 64 * np.arange(nk))
+    return int(((cls_np != 0) * rows[None, :, None] * cols[None, None, :]).sum())
+
+
+def stats(xs):
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(xs.mean()), "median": float(np.median(xs)), "min": float(xs.min())}
+
+
+def long_workload(key, reps=2, attention=True):
+    """Indexer + top-k (and the attention forward) at a long-sequence workload
+    (the metric's 32K and 128K points): one warm-up call, then `reps` timed
+    calls of each, with HIP events on the launch stream."""
     import torch
     from sparse_attention_06_amd import dsa, inputs
     cfg = inputs.CONFIGS[key]
@@ -165,6 +201,36 @@ def selection_long(key, reps=2):
         if i:
             t_idx.append(ev[0].elapsed_time(ev[1]))
             t_top.append(ev[1].elapsed_time(ev[2]))
+    wk = work(cfg, None if x["seg"] is None else x["seg"].cpu().numpy())
+    out = {"workload": cfg.name, "S": cfg.S}
+    # the attention forward on the selection just made (the workload's own pass)
+    if attention:
+        B, S, H = cfg.B, cfg.S, cfg.H
+        dt = cfg.torch_dtype()
+        q = inputs.normal((B, S, H, cfg.Dqk), cfg.Dqk ** -0.5, cfg.seed, "q", dt, "cuda")
+        k = inputs.normal((B, S, H, cfg.Dqk), cfg.Dqk ** -0.5, cfg.seed, "k", dt, "cuda")
+        v = inputs.normal((B, S, H, cfg.Dv), cfg.Dv ** -0.5, cfg.seed, "v", dt, "cuda")
+        o = torch.empty_like(v)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+        t_att = []
+        for i in range(reps + 1):
+            ev[0].record(stream)
+            dsa.dsa_sparse_attn_fwd(q, k, v, mask, cfg.softmax_scale, o, lse)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            if i:
+                t_att.append(ev[0].elapsed_time(ev[1]))
+        _, cls = dsa.mask_views(mask, B, S)
+        executed = executed_tile_pairs(cls.cpu().numpy(), S) * H * 2 * (cfg.Dqk + cfg.Dv)
+        ma = float(np.median(t_att))
+        out["attn_fwd_ms"] = ma
+        out["attn_fwd"] = {"useful_tflops": wk["fwd"] / (ma * 1e-3) / 1e12,
+                           "executed_tile_tflops": executed / (ma * 1e-3) / 1e12,
+                           "frac_useful": wk["fwd"] / (ma * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "frac_executed": executed / (ma * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                           "useful_flops": wk["fwd"], "executed_flops": executed,
+                           "useful_over_executed": wk["fwd"] / executed, "ms": stats(t_att)}
+        del q, k, v, o, lse
     # the fp8 (E4M3) indexer on the same inputs, quantized on the GPU first (untimed)
     q8 = torch.empty(x["q_idx"].shape, dtype=torch.uint8, device="cuda")
     qs = torch.empty(x["q_idx"].shape[:-1], dtype=torch.float32, device="cuda")
@@ -196,87 +262,52 @@ def selection_long(key, reps=2):
             t_rope.append(ev[0].elapsed_time(ev[1]))
     # in place only the rotated dims move: bf16 read + write of 64 of every Di
     rope_bytes = 2 * (x["q_idx"].numel() + x["k_idx"].numel()) * 2 * 64 // cfg.Di
-    wk = work(cfg, None if x["seg"] is None else x["seg"].cpu().numpy())
-    mi, mt = float(np.mean(t_idx)), float(np.mean(t_top))
-    m8 = float(np.mean(t_fp8))
-    mr = float(np.mean(t_rope))
+    mi, mt = float(np.median(t_idx)), float(np.median(t_top))
+    m8 = float(np.median(t_fp8))
+    mr = float(np.median(t_rope))
     del scores, idx, mask, x, q8, qs, k8, ks
     torch.cuda.empty_cache()
     ach_i = wk["indexer"] / (mi * 1e-3) / 1e12
     ach_8 = wk["indexer"] / (m8 * 1e-3) / 1e12
     ach_t = wk["topk_bytes"] / (mt * 1e-3) / 1e9
-    return {"workload": cfg.name, "S": cfg.S, "index_scores_ms": mi, "topk_ms": mt, "indexer_topk_ms": mi + mt,
-            "index_scores": {"achieved": ach_i, "unit": "TFLOP/s", "frac": ach_i / PEAK_BF16_TFLOPS,
+    out.update({
+        "index_scores_ms": mi, "topk_ms": mt, "indexer_topk_ms": mi + mt,
+        "index_scores": {"achieved": ach_i, "unit": "TFLOP/s", "frac": ach_i / PEAK_BF16_TFLOPS,
+                         "algorithmic": wk["indexer"], "ms": stats(t_idx)},
+        "topk": {"achieved": ach_t, "unit": "GB/s", "frac": ach_t / PEAK_HBM_GBS,
+                 "algorithmic": wk["topk_bytes"], "ms": stats(t_top)},
+        # fp8 inputs (not the metric's bf16 workload): the indexer alone and with the same top-k
+        "index_scores_fp8_ms": m8, "indexer_fp8_topk_ms": m8 + mt,
+        "index_scores_fp8": {"achieved": ach_8, "unit": "TFLOP/s", "frac": ach_8 / PEAK_FP8_TFLOPS,
                              "algorithmic": wk["indexer"]},
-            "topk": {"achieved": ach_t, "unit": "GB/s", "frac": ach_t / PEAK_HBM_GBS,
-                     "algorithmic": wk["topk_bytes"]},
-            # fp8 inputs (not the metric's bf16 workload): the indexer alone and with the same top-k
-            "index_scores_fp8_ms": m8, "indexer_fp8_topk_ms": m8 + mt,
-            "index_scores_fp8": {"achieved": ach_8, "unit": "TFLOP/s", "frac": ach_8 / PEAK_FP8_TFLOPS,
-                                 "algorithmic": wk["indexer"]},
-            # input preparation before the indexer (not part of the metric): RoPE of q_idx and k_idx
-            "rope_ms": mr, "rope": {"achieved": rope_bytes / (mr * 1e-3) / 1e9, "unit": "GB/s",
-                                    "frac": rope_bytes / (mr * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                    "algorithmic": rope_bytes}}
+        # input preparation before the indexer (not part of the metric): RoPE of q_idx and k_idx
+        "rope_ms": mr, "rope": {"achieved": rope_bytes / (mr * 1e-3) / 1e9, "unit": "GB/s",
+                                "frac": rope_bytes / (mr * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                "algorithmic": rope_bytes}})
+    return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-long", action="store_true",
-                    help="skip timing indexer + top-k at the 32K and 128K workloads")
-    ap.add_argument("--long-only", action="store_true",
-                    help="only time indexer + top-k at the 32K and 128K workloads (one JSON line)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
-        sys.exit(2)
+CALLS_FWD = ["index_scores", "topk", "attn_fwd"]
+CALLS_BWD = ["attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq"]
 
+
+def time_steps(cfg, steps, warmup, scrub=None, x=None):
+    """Warm up, then time `steps` whole steps of the path at one workload.
+
+    Before every timed step `scrub` (a device buffer) is overwritten. Returns
+    (per-call ms lists, per-step ms list, region ms, inputs, path)."""
     import torch
     from sparse_attention_06_amd import dsa, inputs
     from sparse_attention_06_amd.pipeline import DSAPath
-
-    cfg = inputs.CONFIGS[args.config]
-    dsa.lib()
-    dev = "cuda"
-    if args.copy_mib:
-        n = args.copy_mib * (1 << 20)
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {n} bytes read, {n} bytes written")
-        del src, dst
-
-    if args.long_only:
-        selection = {}
-        for key in ("c3", "c5"):
-            log(f"indexer + top-k at {inputs.CONFIGS[key].name}")
-            r = selection_long(key)
-            selection[f"S{r['S']}"] = r
-            log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms, "
-                f"fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms, rope {r['rope_ms']:.3f} ms")
-        print(json.dumps({"metric": "indexer + top-k ms", "selection": selection}), flush=True)
-        return
-    log(f"config {cfg.name}: generating inputs on the GPU")
-    x = inputs.make(cfg, device=dev)
-    seg_np = None if x["seg"] is None else x["seg"].cpu().numpy()
+    if x is None:
+        x = inputs.make(cfg, device="cuda")
     sdt = torch.bfloat16 if cfg.score_dtype == "bf16" else torch.float32
     path = DSAPath(cfg.B, cfg.S, cfg.Hi, cfg.Di, cfg.K, cfg.H, cfg.Dqk, cfg.Dv, dtype=cfg.torch_dtype(),
-                   score_dtype=sdt, backward=cfg.backward, device=dev)
+                   score_dtype=sdt, backward=cfg.backward, device="cuda")
     scale = cfg.softmax_scale
     seg = x["seg"]
     stream = torch.cuda.current_stream()
-
-    calls = ["index_scores", "topk", "attn_fwd"] + (["attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq"]
-                                                    if cfg.backward else [])
+    calls = CALLS_FWD + (CALLS_BWD if cfg.backward else [])
 
     def step(evs=None):
         def mark(i):
@@ -299,28 +330,27 @@ def main():
                                        path.dq, path.ws)
             mark(6)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step()
         torch.cuda.synchronize()
-        log(f"warmup {i + 1}/{args.warmup} done")
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+        log(f"{cfg.name}: warmup {i + 1}/{warmup} done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)   # cold caches for the step that follows
         step(evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / args.steps
-    per = {c: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(args.steps)]))
-           for j, c in enumerate(calls)}
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step; " + ", ".join(f"{c} {v:.3f}" for c, v in per.items()))
+    per = {c: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)] for j, c in enumerate(calls)}
+    step_ms = [evs[i][0].elapsed_time(evs[i][len(calls)]) for i in range(steps)]
+    return per, step_ms, t_start.elapsed_time(t_end), x, path
 
-    wk = work(cfg, seg_np)
-    useful = wk["indexer"] + wk["fwd"] + (wk["bwd"] if cfg.backward else 0)
-    value = useful / (ms * 1e-3) / 1e12
+
+def kernel_table(cfg, wk, per):
     kern = {
         "index_scores": ("mfma", wk["indexer"]),
         "topk": ("hbm", wk["topk_bytes"]),
@@ -330,40 +360,149 @@ def main():
         "attn_bwd_dkdv": ("mfma", wk["bwd_dkdv"]),
     }
     kernels = {}
-    for c in calls:
+    for c, xs in per.items():
         bound, amount = kern[c]
-        t = per[c] * 1e-3
+        st = stats(xs)
+        t = st["median"] * 1e-3
         if bound == "mfma":
             ach = amount / t / 1e12
-            kernels[c] = {"ms": per[c], "bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
+            kernels[c] = {"ms": st["median"], "ms_stats": st, "bound": "mfma", "achieved": ach, "unit": "TFLOP/s",
                           "frac": ach / PEAK_BF16_TFLOPS, "algorithmic": amount}
         else:
             ach = amount / t / 1e9
-            kernels[c] = {"ms": per[c], "bound": "hbm", "achieved": ach, "unit": "GB/s",
+            kernels[c] = {"ms": st["median"], "ms_stats": st, "bound": "hbm", "achieved": ach, "unit": "GB/s",
                           "frac": ach / PEAK_HBM_GBS, "algorithmic": amount}
-    dom = max(calls, key=lambda c: per[c])
+    return kernels
+
+
+def attention_rate(cfg, wk, kernels):
+    att = [c for c in kernels if c.startswith("attn")]
+    flops = wk["fwd"] + (wk["bwd"] if cfg.backward else 0)
+    return flops / (sum(kernels[c]["ms"] for c in att) * 1e-3) / 1e12
+
+
+def tiny_latency(reps=50):
+    """The tiny fp32 workload (indexer, top-k, forward): microseconds per call
+    and per step, median over `reps` back-to-back steps."""
+    import torch
+    from sparse_attention_06_amd import inputs
+    cfg = inputs.CONFIGS["c1"]
+    per, step_ms, _, _, _ = time_steps(cfg, reps, 3)
+    return {"workload": cfg.name, "step_us": stats([1e3 * v for v in step_ms]),
+            "calls_us": {c: float(np.median(v)) * 1e3 for c, v in per.items()}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 32K and 128K workloads (indexer + top-k + attention forward)")
+    ap.add_argument("--no-c4", action="store_true", help="skip the packed-document fwd+bwd workload")
+    ap.add_argument("--no-c1", action="store_true", help="skip the tiny workload's latency")
+    ap.add_argument("--no-scrub", action="store_true", help="do not overwrite 512 MB before each timed step")
+    ap.add_argument("--long-only", action="store_true",
+                    help="only the 32K and 128K workloads (one JSON line)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_06_amd import dsa, inputs
+
+    cfg = inputs.CONFIGS[args.config]
+    dsa.lib()
+    dev = "cuda"
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+        del src, dst
+
+    def run_long():
+        selection = {}
+        for key in ("c3", "c5"):
+            log(f"indexer + top-k + attention forward at {inputs.CONFIGS[key].name}")
+            r = long_workload(key)
+            selection[f"S{r['S']}"] = r
+            log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms, "
+                f"attn_fwd {r['attn_fwd_ms']:.2f} ms, fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms, "
+                f"rope {r['rope_ms']:.3f} ms")
+        return selection
+
+    if args.long_only:
+        print(json.dumps({"metric": "indexer + top-k ms", "selection": run_long()}), flush=True)
+        return
+
+    scrub = None if args.no_scrub else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    log(f"config {cfg.name}: generating inputs on the GPU")
+    per, step_ms, region_ms, x, path = time_steps(cfg, args.steps, args.warmup, scrub)
+    seg_np = None if x["seg"] is None else x["seg"].cpu().numpy()
+    st = stats(step_ms)
+    ms = st["mean"]
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step (median {st['median']:.3f}, min {st['min']:.3f}); "
+        + ", ".join(f"{c} {np.median(v):.3f}" for c, v in per.items()))
+    wk = work(cfg, seg_np)
+    useful = wk["indexer"] + wk["fwd"] + (wk["bwd"] if cfg.backward else 0)
+    value = useful / (ms * 1e-3) / 1e12
+    kernels = kernel_table(cfg, wk, per)
+    dom = max(kernels, key=lambda c: kernels[c]["ms"])
     kd = kernels[dom]
     roofline = {"bound": kd["bound"], "achieved": kd["achieved"],
                 "peak": PEAK_BF16_TFLOPS if kd["bound"] == "mfma" else PEAK_HBM_GBS, "unit": kd["unit"],
                 "frac": kd["frac"], "traffic": measured_traffic(dom, args.config), "kernel": dom}
+    selection = {f"S{cfg.S}": {"workload": cfg.name, "S": cfg.S, "index_scores_ms": kernels["index_scores"]["ms"],
+                               "topk_ms": kernels["topk"]["ms"],
+                               "indexer_topk_ms": kernels["index_scores"]["ms"] + kernels["topk"]["ms"],
+                               "topk": {"achieved": kernels["topk"]["achieved"], "unit": "GB/s",
+                                        "frac": kernels["topk"]["frac"]}}}
+    x_cpu = None if args.no_cpu else {k: (None if v is None else v.cpu()) for k, v in x.items()}
+    del path, x
+    torch.cuda.empty_cache()
 
-    # the metric's other sequence lengths: indexer + top-k alone at 32K and 128K
-    selection = {f"S{cfg.S}": {"workload": cfg.name, "S": cfg.S, "index_scores_ms": per["index_scores"],
-                               "topk_ms": per["topk"], "indexer_topk_ms": per["index_scores"] + per["topk"]}}
-    if not args.no_long:
-        del path
+    c4 = None
+    if not args.no_c4 and args.config != "c4":
+        c4cfg = inputs.CONFIGS["c4"]
+        log(f"config {c4cfg.name}")
+        p4, s4, _, x4, path4 = time_steps(c4cfg, min(args.steps, 5), 2, scrub)
+        wk4 = work(c4cfg, x4["seg"].cpu().numpy())
+        k4 = kernel_table(c4cfg, wk4, p4)
+        st4 = stats(s4)
+        useful4 = wk4["indexer"] + wk4["fwd"] + wk4["bwd"]
+        c4 = {"workload": c4cfg.name, "ms_per_step": st4["mean"], "ms_stats": st4,
+              "value": useful4 / (st4["mean"] * 1e-3) / 1e12, "unit": "TFLOP/s",
+              "attention_useful_tflops": attention_rate(c4cfg, wk4, k4),
+              "indexer_topk_ms": k4["index_scores"]["ms"] + k4["topk"]["ms"], "kernels": k4,
+              "selected_pairs": wk4["selected"], "valid_pairs": wk4["pairs"]}
+        log(f"  {st4['mean']:.3f} ms/step; " + ", ".join(f"{c} {v['ms']:.3f}" for c, v in k4.items()))
+        del path4, x4
         torch.cuda.empty_cache()
-        for key in ("c3", "c5"):
-            log(f"indexer + top-k at {inputs.CONFIGS[key].name}")
-            r = selection_long(key)
-            selection[f"S{r['S']}"] = r
-            log(f"  index_scores {r['index_scores_ms']:.2f} ms, topk {r['topk_ms']:.2f} ms, "
-                f"fp8 index_scores {r['index_scores_fp8_ms']:.2f} ms, rope {r['rope_ms']:.3f} ms")
+    if scrub is not None:
+        del scrub
+        torch.cuda.empty_cache()
+
+    if not args.no_long:
+        selection.update(run_long())
+
+    c1 = None
+    if not args.no_c1:
+        log("tiny fp32 workload latency")
+        c1 = tiny_latency()
+        log(f"  {c1['step_us']['median']:.1f} us per step")
 
     cpu = None
-    if not args.no_cpu:
+    if x_cpu is not None:
         log("timing the float64 oracle on a row sample (cpu baseline)")
-        x_cpu = {k: (None if v is None else v.cpu()) for k, v in x.items()}
         cpu = cpu_baseline(cfg, x_cpu)
         log(f"cpu baseline: {cpu['value']:.3e} TFLOP/s over {cpu['rows']} rows")
 
@@ -373,12 +512,15 @@ def main():
         "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "fp32", "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "S": cfg.S, "index_heads": cfg.Hi, "index_dim": cfg.Di,
                    "topk": cfg.K, "heads": cfg.H, "dqk": cfg.Dqk, "dv": cfg.Dv, "score_dtype": cfg.score_dtype,
-                   "segments": cfg.segments is not None, "passes": "+".join(calls)},
-        "indexer_topk_ms": per["index_scores"] + per["topk"],
+                   "segments": cfg.segments is not None,
+                   "passes": "+".join(CALLS_FWD + (CALLS_BWD if cfg.backward else []))},
+        "ms_per_step_stats": st, "timed_region_ms": region_ms, "cold_cache_scrub_bytes": 0 if args.no_scrub else 512 << 20,
+        "indexer_topk_ms": kernels["index_scores"]["ms"] + kernels["topk"]["ms"],
         "selection": selection,
-        "attention_useful_tflops": (wk["fwd"] + (wk["bwd"] if cfg.backward else 0)) /
-                                   (sum(per[c] for c in calls if c.startswith("attn")) * 1e-3) / 1e12,
+        "attention_useful_tflops": attention_rate(cfg, wk, kernels),
         "kernels": kernels,
+        "c4": c4,
+        "c1": c1,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

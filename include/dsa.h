@@ -67,7 +67,7 @@ typedef enum {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1, /* NULL pointer, size < 1, bad range, misalignment */
   DSA_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype/dim combination) */
-  DSA_ERR_WORKSPACE = 3,   /* workspace smaller than dsa_bwd_workspace_bytes() */
+  DSA_ERR_WORKSPACE = 3,   /* workspace smaller than dsa_bwd_workspace_min_bytes() */
   DSA_ERR_HIP = 4          /* a HIP launch failed */
 } dsa_status;
 
@@ -90,7 +90,11 @@ typedef enum { DSA_BF16 = 0, DSA_FP32 = 1 } dsa_dtype;
  *   tile_cls  uint8  [B][ceil(S/DSA_TILE_Q)][ceil(S/DSA_TILE_K)], starting at
  *             byte B*S*W*8. Class of each tile of the selection matrix.
  * Produced only by dsa_topk or dsa_build_mask. Every set bit lies in valid(t),
- * so the mask already combines index, causal and segment conditions.
+ * so the mask already combines index, causal and segment conditions: the
+ * attention calls take no segment IDs and apply the mask as given. A caller
+ * who builds index sets elsewhere passes them, with the segment IDs, through
+ * dsa_build_mask, which drops every entry outside valid(t). Writing mask bits
+ * by hand is outside the contract (a bit outside valid(t) would be attended).
  * ------------------------------------------------------------------------- */
 size_t dsa_mask_bytes(int B, int S);
 
@@ -233,13 +237,20 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  *   lse       [B,H,S] float32
  *   mask      the forward's mask
  *   dq, dk    [B,S,H,Dqk] dtype out;  dv [B,S,H,Dv] dtype out
- *   workspace device scratch of at least dsa_bwd_workspace_bytes() bytes; it
- *             receives two float32 [B,H,S] arrays: D = rowsum(dout * o), then
- *             lse * log2(e) (the row's log-sum-exp in base-2 units). With the
- *             bf16 MFMA path (Dqk = 192, Dv = 128) it also holds, from the
- *             next 256-byte boundary, the dS tiles that the key-major kernel
- *             hands to the dQ kernel: 2 bytes per causal (query, key) pair of
- *             every (b, h), rounded to 32 x 64 blocks (about B*H*S*S bytes).
+ *   workspace device scratch of workspace_bytes >= dsa_bwd_workspace_min_bytes()
+ *             bytes. It receives two float32 [B,H,S] arrays: D = rowsum(dout * o),
+ *             then lse * log2(e) (the row's log-sum-exp in base-2 units).
+ *             With the bf16 MFMA path (Dqk = 192, Dv = 128) a larger workspace
+ *             also holds, from the next 256-byte boundary, the dS tiles that the
+ *             key-major kernel hands to the dQ kernel ("handoff"): 2 bytes per
+ *             causal (query, key) pair of every (b, h), rounded to 32 x 64
+ *             blocks, i.e. B*H*4096*T bytes with T = sum over c < ceil(S/32) of
+ *             (c/2 + 1) (about B*H*S*S bytes). The handoff is used exactly when
+ *             workspace_bytes covers it; otherwise the dQ kernel recomputes P
+ *             and dS (same operations, same dQ, about twice the dQ time).
+ *             dsa_bwd_workspace_bytes() returns the size with the handoff when
+ *             the handoff is at most DSA_BWD_HANDOFF_MAX_BYTES, else the
+ *             minimum, so memory stays O(B*H*S) at long sequences.
  * Same as dsa_sparse_attn_bwd_prep, _dkdv and _dq in that order on the same
  * stream. Deterministic: no atomics.
  * ------------------------------------------------------------------------- */
@@ -257,7 +268,9 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
  *          also leaves dS in the workspace.
  *   _dq    query-major. Reads the workspace; writes dq.
  * Arguments as in dsa_sparse_attn_bwd; each returns DSA_ERR_WORKSPACE for a
- * workspace below dsa_bwd_workspace_bytes(). */
+ * workspace below dsa_bwd_workspace_min_bytes(). The three take the route
+ * (handoff or recompute) from workspace_bytes, so pass all three the same
+ * workspace and size. */
 dsa_status dsa_sparse_attn_bwd_prep(const void* o, const void* dout, const float* lse,
                                     int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype,
                                     void* workspace, size_t workspace_bytes, void* stream);
@@ -272,7 +285,20 @@ dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v,
                                   dsa_dtype dtype, void* dq, const void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv);
+/* Largest dS handoff that dsa_bwd_workspace_bytes() asks for: 16 GiB. The
+ * 2B-model shape (B 12, S 4096, 16 heads) needs 3.2 GB and the packed 8K shape
+ * (B 4, S 8192, 32 heads) 8.6 GB; at S = 32768 with 128 heads it would be
+ * 137 GB, so there the recompute route is the default. */
+#define DSA_BWD_HANDOFF_MAX_BYTES (16ull << 30)
+
+/* Workspace sizes of the backward calls, in bytes (0 for sizes < 1).
+ *   _min_bytes: D and the base-2 LSE, 8*B*H*S rounded up to 256; the least
+ *               any backward call accepts (recompute route).
+ *   _bytes:     the recommended size: with the handoff where the dtype and dims
+ *               take the MFMA path and the handoff is <= DSA_BWD_HANDOFF_MAX_BYTES,
+ *               otherwise the minimum. */
+size_t dsa_bwd_workspace_min_bytes(int B, int S, int H);
+size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype);
 
 /* Human-readable name of a status code. Static storage. */
 const char* dsa_status_string(dsa_status s);

@@ -59,17 +59,34 @@ size_t dsa_mask_bytes(int B, int S) {
   return dsa::bits_bytes(B, S) + (size_t)B * dsa::n_qtiles(S) * dsa::n_ktiles(S);
 }
 
-// D, then lse * log2(e) (float32 [B,H,S] each); for the MFMA head dims, the
-// dS^T fragments after them, from a 256-byte boundary
+static bool attn_mfma(int Dqk, int Dv, dsa_dtype dtype) {
+  return dtype == DSA_BF16 && Dqk == 192 && Dv == 128;
+}
+
+// Workspace layout: D, then lse * log2(e) (float32 [B,H,S] each); with the dS
+// handoff, the dS^T fragments after them, from a 256-byte boundary.
 static size_t bwd_frag_offset(int B, int S, int H) {
   return (2 * (size_t)B * H * S * sizeof(float) + 255) / 256 * 256;
 }
+static size_t bwd_handoff_bytes(int B, int S, int H) {
+  return (size_t)B * H * dsa::dsf_tile_base((S + 31) / 32) * 4096;
+}
+// The MFMA backward hands dS from the key-major to the query-major kernel when
+// the workspace the caller passes has room for it; otherwise dQ recomputes dS.
+static bool bwd_handoff(int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype, size_t workspace_bytes) {
+  return attn_mfma(Dqk, Dv, dtype) && workspace_bytes >= bwd_frag_offset(B, S, H) + bwd_handoff_bytes(B, S, H);
+}
 
-size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv) {
+size_t dsa_bwd_workspace_min_bytes(int B, int S, int H) {
   if (B < 1 || S < 1 || H < 1) return 0;
-  if (Dqk == 192 && Dv == 128)
-    return bwd_frag_offset(B, S, H) + (size_t)B * H * dsa::dsf_tile_base((S + 31) / 32) * 4096;
-  return 2 * (size_t)B * H * S * sizeof(float);
+  return bwd_frag_offset(B, S, H);
+}
+
+size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype) {
+  if (B < 1 || S < 1 || H < 1) return 0;
+  if (attn_mfma(Dqk, Dv, dtype) && bwd_handoff_bytes(B, S, H) <= (size_t)DSA_BWD_HANDOFF_MAX_BYTES)
+    return bwd_frag_offset(B, S, H) + bwd_handoff_bytes(B, S, H);
+  return bwd_frag_offset(B, S, H);
 }
 
 const char* dsa_status_string(dsa_status s) {
@@ -234,10 +251,6 @@ static dsa_status check_attn(int B, int S, int H, int Dqk, int Dv, float scale, 
   return DSA_OK;
 }
 
-static bool attn_mfma(int Dqk, int Dv, dsa_dtype dtype) {
-  return dtype == DSA_BF16 && Dqk == 192 && Dv == 128;
-}
-
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
                                int B, int S, int H, int Dqk, int Dv, float softmax_scale,
                                dsa_dtype dtype, void* o, float* lse, void* stream) {
@@ -273,7 +286,7 @@ static dsa_status check_bwd_common(const void* q, const void* k, const void* v, 
   REQ_PTR(workspace);
   dsa_status s = check_attn(B, S, H, Dqk, Dv, scale, dtype);
   if (s != DSA_OK) return s;
-  const size_t need = dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv);
+  const size_t need = dsa_bwd_workspace_min_bytes(B, S, H);
   REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
   return DSA_OK;
 }
@@ -287,7 +300,7 @@ dsa_status dsa_sparse_attn_bwd_prep(const void* o, const void* dout, const float
   REQ_PTR(workspace);
   dsa_status s = check_attn(B, S, H, Dqk, Dv, 1.f, dtype);
   if (s != DSA_OK) return s;
-  const size_t need = dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv);
+  const size_t need = dsa_bwd_workspace_min_bytes(B, S, H);
   REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
   return hip_status(dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, dtype == DSA_BF16, (float*)workspace,
                                               (hipStream_t)stream),
@@ -306,11 +319,13 @@ dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v,
   hipStream_t st = (hipStream_t)stream;
   void* m = const_cast<void*>(mask);
   const float* ws = (const float*)workspace;
-  if (attn_mfma(Dqk, Dv, dtype))
+  if (attn_mfma(Dqk, Dv, dtype)) {
+    void* dsf = bwd_handoff(B, S, H, Dqk, Dv, dtype, workspace_bytes)
+                    ? (void*)((char*)workspace + bwd_frag_offset(B, S, H)) : nullptr;
     return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
-                                                     softmax_scale, dk, dv,
-                                                     (char*)workspace + bwd_frag_offset(B, S, H), st),
+                                                     softmax_scale, dk, dv, dsf, st),
                       "dsa_sparse_attn_bwd_dkdv");
+  }
   return hip_status(dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, H, Dqk, Dv,
                                                     softmax_scale, dtype == DSA_BF16, dk, dv, st),
                     "dsa_sparse_attn_bwd_dkdv");
@@ -327,9 +342,13 @@ dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, c
   hipStream_t st = (hipStream_t)stream;
   void* m = const_cast<void*>(mask);
   const float* ws = (const float*)workspace;
-  if (attn_mfma(Dqk, Dv, dtype))
+  if (bwd_handoff(B, S, H, Dqk, Dv, dtype, workspace_bytes))
     return hip_status(dsa::launch_attn_bwd_dq_mfma(k, (const char*)workspace + bwd_frag_offset(B, S, H),
                                                    cls_of(m, B, S), B, S, H, softmax_scale, dq, st),
+                      "dsa_sparse_attn_bwd_dq");
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_bwd_dq_recompute(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
+                                                        softmax_scale, dq, st),
                       "dsa_sparse_attn_bwd_dq");
   return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, H, Dqk, Dv,
                                                   softmax_scale, dtype == DSA_BF16, dq, st),
@@ -356,5 +375,6 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
   return dsa_sparse_attn_bwd_dq(q, k, v, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dq,
                                 workspace, workspace_bytes, stream);
 }
+
 
 }  // extern "C"

@@ -11,8 +11,10 @@
 //   dV(s) += P dO(t),        dK(s) += scale dS q(t)      (key-major kernel)
 //   dQ(t)  = scale sum_s dS k(s)                         (query-major kernel)
 // The key-major kernel runs first: it recomputes P from LSE, forms dS, and
-// also stores dS^T in the workspace as MFMA B-operand fragments, which the
-// query-major kernel then contracts with K; nothing is recomputed there.
+// (when the workspace has room for them) also stores dS^T as MFMA B-operand
+// fragments, which the query-major kernel then contracts with K; nothing is
+// recomputed there. Without that room the query-major kernel recomputes P and
+// dS itself, in the same operations, so both routes give the same dQ.
 // Neither uses atomics, so the result is deterministic. The key-major kernel
 // reads the same row-major selection words as the forward: a lane owns one
 // query and 16 keys of its word, so no transposed copy of the mask is needed.
@@ -82,6 +84,9 @@ static_assert(NCOPY % 4 == 3, "B waves 0-2 issue NSLOT copies per chunk, wave 3 
 static_assert(bwd::QC == 32, "one copy instruction moves a chunk's LSE and D, one a mask tile");
 }  // namespace dkv
 
+// HANDOFF: also store dS^T for the fragment-reading dQ kernel (the workspace
+// holds them); without it dQ is recomputed by attn_bwd_dq_recompute_kernel.
+template <bool HANDOFF>
 __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws, const uint64_t* __restrict__ bits,
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     bool have = false;
     for (int it = 0; e0 >= 0; ++it) {
       lds_barrier();  // chunk e0 visible (B waited for its copies); B is done with P/dS buffer it&1
-      if (have) {  // streamed: read once, by the dQ kernel
+      if (HANDOFF && have) {  // streamed: read once, by the dQ kernel
         __builtin_nontemporal_store(pend[0], pfr);
         __builtin_nontemporal_store(pend[1], pfr + 64);
         have = false;
@@ -341,7 +346,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       e1 = e2;
       e2 = e3;
     }
-    if (have) {
+    if (HANDOFF && have) {
       __builtin_nontemporal_store(pend[0], pfr);
       __builtin_nontemporal_store(pend[1], pfr + 64);
     }
@@ -590,6 +595,192 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// dQ, query-major, recomputing dS (no handoff): for shapes whose dS tiles would
+// not fit the workspace. Workgroup = (b, h, 256 queries), 8 waves (two per
+// SIMD) of 32 queries. Q and dO of the lane's query stay in VGPRs; K and V
+// tiles are double buffered in natural layout. Per 32-key half of a tile it
+// forms S^T = K Q^T and dP^T = V dO^T, then P = exp2(S^T scale log2e - LSE2)
+// on the kept pairs and dS = P (dP - D), and accumulates dQ^T += K^T dS^T.
+// Every operation and its order match the key-major kernel's A role and the
+// fragment-reading dQ kernel, so the result is the same as with the handoff
+// (halves that kernel skips contribute exact zeros here).
+// ---------------------------------------------------------------------------
+namespace dqr {
+constexpr int NW = 8, QW = 32 * NW;
+constexpr int KSL = bwd::DQK / 8 + 1, VSL = bwd::DV / 8 + 1;  // 16-byte slots per padded row
+constexpr int KP = KSL * 8, VP = VSL * 8;                     // pitches (elements)
+constexpr int KBLK = bwd::TK * KSL / 64, VBLK = bwd::TK * VSL / 64;  // 1 KB blocks per tile
+constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;  // blocks per wave
+static_assert(bwd::TK * KSL % 64 == 0 && bwd::TK * VSL % 64 == 0, "tiles must be whole 1 KB blocks");
+}  // namespace dqr
+
+__global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ ws, const uint64_t* __restrict__ bits,
+    const uint8_t* __restrict__ cls, int B, int S, int H, float scale, float scale_log2,
+    uint16_t* __restrict__ dq) {
+  using namespace bwd;
+  using dqr::NW;
+  using dqr::QW;
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * dqr::KP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smV[2][TK * dqr::VP];
+  __shared__ uint8_t scls[2][kMaxTiles];  // tile classes of the workgroup's two 128-query tiles
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
+  const int half = lane >> 5, col = lane & 31;
+  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int NQW = (S + QW - 1) / QW;
+  int bh, qw;
+  grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
+  const int b = bh / H, h = bh % H;
+  const int tq = qw * QW + wid * 32 + col;  // this lane's query
+  const bool qvalid = tq < S;
+  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
+  const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
+  const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
+  const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
+  const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
+
+  u32x4 qf[DQK / 16], of[DV / 16];
+#pragma unroll
+  for (int ks = 0; ks < DQK / 16; ++ks) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (qvalid) z = *(const u32x4*)(q + ((size_t)b * S + tq) * rs_qk + (size_t)h * DQK + ks * 16 + 8 * half);
+    qf[ks] = z;
+  }
+#pragma unroll
+  for (int ks = 0; ks < DV / 16; ++ks) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (qvalid) z = *(const u32x4*)(dout + ((size_t)b * S + tq) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
+    of[ks] = z;
+  }
+  // D and the base-2 LSE of the lane's query, from the prologue's workspace
+  const size_t qi = ((size_t)b * H + h) * S + (qvalid ? tq : 0);
+  const float Dq = qvalid ? ws[qi] : 0.f;
+  const float Lq = qvalid ? ws[(size_t)B * H * S + qi] : 0.f;
+
+  f32x16 dqacc[DQK / 32];
+#pragma unroll
+  for (int i = 0; i < DQK / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dqacc[i][j] = 0.f;
+
+  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
+  stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
+  const uint8_t* cls0 = scls[0];
+  const uint8_t* cls1 = scls[1];
+  const uint8_t* clsw = scls[qt_w - qt0];
+  const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
+  auto next_tile = [&](int kt) {
+    int n = kt + 1;
+    while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
+    return n;
+  };
+  // this wave's 1 KB blocks of a tile; pad slots copy a harmless chunk and rows
+  // past S copy row S-1
+  auto issue = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < dqr::KI; ++i) {
+      const int j = wid + i * NW;
+      if (j < dqr::KBLK) {
+        const int slot = j * 64 + lane, row = slot / dqr::KSL, c = min(slot % dqr::KSL, dqr::KSL - 2);
+        const int s = min(kt * TK + row, S - 1);
+        g2lds16(kbase + (size_t)s * rs_qk + c * 8, (char*)smK[buf] + j * 1024);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < dqr::VI; ++i) {
+      const int j = wid + i * NW;
+      if (j < dqr::VBLK) {
+        const int slot = j * 64 + lane, row = slot / dqr::VSL, c = min(slot % dqr::VSL, dqr::VSL - 2);
+        const int s = min(kt * TK + row, S - 1);
+        g2lds16(vbase + (size_t)s * rs_v + c * 8, (char*)smV[buf] + j * 1024);
+      }
+    }
+  };
+  // this lane's selection word of tile kt (FULL: all ones; EMPTY: none)
+  auto word = [&](int kt) -> uint64_t {
+    const int c = clsw[kt];
+    if (!qvalid || c == 0) return 0ull;
+    return c == 2 ? ~0ull : bits_q[kt];
+  };
+
+  __syncthreads();  // class rows staged
+  int kt = next_tile(-1);
+  if (kt <= kt_last) issue(kt, 0);
+  uint64_t mw = kt <= kt_last ? word(kt) : 0ull;
+  int buf = 0;
+  while (kt <= kt_last) {
+    const int kn = next_tile(kt);
+    wait_vmem();
+    __syncthreads();  // tile kt visible in `buf`; every wave is done with the other buffer
+    const uint64_t mw_n = kn <= kt_last ? word(kn) : 0ull;
+    if (kn <= kt_last) issue(kn, buf ^ 1);
+    if (__ballot(mw != 0ull)) {
+      const uint16_t* sK = smK[buf];
+      const uint16_t* sV = smV[buf];
+      // this lane's keys are kb*32 + 8i + 4*half + r: the word pre-shifted by 4*half
+      const uint64_t mwh = mw >> (4 * half);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t Wq = (uint32_t)(mwh >> (32 * kb));
+        f32x16 sacc, dpacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
+#pragma unroll
+        for (int ks = 0; ks < DQK / 16; ++ks)
+          sacc = mfma32(*(const u32x4*)(sK + (kb * 32 + col) * dqr::KP + ks * 16 + 8 * half), qf[ks], sacc);
+#pragma unroll
+        for (int ks = 0; ks < DV / 16; ++ks)
+          dpacc = mfma32(*(const u32x4*)(sV + (kb * 32 + col) * dqr::VP + ks * 16 + 8 * half), of[ks], dpacc);
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+          float ds[8];
+#pragma unroll
+          for (int c8 = 0; c8 < 8; ++c8) {
+            const int r = 8 * p2 + c8;
+            const int keep = __builtin_amdgcn_sbfe((int)Wq, 8 * (r >> 2) + (r & 3), 1);
+            const float pr = __int_as_float(keep & __float_as_int(fast_exp2(fmaf(sacc[r], scale_log2, -Lq))));
+            ds[c8] = pr * (dpacc[r] - Dq);
+          }
+          const u32x4 db = pack8(ds);
+          const int r0 = kb * 32 + 16 * p2 + 4 * half;
+#pragma unroll
+          for (int i = 0; i < DQK / 32; ++i)
+            dqacc[i] = mfma32(lds_tr_frag(sK, dqr::KP, r0, r0 + 8, i * 32), db, dqacc[i]);
+        }
+      }
+    }
+    mw = mw_n;
+    buf ^= 1;
+    kt = kn;
+  }
+  if (qvalid) {
+    uint16_t* dqrow = dq + ((size_t)b * S + tq) * rs_qk + (size_t)h * DQK;
+#pragma unroll
+    for (int i = 0; i < DQK / 32; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = i * 32 + 8 * g + 4 * half;
+        *(u32x2*)(dqrow + d) = u32x2{pack_bf2(dqacc[i][4 * g] * scale, dqacc[i][4 * g + 1] * scale),
+                                     pack_bf2(dqacc[i][4 * g + 2] * scale, dqacc[i][4 * g + 3] * scale)};
+      }
+  }
+}
+
+hipError_t launch_attn_bwd_dq_recompute(const void* q, const void* k, const void* v, const void* dout,
+                                        const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
+                                        int H, float scale, void* dq, hipStream_t st) {
+  const size_t nq = (size_t)((S + dqr::QW - 1) / dqr::QW) * B * H;
+  hipLaunchKernelGGL(attn_bwd_dq_recompute_kernel, dim3((unsigned)nq), dim3(dqr::NW * 64), 0, st,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits,
+                     cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dq);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int H,
                                    float scale, void* dq, hipStream_t st) {
   const size_t nq = (size_t)((S + dqk::QW - 1) / dqk::QW) * B * H;
@@ -602,9 +793,15 @@ hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v
                                      const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
                                      int H, float scale, void* dk, void* dv, void* dsf, hipStream_t st) {
   const size_t nkv = (size_t)((S + 127) / 128) * B * H;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits, cls, B, S, H,
-                     scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv, (u32x4*)dsf);
+  if (dsf)
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits,
+                       cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv,
+                       (u32x4*)dsf);
+  else
+    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits,
+                       cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv, nullptr);
   return hipGetLastError();
 }
 

@@ -60,6 +60,11 @@ hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* 
                                       int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dk,
                                       void* dv, hipStream_t st);
 // backward, query-major: dq from the dS^T fragments of the key-major kernel
+// (which then gets a non-null dsf), or with dS recomputed from q, k, v, dout
+// and the workspace's D and base-2 LSE (key-major kernel given dsf = nullptr)
+hipError_t launch_attn_bwd_dq_recompute(const void* q, const void* k, const void* v, const void* dout,
+                                        const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
+                                        int H, float scale, void* dq, hipStream_t st);
 hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int H,
                                    float scale, void* dq, hipStream_t st);
 hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,

@@ -22,7 +22,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
           4: "DSA_ERR_HIP"}
 
 EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
-           "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes",
+           "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -59,13 +59,16 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, sz, vp]
         for f in ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
-                  "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq",
+                  "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep",
+                  "dsa_sparse_attn_bwd_dq",
                   "dsa_sparse_attn_bwd_dkdv"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_mask_bytes.argtypes = [i32, i32]
         L.dsa_mask_bytes.restype = sz
-        L.dsa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        L.dsa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.dsa_bwd_workspace_bytes.restype = sz
+        L.dsa_bwd_workspace_min_bytes.argtypes = [i32, i32, i32]
+        L.dsa_bwd_workspace_min_bytes.restype = sz
         L.dsa_status_string.argtypes = [i32]
         L.dsa_status_string.restype = ctypes.c_char_p
         L.dsa_last_error.argtypes = []
@@ -95,12 +98,14 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _dt(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dt(t) -> int:
+    """DSA dtype code of a tensor or a torch dtype."""
+    d = t if isinstance(t, torch.dtype) else t.dtype
+    if d == torch.bfloat16:
         return DSA_BF16
-    if t.dtype == torch.float32:
+    if d == torch.float32:
         return DSA_FP32
-    raise ValueError(f"unsupported dtype {t.dtype}")
+    raise ValueError(f"unsupported dtype {d}")
 
 
 # ------------------------------------------------------------------ sizes
@@ -108,8 +113,12 @@ def dsa_mask_bytes(B: int, S: int) -> int:
     return int(lib().dsa_mask_bytes(B, S))
 
 
-def dsa_bwd_workspace_bytes(B: int, S: int, H: int, Dqk: int, Dv: int) -> int:
-    return int(lib().dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv))
+def dsa_bwd_workspace_bytes(B: int, S: int, H: int, Dqk: int, Dv: int, dtype=torch.bfloat16) -> int:
+    return int(lib().dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv, _dt(dtype)))
+
+
+def dsa_bwd_workspace_min_bytes(B: int, S: int, H: int) -> int:
+    return int(lib().dsa_bwd_workspace_min_bytes(B, S, H))
 
 
 def mask_views(mask: torch.Tensor, B: int, S: int):

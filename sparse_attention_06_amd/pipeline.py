@@ -37,7 +37,7 @@ class DSAPath:
             self.dq = torch.empty((B, S, H, Dqk), dtype=dtype, device=device)
             self.dk = torch.empty((B, S, H, Dqk), dtype=dtype, device=device)
             self.dv = torch.empty((B, S, H, Dv), dtype=dtype, device=device)
-            nbytes = dsa.dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv)
+            nbytes = dsa.dsa_bwd_workspace_bytes(B, S, H, Dqk, Dv, dtype)
             self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
 
     def select(self, q_idx, k_idx, w, seg=None):

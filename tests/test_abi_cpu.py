@@ -5,6 +5,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from sparse_attention_06_amd import dsa
 
@@ -38,12 +39,23 @@ def test_sizes_and_strings():
     W = (S + 63) // 64
     assert dsa.dsa_mask_bytes(B, S) == B * S * W * 8 + B * ((S + 127) // 128) * ((S + 63) // 64)
     assert dsa.dsa_mask_bytes(0, 5) == 0
-    # D and base-2 LSE; for the MFMA dims also the dS tiles, from a 256-byte
-    # boundary: each 32-query chunk c of a (b, h) holds key tiles 0..c//2, 4 KB each
-    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 64, 64) == 2 * (2 * 3 * 100 * 4)
-    tiles = sum(c // 2 + 1 for c in range((100 + 31) // 32))
+    # D and base-2 LSE, rounded to 256 bytes; for the bf16 MFMA dims also the
+    # dS tiles: each 32-query chunk c of a (b, h) holds key tiles 0..c//2, 4 KB each
     off = -(-(2 * 2 * 3 * 100 * 4) // 256) * 256
+    assert dsa.dsa_bwd_workspace_min_bytes(2, 100, 3) == off
+    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 64, 64) == off
+    assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 192, 128, torch.float32) == off   # plain path: no tiles
+    tiles = sum(c // 2 + 1 for c in range((100 + 31) // 32))
     assert dsa.dsa_bwd_workspace_bytes(2, 100, 3, 192, 128) == off + 2 * 3 * tiles * 4096
+    # the dS handoff is capped at 16 GiB: past it the recommended size is the
+    # minimum (dQ recomputes dS), so memory stays linear in S
+    cap = 16 << 30
+    for B, S, H in ((12, 4096, 16), (4, 8192, 32), (1, 32768, 128), (1, 131072, 128)):
+        t = sum(c // 2 + 1 for c in range((S + 31) // 32)) * 4096 * B * H
+        want = dsa.dsa_bwd_workspace_min_bytes(B, S, H) + (t if t <= cap else 0)
+        assert dsa.dsa_bwd_workspace_bytes(B, S, H, 192, 128) == want
+    assert dsa.dsa_bwd_workspace_bytes(1, 32768, 128, 192, 128) == 8 * 32768 * 128
+    assert dsa.dsa_bwd_workspace_min_bytes(0, 5, 1) == 0
     assert L.dsa_status_string(0) == b"DSA_OK"
     assert L.dsa_status_string(3) == b"DSA_ERR_WORKSPACE"
     assert L.dsa_version() >= 100
@@ -133,7 +145,8 @@ def test_attention_rejects():
     assert fwd(P, P, P, P, 1, 64, 2, 512, 128, f32(0.1), 0, P, P, S_) == 2           # dim > 256
     assert fwd(P, P, P, P, 1, 64, 2, 100, 128, f32(0.1), 0, P, P, S_) == 2           # bf16 dim % 8
     bwd = L.dsa_sparse_attn_bwd
-    need = dsa.dsa_bwd_workspace_bytes(1, 64, 2, 192, 128)
+    need = dsa.dsa_bwd_workspace_min_bytes(1, 64, 2)
     assert bwd(P, P, P, P, P, P, P, 1, 64, 2, 192, 128, f32(0.1), 0, P, P, P, P, need - 4, S_) == 3
     assert b"workspace" in L.dsa_last_error()
     assert bwd(P, P, P, P, P, P, P, 1, 64, 2, 192, 128, f32(0.1), 0, P, P, MIS, P, need, S_) == 1
+

@@ -24,7 +24,7 @@ pytestmark = [pytest.mark.gpu,
 DEV = "cuda"
 
 
-def _rows(S, K, seed, n_rand=12):
+def _rows(S, K, seed, n_rand=64):
     rng = np.random.default_rng(seed)
     r = set(range(8)) | set(range(S - 8, S)) | {K - 2, K - 1, K, K + 1}
     r |= set(rng.integers(0, S, n_rand).tolist())
