@@ -31,6 +31,15 @@ Sources (page title · section):
         indexer section at the end states the readings of that format).
   [P3o] same page · item 1, Indexer: partial RoPE on the indexer's q and k,
         concatenated layout (the RoPE section at the end states the readings).
+  [P2l] "Support Ring Attention with DeepSeek DSA Sparse Indexer" · "Isolated
+        Flax NNX Auxiliary Loss" and "Loss Harvesting & Objective Injection":
+        an indexer loss is added to the training objective, and its gradient
+        reaches the indexer's query and key projections.
+  [P5t] "Implement QK attention head chunking for CSA [Deepseek v4]" · the
+        review of calculate_csa_indexer_loss: the teacher is a float32 softmax
+        of the attention scores, zeroed on invalid tokens and summed over
+        heads; the teacher's inputs carry no gradient (the KL section at the
+        end states the readings).
 
 The indexer formula is not printed on the pages. It is the standard one of
 the method: I[t,s] = sum_j w[t,j] * ReLU(q_idx[t,j,:] . k_idx[s,:]), with a
@@ -577,3 +586,123 @@ def index_scores_fp8_bound_rows(q8_rows, q_scale_rows, k8, k_scale, w_rows, rel:
     (same layout as index_scores_fp8_rows)."""
     R = np.asarray(q8_rows).shape[1]
     return index_scores_fp8_bound(q8_rows, q_scale_rows, k8, k_scale, w_rows, np.arange(R), rel)
+
+
+# ----------------------------------------------------------------------------
+# next row: the indexer's KL auxiliary loss and its gradient     [P2l], [P5t]
+# ----------------------------------------------------------------------------
+# [P2l] says the indexer loss joins the objective and trains the indexer's q/k
+# projections; [P5t] prints the teacher: a float32 softmax of attention
+# scores, masked to valid tokens, summed over heads, with stop-gradient
+# inputs. The pages print neither the student nor the divergence. Readings:
+#   * kept(t): the sorted kept keys of row t (its index list, intersected with
+#     valid(t), as the attention uses it);
+#   * teacher p_t(s) = sum_h P_h(t,s) / sum_s' sum_h P_h(t,s') over s in
+#     kept(t), where P_h is head h's attention probability over kept(t) (the
+#     forward's P). Each P_h sums to 1, so p_t is the mean over heads of P_h.
+#     It carries no gradient;
+#   * student q_t(s) = softmax over s in kept(t) of I[t,s] (the indexer score);
+#   * loss = (1/N) sum_t KL(p_t || q_t) = (1/N) sum_t sum_s p log(p / q) with
+#     0 log 0 = 0, over the N rows with a non-empty kept(t);
+#   * gradient: dloss/dI[t,s] = (q_t(s) - p_t(s)) / N on kept pairs, 0 else;
+#     through I = sum_j w_j ReLU(u_j), u_j = q_idx[t,j] . k_idx[s], with
+#     ReLU'(0) = 0, it reaches q_idx, k_idx and w.
+def _kept_keys(idx_row, seg_b, S: int, t: int) -> np.ndarray:
+    """kept(t) ascending: the index list intersected with valid(t)."""
+    sel = np.asarray(idx_row)
+    sel = sel[(sel >= 0) & (sel < S)]
+    ok = valid_row(seg_b, S, t)
+    return np.unique(sel[ok[sel]])
+
+
+def indexer_teacher(q, k, idx, seg, scale: float, rows) -> np.ndarray:
+    """Teacher distribution of each row over its kept keys, [B, len(rows), K]:
+    entry i is p_t at the i-th smallest kept key (i < |kept(t)|), 0 after.
+    q, k [B, S, H, Dqk]; idx [B, len(rows), K]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    B, S, H, _ = q.shape
+    K = np.asarray(idx).shape[-1]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((B, rows.size, K))
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            ks = _kept_keys(idx[b, r], seg_b, S, int(t))
+            if ks.size == 0:
+                continue
+            acc = np.zeros(ks.size)
+            for h in range(H):
+                logit = scale * (k[b, ks, h] @ q[b, t, h])
+                e = np.exp(logit - logit.max())
+                acc += e / e.sum()                           # P_h over kept(t)
+            out[b, r, : ks.size] = acc / acc.sum()
+    return out
+
+
+def indexer_kl(scores, teacher, idx, seg, rows, S: int, n_norm=None):
+    """Student softmax, KL divergence and its gradient w.r.t. the scores.
+
+    scores [B, len(rows), S] (the indexer scores of the rows), teacher as
+    indexer_teacher returns it, idx [B, len(rows), K]. n_norm is N (default:
+    the number of non-empty rows among `rows`). Returns
+      row_kl [B, len(rows)]  KL(p_t || q_t) (0 for empty rows),
+      loss                   sum of row_kl / N,
+      dscores [B, len(rows), S]  (q - p) / N on kept pairs, 0 elsewhere.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    teacher = np.asarray(teacher, dtype=np.float64)
+    B = scores.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    row_kl = np.zeros((B, rows.size))
+    dscores = np.zeros((B, rows.size, S))
+    kept_rows = []
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            ks = _kept_keys(idx[b, r], seg_b, S, int(t))
+            if ks.size == 0:
+                continue
+            x = scores[b, r, ks]
+            m = x.max()
+            logq = x - m - np.log(np.exp(x - m).sum())
+            p = teacher[b, r, : ks.size]
+            pos = p > 0
+            row_kl[b, r] = np.sum(p[pos] * (np.log(p[pos]) - logq[pos]))
+            kept_rows.append((b, r, ks, np.exp(logq), p))
+    N = len(kept_rows) if n_norm is None else int(n_norm)
+    for b, r, ks, qd, p in kept_rows:
+        dscores[b, r, ks] = (qd - p) / N
+    loss = row_kl.sum() / N if N else 0.0
+    return row_kl, loss, dscores
+
+
+def indexer_bwd(q_idx, k_idx, w, dscores, seg, rows):
+    """Gradients of sum_{t,s} dscores[t,s] * I[t,s] w.r.t. the indexer inputs,
+    for the given query rows (dscores [B, len(rows), S]; entries outside
+    valid(t) must be 0). Returns dq_idx [B, len(rows), Hi, Di],
+    dk_idx [B, S, Di] (the rows' contributions) and dw [B, len(rows), Hi]:
+      u_j = q_idx[t,j] . k_idx[s],  dw[t,j] += g ReLU(u_j),
+      dq_idx[t,j] += g w[t,j] [u_j > 0] k_idx[s],
+      dk_idx[s]   += sum_j g w[t,j] [u_j > 0] q_idx[t,j].
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    k_idx = np.asarray(k_idx, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dscores = np.asarray(dscores, dtype=np.float64)
+    B, S, Hi, Di = q_idx.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((B, rows.size, Hi, Di))
+    dk = np.zeros((B, S, Di))
+    dw = np.zeros((B, rows.size, Hi))
+    for b in range(B):
+        seg_b = None if seg is None else np.asarray(seg)[b]
+        for r, t in enumerate(rows):
+            vs = np.nonzero(valid_row(seg_b, S, int(t)))[0]
+            g = dscores[b, r, vs]                            # [n]
+            u = q_idx[b, t] @ k_idx[b, vs].T                 # [Hi, n]
+            G = g[None, :] * w[b, t][:, None] * (u > 0)      # dI/du_j times g
+            dw[b, r] = (np.maximum(u, 0.0) * g[None, :]).sum(axis=1)
+            dq[b, r] = G @ k_idx[b, vs]
+            dk[b, vs] += G.T @ q_idx[b, t]
+    return dq, dk, dw

@@ -838,3 +838,205 @@ def test_fp8_bound_planted_mistakes_fail_a_pin(monkeypatch):
         with pytest.raises(AssertionError):
             test_fp8_bound_covers_coarse_accumulation_and_is_tight()
         monkeypatch.undo()
+
+
+# ------------------------------------------------ indexer KL loss pins
+# oracle.indexer_teacher / indexer_kl / indexer_bwd (the auxiliary loss of
+# "Support Ring Attention with DeepSeek DSA Sparse Indexer", Loss Harvesting,
+# with the teacher of "Implement QK attention head chunking for CSA
+# [Deepseek v4]", review of calculate_csa_indexer_loss).
+def _kl_case(seed=41, B=2, S=11, K=5, H=3, seg=True):
+    d = _tiny(B=B, S=S, H=H, seed=seed, seg=seg)
+    d["idx"] = inputs.random_index_sets(B, S, K, d["seg"], seed=seed)
+    d["idx"][0, 6] = -1                                    # an empty row
+    return d
+
+
+def test_indexer_teacher_brute_force_and_attention_probabilities():
+    d = _kl_case()
+    B, S, H = d["q"].shape[:3]
+    scale = 0.37
+    rows = np.arange(S)
+    p = ref.indexer_teacher(d["q"], d["k"], d["idx"], d["seg"], scale, rows)
+    for b in range(B):
+        for t in range(S):
+            kept = sorted(set(int(s) for s in d["idx"][b, t] if s >= 0 and s <= t and
+                              d["seg"][b, s] == d["seg"][b, t]))
+            if not kept:
+                assert not p[b, t].any()
+                continue
+            tot = [0.0] * len(kept)
+            for h in range(H):
+                lg = [scale * math.fsum(d["q"][b, t, h, e] * d["k"][b, s, h, e] for e in range(d["q"].shape[-1]))
+                      for s in kept]
+                m = max(lg)
+                z = math.fsum(math.exp(x - m) for x in lg)
+                for i, x in enumerate(lg):
+                    tot[i] += math.exp(x - m) / z
+            zz = math.fsum(tot)                                # summed over heads, then normalised
+            for i in range(len(kept)):
+                assert abs(p[b, t, i] - tot[i] / zz) <= 1e-13
+            assert not p[b, t, len(kept):].any()
+    # one head: the teacher is that head's attention probability exp(logit - LSE)
+    q1, k1 = d["q"][:, :, :1], d["k"][:, :, :1]
+    p1 = ref.indexer_teacher(q1, k1, d["idx"], d["seg"], scale, rows)
+    _, L = ref.attention_fwd(q1, k1, d["v"][:, :, :1], d["idx"], d["seg"], scale, rows)
+    b, t = 1, 9
+    kept = ref._kept(d["idx"][b, t], d["seg"][b], S, t)
+    want = np.exp(scale * (k1[b, kept, 0] @ q1[b, t, 0]) - L[b, 0, t])
+    np.testing.assert_allclose(p1[b, t, : kept.size], want, rtol=1e-12)
+    # invariant to the order of the heads
+    perm = np.array([2, 0, 1])
+    np.testing.assert_allclose(ref.indexer_teacher(d["q"][:, :, perm], d["k"][:, :, perm], d["idx"], d["seg"],
+                                                   scale, rows), p, rtol=1e-13, atol=1e-15)
+
+
+def test_indexer_kl_hand_fixture():
+    # two kept keys, teacher (1/2, 1/2), scores (0, ln 3): student (1/4, 3/4),
+    # KL = ln 2 / 2 + ln(2/3) / 2 = ln(4/3) / 2, gradient (q - p) / N = (-1/4, 1/4)
+    # row 0 keeps only key 0 (KL 0), row 1 is empty, row 2 keeps keys 0 and 2
+    S = 3
+    idx = np.array([[[0, -1], [-1, -1], [0, 2]]], dtype=np.int32)
+    scores = np.full((1, S, S), -np.inf)
+    scores[0, 0, 0] = 0.0
+    scores[0, 2, 0], scores[0, 2, 2] = 0.0, math.log(3.0)
+    teacher = np.array([[[1.0, 0], [0, 0], [0.5, 0.5]]])
+    row_kl, loss, ds = ref.indexer_kl(scores, teacher, idx, None, np.arange(S), S)
+    assert row_kl[0, 0] == 0.0 and row_kl[0, 1] == 0.0
+    assert abs(row_kl[0, 2] - 0.5 * math.log(4.0 / 3.0)) < 1e-15
+    assert abs(loss - 0.25 * math.log(4.0 / 3.0)) < 1e-15            # N = 2 non-empty rows
+    np.testing.assert_allclose(ds[0, 2], [-0.125, 0.0, 0.125], atol=1e-16)
+    np.testing.assert_allclose(ds[0, 0], [0.0, 0.0, 0.0], atol=1e-16)  # one key: q = p = 1
+
+
+def _dense_student_torch(scores, idx, seg, S):
+    """Kept-key masks as a dense [B, S, S] bool array."""
+    B = scores.shape[0]
+    m = np.zeros((B, S, S), bool)
+    for b in range(B):
+        for t in range(S):
+            kept = ref._kept(idx[b, t], None if seg is None else seg[b], S, t)
+            m[b, t, kept] = True
+    return m
+
+
+def test_indexer_kl_matches_torch_kl_div_and_autograd():
+    d = _kl_case()
+    B, S = d["q"].shape[:2]
+    rows = np.arange(S)
+    scores = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], d["seg"], rows)
+    teacher = ref.indexer_teacher(d["q"], d["k"], d["idx"], d["seg"], 0.5, rows)
+    row_kl, loss, ds = ref.indexer_kl(scores, teacher, d["idx"], d["seg"], rows, S)
+    mask = _dense_student_torch(scores, d["idx"], d["seg"], S)
+    x = torch.tensor(np.where(mask, scores, 0.0), dtype=torch.float64, requires_grad=True)
+    tm = torch.tensor(mask)
+    logq = torch.log_softmax(x.masked_fill(~tm, -math.inf), dim=-1)
+    # teacher scattered to key positions
+    pd = np.zeros((B, S, S))
+    for b in range(B):
+        for t in range(S):
+            kept = np.nonzero(mask[b, t])[0]
+            pd[b, t, kept] = teacher[b, t, : kept.size]
+    P = torch.tensor(pd)
+    nonempty = tm.any(dim=-1)
+    per_row = torch.stack([torch.nn.functional.kl_div(logq[b, t][tm[b, t]], P[b, t][tm[b, t]], reduction="sum")
+                           if nonempty[b, t] else torch.zeros((), dtype=torch.float64)
+                           for b in range(B) for t in range(S)]).view(B, S)
+    np.testing.assert_allclose(row_kl, per_row.detach().numpy(), rtol=1e-12, atol=1e-15)
+    tl = per_row.sum() / nonempty.sum()
+    assert abs(loss - tl.item()) < 1e-14
+    tl.backward()
+    np.testing.assert_allclose(ds, np.where(mask, x.grad.numpy(), 0.0), rtol=1e-10, atol=1e-15)
+    assert np.all(row_kl >= -1e-15)
+    # a student equal to the teacher (scores = log p + const) has zero loss and gradient
+    same = np.where(mask, np.log(np.maximum(pd, 1e-300)) + 3.0, -np.inf)
+    rk, l0, g0 = ref.indexer_kl(same, teacher, d["idx"], d["seg"], rows, S)
+    assert abs(l0) < 1e-13 and np.abs(g0).max() < 1e-13
+
+
+def test_indexer_bwd_matches_autograd_and_finite_differences():
+    d = _kl_case(seed=43)
+    B, S, Hi, Di = d["q_idx"].shape
+    rows = np.arange(S)
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal((B, S, S))
+    for b in range(B):
+        for t in range(S):
+            g[b, t, ~ref.valid_row(d["seg"][b], S, t)] = 0.0
+    dq, dk, dw = ref.indexer_bwd(d["q_idx"], d["k_idx"], d["w"], g, d["seg"], rows)
+    # torch float64 autograd of sum(g * I) through a dense masked indexer
+    q = torch.tensor(d["q_idx"], requires_grad=True)
+    k = torch.tensor(d["k_idx"], requires_grad=True)
+    w = torch.tensor(d["w"], requires_grad=True)
+    u = torch.einsum("btjd,bsd->btjs", q, k)
+    I = (w[..., None] * torch.relu(u)).sum(dim=2)                      # [B, S, S]
+    (torch.tensor(g) * I).sum().backward()
+    np.testing.assert_allclose(dq, q.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dk, k.grad.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dw, w.grad.numpy(), rtol=1e-11, atol=1e-13)
+    # end to end: the loss as a function of the indexer inputs (teacher and
+    # kept sets fixed), central finite differences against the chain rule
+    teacher = ref.indexer_teacher(d["q"], d["k"], d["idx"], d["seg"], 0.5, rows)
+
+    def loss_of(qi, ki, wi):
+        sc = ref.index_scores(qi, ki, wi, d["seg"], rows)
+        return ref.indexer_kl(sc, teacher, d["idx"], d["seg"], rows, S)[1]
+
+    sc = ref.index_scores(d["q_idx"], d["k_idx"], d["w"], d["seg"], rows)
+    _, _, ds = ref.indexer_kl(sc, teacher, d["idx"], d["seg"], rows, S)
+    gq, gk, gw = ref.indexer_bwd(d["q_idx"], d["k_idx"], d["w"], ds, d["seg"], rows)
+    h = 1e-6
+    for arr, grad, pick in ((d["q_idx"], gq, (1, 7, 2, 3)), (d["k_idx"], gk, (0, 2, 4)), (d["w"], gw, (1, 8, 1)),
+                            (d["q_idx"], gq, (0, 3, 0, 1)), (d["k_idx"], gk, (1, 5, 0))):
+        xp, xm = arr.copy(), arr.copy()
+        xp[pick] += h
+        xm[pick] -= h
+        args_p = [xp if arr is a else a for a in (d["q_idx"], d["k_idx"], d["w"])]
+        args_m = [xm if arr is a else a for a in (d["q_idx"], d["k_idx"], d["w"])]
+        fd = (loss_of(*args_p) - loss_of(*args_m)) / (2 * h)
+        assert abs(fd - grad[pick]) <= 1e-7 * (1 + abs(fd)), (pick, fd, grad[pick])
+
+
+def test_indexer_kl_planted_mistakes_fail_a_pin(monkeypatch):
+    orig_t, orig_kl, orig_bwd = ref.indexer_teacher, ref.indexer_kl, ref.indexer_bwd
+
+    def teacher_unnormalised(q, k, idx, seg, scale, rows):        # heads summed, not normalised
+        return orig_t(q, k, idx, seg, scale, rows) * q.shape[2]
+
+    def kl_reversed(scores, teacher, idx, seg, rows, S, n_norm=None):   # KL(q || p)
+        scores = np.asarray(scores, np.float64)
+        row_kl, loss, ds = orig_kl(scores, teacher, idx, seg, rows, S, n_norm)
+        out = np.zeros_like(row_kl)
+        for b in range(scores.shape[0]):
+            for r, t in enumerate(rows):
+                ks = ref._kept(idx[b, r], None if seg is None else seg[b], S, int(t))
+                if ks.size:
+                    x = scores[b, r, ks]
+                    qd = np.exp(x - x.max()) / np.exp(x - x.max()).sum()
+                    p = np.maximum(teacher[b, r, : ks.size], 1e-300)
+                    out[b, r] = np.sum(qd * (np.log(qd) - np.log(p)))
+        return out, loss, ds
+
+    def grad_sign(scores, teacher, idx, seg, rows, S, n_norm=None):     # (p - q) / N
+        row_kl, loss, ds = orig_kl(scores, teacher, idx, seg, rows, S, n_norm)
+        return row_kl, loss, -ds
+
+    def bwd_no_w(q_idx, k_idx, w, dscores, seg, rows):               # w dropped from dq
+        dq, dk, dw = orig_bwd(q_idx, k_idx, np.ones_like(w), dscores, seg, rows)
+        return dq, orig_bwd(q_idx, k_idx, w, dscores, seg, rows)[1], dw
+
+    def bwd_dw_linear(q_idx, k_idx, w, dscores, seg, rows):          # u instead of ReLU(u) in dw
+        dq, dk, dw = orig_bwd(q_idx, k_idx, w, dscores, seg, rows)
+        _, _, dwn = orig_bwd(-np.asarray(q_idx), k_idx, w, dscores, seg, rows)
+        return dq, dk, dw - dwn
+
+    for name, bad, test in (("indexer_teacher", teacher_unnormalised,
+                             test_indexer_teacher_brute_force_and_attention_probabilities),
+                            ("indexer_kl", kl_reversed, test_indexer_kl_matches_torch_kl_div_and_autograd),
+                            ("indexer_kl", grad_sign, test_indexer_kl_matches_torch_kl_div_and_autograd),
+                            ("indexer_bwd", bwd_no_w, test_indexer_bwd_matches_autograd_and_finite_differences),
+                            ("indexer_bwd", bwd_dw_linear, test_indexer_bwd_matches_autograd_and_finite_differences)):
+        monkeypatch.setattr(ref, name, bad)
+        with pytest.raises(AssertionError):
+            test()
+        monkeypatch.undo()
