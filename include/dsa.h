@@ -300,6 +300,28 @@ dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v,
 size_t dsa_bwd_workspace_min_bytes(int B, int S, int H);
 size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype);
 
+/* ---------------------------------------------------------------------------
+ * dsa_sparse_attn_bwd_noalloc -- dsa_sparse_attn_bwd with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments and results as dsa_sparse_attn_bwd, with the workspace replaced by
+ * a scratch array inside the library: DSA_NOALLOC_SCRATCH_BYTES (64 MiB) of
+ * device memory per GPU, held from the first call on that GPU until the
+ * process ends. It covers B*H*S <= 8 Mi (D and the base-2 LSE, 8 bytes per
+ * (b, h, t)); larger shapes return DSA_ERR_UNSUPPORTED before any HIP call.
+ * dQ always takes the recompute route (no dS handoff), so the gradients equal
+ * dsa_sparse_attn_bwd's. Nothing is allocated or freed. The scratch array is
+ * shared by every call on the same GPU and keeps the last call's contents
+ * (each call overwrites what it reads first), so calls that overlap in time on
+ * one GPU -- on different streams or host threads -- race and must be
+ * serialised by the caller. The stream must belong to the current device.
+ * ------------------------------------------------------------------------- */
+#define DSA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+dsa_status dsa_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                       const void* dout, const float* lse, const void* mask,
+                                       int B, int S, int H, int Dqk, int Dv, float softmax_scale,
+                                       dsa_dtype dtype, void* dq, void* dk, void* dv, void* stream);
+
 /* Human-readable name of a status code. Static storage. */
 const char* dsa_status_string(dsa_status s);
 /* Detail of the last non-OK return on this thread ("" if none). */

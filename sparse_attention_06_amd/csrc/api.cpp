@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/dsa.h"
 #include "launch.hpp"
@@ -376,5 +377,72 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
                                 workspace, workspace_bytes, stream);
 }
 
+
+// ---------------------------------------------------------------------------
+// Allocation-free backward: the workspace is a file-scope device array, one
+// copy per GPU, whose address is looked up once per device and kept.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device. In host code the array's
+// name is only a stand-in, so kernels and copies get this address instead.
+dsa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  REQ(dev >= 0 && dev < kMaxDevices, DSA_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    REQ(p != nullptr, DSA_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_sparse_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                       const void* dout, const float* lse, const void* mask, int B, int S,
+                                       int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype,
+                                       void* dq, void* dk, void* dv, void* stream) {
+  // every argument check comes before the first HIP call
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(v);
+  REQ_PTR(o);
+  REQ_PTR(dout);
+  REQ_PTR(lse);
+  REQ_PTR(mask);
+  REQ_PTR(dq);
+  REQ_PTR(dk);
+  REQ_PTR(dv);
+  dsa_status s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
+  if (s != DSA_OK) return s;
+  const size_t need = dsa_bwd_workspace_min_bytes(B, S, H);
+  REQ(need <= (size_t)DSA_NOALLOC_SCRATCH_BYTES, DSA_ERR_UNSUPPORTED,
+      "B*H*S = %lld needs %zu bytes of scratch; the allocation-free backward holds %llu "
+      "(B*H*S <= %llu); use dsa_sparse_attn_bwd with a workspace",
+      (long long)B * H * S, need, (unsigned long long)DSA_NOALLOC_SCRATCH_BYTES,
+      (unsigned long long)(DSA_NOALLOC_SCRATCH_BYTES / 8));
+  void* ws = nullptr;
+  s = scratch_of_current_device(&ws);
+  if (s != DSA_OK) return s;
+  // the minimum workspace: D and the base-2 LSE, both overwritten in full by
+  // the prologue, and the recompute route for dQ (no dS tiles)
+  return dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, B, S, H, Dqk, Dv, softmax_scale, dtype, dq, dk, dv, ws,
+                             need, stream);
+}
 
 }  // extern "C"

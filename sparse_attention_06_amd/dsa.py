@@ -22,7 +22,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
           4: "DSA_ERR_HIP"}
 
 EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
-           "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
+           "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -53,13 +53,15 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
         L.dsa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                           vp, vp, vp, vp, sz, vp]
+        L.dsa_sparse_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                                  i32, vp, vp, vp, vp]
         L.dsa_sparse_attn_bwd_prep.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.dsa_sparse_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                                vp, vp, vp, sz, vp]
         L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                              vp, vp, sz, vp]
         for f in ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
-                  "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_prep",
+                  "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep",
                   "dsa_sparse_attn_bwd_dq",
                   "dsa_sparse_attn_bwd_dkdv"):
             getattr(L, f).restype = ctypes.c_int
@@ -198,6 +200,17 @@ def dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, d
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
         float(softmax_scale), _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dsa_sparse_attn_bwd_noalloc(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, dk, dv,
+                                stream=None) -> None:
+    """dsa_sparse_attn_bwd with the library's own scratch array instead of a
+    workspace (allocates nothing; calls overlapping on one GPU race)."""
+    B, S, H, Dqk = q.shape
+    Dv = v.shape[-1]
+    _check("dsa_sparse_attn_bwd_noalloc", lib().dsa_sparse_attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
+        float(softmax_scale), _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
 
 
 def dsa_sparse_attn_bwd_prep(o, dout, lse, Dqk: int, workspace, stream=None) -> None:

@@ -150,3 +150,15 @@ def test_attention_rejects():
     assert b"workspace" in L.dsa_last_error()
     assert bwd(P, P, P, P, P, P, P, 1, 64, 2, 192, 128, f32(0.1), 0, P, P, MIS, P, need, S_) == 1
 
+
+def test_noalloc_backward_rejects_before_any_launch():
+    L = dsa.lib()
+    f32 = ctypes.c_float
+    na = L.dsa_sparse_attn_bwd_noalloc
+    assert na(P, P, P, P, P, P, NUL, 1, 64, 2, 192, 128, f32(0.1), 0, P, P, P, S_) == 1     # mask NULL
+    assert na(P, P, P, P, P, P, P, 1, 64, 2, 192, 128, f32(0.1), 0, P, MIS, P, S_) == 1     # misaligned dk
+    assert na(P, P, P, P, P, P, P, 1, 64, 2, 512, 128, f32(0.1), 0, P, P, P, S_) == 2       # dim > 256
+    # 8 bytes per (b, h, t) must fit the 64 MiB scratch: B*H*S <= 8 Mi
+    assert na(P, P, P, P, P, P, P, 1, 1 << 18, 33, 192, 128, f32(0.1), 0, P, P, P, S_) == 2
+    assert b"scratch" in L.dsa_last_error()
+    assert na(P, P, P, P, P, P, P, 2, 65536, 65, 192, 128, f32(0.1), 0, P, P, P, S_) == 2
