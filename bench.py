@@ -23,6 +23,8 @@ The same line also carries:
   * "selection": indexer + top-k at the 32K and 128K workloads, with the
     attention forward there (useful and executed-tile TFLOP/s);
   * "c1": the tiny fp32 workload's latency in microseconds;
+  * "indexer_loss": the indexer's KL auxiliary loss after the step (teacher,
+    student KL, indexer gradients), timed per call (not part of the step);
   * "roofline" for the dominant kernel, and "cpu_baseline" (the float64
     oracle on a bounded row sample).
 """
@@ -381,6 +383,39 @@ def attention_rate(cfg, wk, kernels):
     return flops / (sum(kernels[c]["ms"] for c in att) * 1e-3) / 1e12
 
 
+def time_indexer_loss(cfg, path, x, reps=3):
+    """The indexer's KL auxiliary loss after a step (teacher, student KL,
+    indexer gradients), each call timed with events; one warm-up call. The
+    score gradient overwrites the float32 scores in place."""
+    import torch
+    from sparse_attention_06_amd import dsa
+    B, S, K = cfg.B, cfg.S, cfg.K
+    dev = "cuda"
+    teacher = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+    row_kl = torch.empty((B, S), dtype=torch.float32, device=dev)
+    loss = torch.empty(2, dtype=torch.float32, device=dev)
+    dq_idx, dk_idx, dw = (torch.empty_like(x[n]) for n in ("q_idx", "k_idx", "w"))
+    dscores = path.scores if path.scores.dtype == torch.float32 else \
+        torch.empty((B, S, S), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    tt, tk, tb = [], [], []
+    for i in range(reps + 1):
+        ev[0].record(stream)
+        dsa.dsa_indexer_teacher(x["q"], x["k"], path.lse, path.mask, K, cfg.softmax_scale, teacher)
+        ev[1].record(stream)
+        dsa.dsa_indexer_kl(path.scores, path.idx, teacher, path.mask, row_kl, loss, dscores)
+        ev[2].record(stream)
+        dsa.dsa_indexer_bwd(x["q_idx"], x["k_idx"], x["w"], dscores, path.mask, dq_idx, dk_idx, dw)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if i:
+            tt.append(ev[0].elapsed_time(ev[1]))
+            tk.append(ev[1].elapsed_time(ev[2]))
+            tb.append(ev[2].elapsed_time(ev[3]))
+    return tt, tk, tb, float(loss[0].item())
+
+
 def tiny_latency(reps=50):
     """The tiny fp32 workload (indexer, top-k, forward): microseconds per call
     and per step, median over `reps` back-to-back steps."""
@@ -404,6 +439,7 @@ def main():
     ap.add_argument("--no-c4", action="store_true", help="skip the packed-document fwd+bwd workload")
     ap.add_argument("--no-c1", action="store_true", help="skip the tiny workload's latency")
     ap.add_argument("--no-scrub", action="store_true", help="do not overwrite 512 MB before each timed step")
+    ap.add_argument("--no-kl", action="store_true", help="skip timing the indexer KL auxiliary loss")
     ap.add_argument("--long-only", action="store_true",
                     help="only the 32K and 128K workloads (one JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -467,6 +503,20 @@ def main():
                                "topk": {"achieved": kernels["topk"]["achieved"], "unit": "GB/s",
                                         "frac": kernels["topk"]["frac"]}}}
     x_cpu = None if args.no_cpu else {k: (None if v is None else v.cpu()) for k, v in x.items()}
+    indexer_loss = None
+    if cfg.dtype == "bf16" and cfg.Hi == 64 and cfg.Di == 128 and not args.no_kl:
+        log("indexer KL auxiliary loss (teacher, KL, indexer backward)")
+        tt, tk, tb, lv = time_indexer_loss(cfg, path, x)
+        mt, mk, mb = (float(np.median(v)) for v in (tt, tk, tb))
+        t_fl = wk["selected"] * cfg.H * 2 * cfg.Dqk                   # P per head on kept pairs
+        b_fl = wk["selected"] * cfg.Hi * 4 * cfg.Di                   # dq_idx and dk_idx on kept pairs
+        indexer_loss = {
+            "loss": lv, "teacher_ms": mt, "kl_ms": mk, "indexer_bwd_ms": mb, "total_ms": mt + mk + mb,
+            "teacher": {"achieved": t_fl / (mt * 1e-3) / 1e12, "unit": "TFLOP/s",
+                        "frac": t_fl / (mt * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic": t_fl},
+            "indexer_bwd": {"achieved": b_fl / (mb * 1e-3) / 1e12, "unit": "TFLOP/s",
+                            "frac": b_fl / (mb * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic": b_fl}}
+        log(f"  teacher {mt:.3f} ms, kl {mk:.3f} ms, indexer bwd {mb:.3f} ms, loss {lv:.5f}")
     del path, x
     torch.cuda.empty_cache()
 
@@ -521,6 +571,7 @@ def main():
         "kernels": kernels,
         "c4": c4,
         "c1": c1,
+        "indexer_loss": indexer_loss,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

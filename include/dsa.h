@@ -301,6 +301,59 @@ size_t dsa_bwd_workspace_min_bytes(int B, int S, int H);
 size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype);
 
 /* ---------------------------------------------------------------------------
+ * The indexer's KL auxiliary loss and its gradient, three calls in this order.
+ * Sources: "Support Ring Attention with DeepSeek DSA Sparse Indexer", sections
+ * "Isolated Flax NNX Auxiliary Loss" and "Loss Harvesting & Objective
+ * Injection" (an indexer loss joins the training objective and trains the
+ * indexer's query/key projections); "Implement QK attention head chunking for
+ * CSA [Deepseek v4]", review of calculate_csa_indexer_loss (the teacher is a
+ * float32 softmax of the attention scores, zeroed on invalid tokens, summed
+ * over heads, with stop-gradient inputs). The pages give no student and no
+ * divergence; the definitions taken here, with kept(t) the row's kept keys:
+ *   teacher p_t(s) = (1/H) sum_h P_h(t,s), P_h head h's attention probability
+ *                    over kept(t) (the heads' sum, normalised); no gradient
+ *   student q_t(s) = softmax over kept(t) of I[t,s]
+ *   loss = (1/N) sum_t KL(p_t || q_t), 0 log 0 = 0, over the N rows with a
+ *          kept key;  dloss/dI[t,s] = (q_t(s) - p_t(s)) / N on kept pairs.
+ *
+ * dsa_indexer_teacher -- p_t over the kept keys, after dsa_sparse_attn_fwd.
+ *   q, k    [B,S,H,Dqk] bf16, Dqk in {64, 128, 192};  lse [B,H,S] from the forward
+ *   mask    the forward's mask
+ *   teacher [B,S,K] float32 out: entry i of row t is p_t at the i-th smallest
+ *           kept key (the i-th entry of dsa_topk's index list); 0 past them.
+ *
+ * dsa_indexer_kl -- student softmax, KL and the gradient w.r.t. the scores.
+ *   scores  [B,S,ld] score_dtype (as given to dsa_topk)
+ *   idx     [B,S,K] int32 from dsa_topk (ascending, -1 padded); teacher as above
+ *   row_kl  [B,S] float32 out: KL(p_t || q_t) (0 for an empty row)
+ *   loss    float32[2] out: {loss, N}
+ *   dscores [B,S,ld_ds] float32 out: row t over [0, t] gets (q - p)/N at kept
+ *           keys and 0 elsewhere; entries past t are untouched. With float32
+ *           scores and ld_ds == ld it may be the scores buffer itself.
+ * Deterministic: N is an integer count, and the loss sums row_kl in a fixed
+ * order in one workgroup.
+ *
+ * dsa_indexer_bwd -- gradients of sum_{t,s} dscores[t,s] I[t,s] w.r.t. the
+ * indexer inputs (with dscores from dsa_indexer_kl: of the loss):
+ *   dw[t,j]     = sum_s g ReLU(u_j),   u_j = q_idx[t,j] . k_idx[s]
+ *   dq_idx[t,j] = sum_s g w[t,j] [u_j > 0] k_idx[s]
+ *   dk_idx[s]   = sum_t sum_j g w[t,j] [u_j > 0] q_idx[t,j]    (ReLU'(0) = 0)
+ *   q_idx [B,S,Hi,Di], k_idx [B,S,Di], w [B,S,Hi] bf16 with Hi = 64, Di = 128
+ *   dscores [B,S,ld] float32 (read over [0, t] of row t)
+ *   mask    the forward's mask (its tile classes skip key tiles with no kept key)
+ *   dq_idx, dk_idx, dw  out, bf16, the shapes of q_idx, k_idx, w
+ * ------------------------------------------------------------------------- */
+dsa_status dsa_indexer_teacher(const void* q, const void* k, const float* lse, const void* mask,
+                               int B, int S, int H, int Dqk, int K, float softmax_scale,
+                               dsa_dtype dtype, float* teacher, void* stream);
+dsa_status dsa_indexer_kl(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* idx,
+                          const float* teacher, const void* mask, int B, int S, int K, float* row_kl,
+                          float* loss, float* dscores, int64_t ld_ds, void* stream);
+dsa_status dsa_indexer_bwd(const void* q_idx, const void* k_idx, const void* w, const float* dscores,
+                           int64_t ld, const void* mask, int B, int S, int Hi, int Di, dsa_dtype dtype,
+                           void* dq_idx, void* dk_idx, void* dw, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dsa_sparse_attn_bwd_noalloc -- dsa_sparse_attn_bwd with no workspace
  * argument, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).

@@ -379,6 +379,73 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
 
 
 // ---------------------------------------------------------------------------
+// Indexer KL auxiliary loss
+// ---------------------------------------------------------------------------
+dsa_status dsa_indexer_teacher(const void* q, const void* k, const float* lse, const void* mask, int B, int S, int H,
+                               int Dqk, int K, float softmax_scale, dsa_dtype dtype, float* teacher, void* stream) {
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(lse);
+  REQ_PTR(mask);
+  REQ_PTR(teacher);
+  REQ(B >= 1 && S >= 1 && H >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d H=%d K=%d)", B, S,
+      H, K);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
+  REQ(dtype_ok(dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  REQ(softmax_scale == softmax_scale && softmax_scale > 0.f, DSA_ERR_INVALID_ARG, "softmax_scale must be > 0");
+  REQ(dtype == DSA_BF16 && (Dqk == 64 || Dqk == 128 || Dqk == 192), DSA_ERR_UNSUPPORTED,
+      "the teacher takes bf16 q, k with Dqk in {64, 128, 192} (Dqk=%d)", Dqk);
+  void* m = const_cast<void*>(mask);
+  return hip_status(dsa::launch_indexer_teacher(q, k, lse, bits_of(m), cls_of(m, B, S), B, S, H, Dqk, K,
+                                                softmax_scale, teacher, (hipStream_t)stream),
+                    "dsa_indexer_teacher");
+}
+
+dsa_status dsa_indexer_kl(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* idx,
+                          const float* teacher, const void* mask, int B, int S, int K, float* row_kl, float* loss,
+                          float* dscores, int64_t ld_ds, void* stream) {
+  REQ_PTR(scores);
+  REQ_PTR(idx);
+  REQ_PTR(teacher);
+  REQ_PTR(mask);
+  REQ_PTR(row_kl);
+  REQ_PTR(dscores);
+  REQ(loss != nullptr && ((uintptr_t)loss & 7) == 0, DSA_ERR_INVALID_ARG, "loss must be a non-NULL, 8-byte aligned float[2]");
+  REQ(B >= 1 && S >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d K=%d)", B, S, K);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
+  REQ(ld >= S && ld_ds >= S, DSA_ERR_INVALID_ARG, "ld=%lld and ld_ds=%lld must be >= S=%d", (long long)ld,
+      (long long)ld_ds, S);
+  REQ(dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown score dtype");
+  return hip_status(dsa::launch_indexer_kl(scores, score_dtype == DSA_BF16, ld, idx, teacher,
+                                           bits_of(const_cast<void*>(mask)), B, S, K, row_kl, loss, dscores, ld_ds,
+                                           (hipStream_t)stream),
+                    "dsa_indexer_kl");
+}
+
+dsa_status dsa_indexer_bwd(const void* q_idx, const void* k_idx, const void* w, const float* dscores, int64_t ld,
+                           const void* mask, int B, int S, int Hi, int Di, dsa_dtype dtype, void* dq_idx,
+                           void* dk_idx, void* dw, void* stream) {
+  REQ_PTR(q_idx);
+  REQ_PTR(k_idx);
+  REQ_PTR(w);
+  REQ_PTR(dscores);
+  REQ_PTR(mask);
+  REQ_PTR(dq_idx);
+  REQ_PTR(dk_idx);
+  REQ_PTR(dw);
+  REQ(B >= 1 && S >= 1 && Hi >= 1 && Di >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d Hi=%d Di=%d)", B,
+      S, Hi, Di);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
+  REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld must be >= S=%d", (long long)ld, S);
+  REQ(dtype_ok(dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  REQ(dtype == DSA_BF16 && Hi == 64 && Di == 128, DSA_ERR_UNSUPPORTED,
+      "the indexer backward takes bf16 inputs with 64 index heads of dim 128 (Hi=%d Di=%d)", Hi, Di);
+  return hip_status(dsa::launch_indexer_bwd(q_idx, k_idx, w, dscores, ld, cls_of(const_cast<void*>(mask), B, S), B, S,
+                                            dq_idx, dk_idx, dw, (hipStream_t)stream),
+                    "dsa_indexer_bwd");
+}
+
+// ---------------------------------------------------------------------------
 // Allocation-free backward: the workspace is a file-scope device array, one
 // copy per GPU, whose address is looked up once per device and kept.
 // ---------------------------------------------------------------------------

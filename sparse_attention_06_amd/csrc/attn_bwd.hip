@@ -34,10 +34,6 @@ constexpr int TK = 64;              // keys per tile (query-major kernel)
 constexpr int QP = DQK + 8;         // LDS pitch (elements) of K rows (query-major kernel)
 }  // namespace bwd
 
-__device__ __forceinline__ u32x4 pack8(const float* x) {
-  return u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
-}
-
 // ---------------------------------------------------------------------------
 // dK / dV, key-major. Workgroup = (b, h, 128 keys) with 8 waves in two roles;
 // wave w and wave w+4 share a SIMD and the same 32 keys:

@@ -31,6 +31,11 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// eight floats as eight bf16 (round to nearest even): one MFMA operand fragment
+__device__ __forceinline__ u32x4 pack8(const float* x) {
+  return u32x4{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]), pack_bf2(x[4], x[5]), pack_bf2(x[6], x[7])};
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static __forceinline__ float load(const float* p) { return *p; }

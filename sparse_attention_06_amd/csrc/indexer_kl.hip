@@ -1,0 +1,672 @@
+// The indexer's KL auxiliary loss and its gradient (gfx950).
+//
+// Sources: "Support Ring Attention with DeepSeek DSA Sparse Indexer",
+// sections "Isolated Flax NNX Auxiliary Loss" and "Loss Harvesting &
+// Objective Injection" (an indexer loss joins the objective and trains the
+// indexer's query/key projections); "Implement QK attention head chunking for
+// CSA [Deepseek v4]", review of calculate_csa_indexer_loss (the teacher is a
+// float32 softmax of the attention scores, zeroed on invalid tokens, summed
+// over heads, from inputs that carry no gradient). With kept(t) the row's kept
+// keys (the selection mask's row):
+//   teacher p_t(s) = (1/H) sum_h P_h(t,s), P_h the attention probability of
+//                    head h over kept(t) (each P_h sums to 1, so this is the
+//                    heads' sum normalised);
+//   student q_t(s) = softmax over kept(t) of I[t,s];
+//   loss = (1/N) sum_t KL(p_t || q_t) over the N rows with a kept key;
+//   dloss/dI[t,s] = (q_t(s) - p_t(s)) / N on kept pairs, and through
+//   I = sum_j w_j ReLU(u_j), u_j = q_idx[t,j] . k_idx[s] (ReLU'(0) = 0):
+//     dw[t,j] = sum_s g ReLU(u_j), dq_idx[t,j] = sum_s g w_j [u_j > 0] k_idx[s],
+//     dk_idx[s] = sum_t sum_j g w_j [u_j > 0] q_idx[t,j].
+//
+// Kernels, in call order:
+//   indexer_teacher_kernel   query-major like the attention forward: for each
+//       non-empty 64-key tile it loops over the heads, forms S^T = K Q^T with
+//       MFMA, adds exp2(S^T scale log2e - LSE_h) into a per-tile register
+//       accumulator, and after the last head writes the mean at each kept
+//       key's rank (the popcount of the row's mask bits before it), so the
+//       teacher row lines up with the ascending index list.
+//   indexer_kl_count_kernel  N (rows whose index list is not empty).
+//   indexer_kl_kernel        one wave per row: the student softmax over the
+//       kept scores, KL, and g = (q - p)/N written densely over [0, t] of the
+//       gradient row (0 at keys that are not kept).
+//   indexer_kl_finalize_kernel  the loss: one workgroup sums the rows' KL in
+//       a fixed order (deterministic).
+//   indexer_bwd_dq_kernel    query-major, per query and 32-head block:
+//       U^T = K Q^T (keys on MFMA rows, heads on columns, the lane's q_idx
+//       fragments are the B operand), G^T = g w [U > 0], and dq^T += K^T G^T
+//       with G^T going straight from the accumulator into the B operand (key
+//       order permuted inside each 16-key step, as the attention forward does
+//       with P); dw is an in-lane sum of g ReLU(U).
+//   indexer_bwd_dk_kernel    key-major, per 32-key block and 32-head block:
+//       U = Q_t K^T (heads on rows, keys on columns, the lane's k_idx
+//       fragments are the B operand), G = g w [U > 0], dk^T += Q_t^T G, with
+//       q_idx[t] staged in LDS per query; the two head blocks' partial sums
+//       are added in a fixed order through LDS.
+// No atomics anywhere, so every result is deterministic.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------
+// Teacher
+// ---------------------------------------------------------------------------
+namespace itc {
+constexpr int TK = 64, NW = 8, QW = 32 * NW;
+}  // namespace itc
+
+template <int DQK>
+__global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
+    const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H, int K,
+    float scale_log2, float inv_h, float* __restrict__ teacher) {
+  using itc::NW;
+  using itc::QW;
+  using itc::TK;
+  constexpr int KS = DQK / 16;
+  constexpr int KSL = DQK / 8 + 1;      // 16-byte slots per padded LDS key row (one pad slot)
+  constexpr int KP = KSL * 8;           // pitch (elements)
+  constexpr int KBLK = TK * KSL / 64;   // 1 KB blocks per tile
+  constexpr int KI = (KBLK + NW - 1) / NW;
+  static_assert(TK * KSL % 64 == 0, "tiles are whole 1 KB blocks");
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * KP];
+  __shared__ uint8_t scls[2][kMaxTiles];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int NQW = (S + QW - 1) / QW;
+  // costliest query blocks first, batch index fastest
+  const int b = (int)blockIdx.x % B;
+  const int qw = NQW - 1 - (int)blockIdx.x / B;
+  const int tq = qw * QW + wid * 32 + col;
+  const bool qvalid = tq < S;
+  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
+  const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
+  const size_t rs = (size_t)H * DQK;  // token stride of q and k
+  const uint16_t* kb_base = k + (size_t)b * S * rs;
+  const uint16_t* q_row = q + ((size_t)b * S + (qvalid ? tq : 0)) * rs;
+  const float* lse_b = lse + (size_t)b * H * S + (qvalid ? tq : 0);
+
+  uint32_t koff[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int slot = (wid + i * NW) * 64 + lane;
+    koff[i] = (uint32_t)(((slot / KSL) * rs + min(slot % KSL, KSL - 2) * 8) * 2);
+  }
+  // K tile kt of head h into buffer buf; rows past S copy row S-1
+  auto issue = [&](int kt, int h, int buf) {
+    const char* tb = (const char*)(kb_base + (size_t)kt * TK * rs + (size_t)h * DQK);
+    const int lim = S - 1 - kt * TK;
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      if (wid + i * NW < KBLK) {
+        const int row = ((wid + i * NW) * 64 + lane) / KSL;
+        const int dr = row - min(row, lim);
+        g2lds16(tb + koff[i] - (size_t)dr * rs * 2, (char*)smK[buf] + (wid + i * NW) * 1024);
+      }
+  };
+  auto load_q = [&](int h, u32x4 (&f)[KS], float& L) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (qvalid) z = *(const u32x4*)(q_row + (size_t)h * DQK + ks * 16 + 8 * half);
+      f[ks] = z;
+    }
+    L = qvalid ? lse_b[(size_t)h * S] * 1.4426950408889634f : 0.f;
+  };
+
+  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
+  stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
+  const uint8_t* cls0 = scls[0];
+  const uint8_t* cls1 = scls[1];
+  const uint8_t* clsw = scls[qt_w - qt0];
+  const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
+  auto next_tile = [&](int kt) {
+    int n = kt + 1;
+    while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
+    return n;
+  };
+  auto word = [&](int kt) -> uint64_t {
+    const int c = clsw[kt];
+    if (!qvalid || c == 0) return 0ull;
+    return c == 2 ? ~0ull : bits_q[kt];
+  };
+  float* trow = teacher + ((size_t)b * S + (qvalid ? tq : 0)) * K;
+
+  float acc[2][16];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+  int base = 0;  // kept keys of this row before the current tile
+
+  __syncthreads();  // class rows staged
+  int kt = next_tile(-1), h = 0;
+  u32x4 qf[KS];
+  float Lh;
+  uint64_t mw = 0ull;
+  if (kt <= kt_last) {
+    issue(kt, 0, 0);
+    mw = word(kt);
+  }
+  load_q(0, qf, Lh);
+  int buf = 0;
+  while (kt <= kt_last) {
+    int kn = kt, hn = h + 1;
+    if (hn == H) {
+      hn = 0;
+      kn = next_tile(kt);
+    }
+    wait_vmem();      // also completes this head's q fragments, loaded one iteration back
+    __syncthreads();  // K tile (kt, h) visible in `buf`; every wave is done with the other buffer
+    if (kn <= kt_last) issue(kn, hn, buf ^ 1);
+    const float Lc = Lh;
+    if (clsw[kt] != 0) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x4 a = *(const u32x4*)(smK[buf] + (kb * 32 + col) * KP + ks * 16 + 8 * half);
+          sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
+        }
+      // the next head's fragments load into the same registers while the
+      // exponentials, the write-out and the barrier run
+      load_q(kn <= kt_last ? hn : 0, qf, Lh);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[kb][r] += fast_exp2(fmaf(sacc[kb][r], scale_log2, -Lc));
+    } else {
+      load_q(kn <= kt_last ? hn : 0, qf, Lh);
+    }
+    if (hn == 0 || kn > kt_last) {
+      // tile kt done for every head: the kept keys' mean at their ranks. Lane
+      // (half, col) holds keys 32*kb + 8*(r/4) + 4*half + r%4 of the tile.
+      const uint64_t wd = mw;
+      if (wd) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int pos = 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int rank = base + __popcll(wd & ((1ull << pos) - 1ull));
+            // a row keeps at most K keys when the mask came with K-wide lists; the check
+            // keeps a narrower teacher buffer in bounds all the same
+            if (((wd >> pos) & 1ull) && rank < K) trow[rank] = acc[kb][r] * inv_h;
+          }
+        base += __popcll(wd);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+      if (kn <= kt_last) mw = word(kn);
+    }
+    kt = kn;
+    h = hn;
+    buf ^= 1;
+  }
+  if (qvalid)
+    for (int i = base; i < K; ++i) trow[i] = 0.f;
+}
+
+hipError_t launch_indexer_teacher(const void* q, const void* k, const float* lse, const uint64_t* bits,
+                                  const uint8_t* cls, int B, int S, int H, int Dqk, int K, float scale,
+                                  float* teacher, hipStream_t st) {
+  const int nqw = (S + itc::QW - 1) / itc::QW;
+  const dim3 grid((unsigned)(nqw * B)), block(itc::NW * 64);
+  const float sl2 = scale * 1.4426950408889634f, ih = 1.f / (float)H;
+#define DSA_TEACHER(D)                                                                                      \
+  hipLaunchKernelGGL(indexer_teacher_kernel<D>, grid, block, 0, st, (const uint16_t*)q, (const uint16_t*)k, \
+                     lse, bits, cls, B, S, H, K, sl2, ih, teacher)
+  if (Dqk == 192)
+    DSA_TEACHER(192);
+  else if (Dqk == 128)
+    DSA_TEACHER(128);
+  else if (Dqk == 64)
+    DSA_TEACHER(64);
+  else
+    return hipErrorInvalidValue;
+#undef DSA_TEACHER
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Student softmax, KL and the gradient w.r.t. the scores
+// ---------------------------------------------------------------------------
+// N = rows with a non-empty index list, stored as float in loss2[1]
+__global__ __launch_bounds__(1024) void indexer_kl_count_kernel(const int32_t* __restrict__ idx, int64_t nrows,
+                                                                int K, float* __restrict__ loss2) {
+  __shared__ uint32_t part[16];
+  uint32_t c = 0;
+  for (int64_t i = threadIdx.x; i < nrows; i += 1024) c += idx[i * K] >= 0 ? 1u : 0u;
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t n = 0;
+    for (int i = 0; i < 16; ++i) n += part[i];
+    loss2[1] = (float)n;
+  }
+}
+
+// One wave per row. The index list holds the row's kept keys ascending, then
+// -1 (as dsa_topk writes it); teacher entry j belongs to idx entry j.
+template <typename ST>
+__global__ __launch_bounds__(256) void indexer_kl_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                         const int32_t* __restrict__ idx,
+                                                         const float* __restrict__ teacher,
+                                                         const uint64_t* __restrict__ bits, int B, int S, int K,
+                                                         const float* __restrict__ loss2, float* __restrict__ row_kl,
+                                                         float* __restrict__ dscores, int64_t ld_ds) {
+  const int lane = threadIdx.x & 63;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (size_t)B * S) return;  // the whole wave leaves together
+  const int t = (int)(row % S);
+  const int W = (S + 63) / 64;
+  const int32_t* irow = idx + row * K;
+  const float* prow = teacher + row * K;
+  const ST* srow = scores + row * ld;
+  float* grow = dscores + row * ld_ds;
+  const float N = loss2[1];
+  const float invN = N > 0.f ? 1.f / N : 0.f;
+  // pass 1: max of the kept scores
+  float m = -INFINITY;
+  for (int j = lane; j < K; j += 64) {
+    const int s = irow[j];
+    if (s >= 0 && s <= t) m = fmaxf(m, Elem<ST>::load(srow + s));
+  }
+  m = wave_max(m);
+  float kl = 0.f;
+  if (m != -INFINITY) {
+    float z = 0.f;
+    for (int j = lane; j < K; j += 64) {
+      const int s = irow[j];
+      if (s >= 0 && s <= t) z += expf(Elem<ST>::load(srow + s) - m);
+    }
+    const float logz = logf(wave_sumf(z));
+    // pass 2: KL terms and the gradient at the kept keys
+    for (int j = lane; j < K; j += 64) {
+      const int s = irow[j];
+      if (s < 0 || s > t) continue;  // kept keys lie in [0, t]
+      const float logq = Elem<ST>::load(srow + s) - m - logz;
+      const float p = prow[j];
+      if (p > 0.f) kl += p * (logf(p) - logq);
+      grow[s] = (expf(logq) - p) * invN;
+    }
+  }
+  // zeros over [0, t] at the keys that are not kept
+  const uint64_t* brow = bits + row * W;
+  for (int w0 = 0; w0 <= t / 64; ++w0) {
+    const int s = 64 * w0 + lane;
+    if (s <= t && !((brow[w0] >> lane) & 1ull)) grow[s] = 0.f;
+  }
+  kl = wave_sumf(kl);
+  if (lane == 0) row_kl[row] = kl;
+}
+
+// loss2[0] = sum of row_kl / N, summed in a fixed order
+__global__ __launch_bounds__(1024) void indexer_kl_finalize_kernel(const float* __restrict__ row_kl, int64_t nrows,
+                                                                   float* __restrict__ loss2) {
+  __shared__ float part[1024];
+  float s = 0.f;
+  for (int64_t i = threadIdx.x; i < nrows; i += 1024) s += row_kl[i];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 512; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float N = loss2[1];
+    loss2[0] = N > 0.f ? part[0] / N : 0.f;
+  }
+}
+
+hipError_t launch_indexer_kl(const void* scores, bool score_bf16, int64_t ld, const int32_t* idx,
+                             const float* teacher, const uint64_t* bits, int B, int S, int K, float* row_kl,
+                             float* loss2, float* dscores, int64_t ld_ds, hipStream_t st) {
+  const int64_t nrows = (int64_t)B * S;
+  hipLaunchKernelGGL(indexer_kl_count_kernel, dim3(1), dim3(1024), 0, st, idx, nrows, K, loss2);
+  const dim3 grid((unsigned)((nrows + 3) / 4)), block(256);
+  if (score_bf16)
+    hipLaunchKernelGGL(indexer_kl_kernel<uint16_t>, grid, block, 0, st, (const uint16_t*)scores, ld, idx, teacher,
+                       bits, B, S, K, loss2, row_kl, dscores, ld_ds);
+  else
+    hipLaunchKernelGGL(indexer_kl_kernel<float>, grid, block, 0, st, (const float*)scores, ld, idx, teacher, bits,
+                       B, S, K, loss2, row_kl, dscores, ld_ds);
+  hipLaunchKernelGGL(indexer_kl_finalize_kernel, dim3(1), dim3(1024), 0, st, row_kl, nrows, loss2);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Indexer backward (64 index heads of dim 128, bf16)
+// ---------------------------------------------------------------------------
+namespace ibw {
+constexpr int HI = 64, DI = 128, HB = HI / 32, KS = DI / 16;
+constexpr int SL = 20, PX = SL * 8;  // swizzled rows: 16 data + 4 pad slots (320 B)
+constexpr int TK = 64;               // keys per tile (dq kernel)
+constexpr int QPW = 8 / HB;          // queries per dq workgroup (8 waves = queries x head blocks)
+constexpr int KB = 128;              // keys per dk workgroup (4 key blocks x 2 head blocks)
+constexpr int NBUF = 3;              // dk stage buffers (copies two queries ahead)
+}  // namespace ibw
+
+// dq_idx and dw. Workgroup = (b, QPW consecutive queries); wave w takes query
+// t0 + w / HB and heads 32 * (w % HB) .. +31.
+__global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
+    const float* __restrict__ dscores, int64_t ld, const uint8_t* __restrict__ cls, int B, int S,
+    uint16_t* __restrict__ dq_idx, uint16_t* __restrict__ dw) {
+  using namespace ibw;
+  constexpr int NBLK = TK * SL / 64;          // 1 KB blocks per k_idx tile (20)
+  constexpr int BI = (NBLK + 7) / 8;          // per wave (3)
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * PX];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int NQB = (S + QPW - 1) / QPW;
+  const int b = (int)blockIdx.x % B;
+  const int qb = NQB - 1 - (int)blockIdx.x / B;     // costliest first
+  const int t0 = qb * QPW;
+  const int t = t0 + wid / HB, hb = wid % HB;
+  const bool qvalid = t < S;
+  const int t_last = min(S - 1, t0 + QPW - 1);
+  const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
+  const uint8_t* crow = cls + ((size_t)b * NQ + t0 / 128) * NK;  // the QPW queries share one 128-query tile
+  const uint16_t* kbase = k_idx + (size_t)b * S * DI;
+
+  // B operand of U^T = K Q^T: lane (half, col) holds q_idx[t, 32*hb + col, 16*ks + 8*half + 0..7]
+  u32x4 qf[KS];
+  float wl = 0.f;
+  {
+    const uint16_t* qr = q_idx + (((size_t)b * S + (qvalid ? t : 0)) * HI + hb * 32 + col) * DI;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      if (qvalid) z = *(const u32x4*)(qr + ks * 16 + 8 * half);
+      qf[ks] = z;
+    }
+    if (qvalid) wl = bf2f(w[((size_t)b * S + t) * HI + hb * 32 + col]);
+  }
+  const float* grow = dscores + ((size_t)b * S + (qvalid ? t : 0)) * ld;
+
+  // swizzled copy of a 64-key tile: chunk c of row r at slot swz_chunk(r, c);
+  // pad slots copy the row's last chunk; rows past S copy row S-1
+  auto issue = [&](int kt, int buf) {
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int blk = wid + i * 8;
+      if (blk < NBLK) {
+        const int slot = blk * 64 + lane, r = slot / SL, sl = slot % SL;
+        // slot sl of row r holds chunk sl ^ ((r >> 2) & 3) (swz_chunk is an involution); pad slots the last chunk
+        const int c = sl < DI / 8 ? swz_chunk(r, sl) : DI / 8 - 1;
+        const int s = min(kt * TK + r, S - 1);
+        g2lds16(kbase + (size_t)s * DI + c * 8, (char*)smK[buf] + blk * 1024);
+      }
+    }
+  };
+
+  f32x16 dqacc[DI / 32];
+#pragma unroll
+  for (int i = 0; i < DI / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dqacc[i][j] = 0.f;
+  float dwacc = 0.f;
+
+  const int kt_last = t_last / TK;
+  auto next_tile = [&](int kt) {
+    int n = kt + 1;
+    while (n <= kt_last && crow[n] == 0) ++n;
+    return n;
+  };
+  int kt = next_tile(-1);
+  if (kt <= kt_last) issue(kt, 0);
+  int buf = 0;
+  while (kt <= kt_last) {
+    const int kn = next_tile(kt);
+    wait_vmem();
+    __syncthreads();  // tile kt visible; every wave is done with the other buffer
+    if (kn <= kt_last) issue(kn, buf ^ 1);
+    const uint16_t* sK = smK[buf];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int s0 = kt * TK + kb * 32;
+      if (!qvalid || s0 > t) continue;  // wave-uniform: the block lies past this query
+      f32x16 u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) u = mfma32(lds_frag_x(sK, PX, kb * 32 + col, 2 * ks + half), qf[ks], u);
+      // lane (half, col): head 32*hb + col, keys s0 + 8*i + 4*half + j (r = 4i + j)
+      float g[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + 8 * i + 4 * half;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[4 * i + j] = s + j <= t ? grow[s + j] : 0.f;  // only [0, t] is written
+      }
+      float G[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dwacc = fmaf(g[r], fmaxf(u[r], 0.f), dwacc);
+        G[r] = u[r] > 0.f ? g[r] * wl : 0.f;
+      }
+      // dq^T[d, head] += K^T[d, key] G^T[key, head], keys permuted inside each 16-key step
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const u32x4 gb = pack8(G + 8 * p2);
+        const int r0 = kb * 32 + 16 * p2 + 4 * half;
+#pragma unroll
+        for (int db = 0; db < DI / 32; ++db) dqacc[db] = mfma32(lds_tr_frag_x(sK, PX, r0, r0 + 8, db * 32), gb, dqacc[db]);
+      }
+    }
+    buf ^= 1;
+    kt = kn;
+  }
+  dwacc = half_sum(dwacc);
+  if (qvalid) {
+    uint16_t* dqr = dq_idx + (((size_t)b * S + t) * HI + hb * 32 + col) * DI;
+#pragma unroll
+    for (int db = 0; db < DI / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * half;
+        *(u32x2*)(dqr + d) = u32x2{pack_bf2(dqacc[db][4 * g4], dqacc[db][4 * g4 + 1]),
+                                   pack_bf2(dqacc[db][4 * g4 + 2], dqacc[db][4 * g4 + 3])};
+      }
+    if (half == 0) dw[((size_t)b * S + t) * HI + hb * 32 + col] = f2bf(dwacc);
+  }
+}
+
+// dk_idx. Workgroup = (b, 128 keys), 8 waves: wave w takes keys 32*(w%4) ..
+// and heads 32*(w/4) ..; per query t >= the first key, q_idx[t] (64 x 128,
+// swizzled), w[t] and the gradient row's 128 entries are staged in LDS, three
+// queries deep. Query tiles that are EMPTY for both of the workgroup's key
+// tiles are skipped.
+__global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
+    const float* __restrict__ dscores, int64_t ld, const uint8_t* __restrict__ cls, int B, int S,
+    uint16_t* __restrict__ dk_idx) {
+  using namespace ibw;
+  constexpr int QBLK = HI * SL / 64;   // 1 KB blocks of a staged q_idx[t] (20)
+  // copies per wave per query: 20 q blocks over 8 waves (3, 3, 3, 3, 2, 2, 2, 2), then
+  // waves 4-5 the gradient entries (2 x 64 floats), wave 6 the weights, wave 7 a filler
+  constexpr int NCP = 3;
+  __shared__ __attribute__((aligned(1024))) uint16_t smQ[NBUF][HI * PX];
+  __shared__ __attribute__((aligned(16))) float smG[NBUF][KB];
+  __shared__ __attribute__((aligned(16))) uint16_t smW[NBUF][128];  // 64 weights (+ filler room)
+  __shared__ __attribute__((aligned(16))) float smP[4][DI / 32][16][64];  // head block 1's partial dk
+  __shared__ uint16_t qlist[kMaxS / 128];
+  __shared__ int s_nq;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, col = lane & 31;
+  const int kbk = wid & 3, hb = wid >> 2;
+  const int NKB = (S + KB - 1) / KB;
+  const int b = (int)blockIdx.x % B;
+  const int kblk = (int)blockIdx.x / B;               // smaller key blocks see more queries: first
+  const int k0 = kblk * KB;
+  const int sk = k0 + kbk * 32 + col;                  // this lane's key
+  const bool kvalid = sk < S;
+  const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
+  const int kt0 = k0 / 64, kt1 = min(NK - 1, kt0 + 1);
+
+  // B operand of U = Q_t K^T: lane (half, col) holds k_idx[sk, 16*ks + 8*half + 0..7]
+  u32x4 kf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (kvalid) z = *(const u32x4*)(k_idx + ((size_t)b * S + sk) * DI + ks * 16 + 8 * half);
+    kf[ks] = z;
+  }
+  // query tiles from the key block's own on, non-empty for one of its two key tiles
+  if (wid == 0) {
+    int cnt = 0;
+    for (int base = k0 / 128; base < NQ; base += 64) {
+      const int qt = base + lane;
+      bool ne = false;
+      if (qt < NQ) {
+        const uint8_t* c = cls + ((size_t)b * NQ + qt) * NK;
+        ne = c[kt0] != 0 || c[kt1] != 0;
+      }
+      const uint64_t m = __ballot(ne);
+      if (ne) qlist[cnt + lanes_below(m)] = (uint16_t)qt;
+      cnt += __popcll(m);
+    }
+    if (lane == 0) s_nq = cnt;
+  }
+  __syncthreads();
+  const int nq = s_nq;
+  // the queries, in order: every query of the listed 128-query tiles (k0 is a
+  // multiple of 128, so the first listed tile starts at or after the keys);
+  // the query after tt, moving to the next listed tile at a tile end or at S
+  auto advance = [&](int& qi, int tt) -> int {
+    const int n = tt + 1;
+    if ((n & 127) != 0 && n < S) return n;
+    ++qi;
+    return qi < nq ? 128 * (int)qlist[qi] : -1;
+  };
+  // this wave's copy slots, fixed per wave: q blocks, then g / w / filler
+  auto issue = [&](int tt, int bi) {
+    const uint16_t* qs = q_idx + ((size_t)b * S + tt) * HI * DI;
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int blk = wid + 8 * i;
+      if (blk < QBLK) {
+        const int slot = blk * 64 + lane, r = slot / SL, sl = slot % SL;
+        // slot sl of row r holds chunk sl ^ ((r >> 2) & 3) (swz_chunk is an involution); pad slots the last chunk
+        const int c = sl < DI / 8 ? swz_chunk(r, sl) : DI / 8 - 1;
+        g2lds16_async(qs + (size_t)r * DI + c * 8, (char*)smQ[bi] + blk * 1024);
+      } else if (blk == QBLK + 0 || blk == QBLK + 1) {
+        const int h = blk - QBLK;
+        const int s = min(k0 + 64 * h + lane, S - 1);
+        g2lds4_async(dscores + ((size_t)b * S + tt) * ld + s, smG[bi] + 64 * h);
+      } else if (blk == QBLK + 2) {
+        // 64 bf16 weights: lanes 0-31 copy pairs, lanes 32-63 repeat them
+        g2lds4_async(w + ((size_t)b * S + tt) * HI + 2 * (lane & 31), smW[bi]);
+      } else {
+        g2lds4_async(dscores + ((size_t)b * S + tt) * ld + min(k0 + lane, S - 1), smG[bi]);  // filler: same data
+      }
+    }
+  };
+  static_assert(QBLK + 3 <= 8 * NCP, "copy slots");
+
+  f32x16 dkacc[DI / 32];
+#pragma unroll
+  for (int i = 0; i < DI / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) dkacc[i][j] = 0.f;
+
+  int qiC = 0;
+  const int tA0 = nq > 0 ? 128 * (int)qlist[0] : -1;
+  int tA = tA0, tB = -1, tC = -1;
+  if (tA >= 0) tB = advance(qiC, tA);
+  if (tB >= 0) tC = advance(qiC, tB);
+  if (tA >= 0) issue(tA, 0);
+  if (tB >= 0) issue(tB, 1);
+  int bi = 0;
+  while (tA >= 0) {
+    if (tB >= 0)
+      wait_vmem_n<NCP>();  // query tA's copies done; tB's may still fly
+    else
+      wait_vmem();
+    lds_barrier();
+    if (tC >= 0) issue(tC, (bi + 2) % NBUF);
+    const uint16_t* sQ = smQ[bi];
+    // U[head, key] = q_idx[t, head] . k_idx[key]: heads on rows (this wave's
+    // 32-head block), keys on columns
+    if (k0 + kbk * 32 <= tA) {  // wave-uniform: some of the wave's keys are at or before the query
+      f32x16 u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) u[i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) u = mfma32(lds_frag_x(sQ, PX, hb * 32 + col, 2 * ks + half), kf[ks], u);
+      const float g = sk <= tA ? smG[bi][kbk * 32 + col] : 0.f;
+      float G[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int head = hb * 32 + acc_row(r, half);
+        G[r] = u[r] > 0.f ? g * bf2f(smW[bi][head]) : 0.f;
+      }
+      // dk^T[d, key] += q_idx[t]^T[d, head] G[head, key], heads permuted inside each 16-head step
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const u32x4 gb = pack8(G + 8 * p2);
+        const int r0 = hb * 32 + 16 * p2 + 4 * half;
+#pragma unroll
+        for (int db = 0; db < DI / 32; ++db) dkacc[db] = mfma32(lds_tr_frag_x(sQ, PX, r0, r0 + 8, db * 32), gb, dkacc[db]);
+      }
+    }
+    bi = (bi + 1) % NBUF;
+    tA = tB;
+    tB = tC;
+    if (tC >= 0) tC = advance(qiC, tC);
+  }
+  wait_vmem();
+  // head block 1 hands its partial sums to head block 0, which adds them in a fixed order
+  if (hb == 1)
+#pragma unroll
+    for (int db = 0; db < DI / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) smP[kbk][db][r][lane] = dkacc[db][r];
+  __syncthreads();
+  if (hb == 0 && kvalid) {
+    uint16_t* dkr = dk_idx + ((size_t)b * S + sk) * DI;
+#pragma unroll
+    for (int db = 0; db < DI / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = dkacc[db][4 * g4 + j] + smP[kbk][db][4 * g4 + j][lane];
+        *(u32x2*)(dkr + d) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+      }
+  }
+}
+
+hipError_t launch_indexer_bwd(const void* q_idx, const void* k_idx, const void* w, const float* dscores, int64_t ld,
+                              const uint8_t* cls, int B, int S, void* dq_idx, void* dk_idx, void* dw,
+                              hipStream_t st) {
+  using namespace ibw;
+  const int nqb = (S + QPW - 1) / QPW;
+  hipLaunchKernelGGL(indexer_bwd_dq_kernel, dim3((unsigned)(nqb * B)), dim3(512), 0, st, (const uint16_t*)q_idx,
+                     (const uint16_t*)k_idx, (const uint16_t*)w, dscores, ld, cls, B, S, (uint16_t*)dq_idx,
+                     (uint16_t*)dw);
+  const int nkb = (S + KB - 1) / KB;
+  hipLaunchKernelGGL(indexer_bwd_dk_kernel, dim3((unsigned)(nkb * B)), dim3(512), 0, st, (const uint16_t*)q_idx,
+                     (const uint16_t*)k_idx, (const uint16_t*)w, dscores, ld, cls, B, S, (uint16_t*)dk_idx);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -72,6 +72,19 @@ hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,
                                     int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
                                     void* dq, hipStream_t st);
 
+// indexer KL auxiliary loss: teacher [B,S,K] (bf16 q, k with Dqk in {64, 128,
+// 192}); student softmax, KL per row, loss2 = {loss, N} and the dense score
+// gradient over [0, t] of each row; the indexer backward (64 x 128 bf16)
+hipError_t launch_indexer_teacher(const void* q, const void* k, const float* lse, const uint64_t* bits,
+                                  const uint8_t* cls, int B, int S, int H, int Dqk, int K, float scale,
+                                  float* teacher, hipStream_t st);
+hipError_t launch_indexer_kl(const void* scores, bool score_bf16, int64_t ld, const int32_t* idx,
+                             const float* teacher, const uint64_t* bits, int B, int S, int K, float* row_kl,
+                             float* loss2, float* dscores, int64_t ld_ds, hipStream_t st);
+hipError_t launch_indexer_bwd(const void* q_idx, const void* k_idx, const void* w, const float* dscores, int64_t ld,
+                              const uint8_t* cls, int B, int S, void* dq_idx, void* dk_idx, void* dw,
+                              hipStream_t st);
+
 // dS^T fragments that the key-major backward kernel leaves for the dQ kernel:
 // per (b, h), 32-query chunk qc holds key tiles 0 .. qc/2 (the causal ones),
 // each as four 1 KB MFMA B-operand blocks (one per 16-key step). This is the

@@ -23,6 +23,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
 
 EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
+           "dsa_indexer_teacher", "dsa_indexer_kl", "dsa_indexer_bwd",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -56,6 +57,9 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                                   i32, vp, vp, vp, vp]
         L.dsa_sparse_attn_bwd_prep.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.dsa_indexer_teacher.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+        L.dsa_indexer_kl.argtypes = [vp, i32, i64, vp, vp, vp, i32, i32, i32, vp, vp, vp, i64, vp]
+        L.dsa_indexer_bwd.argtypes = [vp, vp, vp, vp, i64, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.dsa_sparse_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                                vp, vp, vp, sz, vp]
         L.dsa_sparse_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
@@ -63,7 +67,7 @@ def lib() -> ctypes.CDLL:
         for f in ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
                   "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep",
                   "dsa_sparse_attn_bwd_dq",
-                  "dsa_sparse_attn_bwd_dkdv"):
+                  "dsa_sparse_attn_bwd_dkdv", "dsa_indexer_teacher", "dsa_indexer_kl", "dsa_indexer_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_mask_bytes.argtypes = [i32, i32]
         L.dsa_mask_bytes.restype = sz
@@ -242,3 +246,31 @@ def dsa_sparse_attn_bwd_dq(q, k, v, dout, lse, mask, softmax_scale: float, dq, w
         _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(mask), B, S, H, Dqk, Dv,
         float(softmax_scale), _dt(q), _ptr(dq), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+# ------------------------------------------------------------------ indexer KL loss
+def dsa_indexer_teacher(q, k, lse, mask, K: int, softmax_scale: float, teacher, stream=None) -> None:
+    """teacher [B,S,K] float32: the head-averaged attention probabilities of
+    each row's kept keys, in index-list order (0 past them)."""
+    B, S, H, Dqk = q.shape
+    _check("dsa_indexer_teacher", lib().dsa_indexer_teacher(
+        _ptr(q), _ptr(k), _ptr(lse), _ptr(mask), B, S, H, Dqk, K, float(softmax_scale), _dt(q), _ptr(teacher),
+        _stream(stream)))
+
+
+def dsa_indexer_kl(scores, idx, teacher, mask, row_kl, loss, dscores, stream=None) -> None:
+    """Student softmax over the kept scores, KL per row (row_kl [B,S]),
+    loss = {mean KL, N} (float32[2]) and the score gradient dscores
+    [B,S,ld_ds] float32 (over [0, t] of each row)."""
+    B, S, K = idx.shape
+    _check("dsa_indexer_kl", lib().dsa_indexer_kl(
+        _ptr(scores), _dt(scores), scores.shape[-1], _ptr(idx), _ptr(teacher), _ptr(mask), B, S, K, _ptr(row_kl),
+        _ptr(loss), _ptr(dscores), dscores.shape[-1], _stream(stream)))
+
+
+def dsa_indexer_bwd(q_idx, k_idx, w, dscores, mask, dq_idx, dk_idx, dw, stream=None) -> None:
+    """Gradients of sum(dscores * I) w.r.t. q_idx, k_idx and w."""
+    B, S, Hi, Di = q_idx.shape
+    _check("dsa_indexer_bwd", lib().dsa_indexer_bwd(
+        _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(dscores), dscores.shape[-1], _ptr(mask), B, S, Hi, Di, _dt(q_idx),
+        _ptr(dq_idx), _ptr(dk_idx), _ptr(dw), _stream(stream)))

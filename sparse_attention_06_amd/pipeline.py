@@ -69,6 +69,30 @@ class DSAPath:
         dsa.dsa_sparse_attn_bwd(q, k, v, self.o, dout, self.lse, self.mask, scale, self.dq, self.dk,
                                 self.dv, self.ws)
 
+    def indexer_loss(self, x: dict, scale: float, inplace: bool = True):
+        """The indexer's KL auxiliary loss after forward(): teacher, student
+        KL and the gradients of q_idx, k_idx and w. With float32 scores and
+        ``inplace``, the score gradient overwrites the scores buffer."""
+        B, S, K = self.B, self.S, self.K
+        dev = self.device
+        if not hasattr(self, "teacher"):
+            self.teacher = torch.empty((B, S, K), dtype=torch.float32, device=dev)
+            self.row_kl = torch.empty((B, S), dtype=torch.float32, device=dev)
+            self.loss = torch.empty(2, dtype=torch.float32, device=dev)
+            self.dq_idx = torch.empty(x["q_idx"].shape, dtype=x["q_idx"].dtype, device=dev)
+            self.dk_idx = torch.empty(x["k_idx"].shape, dtype=x["k_idx"].dtype, device=dev)
+            self.dw = torch.empty(x["w"].shape, dtype=x["w"].dtype, device=dev)
+        if self.slab != S:
+            raise ValueError("the indexer loss needs the scores of every row (no slabs)")
+        if inplace and self.scores.dtype == torch.float32:
+            self.dscores = self.scores
+        elif getattr(self, "dscores", None) is None or self.dscores is self.scores:
+            self.dscores = torch.empty((B, S, S), dtype=torch.float32, device=dev)
+        dsa.dsa_indexer_teacher(x["q"], x["k"], self.lse, self.mask, K, scale, self.teacher)
+        dsa.dsa_indexer_kl(self.scores, self.idx, self.teacher, self.mask, self.row_kl, self.loss, self.dscores)
+        dsa.dsa_indexer_bwd(x["q_idx"], x["k_idx"], x["w"], self.dscores, self.mask, self.dq_idx, self.dk_idx,
+                            self.dw)
+
     def step(self, x: dict, scale: float, backward: bool = False):
         self.select(x["q_idx"], x["k_idx"], x["w"], x.get("seg"))
         self.forward(x["q"], x["k"], x["v"], scale)

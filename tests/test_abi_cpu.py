@@ -162,3 +162,24 @@ def test_noalloc_backward_rejects_before_any_launch():
     assert na(P, P, P, P, P, P, P, 1, 1 << 18, 33, 192, 128, f32(0.1), 0, P, P, P, S_) == 2
     assert b"scratch" in L.dsa_last_error()
     assert na(P, P, P, P, P, P, P, 2, 65536, 65, 192, 128, f32(0.1), 0, P, P, P, S_) == 2
+
+
+def test_indexer_loss_calls_reject_before_any_launch():
+    L = dsa.lib()
+    f32 = ctypes.c_float
+    # teacher: bf16 only, Dqk in {64, 128, 192}
+    assert L.dsa_indexer_teacher(P, P, P, P, 1, 64, 2, 192, 16, f32(0.1), 1, P, S_) == 2
+    assert L.dsa_indexer_teacher(P, P, P, P, 1, 64, 2, 96, 16, f32(0.1), 0, P, S_) == 2
+    assert L.dsa_indexer_teacher(P, P, P, P, 1, 64, 2, 192, 0, f32(0.1), 0, P, S_) == 1
+    assert L.dsa_indexer_teacher(P, P, NUL, P, 1, 64, 2, 192, 16, f32(0.1), 0, P, S_) == 1
+    # kl: loss must be an 8-byte aligned float[2]; ld >= S
+    kl = L.dsa_indexer_kl
+    assert kl(P, 1, 64, P, P, P, 1, 64, 16, P, ctypes.c_void_p(0x10004), P, 64, S_) == 1
+    assert kl(P, 1, 63, P, P, P, 1, 64, 16, P, P, P, 64, S_) == 1
+    assert kl(P, 1, 64, P, P, P, 1, 64, 16, P, P, P, 60, S_) == 1
+    # bwd: 64 x 128 bf16, ld >= S
+    bw = L.dsa_indexer_bwd
+    assert bw(P, P, P, P, 64, P, 1, 64, 32, 128, 0, P, P, P, S_) == 2
+    assert bw(P, P, P, P, 64, P, 1, 64, 64, 64, 0, P, P, P, S_) == 2
+    assert bw(P, P, P, P, 63, P, 1, 64, 64, 128, 0, P, P, P, S_) == 1
+    assert bw(P, P, P, P, 64, P, 1, 64, 64, 128, 1, P, P, P, S_) == 2
