@@ -172,6 +172,13 @@ __device__ __forceinline__ void g2lds16_async_off_nt(const void* gbase, uint32_t
                "global_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
                : "=&s"(save) : "v"(off), "s"(gbase), "s"(lds_addr(lds_base)) : "memory");
 }
+// 4 bytes per lane from a wave-uniform base (SGPR pair) plus a per-lane byte offset
+__device__ __forceinline__ void g2lds4_async_off(const void* gbase, uint32_t off, void* lds_base) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+               "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(off), "s"(gbase), "s"(lds_addr(lds_base)) : "memory");
+}
 __device__ __forceinline__ void g2lds4_async(const void* gsrc, void* lds_base) {
   uint32_t save;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"

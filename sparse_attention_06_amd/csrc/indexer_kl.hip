@@ -19,7 +19,8 @@
 //     dk_idx[s] = sum_t sum_j g w_j [u_j > 0] q_idx[t,j].
 //
 // Kernels, in call order:
-//   indexer_teacher_kernel   query-major like the attention forward: for each
+//   indexer_teacher_kernel   query-major like the attention forward, with the
+//       key axis split into chunks of 4 tiles across workgroups: for each
 //       non-empty 64-key tile it loops over the heads, forms S^T = K Q^T with
 //       MFMA, adds exp2(S^T scale log2e - LSE_h) into a per-tile register
 //       accumulator, and after the last head writes the mean at each kept
@@ -31,17 +32,19 @@
 //       gradient row (0 at keys that are not kept).
 //   indexer_kl_finalize_kernel  the loss: one workgroup sums the rows' KL in
 //       a fixed order (deterministic).
-//   indexer_bwd_dq_kernel    query-major, per query and 32-head block:
+//   indexer_bwd_dq_kernel    (runs after dk) query-major, per query and 32-head block:
 //       U^T = K Q^T (keys on MFMA rows, heads on columns, the lane's q_idx
 //       fragments are the B operand), G^T = g w [U > 0], and dq^T += K^T G^T
 //       with G^T going straight from the accumulator into the B operand (key
 //       order permuted inside each 16-key step, as the attention forward does
 //       with P); dw is an in-lane sum of g ReLU(U).
-//   indexer_bwd_dk_kernel    key-major, per 32-key block and 32-head block:
+//   indexer_bwd_dk_kernel    key-major, per 32-key block and 32-head block, with
+//       each key block's queries split into segments across workgroups:
 //       U = Q_t K^T (heads on rows, keys on columns, the lane's k_idx
 //       fragments are the B operand), G = g w [U > 0], dk^T += Q_t^T G, with
-//       q_idx[t] staged in LDS per query; the two head blocks' partial sums
-//       are added in a fixed order through LDS.
+//       q_idx[t] staged in LDS per query. The float32 partials of the head
+//       blocks and segments (staged in dq_idx's memory before dq is written)
+//       are added in a fixed order by indexer_bwd_dk_combine_kernel.
 // No atomics anywhere, so every result is deterministic.
 #include "common.hpp"
 #include "launch.hpp"
@@ -53,6 +56,7 @@ namespace dsa {
 // ---------------------------------------------------------------------------
 namespace itc {
 constexpr int TK = 64, NW = 8, QW = 32 * NW;
+constexpr int CH = 4;  // key tiles per workgroup: the key axis is split so the grid fills the chip
 }  // namespace itc
 
 template <int DQK>
@@ -77,9 +81,17 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
-  // costliest query blocks first, batch index fastest
+  const int NCH = (NK + itc::CH - 1) / itc::CH;
+  // workgroup = (b, 256-query block, chunk of CH key tiles); batch fastest,
+  // then chunk, query blocks from the last (longest rows) on
   const int b = (int)blockIdx.x % B;
-  const int qw = NQW - 1 - (int)blockIdx.x / B;
+  const int c = ((int)blockIdx.x / B) % NCH;
+  const int qw = NQW - 1 - (int)blockIdx.x / (B * NCH);
+  const int kt_end = min(S - 1, qw * QW + QW - 1) / TK;  // the block's last key tile (diagonal)
+  const int c_last = kt_end / itc::CH;
+  if (c > c_last) return;  // whole workgroup: the chunk lies past the block's diagonal
+  const int kt_lo = c * itc::CH;
+  const int kt_last = min(kt_end, kt_lo + itc::CH - 1);
   const int tq = qw * QW + wid * 32 + col;
   const bool qvalid = tq < S;
   const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
@@ -96,17 +108,28 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
     koff[i] = (uint32_t)(((slot / KSL) * rs + min(slot % KSL, KSL - 2) * 8) * 2);
   }
   // K tile kt of head h into buffer buf; rows past S copy row S-1
+  // untracked copies: the compiler adds no wait for them before LDS reads of
+  // the other buffer; the wait at the top of the next iteration covers them.
+  // Whole tiles copy from a scalar base plus the fixed lane offsets.
   auto issue = [&](int kt, int h, int buf) {
-    const char* tb = (const char*)(kb_base + (size_t)kt * TK * rs + (size_t)h * DQK);
+    const char* tb = uniform_ptr((const char*)(kb_base + (size_t)kt * TK * rs + (size_t)h * DQK));
     const int lim = S - 1 - kt * TK;
+    if (lim >= TK - 1) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i)
-      if (wid + i * NW < KBLK) {
-        const int row = ((wid + i * NW) * 64 + lane) / KSL;
-        const int dr = row - min(row, lim);
-        g2lds16(tb + koff[i] - (size_t)dr * rs * 2, (char*)smK[buf] + (wid + i * NW) * 1024);
-      }
+      for (int i = 0; i < KI; ++i)
+        if (wid + i * NW < KBLK) g2lds16_async_off(tb, koff[i], (char*)smK[buf] + (wid + i * NW) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KI; ++i)
+        if (wid + i * NW < KBLK) {
+          const int row = ((wid + i * NW) * 64 + lane) / KSL;
+          const int dr = row - min(row, lim);
+          g2lds16_async(tb + koff[i] - (size_t)dr * rs * 2, (char*)smK[buf] + (wid + i * NW) * 1024);
+        }
+    }
   };
+  // q fragments and the natural-log LSE of head h (scaled to base 2 where used,
+  // so that the load is not waited for here)
   auto load_q = [&](int h, u32x4 (&f)[KS], float& L) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -114,10 +137,9 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
       if (qvalid) z = *(const u32x4*)(q_row + (size_t)h * DQK + ks * 16 + 8 * half);
       f[ks] = z;
     }
-    L = qvalid ? lse_b[(size_t)h * S] * 1.4426950408889634f : 0.f;
+    L = qvalid ? lse_b[(size_t)h * S] : 0.f;
   };
 
-  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
   stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
   stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
   const uint8_t* cls0 = scls[0];
@@ -141,10 +163,14 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
-  int base = 0;  // kept keys of this row before the current tile
+  // kept keys of this row before the current tile: those of the chunks before
+  // this one, then this chunk's tiles as they are written
+  int base = 0;
+  if (qvalid)
+    for (int w0 = 0; w0 < kt_lo; ++w0) base += __popcll(bits_q[w0]);
 
   __syncthreads();  // class rows staged
-  int kt = next_tile(-1), h = 0;
+  int kt = next_tile(kt_lo - 1), h = 0;
   u32x4 qf[KS];
   float Lh;
   uint64_t mw = 0ull;
@@ -160,10 +186,10 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
       hn = 0;
       kn = next_tile(kt);
     }
-    wait_vmem();      // also completes this head's q fragments, loaded one iteration back
-    __syncthreads();  // K tile (kt, h) visible in `buf`; every wave is done with the other buffer
+    wait_vmem();      // K tile (kt, h) and this head's q fragments, issued one iteration back
+    lds_barrier();    // K tile (kt, h) visible in `buf`; every wave is done with the other buffer
     if (kn <= kt_last) issue(kn, hn, buf ^ 1);
-    const float Lc = Lh;
+    const float Lc = Lh * 1.4426950408889634f;
     if (clsw[kt] != 0) {
       f32x16 sacc[2];
 #pragma unroll
@@ -214,7 +240,8 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
     h = hn;
     buf ^= 1;
   }
-  if (qvalid)
+  // the chunk with the diagonal has seen every kept key of its rows
+  if (qvalid && c == c_last)
     for (int i = base; i < K; ++i) trow[i] = 0.f;
 }
 
@@ -222,7 +249,8 @@ hipError_t launch_indexer_teacher(const void* q, const void* k, const float* lse
                                   const uint8_t* cls, int B, int S, int H, int Dqk, int K, float scale,
                                   float* teacher, hipStream_t st) {
   const int nqw = (S + itc::QW - 1) / itc::QW;
-  const dim3 grid((unsigned)(nqw * B)), block(itc::NW * 64);
+  const int nch = ((S + itc::TK - 1) / itc::TK + itc::CH - 1) / itc::CH;
+  const dim3 grid((unsigned)((size_t)nqw * nch * B)), block(itc::NW * 64);
   const float sl2 = scale * 1.4426950408889634f, ih = 1.f / (float)H;
 #define DSA_TEACHER(D)                                                                                      \
   hipLaunchKernelGGL(indexer_teacher_kernel<D>, grid, block, 0, st, (const uint16_t*)q, (const uint16_t*)k, \
@@ -367,8 +395,11 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
     uint16_t* __restrict__ dq_idx, uint16_t* __restrict__ dw) {
   using namespace ibw;
   constexpr int NBLK = TK * SL / 64;          // 1 KB blocks per k_idx tile (20)
-  constexpr int BI = (NBLK + 7) / 8;          // per wave (3)
+  constexpr int BI = (NBLK + 7) / 8;          // per wave (3): waves 4-7 copy two blocks and a gradient row
+  static_assert(NBLK == 20 && QPW == 4, "copy slots: waves 0-3 take 3 blocks, waves 4-7 2 blocks + 1 row");
   __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * PX];
+  __shared__ __attribute__((aligned(16))) float smG[2][QPW][TK];  // the tile's gradient entries per query
+  __shared__ uint8_t scls[kMaxTiles];                             // the query tile's class row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -381,7 +412,6 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   const bool qvalid = t < S;
   const int t_last = min(S - 1, t0 + QPW - 1);
   const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
-  const uint8_t* crow = cls + ((size_t)b * NQ + t0 / 128) * NK;  // the QPW queries share one 128-query tile
   const uint16_t* kbase = k_idx + (size_t)b * S * DI;
 
   // B operand of U^T = K Q^T: lane (half, col) holds q_idx[t, 32*hb + col, 16*ks + 8*half + 0..7]
@@ -397,10 +427,13 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
     }
     if (qvalid) wl = bf2f(w[((size_t)b * S + t) * HI + hb * 32 + col]);
   }
-  const float* grow = dscores + ((size_t)b * S + (qvalid ? t : 0)) * ld;
-
+  wait_vmem();  // once: q_idx fragments and the weight are in before the tile loop
   // swizzled copy of a 64-key tile: chunk c of row r at slot swz_chunk(r, c);
-  // pad slots copy the row's last chunk; rows past S copy row S-1
+  // pad slots copy the row's last chunk; rows past S copy row S-1. Waves 4-7
+  // also copy query (w - 4)'s gradient entries of the tile (keys past S copy
+  // key S-1's; entries past the query are never used). Every copy goes through
+  // the untracked path and every wave issues exactly three, waited for at the
+  // top of the next iteration.
   auto issue = [&](int kt, int buf) {
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -410,7 +443,10 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
         // slot sl of row r holds chunk sl ^ ((r >> 2) & 3) (swz_chunk is an involution); pad slots the last chunk
         const int c = sl < DI / 8 ? swz_chunk(r, sl) : DI / 8 - 1;
         const int s = min(kt * TK + r, S - 1);
-        g2lds16(kbase + (size_t)s * DI + c * 8, (char*)smK[buf] + blk * 1024);
+        g2lds16_async(kbase + (size_t)s * DI + c * 8, (char*)smK[buf] + blk * 1024);
+      } else {
+        const int qq = wid - 4, tt = min(t0 + qq, S - 1), s = min(kt * TK + lane, S - 1);
+        g2lds4_async(dscores + ((size_t)b * S + tt) * ld + s, smG[buf][qq]);
       }
     }
   };
@@ -423,9 +459,12 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   float dwacc = 0.f;
 
   const int kt_last = t_last / TK;
+  // the QPW queries share one 128-query tile: its class row, staged in LDS
+  stage_bytes(scls, cls + ((size_t)b * NQ + t0 / 128) * NK, kt_last + 1);
+  __syncthreads();
   auto next_tile = [&](int kt) {
     int n = kt + 1;
-    while (n <= kt_last && crow[n] == 0) ++n;
+    while (n <= kt_last && scls[n] == 0) ++n;
     return n;
   };
   int kt = next_tile(-1);
@@ -433,10 +472,11 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   int buf = 0;
   while (kt <= kt_last) {
     const int kn = next_tile(kt);
-    wait_vmem();
-    __syncthreads();  // tile kt visible; every wave is done with the other buffer
+    wait_vmem();      // this wave's copies of tile kt (issued one tile back)
+    lds_barrier();    // tile kt visible; every wave is done with the other buffer
     if (kn <= kt_last) issue(kn, buf ^ 1);
     const uint16_t* sK = smK[buf];
+    const float* gq = smG[buf][wid / HB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int s0 = kt * TK + kb * 32;
@@ -446,13 +486,13 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
       for (int i = 0; i < 16; ++i) u[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) u = mfma32(lds_frag_x(sK, PX, kb * 32 + col, 2 * ks + half), qf[ks], u);
-      // lane (half, col): head 32*hb + col, keys s0 + 8*i + 4*half + j (r = 4i + j)
+      // lane (half, col): keys s0 + 8*i + 4*half + j (r = 4i + j); only [0, t] of the row is written
       float g[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s = s0 + 8 * i + 4 * half;
+        const f32x4 gv = *(const f32x4*)(gq + kb * 32 + 8 * i + 4 * half);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g[4 * i + j] = s + j <= t ? grow[s + j] : 0.f;  // only [0, t] is written
+        for (int j = 0; j < 4; ++j) g[4 * i + j] = s0 + 8 * i + 4 * half + j <= t ? gv[j] : 0.f;
       }
       float G[16];
 #pragma unroll
@@ -487,15 +527,18 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   }
 }
 
-// dk_idx. Workgroup = (b, 128 keys), 8 waves: wave w takes keys 32*(w%4) ..
-// and heads 32*(w/4) ..; per query t >= the first key, q_idx[t] (64 x 128,
-// swizzled), w[t] and the gradient row's 128 entries are staged in LDS, three
-// queries deep. Query tiles that are EMPTY for both of the workgroup's key
-// tiles are skipped.
+// dk_idx, partial sums. Workgroup = (b, 128 keys, segment of qseg queries):
+// the key block's queries are split into segments across workgroups, so no
+// workgroup walks a whole causal column alone. 8 waves: wave w takes keys
+// 32*(w%4) .. and heads 32*(w/4) ..; per query, q_idx[t] (64 x 128, swizzled),
+// w[t] and the gradient row's 128 entries are staged in LDS, three queries
+// deep. Query tiles that are EMPTY for both of the workgroup's key tiles are
+// skipped. Each wave writes its float32 partial dk (its keys, its 32 heads, its
+// segment) to `part`; indexer_bwd_dk_combine_kernel adds them in a fixed order.
 __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx, const uint16_t* __restrict__ w,
-    const float* __restrict__ dscores, int64_t ld, const uint8_t* __restrict__ cls, int B, int S,
-    uint16_t* __restrict__ dk_idx) {
+    const float* __restrict__ dscores, int64_t ld, const uint8_t* __restrict__ cls, int B, int S, int qseg,
+    float* __restrict__ part) {
   using namespace ibw;
   constexpr int QBLK = HI * SL / 64;   // 1 KB blocks of a staged q_idx[t] (20)
   // copies per wave per query: 20 q blocks over 8 waves (3, 3, 3, 3, 2, 2, 2, 2), then
@@ -504,7 +547,6 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t smQ[NBUF][HI * PX];
   __shared__ __attribute__((aligned(16))) float smG[NBUF][KB];
   __shared__ __attribute__((aligned(16))) uint16_t smW[NBUF][128];  // 64 weights (+ filler room)
-  __shared__ __attribute__((aligned(16))) float smP[4][DI / 32][16][64];  // head block 1's partial dk
   __shared__ uint16_t qlist[kMaxS / 128];
   __shared__ int s_nq;
 
@@ -512,10 +554,13 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int kbk = wid & 3, hb = wid >> 2;
-  const int NKB = (S + KB - 1) / KB;
+  const int NSEG = (S + qseg - 1) / qseg;
   const int b = (int)blockIdx.x % B;
-  const int kblk = (int)blockIdx.x / B;               // smaller key blocks see more queries: first
+  const int seg = ((int)blockIdx.x / B) % NSEG;
+  const int kblk = (int)blockIdx.x / (B * NSEG);
   const int k0 = kblk * KB;
+  const int q_lo = k0 + seg * qseg;                    // this workgroup's queries: [q_lo, q_lo + qseg) ∩ [0, S)
+  if (q_lo >= S) return;                               // whole workgroup: the segment lies past S
   const int sk = k0 + kbk * 32 + col;                  // this lane's key
   const bool kvalid = sk < S;
   const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
@@ -529,13 +574,17 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
     if (kvalid) z = *(const u32x4*)(k_idx + ((size_t)b * S + sk) * DI + ks * 16 + 8 * half);
     kf[ks] = z;
   }
-  // query tiles from the key block's own on, non-empty for one of its two key tiles
+  // once: the loop's counted waits then only concern the staging copies (which
+  // the compiler does not track), and it adds no wait of its own for kf
+  wait_vmem();
+  // the segment's query tiles that are non-empty for one of the two key tiles
+  const int qt_hi = min(NQ, (q_lo + qseg) / 128);
   if (wid == 0) {
     int cnt = 0;
-    for (int base = k0 / 128; base < NQ; base += 64) {
+    for (int base = q_lo / 128; base < qt_hi; base += 64) {
       const int qt = base + lane;
       bool ne = false;
-      if (qt < NQ) {
+      if (qt < qt_hi) {
         const uint8_t* c = cls + ((size_t)b * NQ + qt) * NK;
         ne = c[kt0] != 0 || c[kt1] != 0;
       }
@@ -556,27 +605,42 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
     ++qi;
     return qi < nq ? 128 * (int)qlist[qi] : -1;
   };
-  // this wave's copy slots, fixed per wave: q blocks, then g / w / filler
+  // this wave's copy slots, fixed per wave: q blocks, then g / w / filler.
+  // Each slot's per-lane byte offset is fixed, so it is formed once; per
+  // query only the scalar row bases change.
+  uint32_t coff[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int blk = wid + 8 * i;
+    if (blk < QBLK) {
+      const int slot = blk * 64 + lane, r = slot / SL, sl = slot % SL;
+      // slot sl of row r holds chunk sl ^ ((r >> 2) & 3) (swz_chunk is an involution); pad slots the last chunk
+      const int c = sl < DI / 8 ? swz_chunk(r, sl) : DI / 8 - 1;
+      coff[i] = (uint32_t)((r * DI + c * 8) * 2);
+    } else if (blk == QBLK + 0 || blk == QBLK + 1) {
+      coff[i] = (uint32_t)min(k0 + 64 * (blk - QBLK) + lane, S - 1) * 4u;
+    } else if (blk == QBLK + 2) {
+      coff[i] = (uint32_t)(2 * (lane & 31)) * 2u;  // 64 bf16 weights: lanes 32-63 repeat lanes 0-31
+    } else {
+      coff[i] = (uint32_t)min(k0 + lane, S - 1) * 4u;  // filler: the same data as the first gradient slot
+    }
+  }
   auto issue = [&](int tt, int bi) {
-    const uint16_t* qs = q_idx + ((size_t)b * S + tt) * HI * DI;
+    const size_t row = (size_t)b * S + tt;
+    const uint16_t* qs = uniform_ptr(q_idx + row * HI * DI);
+    const float* gs = uniform_ptr(dscores + row * ld);
+    const uint16_t* ws = uniform_ptr(w + row * HI);
 #pragma unroll
     for (int i = 0; i < NCP; ++i) {
       const int blk = wid + 8 * i;
-      if (blk < QBLK) {
-        const int slot = blk * 64 + lane, r = slot / SL, sl = slot % SL;
-        // slot sl of row r holds chunk sl ^ ((r >> 2) & 3) (swz_chunk is an involution); pad slots the last chunk
-        const int c = sl < DI / 8 ? swz_chunk(r, sl) : DI / 8 - 1;
-        g2lds16_async(qs + (size_t)r * DI + c * 8, (char*)smQ[bi] + blk * 1024);
-      } else if (blk == QBLK + 0 || blk == QBLK + 1) {
-        const int h = blk - QBLK;
-        const int s = min(k0 + 64 * h + lane, S - 1);
-        g2lds4_async(dscores + ((size_t)b * S + tt) * ld + s, smG[bi] + 64 * h);
-      } else if (blk == QBLK + 2) {
-        // 64 bf16 weights: lanes 0-31 copy pairs, lanes 32-63 repeat them
-        g2lds4_async(w + ((size_t)b * S + tt) * HI + 2 * (lane & 31), smW[bi]);
-      } else {
-        g2lds4_async(dscores + ((size_t)b * S + tt) * ld + min(k0 + lane, S - 1), smG[bi]);  // filler: same data
-      }
+      if (blk < QBLK)
+        g2lds16_async_off(qs, coff[i], (char*)smQ[bi] + blk * 1024);
+      else if (blk == QBLK + 0 || blk == QBLK + 1)
+        g2lds4_async_off(gs, coff[i], smG[bi] + 64 * (blk - QBLK));
+      else if (blk == QBLK + 2)
+        g2lds4_async_off(ws, coff[i], smW[bi]);
+      else
+        g2lds4_async_off(gs, coff[i], smG[bi]);
     }
   };
   static_assert(QBLK + 3 <= 8 * NCP, "copy slots");
@@ -612,11 +676,15 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) u = mfma32(lds_frag_x(sQ, PX, hb * 32 + col, 2 * ks + half), kf[ks], u);
       const float g = sk <= tA ? smG[bi][kbk * 32 + col] : 0.f;
+      // accumulator rows 4i .. 4i+3 are heads hb*32 + 8i + 4*half + 0..3: one 8-byte read each
       float G[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int head = hb * 32 + acc_row(r, half);
-        G[r] = u[r] > 0.f ? g * bf2f(smW[bi][head]) : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const u32x2 wv = *(const u32x2*)(smW[bi] + hb * 32 + 8 * i + 4 * half);
+        const float wr[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
+                             __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) G[4 * i + j] = u[4 * i + j] > 0.f ? g * wr[j] : 0.f;
       }
       // dk^T[d, key] += q_idx[t]^T[d, head] G[head, key], heads permuted inside each 16-head step
 #pragma unroll
@@ -633,39 +701,59 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
     if (tC >= 0) tC = advance(qiC, tC);
   }
   wait_vmem();
-  // head block 1 hands its partial sums to head block 0, which adds them in a fixed order
-  if (hb == 1)
+  // partial [(seg * 2 + hb)][b][key][d] (float32), zeros where nothing was added
+  if (kvalid) {
+    float* pr = part + (((size_t)(seg * 2 + hb) * B + b) * S + sk) * DI;
 #pragma unroll
     for (int db = 0; db < DI / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) smP[kbk][db][r][lane] = dkacc[db][r];
-  __syncthreads();
-  if (hb == 0 && kvalid) {
-    uint16_t* dkr = dk_idx + ((size_t)b * S + sk) * DI;
-#pragma unroll
-    for (int db = 0; db < DI / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + 8 * g4 + 4 * half;
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = dkacc[db][4 * g4 + j] + smP[kbk][db][4 * g4 + j][lane];
-        *(u32x2*)(dkr + d) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
-      }
+      for (int g4 = 0; g4 < 4; ++g4)
+        *(f32x4*)(pr + db * 32 + 8 * g4 + 4 * half) =
+            f32x4{dkacc[db][4 * g4], dkacc[db][4 * g4 + 1], dkacc[db][4 * g4 + 2], dkacc[db][4 * g4 + 3]};
   }
+}
+
+// dk_idx[b, s, :] = the sum of the partials of key s's segments and head
+// blocks, in a fixed order; one thread per 4 dims
+__global__ __launch_bounds__(256) void indexer_bwd_dk_combine_kernel(const float* __restrict__ part, int B, int S,
+                                                                     int qseg, uint16_t* __restrict__ dk_idx) {
+  using namespace ibw;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)B * S * (DI / 4)) return;
+  const int d4 = (int)(i % (DI / 4));
+  const size_t bs = i / (DI / 4);
+  const int s = (int)(bs % S), b = (int)(bs / S);
+  const int k0 = s / KB * KB;
+  const int nseg = (S - k0 + qseg - 1) / qseg;  // segments that exist for key s's block
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2 * nseg; ++j) {
+    const f32x4 v = *(const f32x4*)(part + (((size_t)j * B + b) * S + s) * DI + 4 * d4);
+    acc += v;
+  }
+  *(u32x2*)(dk_idx + bs * DI + 4 * d4) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
 }
 
 hipError_t launch_indexer_bwd(const void* q_idx, const void* k_idx, const void* w, const float* dscores, int64_t ld,
                               const uint8_t* cls, int B, int S, void* dq_idx, void* dk_idx, void* dw,
                               hipStream_t st) {
   using namespace ibw;
+  // dk first: its float32 partials (2 head blocks x nseg query segments, 1 KB
+  // per key each) are staged in dq_idx's memory (16 KB per query), which the
+  // dq kernel then overwrites; nseg <= 16 keeps them inside it
+  const int qseg = max(512, ((S + 15) / 16 + 127) / 128 * 128);
+  const int nseg = (S + qseg - 1) / qseg;
+  const int nkb = (S + KB - 1) / KB;
+  float* part = (float*)dq_idx;
+  hipLaunchKernelGGL(indexer_bwd_dk_kernel, dim3((unsigned)((size_t)nkb * nseg * B)), dim3(512), 0, st,
+                     (const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w, dscores, ld, cls, B, S, qseg,
+                     part);
+  const size_t nthr = (size_t)B * S * (DI / 4);
+  hipLaunchKernelGGL(indexer_bwd_dk_combine_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st, part, B,
+                     S, qseg, (uint16_t*)dk_idx);
   const int nqb = (S + QPW - 1) / QPW;
   hipLaunchKernelGGL(indexer_bwd_dq_kernel, dim3((unsigned)(nqb * B)), dim3(512), 0, st, (const uint16_t*)q_idx,
                      (const uint16_t*)k_idx, (const uint16_t*)w, dscores, ld, cls, B, S, (uint16_t*)dq_idx,
                      (uint16_t*)dw);
-  const int nkb = (S + KB - 1) / KB;
-  hipLaunchKernelGGL(indexer_bwd_dk_kernel, dim3((unsigned)(nkb * B)), dim3(512), 0, st, (const uint16_t*)q_idx,
-                     (const uint16_t*)k_idx, (const uint16_t*)w, dscores, ld, cls, B, S, (uint16_t*)dk_idx);
   return hipGetLastError();
 }
 
