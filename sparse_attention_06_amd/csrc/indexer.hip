@@ -17,7 +17,8 @@
 // blocks, software-pipelined: the MFMAs of one block run while the previous
 // block's ReLU and weighted sums are formed, across the tile barrier too.
 // Lane l stores key 128*kt + l from blocks 0/1 and 128*kt + 64 + l from
-// blocks 2/3.
+// blocks 2/3. With segment IDs the walk starts at the tile of the rows'
+// first same-segment key (packed documents skip the keys of earlier ones).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   constexpr int BI = (NBLK + 3) / 4;           // blocks per wave
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][NBLK * 1024];
   __shared__ int32_t lseg[2][TILE];            // segment IDs of the tile's keys (when given)
+  __shared__ uint32_t red[4];
   static_assert((Di * 2 & (Di * 2 - 1)) == 0, "key rows are a power-of-two number of bytes");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -155,14 +157,46 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   // the next tile's copies does not wait for a store issued just before it.
   OutT* out_row = scores + ((size_t)b * nrows + r) * ld;
   f32x16 accA[HB], accB[HB];
+  // With segment IDs, valid(t) starts at t's segment's first position: the
+  // loop starts at the tile of the first position whose ID is one of the
+  // workgroup's rows' IDs (the smallest of their first positions), found by a
+  // forward scan of 1024 positions per step. Rows past the range use the
+  // first row's ID.
+  int kt0 = 0;
+  if (seg) {
+    const int32_t* segb = seg + (size_t)b * S;
+    int ids[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ids[i] = segb[row0 + min(rb * 4 + i, nrows - 1)];
+    uint32_t first = 0xffffffffu;
+    for (int base = 0; base <= t_last && first == 0xffffffffu; base += 1024) {
+      uint32_t m = 0xffffffffu;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = base + 256 * j + tid;
+        if (p <= t_last) {
+          const int sp = segb[p];
+          if (sp == ids[0] || sp == ids[1] || sp == ids[2] || sp == ids[3]) m = min(m, (uint32_t)p);
+        }
+      }
+      m = wave_umin(m);
+      if (lane == 0) red[wid] = m;
+      __syncthreads();
+      first = min(min(red[0], red[1]), min(red[2], red[3]));
+      __syncthreads();
+    }
+    // found (every row's own position matches); the same in every lane, made
+    // provably uniform so that tile bases stay in scalar registers
+    kt0 = __builtin_amdgcn_readfirstlane((int)(first / TILE));
+  }
   wait_vmem();  // this wave's query fragments and weights are in
-  issue(0, 0);
+  issue(kt0, 0);
   wait_vmem();
   lds_barrier();
-  if (nkt > 1) issue(1, 1);
+  if (kt0 + 1 < nkt) issue(kt0 + 1, 1);
   mfma_block(0, 0, accA);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt0; kt < nkt; ++kt) {
+    const int buf = (kt - kt0) & 1;
     const int s_lo = kt * TILE + lane, s_hi = s_lo + 64;
     bool ok_lo = active && s_lo <= t, ok_hi = active && s_hi <= t;
     if (seg) {

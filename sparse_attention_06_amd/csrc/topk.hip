@@ -9,7 +9,8 @@
 // Selection rule: n = min(K, |valid(t)|) keys. Larger scores win. Among equal
 // scores the smaller key position wins, and -0 equals +0.
 //
-// One workgroup per query row, three kernels by row length L = t + 1:
+// One workgroup per query row, three kernels by row length L = t + 1 (with
+// segment IDs, by the span from the row's first same-segment key to t):
 //   * L <= 4096: the row's keys in VGPRs (topk_reg_kernel);
 //   * longer rows: one read of the row that lists only the keys above a
 //     sampled lower bound of the threshold (topk_stash_kernel);
@@ -97,6 +98,43 @@ __device__ __forceinline__ float kfloat(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// First position s <= t whose segment ID is seg_t (t's own), found by a
+// forward scan over [0, t] in chunks of 4 positions per thread; every thread
+// of the block returns it. With packed documents it is the start of t's
+// document, and valid(t) lies in [first, t] for any segment IDs, so the
+// selection only needs the words from first / 64 on. `red` holds NT / 64
+// words of LDS.
+template <int NT>
+__device__ int first_same_segment(const int32_t* segb, int t, int seg_t, uint32_t* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int base = 0; base <= t; base += 4 * NT) {
+    uint32_t m = 0xffffffffu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = base + NT * j + tid;
+      if (p <= t && segb[p] == seg_t) m = min(m, (uint32_t)p);
+    }
+    m = wave_umin(m);
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) m = min(m, red[i]);
+    __syncthreads();  // red is reused
+    if (m != 0xffffffffu) return (int)m;
+  }
+  return t;  // not reached: seg[t] == seg_t
+}
+
+// first index-list entry of a row that topk_reg_kernel leaves to the long-row kernels
+constexpr int32_t kLongRow = -2;
+
+// Rows whose same-segment span [first, t] covers at most 64 * 4 * kRegWords
+// keys (in whole 64-key words) go to the register kernel; the long-row kernels
+// leave them alone. Without segment IDs the span starts at 0.
+__host__ __device__ inline bool span_fits_regs(int first, int t, int reg_words) {
+  return t / 64 - first / 64 + 1 <= reg_words;
+}
+
 // Rows of at most 64 * 4 * kRegWords keys: the row's keys stay in VGPRs.
 // Wave w holds 64-key words w, w+4, w+8, ... (lane = position in the word), so
 // every pass is register work, and the compaction handles all words in
@@ -121,17 +159,17 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
     r = rbeg + rcount - 1 - i / B;
   };
   auto reads_scores = [&](int t) { return seg != nullptr || t + 1 > K; };
-  // raw scores of a row's positions held by this lane (positions >= L are not read)
+  // raw scores of a row's positions held by this lane, from word wb of the row
+  // on (positions past t are not read)
   ST raw[kRegWords];
-  auto load_row = [&](int i) {
+  auto load_row = [&](int i, int wb) {
     int b, r;
     row_of(i, b, r);
     const int t = row0 + r;
-    if (!reads_scores(t)) return;
     const ST* row = scores + ((size_t)b * nrows + r) * ld;
 #pragma unroll
     for (int j = 0; j < kRegWords; ++j) {
-      const int s = 64 * (4 * j + wid) + lane;
+      const int s = 64 * (wb + 4 * j + wid) + lane;
       if (s <= t) raw[j] = row[s];
     }
   };
@@ -143,7 +181,6 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
     const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
     const int seg_t = seg ? segb[t] : 0;
     const int L = t + 1;
-    const int nw = (L + 63) / 64;
     int32_t* idx_row = idx + ((size_t)b * S + t) * K;
     uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
     if (!reads_scores(t)) {
@@ -153,25 +190,41 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
         bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
       return;
     }
-    load_row(item);  // all of the row's score loads in flight at once
+    // the row's keys lie in words wb .. t/64 (wb > 0 only with segment IDs);
+    // a span wider than the registers hold is the long-row kernels' row
+    int wb = 0;
+    if (segb) {
+      wb = first_same_segment<256>(segb, t, seg_t, sh.red_u) / 64;
+      if (!span_fits_regs(64 * wb, t, 4 * kRegWords)) {
+        // the long-row kernels' row: marked for them (a row this kernel
+        // finishes always gets a key or -1 in its first entry)
+        if (tid == 0) idx_row[0] = kLongRow;
+        return;  // whole workgroup
+      }
+    }
+    const int nw = t / 64 - wb + 1;  // the row's words from wb on
+    // all of the row's score loads in flight at once; with segment IDs only
+    // after counting the valid keys, since a row keeping all of them needs none
+    if (!segb) load_row(item, wb);
     // keys of the valid positions (0 = not valid); take-all rows only need validity
     uint32_t nv = 0;
 #pragma unroll
     for (int j = 0; j < kRegWords; ++j) {
-      const int s = 64 * (4 * j + wid) + lane;
-      nv += __popcll(__ballot(s < L && (!segb || segb[s] == seg_t)));
+      const int s = 64 * (wb + 4 * j + wid) + lane;
+      nv += __popcll(__ballot(s <= t && (!segb || segb[s] == seg_t)));
     }
     __syncthreads();  // the previous row is done with the shared state
     if (lane == 0) sh.red_u[wid] = nv;
     __syncthreads();
     const uint32_t n_valid = sh.red_u[0] + sh.red_u[1] + sh.red_u[2] + sh.red_u[3];
     const bool take_all = n_valid <= (uint32_t)K;
+    if (segb && !take_all) load_row(item, wb);
     uint32_t key[kRegWords];
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int j = 0; j < kRegWords; ++j) {
-      const int s = 64 * (4 * j + wid) + lane;
-      const bool valid = s < L && (!segb || segb[s] == seg_t);
+      const int s = 64 * (wb + 4 * j + wid) + lane;
+      const bool valid = s <= t && (!segb || segb[s] == seg_t);
       uint32_t kk = 0u;
       if (valid) kk = take_all ? 1u : fkey(ScoreLoad<ST>::get(&raw[j], 0));
       key[j] = kk;
@@ -282,7 +335,7 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
     for (int j = 0; j < kRegWords; ++j) {
       const int w = 4 * j + wid;
       if (w >= nw) continue;  // wave-uniform
-      const int s = 64 * w + lane;
+      const int s = 64 * (wb + w) + lane;
       const uint32_t gb = __builtin_amdgcn_readlane(gx, w), eb = __builtin_amdgcn_readlane(ex, w);
       const bool gt = is_gt(key[j]), eq = is_eq(key[j]);
       const uint32_t eq_rank = eb + lanes_below(__ballot(eq));
@@ -290,9 +343,10 @@ __global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ sc
       const uint64_t selm = __ballot(sel);
       const uint32_t pos = gb + min(eb, c_eq) + lanes_below(selm);
       if (sel && pos < (uint32_t)K) idx_row[pos] = s;
-      if (lane == 0) bits_row[w] = selm;
+      if (lane == 0) bits_row[wb + w] = selm;
     }
-    for (int w = nw + tid; w < W; w += 256) bits_row[w] = 0ull;
+    for (int w = tid; w < wb; w += 256) bits_row[w] = 0ull;
+    for (int w = wb + nw + tid; w < W; w += 256) bits_row[w] = 0ull;
     const int n = take_all ? (int)n_valid : K;
     for (int i = n + tid; i < K; i += 256) idx_row[i] = -1;
   }
@@ -653,6 +707,8 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   const int b = blockIdx.x % B;
   const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
   const int t = row0 + r;
+  // with segment IDs, topk_reg_kernel (run before) marks the rows it leaves
+  if (SEG && idx[((size_t)b * S + t) * K] != kLongRow) return;
   multipass_row<ST, SEG, NW>(scores + ((size_t)b * nrows + r) * ld, SEG ? seg + (size_t)b * S : nullptr, S, K, t,
                              idx + ((size_t)b * S + t) * K, bits + ((size_t)b * S + t) * ((S + 63) / 64), sh,
                              (uint64_t*)dyn);
@@ -749,6 +805,8 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   int32_t* idx_row = idx + ((size_t)b * S + t) * K;
   uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
 
+  // with segment IDs, topk_reg_kernel (run before) marks the rows it leaves
+  if (SEG && idx_row[0] != kLongRow) return;
   if (!SEG && L <= K) {
     // causal-only row with at most K keys: every key 0..t, no score read
     for (int i = tid; i < K; i += NT) idx_row[i] = i < L ? i : -1;
@@ -1162,21 +1220,30 @@ static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* 
 // kRegWords keys in VGPRs; longer rows are read once into a short list of
 // their largest keys, with the multi-pass selection behind for rows where
 // the list misses.
+// With segment IDs a row's keys lie in [first, t], first its segment's first
+// position: every row goes to the register kernel, which leaves the rows whose
+// span is wider than the registers hold to the long-row kernels (it marks them
+// in their first index entry, and those kernels skip every other row), so
+// packed documents of up to 4096 keys never take the long path.
 template <typename ST>
 static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
                                 int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
   const ST* sc = (const ST*)scores;
   const int l_reg = 64 * 4 * kRegWords;
-  const int n_reg = max(0, min(nrows, l_reg - row0));  // rows with L <= l_reg
+  const int n_long_from = max(0, min(nrows, l_reg - row0));  // rows with L > l_reg start here
+  const int n_reg = seg ? nrows : n_long_from;                // rows the register kernel looks at
   hipError_t e = hipSuccess;
-  if (nrows > n_reg)
-    e = seg ? launch_long_rows<ST, true>(sc, ld, seg, B, S, K, row0, nrows, n_reg, nrows - n_reg, idx, bits, st)
-            : launch_long_rows<ST, false>(sc, ld, seg, B, S, K, row0, nrows, n_reg, nrows - n_reg, idx, bits, st);
-  if (e == hipSuccess && n_reg > 0) {
+  // the register kernel first: with segment IDs it marks the rows it leaves
+  if (n_reg > 0) {
     hipLaunchKernelGGL((topk_reg_kernel<ST>), dim3((unsigned)((size_t)n_reg * B)), dim3(256), 0, st, sc, ld,
                        seg, B, S, K, row0, nrows, 0, n_reg, idx, bits);
     e = hipGetLastError();
   }
+  if (e == hipSuccess && nrows > n_long_from)
+    e = seg ? launch_long_rows<ST, true>(sc, ld, seg, B, S, K, row0, nrows, n_long_from, nrows - n_long_from, idx,
+                                         bits, st)
+            : launch_long_rows<ST, false>(sc, ld, seg, B, S, K, row0, nrows, n_long_from, nrows - n_long_from, idx,
+                                          bits, st);
   return e;
 }
 
