@@ -9,10 +9,10 @@
 // Selection rule: n = min(K, |valid(t)|) keys. Larger scores win. Among equal
 // scores the smaller key position wins, and -0 equals +0.
 //
-// One workgroup per query row, three kernels by row length L = t + 1 (with
-// segment IDs, by the span from the row's first same-segment key to t):
-//   * L <= 4096: the row's keys in VGPRs (topk_reg_kernel);
-//   * longer rows: one read of the row that lists only the keys above a
+// Three kernels by row length L = t + 1 (with segment IDs, by the span from
+// the row's first same-segment key to t):
+//   * L <= 4096: one wave per row, the row's keys in VGPRs (topk_wave_kernel);
+//   * longer rows, one workgroup each: one read of the row that lists only the keys above a
 //     sampled lower bound of the threshold (topk_stash_kernel);
 //   * rows that list falls short for, and any row when K is too large for
 //     the list: a multi-pass kernel that re-reads the row (topk_long_kernel).
@@ -29,6 +29,18 @@ namespace dsa {
 
 constexpr int kNB = 2048;  // histogram bins
 
+// A score's bits in a 32-bit register (bf16 in the high half, as a float) and
+// its value
+template <typename ST> struct ScoreBits;
+template <> struct ScoreBits<float> {
+  __device__ static __forceinline__ uint32_t load(const float* p, int s) { return __float_as_uint(p[s]); }
+  __device__ static __forceinline__ float value(uint32_t b) { return __uint_as_float(b); }
+};
+template <> struct ScoreBits<uint16_t> {
+  __device__ static __forceinline__ uint32_t load(const uint16_t* p, int s) { return (uint32_t)p[s] << 16; }
+  __device__ static __forceinline__ float value(uint32_t b) { return __uint_as_float(b & 0xffff0000u); }
+};
+
 template <typename ST> struct ScoreLoad;
 template <> struct ScoreLoad<float> {
   __device__ static __forceinline__ float get(const float* p, int s) { return p[s]; }
@@ -37,319 +49,256 @@ template <> struct ScoreLoad<uint16_t> {
   __device__ static __forceinline__ float get(const uint16_t* p, int s) { return bf2f(p[s]); }
 };
 
-constexpr int kCand = 256;  // candidates ranked directly (one per thread)
-
-struct TopkShared {
-  uint32_t hist[kNB];
-  uint32_t red_u[8];
-  float red_f[8];
-  uint32_t found_bin, found_above;
-  uint32_t wave_gt[4], wave_eq[4];
-  uint32_t ncand, thresh;
-  uint32_t cand[kCand];
-};
-
-__device__ __forceinline__ void block_uminmax(uint32_t& mn, uint32_t& mx, TopkShared& sh) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  mn = wave_umin(mn);
-  mx = wave_umax(mx);
-  if (lane == 0) { sh.red_u[wid] = mn; sh.red_u[4 + wid] = mx; }
-  __syncthreads();
-  mn = min(min(sh.red_u[0], sh.red_u[1]), min(sh.red_u[2], sh.red_u[3]));
-  mx = max(max(sh.red_u[4], sh.red_u[5]), max(sh.red_u[6], sh.red_u[7]));
-  __syncthreads();
-}
-
-// Given the histogram in sh.hist[0..kNB), find the largest bin b with
-// count(bins >= b) >= need. Writes b and count(bins > b) to sh. Needs
-// count(all bins) >= need >= 1.
-__device__ void find_bin(TopkShared& sh, uint32_t need) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // thread i owns bins [8i, 8i+8); the scan runs in descending bin order, so
-  // thread 255 - i covers the i-th chunk from the top
-  uint32_t c[8];
-  uint32_t tot = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { c[i] = sh.hist[8 * tid + i]; tot += c[i]; }
-  // inclusive prefix in descending bin order within the wave, i.e. a suffix
-  // scan over lanes: incl = sum of tot over lanes >= this lane.
-  const uint32_t pre = wave_incl_scan(tot);
-  const uint32_t incl = __builtin_amdgcn_readlane(pre, 63) - pre + tot;
-  if (lane == 0) sh.red_u[wid] = incl;  // wave total
-  __syncthreads();
-  // waves with larger wid hold higher bins
-  uint32_t above_waves = 0;
-  for (int w2 = wid + 1; w2 < 4; ++w2) above_waves += sh.red_u[w2];
-  __syncthreads();
-  uint32_t running = above_waves + incl - tot;  // count of bins above this thread's chunk
-#pragma unroll
-  for (int i = 7; i >= 0; --i) {
-    if (running < need && running + c[i] >= need) {
-      sh.found_bin = 8 * tid + i;
-      sh.found_above = running;
-    }
-    running += c[i];
-  }
-  __syncthreads();
-}
-
 // inverse of fkey for a valid (non-zero) key
 __device__ __forceinline__ float kfloat(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// First position s <= t whose segment ID is seg_t (t's own), found by a
-// forward scan over [0, t] in chunks of 4 positions per thread; every thread
-// of the block returns it. With packed documents it is the start of t's
+// first index-list entry of a row that topk_wave_kernel leaves to the long-row kernels
+constexpr int32_t kLongRow = -2;
+
+// Rows whose keys fit kWaveWords 64-key words from their first valid word go
+// to topk_wave_kernel, one wave per row.
+constexpr int kWaveWords = 64;
+
+// First position s <= t whose segment ID is seg_t (t's own), by one wave: a
+// forward scan over [0, t], 16 positions per lane and step (all loads of a
+// step in flight together). With packed documents it is the start of t's
 // document, and valid(t) lies in [first, t] for any segment IDs, so the
-// selection only needs the words from first / 64 on. `red` holds NT / 64
-// words of LDS.
-template <int NT>
-__device__ int first_same_segment(const int32_t* segb, int t, int seg_t, uint32_t* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  for (int base = 0; base <= t; base += 4 * NT) {
-    uint32_t m = 0xffffffffu;
+// selection only needs the words from first / 64 on.
+__device__ int first_same_segment_wave(const int32_t* segb, int t, int seg_t) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kStep = 16;
+  for (int base = 0; base <= t; base += 64 * kStep) {
+    int v[kStep];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = base + NT * j + tid;
-      if (p <= t && segb[p] == seg_t) m = min(m, (uint32_t)p);
+    for (int j = 0; j < kStep; ++j) {
+      const int p = base + 64 * j + lane;
+      v[j] = p <= t ? segb[p] : 0;
     }
-    m = wave_umin(m);
-    if (lane == 0) red[wid] = m;
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < NT / 64; ++i) m = min(m, red[i]);
-    __syncthreads();  // red is reused
-    if (m != 0xffffffffu) return (int)m;
+    for (int j = 0; j < kStep; ++j) {
+      const uint64_t m = __ballot(base + 64 * j + lane <= t && v[j] == seg_t);
+      if (m) return base + 64 * j + (int)__builtin_ctzll(m);
+    }
   }
   return t;  // not reached: seg[t] == seg_t
 }
 
-// first index-list entry of a row that topk_reg_kernel leaves to the long-row kernels
-constexpr int32_t kLongRow = -2;
+// Per-wave scratch of topk_wave_kernel: a histogram and a candidate list
+struct WaveTopkShared {
+  uint32_t hist[kNB];
+  uint32_t cand[64];
+  uint64_t words[kWaveWords];
+};
 
-// Rows whose same-segment span [first, t] covers at most 64 * 4 * kRegWords
-// keys (in whole 64-key words) go to the register kernel; the long-row kernels
-// leave them alone. Without segment IDs the span starts at 0.
-__host__ __device__ inline bool span_fits_regs(int first, int t, int reg_words) {
-  return t / 64 - first / 64 + 1 <= reg_words;
-}
-
-// Rows of at most 64 * 4 * kRegWords keys: the row's keys stay in VGPRs.
-// Wave w holds 64-key words w, w+4, w+8, ... (lane = position in the word), so
-// every pass is register work, and the compaction handles all words in
-// parallel: per-word counts of the "greater" and "tied" keys go to LDS, one
-// wave-wide prefix scan gives every word its first slot, and ballot/mbcnt
-// place the keys inside a word. One workgroup per row, longest rows first.
-constexpr int kRegWords = 16;
-
+// Rows whose keys lie within kWaveWords words (4096 keys): one wave per row,
+// four rows per workgroup, and no workgroup barrier. Lane l holds position l
+// of each of the row's words, so a row's keys sit in 64 VGPRs per lane.
+//   * The K-th largest key T: the keys (order-preserving integers, 0 for
+//     invalid positions) are binned into 2048 bins over [min, max] by their
+//     top bits in the wave's own LDS histogram; a suffix scan over the lanes
+//     finds T's bin. A bin of at most 64 keys is ranked directly (each lane
+//     one candidate, compared with every other through readlane); a crowded
+//     bin is binned again over its own key interval, until one key is left.
+//   * Compaction walks the words in order with running counts of the keys
+//     above T and tied at T: a ballot per word gives its mask word, and
+//     ballot/mbcnt give each selected key its slot. Ties at T go to the lowest
+//     positions.
+// Longest rows first. With segment IDs, a row's span from its first
+// same-segment key must fit kWaveWords words; wider rows get kLongRow in
+// their first index entry and are left to the long-row kernels.
 template <typename ST>
-__global__ __launch_bounds__(256) void topk_reg_kernel(const ST* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ seg, int B, int S,
-                                                       int K, int row0, int nrows, int rbeg, int rcount,
-                                                       int32_t* __restrict__ idx,
-                                                       uint64_t* __restrict__ bits) {
-  __shared__ TopkShared sh;
-  __shared__ uint32_t wgt[64], weq[64];  // per 64-key word: keys above T, keys equal to T
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void topk_wave_kernel(const ST* __restrict__ scores, int64_t ld,
+                                                        const int32_t* __restrict__ seg, int B, int S,
+                                                        int K, int row0, int nrows, int nreg,
+                                                        int32_t* __restrict__ idx,
+                                                        uint64_t* __restrict__ bits) {
+  __shared__ WaveTopkShared shw[4];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int item = (int)blockIdx.x * 4 + wid;
+  if (item >= nreg * B) return;  // the whole wave: nothing in this kernel waits for other waves
+  WaveTopkShared& sh = shw[wid];
+  const int b = item % B, r = nreg - 1 - item / B;  // longest rows first
+  const int t = row0 + r, L = t + 1;
   const int W = (S + 63) / 64;
-  // row of work item i (longest rows first), and whether it reads scores
-  auto row_of = [&](int i, int& b, int& r) {
-    b = i % B;
-    r = rbeg + rcount - 1 - i / B;
-  };
-  auto reads_scores = [&](int t) { return seg != nullptr || t + 1 > K; };
-  // raw scores of a row's positions held by this lane, from word wb of the row
-  // on (positions past t are not read)
-  ST raw[kRegWords];
-  auto load_row = [&](int i, int wb) {
-    int b, r;
-    row_of(i, b, r);
-    const int t = row0 + r;
-    const ST* row = scores + ((size_t)b * nrows + r) * ld;
-#pragma unroll
-    for (int j = 0; j < kRegWords; ++j) {
-      const int s = 64 * (wb + 4 * j + wid) + lane;
-      if (s <= t) raw[j] = row[s];
-    }
-  };
-  {
-    const int item = blockIdx.x;
-    int b, r;
-    row_of(item, b, r);
-    const int t = row0 + r;
-    const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
-    const int seg_t = seg ? segb[t] : 0;
-    const int L = t + 1;
-    int32_t* idx_row = idx + ((size_t)b * S + t) * K;
-    uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
-    if (!reads_scores(t)) {
-      // causal-only row with at most K keys: every key 0..t, no score read
-      for (int i = tid; i < K; i += 256) idx_row[i] = i < L ? i : -1;
-      for (int w = tid; w < W; w += 256)
-        bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
+  int32_t* idx_row = idx + ((size_t)b * S + t) * K;
+  uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
+  const ST* row = scores + ((size_t)b * nrows + r) * ld;
+  const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
+
+  if (!segb && L <= K) {
+    // causal-only row with at most K keys: every key 0..t, no score read
+    for (int i = lane; i < K; i += 64) idx_row[i] = i < L ? i : -1;
+    for (int w = lane; w < W; w += 64)
+      bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
+    return;
+  }
+  int wb = 0, seg_t = 0;
+  if (segb) {
+    seg_t = segb[t];
+    wb = __builtin_amdgcn_readfirstlane(first_same_segment_wave(segb, t, seg_t) / 64);
+    if (t / 64 - wb + 1 > kWaveWords) {
+      if (lane == 0) idx_row[0] = kLongRow;
       return;
     }
-    // the row's keys lie in words wb .. t/64 (wb > 0 only with segment IDs);
-    // a span wider than the registers hold is the long-row kernels' row
-    int wb = 0;
-    if (segb) {
-      wb = first_same_segment<256>(segb, t, seg_t, sh.red_u) / 64;
-      if (!span_fits_regs(64 * wb, t, 4 * kRegWords)) {
-        // the long-row kernels' row: marked for them (a row this kernel
-        // finishes always gets a key or -1 in its first entry)
-        if (tid == 0) idx_row[0] = kLongRow;
-        return;  // whole workgroup
-      }
-    }
-    const int nw = t / 64 - wb + 1;  // the row's words from wb on
-    // all of the row's score loads in flight at once; with segment IDs only
-    // after counting the valid keys, since a row keeping all of them needs none
-    if (!segb) load_row(item, wb);
-    // keys of the valid positions (0 = not valid); take-all rows only need validity
-    uint32_t nv = 0;
+  }
+  const int nw = t / 64 - wb + 1;  // the row's words from wb on
+  const int s_lane = 64 * wb + lane;  // this lane's position in word wb
+  // keys: 0 for positions that are not valid; first 1 for the valid ones
+  uint32_t key[kWaveWords];
+  uint32_t n_valid = 0;
+  if (segb) {
 #pragma unroll
-    for (int j = 0; j < kRegWords; ++j) {
-      const int s = 64 * (wb + 4 * j + wid) + lane;
-      nv += __popcll(__ballot(s <= t && (!segb || segb[s] == seg_t)));
+    for (int j = 0; j < kWaveWords; ++j) key[j] = (j < nw && s_lane + 64 * j <= t) ? (uint32_t)segb[s_lane + 64 * j] : 0u;
+#pragma unroll
+    for (int j = 0; j < kWaveWords; ++j) {
+      key[j] = (j < nw && s_lane + 64 * j <= t && (int)key[j] == seg_t) ? 1u : 0u;
+      n_valid += (uint32_t)__popcll(__ballot(key[j] != 0u));
     }
-    __syncthreads();  // the previous row is done with the shared state
-    if (lane == 0) sh.red_u[wid] = nv;
-    __syncthreads();
-    const uint32_t n_valid = sh.red_u[0] + sh.red_u[1] + sh.red_u[2] + sh.red_u[3];
-    const bool take_all = n_valid <= (uint32_t)K;
-    if (segb && !take_all) load_row(item, wb);
-    uint32_t key[kRegWords];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWaveWords; ++j) key[j] = (j < nw && s_lane + 64 * j <= t) ? 1u : 0u;
+    n_valid = (uint32_t)L;
+  }
+  // the K-th largest key T, how many of the keys equal to T are taken
+  // (c_eq), and how many there are (n_eq); a row that keeps every valid key
+  // has T = 1 with all of its keys tied at T
+  uint32_t T = 1, c_eq = n_valid, n_eq = n_valid;
+  if (n_valid > (uint32_t)K) {
+    // the scores of the valid positions, all loads in flight at once, into
+    // the key registers as raw bits; positions that are not valid hold
+    // 0xffffffff, a NaN pattern no (finite) score has
+#pragma unroll
+    for (int j = 0; j < kWaveWords; ++j)
+      key[j] = (j < nw && key[j]) ? ScoreBits<ST>::load(row, s_lane + 64 * j) : 0xffffffffu;
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-    for (int j = 0; j < kRegWords; ++j) {
-      const int s = 64 * (wb + 4 * j + wid) + lane;
-      const bool valid = s <= t && (!segb || segb[s] == seg_t);
-      uint32_t kk = 0u;
-      if (valid) kk = take_all ? 1u : fkey(ScoreLoad<ST>::get(&raw[j], 0));
+    for (int j = 0; j < kWaveWords; ++j) {
+      const uint32_t kk = key[j] != 0xffffffffu ? fkey(ScoreBits<ST>::value(key[j])) : 0u;
       key[j] = kk;
-      if (kk) {
-        kmin = min(kmin, kk);
-        kmax = max(kmax, kk);
-      }
+      kmin = min(kmin, kk - 1u);  // 0 (not valid) wraps to the largest value
+      kmax = max(kmax, kk);
     }
-    uint32_t T = 0, c_eq = 0;
-    if (!take_all) {
-      __syncthreads();  // red_u is reused
-      block_uminmax(kmin, kmax, sh);
-      uint32_t need = (uint32_t)K;
-      uint32_t klo, khi;
-      if (kmin == kmax) {
-        klo = khi = kmax;
-      } else {
-        // value-linear bins: monotone in the score, so equal scores share a bin
-        const float mn = kfloat(kmin), mx = kfloat(kmax);
-        const float inv = (float)kNB / (mx - mn);
-        for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
-        __syncthreads();
-        auto bin_of = [&](uint32_t kk) {
-          return (int)fminf(fmaxf((kfloat(kk) - mn) * inv, 0.f), (float)(kNB - 1));
-        };
+    kmin = wave_umin(kmin) + 1u;
+    kmax = wave_umax(kmax);
+    uint32_t klo = kmin, khi = kmax, need = (uint32_t)K;
+    n_eq = 0;
+    while (klo != khi) {
+      const uint32_t span = khi - klo;
+      const int nbits = 32 - __clz(span);
+      const int shift = nbits > 11 ? nbits - 11 : 0;
 #pragma unroll
-        for (int j = 0; j < kRegWords; ++j)
-          if (key[j]) atomicAdd(&sh.hist[bin_of(key[j])], 1u);
-        __syncthreads();
-        find_bin(sh, need);
-        const int bstar = (int)sh.found_bin;
-        need -= sh.found_above;
-        if (tid == 0) sh.ncand = 0;
-        __syncthreads();
-        klo = 0xffffffffu;
-        khi = 0u;
+      for (int i = 0; i < kNB / 256; ++i) *(u32x4*)&sh.hist[4 * (64 * i + lane)] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < kRegWords; ++j)
-          if (key[j] && bin_of(key[j]) == bstar) {
-            klo = min(klo, key[j]);
-            khi = max(khi, key[j]);
-            const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-            if (slot < (uint32_t)kCand) sh.cand[slot] = key[j];
+      for (int j = 0; j < kWaveWords; ++j) {
+        const uint32_t d = key[j] - klo;  // keys outside [klo, khi] (and 0) wrap above span
+        if (d <= span) atomicAdd(&sh.hist[d >> shift], 1u);
+      }
+      // lane l holds bins [32l, 32l+32); counts above a lane's bins by a
+      // scan over the lanes, then the lane walks its own bins downwards
+      // (read again from LDS, so no bin counts stay in registers)
+      uint32_t tot = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const u32x4 x = *(const u32x4*)&sh.hist[32 * lane + 4 * i];
+        tot += x[0] + x[1] + x[2] + x[3];
+      }
+      const uint32_t pre = wave_incl_scan(tot);
+      uint32_t running = __builtin_amdgcn_readlane(pre, 63) - pre;  // keys in bins of higher lanes
+      int fb = -1;
+      uint32_t fab = 0, fcnt = 0;
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        const u32x4 x = *(const u32x4*)&sh.hist[32 * lane + 4 * i];
+#pragma unroll
+        for (int r = 3; r >= 0; --r) {
+          if (running < need && running + x[r] >= need) {
+            fb = 32 * lane + 4 * i + r;
+            fab = running;
+            fcnt = x[r];
           }
-        block_uminmax(klo, khi, sh);
-        const uint32_t nc = sh.ncand;
-        if (nc <= (uint32_t)kCand) {
-          // candidate i is the threshold when #greater < need <= #greater + #equal
-          if (tid < (int)nc) {
-            const uint32_t ki = sh.cand[tid];
-            uint32_t gt = 0, eq = 0;
-            for (uint32_t jj = 0; jj < nc; ++jj) {
-              const uint32_t kj = sh.cand[jj];
-              gt += kj > ki;
-              eq += kj == ki;
-            }
-            if (gt < need && need <= gt + eq) {
-              sh.thresh = ki;  // every thread that writes holds the same key
-              sh.found_above = gt;
-            }
-          }
-          __syncthreads();
-          klo = khi = sh.thresh;
-          need -= sh.found_above;
+          running += x[r];
         }
       }
-      // radix refinement on the key interval [klo, khi] (crowded threshold bins)
-      while (klo != khi) {
-        const uint32_t span = khi - klo;
-        const int nbits = 32 - __clz(span);
-        const int shift = nbits > 11 ? nbits - 11 : 0;
-        for (int i = tid; i < kNB; i += 256) sh.hist[i] = 0;
-        __syncthreads();
+      const int src = (int)__builtin_ctzll(__ballot(fb >= 0));
+      const uint32_t bstar = (uint32_t)__builtin_amdgcn_readlane(fb, src);
+      need -= (uint32_t)__builtin_amdgcn_readlane((int)fab, src);
+      const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)fcnt, src);
+      const uint32_t nlo = klo + (bstar << shift);
+      const uint32_t nhi = shift == 0 ? nlo : min(khi, nlo + ((1u << shift) - 1u));
+      n_eq = cnt;  // the bin's keys, all equal once the bin is one value
+      if (nlo != nhi && cnt <= 64u) {
+        // rank the bin's keys directly: the candidate with #greater < need <=
+        // #greater + #equal is T
+        uint32_t nc = 0;
 #pragma unroll
-        for (int j = 0; j < kRegWords; ++j)
-          if (key[j] >= klo && key[j] <= khi) atomicAdd(&sh.hist[(key[j] - klo) >> shift], 1u);
-        __syncthreads();
-        find_bin(sh, need);
-        need -= sh.found_above;
-        const uint32_t nlo = klo + (sh.found_bin << shift);
-        const uint32_t nhi = shift == 0 ? nlo : min(khi, nlo + ((1u << shift) - 1u));
-        klo = nlo;
-        khi = nhi;
+        for (int j = 0; j < kWaveWords; ++j) {
+          const bool inb = key[j] - nlo <= nhi - nlo;
+          const uint64_t m = __ballot(inb);
+          if (inb) sh.cand[nc + lanes_below(m)] = key[j];
+          nc += (uint32_t)__popcll(m);
+        }
+        const uint32_t ki = lane < (int)nc ? sh.cand[lane] : 0u;
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t jj = 0; jj < nc; ++jj) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ki, (int)jj);
+          gt += kj > ki;
+          eq += kj == ki;
+        }
+        const int hit = (int)__builtin_ctzll(__ballot(lane < (int)nc && gt < need && need <= gt + eq));
+        klo = khi = (uint32_t)__builtin_amdgcn_readlane((int)ki, hit);
+        need -= (uint32_t)__builtin_amdgcn_readlane((int)gt, hit);
+        n_eq = (uint32_t)__builtin_amdgcn_readlane((int)eq, hit);
+        break;
       }
-      T = klo;
-      c_eq = need;
+      klo = nlo;
+      khi = nhi;
     }
-
-    // ---- compaction: per-word counts, one scan, then every word in parallel
-    auto is_gt = [&](uint32_t kk) { return take_all ? kk != 0u : (kk != 0u && kk > T); };
-    auto is_eq = [&](uint32_t kk) { return !take_all && kk != 0u && kk == T; };
-#pragma unroll
-    for (int j = 0; j < kRegWords; ++j) {
-      const uint32_t cg = (uint32_t)__popcll(__ballot(is_gt(key[j])));
-      const uint32_t ce = (uint32_t)__popcll(__ballot(is_eq(key[j])));
-      const int w = 4 * j + wid;
-      if (lane == 0 && w < 64) {
-        wgt[w] = cg;
-        weq[w] = ce;
-      }
-    }
-    __syncthreads();
-    // exclusive prefix over the row's words (lane = word), in every wave
-    const uint32_t g = lane < nw ? wgt[lane] : 0u, e = lane < nw ? weq[lane] : 0u;
-    const uint32_t gi = wave_incl_scan(g), ei = wave_incl_scan(e);
-    const uint32_t gx = gi - g, ex = ei - e;  // keys above T / ties in the words before
-#pragma unroll
-    for (int j = 0; j < kRegWords; ++j) {
-      const int w = 4 * j + wid;
-      if (w >= nw) continue;  // wave-uniform
-      const int s = 64 * (wb + w) + lane;
-      const uint32_t gb = __builtin_amdgcn_readlane(gx, w), eb = __builtin_amdgcn_readlane(ex, w);
-      const bool gt = is_gt(key[j]), eq = is_eq(key[j]);
-      const uint32_t eq_rank = eb + lanes_below(__ballot(eq));
-      const bool sel = gt || (eq && eq_rank < c_eq);
-      const uint64_t selm = __ballot(sel);
-      const uint32_t pos = gb + min(eb, c_eq) + lanes_below(selm);
-      if (sel && pos < (uint32_t)K) idx_row[pos] = s;
-      if (lane == 0) bits_row[wb + w] = selm;
-    }
-    for (int w = tid; w < wb; w += 256) bits_row[w] = 0ull;
-    for (int w = wb + nw + tid; w < W; w += 256) bits_row[w] = 0ull;
-    const int n = take_all ? (int)n_valid : K;
-    for (int i = n + tid; i < K; i += 256) idx_row[i] = -1;
+    if (kmin == kmax) n_eq = n_valid;  // every valid key is the same value
+    T = klo;
+    c_eq = need;
   }
+
+  // compaction, words in order with running counts of selected keys; when
+  // every key tied at T is taken a key is selected iff key >= T, else the
+  // ties at T go to the lowest positions
+  uint32_t nsel = 0, eb = 0;
+  // the mask words go to the wave's LDS slice, then out in one store
+  auto put_word = [&](int j, uint64_t m) {
+    if (lane == 0) sh.words[j] = m;
+  };
+  if (n_eq == c_eq) {
+#pragma unroll
+    for (int j = 0; j < kWaveWords; ++j) {
+      if (j < nw) {  // wave-uniform
+        const bool sel = key[j] >= T;
+        const uint64_t selm = __ballot(sel);
+        if (sel) idx_row[nsel + lanes_below(selm)] = s_lane + 64 * j;
+        put_word(j, selm);
+        nsel += (uint32_t)__popcll(selm);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kWaveWords; ++j) {
+      if (j < nw) {  // wave-uniform
+        const bool eq = key[j] == T;
+        const uint64_t eqm = __ballot(eq);
+        const bool sel = key[j] > T || (eq && eb + lanes_below(eqm) < c_eq);
+        const uint64_t selm = __ballot(sel);
+        if (sel) idx_row[nsel + lanes_below(selm)] = s_lane + 64 * j;
+        put_word(j, selm);
+        nsel += (uint32_t)__popcll(selm);
+        eb += (uint32_t)__popcll(eqm);
+      }
+    }
+  }
+  if (lane < nw) bits_row[wb + lane] = sh.words[lane];
+  for (int w = lane; w < wb; w += 64) bits_row[w] = 0ull;
+  for (int w = wb + nw + lane; w < W; w += 64) bits_row[w] = 0ull;
+  for (int i = (int)nsel + lane; i < K; i += 64) idx_row[i] = -1;
 }
 
 // ---- multi-pass selection of a long row (any K; the rows the single-read
@@ -707,14 +656,14 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   const int b = blockIdx.x % B;
   const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
   const int t = row0 + r;
-  // with segment IDs, topk_reg_kernel (run before) marks the rows it leaves
+  // with segment IDs, topk_wave_kernel (run before) marks the rows it leaves
   if (SEG && idx[((size_t)b * S + t) * K] != kLongRow) return;
   multipass_row<ST, SEG, NW>(scores + ((size_t)b * nrows + r) * ld, SEG ? seg + (size_t)b * S : nullptr, S, K, t,
                              idx + ((size_t)b * S + t) * K, bits + ((size_t)b * S + t) * ((S + 63) / 64), sh,
                              (uint64_t*)dyn);
 }
 
-// ---- rows longer than 64 * 4 * kRegWords keys, read once
+// ---- rows longer than 64 * kWaveWords keys, read once
 //
 // A strided sample of the row (32 runs of 64 consecutive keys) gives a lower
 // bound lo on the threshold, chosen so that about 2K of the row's keys are at
@@ -805,7 +754,7 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   int32_t* idx_row = idx + ((size_t)b * S + t) * K;
   uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
 
-  // with segment IDs, topk_reg_kernel (run before) marks the rows it leaves
+  // with segment IDs, topk_wave_kernel (run before) marks the rows it leaves
   if (SEG && idx_row[0] != kLongRow) return;
   if (!SEG && L <= K) {
     // causal-only row with at most K keys: every key 0..t, no score read
@@ -1207,7 +1156,7 @@ static hipError_t launch_stash(const ST* scores, int64_t ld, const int32_t* seg,
                      st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max, idx, bits);
   return hipGetLastError();
 }
-// rows [rbeg, rbeg + rcount) of the slab, all longer than 64 * 4 * kRegWords keys
+// rows [rbeg, rbeg + rcount) of the slab, all longer than 64 * kWaveWords keys
 template <typename ST, bool SEG>
 static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K, int row0,
                                    int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits, hipStream_t st) {
@@ -1216,27 +1165,27 @@ static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* 
   return launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
 }
 
-// Rows are routed by length L = t + 1 (longest first): up to 64 * 4 *
-// kRegWords keys in VGPRs; longer rows are read once into a short list of
-// their largest keys, with the multi-pass selection behind for rows where
-// the list misses.
+// Rows are routed by length L = t + 1 (longest first): up to 64 *
+// kWaveWords keys in one wave's VGPRs; longer rows are read once into a short
+// list of their largest keys, with the multi-pass selection behind for rows
+// where the list misses.
 // With segment IDs a row's keys lie in [first, t], first its segment's first
-// position: every row goes to the register kernel, which leaves the rows whose
-// span is wider than the registers hold to the long-row kernels (it marks them
+// position: every row goes to the one-wave kernel, which leaves the rows whose
+// span is wider than its registers hold to the long-row kernels (it marks them
 // in their first index entry, and those kernels skip every other row), so
 // packed documents of up to 4096 keys never take the long path.
 template <typename ST>
 static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
                                 int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
   const ST* sc = (const ST*)scores;
-  const int l_reg = 64 * 4 * kRegWords;
+  const int l_reg = 64 * kWaveWords;
   const int n_long_from = max(0, min(nrows, l_reg - row0));  // rows with L > l_reg start here
-  const int n_reg = seg ? nrows : n_long_from;                // rows the register kernel looks at
+  const int n_reg = seg ? nrows : n_long_from;                // rows the one-wave kernel looks at
   hipError_t e = hipSuccess;
-  // the register kernel first: with segment IDs it marks the rows it leaves
+  // the one-wave kernel first: with segment IDs it marks the rows it leaves
   if (n_reg > 0) {
-    hipLaunchKernelGGL((topk_reg_kernel<ST>), dim3((unsigned)((size_t)n_reg * B)), dim3(256), 0, st, sc, ld,
-                       seg, B, S, K, row0, nrows, 0, n_reg, idx, bits);
+    hipLaunchKernelGGL((topk_wave_kernel<ST>), dim3((unsigned)(((size_t)n_reg * B + 3) / 4)), dim3(256), 0, st,
+                       sc, ld, seg, B, S, K, row0, nrows, n_reg, idx, bits);
     e = hipGetLastError();
   }
   if (e == hipSuccess && nrows > n_long_from)
