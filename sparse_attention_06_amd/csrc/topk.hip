@@ -157,9 +157,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
       key[j] = (j < nw && s_lane + 64 * j <= t && (int)key[j] == seg_t) ? 1u : 0u;
       n_valid += (uint32_t)__popcll(__ballot(key[j] != 0u));
     }
-  } else {
+  } else {  // only the last word can hold positions past t
 #pragma unroll
-    for (int j = 0; j < kWaveWords; ++j) key[j] = (j < nw && s_lane + 64 * j <= t) ? 1u : 0u;
+    for (int j = 0; j < kWaveWords; ++j) key[j] = j < nw - 1 ? 1u : (j == nw - 1 && s_lane + 64 * j <= t) ? 1u : 0u;
     n_valid = (uint32_t)L;
   }
   // the K-th largest key T, how many of the keys equal to T are taken
