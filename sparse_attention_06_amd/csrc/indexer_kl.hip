@@ -527,9 +527,12 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   }
 }
 
-// dk_idx, partial sums. Workgroup = (b, 128 keys, segment of qseg queries):
-// the key block's queries are split into segments across workgroups, so no
-// workgroup walks a whole causal column alone. 8 waves: wave w takes keys
+// dk_idx, partial sums. Workgroup = (b, 128 keys, query segment qs): the
+// queries are split into absolute segments [qs*qseg, (qs+1)*qseg) across
+// workgroups, so no workgroup walks a whole causal column alone, and the
+// workgroups of one (b, qs) -- every key block that segment reaches -- are
+// adjacent in the XCD-remapped block order: they run together on one XCD and
+// read the same q_idx rows, mostly from its L2. 8 waves: wave w takes keys
 // 32*(w%4) .. and heads 32*(w/4) ..; per query, q_idx[t] (64 x 128, swizzled),
 // w[t] and the gradient row's 128 entries are staged in LDS, three queries
 // deep. Query tiles that are EMPTY for both of the workgroup's key tiles are
@@ -554,13 +557,16 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int kbk = wid & 3, hb = wid >> 2;
-  const int NSEG = (S + qseg - 1) / qseg;
-  const int b = (int)blockIdx.x % B;
-  const int seg = ((int)blockIdx.x / B) % NSEG;
-  const int kblk = (int)blockIdx.x / (B * NSEG);
+  const int NSEG = (S + qseg - 1) / qseg, nkb = (S + KB - 1) / KB;
+  const int Lb = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int kblk = Lb % nkb;
+  const int qs = (Lb / nkb) % NSEG;
+  const int b = Lb / (nkb * NSEG);
   const int k0 = kblk * KB;
-  const int q_lo = k0 + seg * qseg;                    // this workgroup's queries: [q_lo, q_lo + qseg) ∩ [0, S)
-  if (q_lo >= S) return;                               // whole workgroup: the segment lies past S
+  // this workgroup's queries: [q_lo, (qs+1)*qseg) ∩ [0, S); both ends multiples of 128 or S
+  const int q_lo = max(k0, qs * qseg);
+  if (q_lo >= min(S, (qs + 1) * qseg)) return;        // whole workgroup: no query of the segment reaches the keys
+  const int seg = qs - k0 / qseg;                      // the partial's index among key block k0's segments
   const int sk = k0 + kbk * 32 + col;                  // this lane's key
   const bool kvalid = sk < S;
   const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
@@ -578,7 +584,7 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
   // the compiler does not track), and it adds no wait of its own for kf
   wait_vmem();
   // the segment's query tiles that are non-empty for one of the two key tiles
-  const int qt_hi = min(NQ, (q_lo + qseg) / 128);
+  const int qt_hi = min(NQ, (qs + 1) * qseg / 128);
   if (wid == 0) {
     int cnt = 0;
     for (int base = q_lo / 128; base < qt_hi; base += 64) {
@@ -724,7 +730,7 @@ __global__ __launch_bounds__(256) void indexer_bwd_dk_combine_kernel(const float
   const size_t bs = i / (DI / 4);
   const int s = (int)(bs % S), b = (int)(bs / S);
   const int k0 = s / KB * KB;
-  const int nseg = (S - k0 + qseg - 1) / qseg;  // segments that exist for key s's block
+  const int nseg = (S + qseg - 1) / qseg - k0 / qseg;  // segments that reach key s's block
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < 2 * nseg; ++j) {
     const f32x4 v = *(const f32x4*)(part + (((size_t)j * B + b) * S + s) * DI + 4 * d4);
