@@ -91,7 +91,7 @@ def work(cfg, seg_np):
 KERNEL_SRC = {"index_scores": "indexer.hip", "topk": "topk.hip", "attn_fwd": "attn_fwd.hip",
               "attn_bwd_prep": "attn_bwd_plain.hip",
               "attn_bwd_dq": "attn_bwd.hip", "attn_bwd_dkdv": "attn_bwd.hip"}
-KERNEL_SYM = {"index_scores": "index_scores_mfma_kernel", "topk": "topk_reg_kernel", "attn_fwd": "attn_fwd_mfma_kernel",
+KERNEL_SYM = {"index_scores": "index_scores_mfma_kernel", "topk": "topk_wave_kernel", "attn_fwd": "attn_fwd_mfma_kernel",
               "attn_bwd_prep": "attn_bwd_prep_kernel",
               "attn_bwd_dq": "attn_bwd_dq_kernel", "attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
 
