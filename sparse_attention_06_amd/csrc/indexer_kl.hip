@@ -56,14 +56,28 @@ namespace dsa {
 // ---------------------------------------------------------------------------
 namespace itc {
 constexpr int TK = 64, NW = 8, QW = 32 * NW;
-constexpr int CH = 4;  // key tiles per workgroup: the key axis is split so the grid fills the chip
+constexpr int CH = 4;   // key tiles per workgroup: the key axis is split so the grid fills the chip
+constexpr int NBK = 3;  // K tile buffers: copies run two (head, tile) steps ahead
 }  // namespace itc
 
+// Workgroup = (b, 256-query block, chunk of CH key tiles), 8 waves of 32
+// queries. Heads are the outer loop and the chunk's non-empty tiles the inner
+// one, so a wave loads its queries' fragments of a head once (after the
+// head's last tile, for the next head) and keeps the per-tile head sums of
+// exp2(S scale log2e - LSE_h) in registers across heads. K tiles of (head,
+// tile) go through three LDS buffers, issued two steps ahead; every wave
+// issues the same number of copies per tile (dummies where it has none), so a
+// counted wait inside a head leaves the next tile's copies in flight. After
+// the last head, each lane writes the mean at each kept key's rank (the
+// popcount of its row's mask bits before it), so the teacher row lines up
+// with the ascending index list.
 template <int DQK>
 __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ lse,
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H, int K,
     float scale_log2, float inv_h, float* __restrict__ teacher) {
+  using itc::CH;
+  using itc::NBK;
   using itc::NW;
   using itc::QW;
   using itc::TK;
@@ -71,9 +85,10 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
   constexpr int KSL = DQK / 8 + 1;      // 16-byte slots per padded LDS key row (one pad slot)
   constexpr int KP = KSL * 8;           // pitch (elements)
   constexpr int KBLK = TK * KSL / 64;   // 1 KB blocks per tile
-  constexpr int KI = (KBLK + NW - 1) / NW;
+  constexpr int KI = (KBLK + NW - 1) / NW;  // copies per wave and tile (some of them dummies)
   static_assert(TK * KSL % 64 == 0, "tiles are whole 1 KB blocks");
-  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * KP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[NBK][TK * KP];
+  __shared__ __attribute__((aligned(1024))) unsigned char smX[1024];  // target of the dummy copies, never read
   __shared__ uint8_t scls[2][kMaxTiles];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -81,17 +96,16 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
-  const int NCH = (NK + itc::CH - 1) / itc::CH;
-  // workgroup = (b, 256-query block, chunk of CH key tiles); batch fastest,
-  // then chunk, query blocks from the last (longest rows) on
+  const int NCH = (NK + CH - 1) / CH;
+  // batch fastest, then chunk, query blocks from the last (longest rows) on
   const int b = (int)blockIdx.x % B;
   const int c = ((int)blockIdx.x / B) % NCH;
   const int qw = NQW - 1 - (int)blockIdx.x / (B * NCH);
   const int kt_end = min(S - 1, qw * QW + QW - 1) / TK;  // the block's last key tile (diagonal)
-  const int c_last = kt_end / itc::CH;
+  const int c_last = kt_end / CH;
   if (c > c_last) return;  // whole workgroup: the chunk lies past the block's diagonal
-  const int kt_lo = c * itc::CH;
-  const int kt_last = min(kt_end, kt_lo + itc::CH - 1);
+  const int kt_lo = c * CH;
+  const int kt_last = min(kt_end, kt_lo + CH - 1);
   const int tq = qw * QW + wid * 32 + col;
   const bool qvalid = tq < S;
   const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
@@ -104,32 +118,28 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
   uint32_t koff[KI];
 #pragma unroll
   for (int i = 0; i < KI; ++i) {
-    const int slot = (wid + i * NW) * 64 + lane;
+    const int slot = (min(wid + i * NW, KBLK - 1)) * 64 + lane;
     koff[i] = (uint32_t)(((slot / KSL) * rs + min(slot % KSL, KSL - 2) * 8) * 2);
   }
-  // K tile kt of head h into buffer buf; rows past S copy row S-1
-  // untracked copies: the compiler adds no wait for them before LDS reads of
-  // the other buffer; the wait at the top of the next iteration covers them.
-  // Whole tiles copy from a scalar base plus the fixed lane offsets.
+  // K tile kt of head h into buffer buf (rows past S copy row S-1), through
+  // the untracked copy path: exactly KI copies per wave
   auto issue = [&](int kt, int h, int buf) {
     const char* tb = uniform_ptr((const char*)(kb_base + (size_t)kt * TK * rs + (size_t)h * DQK));
     const int lim = S - 1 - kt * TK;
-    if (lim >= TK - 1) {
 #pragma unroll
-      for (int i = 0; i < KI; ++i)
-        if (wid + i * NW < KBLK) g2lds16_async_off(tb, koff[i], (char*)smK[buf] + (wid + i * NW) * 1024);
-    } else {
-#pragma unroll
-      for (int i = 0; i < KI; ++i)
-        if (wid + i * NW < KBLK) {
-          const int row = ((wid + i * NW) * 64 + lane) / KSL;
-          const int dr = row - min(row, lim);
-          g2lds16_async(tb + koff[i] - (size_t)dr * rs * 2, (char*)smK[buf] + (wid + i * NW) * 1024);
-        }
+    for (int i = 0; i < KI; ++i) {
+      const int blk = wid + i * NW;
+      char* dst = blk < KBLK ? (char*)smK[buf] + blk * 1024 : (char*)smX;
+      if (lim >= TK - 1) {
+        g2lds16_async_off(tb, koff[i], dst);
+      } else {
+        const int row = ((min(blk, KBLK - 1)) * 64 + lane) / KSL;
+        const int dr = row - min(row, lim);
+        g2lds16_async(tb + koff[i] - (size_t)dr * rs * 2, dst);
+      }
     }
   };
-  // q fragments and the natural-log LSE of head h (scaled to base 2 where used,
-  // so that the load is not waited for here)
+  // q fragments and the natural-log LSE of head h
   auto load_q = [&](int h, u32x4 (&f)[KS], float& L) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -142,81 +152,102 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
 
   stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
   stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
-  const uint8_t* cls0 = scls[0];
-  const uint8_t* cls1 = scls[1];
-  const uint8_t* clsw = scls[qt_w - qt0];
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
-  auto next_tile = [&](int kt) {
-    int n = kt + 1;
-    while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
-    return n;
-  };
-  auto word = [&](int kt) -> uint64_t {
-    const int c = clsw[kt];
-    if (!qvalid || c == 0) return 0ull;
-    return c == 2 ? ~0ull : bits_q[kt];
-  };
   float* trow = teacher + ((size_t)b * S + (qvalid ? tq : 0)) * K;
+  __syncthreads();  // class rows staged
+  // the chunk's tiles that are non-empty for the workgroup: bit j for tile
+  // kt_lo + j (uniform); tile_n(n) is the n-th of them
+  int tmask = 0;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int kt = kt_lo + j;
+    if (kt <= kt_last && (scls[0][kt] != 0 || scls[1][kt] != 0)) tmask |= 1 << j;
+  }
+  tmask = __builtin_amdgcn_readfirstlane(tmask);
+  const int nt = __popc(tmask);
+  auto tile_n = [&](int n) {
+    int m = tmask, kt = kt_lo;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (i == n) kt = kt_lo + __builtin_ctz(m | (1 << CH));
+      m &= m - 1;
+    }
+    return kt;
+  };
+  const uint8_t* clsw = scls[qt_w - qt0];
 
-  float acc[2][16];
+  float acc[CH][2][16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int j = 0; j < CH; ++j)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
-  // kept keys of this row before the current tile: those of the chunks before
-  // this one, then this chunk's tiles as they are written
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][kb][r] = 0.f;
+
+  if (nt > 0) {
+    // step s = h * nt + j handles tile tl[j] of head h, from buffer s % NBK
+    const int nsteps = H * nt;
+    auto step_tile = [&](int s_) { return tile_n(s_ % nt); };
+    auto step_head = [&](int s_) { return s_ / nt; };
+    issue(step_tile(0), 0, 0);
+    if (nsteps > 1) issue(step_tile(1), step_head(1), 1);
+    u32x4 qf[KS];
+    float Lh;
+    load_q(0, qf, Lh);
+    int s = 0;
+    for (int h = 0; h < H; ++h) {
+      const float Lc = Lh * 1.4426950408889634f;
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        if (j < nt) {  // wave-uniform
+          // this step's K tile (issued two steps back) and, at a head's first
+          // tile, the head's q fragments; the next step's copies may still fly
+          if (j == 0 || s + 1 >= nsteps)
+            wait_vmem();
+          else
+            wait_vmem_n<KI>();
+          lds_barrier();  // tile visible; every wave is done with the buffer step s+2 goes to
+          if (s + 2 < nsteps) issue(step_tile(s + 2), step_head(s + 2), (s + 2) % NBK);
+          const int kt = tile_n(j);
+          if (clsw[kt] != 0) {
+            const uint16_t* sK = smK[s % NBK];
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 a = *(const u32x4*)(sK + (kb * 32 + col) * KP + ks * 16 + 8 * half);
+                sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
+              }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[j][kb][r] += fast_exp2(fmaf(sacc[kb][r], scale_log2, -Lc));
+          }
+          ++s;
+        }
+      }
+      // the next head's fragments (waited for at its first tile)
+      if (h + 1 < H) load_q(h + 1, qf, Lh);
+    }
+  }
+
+  // kept keys of this row before the chunk, then the chunk's tiles in order:
+  // the kept keys' mean at their ranks. Lane (half, col) holds keys
+  // 32*kb + 8*(r/4) + 4*half + r%4 of a tile.
   int base = 0;
   if (qvalid)
     for (int w0 = 0; w0 < kt_lo; ++w0) base += __popcll(bits_q[w0]);
-
-  __syncthreads();  // class rows staged
-  int kt = next_tile(kt_lo - 1), h = 0;
-  u32x4 qf[KS];
-  float Lh;
-  uint64_t mw = 0ull;
-  if (kt <= kt_last) {
-    issue(kt, 0, 0);
-    mw = word(kt);
-  }
-  load_q(0, qf, Lh);
-  int buf = 0;
-  while (kt <= kt_last) {
-    int kn = kt, hn = h + 1;
-    if (hn == H) {
-      hn = 0;
-      kn = next_tile(kt);
-    }
-    wait_vmem();      // K tile (kt, h) and this head's q fragments, issued one iteration back
-    lds_barrier();    // K tile (kt, h) visible in `buf`; every wave is done with the other buffer
-    if (kn <= kt_last) issue(kn, hn, buf ^ 1);
-    const float Lc = Lh * 1.4426950408889634f;
-    if (clsw[kt] != 0) {
-      f32x16 sacc[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = *(const u32x4*)(smK[buf] + (kb * 32 + col) * KP + ks * 16 + 8 * half);
-          sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
-        }
-      // the next head's fragments load into the same registers while the
-      // exponentials, the write-out and the barrier run
-      load_q(kn <= kt_last ? hn : 0, qf, Lh);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[kb][r] += fast_exp2(fmaf(sacc[kb][r], scale_log2, -Lc));
-    } else {
-      load_q(kn <= kt_last ? hn : 0, qf, Lh);
-    }
-    if (hn == 0 || kn > kt_last) {
-      // tile kt done for every head: the kept keys' mean at their ranks. Lane
-      // (half, col) holds keys 32*kb + 8*(r/4) + 4*half + r%4 of the tile.
-      const uint64_t wd = mw;
+  for (int j = 0; j < CH; ++j) {
+    if (j < nt) {
+      const int kt = tile_n(j);
+      const int cw = clsw[kt];
+      const uint64_t wd = (!qvalid || cw == 0) ? 0ull : (cw == 2 ? ~0ull : bits_q[kt]);
       if (wd) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -226,19 +257,11 @@ __global__ __launch_bounds__(itc::NW * 64) void indexer_teacher_kernel(
             const int rank = base + __popcll(wd & ((1ull << pos) - 1ull));
             // a row keeps at most K keys when the mask came with K-wide lists; the check
             // keeps a narrower teacher buffer in bounds all the same
-            if (((wd >> pos) & 1ull) && rank < K) trow[rank] = acc[kb][r] * inv_h;
+            if (((wd >> pos) & 1ull) && rank < K) trow[rank] = acc[j][kb][r] * inv_h;
           }
         base += __popcll(wd);
       }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
-      if (kn <= kt_last) mw = word(kn);
     }
-    kt = kn;
-    h = hn;
-    buf ^= 1;
   }
   // the chunk with the diagonal has seen every kept key of its rows
   if (qvalid && c == c_last)
