@@ -36,8 +36,8 @@ constexpr int QP = DQK + 8;         // LDS pitch (elements) of K rows (query-maj
 
 // ---------------------------------------------------------------------------
 // dK / dV, key-major. Workgroup = (b, h, 128 keys) with 8 waves in two roles;
-// wave w and wave w+4 share a SIMD and the same 32 keys:
-//   waves 0-3 ("A", K/V fragments in VGPRs, raised issue priority):
+// wave w and wave w+4 share a SIMD:
+//   waves 0-3 ("A", K/V fragments of 32 keys in VGPRs, raised issue priority):
 //     S^T = K Q^T and dP^T = V dO^T for a 32-query chunk, then P and
 //     dS = P (dP - D). In the transposed orientation a lane holds one query
 //     (so one LSE, one D and one mask word per lane) and 16 keys, which is
@@ -45,8 +45,11 @@ constexpr int QP = DQK + 8;         // LDS pitch (elements) of K rows (query-maj
 //     workspace straight from registers. P and dS also go to LDS as
 //     row-major [32 queries][32 keys] tiles.
 //   waves 4-7 ("B", dV^T and dK^T accumulators): dV^T += dO^T P and
-//     dK^T += Q^T dS, one chunk behind A, with P and dS read transposed.
-// Each role issues 20 MFMAs per chunk. A's softmax-gradient VALU work hides
+//     dK^T += Q^T dS, one chunk behind A, with P and dS read transposed. A B
+//     wave owns 64 keys (two A waves' P and dS tiles) and half of their ten
+//     32-row blocks of dK^T / dV^T, so every transposed Q^T or dO^T fragment
+//     it reads feeds two MFMAs.
+// Each wave issues 20 MFMAs per chunk. A's softmax-gradient VALU work hides
 // under B's MFMAs: A has priority, so its MFMAs issue first after a barrier
 // and B's fill the matrix pipe while A works on P and dS. Chunks with EMPTY
 // tiles for the workgroup's keys are skipped.
@@ -151,16 +154,16 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   }
   __syncthreads();
   const int nlist = s_nlist;
-  auto entry = [&](int j) -> int { return j < nlist ? (int)clist[j] : -1; };
+  auto entry = [&](int j) __attribute__((always_inline)) -> int { return j < nlist ? (int)clist[j] : -1; };
   // this wave pair's keys take part in the chunk: its key tile is non-empty
   // there and the chunk reaches the pair's first key (causal)
-  auto active = [&](int e) {
+  auto active = [&](int e) __attribute__((always_inline)) {
     return ((e >> (14 + (kw >> 1))) & 1) != 0 && s0 <= (e & 0x3FFF) * QC + QC - 1;
   };
 
   // source offsets (elements from the chunk's first row) of this lane's Q / dO
   // slots: swizzled padded rows, pad slots copy the row's last chunk
-  auto slot_src = [&](int kslot, int& row) -> uint32_t {
+  auto slot_src = [&](int kslot, int& row) __attribute__((always_inline)) -> uint32_t {
     if (kslot < dkv::QBLK) {
       const int slot = kslot * 64 + lane, pc = slot % dkv::QSL;
       row = slot / dkv::QSL;
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     soff[i] = kslot < dkv::K_LD ? slot_src(kslot, row) : 0u;
   }
   // chunk qc's copies into buffer bi (B waves)
-  auto issue = [&](int qc, int bi) {
+  auto issue = [&](int qc, int bi) __attribute__((always_inline)) {
     const int q0 = qc * QC;
     const bool ragged = q0 + QC > S;  // rows past S copy row S-1
     const uint16_t* qsrc = uniform_ptr(qbase + (size_t)q0 * rs_qk);
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   };
   // The wave that copies a mask tile clears, once the copy has landed, the
   // rows of a ragged last chunk that lie past S (they hold row S-1's words).
-  auto fix_ragged = [&](int qc, int bi) {
+  auto fix_ragged = [&](int qc, int bi) __attribute__((always_inline)) {
     const int q0 = qc * QC;
     if (q0 + QC <= S) return;
 #pragma unroll
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   }
   // B: chunk e0 (issued two chunks back) complete, then published; e1's copies
   // may still be in flight
-  auto publish_b = [&](int it) {
+  auto publish_b = [&](int it) __attribute__((always_inline)) {
     if (e1 >= 0) {
       if (kw == 3)
         wait_vmem_n<dkv::NSLOT - 1>();
@@ -348,15 +351,12 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     }
     lds_barrier();  // matches B's final barrier
   } else {
-    f32x16 dkacc[DQK / 32], dvacc[DV / 32];
-#pragma unroll
-    for (int i = 0; i < DQK / 32; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dkacc[i][j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) dvacc[i][j] = 0.f;
+    // B wave kw owns the 64 keys of A waves 2*kh and 2*kh+1 (kh = kw / 2) and
+    // half of their ten 32-row blocks of dK^T and dV^T: role 0 dK^T rows
+    // 0..159, role 1 dK^T rows 160..191 and all of dV^T. Each transposed Q^T /
+    // dO^T fragment read from LDS then feeds two MFMAs (one per key block).
+    const int kh = kw >> 1;
+    const int sb = kb0 + 64 * kh;  // first key of the 64
     // byte offsets of this lane's transposing reads in the swizzled Q / dO
     // chunks: rows r0 + j/4 and r0 + 8 + j/4 (r0 = 16*p2 + 4*half), 4-column
     // group j%4 of the lane's 16-column half; column block n adds 64*n bytes
@@ -371,65 +371,107 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         qt[p2][kk] = (uint32_t)(row * dkv::QPX * 2 + 16 * chunk + 8 * (j16 & 1));
         ot[p2][kk] = (uint32_t)(row * dkv::OPX * 2 + 16 * chunk + 8 * (j16 & 1));
       }
-    auto tr = [&](const char* base, uint32_t oa_, uint32_t ob_) -> u32x4 {
-      const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + oa_));
-      const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + ob_));
-      const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
-      return u32x4{ux[0], ux[1], uy[0], uy[1]};
-    };
-    // dV^T[e, s] += dO^T[e, q] P[q, s] and dK^T[d, s] += Q^T[d, q] dS[q, s] for
-    // the chunk of iteration `it`; the query order inside each 16-query step
-    // matches the A wave's accumulator rows
-    auto update = [&](int it) {
-      const char* sQ = (const char*)smQ[it % NB];
-      const char* sO = (const char*)smO[it % NB];
+    // one code path per role: a runtime role test inside the loop made the
+    // compiler keep both roles' operands live
+    auto run = [&](auto R) __attribute__((always_inline)) {
+      constexpr int role = decltype(R)::value;
+      f32x16 acc[2][5];
 #pragma unroll
-      for (int p2 = 0; p2 < 2; ++p2) {
-        // lane (half, col): key col, queries 16*p2 + 4*half + {0..3, 8..11}
-        const u32x4 pb = lds_tr_frag(smP[it & 1][kw], dkv::TP, 16 * p2 + 4 * half, 16 * p2 + 4 * half + 8, 0);
-        const u32x4 db = lds_tr_frag(smT[it & 1][kw], dkv::TP, 16 * p2 + 4 * half, 16 * p2 + 4 * half + 8, 0);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int eb = 0; eb < DV / 32; ++eb)
-          dvacc[eb] = mfma32(tr(sO + 64 * eb, ot[p2][0], ot[p2][1]), pb, dvacc[eb]);
+        for (int i = 0; i < 5; ++i)
 #pragma unroll
-        for (int d2 = 0; d2 < DQK / 32; ++d2)
-          dkacc[d2] = mfma32(tr(sQ + 64 * d2, qt[p2][0], qt[p2][1]), db, dkacc[d2]);
+          for (int x = 0; x < 16; ++x) acc[j][i][x] = 0.f;
+      auto tr = [&](const char* base, uint32_t oa_, uint32_t ob_) __attribute__((always_inline)) -> u32x4 {
+        const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + oa_));
+        const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + ob_));
+        const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+        return u32x4{ux[0], ux[1], uy[0], uy[1]};
+      };
+      // dK^T[d, s] += Q^T[d, q] dS[q, s] and dV^T[e, s] += dO^T[e, q] P[q, s]
+      // for the chunk of iteration `it`; the query order inside each 16-query
+      // step matches the A waves' accumulator rows. When only the first key
+      // block took part in the chunk (the diagonal), the second block's P and dS
+      // operands are zero.
+      auto update = [&](int it, bool both) __attribute__((always_inline)) {
+        const char* sQ = (const char*)smQ[it % NB];
+        const char* sO = (const char*)smO[it % NB];
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+          const int r0 = 16 * p2 + 4 * half;
+          // lane (half, col): key col of the block, queries r0 + {0..3, 8..11}
+          const u32x4 d0 = lds_tr_frag(smT[it & 1][2 * kh], dkv::TP, r0, r0 + 8, 0);
+          u32x4 d1 = lds_tr_frag(smT[it & 1][2 * kh + 1], dkv::TP, r0, r0 + 8, 0);
+          if (!both) d1 = z;
+          if constexpr (role == 0) {
+#pragma unroll
+            for (int d2 = 0; d2 < 5; ++d2) {
+              const u32x4 a = tr(sQ + 64 * d2, qt[p2][0], qt[p2][1]);
+              acc[0][d2] = mfma32(a, d0, acc[0][d2]);
+              acc[1][d2] = mfma32(a, d1, acc[1][d2]);
+            }
+          } else {
+            const u32x4 p0 = lds_tr_frag(smP[it & 1][2 * kh], dkv::TP, r0, r0 + 8, 0);
+            u32x4 p1 = lds_tr_frag(smP[it & 1][2 * kh + 1], dkv::TP, r0, r0 + 8, 0);
+            if (!both) p1 = z;
+            const u32x4 a = tr(sQ + 64 * 5, qt[p2][0], qt[p2][1]);
+            acc[0][0] = mfma32(a, d0, acc[0][0]);
+            acc[1][0] = mfma32(a, d1, acc[1][0]);
+#pragma unroll
+            for (int eb = 0; eb < DV / 32; ++eb) {
+              const u32x4 o = tr(sO + 64 * eb, ot[p2][0], ot[p2][1]);
+              acc[0][1 + eb] = mfma32(o, p0, acc[0][1 + eb]);
+              acc[1][1 + eb] = mfma32(o, p1, acc[1][1 + eb]);
+            }
+          }
+        }
+      };
+      // the A waves of key block j took part in chunk e: their key tile is
+      // non-empty there and the chunk reaches the block's first key
+      auto act = [&](int e, int j) __attribute__((always_inline)) {
+        return ((e >> (14 + kh)) & 1) != 0 && sb + 32 * j <= (e & 0x3FFF) * QC + QC - 1;
+      };
+      bool prev = false, prev2 = false;
+      int it = 0;
+      for (; e0 >= 0; ++it) {
+        publish_b(it);
+        if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
+        const int e3 = entry(it + 3);
+        if (prev) update(it - 1, prev2);  // the chunk A finished before this barrier
+        prev = act(e0, 0);
+        prev2 = act(e0, 1);
+        e0 = e1;
+        e1 = e2;
+        e2 = e3;
+      }
+      lds_barrier();  // A's P and dS of the last chunk are visible
+      if (prev) update(it - 1, prev2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int s = sb + 32 * j + col;
+        if (s >= S) continue;
+        uint16_t* dkrow = dk + ((size_t)b * S + s) * rs_qk + (size_t)h * DQK;
+        uint16_t* dvrow = dv + ((size_t)b * S + s) * rs_v + (size_t)h * DV;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+          // role 0: dK^T block i; role 1: dK^T block 5 (i == 0), dV^T block i-1
+          const bool isk = role == 0 || i == 0;
+          const float sc = isk ? scale : 1.f;
+          uint16_t* row = isk ? dkrow + 32 * (role == 0 ? i : 5) : dvrow + 32 * (i - 1);
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg) {
+            const int d = 8 * gg + 4 * half;
+            *(u32x2*)(row + d) = u32x2{pack_bf2(acc[j][i][4 * gg] * sc, acc[j][i][4 * gg + 1] * sc),
+                                       pack_bf2(acc[j][i][4 * gg + 2] * sc, acc[j][i][4 * gg + 3] * sc)};
+          }
+        }
       }
     };
-    bool prev = false;
-    int it = 0;
-    for (; e0 >= 0; ++it) {
-      publish_b(it);
-      if (e2 >= 0) issue(e2 & 0x3FFF, (it + 2) % NB);
-      const int e3 = entry(it + 3);
-      if (prev) update(it - 1);  // the chunk A finished before this barrier
-      prev = active(e0);
-      e0 = e1;
-      e1 = e2;
-      e2 = e3;
-    }
-    lds_barrier();  // A's P and dS of the last chunk are visible
-    if (prev) update(it - 1);
-    if (kvalid) {
-      uint16_t* dkrow = dk + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK;
-#pragma unroll
-      for (int i = 0; i < DQK / 32; ++i)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int d = i * 32 + 8 * gg + 4 * half;
-          *(u32x2*)(dkrow + d) = u32x2{pack_bf2(dkacc[i][4 * gg] * scale, dkacc[i][4 * gg + 1] * scale),
-                                       pack_bf2(dkacc[i][4 * gg + 2] * scale, dkacc[i][4 * gg + 3] * scale)};
-        }
-      uint16_t* dvrow = dv + ((size_t)b * S + sk) * rs_v + (size_t)h * DV;
-#pragma unroll
-      for (int i = 0; i < DV / 32; ++i)
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          const int e = i * 32 + 8 * gg + 4 * half;
-          *(u32x2*)(dvrow + e) = u32x2{pack_bf2(dvacc[i][4 * gg], dvacc[i][4 * gg + 1]),
-                                       pack_bf2(dvacc[i][4 * gg + 2], dvacc[i][4 * gg + 3])};
-        }
-    }
+    if (kw & 1)
+      run(std::integral_constant<int, 1>{});
+    else
+      run(std::integral_constant<int, 0>{});
   }
 }
 
