@@ -212,3 +212,16 @@ def check_key_gradients_on_given_sets(r):
             dv += dv_sel[pos, 0]
         _check_rel(f"dk[{b},{s},{h}]", _f64(path.dk[b, s, h]), dk)
         _check_rel(f"dv[{b},{s},{h}]", _f64(path.dv[b, s, h]), dv)
+    # every element of dK/dV for the last NT keys of one head: only rows
+    # t >= S - NT can keep those keys, so the oracle over those rows has every
+    # term (eight 128-key workgroups of the key-major kernel)
+    NT = min(S, 1024)
+    s0, h = S - NT, cfg.H // 2 + 1
+    rows = np.arange(s0, S)
+    sl = slice(h, h + 1)
+    _, dk_all, dv_all = ref.attention_bwd(_f64(r.x["q"][b:b + 1, :, sl]), _f64(r.x["k"][b:b + 1, :, sl]),
+                                          _f64(r.x["v"][b:b + 1, :, sl]), _f64(r.x["dout"][b:b + 1, :, sl]),
+                                          sets[b:b + 1, s0:S], None if seg is None else seg[b:b + 1],
+                                          cfg.softmax_scale, rows)
+    _check_rel(f"dk[{b},{s0}:,{h}]", _f64(path.dk[b, s0:, h]), dk_all[0, s0:, 0])
+    _check_rel(f"dv[{b},{s0}:,{h}]", _f64(path.dv[b, s0:, h]), dv_all[0, s0:, 0])
