@@ -142,7 +142,12 @@ __device__ __forceinline__ void g2lds4(const void* gsrc, void* lds_base) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
-// M0 (the LDS base of the copy) is saved and restored around it.
+// M0 (the LDS base of the copy) is saved and restored around it: M0 is a
+// register the compiler allocates itself (LDS-parameter, readlane-index and
+// message uses), and an asm statement cannot declare it clobbered, so a value
+// the compiler holds there must survive the copy. The two scalar moves cost
+// little beside the copy itself, whose issue stalls the wave for ~100+ cycles
+// when several are queued.
 __device__ __forceinline__ void g2lds16_async(const void* gsrc, void* lds_base) {
   uint32_t save;
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"

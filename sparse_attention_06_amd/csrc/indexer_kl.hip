@@ -20,10 +20,10 @@
 //
 // Kernels, in call order:
 //   indexer_teacher_kernel   query-major like the attention forward, with the
-//       key axis split into chunks of 4 tiles across workgroups: for each
-//       non-empty 64-key tile it loops over the heads, forms S^T = K Q^T with
-//       MFMA, adds exp2(S^T scale log2e - LSE_h) into a per-tile register
-//       accumulator, and after the last head writes the mean at each kept
+//       key axis split into chunks of 4 tiles across workgroups: for each head
+//       it walks the chunk's non-empty 64-key tiles, forms S^T = K Q^T with
+//       MFMA, adds exp2(S^T scale log2e - LSE_h) into per-tile register
+//       accumulators, and after the last head writes the mean at each kept
 //       key's rank (the popcount of the row's mask bits before it), so the
 //       teacher row lines up with the ascending index list.
 //   indexer_kl_count_kernel  N (rows whose index list is not empty).
