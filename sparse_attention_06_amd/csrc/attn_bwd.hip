@@ -31,7 +31,7 @@ namespace bwd {
 constexpr int DQK = 192, DV = 128;
 constexpr int QC = 32;              // queries per chunk (key-major kernel)
 constexpr int TK = 64;              // keys per tile (query-major kernel)
-constexpr int QP = DQK + 8;         // LDS pitch (elements) of K rows (query-major kernel)
+constexpr int QP = DQK + 32;        // LDS pitch (elements) of K rows (query-major kernel): 448 B
 }  // namespace bwd
 
 // ---------------------------------------------------------------------------
@@ -491,7 +491,10 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 // ---------------------------------------------------------------------------
 namespace dqk {
 constexpr int NW = 8, QW = 32 * NW;
-constexpr int KSL = bwd::DQK / 8 + 1;  // 16-byte slots per padded K row
+// 16-byte slots per padded K row: at 28 slots (448 B) the 4 rows x 4 slots of
+// a transposing read fall on 16 distinct bank groups (at 25 slots, two-way
+// conflicts). Pad slots copy the row's last chunk.
+constexpr int KSL = bwd::DQK / 8 + 4;
 constexpr int KBLK = bwd::TK * KSL / 64;
 constexpr int KI = (KBLK + NW - 1) / NW;
 constexpr int NF = 3;  // fragment ring slots
@@ -553,7 +556,7 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   for (int i = 0; i < dqk::KI; ++i) {
     const int slot = (wid + i * NW) * 64 + lane;
     krow[i] = slot / dqk::KSL;
-    koff[i] = (uint32_t)((krow[i] * rs_qk + min(slot % dqk::KSL, dqk::KSL - 2) * 8) * 2);
+    koff[i] = (uint32_t)((krow[i] * rs_qk + min(slot % dqk::KSL, DQK / 8 - 1) * 8) * 2);
   }
   auto issue_k = [&](int kt, int buf) {
     const uint16_t* tb = kbase + (size_t)kt * TK * rs_qk;
