@@ -77,7 +77,13 @@ constexpr int OBLK = bwd::QC * OSL / 64;                       // ... per dO chu
 // the two mask-word tiles
 constexpr int K_LD = QBLK + OBLK, K_W = K_LD + 1, NCOPY = K_W + 2;  // 27
 constexpr int NSLOT = (NCOPY + 3) / 4;                              // per B wave, at most (7)
-constexpr int TP = 40;  // pitch (elements) of the dS tile: 80-byte rows spread 16 rows over all 64 banks
+// P and dS tiles: [32 queries][32 keys], 64-byte rows of eight 4-key groups
+// (8 bytes each); group g of query q sits at group g ^ ((q >> 2) & 7). A
+// writes 8-byte groups of 32 queries at one group index, B reads them back
+// transposed (4 queries x 8 groups per 32 lanes): both land on 32 distinct
+// 8-byte bank pairs. (Unswizzled 80-byte rows gave two-way conflicts.)
+constexpr int TP = 32;  // pitch (elements)
+__device__ __forceinline__ int pds_swz(int q) { return (q >> 2) & 7; }
 static_assert(bwd::QC * QSL % 64 == 0 && bwd::QC * OSL % 64 == 0, "chunks must be whole 1 KB blocks");
 static_assert(NCOPY % 4 == 3, "B waves 0-2 issue NSLOT copies per chunk, wave 3 one fewer");
 static_assert(bwd::QC == 32, "one copy instruction moves a chunk's LSE and D, one a mask tile");
@@ -96,8 +102,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   using dkv::NB;
   __shared__ __attribute__((aligned(1024))) unsigned char smQ[NB][dkv::QBLK * 1024];
   __shared__ __attribute__((aligned(1024))) unsigned char smO[NB][dkv::OBLK * 1024];
-  // P and dS of each A wave as row-major [32 queries][32 keys] tiles (pitch
-  // dkv::TP), which B reads transposed as MFMA B operands
+  // P and dS of each A wave as [32 queries][32 keys] tiles (64-byte rows, 4-key
+  // groups swizzled), which B reads transposed as MFMA B operands
   __shared__ __attribute__((aligned(16))) uint16_t smP[2][4][32 * dkv::TP];
   __shared__ __attribute__((aligned(16))) uint16_t smT[2][4][32 * dkv::TP];
   // per chunk: LSE in base-2 units of its 32 queries, then D
@@ -277,6 +283,9 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       oa[par] = (uint32_t)(col * dkv::OPX * 2 + 16 * ((2 * par + half) ^ u));
     }
     const int wsel = (kw >> 1), hsel = (s0 >> 5) & 1;  // the pair's key tile and word half
+    // element offset of this lane's 4-key group 4*p2 + half (+ 2: ^ 8) of row
+    // col in the P / dS tiles: p2 adds ^ 16
+    const int pds_base = col * dkv::TP + 4 * (half ^ dkv::pds_swz(col));
     // a chunk's dS^T fragments are stored right after the next barrier, while
     // the wave waits for its first LDS reads, not at the end of the chunk,
     // where the wave is on the way to the barrier
@@ -329,13 +338,13 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
           // keys 16*p2 + 4*half + 0..3 and 16*p2 + 8 + 4*half + 0..3 of query
           // col: a row segment of the [query][key] P and dS tiles, and, for dS,
           // exactly the dQ kernel's B-operand fragment for this 16-key step
+          // (4-key groups 4*p2 + half and 4*p2 + half + 2 of the row, swizzled)
           const u32x4 pp = pack8(p), dsp = pack8(ds);
-          uint16_t* prow = smP[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
-          uint16_t* trow = smT[it & 1][kw] + col * dkv::TP + 16 * p2 + 4 * half;
-          *(u32x2*)prow = u32x2{pp[0], pp[1]};
-          *(u32x2*)(prow + 8) = u32x2{pp[2], pp[3]};
-          *(u32x2*)trow = u32x2{dsp[0], dsp[1]};
-          *(u32x2*)(trow + 8) = u32x2{dsp[2], dsp[3]};
+          const int e0 = pds_base ^ (16 * p2), e1 = e0 ^ 8;
+          *(u32x2*)(smP[it & 1][kw] + e0) = u32x2{pp[0], pp[1]};
+          *(u32x2*)(smP[it & 1][kw] + e1) = u32x2{pp[2], pp[3]};
+          *(u32x2*)(smT[it & 1][kw] + e0) = u32x2{dsp[0], dsp[1]};
+          *(u32x2*)(smT[it & 1][kw] + e1) = u32x2{dsp[2], dsp[3]};
           pend[p2] = dsp;
           pfr = fr;
           have = true;
@@ -388,6 +397,20 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
         return u32x4{ux[0], ux[1], uy[0], uy[1]};
       };
+      // B operand from a P / dS tile: lane (half, col) gets key col of the
+      // tile's queries r0 + {0..3} and r0 + 8 + {0..3} (r0 a multiple of 4).
+      // Transposing read: source lane j of each 16-lane group g16 points at
+      // the 4-key group 4*g16 + j%4 of query r + j/4.
+      auto pds_frag = [&](const uint16_t* X, int r0) __attribute__((always_inline)) -> u32x4 {
+        const int j = lane & 15, g = 4 * ((lane >> 4) & 1) + (j & 3);
+        const int ra = r0 + (j >> 2), rb = r0 + 8 + (j >> 2);
+        const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_ptr)(X + ra * dkv::TP + 4 * (g ^ dkv::pds_swz(ra))));
+        const v4i16 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_ptr)(X + rb * dkv::TP + 4 * (g ^ dkv::pds_swz(rb))));
+        const u32x2 ua = __builtin_bit_cast(u32x2, a), uc = __builtin_bit_cast(u32x2, c);
+        return u32x4{ua[0], ua[1], uc[0], uc[1]};
+      };
       // dK^T[d, s] += Q^T[d, q] dS[q, s] and dV^T[e, s] += dO^T[e, q] P[q, s]
       // for the chunk of iteration `it`; the query order inside each 16-query
       // step matches the A waves' accumulator rows. When only the first key
@@ -401,8 +424,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         for (int p2 = 0; p2 < 2; ++p2) {
           const int r0 = 16 * p2 + 4 * half;
           // lane (half, col): key col of the block, queries r0 + {0..3, 8..11}
-          const u32x4 d0 = lds_tr_frag(smT[it & 1][2 * kh], dkv::TP, r0, r0 + 8, 0);
-          u32x4 d1 = lds_tr_frag(smT[it & 1][2 * kh + 1], dkv::TP, r0, r0 + 8, 0);
+          const u32x4 d0 = pds_frag(smT[it & 1][2 * kh], r0);
+          u32x4 d1 = pds_frag(smT[it & 1][2 * kh + 1], r0);
           if (!both) d1 = z;
           if constexpr (role == 0) {
 #pragma unroll
@@ -412,8 +435,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
               acc[1][d2] = mfma32(a, d1, acc[1][d2]);
             }
           } else {
-            const u32x4 p0 = lds_tr_frag(smP[it & 1][2 * kh], dkv::TP, r0, r0 + 8, 0);
-            u32x4 p1 = lds_tr_frag(smP[it & 1][2 * kh + 1], dkv::TP, r0, r0 + 8, 0);
+            const u32x4 p0 = pds_frag(smP[it & 1][2 * kh], r0);
+            u32x4 p1 = pds_frag(smP[it & 1][2 * kh + 1], r0);
             if (!both) p1 = z;
             const u32x4 a = tr(sQ + 64 * 5, qt[p2][0], qt[p2][1]);
             acc[0][0] = mfma32(a, d0, acc[0][0]);
