@@ -309,12 +309,20 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         for (int i = 0; i < 16; ++i) { sacc[i] = 0.f; dpacc[i] = 0.f; }
         // transposed scores: S^T = K Q^T and dP^T = V dO^T, so lane (half, col)
         // holds query col and keys 8i + 4*half + r (i, r = 0..3) of the pair
+        // the two accumulator chains alternate, and each operand read is issued
+        // four MFMAs ahead of its use (a read one MFMA ahead waits on the LDS)
 #pragma unroll
-        for (int ks = 0; ks < DQK / 16; ++ks)
+        for (int ks = 0; ks < DQK / 16; ++ks) {
           sacc = mfma32(kf[ks], *(const u32x4*)(sQ + qa[ks & 1] + 64 * (ks >> 1)), sacc);
+          if (ks < DV / 16) dpacc = mfma32(vf[ks], *(const u32x4*)(sO + oa[ks & 1] + 64 * (ks >> 1)), dpacc);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 LDS reads
 #pragma unroll
-        for (int ks = 0; ks < DV / 16; ++ks)
-          dpacc = mfma32(vf[ks], *(const u32x4*)(sO + oa[ks & 1] + 64 * (ks >> 1)), dpacc);
+        for (int g = 0; g < 16; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // the last 4 MFMAs
         // the lane's query: base-2 LSE, D and the pair's 32-bit half of its mask
         // word, shifted so that key 8i + 4*half + r sits at bit 8i + r. FULL
         // tiles have every in-range bit set.
