@@ -297,8 +297,18 @@ hipError_t launch_indexer_teacher(const void* q, const void* k, const float* lse
 __global__ __launch_bounds__(1024) void indexer_kl_count_kernel(const int32_t* __restrict__ idx, int64_t nrows,
                                                                 int K, float* __restrict__ loss2) {
   __shared__ uint32_t part[16];
+  // 16 rows per thread and round trip: the loads of a batch are issued together
   uint32_t c = 0;
-  for (int64_t i = threadIdx.x; i < nrows; i += 1024) c += idx[i * K] >= 0 ? 1u : 0u;
+  for (int64_t i0 = 0; i0 < nrows; i0 += 16 * 1024) {
+    int32_t v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int64_t i = i0 + (int64_t)u * 1024 + threadIdx.x;
+      v[u] = i < nrows ? idx[i * K] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) c += v[u] >= 0 ? 1u : 0u;
+  }
   c = wave_sum(c);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = c;
   __syncthreads();
@@ -329,36 +339,74 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(const ST* __restrict__ 
   float* grow = dscores + row * ld_ds;
   const float N = loss2[1];
   const float invN = N > 0.f ? 1.f / N : 0.f;
-  // pass 1: max of the kept scores
-  float m = -INFINITY;
-  for (int j = lane; j < K; j += 64) {
-    const int s = irow[j];
-    if (s >= 0 && s <= t) m = fmaxf(m, Elem<ST>::load(srow + s));
+  // The index list goes in batches of 64*U entries, U per lane: the U index
+  // loads of a batch are issued together, then the U score gathers, so a
+  // batch costs two memory round trips instead of two per entry.
+  constexpr int U = 16;
+  // pass 1: running max and sum of exp over the kept scores, per lane, then
+  // combined over the wave
+  float m = -INFINITY, z = 0.f;
+  for (int j0 = 0; j0 < K; j0 += 64 * U) {
+    int sj[U];
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + 64 * u + lane;
+      sj[u] = j < K ? irow[j] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = (sj[u] >= 0 && sj[u] <= t) ? Elem<ST>::load(srow + sj[u]) : -INFINITY;
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) bm = fmaxf(bm, v[u]);
+    const float mn = fmaxf(m, bm);
+    if (mn != -INFINITY) {
+      float add = 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) add += expf(v[u] - mn);  // exp(-inf) = 0 for entries not kept
+      z = z * expf(m - mn) + add;                          // m = -inf: z is still 0
+      m = mn;
+    }
   }
-  m = wave_max(m);
+  const float M = wave_max(m);
   float kl = 0.f;
-  if (m != -INFINITY) {
-    float z = 0.f;
-    for (int j = lane; j < K; j += 64) {
-      const int s = irow[j];
-      if (s >= 0 && s <= t) z += expf(Elem<ST>::load(srow + s) - m);
-    }
-    const float logz = logf(wave_sumf(z));
+  if (M != -INFINITY) {
+    const float logz = logf(wave_sumf(m == -INFINITY ? 0.f : z * expf(m - M)));
     // pass 2: KL terms and the gradient at the kept keys
-    for (int j = lane; j < K; j += 64) {
-      const int s = irow[j];
-      if (s < 0 || s > t) continue;  // kept keys lie in [0, t]
-      const float logq = Elem<ST>::load(srow + s) - m - logz;
-      const float p = prow[j];
-      if (p > 0.f) kl += p * (logf(p) - logq);
-      grow[s] = (expf(logq) - p) * invN;
+    for (int j0 = 0; j0 < K; j0 += 64 * U) {
+      int sj[U];
+      float pj[U], v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + 64 * u + lane;
+        sj[u] = j < K ? irow[j] : -1;
+        pj[u] = j < K ? prow[j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = (sj[u] >= 0 && sj[u] <= t) ? Elem<ST>::load(srow + sj[u]) : 0.f;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (sj[u] < 0 || sj[u] > t) continue;  // kept keys lie in [0, t]
+        const float logq = v[u] - M - logz;
+        const float p = pj[u];
+        if (p > 0.f) kl += p * (logf(p) - logq);
+        grow[sj[u]] = (expf(logq) - p) * invN;
+      }
     }
   }
-  // zeros over [0, t] at the keys that are not kept
+  // zeros over [0, t] at the keys that are not kept: 64 mask words per load,
+  // lane w holding word w0 + w
   const uint64_t* brow = bits + row * W;
-  for (int w0 = 0; w0 <= t / 64; ++w0) {
-    const int s = 64 * w0 + lane;
-    if (s <= t && !((brow[w0] >> lane) & 1ull)) grow[s] = 0.f;
+  const int nwd = t / 64 + 1;
+  for (int w0 = 0; w0 < nwd; w0 += 64) {
+    const uint64_t bw = w0 + lane < nwd ? brow[w0 + lane] : 0ull;
+    const int nw = min(64, nwd - w0);
+    for (int w = 0; w < nw; ++w) {
+      const uint64_t word = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(bw >> 32), w) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)bw, w);
+      const int s = 64 * (w0 + w) + lane;
+      if (s <= t && !((word >> lane) & 1ull)) grow[s] = 0.f;
+    }
   }
   kl = wave_sumf(kl);
   if (lane == 0) row_kl[row] = kl;
