@@ -330,33 +330,46 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         const uint32_t Wq = smW[bi][wsel][hsel][col] >> (4 * half);
         u32x4* fr = dsf + (((size_t)bh * dsf_tile_base(nchunks) + dsf_tile_base(qc) + kt_lo + (kw >> 1)) * 4 +
                            2 * (kw & 1)) * 64 + lane;
+        // P and dS. On a chunk of a FULL tile every pair is kept and the mask
+        // select is skipped; not on a ragged last chunk, whose rows past S (kept
+        // out of the tile class) rely on their cleared mask words.
+        auto softmax = [&](auto FULLC) __attribute__((always_inline)) {
+          constexpr bool FULL = decltype(FULLC)::value;
 #pragma unroll
-        for (int p2 = 0; p2 < 2; ++p2) {
-          float p[8], ds[8];
+          for (int p2 = 0; p2 < 2; ++p2) {
+            float p[8], ds[8];
 #pragma unroll
-          for (int c8 = 0; c8 < 8; ++c8) {
-            const int r = 8 * p2 + c8;
-            // keep ? P : 0 as a bit select on an all-ones / all-zeros field
-            const int keep = __builtin_amdgcn_sbfe((int)Wq, 8 * (r >> 2) + (r & 3), 1);
-            const float pr =
-                __int_as_float(keep & __float_as_int(fast_exp2(fmaf(sacc[r], scale_log2, -Lq))));
-            p[c8] = pr;
-            ds[c8] = pr * (dpacc[r] - Dq);
+            for (int c8 = 0; c8 < 8; ++c8) {
+              const int r = 8 * p2 + c8;
+              const float e = fast_exp2(fmaf(sacc[r], scale_log2, -Lq));
+              float pr = e;
+              if constexpr (!FULL) {
+                // keep ? P : 0 as a bit select on an all-ones / all-zeros field
+                const int keep = __builtin_amdgcn_sbfe((int)Wq, 8 * (r >> 2) + (r & 3), 1);
+                pr = __int_as_float(keep & __float_as_int(e));
+              }
+              p[c8] = pr;
+              ds[c8] = pr * (dpacc[r] - Dq);
+            }
+            // keys 16*p2 + 4*half + 0..3 and 16*p2 + 8 + 4*half + 0..3 of query
+            // col: a row segment of the [query][key] P and dS tiles, and, for dS,
+            // exactly the dQ kernel's B-operand fragment for this 16-key step
+            // (4-key groups 4*p2 + half and 4*p2 + half + 2 of the row, swizzled)
+            const u32x4 pp = pack8(p), dsp = pack8(ds);
+            const int o0 = pds_base ^ (16 * p2), o1 = o0 ^ 8;
+            *(u32x2*)(smP[it & 1][kw] + o0) = u32x2{pp[0], pp[1]};
+            *(u32x2*)(smP[it & 1][kw] + o1) = u32x2{pp[2], pp[3]};
+            *(u32x2*)(smT[it & 1][kw] + o0) = u32x2{dsp[0], dsp[1]};
+            *(u32x2*)(smT[it & 1][kw] + o1) = u32x2{dsp[2], dsp[3]};
+            pend[p2] = dsp;
+            pfr = fr;
+            have = true;
           }
-          // keys 16*p2 + 4*half + 0..3 and 16*p2 + 8 + 4*half + 0..3 of query
-          // col: a row segment of the [query][key] P and dS tiles, and, for dS,
-          // exactly the dQ kernel's B-operand fragment for this 16-key step
-          // (4-key groups 4*p2 + half and 4*p2 + half + 2 of the row, swizzled)
-          const u32x4 pp = pack8(p), dsp = pack8(ds);
-          const int e0 = pds_base ^ (16 * p2), e1 = e0 ^ 8;
-          *(u32x2*)(smP[it & 1][kw] + e0) = u32x2{pp[0], pp[1]};
-          *(u32x2*)(smP[it & 1][kw] + e1) = u32x2{pp[2], pp[3]};
-          *(u32x2*)(smT[it & 1][kw] + e0) = u32x2{dsp[0], dsp[1]};
-          *(u32x2*)(smT[it & 1][kw] + e1) = u32x2{dsp[2], dsp[3]};
-          pend[p2] = dsp;
-          pfr = fr;
-          have = true;
-        }
+        };
+        if (__builtin_amdgcn_readfirstlane((int)scls[wsel][qc >> 2]) == 2 && qc * QC + QC <= S)
+          softmax(std::integral_constant<bool, true>{});
+        else
+          softmax(std::integral_constant<bool, false>{});
       }
       e0 = e1;
       e1 = e2;
