@@ -26,7 +26,10 @@ The same line also carries:
   * "indexer_loss": the indexer's KL auxiliary loss after the step (teacher,
     student KL, indexer gradients), timed per call (not part of the step);
   * "roofline" for the dominant kernel, and "cpu_baseline" (the float64
-    oracle on a bounded row sample).
+    oracle on a bounded row sample);
+  * "measured_peaks": a bf16 GEMM and a device copy timed on the same GPU,
+    and every kernel's fraction of them ("frac_measured") next to its
+    fraction of the datasheet peak ("frac").
 """
 from __future__ import annotations
 
@@ -352,6 +355,51 @@ def time_steps(cfg, steps, warmup, scrub=None, x=None):
     return per, step_ms, t_start.elapsed_time(t_end), x, path
 
 
+def measured_peaks():
+    """Ceilings measured on this GPU, to set the kernels' rates against besides
+    the datasheet peaks: a bf16 GEMM (8192^3, N(0,1) operands, the vendor
+    library through torch) and a plain device-to-device copy of 2 GiB (bytes
+    read + written). Each is the best of 10 timed calls after 3 warm-ups."""
+    import torch
+    n = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    src = torch.ones(1 << 31, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def best(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+    t_mm = best(lambda: torch.matmul(a, b))
+    t_cp = best(lambda: dst.copy_(src))
+    del a, b, src, dst
+    torch.cuda.empty_cache()
+    return {"gemm_bf16_tflops": 2.0 * n ** 3 / (t_mm * 1e-3) / 1e12, "gemm_shape": [n, n, n],
+            "copy_gbs": 2.0 * (1 << 31) / (t_cp * 1e-3) / 1e9, "copy_bytes": 1 << 31,
+            "datasheet": {"bf16_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}}
+
+
+def add_measured(kernels, mp):
+    """frac_measured: each kernel's rate over the measured GEMM or copy rate."""
+    if mp is None:
+        return
+    for v in kernels.values():
+        ref = mp["gemm_bf16_tflops"] if v.get("bound") == "mfma" else mp["copy_gbs"]
+        v["frac_measured"] = v["achieved"] / ref
+
+
 def kernel_table(cfg, wk, per):
     kern = {
         "index_scores": ("mfma", wk["indexer"]),
@@ -550,6 +598,14 @@ def main():
         c1 = tiny_latency()
         log(f"  {c1['step_us']['median']:.1f} us per step")
 
+    log("measured ceilings: bf16 GEMM and device copy")
+    mp = measured_peaks()
+    log(f"  GEMM {mp['gemm_bf16_tflops']:.0f} TFLOP/s, copy {mp['copy_gbs']:.0f} GB/s")
+    add_measured(kernels, mp)
+    if c4 is not None:
+        add_measured(c4["kernels"], mp)
+    roofline["frac_measured"] = kernels[dom]["frac_measured"]
+
     cpu = None
     if x_cpu is not None:
         log("timing the float64 oracle on a row sample (cpu baseline)")
@@ -573,6 +629,7 @@ def main():
         "c1": c1,
         "indexer_loss": indexer_loss,
         "roofline": roofline,
+        "measured_peaks": mp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
