@@ -468,8 +468,8 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   constexpr int NBLK = TK * SL / 64;          // 1 KB blocks per k_idx tile (20)
   constexpr int BI = (NBLK + 7) / 8;          // per wave (3): waves 4-7 copy two blocks and a gradient row
   static_assert(NBLK == 20 && QPW == 4, "copy slots: waves 0-3 take 3 blocks, waves 4-7 2 blocks + 1 row");
-  __shared__ __attribute__((aligned(1024))) uint16_t smK[2][TK * PX];
-  __shared__ __attribute__((aligned(16))) float smG[2][QPW][TK];  // the tile's gradient entries per query
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[3][TK * PX];
+  __shared__ __attribute__((aligned(16))) float smG[3][QPW][TK];  // the tile's gradient entries per query
   __shared__ uint8_t scls[kMaxTiles];                             // the query tile's class row
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -503,8 +503,8 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
   // pad slots copy the row's last chunk; rows past S copy row S-1. Waves 4-7
   // also copy query (w - 4)'s gradient entries of the tile (keys past S copy
   // key S-1's; entries past the query are never used). Every copy goes through
-  // the untracked path and every wave issues exactly three, waited for at the
-  // top of the next iteration.
+  // the untracked path and every wave issues exactly three per tile, so a
+  // counted wait finds one tile complete while the next is in flight.
   auto issue = [&](int kt, int buf) {
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -538,14 +538,20 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
     while (n <= kt_last && scls[n] == 0) ++n;
     return n;
   };
+  // three tile buffers, copies two tiles ahead
   int kt = next_tile(-1);
+  int kn = next_tile(kt);
   if (kt <= kt_last) issue(kt, 0);
+  if (kn <= kt_last) issue(kn, 1);
   int buf = 0;
   while (kt <= kt_last) {
-    const int kn = next_tile(kt);
-    wait_vmem();      // this wave's copies of tile kt (issued one tile back)
-    lds_barrier();    // tile kt visible; every wave is done with the other buffer
-    if (kn <= kt_last) issue(kn, buf ^ 1);
+    const int kn2 = next_tile(kn);
+    if (kn <= kt_last)
+      wait_vmem_n<BI>();  // tile kt's copies are in; tile kn's (the last BI) may still fly
+    else
+      wait_vmem();
+    lds_barrier();  // tile kt visible; every wave is done with the buffer tile kn2 goes to
+    if (kn2 <= kt_last) issue(kn2, buf == 0 ? 2 : buf - 1);
     const uint16_t* sK = smK[buf];
     const float* gq = smG[buf][wid / HB];
 #pragma unroll
@@ -580,8 +586,9 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
         for (int db = 0; db < DI / 32; ++db) dqacc[db] = mfma32(lds_tr_frag_x(sK, PX, r0, r0 + 8, db * 32), gb, dqacc[db]);
       }
     }
-    buf ^= 1;
+    buf = buf == 2 ? 0 : buf + 1;
     kt = kn;
+    kn = kn2;
   }
   dwacc = half_sum(dwacc);
   if (qvalid) {
