@@ -43,7 +43,7 @@ constexpr int QP = DQK + 32;        // LDS pitch (elements) of K rows (query-maj
 //     (so one LSE, one D and one mask word per lane) and 16 keys, which is
 //     exactly the dQ kernel's B-operand fragment of dS^T: A stores it to the
 //     workspace straight from registers. P and dS also go to LDS as
-//     row-major [32 queries][32 keys] tiles.
+//     [32 queries][32 keys] tiles (4-key groups swizzled, see dkv::TP).
 //   waves 4-7 ("B", dV^T and dK^T accumulators): dV^T += dO^T P and
 //     dK^T += Q^T dS, one chunk behind A, with P and dS read transposed. A B
 //     wave owns 64 keys (two A waves' P and dS tiles) and half of their ten
@@ -55,8 +55,10 @@ constexpr int QP = DQK + 32;        // LDS pitch (elements) of K rows (query-maj
 // tiles for the workgroup's keys are skipped.
 // A chunk's operands -- Q and dO rows, LSE and D, and the 32-bit halves of the
 // mask words of the workgroup's two key tiles -- all reach LDS through direct
-// global->LDS copies, issued by the B waves only: a wave stalls while the copy
-// path accepts its copies, and A is the critical path. A chunk is only ~1.3k
+// global->LDS copies, issued by the B waves only, right after the barrier: a
+// wave stalls while the copy path accepts its copies, and every other
+// placement measured (on A, on both roles, later in B's update) was slower.
+// A chunk is only ~1.3k
 // MFMA cycles of work, less than a global load's latency, so copies run two
 // chunks ahead: four chunk buffers (B reads the previous chunk, A the current
 // one, one is in flight, one being issued). Each B wave issues a fixed number
