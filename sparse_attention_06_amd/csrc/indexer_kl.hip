@@ -42,7 +42,7 @@
 //       each key block's queries split into segments across workgroups:
 //       U = Q_t K^T (heads on rows, keys on columns, the lane's k_idx
 //       fragments are the B operand), G = g w [U > 0], dk^T += Q_t^T G, with
-//       q_idx[t] staged in LDS per query. The float32 partials of the head
+//       q_idx[t] staged in LDS two queries per stage. The float32 partials of the head
 //       blocks and segments (staged in dq_idx's memory before dq is written)
 //       are added in a fixed order by indexer_bwd_dk_combine_kernel.
 // No atomics anywhere, so every result is deterministic.
@@ -625,9 +625,10 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
   // copies per wave per query: 20 q blocks over 8 waves (3, 3, 3, 3, 2, 2, 2, 2), then
   // waves 4-5 the gradient entries (2 x 64 floats), wave 6 the weights, wave 7 a filler
   constexpr int NCP = 3;
-  __shared__ __attribute__((aligned(1024))) uint16_t smQ[NBUF][HI * PX];
-  __shared__ __attribute__((aligned(16))) float smG[NBUF][KB];
-  __shared__ __attribute__((aligned(16))) uint16_t smW[NBUF][128];  // 64 weights (+ filler room)
+  // NBUF stages of two queries each (one barrier per pair)
+  __shared__ __attribute__((aligned(1024))) uint16_t smQ[NBUF][2][HI * PX];
+  __shared__ __attribute__((aligned(16))) float smG[NBUF][2][KB];
+  __shared__ __attribute__((aligned(16))) uint16_t smW[NBUF][2][128];  // 64 weights (+ filler room)
   __shared__ uint16_t qlist[kMaxS / 128];
   __shared__ int s_nq;
 
@@ -683,7 +684,7 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
   // the queries, in order: every query of the listed 128-query tiles (k0 is a
   // multiple of 128, so the first listed tile starts at or after the keys);
   // the query after tt, moving to the next listed tile at a tile end or at S
-  auto advance = [&](int& qi, int tt) -> int {
+  auto advance = [&](int& qi, int tt) __attribute__((always_inline)) -> int {
     const int n = tt + 1;
     if ((n & 127) != 0 && n < S) return n;
     ++qi;
@@ -709,7 +710,7 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
       coff[i] = (uint32_t)min(k0 + lane, S - 1) * 4u;  // filler: the same data as the first gradient slot
     }
   }
-  auto issue = [&](int tt, int bi) {
+  auto issue = [&](int tt, int bi, int k) __attribute__((always_inline)) {
     const size_t row = (size_t)b * S + tt;
     const uint16_t* qs = uniform_ptr(q_idx + row * HI * DI);
     const float* gs = uniform_ptr(dscores + row * ld);
@@ -718,13 +719,13 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
     for (int i = 0; i < NCP; ++i) {
       const int blk = wid + 8 * i;
       if (blk < QBLK)
-        g2lds16_async_off(qs, coff[i], (char*)smQ[bi] + blk * 1024);
+        g2lds16_async_off(qs, coff[i], (char*)smQ[bi][k] + blk * 1024);
       else if (blk == QBLK + 0 || blk == QBLK + 1)
-        g2lds4_async_off(gs, coff[i], smG[bi] + 64 * (blk - QBLK));
+        g2lds4_async_off(gs, coff[i], smG[bi][k] + 64 * (blk - QBLK));
       else if (blk == QBLK + 2)
-        g2lds4_async_off(ws, coff[i], smW[bi]);
+        g2lds4_async_off(ws, coff[i], smW[bi][k]);
       else
-        g2lds4_async_off(gs, coff[i], smG[bi]);
+        g2lds4_async_off(gs, coff[i], smG[bi][k]);
     }
   };
   static_assert(QBLK + 3 <= 8 * NCP, "copy slots");
@@ -735,36 +736,32 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dkacc[i][j] = 0.f;
 
+  // the queries in pairs, in order; a stage holds a pair, copies run two pairs
+  // ahead. A pair with one query copies it twice, so that every wave issues
+  // exactly 2 * NCP copies per stage.
   int qiC = 0;
-  const int tA0 = nq > 0 ? 128 * (int)qlist[0] : -1;
-  int tA = tA0, tB = -1, tC = -1;
-  if (tA >= 0) tB = advance(qiC, tA);
-  if (tB >= 0) tC = advance(qiC, tB);
-  if (tA >= 0) issue(tA, 0);
-  if (tB >= 0) issue(tB, 1);
-  int bi = 0;
-  while (tA >= 0) {
-    if (tB >= 0)
-      wait_vmem_n<NCP>();  // query tA's copies done; tB's may still fly
-    else
-      wait_vmem();
-    lds_barrier();
-    if (tC >= 0) issue(tC, (bi + 2) % NBUF);
-    const uint16_t* sQ = smQ[bi];
+  auto next_q = [&](int tt) __attribute__((always_inline)) -> int { return tt >= 0 ? advance(qiC, tt) : -1; };
+  auto issue2 = [&](int t0, int t1, int bi) __attribute__((always_inline)) {
+    issue(t0, bi, 0);
+    issue(t1 >= 0 ? t1 : t0, bi, 1);
+  };
+  // one query of the stage in buffer bi, slot k
+  auto compute = [&](int tq, int bi, int k) __attribute__((always_inline)) {
+    const uint16_t* sQ = smQ[bi][k];
     // U[head, key] = q_idx[t, head] . k_idx[key]: heads on rows (this wave's
     // 32-head block), keys on columns
-    if (k0 + kbk * 32 <= tA) {  // wave-uniform: some of the wave's keys are at or before the query
+    if (k0 + kbk * 32 <= tq) {  // wave-uniform: some of the wave's keys are at or before the query
       f32x16 u;
 #pragma unroll
       for (int i = 0; i < 16; ++i) u[i] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) u = mfma32(lds_frag_x(sQ, PX, hb * 32 + col, 2 * ks + half), kf[ks], u);
-      const float g = sk <= tA ? smG[bi][kbk * 32 + col] : 0.f;
+      const float g = sk <= tq ? smG[bi][k][kbk * 32 + col] : 0.f;
       // accumulator rows 4i .. 4i+3 are heads hb*32 + 8i + 4*half + 0..3: one 8-byte read each
       float G[16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x2 wv = *(const u32x2*)(smW[bi] + hb * 32 + 8 * i + 4 * half);
+        const u32x2 wv = *(const u32x2*)(smW[bi][k] + hb * 32 + 8 * i + 4 * half);
         const float wr[4] = {__uint_as_float(wv[0] << 16), __uint_as_float(wv[0] & 0xffff0000u),
                              __uint_as_float(wv[1] << 16), __uint_as_float(wv[1] & 0xffff0000u)};
 #pragma unroll
@@ -779,10 +776,30 @@ __global__ __launch_bounds__(512) void indexer_bwd_dk_kernel(
         for (int db = 0; db < DI / 32; ++db) dkacc[db] = mfma32(lds_tr_frag_x(sQ, PX, r0, r0 + 8, db * 32), gb, dkacc[db]);
       }
     }
+  };
+  int a0 = nq > 0 ? 128 * (int)qlist[0] : -1;
+  int a1 = next_q(a0);
+  int b0 = next_q(a1), b1 = next_q(b0);
+  int c0 = next_q(b1), c1 = next_q(c0);
+  if (a0 >= 0) issue2(a0, a1, 0);
+  if (b0 >= 0) issue2(b0, b1, 1);
+  int bi = 0;
+  while (a0 >= 0) {
+    if (b0 >= 0)
+      wait_vmem_n<2 * NCP>();  // pair a's copies done; pair b's may still fly
+    else
+      wait_vmem();
+    lds_barrier();
+    if (c0 >= 0) issue2(c0, c1, (bi + 2) % NBUF);
+    compute(a0, bi, 0);
+    if (a1 >= 0) compute(a1, bi, 1);
     bi = (bi + 1) % NBUF;
-    tA = tB;
-    tB = tC;
-    if (tC >= 0) tC = advance(qiC, tC);
+    a0 = b0;
+    a1 = b1;
+    b0 = c0;
+    b1 = c1;
+    c0 = next_q(c1);
+    c1 = next_q(c0);
   }
   wait_vmem();
   // partial [(seg * 2 + hb)][b][key][d] (float32), zeros where nothing was added
