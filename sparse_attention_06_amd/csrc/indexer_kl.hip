@@ -569,7 +569,12 @@ __global__ __launch_bounds__(512) void indexer_bwd_dq_kernel(
       for (int i = 0; i < 4; ++i) {
         const f32x4 gv = *(const f32x4*)(gq + kb * 32 + 8 * i + 4 * half);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g[4 * i + j] = s0 + 8 * i + 4 * half + j <= t ? gv[j] : 0.f;
+        for (int j = 0; j < 4; ++j) g[4 * i + j] = gv[j];
+      }
+      if (s0 + 31 > t) {  // wave-uniform: only the diagonal block has keys past the query
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (s0 + 8 * (r >> 2) + 4 * half + (r & 3) > t) g[r] = 0.f;
       }
       float G[16];
 #pragma unroll
