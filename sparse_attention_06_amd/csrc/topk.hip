@@ -129,8 +129,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
   const int32_t* segb = seg ? seg + (size_t)b * S : nullptr;
 
   if (!segb && L <= K) {
-    // causal-only row with at most K keys: every key 0..t, no score read
-    for (int i = lane; i < K; i += 64) idx_row[i] = i < L ? i : -1;
+    // causal-only row with at most K keys: every key 0..t, no score read;
+    // 16-byte stores when the rows are 16-byte aligned (K a multiple of 4)
+    if ((K & 3) == 0) {
+      for (int i = 4 * lane; i < K; i += 256)
+        *(int4*)(idx_row + i) = make_int4(i < L ? i : -1, i + 1 < L ? i + 1 : -1, i + 2 < L ? i + 2 : -1,
+                                          i + 3 < L ? i + 3 : -1);
+    } else {
+      for (int i = lane; i < K; i += 64) idx_row[i] = i < L ? i : -1;
+    }
     for (int w = lane; w < W; w += 64)
       bits_row[w] = w < L / 64 ? ~0ull : (w == L / 64 && (L & 63) ? (1ull << (L & 63)) - 1ull : 0ull);
     return;
