@@ -8,28 +8,31 @@
 //
 // MFMA kernel (bf16, Dqk = 192, Dv = 128). A workgroup is one (b, h, 256-query
 // block) with 8 waves of 32 queries each, two waves per SIMD. It walks the
-// 64-key tiles up to the diagonal. Tiles that are EMPTY for both of its
-// 128-query tiles are skipped outright. A wave whose own tile is EMPTY, or
-// whose 32 queries keep no key of the tile, idles on it. PARTIAL tiles read
-// one u64 selection word per query.
+// 64-key tiles that are non-empty for either of its two 128-query tiles; the
+// list of them is compacted into LDS once at start, so the walk costs one LDS
+// read per tile, issued a tile ahead. PARTIAL tiles read one u64 selection
+// word per query (loaded unconditionally a tile ahead, the tile class applied
+// where the word is used, so no branch ever joins on a pending load).
 //   S^T = K Q^T: keys on MFMA rows, queries on columns, so each lane owns one
-//   query and 32 of the tile's 64 logits. The online-softmax max and sum are
-//   in-lane, with one exchange between lane halves. Q stays in VGPRs.
-//   O^T += V^T P^T: the probabilities go straight from the S^T accumulator
-//   into the B operand. The key order inside each 16-wide k step is permuted
-//   to match the accumulator layout. V^T comes from the natural V tile in LDS
-//   through the gfx950 transposing LDS read, with the same permutation.
-// The tile walk reads the workgroup's tile-class rows from LDS, where they are
-// staged at start. K/V tiles are double buffered and filled by direct
-// global->LDS copies; the next tile's copies are issued right after the
-// barrier and land while the current tile is computed. The per-query
-// selection word of the next tile is loaded before those copies, so waiting
-// for it never waits for them.
-// LDS pitches: K rows 400 B (b128 reads of 16 consecutive rows hit distinct
-// banks), V rows 320 B (the four rows of a transposing read cover all 64
-// banks). exp2 is the hardware v_exp_f32, with the scale folded in
-// (scale * log2 e). O is rescaled only when a tile max passes the reference
-// max by more than 2^8.
+//   query and 16 logits of each 32-key block. Max and sum are in-lane, with
+//   one exchange between lane halves. Q stays in VGPRs.
+//   O^T += V^T P^T: probabilities go straight from the S^T accumulator into
+//   the B operand, with the key order inside each 16-key step permuted to
+//   match; V^T comes through the transposing LDS read with the same order.
+// Each wave software-pipelines its 32-key blocks: while the MFMAs of block
+// i+1's scores run, the VALU forms block i's probabilities; while block i's
+// PV MFMAs run, block i+1 is masked and its max taken. Hard scheduling fences
+// hold that interleave (six groups of two score MFMAs, four of two PV MFMAs).
+// The online-softmax reference max is updated per block, lazily: O and l are
+// rescaled only when a block max passes it by more than 2^8.
+// K tiles are double buffered and V tiles triple buffered, both copied two
+// tiles ahead by direct global->LDS copies spread over the score groups of the
+// step after the tile barrier; one barrier per tile. Tiles are unpadded
+// (384-byte K rows, 256-byte V rows) with XOR-swizzled 16-byte chunks (K:
+// chunk ^ ((row >> 1) & 7); V: chunk ^ 4 * (row & 3)) that keep the K row
+// reads and the V transposing reads free of bank conflicts, so a tile is a
+// whole number of 1 KB copy blocks per wave (3 K + 2 V). exp2 is the hardware
+// v_exp_f32 with the scale folded in (scale * log2 e).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -37,176 +40,86 @@ namespace dsa {
 
 namespace fwd {
 constexpr int DQK = 192, DV = 128, TK = 64;
-constexpr int NW = 8;                // waves per workgroup: 2 per SIMD
+constexpr int NW = 8;                // waves per workgroup: two per SIMD
 constexpr int QW = 32 * NW;          // queries per workgroup (two 128-query tiles)
 constexpr int KS = DQK / 16;         // k steps of S^T
-constexpr int NB = 2;                // K/V tile buffers
-constexpr int KSL = DQK / 8 + 1;     // 16-byte slots per LDS K row (one pad slot): 400 B
-constexpr int VSL = DV / 8 + 4;      // ... per V row (four pad slots): 320 B
-constexpr int KP = KSL * 8;          // LDS pitch of a K row (elements)
-constexpr int VP = VSL * 8;          // LDS pitch of a V row
-constexpr int KBLK = TK * KSL / 64;  // 1 KB blocks per K tile (25)
-constexpr int VBLK = TK * VSL / 64;  // ... per V tile (20)
-constexpr int KI = (KBLK + NW - 1) / NW, VI = (VBLK + NW - 1) / NW;  // blocks per wave
-static_assert(TK * KSL % 64 == 0 && TK * VSL % 64 == 0, "tiles must be whole 1 KB blocks");
+constexpr int KCH = DQK / 8, VCH = DV / 8;  // 16-byte chunks per K row (24) and V row (16), unpadded
+constexpr int KBLK = TK * KCH / 64, VBLK = TK * VCH / 64;  // 1 KB blocks per tile: 24, 16
+constexpr int KC = KBLK / NW, VC = VBLK / NW;  // copies per wave: 3 K, 2 V
+constexpr int NC = KC + VC;
+constexpr int KBUF = 2, VBUF = 3;    // K tiles double, V tiles triple buffered
+static_assert(KBLK % NW == 0 && VBLK % NW == 0, "copies split evenly over the waves");
+// swizzles: physical 16-byte chunk of logical chunk c in row r
+__device__ __forceinline__ constexpr int kswz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ constexpr int vswz(int r, int c) { return c ^ (4 * (r & 3)); }
 }  // namespace fwd
-
-// Scores phase of one 64-key tile for a wave's 32 queries: S^T into sacc,
-// masked (dropped keys become -inf), and the tile max of each query in log2
-// units. This lane's keys are kb*32 + 8i + 4*half + r (i, r in 0..3); with
-// the query word shifted right by 4*half, the bit of accumulator register r of
-// half kb sits at position 32*kb + 8*(r/4) + r%4.
-__device__ __forceinline__ float fwd_scores(const uint16_t* sK, const u32x4 (&qf)[fwd::KS], uint64_t mw,
-                                            bool full, float scale_log2, f32x16 (&sacc)[2]) {
-  using namespace fwd;
-  const int lane = threadIdx.x & 63, half = lane >> 5, col = lane & 31;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const u32x4 a = *(const u32x4*)(sK + (kb * 32 + col) * KP + ks * 16 + 8 * half);
-      sacc[kb] = mfma32(a, qf[ks], sacc[kb]);
-    }
-  float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  if (full) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], sacc[kb][r]);
-  } else {
-    const uint64_t mwh = mw >> (4 * half);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t w = (uint32_t)(mwh >> (32 * kb));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // keep ? x : -inf as a bit select on an all-ones / all-zeros field
-        const int keep = __builtin_amdgcn_sbfe((int)w, 8 * (r >> 2) + (r & 3), 1);
-        const float x = __int_as_float((keep & __float_as_int(sacc[kb][r])) | (~keep & (int)0xff800000u));
-        sacc[kb][r] = x;
-        tm[r & 3] = fmaxf(tm[r & 3], x);
-      }
-    }
-  }
-  const float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-  return half_max(tmax) * scale_log2;  // scale > 0 commutes with max
-}
-
-// Update phase: online-softmax step with the masked logits of fwd_scores and
-// the PV MFMAs against the tile's V. Lazy rescaling: probabilities are taken
-// relative to a reference max m that only moves when the tile max exceeds it
-// by more than 8 (log2 units), so p <= 2^8. O and l share the reference, so
-// the result is unchanged; the O rescale (64 accumulator multiplies) is rare.
-__device__ __forceinline__ void fwd_update(const uint16_t* sV, const f32x16 (&sacc)[2], float tmax,
-                                           float scale_log2, float& m, float& l, f32x16 (&oacc)[4]) {
-  using namespace fwd;
-  const int lane = threadIdx.x & 63, half = lane >> 5;
-  const bool bump = tmax > m + 8.f;
-  if (__ballot(bump)) {
-    const float m_new = bump ? tmax : m;
-    const float alpha = bump ? fast_exp2(m - m_new) : 1.f;  // m = -inf on a first bump: alpha = 0
-    l *= alpha;
-#pragma unroll
-    for (int eb = 0; eb < 4; ++eb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
-    m = m_new;
-  }
-  const float neg_m = m == -INFINITY ? 0.f : -m;
-  // O^T[e, q] += V^T[e, key] P^T[key, q]; V^T fragments read transposed from the V tile,
-  // keys permuted inside each 16-key step to match the S^T accumulator rows
-  float ls[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
-      float pv8[8];
-#pragma unroll
-      for (int c8 = 0; c8 < 8; ++c8) {
-        pv8[c8] = fast_exp2(fmaf(sacc[kb][8 * p2 + c8], scale_log2, neg_m));
-        ls[c8 & 3] += pv8[c8];
-      }
-      const u32x4 pb = u32x4{pack_bf2(pv8[0], pv8[1]), pack_bf2(pv8[2], pv8[3]), pack_bf2(pv8[4], pv8[5]),
-                             pack_bf2(pv8[6], pv8[7])};
-      const int r0 = kb * 32 + 16 * p2 + 4 * half;
-#pragma unroll
-      for (int eb = 0; eb < 4; ++eb) oacc[eb] = mfma32(lds_tr_frag(sV, VP, r0, r0 + 8, eb * 32), pb, oacc[eb]);
-    }
-  l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
-}
 
 __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
     float scale_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace fwd;
-  __shared__ __attribute__((aligned(1024))) uint16_t smK[NB][TK * KP];
-  __shared__ __attribute__((aligned(1024))) uint16_t smV[NB][TK * VP];
-  __shared__ uint8_t scls[2][kMaxTiles];  // tile classes of the workgroup's two 128-query tiles
+  __shared__ __attribute__((aligned(1024))) uint16_t smK[KBUF][KBLK * 512];
+  __shared__ __attribute__((aligned(1024))) uint16_t smV[VBUF][VBLK * 512];
+  __shared__ uint8_t scls[2][kMaxTiles];
+  __shared__ uint32_t tlist[kMaxTiles + 2];  // non-empty tiles: kt | class0 << 16 | class1 << 24
+  __shared__ int s_ntl;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
   const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
-  // the query blocks of a (b, h) on one XCD (they share K/V), costliest first
   int bh, qw;
   grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
   const int b = bh / H, h = bh % H;
-  const int tq = qw * QW + wid * 32 + col;  // this lane's query
+  const int tq = qw * QW + wid * 32 + col;
   const bool qvalid = tq < S;
-  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);  // this wave's 128-query tile
+  const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
   const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
-  const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;  // token strides
+  const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
   const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
   const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
 
-  // this wave's 1 KB blocks of a tile: block j covers slots 64j .. 64j+63 of the
-  // padded [64 rows][KSL or VSL slots] layout; pad slots copy a harmless chunk.
-  // Row and chunk of each slot are fixed, so byte offsets within the tile's
-  // rows are computed once.
-  uint32_t koff[KI], voff[VI];
-#pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int slot = (wid + i * NW) * 64 + lane;
-    koff[i] = (uint32_t)(((slot / KSL) * rs_qk + min(slot % KSL, KSL - 2) * 8) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < VI; ++i) {
-    const int slot = (wid + i * NW) * 64 + lane;
-    voff[i] = (uint32_t)(((slot / VSL) * rs_v + min(slot % VSL, DV / 8 - 1) * 8) * 2);
-  }
-  auto issue = [&](int kt, int buf) {
-    const char* kt_base = (const char*)(kbase + (size_t)kt * TK * rs_qk);
-    const char* vt_base = (const char*)(vbase + (size_t)kt * TK * rs_v);
-    const int lim = S - 1 - kt * TK;  // last in-range row of the tile
-    if (lim >= TK - 1) {
-#pragma unroll
-      for (int i = 0; i < KI; ++i)
-        if (wid + i * NW < KBLK) g2lds16(kt_base + koff[i], (char*)smK[buf] + (wid + i * NW) * 1024);
-#pragma unroll
-      for (int i = 0; i < VI; ++i)
-        if (wid + i * NW < VBLK) g2lds16(vt_base + voff[i], (char*)smV[buf] + (wid + i * NW) * 1024);
-    } else {  // ragged last tile: rows past S copy row S-1
-#pragma unroll
-      for (int i = 0; i < KI; ++i)
-        if (wid + i * NW < KBLK) {
-          const int row = ((wid + i * NW) * 64 + lane) / KSL;
-          const int dr = row - min(row, lim);
-          g2lds16(kt_base + koff[i] - (size_t)dr * rs_qk * 2, (char*)smK[buf] + (wid + i * NW) * 1024);
-        }
-#pragma unroll
-      for (int i = 0; i < VI; ++i)
-        if (wid + i * NW < VBLK) {
-          const int row = ((wid + i * NW) * 64 + lane) / VSL;
-          const int dr = row - min(row, lim);
-          g2lds16(vt_base + voff[i] - (size_t)dr * rs_v * 2, (char*)smV[buf] + (wid + i * NW) * 1024);
-        }
+  // copy c < KC moves K block wid + 8c, copy KC + c' V block wid + 8c'. Lane l
+  // fills LDS slot 64*blk + l, i.e. row slot / chunks-per-row at physical chunk
+  // slot % chunks-per-row, from the logical chunk the swizzle puts there.
+  auto copy_row = [&](int c) -> int {
+    const int blk = wid + NW * (c < KC ? c : c - KC);
+    return c < KC ? (blk * 64 + lane) / KCH : (blk * 64 + lane) / VCH;
+  };
+  auto copy_off = [&](int c, int row) -> uint32_t {
+    const int blk = wid + NW * (c < KC ? c : c - KC);
+    if (c < KC) {
+      const int pc = (blk * 64 + lane) % KCH;
+      return (uint32_t)((row * rs_qk + kswz(row, pc) * 8) * 2);
     }
+    const int pc = (blk * 64 + lane) % VCH;
+    return (uint32_t)((row * rs_v + vswz(row, pc) * 8) * 2);
+  };
+  uint32_t coff[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) coff[c] = copy_off(c, copy_row(c));
+  // copy c of the tile whose K/V rows start at ksrc / vsrc; lim is the tile's
+  // last in-range row. On a ragged last tile, rows past it copy from row lim
+  // (finite data under keys that every mask drops)
+  auto copy = [&](int c, const uint16_t* ksrc, const uint16_t* vsrc, int lim, uint16_t* kdst, uint16_t* vdst)
+      __attribute__((always_inline)) {
+    uint32_t off = coff[c];
+    if (lim < TK - 1) {  // wave-uniform, rare: recomputed here, never hoisted into live registers
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int blk = wid + NW * (c < KC ? c : c - KC);
+      const int slot = blk * 64 + ln;
+      const int row = c < KC ? slot / KCH : slot / VCH;
+      const int r = min(row, lim);
+      off = c < KC ? (uint32_t)((r * rs_qk + kswz(row, slot % KCH) * 8) * 2)
+                   : (uint32_t)((r * rs_v + vswz(row, slot % VCH) * 8) * 2);
+    }
+    if (c < KC)
+      g2lds16_async_off(ksrc, off, (char*)kdst + (wid + NW * c) * 1024);
+    else
+      g2lds16_async_off(vsrc, off, (char*)vdst + (wid + NW * (c - KC)) * 1024);
   };
 
   u32x4 qf[KS];
@@ -217,7 +130,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     qf[ks] = z;
   }
 
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, neg_m = 0.f;
   f32x16 oacc[4];
 #pragma unroll
   for (int eb = 0; eb < 4; ++eb)
@@ -229,40 +142,225 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
   stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
   const uint8_t* cls0 = scls[0];
   const uint8_t* cls1 = scls[1];
-  const uint8_t* clsw = scls[qt_w - qt0];
   const uint64_t* bits_q = bits + ((size_t)b * S + (qvalid ? tq : 0)) * W;
-  auto next_tile = [&](int kt) {
-    int n = kt + 1;
-    while (n <= kt_last && cls0[n] == 0 && cls1[n] == 0) ++n;
-    return n;
+  // this lane's selection word of a tile is loaded unconditionally (clamped
+  // index) and its class applied where it is used, so no branch joins on a
+  // pending load: sel 0 = no key kept, 1 = all kept (FULL), 2 = the loaded word
+  const int qsh = 16 + 8 * (qt_w - qt0);
+  auto word_raw = [&](int kt) -> uint64_t { return bits_q[min(kt, kt_last)]; };
+  auto word_sel = [&](uint32_t ent) -> int {
+    const int c = (int)((ent >> qsh) & 0xff);
+    return !qvalid || (int)(ent & 0xffff) > kt_last || c == 0 ? 0 : c == 2 ? 1 : 2;
   };
-  // this lane's selection word of tile kt (FULL: all ones; EMPTY: none)
-  auto word = [&](int kt) -> uint64_t {
-    const int c = clsw[kt];
-    if (!qvalid || c == 0) return 0ull;
-    return c == 2 ? ~0ull : bits_q[kt];
+  auto word_of = [&](uint64_t raw, int sel) -> uint64_t { return sel == 2 ? raw : sel == 1 ? ~0ull : 0ull; };
+  auto issue_tile = [&](int kt, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+    const uint16_t* ks = uniform_ptr(kbase + (size_t)kt * TK * rs_qk);
+    const uint16_t* vs = uniform_ptr(vbase + (size_t)kt * TK * rs_v);
+    const int lim = S - 1 - kt * TK;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) copy(c, ks, vs, lim, kdst, vdst);
   };
 
-  f32x16 sacc[2];
-  __syncthreads();  // class rows staged
-  int kt = next_tile(-1);
-  if (kt <= kt_last) issue(kt, 0);
-  uint64_t mw = kt <= kt_last ? word(kt) : 0ull;
-  int buf = 0;
-  while (kt <= kt_last) {
-    const int kn = next_tile(kt);
-    const int c = clsw[kt];
-    wait_vmem();
-    __syncthreads();  // tile kt visible in `buf`; every wave is done with the other buffer
-    const uint64_t mw_n = kn <= kt_last ? word(kn) : 0ull;
-    if (kn <= kt_last) issue(kn, buf ^ 1);
-    if (c != 0 && __ballot(mw != 0ull)) {
-      const float tmax = fwd_scores(smK[buf], qf, mw, c == 2, scale_log2, sacc);
-      fwd_update(smV[buf], sacc, tmax, scale_log2, m, l, oacc);
+  // logits r0..r0+3 of a 32-key block masked (keep ? x : -inf), with the running max
+  auto mask_max = [&](f32x16& s, uint64_t mw, int kb, int r0, float (&tm)[4]) __attribute__((always_inline)) {
+    const uint32_t w = (uint32_t)((mw >> (4 * half)) >> (32 * kb));
+#pragma unroll
+    for (int r = r0; r < r0 + 4; ++r) {
+      const int keep = __builtin_amdgcn_sbfe((int)w, 8 * (r >> 2) + (r & 3), 1);
+      const float x = __int_as_float((keep & __float_as_int(s[r])) | (~keep & (int)0xff800000u));
+      s[r] = x;
+      tm[r & 3] = fmaxf(tm[r & 3], x);
     }
-    mw = mw_n;
-    buf ^= 1;
-    kt = kn;
+  };
+  // lazy max: O and l are rescaled only when a block max passes the reference max by more than 2^8
+  auto bump = [&](float tmax) __attribute__((always_inline)) {
+    const bool bq = tmax > m + 8.f;
+    if (__ballot(bq)) {
+      const float m_new = bq ? tmax : m;
+      const float alpha = bq ? fast_exp2(m - m_new) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[eb][i] *= alpha;
+      m = m_new;
+    }
+    neg_m = m == -INFINITY ? 0.f : -m;
+  };
+  // LDS fragment reads: a per-lane base (one per k step mod 4 for K, one per
+  // 32-dim block for V, the swizzle folded in) plus a constant offset
+  const int g_k = (col >> 1) & 7;
+  int kb4[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) kb4[bb] = col * DQK + 8 * ((2 * bb + half) ^ g_k);
+  const int jj = lane & 15, rr = jj >> 2;
+  int vb4[4];
+#pragma unroll
+  for (int eb = 0; eb < 4; ++eb)
+    vb4[eb] = (4 * half + rr) * DV + 8 * (4 * (eb ^ rr) + 2 * ((lane >> 4) & 1) + ((jj & 3) >> 1)) + 4 * (jj & 1);
+  // S^T A fragment: keys kb*32 + col, dims 16ks + 8*half ..
+  auto kread = [&](const uint16_t* sK, int ks, int kb) __attribute__((always_inline)) -> u32x4 {
+    return *(const u32x4*)(sK + kb4[ks & 3] + kb * 32 * DQK + 64 * (ks >> 2));
+  };
+  // V^T fragment for keys kb*32 + 16*p2 + {4h..4h+3, 8+4h..8+4h+3} (h the lane half), dims eb*32..
+  auto vread = [&](const uint16_t* sV, int kb, int p2, int eb) __attribute__((always_inline)) -> u32x4 {
+    const uint16_t* base = sV + vb4[eb] + (kb * 32 + 16 * p2) * DV;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)base);
+    const v4i16 bb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * DV));
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, bb);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+  };
+
+  u32x4 pf[2];
+  float ls[4];
+  // probabilities of 8 logits (p2 half, c8 in [c0, c0+4)) of a block
+  auto soft4 = [&](const f32x16& sc, int p2, int c0, float (&pv8)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c8 = c0; c8 < c0 + 4; ++c8) {
+      pv8[c8] = fast_exp2(fmaf(sc[8 * p2 + c8], scale_log2, neg_m));
+      ls[c8 & 3] += pv8[c8];
+    }
+  };
+  auto pack = [&](int p2, const float (&pv8)[8]) __attribute__((always_inline)) {
+    pf[p2] = u32x4{pack_bf2(pv8[0], pv8[1]), pack_bf2(pv8[2], pv8[3]), pack_bf2(pv8[4], pv8[5]),
+                   pack_bf2(pv8[6], pv8[7])};
+  };
+
+  f32x16 S0, S1;
+  u32x4 ka[2], vf[2];
+  float pvA[8], pvB[8];
+  __syncthreads();  // class rows staged
+  if (wid == 0) {   // compact the tiles that are non-empty for either query tile
+    int cnt = 0;
+    for (int base = 0; base <= kt_last; base += 64) {
+      const int kt = base + lane;
+      const int c0 = kt <= kt_last ? cls0[kt] : 0, c1 = kt <= kt_last ? cls1[kt] : 0;
+      const bool ne = (c0 | c1) != 0;
+      const uint64_t mb = __ballot(ne);
+      if (ne) tlist[cnt + lanes_below(mb)] = (uint32_t)kt | ((uint32_t)c0 << 16) | ((uint32_t)c1 << 24);
+      cnt += __popcll(mb);
+    }
+    if (lane < 2) tlist[cnt + lane] = (uint32_t)(kt_last + 1);  // two sentinels: past the last tile
+    if (lane == 0) s_ntl = cnt;
+  }
+  __syncthreads();
+  const int ntl = s_ntl;
+  if (ntl == 0) {
+    if (qvalid) {
+      uint16_t* orow = o + ((size_t)b * S + tq) * rs_v + (size_t)h * DV;
+#pragma unroll
+      for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) *(u32x2*)(orow + eb * 32 + 8 * g + 4 * half) = u32x2{0u, 0u};
+      if (half == 0) lse[((size_t)b * H + h) * S + tq] = -INFINITY;
+    }
+    return;
+  }
+  uint32_t e_c = tlist[0], e_n = tlist[1];
+  int kc = (int)(e_c & 0xffff), kn = (int)(e_n & 0xffff);
+  int jpos = 0;  // position of tile kc in the workgroup's tile list
+  issue_tile(kc, smK[0], smV[0]);
+  if (kn <= kt_last) issue_tile(kn, smK[1], smV[1]);
+  uint64_t raw_c = word_raw(kc), raw_n = word_raw(kn);
+  int sel_c = word_sel(e_c), sel_n = word_sel(e_n);
+  wait_vmem();
+  lds_barrier();
+  const uint64_t mw_c0 = word_of(raw_c, sel_c);
+  // block (0, 0): scores, mask, max
+  {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S0[i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) S0 = mfma32(kread(smK[0], ks, 0), qf[ks], S0);
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += 4) mask_max(S0, mw_c0, 0, r0, tm);
+    bump(half_max(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]))) * scale_log2);
+  }
+
+  // One pipeline step: probabilities of block Sc (in pvA/pvB, then pf) while
+  // the scores of the next block (key half kbn of the K tile at sKn) go into
+  // Sn; then O += V^T P^T of block Sc (key half kbc of the V tile at sVc)
+  // while Sn is masked with word mwn and its max taken. `cp(g)` issues the
+  // tile copies of score group g.
+  auto step = [&](f32x16& Sc, f32x16& Sn, const uint16_t* sKn, int kbn, uint64_t mwn, const uint16_t* sVc,
+                  int kbc, auto cp) __attribute__((always_inline)) {
+    ls[0] = ls[1] = ls[2] = ls[3] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Sn[i] = 0.f;
+    ka[0] = kread(sKn, 0, kbn);
+    ka[1] = kread(sKn, 1, kbn);
+    __builtin_amdgcn_sched_barrier(0);
+    // phase 1: 6 groups of 2 score MFMAs; probabilities in slices of 4
+#pragma unroll
+    for (int g = 0; g < 6; ++g) {
+      cp(g);
+      Sn = mfma32(ka[0], qf[2 * g], Sn);
+      if (2 * g + 2 < KS) ka[0] = kread(sKn, 2 * g + 2, kbn);
+      Sn = mfma32(ka[1], qf[2 * g + 1], Sn);
+      if (2 * g + 3 < KS) ka[1] = kread(sKn, 2 * g + 3, kbn);
+      if (g < 2) soft4(Sc, 0, 4 * (g & 1), pvA);
+      else if (g < 4) soft4(Sc, 1, 4 * (g & 1), pvB);
+      if (g == 1) pack(0, pvA);
+      if (g == 3) pack(1, pvB);
+      if (g == 5) {
+        vf[0] = vread(sVc, kbc, 0, 0);
+        vf[1] = vread(sVc, kbc, 0, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // phase 2: 4 groups of 2 PV MFMAs; masks and max of the next block
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int p2 = g >> 1, e0 = 2 * (g & 1);
+      oacc[e0] = mfma32(vf[0], pf[p2], oacc[e0]);
+      if (g + 1 < 4) vf[0] = vread(sVc, kbc, (g + 1) >> 1, 2 * ((g + 1) & 1));
+      oacc[e0 + 1] = mfma32(vf[1], pf[p2], oacc[e0 + 1]);
+      if (g + 1 < 4) vf[1] = vread(sVc, kbc, (g + 1) >> 1, 2 * ((g + 1) & 1) + 1);
+      mask_max(Sn, mwn, kbn, 4 * g, tm);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    bump(half_max(fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]))) * scale_log2);
+  };
+  auto no_cp = [](int) {};
+
+  for (;;) {
+    const uint16_t* sKc = smK[jpos & 1];
+    const uint16_t* sKn = smK[(jpos + 1) & 1];
+    const uint16_t* sVc = smV[jpos % 3];
+    const uint32_t e_nn = tlist[min(jpos + 2, ntl + 1)];  // read early; used after the barrier
+    // step (j, 0): scores of key half 1 of tile j, probabilities and O of half 0
+    step(S0, S1, sKc, 1, word_of(raw_c, sel_c), sVc, 0, no_cp);
+    const bool has_n = kn <= kt_last;
+    // every wave is done with K(j) and V(j-1); K(j+1) and V(j+1) have landed
+    wait_vmem();
+    lds_barrier();
+    const int knn = (int)(__builtin_amdgcn_readfirstlane((int)e_nn) & 0xffff);
+    const uint64_t raw_nn = word_raw(knn);
+    const int sel_nn = word_sel(e_nn);
+    // copies of tile j+2 (when there is none, of tile j again: valid memory,
+    // into buffers that are not read again)
+    const int kcp = knn <= kt_last ? knn : kc;
+    const uint16_t* ks = uniform_ptr(kbase + (size_t)kcp * TK * rs_qk);
+    const uint16_t* vs = uniform_ptr(vbase + (size_t)kcp * TK * rs_v);
+    const int lim = S - 1 - kcp * TK;
+    uint16_t* kd = smK[jpos & 1];
+    uint16_t* vd = smV[(jpos + 2) % 3];
+    auto cp = [&](int g) __attribute__((always_inline)) { if (g < NC) copy(g, ks, vs, lim, kd, vd); };
+    // step (j, 1): scores of key half 0 of tile j+1 (after the last tile: of a
+    // stale buffer, masked to nothing and dropped), probabilities and O of half 1 of tile j
+    step(S1, S0, sKn, 0, word_of(raw_n, sel_n), sVc, 1, cp);
+    if (!has_n) {
+      wait_vmem();  // no copy may still be landing when the workgroup's LDS is released
+      break;
+    }
+    raw_c = raw_n; sel_c = sel_n;
+    raw_n = raw_nn; sel_n = sel_nn;
+    kc = kn;
+    kn = knn;
+    ++jpos;
   }
 
   const float l_tot = half_sum(l);
@@ -279,8 +377,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
         *(u32x2*)(orow + e) = pk2;
       }
     if (half == 0)
-      lse[((size_t)b * H + h) * S + tq] =
-          l_tot > 0.f ? m * 0.69314718055994530942f + logf(l_tot) : -INFINITY;
+      lse[((size_t)b * H + h) * S + tq] = l_tot > 0.f ? m * 0.69314718055994530942f + logf(l_tot) : -INFINITY;
   }
 }
 
