@@ -41,6 +41,15 @@ Sources (page title · section):
         heads; the teacher's inputs carry no gradient (the KL section at the
         end states the readings).
 
+  [P4c] "Add Flash Attention Support to Deepseek v4" · Description: the V4
+        layers CSA (compression ratio 4) and HCA (ratio 128) attend over
+        compressed KV blocks with block-aligned masks (causal, sliding
+        window); compressed KV is padded to a multiple of the kernel's block.
+  [P5c] "Implement QK attention head chunking for CSA [Deepseek v4]" ·
+        Description: CSA works on compressed blocks, and its indexer scores
+        queries against them (the compressed-attention section at the end
+        states the readings).
+
 The indexer formula is not printed on the pages. It is the standard one of
 the method: I[t,s] = sum_j w[t,j] * ReLU(q_idx[t,j,:] . k_idx[s,:]), with a
 per-token, per-index-head weight w and one index key per token shared by all
@@ -706,3 +715,85 @@ def indexer_bwd(q_idx, k_idx, w, dscores, seg, rows):
             dq[b, r] = G @ k_idx[b, vs]
             dk[b, vs] += G.T @ q_idx[b, t]
     return dq, dk, dw
+
+
+# ----------------------------------------------------------------------------
+# next row: compressed sparse attention (DeepSeek-V4 CSA)          [P4c], [P5c]
+# ----------------------------------------------------------------------------
+# [P4c] says only that CSA compresses KV at ratio 4 and needs block-aligned
+# causal (and sliding-window) masks; [P5c] that its indexer scores queries
+# against the compressed blocks. Neither gives the compressor, the block-level
+# causal rule or the window. Readings taken here:
+#   * The compressed K, V and index keys are inputs (the compressor's
+#     arithmetic is not given; like RoPE it is preparation before the path).
+#     There are Sk = floor(S / ratio) entries; entry c stands for tokens
+#     ratio*c .. ratio*c + ratio - 1, and tokens past ratio*Sk have none.
+#   * Block causality: query t sees entry c when the entry's whole block lies
+#     at or before t, i.e. ratio*c + ratio - 1 <= t. Rows t < ratio - 1 see
+#     nothing (O = 0, LSE = -inf). With ratio 1 this is DSA's causal rule.
+#   * Indexer, top-k and attention are DSA's formulas over the visible
+#     entries. No segment IDs (the pages do not say how compression meets
+#     packed documents) and no sliding window (its size and combination are
+#     not given).
+def csa_valid_row(Sk: int, ratio: int, t: int) -> np.ndarray:
+    """Boolean [Sk]: entry c is visible to query t when ratio*c + ratio - 1 <= t."""
+    c = np.arange(Sk)
+    return ratio * c + (ratio - 1) <= t
+
+
+def csa_index_scores(q_idx, k_idx_c, w, ratio: int, rows) -> np.ndarray:
+    """Indexer scores over the compressed index keys for the given query rows.
+
+    q_idx [B,S,Hi,Di], k_idx_c [B,Sk,Di], w [B,S,Hi]. Returns [B, len(rows), Sk]
+    float64: I[b, t, c] for visible c, -inf elsewhere.
+    """
+    q_idx = np.asarray(q_idx, dtype=np.float64)
+    k_idx_c = np.asarray(k_idx_c, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    B, Sk = k_idx_c.shape[:2]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((B, rows.size, Sk), NEG_INF, dtype=np.float64)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            out[b, r] = index_scores_row(q_idx[b, t], w[b, t], k_idx_c[b], csa_valid_row(Sk, ratio, int(t)))
+    return out
+
+
+def csa_topk(scores, ratio: int, rows, K: int, Sk: int) -> np.ndarray:
+    """Top-k lists [B, len(rows), K] int32 over the visible entries of each
+    row (ascending, padded with -1); ``scores`` is [B, len(rows), Sk]."""
+    scores = np.asarray(scores)
+    B = scores.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.full((B, rows.size, K), -1, dtype=np.int32)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            sel = topk_row(scores[b, r], csa_valid_row(Sk, ratio, int(t)), K)
+            out[b, r, : sel.size] = sel
+    return out
+
+
+def csa_attention_fwd(q, k_c, v_c, idx, ratio: int, scale: float, rows):
+    """Softmax attention of the given query rows over their kept compressed
+    entries (index list intersected with visibility).
+
+    q [B,S,H,Dqk], k_c [B,Sk,H,Dqk], v_c [B,Sk,H,Dv], idx [B, len(rows), K].
+    Returns O [B, len(rows), H, Dv] and LSE [B, H, len(rows)]; a row with no
+    kept entry has O = 0 and LSE = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_c = np.asarray(k_c, dtype=np.float64)
+    v_c = np.asarray(v_c, dtype=np.float64)
+    B, Sk, H, _ = k_c.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.zeros((B, rows.size, H, v_c.shape[-1]))
+    L = np.full((B, H, rows.size), NEG_INF)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            sel = np.asarray(idx[b, r])
+            sel = sel[sel >= 0]
+            ks = np.unique(sel[csa_valid_row(Sk, ratio, int(t))[sel]])
+            if ks.size == 0:
+                continue
+            O[b, r], L[b, :, r] = attention_fwd_row(q[b, t], k_c[b, ks], v_c[b, ks], scale)
+    return O, L

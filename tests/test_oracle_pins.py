@@ -1040,3 +1040,128 @@ def test_indexer_kl_planted_mistakes_fail_a_pin(monkeypatch):
         with pytest.raises(AssertionError):
             test()
         monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- compressed sparse attention (CSA)
+def test_csa_visibility_brute_force():
+    """csa_valid_row against the block-completeness reading, token by token:
+    entry c is visible to t when every token of its block lies at or before t."""
+    for ratio in (1, 2, 3, 4, 7):
+        Sk = 40 // ratio
+        for t in range(44):
+            want = np.array([all(ratio * c + i <= t for i in range(ratio)) for c in range(Sk)], dtype=bool)
+            assert np.array_equal(ref.csa_valid_row(Sk, ratio, t), want), (ratio, t)
+    for t in range(30):  # ratio 1 is DSA's causal rule
+        assert np.array_equal(ref.csa_valid_row(30, 1, t), ref.valid_row(None, 30, t))
+    # the first complete block of ratio 4 ends at token 3
+    assert not ref.csa_valid_row(10, 4, 2).any()
+    assert np.array_equal(np.nonzero(ref.csa_valid_row(10, 4, 3))[0], [0])
+    assert np.array_equal(np.nonzero(ref.csa_valid_row(10, 4, 8))[0], [0, 1])
+
+
+def _on_token_axis(x_c, ratio, S):
+    """Compressed entries placed at their blocks' last tokens ratio*c + ratio - 1 of
+    a token axis of length S (zeros at every other position)."""
+    x_c = np.asarray(x_c, dtype=np.float64)
+    Sk = x_c.shape[1]
+    out = np.zeros((x_c.shape[0], S) + x_c.shape[2:])
+    out[:, ratio * np.arange(Sk) + ratio - 1] = x_c
+    return out
+
+
+def test_csa_equals_dsa_on_the_token_axis():
+    """CSA over Sk compressed entries is DSA over the S token positions with
+    entry c at p(c) = ratio*c + ratio - 1 and every other position excluded:
+    the pinned DSA indexer, top-k and attention give the same scores, lists
+    (mapped back to entries) and outputs."""
+    rng = np.random.default_rng(5)
+    B, S, ratio, Hi, Di, H, Dqk, Dv, K = 2, 39, 4, 3, 8, 2, 8, 6, 3
+    Sk = S // ratio
+    pos = ratio * np.arange(Sk) + ratio - 1
+    q_idx = rng.standard_normal((B, S, Hi, Di))
+    w = rng.standard_normal((B, S, Hi))
+    k_idx_c = rng.standard_normal((B, Sk, Di))
+    q = rng.standard_normal((B, S, H, Dqk))
+    k_c = rng.standard_normal((B, Sk, H, Dqk))
+    v_c = rng.standard_normal((B, Sk, H, Dv))
+    scale = 0.4
+    rows = np.arange(S)
+    sc = ref.csa_index_scores(q_idx, k_idx_c, w, ratio, rows)
+    idx_c = ref.csa_topk(sc, ratio, rows, K, Sk)
+    O_c, L_c = ref.csa_attention_fwd(q, k_c, v_c, idx_c, ratio, scale, rows)
+    k_tok = _on_token_axis(k_idx_c, ratio, S)
+    on_grid = np.isin(np.arange(S), pos)
+    idx_tok = np.full((B, S, K), -1, np.int32)
+    for b in range(B):
+        for t in range(S):
+            valid_tok = ref.valid_row(None, S, t) & on_grid
+            s_tok = ref.index_scores_row(q_idx[b, t], w[b, t], k_tok[b], valid_tok)
+            np.testing.assert_allclose(sc[b, t], s_tok[pos], rtol=1e-12, atol=1e-12)
+            sel_tok = ref.topk_row(s_tok, valid_tok, K)
+            sel_c = idx_c[b, t][idx_c[b, t] >= 0]
+            assert np.array_equal(pos[sel_c], sel_tok), (b, t)
+            idx_tok[b, t, : sel_tok.size] = sel_tok
+    O_t, L_t = ref.attention_fwd(q, _on_token_axis(k_c, ratio, S), _on_token_axis(v_c, ratio, S), idx_tok, None,
+                                 scale, rows)
+    np.testing.assert_allclose(O_c, O_t, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(L_c), np.isinf(L_t))
+    fin = np.isfinite(L_t)
+    np.testing.assert_allclose(L_c[fin], L_t[fin], rtol=1e-12, atol=1e-12)
+    assert np.isinf(L_c[:, :, : ratio - 1]).all() and not O_c[:, : ratio - 1].any()  # rows before the first block
+
+
+def test_csa_keep_all_is_block_causal_dense_attention():
+    """Index lists naming every entry (future ones included) give torch float64
+    SDPA over the compressed keys under the block-causal mask."""
+    rng = np.random.default_rng(6)
+    B, S, ratio, H, Dqk, Dv = 2, 29, 4, 3, 8, 5
+    Sk = S // ratio
+    q = rng.standard_normal((B, S, H, Dqk))
+    k_c = rng.standard_normal((B, Sk, H, Dqk))
+    v_c = rng.standard_normal((B, Sk, H, Dv))
+    scale = 0.3
+    rows = np.arange(S)
+    idx = np.broadcast_to(np.arange(Sk, dtype=np.int32), (B, S, Sk)).copy()
+    O, L = ref.csa_attention_fwd(q, k_c, v_c, idx, ratio, scale, rows)
+    vis = np.array([[ratio * c + ratio - 1 <= t for c in range(Sk)] for t in range(S)])
+    live = vis.any(axis=1)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)[:, :, live]
+    tk = torch.from_numpy(k_c).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v_c).permute(0, 2, 1, 3)
+    m = torch.from_numpy(vis[live])
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=scale)
+    np.testing.assert_allclose(O[:, live], want.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-12)
+    logits = torch.einsum("bhtd,bhsd->bhts", tq, tk) * scale
+    lse = torch.logsumexp(logits.masked_fill(~m, -math.inf), dim=-1)
+    np.testing.assert_allclose(L[:, :, live], lse.numpy(), rtol=1e-10, atol=1e-12)
+    assert not O[:, ~live].any() and np.isinf(L[:, :, ~live]).all()
+
+
+def test_csa_planted_mistakes_fail_a_pin(monkeypatch):
+    orig_fwd = ref.csa_attention_fwd
+
+    def from_block_start(Sk, ratio, t):      # sees a block from its first token
+        return ratio * np.arange(Sk) <= t
+
+    def one_token_late(Sk, ratio, t):        # needs one token past the block
+        return ratio * np.arange(Sk) + ratio <= t
+
+    def no_visibility_cut(q, k_c, v_c, idx, ratio, scale, rows):   # index list used as is
+        saved = ref.csa_valid_row
+        try:
+            ref.csa_valid_row = lambda Sk, r, t: np.ones(Sk, dtype=bool)
+            return orig_fwd(q, k_c, v_c, idx, ratio, scale, rows)
+        finally:
+            ref.csa_valid_row = saved
+
+    for bad in (from_block_start, one_token_late):
+        monkeypatch.setattr(ref, "csa_valid_row", bad)
+        with pytest.raises(AssertionError):
+            test_csa_visibility_brute_force()
+        with pytest.raises(AssertionError):
+            test_csa_keep_all_is_block_causal_dense_attention()
+        monkeypatch.undo()
+    monkeypatch.setattr(ref, "csa_attention_fwd", no_visibility_cut)
+    with pytest.raises(AssertionError):
+        test_csa_keep_all_is_block_causal_dense_attention()
+    monkeypatch.undo()
