@@ -211,14 +211,15 @@ def pack_bits(M) -> np.ndarray:
 
 
 def tile_classes(M, TQ: int, TK: int) -> np.ndarray:
-    """Tile class [B, ceil(S/TQ), ceil(S/TK)] uint8 of a selection matrix.
+    """Tile class [B, ceil(S/TQ), ceil(Sk/TK)] uint8 of a selection matrix
+    M [B, S, Sk] (Sk = S for token keys, the entry count for compressed keys).
 
-    0 = no selected pair in the tile, 2 = every in-range pair (t < S, s < S)
+    0 = no selected pair in the tile, 2 = every in-range pair (t < S, s < Sk)
     selected, 1 = otherwise.
     """
     M = np.asarray(M, dtype=bool)
-    B, S, _ = M.shape
-    nq, nk = (S + TQ - 1) // TQ, (S + TK - 1) // TK
+    B, S, Sk = M.shape
+    nq, nk = (S + TQ - 1) // TQ, (Sk + TK - 1) // TK
     out = np.zeros((B, nq, nk), dtype=np.uint8)
     for b in range(B):
         for i in range(nq):

@@ -232,6 +232,19 @@ def test_pack_bits_and_tile_classes_brute():
             nz = np.nonzero(M[b, t])[0]
             idx[b, t, : nz.size] = nz
     assert np.array_equal(ref.selection_matrix(idx, S), M)
+    # a rectangular selection (compressed keys): S rows, Sk keys
+    Sk = 45
+    Mr = rng.random((B, S, Sk)) < 0.4
+    Mr[:, :32, :16] = True
+    bits = ref.pack_bits(Mr)
+    assert bits.shape == (B, S, 1)
+    for b, t, s in itertools.product(range(B), range(S), range(Sk)):
+        assert bool((int(bits[b, t, s // 64]) >> (s % 64)) & 1) == Mr[b, t, s]
+    cls = ref.tile_classes(Mr, TQ, TK)
+    assert cls.shape == (B, -(-S // TQ), -(-Sk // TK))
+    for b, i, j in itertools.product(range(B), range(cls.shape[1]), range(cls.shape[2])):
+        vals = [Mr[b, t, s] for t in range(i * TQ, min(S, (i + 1) * TQ)) for s in range(j * TK, min(Sk, (j + 1) * TK))]
+        assert cls[b, i, j] == (2 if all(vals) else (1 if any(vals) else 0))
 
 
 # --------------------------------------------------------- attention fwd pins
