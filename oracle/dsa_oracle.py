@@ -778,7 +778,8 @@ def csa_attention_fwd(q, k_c, v_c, idx, ratio: int, scale: float, rows):
     """Softmax attention of the given query rows over their kept compressed
     entries (index list intersected with visibility).
 
-    q [B,S,H,Dqk], k_c [B,Sk,H,Dqk], v_c [B,Sk,H,Dv], idx [B, len(rows), K].
+    q [B,S,H,Dqk], k_c [B,Sk,H,Dqk], v_c [B,Sk,H,Dv], idx [B, len(rows), K]
+    (entries outside [0, Sk) name no entry and are dropped).
     Returns O [B, len(rows), H, Dv] and LSE [B, H, len(rows)]; a row with no
     kept entry has O = 0 and LSE = -inf.
     """
@@ -792,7 +793,7 @@ def csa_attention_fwd(q, k_c, v_c, idx, ratio: int, scale: float, rows):
     for b in range(B):
         for r, t in enumerate(rows):
             sel = np.asarray(idx[b, r])
-            sel = sel[sel >= 0]
+            sel = sel[(sel >= 0) & (sel < Sk)]      # entries that do not exist are not visible
             ks = np.unique(sel[csa_valid_row(Sk, ratio, int(t))[sel]])
             if ks.size == 0:
                 continue

@@ -1135,6 +1135,7 @@ def test_csa_keep_all_is_block_causal_dense_attention():
     scale = 0.3
     rows = np.arange(S)
     idx = np.broadcast_to(np.arange(Sk, dtype=np.int32), (B, S, Sk)).copy()
+    idx = np.concatenate([idx, np.full((B, S, 2), [Sk, -1], np.int32)], axis=-1)  # no entry Sk: dropped
     O, L = ref.csa_attention_fwd(q, k_c, v_c, idx, ratio, scale, rows)
     vis = np.array([[ratio * c + ratio - 1 <= t for c in range(Sk)] for t in range(S)])
     live = vis.any(axis=1)
