@@ -229,6 +229,45 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
                                dsa_dtype dtype, void* o, float* lse, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Compressed sparse attention (CSA): the forward path over compressed keys.
+ * Source: "Add Flash Attention Support to Deepseek v4", Description (CSA, at
+ * compression ratio 4, attends over compressed KV blocks with block-aligned
+ * causal masks); "Implement QK attention head chunking for CSA [Deepseek v4]",
+ * Description (its indexer scores queries against the compressed blocks).
+ * The pages give neither the compressor nor the block rule; the readings:
+ *   * k_idx, k and v hold Sk = S / ratio (floor) compressed entries per batch
+ *     row, made by the caller; entry c stands for tokens ratio*c .. ratio*c +
+ *     ratio - 1 (tokens past ratio*Sk belong to no entry);
+ *   * query t sees entry c iff ratio*c + ratio - 1 <= t (its block is
+ *     complete); rows t < ratio - 1 see nothing (O = 0, LSE = -inf);
+ *   * indexer, selection rule and attention are the DSA ones over the visible
+ *     entries. No segment IDs, no sliding window. ratio 1 is DSA exactly.
+ * Layouts follow the DSA calls with the key axis of length Sk:
+ *   q_idx [B,S,Hi,Di], k_idx [B,Sk,Di], w [B,S,Hi]; scores [B,nrows,ld], ld >= Sk
+ *   q [B,S,H,Dqk], k [B,Sk,H,Dqk], v [B,Sk,H,Dv]; o [B,S,H,Dv], lse [B,H,S]
+ *   idx [B,S,K] int32 entry indices ascending, then -1 (dsa_csa_build_mask
+ *       ignores entries < 0, >= Sk or not visible to the row; duplicates are
+ *       harmless)
+ *   mask  dsa_csa_mask_bytes(B,S,Sk) bytes: sel_bits uint64 [B][S][ceil(Sk/64)]
+ *         then tile_cls uint8 [B][ceil(S/DSA_TILE_Q)][ceil(Sk/DSA_TILE_K)]
+ * Errors: DSA_ERR_INVALID_ARG for ratio < 1, Sk != S / ratio, Sk < 1, ld < Sk
+ * or the argument checks of the matching DSA call; dtype, dims, row slabs and
+ * kernels (MFMA or plain) as in those calls. Only the forward is provided: the
+ * backward calls take token-level (ratio 1) masks.
+ * ------------------------------------------------------------------------- */
+size_t dsa_csa_mask_bytes(int B, int S, int Sk);
+dsa_status dsa_csa_index_scores(const void* q_idx, const void* k_idx, const void* w, int B, int S, int Sk,
+                                int ratio, int Hi, int Di, dsa_dtype in_dtype, int row0, int nrows,
+                                void* scores, dsa_dtype score_dtype, int64_t ld, void* stream);
+dsa_status dsa_csa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, int B, int S, int Sk, int ratio,
+                        int K, int row0, int nrows, int32_t* idx, void* mask, void* stream);
+dsa_status dsa_csa_build_mask(const int32_t* idx, int B, int S, int Sk, int ratio, int K, void* mask,
+                              void* stream);
+dsa_status dsa_csa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask, int B, int S,
+                                   int Sk, int ratio, int H, int Dqk, int Dv, float softmax_scale,
+                                   dsa_dtype dtype, void* o, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
  * dsa_sparse_attn_bwd -- gradients of sum(O * dout) w.r.t. q, k, v.
  * Source: "Support Ring Attention with DeepSeek DSA Sparse Indexer", Backward
  * Flow (dQ = dP K, dK = dP^T Q, dV = P^T dO, each on the kept entries; dK/dV

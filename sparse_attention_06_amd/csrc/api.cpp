@@ -49,7 +49,8 @@ dsa_status hip_status(hipError_t e, const char* what) {
 bool dtype_ok(dsa_dtype d) { return d == DSA_BF16 || d == DSA_FP32; }
 
 uint64_t* bits_of(void* mask) { return (uint64_t*)mask; }
-uint8_t* cls_of(void* mask, int B, int S) { return (uint8_t*)mask + dsa::bits_bytes(B, S); }
+uint8_t* cls_of(void* mask, int B, int S, int Sk) { return (uint8_t*)mask + dsa::bits_bytes(B, S, Sk); }
+uint8_t* cls_of(void* mask, int B, int S) { return cls_of(mask, B, S, S); }
 
 }  // namespace
 
@@ -105,6 +106,28 @@ const char* dsa_last_error(void) { return g_err; }
 
 int dsa_version(void) { return 100; }  // 0.1.0
 
+// the indexer over Sk keys of ratio tokens each (ratio 1, Sk = S: token level)
+static dsa_status index_scores_impl(const void* q_idx, const void* k_idx, const void* w, const int32_t* seg, int B,
+                                    int S, int Sk, int ratio, int Hi, int Di, dsa_dtype in_dtype, int row0,
+                                    int nrows, void* scores, dsa_dtype score_dtype, int64_t ld, void* stream,
+                                    const char* name) {
+  REQ(dtype_ok(in_dtype) && dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
+  const bool in_bf16 = in_dtype == DSA_BF16, out_bf16 = score_dtype == DSA_BF16;
+  REQ(!in_bf16 || Di % 8 == 0, DSA_ERR_UNSUPPORTED, "bf16 index dim must be a multiple of 8");
+  hipStream_t st = (hipStream_t)stream;
+  if (in_bf16 && (Hi == 32 || Hi == 64) && (Di == 64 || Di == 128))
+    return hip_status(dsa::launch_index_scores_mfma(q_idx, k_idx, w, seg, B, S, Sk, ratio, Hi, Di, row0, nrows,
+                                                    scores, out_bf16, ld, st),
+                      name);
+  // the plain kernel stages the query's Hi x Di values and Hi weights as
+  // float32 in 64 KB of LDS; the product is formed in 64 bits
+  REQ(((int64_t)Hi * Di + Hi) * 4 <= 65536, DSA_ERR_UNSUPPORTED,
+      "Hi*Di=%lld too large for the plain indexer kernel", (long long)Hi * Di);
+  return hip_status(dsa::launch_index_scores_plain(q_idx, k_idx, w, seg, B, S, Sk, ratio, Hi, Di, in_bf16, row0,
+                                                   nrows, scores, out_bf16, ld, st),
+                    name);
+}
+
 dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
                             const int32_t* seg, int B, int S, int Hi, int Di,
                             dsa_dtype in_dtype, int row0, int nrows, void* scores,
@@ -120,21 +143,8 @@ dsa_status dsa_index_scores(const void* q_idx, const void* k_idx, const void* w,
   REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
       "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
   REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld < S=%d", (long long)ld, S);
-  REQ(dtype_ok(in_dtype) && dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown dtype");
-  const bool in_bf16 = in_dtype == DSA_BF16, out_bf16 = score_dtype == DSA_BF16;
-  REQ(!in_bf16 || Di % 8 == 0, DSA_ERR_UNSUPPORTED, "bf16 index dim must be a multiple of 8");
-  hipStream_t st = (hipStream_t)stream;
-  if (in_bf16 && (Hi == 32 || Hi == 64) && (Di == 64 || Di == 128))
-    return hip_status(dsa::launch_index_scores_mfma(q_idx, k_idx, w, seg, B, S, Hi, Di, row0, nrows,
-                                                    scores, out_bf16, ld, st),
-                      "dsa_index_scores");
-  // the plain kernel stages the query's Hi x Di values and Hi weights as
-  // float32 in 64 KB of LDS; the product is formed in 64 bits
-  REQ(((int64_t)Hi * Di + Hi) * 4 <= 65536, DSA_ERR_UNSUPPORTED,
-      "Hi*Di=%lld too large for the plain indexer kernel", (long long)Hi * Di);
-  return hip_status(dsa::launch_index_scores_plain(q_idx, k_idx, w, seg, B, S, Hi, Di, in_bf16, row0,
-                                                   nrows, scores, out_bf16, ld, st),
-                    "dsa_index_scores");
+  return index_scores_impl(q_idx, k_idx, w, seg, B, S, S, 1, Hi, Di, in_dtype, row0, nrows, scores, score_dtype,
+                           ld, stream, "dsa_index_scores");
 }
 
 dsa_status dsa_quant_fp8_rows(const void* x, dsa_dtype x_dtype, int64_t nrows, int D, uint8_t* codes,
@@ -200,6 +210,21 @@ dsa_status dsa_indexer_rope(const void* x, int B, int S, int nh, int D, int rope
                     "dsa_indexer_rope");
 }
 
+static dsa_status topk_impl(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* seg, int B, int S,
+                            int Sk, int ratio, int K, int row0, int nrows, int32_t* idx, void* mask, void* stream,
+                            const char* name) {
+  REQ(row0 % DSA_TILE_Q == 0 && ((row0 + nrows) % DSA_TILE_Q == 0 || row0 + nrows == S),
+      DSA_ERR_INVALID_ARG, "row slab [%d, %d) must start and end on a %d-row query tile (or at S)",
+      row0, row0 + nrows, DSA_TILE_Q);
+  REQ(dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown score dtype");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = dsa::launch_topk(scores, score_dtype == DSA_BF16, ld, seg, B, S, Sk, ratio, K, row0, nrows, idx,
+                                  bits_of(mask), st);
+  if (e != hipSuccess) return hip_status(e, name);
+  const int qt0 = row0 / DSA_TILE_Q, qt1 = (row0 + nrows + DSA_TILE_Q - 1) / DSA_TILE_Q;
+  return hip_status(dsa::launch_tile_classes(bits_of(mask), B, S, Sk, qt0, qt1, cls_of(mask, B, S, Sk), st), name);
+}
+
 dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, const int32_t* seg,
                     int B, int S, int K, int row0, int nrows, int32_t* idx, void* mask,
                     void* stream) {
@@ -211,18 +236,18 @@ dsa_status dsa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, const
   REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
   REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
       "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
-  REQ(row0 % DSA_TILE_Q == 0 && ((row0 + nrows) % DSA_TILE_Q == 0 || row0 + nrows == S),
-      DSA_ERR_INVALID_ARG, "row slab [%d, %d) must start and end on a %d-row query tile (or at S)",
-      row0, row0 + nrows, DSA_TILE_Q);
   REQ(ld >= S, DSA_ERR_INVALID_ARG, "ld=%lld < S=%d", (long long)ld, S);
-  REQ(dtype_ok(score_dtype), DSA_ERR_INVALID_ARG, "unknown score dtype");
+  return topk_impl(scores, score_dtype, ld, seg, B, S, S, 1, K, row0, nrows, idx, mask, stream, "dsa_topk");
+}
+
+static dsa_status build_mask_impl(const int32_t* idx, const int32_t* seg, int B, int S, int Sk, int ratio, int K,
+                                  void* mask, void* stream, const char* name) {
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = dsa::launch_topk(scores, score_dtype == DSA_BF16, ld, seg, B, S, K, row0, nrows, idx,
-                                  bits_of(mask), st);
-  if (e != hipSuccess) return hip_status(e, "dsa_topk");
-  const int qt0 = row0 / DSA_TILE_Q, qt1 = (row0 + nrows + DSA_TILE_Q - 1) / DSA_TILE_Q;
-  return hip_status(dsa::launch_tile_classes(bits_of(mask), B, S, qt0, qt1, cls_of(mask, B, S), st),
-                    "dsa_topk tile classes");
+  hipError_t e = dsa::launch_build_bits(idx, seg, B, S, Sk, ratio, K, bits_of(mask), st);
+  if (e != hipSuccess) return hip_status(e, name);
+  return hip_status(dsa::launch_tile_classes(bits_of(mask), B, S, Sk, 0, dsa::n_qtiles(S), cls_of(mask, B, S, Sk),
+                                             st),
+                    name);
 }
 
 dsa_status dsa_build_mask(const int32_t* idx, const int32_t* seg, int B, int S, int K, void* mask,
@@ -232,12 +257,7 @@ dsa_status dsa_build_mask(const int32_t* idx, const int32_t* seg, int B, int S, 
   REQ(seg == nullptr || aligned16(seg), DSA_ERR_INVALID_ARG, "seg must be 16-byte aligned");
   REQ(B >= 1 && S >= 1 && K >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d K=%d)", B, S, K);
   REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = dsa::launch_build_bits(idx, seg, B, S, K, bits_of(mask), st);
-  if (e != hipSuccess) return hip_status(e, "dsa_build_mask");
-  return hip_status(dsa::launch_tile_classes(bits_of(mask), B, S, 0, dsa::n_qtiles(S),
-                                             cls_of(mask, B, S), st),
-                    "dsa_build_mask tile classes");
+  return build_mask_impl(idx, seg, B, S, S, 1, K, mask, stream, "dsa_build_mask");
 }
 
 static dsa_status check_attn(int B, int S, int H, int Dqk, int Dv, float scale, dsa_dtype dtype) {
@@ -252,6 +272,20 @@ static dsa_status check_attn(int B, int S, int H, int Dqk, int Dv, float scale, 
   return DSA_OK;
 }
 
+static dsa_status attn_fwd_impl(const void* q, const void* k, const void* v, const void* mask, int B, int S, int Sk,
+                                int ratio, int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype, void* o,
+                                float* lse, void* stream, const char* name) {
+  hipStream_t st = (hipStream_t)stream;
+  void* m = const_cast<void*>(mask);
+  if (attn_mfma(Dqk, Dv, dtype))
+    return hip_status(dsa::launch_attn_fwd_mfma(q, k, v, bits_of(m), cls_of(m, B, S, Sk), B, S, Sk, ratio, H,
+                                                softmax_scale, o, lse, st),
+                      name);
+  return hip_status(dsa::launch_attn_fwd_plain(q, k, v, bits_of(m), B, S, Sk, ratio, H, Dqk, Dv, softmax_scale,
+                                               dtype == DSA_BF16, o, lse, st),
+                    name);
+}
+
 dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask,
                                int B, int S, int H, int Dqk, int Dv, float softmax_scale,
                                dsa_dtype dtype, void* o, float* lse, void* stream) {
@@ -263,15 +297,80 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
   REQ_PTR(lse);
   dsa_status s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
   if (s != DSA_OK) return s;
-  hipStream_t st = (hipStream_t)stream;
-  void* m = const_cast<void*>(mask);
-  if (attn_mfma(Dqk, Dv, dtype))
-    return hip_status(dsa::launch_attn_fwd_mfma(q, k, v, bits_of(m), cls_of(m, B, S), B, S, H,
-                                                softmax_scale, o, lse, st),
-                      "dsa_sparse_attn_fwd");
-  return hip_status(dsa::launch_attn_fwd_plain(q, k, v, bits_of(m), B, S, H, Dqk, Dv, softmax_scale,
-                                               dtype == DSA_BF16, o, lse, st),
-                    "dsa_sparse_attn_fwd");
+  return attn_fwd_impl(q, k, v, mask, B, S, S, 1, H, Dqk, Dv, softmax_scale, dtype, o, lse, stream,
+                       "dsa_sparse_attn_fwd");
+}
+
+// ---------------------------------------------------------------- compressed sparse attention
+static dsa_status check_csa(int B, int S, int Sk, int ratio) {
+  REQ(B >= 1 && S >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d S=%d)", B, S);
+  REQ(S <= dsa::kMaxS, DSA_ERR_UNSUPPORTED, "S=%d exceeds %d", S, dsa::kMaxS);
+  REQ(ratio >= 1, DSA_ERR_INVALID_ARG, "ratio=%d must be >= 1", ratio);
+  REQ(Sk >= 1 && Sk == S / ratio, DSA_ERR_INVALID_ARG, "Sk=%d must be S / ratio = %d (and >= 1)", Sk, S / ratio);
+  return DSA_OK;
+}
+
+size_t dsa_csa_mask_bytes(int B, int S, int Sk) {
+  if (B < 1 || S < 1 || Sk < 1) return 0;
+  return dsa::bits_bytes(B, S, Sk) + (size_t)B * dsa::n_qtiles(S) * dsa::n_ktiles(Sk);
+}
+
+dsa_status dsa_csa_index_scores(const void* q_idx, const void* k_idx, const void* w, int B, int S, int Sk, int ratio,
+                                int Hi, int Di, dsa_dtype in_dtype, int row0, int nrows, void* scores,
+                                dsa_dtype score_dtype, int64_t ld, void* stream) {
+  REQ_PTR(q_idx);
+  REQ_PTR(k_idx);
+  REQ_PTR(w);
+  REQ_PTR(scores);
+  dsa_status s = check_csa(B, S, Sk, ratio);
+  if (s != DSA_OK) return s;
+  REQ(Hi >= 1 && Di >= 1, DSA_ERR_INVALID_ARG, "sizes must be >= 1 (Hi=%d Di=%d)", Hi, Di);
+  REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
+      "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
+  REQ(ld >= Sk, DSA_ERR_INVALID_ARG, "ld=%lld < Sk=%d", (long long)ld, Sk);
+  return index_scores_impl(q_idx, k_idx, w, nullptr, B, S, Sk, ratio, Hi, Di, in_dtype, row0, nrows, scores,
+                           score_dtype, ld, stream, "dsa_csa_index_scores");
+}
+
+dsa_status dsa_csa_topk(const void* scores, dsa_dtype score_dtype, int64_t ld, int B, int S, int Sk, int ratio, int K,
+                        int row0, int nrows, int32_t* idx, void* mask, void* stream) {
+  REQ_PTR(scores);
+  REQ_PTR(idx);
+  REQ_PTR(mask);
+  dsa_status s = check_csa(B, S, Sk, ratio);
+  if (s != DSA_OK) return s;
+  REQ(K >= 1, DSA_ERR_INVALID_ARG, "K=%d must be >= 1", K);
+  REQ(row0 >= 0 && nrows >= 1 && (int64_t)row0 + nrows <= S, DSA_ERR_INVALID_ARG,
+      "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, S);
+  REQ(ld >= Sk, DSA_ERR_INVALID_ARG, "ld=%lld < Sk=%d", (long long)ld, Sk);
+  return topk_impl(scores, score_dtype, ld, nullptr, B, S, Sk, ratio, K, row0, nrows, idx, mask, stream,
+                   "dsa_csa_topk");
+}
+
+dsa_status dsa_csa_build_mask(const int32_t* idx, int B, int S, int Sk, int ratio, int K, void* mask, void* stream) {
+  REQ_PTR(idx);
+  REQ_PTR(mask);
+  dsa_status s = check_csa(B, S, Sk, ratio);
+  if (s != DSA_OK) return s;
+  REQ(K >= 1, DSA_ERR_INVALID_ARG, "K=%d must be >= 1", K);
+  return build_mask_impl(idx, nullptr, B, S, Sk, ratio, K, mask, stream, "dsa_csa_build_mask");
+}
+
+dsa_status dsa_csa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask, int B, int S,
+                                   int Sk, int ratio, int H, int Dqk, int Dv, float softmax_scale, dsa_dtype dtype,
+                                   void* o, float* lse, void* stream) {
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(v);
+  REQ_PTR(mask);
+  REQ_PTR(o);
+  REQ_PTR(lse);
+  dsa_status s = check_csa(B, S, Sk, ratio);
+  if (s != DSA_OK) return s;
+  s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
+  if (s != DSA_OK) return s;
+  return attn_fwd_impl(q, k, v, mask, B, S, Sk, ratio, H, Dqk, Dv, softmax_scale, dtype, o, lse, stream,
+                       "dsa_csa_sparse_attn_fwd");
 }
 
 static dsa_status check_bwd_common(const void* q, const void* k, const void* v, const void* dout,

@@ -6,6 +6,10 @@
 // "Integrate DeepSeek Sparse Attention with Tokamax Flash Attention",
 // Description (flash attention driven by a dynamic 3-D index mask).
 //
+// Keys may be compressed blocks ("Add Flash Attention Support to Deepseek v4",
+// Description): Sk keys, key s visible to query t when s <= (t + 1) / ratio -
+// 1; the mask rows are then ceil(Sk / 64) words. ratio 1 and Sk = S is DSA.
+//
 // MFMA kernel (bf16, Dqk = 192, Dv = 128). A workgroup is one (b, h, 256-query
 // block) with 8 waves of 32 queries each, two waves per SIMD. It walks the
 // 64-key tiles that are non-empty for either of its two 128-query tiles; the
@@ -56,7 +60,7 @@ __device__ __forceinline__ constexpr int vswz(int r, int c) { return c ^ (4 * (r
 
 __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int H,
+    const uint64_t* __restrict__ bits, const uint8_t* __restrict__ cls, int B, int S, int Sk, int ratio, int H,
     float scale_log2, uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace fwd;
   __shared__ __attribute__((aligned(1024))) uint16_t smK[KBUF][KBLK * 512];
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, col = lane & 31;
-  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int W = (Sk + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
   int bh, qw;
   grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
@@ -78,8 +82,8 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
   const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
   const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
-  const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
-  const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
+  const uint16_t* kbase = k + (size_t)b * Sk * rs_qk + (size_t)h * DQK;
+  const uint16_t* vbase = v + (size_t)b * Sk * rs_v + (size_t)h * DV;
 
   // copy c < KC moves K block wid + 8c, copy KC + c' V block wid + 8c'. Lane l
   // fills LDS slot 64*blk + l, i.e. row slot / chunks-per-row at physical chunk
@@ -137,7 +141,9 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[eb][i] = 0.f;
 
-  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  // last key tile any of the workgroup's queries sees (-1: none)
+  const int kl_last = (min(S - 1, qw * QW + QW - 1) + 1) / ratio - 1;
+  const int kt_last = kl_last < 0 ? -1 : kl_last / TK;
   stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
   stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
   const uint8_t* cls0 = scls[0];
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
   auto issue_tile = [&](int kt, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
     const uint16_t* ks = uniform_ptr(kbase + (size_t)kt * TK * rs_qk);
     const uint16_t* vs = uniform_ptr(vbase + (size_t)kt * TK * rs_v);
-    const int lim = S - 1 - kt * TK;
+    const int lim = Sk - 1 - kt * TK;
 #pragma unroll
     for (int c = 0; c < NC; ++c) copy(c, ks, vs, lim, kdst, vdst);
   };
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
     const int kcp = knn <= kt_last ? knn : kc;
     const uint16_t* ks = uniform_ptr(kbase + (size_t)kcp * TK * rs_qk);
     const uint16_t* vs = uniform_ptr(vbase + (size_t)kcp * TK * rs_v);
-    const int lim = S - 1 - kcp * TK;
+    const int lim = Sk - 1 - kcp * TK;
     uint16_t* kd = smK[jpos & 1];
     uint16_t* vd = smV[(jpos + 2) % 3];
     auto cp = [&](int g) __attribute__((always_inline)) { if (g < NC) copy(g, ks, vs, lim, kd, vd); };
@@ -387,7 +393,7 @@ __global__ __launch_bounds__(fwd::NW * 64) void attn_fwd_mfma_kernel(
 template <typename T>
 __global__ __launch_bounds__(256) void attn_fwd_plain_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const uint64_t* __restrict__ bits, int B, int S, int H, int Dqk, int Dv, float scale,
+    const uint64_t* __restrict__ bits, int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale,
     T* __restrict__ o, float* __restrict__ lse) {
   __shared__ float qs[4][256];
   __shared__ float ps[4][64];
@@ -397,20 +403,21 @@ __global__ __launch_bounds__(256) void attn_fwd_plain_kernel(
   const int h = (int)(row % H);
   const int t = (int)((row / H) % S);
   const int b = (int)(row / ((size_t)H * S));
-  const int W = (S + 63) / 64;
+  const int W = (Sk + 63) / 64;
+  const int tk = (t + 1) / ratio - 1;  // last visible key
   const T* qrow = q + ((size_t)b * S + t) * H * Dqk + (size_t)h * Dqk;
   for (int d = lane; d < Dqk; d += 64) qs[wid][d] = Elem<T>::load(qrow + d);
   __builtin_amdgcn_wave_barrier();
   float m = -INFINITY, l = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const uint64_t* brow = bits + ((size_t)b * S + t) * W;
-  for (int w = 0; w <= t / 64; ++w) {
+  for (int w = 0; w < (tk + 64) / 64; ++w) {
     const uint64_t word = brow[w];
     if (word == 0ull) continue;
     const int s = 64 * w + lane;
     float x = -INFINITY;
     if ((word >> lane) & 1ull) {
-      const T* krow = k + ((size_t)b * S + s) * H * Dqk + (size_t)h * Dqk;
+      const T* krow = k + ((size_t)b * Sk + s) * H * Dqk + (size_t)h * Dqk;
       float dot = 0.f;
       for (int d = 0; d < Dqk; ++d) dot = fmaf(qs[wid][d], Elem<T>::load(krow + d), dot);
       x = dot * scale;
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(256) void attn_fwd_plain_kernel(
     for (int jj = 0; jj < 64; ++jj) {
       if (!((word >> jj) & 1ull)) continue;
       const float pj = ps[wid][jj];
-      const T* vrow = v + ((size_t)b * S + 64 * w + jj) * H * Dv + (size_t)h * Dv;
+      const T* vrow = v + ((size_t)b * Sk + 64 * w + jj) * H * Dv + (size_t)h * Dv;
       for (int j = 0; j < 4; ++j) {
         const int e = lane + 64 * j;
         if (e < Dv) acc[j] = fmaf(pj, Elem<T>::load(vrow + e), acc[j]);
@@ -444,26 +451,26 @@ __global__ __launch_bounds__(256) void attn_fwd_plain_kernel(
 }
 
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, const uint64_t* bits,
-                                const uint8_t* cls, int B, int S, int H, float scale, void* o,
+                                const uint8_t* cls, int B, int S, int Sk, int ratio, int H, float scale, void* o,
                                 float* lse, hipStream_t st) {
   const size_t nblk = (size_t)((S + fwd::QW - 1) / fwd::QW) * B * H;
   hipLaunchKernelGGL(attn_fwd_mfma_kernel, dim3((unsigned)nblk), dim3(fwd::NW * 64), 0, st,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, bits, cls, B, S, H,
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, bits, cls, B, S, Sk, ratio, H,
                      scale * 1.4426950408889634f, (uint16_t*)o, lse);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_fwd_plain(const void* q, const void* k, const void* v, const uint64_t* bits,
-                                 int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
+                                 int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale, bool bf16,
                                  void* o, float* lse, hipStream_t st) {
   const size_t nblk = ((size_t)B * S * H + 3) / 4;
   if (bf16)
     hipLaunchKernelGGL(attn_fwd_plain_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, bits, B, S, H,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, bits, B, S, Sk, ratio, H,
                        Dqk, Dv, scale, (uint16_t*)o, lse);
   else
     hipLaunchKernelGGL(attn_fwd_plain_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
-                       (const float*)q, (const float*)k, (const float*)v, bits, B, S, H, Dqk, Dv,
+                       (const float*)q, (const float*)k, (const float*)v, bits, B, S, Sk, ratio, H, Dqk, Dv,
                        scale, (float*)o, lse);
   return hipGetLastError();
 }

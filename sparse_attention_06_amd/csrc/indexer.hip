@@ -4,6 +4,11 @@
 // valid(t) (causal with the diagonal, same segment). Source: "DeepSeek3.2:
 // Onboard sparse attention", Background (the indexer's parametric query-key
 // product) and "What this PR does", item 2 (64 index heads x 128).
+// Keys may be compressed blocks ("Add Flash Attention Support to Deepseek v4",
+// Description; "Implement QK attention head chunking for CSA [Deepseek v4]",
+// Description): Sk keys, key s standing for tokens ratio*s .. ratio*s +
+// ratio - 1 and visible to query t once its block is complete, s <=
+// (t + 1) / ratio - 1. ratio 1 and Sk = S is the token-level indexer.
 //
 // MFMA kernel: per query t, the product of its index heads with a tile of 32
 // keys is a [Hi x 32] GEMM with K = Di. Heads go on the MFMA row dimension and
@@ -27,8 +32,8 @@ namespace dsa {
 template <int HB, int KS, typename OutT>
 __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_idx,
-    const uint16_t* __restrict__ w, const int32_t* __restrict__ seg, int B, int S, int row0,
-    int nrows, OutT* __restrict__ scores, int64_t ld) {
+    const uint16_t* __restrict__ w, const int32_t* __restrict__ seg, int B, int S, int Sk, int ratio,
+    int row0, int nrows, OutT* __restrict__ scores, int64_t ld) {
   constexpr int Hi = HB * 32, Di = KS * 16;
   constexpr int TILE = 128;                  // keys per iteration: four 32-key MFMA column blocks
   constexpr int SL = Di / 8 + 1;             // 16-byte slots per padded LDS key row
@@ -56,8 +61,11 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   const bool active = r < nrows;
   const int t = row0 + r;
   const int t_last = row0 + min(nrows - 1, rb * 4 + 3);
-  const int nkt = t_last / TILE + 1;
-  const uint16_t* kb_base = uniform_ptr(k_idx + (size_t)b * S * Di);
+  const int kl_last = (t_last + 1) / ratio - 1;  // last key any of the rows sees
+  if (kl_last < 0) return;                       // the whole workgroup: no visible key
+  const int nkt = kl_last / TILE + 1;
+  const int tk = (t + 1) / ratio - 1;            // this row's last visible key
+  const uint16_t* kb_base = uniform_ptr(k_idx + (size_t)b * Sk * Di);
 
   u32x4 afrag[HB][KS];
   float wreg[HB][16];
@@ -101,7 +109,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
     coff[i] = (uint32_t)((row * Di + c * 8) * 2);
   }
   auto issue = [&](int kt, int buf) {
-    if ((kt + 1) * TILE <= S) {
+    if ((kt + 1) * TILE <= Sk) {
       const uint16_t* tb = kb_base + (size_t)kt * TILE * Di;
 #pragma unroll
       for (int i = 0; i < BI; ++i)
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
       for (int i = 0; i < BI; ++i)
         if (wid + i * 4 < NBLK) {
           const int row = (int)(coff[i] / (Di * 2));
-          const int s = min(kt * TILE + row, S - 1);
+          const int s = min(kt * TILE + row, Sk - 1);
           const uint32_t c_bytes = coff[i] % (Di * 2);
           g2lds16_async((const char*)(kb_base + (size_t)s * Di) + c_bytes, lds[buf] + (wid + i * 4) * 1024);
         }
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
   for (int kt = kt0; kt < nkt; ++kt) {
     const int buf = (kt - kt0) & 1;
     const int s_lo = kt * TILE + lane, s_hi = s_lo + 64;
-    bool ok_lo = active && s_lo <= t, ok_hi = active && s_hi <= t;
+    bool ok_lo = active && s_lo <= tk, ok_hi = active && s_hi <= tk;
     if (seg) {
       ok_lo = ok_lo && lseg[buf][lane] == seg_t;
       ok_hi = ok_hi && lseg[buf][64 + lane] == seg_t;
@@ -229,23 +237,24 @@ __global__ __launch_bounds__(256) void index_scores_mfma_kernel(
 template <typename InT, typename OutT>
 __global__ __launch_bounds__(256) void index_scores_plain_kernel(
     const InT* __restrict__ q_idx, const InT* __restrict__ k_idx, const InT* __restrict__ w,
-    const int32_t* __restrict__ seg, int S, int Hi, int Di, int row0, int nrows,
+    const int32_t* __restrict__ seg, int S, int Sk, int ratio, int Hi, int Di, int row0, int nrows,
     OutT* __restrict__ scores, int64_t ld) {
   extern __shared__ float smem[];  // Hi*Di query values, then Hi weights
-  const int nkb = (S + 255) / 256;
+  const int nkb = (Sk + 255) / 256;
   const int r = blockIdx.x / nkb, kb = blockIdx.x % nkb, b = blockIdx.y;
   const int t = row0 + r;
+  const int tk = (t + 1) / ratio - 1;  // last visible key
   const int s = kb * 256 + threadIdx.x;
-  if (kb * 256 > t) return;  // whole block in the future (uniform)
+  if (kb * 256 > tk) return;  // whole block in the future (uniform)
   float* qs = smem;
   float* ws = smem + Hi * Di;
   const InT* qrow = q_idx + ((size_t)b * S + t) * Hi * Di;
   for (int i = threadIdx.x; i < Hi * Di; i += 256) qs[i] = Elem<InT>::load(qrow + i);
   for (int i = threadIdx.x; i < Hi; i += 256) ws[i] = Elem<InT>::load(w + ((size_t)b * S + t) * Hi + i);
   __syncthreads();
-  if (s > t) return;
+  if (s > tk) return;
   if (seg && seg[(size_t)b * S + s] != seg[(size_t)b * S + t]) return;
-  const InT* krow = k_idx + ((size_t)b * S + s) * Di;
+  const InT* krow = k_idx + ((size_t)b * Sk + s) * Di;
   float part = 0.f;
   for (int j = 0; j < Hi; ++j) {
     float dot = 0.f;
@@ -257,45 +266,45 @@ __global__ __launch_bounds__(256) void index_scores_plain_kernel(
 
 template <int HB, int KS>
 static hipError_t launch_mfma_t(const void* q_idx, const void* k_idx, const void* w,
-                                const int32_t* seg, int B, int S, int row0, int nrows,
+                                const int32_t* seg, int B, int S, int Sk, int ratio, int row0, int nrows,
                                 void* scores, bool out_bf16, int64_t ld, hipStream_t st) {
   const int nrb = (nrows + 3) / 4;
   dim3 grid((unsigned)(nrb * B)), block(256);
   if (out_bf16)
     hipLaunchKernelGGL((index_scores_mfma_kernel<HB, KS, uint16_t>), grid, block, 0, st,
                        (const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w, seg, B,
-                       S, row0, nrows, (uint16_t*)scores, ld);
+                       S, Sk, ratio, row0, nrows, (uint16_t*)scores, ld);
   else
     hipLaunchKernelGGL((index_scores_mfma_kernel<HB, KS, float>), grid, block, 0, st,
                        (const uint16_t*)q_idx, (const uint16_t*)k_idx, (const uint16_t*)w, seg, B,
-                       S, row0, nrows, (float*)scores, ld);
+                       S, Sk, ratio, row0, nrows, (float*)scores, ld);
   return hipGetLastError();
 }
 
 hipError_t launch_index_scores_mfma(const void* q_idx, const void* k_idx, const void* w,
-                                    const int32_t* seg, int B, int S, int Hi, int Di, int row0,
-                                    int nrows, void* scores, bool out_bf16, int64_t ld,
+                                    const int32_t* seg, int B, int S, int Sk, int ratio, int Hi, int Di,
+                                    int row0, int nrows, void* scores, bool out_bf16, int64_t ld,
                                     hipStream_t st) {
   if (Hi == 64 && Di == 128)
-    return launch_mfma_t<2, 8>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+    return launch_mfma_t<2, 8>(q_idx, k_idx, w, seg, B, S, Sk, ratio, row0, nrows, scores, out_bf16, ld, st);
   if (Hi == 32 && Di == 128)
-    return launch_mfma_t<1, 8>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+    return launch_mfma_t<1, 8>(q_idx, k_idx, w, seg, B, S, Sk, ratio, row0, nrows, scores, out_bf16, ld, st);
   if (Hi == 64 && Di == 64)
-    return launch_mfma_t<2, 4>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+    return launch_mfma_t<2, 4>(q_idx, k_idx, w, seg, B, S, Sk, ratio, row0, nrows, scores, out_bf16, ld, st);
   if (Hi == 32 && Di == 64)
-    return launch_mfma_t<1, 4>(q_idx, k_idx, w, seg, B, S, row0, nrows, scores, out_bf16, ld, st);
+    return launch_mfma_t<1, 4>(q_idx, k_idx, w, seg, B, S, Sk, ratio, row0, nrows, scores, out_bf16, ld, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const void* w,
-                                     const int32_t* seg, int B, int S, int Hi, int Di,
+                                     const int32_t* seg, int B, int S, int Sk, int ratio, int Hi, int Di,
                                      bool in_bf16, int row0, int nrows, void* scores,
                                      bool out_bf16, int64_t ld, hipStream_t st) {
-  dim3 grid((unsigned)(((S + 255) / 256) * nrows), (unsigned)B), block(256);
+  dim3 grid((unsigned)(((Sk + 255) / 256) * nrows), (unsigned)B), block(256);
   const size_t shm = ((size_t)Hi * Di + Hi) * sizeof(float);  // the caller bounds it to 64 KB
 #define DSA_IDX_PLAIN(IT, OT)                                                               \
   hipLaunchKernelGGL((index_scores_plain_kernel<IT, OT>), grid, block, shm, st, (const IT*)q_idx, \
-                     (const IT*)k_idx, (const IT*)w, seg, S, Hi, Di, row0, nrows, (OT*)scores, ld)
+                     (const IT*)k_idx, (const IT*)w, seg, S, Sk, ratio, Hi, Di, row0, nrows, (OT*)scores, ld)
   if (in_bf16) {
     if (out_bf16) DSA_IDX_PLAIN(uint16_t, uint16_t); else DSA_IDX_PLAIN(uint16_t, float);
   } else {

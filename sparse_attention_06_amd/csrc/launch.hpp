@@ -14,13 +14,17 @@ namespace dsa {
 // LDS.
 constexpr int kMaxS = 1 << 18;
 
+// Key axis: Sk keys, key s visible to query t when s <= (t + 1) / ratio - 1
+// (compressed blocks of `ratio` tokens); ratio 1 and Sk = S is token-level DSA.
+// Masks built over it have ceil(Sk / 64) words per row and ceil(Sk / 64) key
+// tiles.
 // scores: in_bf16 selects bf16 vs fp32 inputs, out_bf16 the score storage.
 hipError_t launch_index_scores_mfma(const void* q_idx, const void* k_idx, const void* w,
-                                    const int32_t* seg, int B, int S, int Hi, int Di, int row0,
-                                    int nrows, void* scores, bool out_bf16, int64_t ld,
+                                    const int32_t* seg, int B, int S, int Sk, int ratio, int Hi, int Di,
+                                    int row0, int nrows, void* scores, bool out_bf16, int64_t ld,
                                     hipStream_t st);
 hipError_t launch_index_scores_plain(const void* q_idx, const void* k_idx, const void* w,
-                                     const int32_t* seg, int B, int S, int Hi, int Di,
+                                     const int32_t* seg, int B, int S, int Sk, int ratio, int Hi, int Di,
                                      bool in_bf16, int row0, int nrows, void* scores,
                                      bool out_bf16, int64_t ld, hipStream_t st);
 
@@ -31,19 +35,18 @@ hipError_t launch_quant_fp8_rows(const void* x, bool in_bf16, int64_t nrows, int
                                  float* scale, hipStream_t st);
 hipError_t launch_rope_rows(const void* x, int B, int S, int nh, int D, int rope_dim, int P, const float* cos_t,
                             const float* sin_t, const int32_t* pos, void* out, hipStream_t st);
-hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
-                       int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
-                       hipStream_t st);
-hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int K,
+hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg, int B, int S, int Sk,
+                       int ratio, int K, int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st);
+hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int Sk, int ratio, int K,
                              uint64_t* bits, hipStream_t st);
-hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int qt0, int qt1,
-                               uint8_t* cls, hipStream_t st);
+hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int Sk, int qt0, int qt1, uint8_t* cls,
+                               hipStream_t st);
 
 hipError_t launch_attn_fwd_mfma(const void* q, const void* k, const void* v, const uint64_t* bits,
-                                const uint8_t* cls, int B, int S, int H, float scale, void* o,
+                                const uint8_t* cls, int B, int S, int Sk, int ratio, int H, float scale, void* o,
                                 float* lse, hipStream_t st);
 hipError_t launch_attn_fwd_plain(const void* q, const void* k, const void* v, const uint64_t* bits,
-                                 int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
+                                 int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale, bool bf16,
                                  void* o, float* lse, hipStream_t st);
 
 // backward prologue: D = rowsum(dout * o) and lse * log2(e), two float32
@@ -98,6 +101,7 @@ __host__ __device__ inline size_t dsf_tile_base(int qc) {
 inline int mask_words(int S) { return (S + 63) / 64; }
 inline int n_qtiles(int S) { return (S + 127) / 128; }
 inline int n_ktiles(int S) { return (S + 63) / 64; }
-inline size_t bits_bytes(int B, int S) { return (size_t)B * S * mask_words(S) * 8; }
+inline size_t bits_bytes(int B, int S, int Sk) { return (size_t)B * S * mask_words(Sk) * 8; }
+inline size_t bits_bytes(int B, int S) { return bits_bytes(B, S, S); }
 
 }  // namespace dsa

@@ -6,6 +6,12 @@
 // with DeepSeek DSA Sparse Indexer", Forward Flow (the index mask is
 // [batch, S, S], shared by all heads, tiled into partial-mask blocks).
 //
+// Keys may be compressed blocks ("Add Flash Attention Support to Deepseek v4",
+// Description): Sk keys per row, key s visible to query t when s <= (t + 1) /
+// ratio - 1, so a row's keys are 0 .. L - 1 with L = (t + 1) / ratio, and the
+// mask rows are ceil(Sk / 64) words. ratio 1 and Sk = S is token-level DSA;
+// segment IDs come only with ratio 1.
+//
 // Selection rule: n = min(K, |valid(t)|) keys. Larger scores win. Among equal
 // scores the smaller key position wins, and -0 equals +0.
 //
@@ -111,7 +117,7 @@ struct WaveTopkShared {
 template <typename ST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void topk_wave_kernel(const ST* __restrict__ scores, int64_t ld,
                                                         const int32_t* __restrict__ seg, int B, int S,
-                                                        int K, int row0, int nrows, int nreg,
+                                                        int Sk, int ratio, int K, int row0, int nrows, int nreg,
                                                         int32_t* __restrict__ idx,
                                                         uint64_t* __restrict__ bits) {
   __shared__ WaveTopkShared shw[4];
@@ -121,8 +127,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
   if (item >= nreg * B) return;  // the whole wave: nothing in this kernel waits for other waves
   WaveTopkShared& sh = shw[wid];
   const int b = item % B, r = nreg - 1 - item / B;  // longest rows first
-  const int t = row0 + r, L = t + 1;
-  const int W = (S + 63) / 64;
+  const int t = row0 + r;
+  const int tk = (t + 1) / ratio - 1, L = tk + 1;  // last visible key, row length
+  const int W = (Sk + 63) / 64;
   int32_t* idx_row = idx + ((size_t)b * S + t) * K;
   uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
   const ST* row = scores + ((size_t)b * nrows + r) * ld;
@@ -151,22 +158,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void t
       return;
     }
   }
-  const int nw = t / 64 - wb + 1;  // the row's words from wb on
+  const int nw = tk / 64 - wb + 1;  // the row's words from wb on
   const int s_lane = 64 * wb + lane;  // this lane's position in word wb
   // keys: 0 for positions that are not valid; first 1 for the valid ones
   uint32_t key[kWaveWords];
   uint32_t n_valid = 0;
   if (segb) {
 #pragma unroll
-    for (int j = 0; j < kWaveWords; ++j) key[j] = (j < nw && s_lane + 64 * j <= t) ? (uint32_t)segb[s_lane + 64 * j] : 0u;
+    for (int j = 0; j < kWaveWords; ++j) key[j] = (j < nw && s_lane + 64 * j <= tk) ? (uint32_t)segb[s_lane + 64 * j] : 0u;
 #pragma unroll
     for (int j = 0; j < kWaveWords; ++j) {
-      key[j] = (j < nw && s_lane + 64 * j <= t && (int)key[j] == seg_t) ? 1u : 0u;
+      key[j] = (j < nw && s_lane + 64 * j <= tk && (int)key[j] == seg_t) ? 1u : 0u;
       n_valid += (uint32_t)__popcll(__ballot(key[j] != 0u));
     }
   } else {  // only the last word can hold positions past t
 #pragma unroll
-    for (int j = 0; j < kWaveWords; ++j) key[j] = j < nw - 1 ? 1u : (j == nw - 1 && s_lane + 64 * j <= t) ? 1u : 0u;
+    for (int j = 0; j < kWaveWords; ++j) key[j] = j < nw - 1 ? 1u : (j == nw - 1 && s_lane + 64 * j <= tk) ? 1u : 0u;
     n_valid = (uint32_t)L;
   }
   // the K-th largest key T, how many of the keys equal to T are taken
@@ -409,15 +416,14 @@ __device__ __forceinline__ uint32_t popc64(uint64_t m) { return (uint32_t)__popc
 // `segb` of that batch row (SEG), outputs idx_row / bits_row. sh and segw
 // (one u64 per 64-key word, SEG) are the workgroup's LDS.
 template <typename ST, bool SEG, int NW>
-__device__ void multipass_row(const ST* __restrict__ row, const int32_t* __restrict__ segb, int S, int K, int t,
-                              int32_t* __restrict__ idx_row, uint64_t* __restrict__ bits_row, LongShared& sh,
+__device__ void multipass_row(const ST* __restrict__ row, const int32_t* __restrict__ segb, int W, int K, int t,
+                              int L, int32_t* __restrict__ idx_row, uint64_t* __restrict__ bits_row, LongShared& sh,
                               uint64_t* segw) {
   constexpr int NT = 64 * NW;
   constexpr int kU = 8;  // words per step: all of their reads issued first
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int W = (S + 63) / 64;
-  const int L = t + 1, nw = (L + 63) / 64;
+  const int nw = (L + 63) / 64;  // the row's keys are 0 .. L - 1, its mask row W words
   // this wave's words [wa, wb)
   const int nwp = (nw + NW - 1) / NW;
   const int wa = min(nw, wid * nwp), wb = min(nw, wa + nwp);
@@ -656,8 +662,9 @@ __device__ void multipass_row(const ST* __restrict__ row, const int32_t* __restr
 template <typename ST, bool SEG, int NW>
 __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict__ scores, int64_t ld,
                                                             const int32_t* __restrict__ seg, int B, int S,
-                                                            int K, int row0, int nrows, int rbeg, int rcount,
-                                                            int32_t* __restrict__ idx, uint64_t* __restrict__ bits) {
+                                                            int Sk, int ratio, int K, int row0, int nrows, int rbeg,
+                                                            int rcount, int32_t* __restrict__ idx,
+                                                            uint64_t* __restrict__ bits) {
   __shared__ LongShared sh;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   const int b = blockIdx.x % B;
@@ -665,8 +672,9 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
   const int t = row0 + r;
   // with segment IDs, topk_wave_kernel (run before) marks the rows it leaves
   if (SEG && idx[((size_t)b * S + t) * K] != kLongRow) return;
-  multipass_row<ST, SEG, NW>(scores + ((size_t)b * nrows + r) * ld, SEG ? seg + (size_t)b * S : nullptr, S, K, t,
-                             idx + ((size_t)b * S + t) * K, bits + ((size_t)b * S + t) * ((S + 63) / 64), sh,
+  const int W = (Sk + 63) / 64;
+  multipass_row<ST, SEG, NW>(scores + ((size_t)b * nrows + r) * ld, SEG ? seg + (size_t)b * S : nullptr, W, K, t,
+                             (t + 1) / ratio, idx + ((size_t)b * S + t) * K, bits + ((size_t)b * S + t) * W, sh,
                              (uint64_t*)dyn);
 }
 
@@ -734,8 +742,9 @@ constexpr int stash_waves_per_simd() { return (sizeof(ST) == 4 && !SEG) ? 8 : 1;
 
 template <typename ST, bool SEG, int NW>
 __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void topk_stash_kernel(const ST* __restrict__ scores, int64_t ld,
-                                                             const int32_t* __restrict__ seg, int B, int S, int K,
-                                                             int row0, int nrows, int rbeg, int rcount, int nw_max,
+                                                             const int32_t* __restrict__ seg, int B, int S, int Sk,
+                                                             int ratio, int K, int row0, int nrows, int rbeg,
+                                                             int rcount, int nw_max,
                                                              int32_t* __restrict__ idx,
                                                              uint64_t* __restrict__ bits) {
   constexpr int NT = 64 * NW;
@@ -755,8 +764,8 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   const int b = blockIdx.x % B;
   const int r = rbeg + rcount - 1 - (int)(blockIdx.x / B);  // longest rows first
   const int t = row0 + r;
-  const int W = (S + 63) / 64;
-  const int L = t + 1, nw = (L + 63) / 64;
+  const int W = (Sk + 63) / 64;
+  const int L = (t + 1) / ratio, nw = (L + 63) / 64;
   const ST* row = scores + ((size_t)b * nrows + r) * ld;
   int32_t* idx_row = idx + ((size_t)b * S + t) * K;
   uint64_t* bits_row = bits + ((size_t)b * S + t) * W;
@@ -1043,7 +1052,7 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   if (fail) {  // uniform: the multi-pass selection, its state in the list's LDS
     static_assert(sizeof(LongShared) <= kStash * 4, "multi-pass state must fit the list");
     __syncthreads();
-    multipass_row<ST, SEG, NW>(row, SEG ? seg + (size_t)b * S : nullptr, S, K, t, idx_row, bits_row,
+    multipass_row<ST, SEG, NW>(row, SEG ? seg + (size_t)b * S : nullptr, W, K, t, L, idx_row, bits_row,
                                *reinterpret_cast<LongShared*>(stash), segw);
     return;
   }
@@ -1080,17 +1089,19 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
 // assembled in LDS with atomic ORs, then written out whole.
 __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ seg, int B,
-                                                         int S, int K, uint64_t* __restrict__ bits) {
+                                                         int S, int Sk, int ratio, int K,
+                                                         uint64_t* __restrict__ bits) {
   extern __shared__ unsigned long long words[];
-  const int W = (S + 63) / 64;
+  const int W = (Sk + 63) / 64;
   const int b = blockIdx.x % B, t = blockIdx.x / B;
+  const int tk = (t + 1) / ratio - 1;  // last visible key
   for (int w = threadIdx.x; w < W; w += 256) words[w] = 0ull;
   __syncthreads();
   const int32_t* row = idx + ((size_t)b * S + t) * K;
   const int seg_t = seg ? seg[(size_t)b * S + t] : 0;
   for (int i = threadIdx.x; i < K; i += 256) {
     const int s = row[i];
-    if (s >= 0 && s <= t && (!seg || seg[(size_t)b * S + s] == seg_t))
+    if (s >= 0 && s <= tk && (!seg || seg[(size_t)b * S + s] == seg_t))
       atomicOr(&words[s >> 6], 1ull << (s & 63));
   }
   __syncthreads();
@@ -1102,10 +1113,10 @@ __global__ __launch_bounds__(256) void build_bits_kernel(const int32_t* __restri
 // key tiles). Lane = key tile (one mask word per row), wave w takes rows
 // t0 + 32w .. t0 + 32w + 31 of the query tile, and the four waves' OR and AND
 // of their words are combined in LDS.
-__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int S, int qt0,
+__global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restrict__ bits, int S, int Sk, int qt0,
                                                          uint8_t* __restrict__ cls) {
   __shared__ uint64_t s_or[4][64], s_and[4][64];
-  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int W = (Sk + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int kt = blockIdx.x * 64 + lane;
   const int qt = qt0 + blockIdx.y, b = blockIdx.z;
@@ -1127,16 +1138,20 @@ __global__ __launch_bounds__(256) void tile_class_kernel(const uint64_t* __restr
   if (wv == 0 && kt < NK) {
     o = s_or[0][lane] | s_or[1][lane] | s_or[2][lane] | s_or[3][lane];
     a = s_and[0][lane] & s_and[1][lane] & s_and[2][lane] & s_and[3][lane];
-    const bool keys_in_range = (kt + 1) * 64 <= S;
+    const bool keys_in_range = (kt + 1) * 64 <= Sk;
     cls[((size_t)b * NQ + qt) * NK + kt] = o == 0ull ? 0 : ((keys_in_range && a == ~0ull) ? 2 : 1);
   }
 }
 
+// words of the longest row among rows [rbeg, rbeg + rcount) of the slab
+static int longest_row_words(int row0, int rbeg, int rcount, int ratio) {
+  return ((row0 + rbeg + rcount) / ratio + 63) / 64;
+}
 template <typename ST, bool SEG, int NW>
-static hipError_t launch_multipass(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
-                                   int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
+static hipError_t launch_multipass(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int Sk, int ratio,
+                                   int K, int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
                                    hipStream_t st) {
-  const int nw_max = (row0 + rbeg + rcount + 63) / 64;  // words of the range's longest row
+  const int nw_max = longest_row_words(row0, rbeg, rcount, ratio);
   const size_t shm = SEG ? (size_t)nw_max * 8 : 0;
   if (shm + sizeof(LongShared) > 160 * 1024) return hipErrorInvalidValue;
   const void* fn = (const void*)topk_long_kernel<ST, SEG, NW>;
@@ -1145,13 +1160,14 @@ static hipError_t launch_multipass(const ST* scores, int64_t ld, const int32_t* 
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((topk_long_kernel<ST, SEG, NW>), dim3((unsigned)((size_t)rcount * B)), dim3(64 * NW),
-                     shm, st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits);
+                     shm, st, scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, rbeg, rcount, idx, bits);
   return hipGetLastError();
 }
 template <typename ST, bool SEG, int NW>
-static hipError_t launch_stash(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K, int row0,
-                               int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits, hipStream_t st) {
-  const int nw_max = (row0 + rbeg + rcount + 63) / 64;
+static hipError_t launch_stash(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int Sk, int ratio,
+                               int K, int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
+                               hipStream_t st) {
+  const int nw_max = longest_row_words(row0, rbeg, rcount, ratio);
   const size_t shm = stash_lds_bytes(nw_max, SEG);
   if (shm + sizeof(StashShared) > 160 * 1024) return hipErrorInvalidValue;
   const void* fn = (const void*)topk_stash_kernel<ST, SEG, NW>;
@@ -1160,19 +1176,21 @@ static hipError_t launch_stash(const ST* scores, int64_t ld, const int32_t* seg,
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((topk_stash_kernel<ST, SEG, NW>), dim3((unsigned)((size_t)rcount * B)), dim3(64 * NW), shm,
-                     st, scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, nw_max, idx, bits);
+                     st, scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, rbeg, rcount, nw_max, idx, bits);
   return hipGetLastError();
 }
 // rows [rbeg, rbeg + rcount) of the slab, all longer than 64 * kWaveWords keys
 template <typename ST, bool SEG>
-static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int K, int row0,
-                                   int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits, hipStream_t st) {
+static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int Sk, int ratio,
+                                   int K, int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
+                                   hipStream_t st) {
   if (2 * K > kStash)  // the listed keys could not hold the selection: multi-pass only
-    return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
-  return launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, K, row0, nrows, rbeg, rcount, idx, bits, st);
+    return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, rbeg, rcount, idx, bits,
+                                         st);
+  return launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, rbeg, rcount, idx, bits, st);
 }
 
-// Rows are routed by length L = t + 1 (longest first): up to 64 *
+// Rows are routed by length L = (t + 1) / ratio (longest first): up to 64 *
 // kWaveWords keys in one wave's VGPRs; longer rows are read once into a short
 // list of their largest keys, with the multi-pass selection behind for rows
 // where the list misses.
@@ -1182,47 +1200,47 @@ static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* 
 // in their first index entry, and those kernels skip every other row), so
 // packed documents of up to 4096 keys never take the long path.
 template <typename ST>
-static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int K,
-                                int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
+static hipError_t launch_topk_t(const void* scores, int64_t ld, const int32_t* seg, int B, int S, int Sk, int ratio,
+                                int K, int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
   const ST* sc = (const ST*)scores;
   const int l_reg = 64 * kWaveWords;
-  const int n_long_from = max(0, min(nrows, l_reg - row0));  // rows with L > l_reg start here
-  const int n_reg = seg ? nrows : n_long_from;                // rows the one-wave kernel looks at
+  // rows with L > l_reg, i.e. t >= ratio * (l_reg + 1) - 1, start here
+  const int n_long_from = (int)max((int64_t)0, min((int64_t)nrows, (int64_t)ratio * (l_reg + 1) - 1 - row0));
+  const int n_reg = seg ? nrows : n_long_from;  // rows the one-wave kernel looks at
   hipError_t e = hipSuccess;
   // the one-wave kernel first: with segment IDs it marks the rows it leaves
   if (n_reg > 0) {
     hipLaunchKernelGGL((topk_wave_kernel<ST>), dim3((unsigned)(((size_t)n_reg * B + 3) / 4)), dim3(256), 0, st,
-                       sc, ld, seg, B, S, K, row0, nrows, n_reg, idx, bits);
+                       sc, ld, seg, B, S, Sk, ratio, K, row0, nrows, n_reg, idx, bits);
     e = hipGetLastError();
   }
   if (e == hipSuccess && nrows > n_long_from)
-    e = seg ? launch_long_rows<ST, true>(sc, ld, seg, B, S, K, row0, nrows, n_long_from, nrows - n_long_from, idx,
-                                         bits, st)
-            : launch_long_rows<ST, false>(sc, ld, seg, B, S, K, row0, nrows, n_long_from, nrows - n_long_from, idx,
-                                          bits, st);
+    e = seg ? launch_long_rows<ST, true>(sc, ld, seg, B, S, Sk, ratio, K, row0, nrows, n_long_from,
+                                         nrows - n_long_from, idx, bits, st)
+            : launch_long_rows<ST, false>(sc, ld, seg, B, S, Sk, ratio, K, row0, nrows, n_long_from,
+                                          nrows - n_long_from, idx, bits, st);
   return e;
 }
 
-hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg,
-                       int B, int S, int K, int row0, int nrows, int32_t* idx, uint64_t* bits,
-                       hipStream_t st) {
-  return score_bf16 ? launch_topk_t<uint16_t>(scores, ld, seg, B, S, K, row0, nrows, idx, bits, st)
-                    : launch_topk_t<float>(scores, ld, seg, B, S, K, row0, nrows, idx, bits, st);
+hipError_t launch_topk(const void* scores, bool score_bf16, int64_t ld, const int32_t* seg, int B, int S, int Sk,
+                       int ratio, int K, int row0, int nrows, int32_t* idx, uint64_t* bits, hipStream_t st) {
+  return score_bf16 ? launch_topk_t<uint16_t>(scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, idx, bits, st)
+                    : launch_topk_t<float>(scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, idx, bits, st);
 }
 
-hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int K,
+hipError_t launch_build_bits(const int32_t* idx, const int32_t* seg, int B, int S, int Sk, int ratio, int K,
                              uint64_t* bits, hipStream_t st) {
-  const size_t shm = (size_t)mask_words(S) * 8;
+  const size_t shm = (size_t)mask_words(Sk) * 8;
   hipLaunchKernelGGL(build_bits_kernel, dim3((unsigned)((size_t)B * S)), dim3(256), shm, st, idx,
-                     seg, B, S, K, bits);
+                     seg, B, S, Sk, ratio, K, bits);
   return hipGetLastError();
 }
 
-hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int qt0, int qt1, uint8_t* cls,
+hipError_t launch_tile_classes(const uint64_t* bits, int B, int S, int Sk, int qt0, int qt1, uint8_t* cls,
                                hipStream_t st) {
   if (qt1 <= qt0) return hipSuccess;
-  dim3 grid((unsigned)((n_ktiles(S) + 63) / 64), (unsigned)(qt1 - qt0), (unsigned)B);
-  hipLaunchKernelGGL(tile_class_kernel, grid, dim3(256), 0, st, bits, S, qt0, cls);
+  dim3 grid((unsigned)((n_ktiles(Sk) + 63) / 64), (unsigned)(qt1 - qt0), (unsigned)B);
+  hipLaunchKernelGGL(tile_class_kernel, grid, dim3(256), 0, st, bits, S, Sk, qt0, cls);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED", 3: "D
 EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "dsa_indexer_rope", "dsa_topk", "dsa_build_mask", "dsa_sparse_attn_fwd",
            "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
            "dsa_indexer_teacher", "dsa_indexer_kl", "dsa_indexer_bwd",
+           "dsa_csa_mask_bytes", "dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -69,6 +70,16 @@ def lib() -> ctypes.CDLL:
                   "dsa_sparse_attn_bwd_dq",
                   "dsa_sparse_attn_bwd_dkdv", "dsa_indexer_teacher", "dsa_indexer_kl", "dsa_indexer_bwd"):
             getattr(L, f).restype = ctypes.c_int
+        L.dsa_csa_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, i32, i64,
+                                           vp]
+        L.dsa_csa_topk.argtypes = [vp, i32, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.dsa_csa_build_mask.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
+        L.dsa_csa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp,
+                                              vp]
+        for f in ("dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd"):
+            getattr(L, f).restype = i32
+        L.dsa_csa_mask_bytes.argtypes = [i32, i32, i32]
+        L.dsa_csa_mask_bytes.restype = sz
         L.dsa_mask_bytes.argtypes = [i32, i32]
         L.dsa_mask_bytes.restype = sz
         L.dsa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -127,10 +138,16 @@ def dsa_bwd_workspace_min_bytes(B: int, S: int, H: int) -> int:
     return int(lib().dsa_bwd_workspace_min_bytes(B, S, H))
 
 
-def mask_views(mask: torch.Tensor, B: int, S: int):
-    """(sel_bits int64 [B,S,W], tile_cls uint8 [B,NQ,NK]) views of a mask buffer."""
-    W = (S + 63) // 64
-    nq, nk = (S + TILE_Q - 1) // TILE_Q, (S + TILE_K - 1) // TILE_K
+def dsa_csa_mask_bytes(B: int, S: int, Sk: int) -> int:
+    return int(lib().dsa_csa_mask_bytes(B, S, Sk))
+
+
+def mask_views(mask: torch.Tensor, B: int, S: int, Sk: Optional[int] = None):
+    """(sel_bits int64 [B,S,W], tile_cls uint8 [B,NQ,NK]) views of a mask buffer
+    (keys: S tokens, or Sk compressed entries)."""
+    Sk = S if Sk is None else Sk
+    W = (Sk + 63) // 64
+    nq, nk = (S + TILE_Q - 1) // TILE_Q, (Sk + TILE_K - 1) // TILE_K
     nb = B * S * W * 8
     bits = mask[:nb].view(torch.int64).view(B, S, W)
     cls = mask[nb:nb + B * nq * nk].view(B, nq, nk)
@@ -194,6 +211,35 @@ def dsa_sparse_attn_fwd(q, k, v, mask, softmax_scale: float, o, lse, stream=None
     _check("dsa_sparse_attn_fwd", lib().dsa_sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(mask), B, S, H, Dqk, Dv, float(softmax_scale), _dt(q),
         _ptr(o), _ptr(lse), _stream(stream)))
+
+
+# compressed sparse attention: keys are Sk = S // ratio compressed entries
+def dsa_csa_index_scores(q_idx, k_idx, w, ratio: int, row0: int, nrows: int, scores, stream=None) -> None:
+    B, S, Hi, Di = q_idx.shape
+    Sk = k_idx.shape[1]
+    _check("dsa_csa_index_scores", lib().dsa_csa_index_scores(
+        _ptr(q_idx), _ptr(k_idx), _ptr(w), B, S, Sk, ratio, Hi, Di, _dt(q_idx), row0, nrows, _ptr(scores),
+        _dt(scores), scores.shape[-1], _stream(stream)))
+
+
+def dsa_csa_topk(scores, B: int, S: int, Sk: int, ratio: int, K: int, row0: int, nrows: int, idx, mask,
+                 stream=None) -> None:
+    _check("dsa_csa_topk", lib().dsa_csa_topk(
+        _ptr(scores), _dt(scores), scores.shape[-1], B, S, Sk, ratio, K, row0, nrows, _ptr(idx), _ptr(mask),
+        _stream(stream)))
+
+
+def dsa_csa_build_mask(idx, Sk: int, ratio: int, mask, stream=None) -> None:
+    B, S, K = idx.shape
+    _check("dsa_csa_build_mask", lib().dsa_csa_build_mask(_ptr(idx), B, S, Sk, ratio, K, _ptr(mask), _stream(stream)))
+
+
+def dsa_csa_sparse_attn_fwd(q, k, v, mask, ratio: int, softmax_scale: float, o, lse, stream=None) -> None:
+    B, S, H, Dqk = q.shape
+    Sk, Dv = k.shape[1], v.shape[-1]
+    _check("dsa_csa_sparse_attn_fwd", lib().dsa_csa_sparse_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(mask), B, S, Sk, ratio, H, Dqk, Dv, float(softmax_scale), _dt(q), _ptr(o),
+        _ptr(lse), _stream(stream)))
 
 
 def dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, dk, dv, workspace,

@@ -57,6 +57,12 @@ class Config:
     backward: bool = False
     score_dtype: str = "fp32"
     seed: int = 0
+    ratio: int = 1   # keys are compressed blocks of `ratio` tokens (1: token-level DSA)
+
+    @property
+    def Sk(self) -> int:
+        """Keys per batch row: S tokens, or S // ratio compressed entries."""
+        return self.S // self.ratio
 
     @property
     def softmax_scale(self) -> float:
@@ -81,6 +87,13 @@ CONFIGS = {
                  segments=(64, 4096), backward=True),
     "c5": Config("c5_long_s128k", 1, 131072, 64, 128, 2048, 128, 192, 128, "bf16", True,
                  score_dtype="bf16"),
+}
+
+# Compressed sparse attention (DeepSeek-V4 CSA, compression ratio 4) on the 2B
+# shape: 1024 compressed entries per row of 4096 tokens; top-k scaled by the
+# ratio (2048 / 4). Forward only. Not one of the five metric workloads.
+CSA_CONFIGS = {
+    "csa": Config("csa_r4_b12_s4k", 12, 4096, 64, 128, 512, 16, 192, 128, "bf16", True, ratio=4),
 }
 
 
@@ -123,12 +136,13 @@ def make(cfg: Config, device="cpu", with_dout: Optional[bool] = None) -> dict:
     def sig(d):
         return float(d) ** -0.5 if cfg.scaled else 1.0
 
+    Sk = cfg.Sk  # key-side rows: tokens, or compressed entries
     out = {
         "q": normal((B, S, cfg.H, cfg.Dqk), sig(cfg.Dqk), cfg.seed, "q", dt, device),
-        "k": normal((B, S, cfg.H, cfg.Dqk), sig(cfg.Dqk), cfg.seed, "k", dt, device),
-        "v": normal((B, S, cfg.H, cfg.Dv), sig(cfg.Dv), cfg.seed, "v", dt, device),
+        "k": normal((B, Sk, cfg.H, cfg.Dqk), sig(cfg.Dqk), cfg.seed, "k", dt, device),
+        "v": normal((B, Sk, cfg.H, cfg.Dv), sig(cfg.Dv), cfg.seed, "v", dt, device),
         "q_idx": normal((B, S, cfg.Hi, cfg.Di), sig(cfg.Di), cfg.seed, "q_idx", dt, device),
-        "k_idx": normal((B, S, cfg.Di), sig(cfg.Di), cfg.seed, "k_idx", dt, device),
+        "k_idx": normal((B, Sk, cfg.Di), sig(cfg.Di), cfg.seed, "k_idx", dt, device),
         "w": normal((B, S, cfg.Hi), float(cfg.Hi) ** -0.5, cfg.seed, "w", dt, device),
     }
     if with_dout is None:

@@ -183,3 +183,39 @@ def test_indexer_loss_calls_reject_before_any_launch():
     assert bw(P, P, P, P, 64, P, 1, 64, 64, 64, 0, P, P, P, S_) == 2
     assert bw(P, P, P, P, 63, P, 1, 64, 64, 128, 0, P, P, P, S_) == 1
     assert bw(P, P, P, P, 64, P, 1, 64, 64, 128, 1, P, P, P, S_) == 2
+
+
+def test_csa_sizes_and_rejects():
+    """Compressed-key calls: mask size over Sk keys; ratio, Sk and ld checked
+    on the host before any launch."""
+    L = dsa.lib()
+    B, S, Sk = 2, 1000, 250
+    W = (Sk + 63) // 64
+    assert dsa.dsa_csa_mask_bytes(B, S, Sk) == B * S * W * 8 + B * ((S + 127) // 128) * ((Sk + 63) // 64)
+    assert dsa.dsa_csa_mask_bytes(B, S, S) == dsa.dsa_mask_bytes(B, S)
+    assert dsa.dsa_csa_mask_bytes(B, S, 0) == 0
+
+    def scores(**kw):
+        a = dict(B=1, S=128, Sk=32, r=4, ld=32, row0=0, nrows=128)
+        a.update(kw)
+        return L.dsa_csa_index_scores(P, P, P, a["B"], a["S"], a["Sk"], a["r"], 64, 128, 0, a["row0"], a["nrows"],
+                                      P, 1, a["ld"], S_)
+
+    for kw in (dict(r=0), dict(Sk=33), dict(Sk=31), dict(S=3, Sk=0, nrows=3), dict(ld=31), dict(nrows=129)):
+        assert scores(**kw) == 1, kw
+
+    def topk(**kw):
+        a = dict(S=128, Sk=32, r=4, K=8, ld=32, row0=0, nrows=128)
+        a.update(kw)
+        return L.dsa_csa_topk(P, 0, a["ld"], 1, a["S"], a["Sk"], a["r"], a["K"], a["row0"], a["nrows"], P, P, S_)
+
+    for kw in (dict(r=-1), dict(Sk=64), dict(K=0), dict(ld=16), dict(row0=64, nrows=64)):
+        assert topk(**kw) == 1, kw
+    assert L.dsa_csa_build_mask(P, 1, 128, 64, 4, 8, P, S_) == 1       # Sk != S / ratio
+    assert L.dsa_csa_build_mask(NUL, 1, 128, 32, 4, 8, P, S_) == 1
+    fwd = L.dsa_csa_sparse_attn_fwd
+    assert fwd(P, P, P, P, 1, 128, 32, 0, 2, 192, 128, 0.1, 0, P, P, S_) == 1      # ratio 0
+    assert fwd(P, P, P, P, 1, 128, 31, 4, 2, 192, 128, 0.1, 0, P, P, S_) == 1      # Sk
+    assert fwd(P, P, P, P, 1, 128, 32, 4, 2, 192, 128, -1.0, 0, P, P, S_) == 1     # scale
+    assert fwd(P, P, P, MIS, 1, 128, 32, 4, 2, 192, 128, 0.1, 0, P, P, S_) == 1    # misaligned mask
+    assert fwd(P, P, P, P, 1, 128, 32, 4, 2, 512, 128, 0.1, 0, P, P, S_) == 2      # head dim above 256
