@@ -292,6 +292,67 @@ def long_workload(key, reps=2, attention=True):
     return out
 
 
+def csa_workload(reps=5):
+    """The compressed-key (CSA) forward path at its workload: indexer over the
+    Sk = S / ratio compressed entries, top-k and the attention forward, one
+    warm-up pass then `reps` timed passes, HIP events on the launch stream.
+    Useful work counts the entries visible to each row, (t + 1) // ratio."""
+    import torch
+    from sparse_attention_06_amd import dsa, inputs
+    cfg = inputs.CSA_CONFIGS["csa"]
+    B, S, Sk, K, H, r = cfg.B, cfg.S, cfg.Sk, cfg.K, cfg.H, cfg.ratio
+    x = inputs.make(cfg, device="cuda")
+    scores = torch.empty((B, S, Sk), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, S, K), dtype=torch.int32, device="cuda")
+    mask = torch.empty(dsa.dsa_csa_mask_bytes(B, S, Sk), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, S, H, cfg.Dv), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    t = {"index_scores": [], "topk": [], "attn_fwd": []}
+    for i in range(reps + 1):
+        ev[0].record(stream)
+        dsa.dsa_csa_index_scores(x["q_idx"], x["k_idx"], x["w"], r, 0, S, scores)
+        ev[1].record(stream)
+        dsa.dsa_csa_topk(scores, B, S, Sk, r, K, 0, S, idx, mask)
+        ev[2].record(stream)
+        dsa.dsa_csa_sparse_attn_fwd(x["q"], x["k"], x["v"], mask, r, cfg.softmax_scale, o, lse)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if i:
+            for j, c in enumerate(t):
+                t[c].append(ev[j].elapsed_time(ev[j + 1]))
+    nv = np.broadcast_to((np.arange(S, dtype=np.int64) + 1) // r, (B, S))
+    sel = np.minimum(nv, K)
+    W = (Sk + 63) // 64
+    flops_idx = int(nv.sum()) * cfg.Hi * 2 * cfg.Di
+    flops_fwd = int(sel.sum()) * H * 2 * (cfg.Dqk + cfg.Dv)
+    topk_bytes = int(nv[nv > K].sum()) * 4 + B * S * K * 4 + B * S * W * 8
+    _, cls = dsa.mask_views(mask, B, S, Sk)
+    cls_np = cls.cpu().numpy()
+    executed = int((cls_np != 0).sum()) * 128 * 64 * H * 2 * (cfg.Dqk + cfg.Dv)
+    ms = {c: float(np.median(v)) for c, v in t.items()}
+    kern = {
+        "index_scores": {"ms": ms["index_scores"], "achieved": flops_idx / (ms["index_scores"] * 1e-3) / 1e12,
+                         "unit": "TFLOP/s", "bound": "mfma", "algorithmic": flops_idx},
+        "topk": {"ms": ms["topk"], "achieved": topk_bytes / (ms["topk"] * 1e-3) / 1e9, "unit": "GB/s",
+                 "bound": "hbm", "algorithmic": topk_bytes},
+        "attn_fwd": {"ms": ms["attn_fwd"], "achieved": flops_fwd / (ms["attn_fwd"] * 1e-3) / 1e12,
+                     "unit": "TFLOP/s", "bound": "mfma", "algorithmic": flops_fwd,
+                     "executed_tile_tflops": executed / (ms["attn_fwd"] * 1e-3) / 1e12,
+                     "useful_over_executed": flops_fwd / executed},
+    }
+    for c, k in kern.items():
+        k["frac"] = k["achieved"] / (PEAK_HBM_GBS if k["bound"] == "hbm" else PEAK_BF16_TFLOPS)
+        k["ms_stats"] = stats(t[c])
+    total = sum(ms.values())
+    del x, scores, idx, mask, o, lse
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "ratio": r, "S": S, "Sk": Sk, "K": K, "heads": H, "passes": "+".join(t),
+            "ms_per_pass": total, "useful_tflops": (flops_idx + flops_fwd) / (total * 1e-3) / 1e12,
+            "indexer_topk_ms": ms["index_scores"] + ms["topk"], "kernels": kern}
+
+
 CALLS_FWD = ["index_scores", "topk", "attn_fwd"]
 CALLS_BWD = ["attn_bwd_prep", "attn_bwd_dkdv", "attn_bwd_dq"]
 
@@ -488,6 +549,7 @@ def main():
     ap.add_argument("--no-c1", action="store_true", help="skip the tiny workload's latency")
     ap.add_argument("--no-scrub", action="store_true", help="do not overwrite 512 MB before each timed step")
     ap.add_argument("--no-kl", action="store_true", help="skip timing the indexer KL auxiliary loss")
+    ap.add_argument("--no-csa", action="store_true", help="skip the compressed-key (CSA) forward workload")
     ap.add_argument("--long-only", action="store_true",
                     help="only the 32K and 128K workloads (one JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -592,6 +654,13 @@ def main():
     if not args.no_long:
         selection.update(run_long())
 
+    csa = None
+    if not args.no_csa:
+        log("compressed-key (CSA) forward workload")
+        csa = csa_workload()
+        log(f"  {csa['ms_per_pass']:.3f} ms per pass; " +
+            ", ".join(f"{c} {v['ms']:.3f}" for c, v in csa["kernels"].items()))
+
     c1 = None
     if not args.no_c1:
         log("tiny fp32 workload latency")
@@ -604,6 +673,8 @@ def main():
     add_measured(kernels, mp)
     if c4 is not None:
         add_measured(c4["kernels"], mp)
+    if csa is not None:
+        add_measured(csa["kernels"], mp)
     roofline["frac_measured"] = kernels[dom]["frac_measured"]
 
     cpu = None
@@ -627,6 +698,7 @@ def main():
         "kernels": kernels,
         "c4": c4,
         "c1": c1,
+        "csa": csa,
         "indexer_loss": indexer_loss,
         "roofline": roofline,
         "measured_peaks": mp,
