@@ -792,10 +792,39 @@ def csa_attention_fwd(q, k_c, v_c, idx, ratio: int, scale: float, rows):
     L = np.full((B, H, rows.size), NEG_INF)
     for b in range(B):
         for r, t in enumerate(rows):
-            sel = np.asarray(idx[b, r])
-            sel = sel[(sel >= 0) & (sel < Sk)]      # entries that do not exist are not visible
-            ks = np.unique(sel[csa_valid_row(Sk, ratio, int(t))[sel]])
+            ks = _csa_kept(idx[b, r], Sk, ratio, int(t))   # entries that do not exist are not visible
             if ks.size == 0:
                 continue
             O[b, r], L[b, :, r] = attention_fwd_row(q[b, t], k_c[b, ks], v_c[b, ks], scale)
     return O, L
+
+
+def _csa_kept(idx_row, Sk: int, ratio: int, t: int) -> np.ndarray:
+    """Entries kept for query t: its index list within [0, Sk), cut to the visible ones."""
+    sel = np.asarray(idx_row)
+    sel = sel[(sel >= 0) & (sel < Sk)]
+    return np.unique(sel[csa_valid_row(Sk, ratio, t)[sel]])
+
+
+def csa_attention_bwd(q, k_c, v_c, dout, idx, ratio: int, scale: float):
+    """Gradients of sum(O * dout) w.r.t. q, k_c, v_c over every row, in float64:
+    DSA's backward (same P, dS and sums) over each row's kept compressed entries.
+    idx [B, S, K]. Returns dq [B,S,H,Dqk], dk_c [B,Sk,H,Dqk], dv_c [B,Sk,H,Dv]."""
+    q = np.asarray(q, dtype=np.float64)
+    k_c = np.asarray(k_c, dtype=np.float64)
+    v_c = np.asarray(v_c, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S = q.shape[:2]
+    Sk = k_c.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k_c)
+    dv = np.zeros_like(v_c)
+    for b in range(B):
+        for t in range(S):
+            ks = _csa_kept(idx[b, t], Sk, ratio, t)
+            if ks.size == 0:
+                continue
+            dq[b, t], dk_sel, dv_sel = attention_bwd_row(q[b, t], k_c[b, ks], v_c[b, ks], dout[b, t], scale)
+            dk[b, ks] += dk_sel
+            dv[b, ks] += dv_sel
+    return dq, dk, dv

@@ -1175,7 +1175,57 @@ def test_csa_planted_mistakes_fail_a_pin(monkeypatch):
         with pytest.raises(AssertionError):
             test_csa_keep_all_is_block_causal_dense_attention()
         monkeypatch.undo()
+        monkeypatch.setattr(ref, "csa_valid_row", bad)
+        with pytest.raises(AssertionError):
+            test_csa_backward_equals_dsa_on_the_token_axis_and_autograd()
+        monkeypatch.undo()
     monkeypatch.setattr(ref, "csa_attention_fwd", no_visibility_cut)
     with pytest.raises(AssertionError):
         test_csa_keep_all_is_block_causal_dense_attention()
     monkeypatch.undo()
+
+
+def test_csa_backward_equals_dsa_on_the_token_axis_and_autograd():
+    """CSA gradients: (1) the pinned DSA backward on the token axis (entry c at
+    token ratio*c + ratio - 1, other positions never kept), gradients of the
+    token positions mapped back; (2) with every entry listed, torch float64
+    autograd through dense attention under the block-causal mask."""
+    rng = np.random.default_rng(8)
+    B, S, ratio, H, Dqk, Dv, K = 2, 27, 4, 2, 6, 5, 4
+    Sk = S // ratio
+    pos = ratio * np.arange(Sk) + ratio - 1
+    q = rng.standard_normal((B, S, H, Dqk))
+    k_c = rng.standard_normal((B, Sk, H, Dqk))
+    v_c = rng.standard_normal((B, Sk, H, Dv))
+    dout = rng.standard_normal((B, S, H, Dv))
+    scale = 0.45
+    tok = inputs.random_index_sets(B, S, K, None, seed=4)
+    idx_c = np.where(tok >= 0, tok // ratio, -1).astype(np.int32)
+    dq, dk, dv = ref.csa_attention_bwd(q, k_c, v_c, dout, idx_c, ratio, scale)
+    idx_tok = np.full((B, S, K), -1, np.int32)
+    for b in range(B):
+        for t in range(S):
+            kept = ref._csa_kept(idx_c[b, t], Sk, ratio, t)
+            idx_tok[b, t, : kept.size] = pos[kept]
+    dq_t, dk_t, dv_t = ref.attention_bwd(q, _on_token_axis(k_c, ratio, S), _on_token_axis(v_c, ratio, S), dout,
+                                         idx_tok, None, scale)
+    np.testing.assert_allclose(dq, dq_t, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_t[:, pos], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_t[:, pos], rtol=1e-12, atol=1e-12)
+    off_grid = np.setdiff1d(np.arange(S), pos)
+    assert not dk_t[:, off_grid].any() and not dv_t[:, off_grid].any()
+    # keep-all against autograd
+    idx_all = np.broadcast_to(np.arange(Sk, dtype=np.int32), (B, S, Sk)).copy()
+    dq, dk, dv = ref.csa_attention_bwd(q, k_c, v_c, dout, idx_all, ratio, scale)
+    vis = torch.from_numpy(np.array([[ratio * c + ratio - 1 <= t for c in range(Sk)] for t in range(S)]))
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k_c).requires_grad_()
+    tv = torch.from_numpy(v_c).requires_grad_()
+    logits = torch.einsum("bthd,bchd->bhtc", tq, tk) * scale
+    logits = logits.masked_fill(~vis, -math.inf)
+    p = torch.softmax(logits, dim=-1).nan_to_num(0.0)      # rows before the first block: no entry
+    o = torch.einsum("bhtc,bchd->bthd", p, tv)
+    (o * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
