@@ -252,8 +252,12 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  *         then tile_cls uint8 [B][ceil(S/DSA_TILE_Q)][ceil(Sk/DSA_TILE_K)]
  * Errors: DSA_ERR_INVALID_ARG for ratio < 1, Sk != S / ratio, Sk < 1, ld < Sk
  * or the argument checks of the matching DSA call; dtype, dims, row slabs and
- * kernels (MFMA or plain) as in those calls. Only the forward is provided: the
- * backward calls take token-level (ratio 1) masks.
+ * kernels (MFMA or plain) as in those calls.
+ * dsa_csa_sparse_attn_bwd: gradients of sum(O * dout) w.r.t. q, k, v with the
+ * forward's o, lse and mask; dq [B,S,H,Dqk], dk [B,Sk,H,Dqk], dv [B,Sk,H,Dv];
+ * workspace >= dsa_bwd_workspace_min_bytes(B,S,H) (D and LSE only: it runs the
+ * prologue and the plain key-major and query-major kernels, any dims up to 256,
+ * bf16 or fp32). The token-level backward calls take ratio-1 masks only.
  * ------------------------------------------------------------------------- */
 size_t dsa_csa_mask_bytes(int B, int S, int Sk);
 dsa_status dsa_csa_index_scores(const void* q_idx, const void* k_idx, const void* w, int B, int S, int Sk,
@@ -266,6 +270,10 @@ dsa_status dsa_csa_build_mask(const int32_t* idx, int B, int S, int Sk, int rati
 dsa_status dsa_csa_sparse_attn_fwd(const void* q, const void* k, const void* v, const void* mask, int B, int S,
                                    int Sk, int ratio, int H, int Dqk, int Dv, float softmax_scale,
                                    dsa_dtype dtype, void* o, float* lse, void* stream);
+dsa_status dsa_csa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, const void* mask, int B, int S, int Sk, int ratio, int H,
+                                   int Dqk, int Dv, float softmax_scale, dsa_dtype dtype, void* dq, void* dk,
+                                   void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * dsa_sparse_attn_bwd -- gradients of sum(O * dout) w.r.t. q, k, v.

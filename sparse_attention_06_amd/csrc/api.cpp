@@ -426,7 +426,7 @@ dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v,
                                                      softmax_scale, dk, dv, dsf, st),
                       "dsa_sparse_attn_bwd_dkdv");
   }
-  return hip_status(dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, H, Dqk, Dv,
+  return hip_status(dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, S, 1, H, Dqk, Dv,
                                                     softmax_scale, dtype == DSA_BF16, dk, dv, st),
                     "dsa_sparse_attn_bwd_dkdv");
 }
@@ -450,7 +450,7 @@ dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, c
     return hip_status(dsa::launch_attn_bwd_dq_recompute(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
                                                         softmax_scale, dq, st),
                       "dsa_sparse_attn_bwd_dq");
-  return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, H, Dqk, Dv,
+  return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, S, 1, H, Dqk, Dv,
                                                   softmax_scale, dtype == DSA_BF16, dq, st),
                     "dsa_sparse_attn_bwd_dq");
 }
@@ -476,6 +476,44 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
                                 workspace, workspace_bytes, stream);
 }
 
+
+// compressed keys: the prologue, then the plain key-major and query-major
+// kernels over the Sk entries (the MFMA dK/dV grid and its dS handoff layout
+// follow token causality)
+dsa_status dsa_csa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                   const float* lse, const void* mask, int B, int S, int Sk, int ratio, int H,
+                                   int Dqk, int Dv, float softmax_scale, dsa_dtype dtype, void* dq, void* dk,
+                                   void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  REQ_PTR(q);
+  REQ_PTR(k);
+  REQ_PTR(v);
+  REQ_PTR(o);
+  REQ_PTR(dout);
+  REQ_PTR(lse);
+  REQ_PTR(mask);
+  REQ_PTR(dq);
+  REQ_PTR(dk);
+  REQ_PTR(dv);
+  REQ_PTR(workspace);
+  dsa_status s = check_csa(B, S, Sk, ratio);
+  if (s != DSA_OK) return s;
+  s = check_attn(B, S, H, Dqk, Dv, softmax_scale, dtype);
+  if (s != DSA_OK) return s;
+  const size_t need = dsa_bwd_workspace_min_bytes(B, S, H);
+  REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = dtype == DSA_BF16;
+  const uint64_t* bits = bits_of(const_cast<void*>(mask));
+  float* ws = (float*)workspace;
+  hipError_t e = dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, bf16, ws, st);
+  if (e == hipSuccess)
+    e = dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, ws, bits, B, S, Sk, ratio, H, Dqk, Dv, softmax_scale,
+                                        bf16, dk, dv, st);
+  if (e == hipSuccess)
+    e = dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits, B, S, Sk, ratio, H, Dqk, Dv, softmax_scale, bf16,
+                                      dq, st);
+  return hip_status(e, "dsa_csa_sparse_attn_bwd");
+}
 
 // ---------------------------------------------------------------------------
 // Indexer KL auxiliary loss

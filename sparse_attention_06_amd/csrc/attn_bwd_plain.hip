@@ -68,12 +68,16 @@ hipError_t launch_attn_bwd_prep(const void* o, const void* dout, const float* ls
 // dq: one wave per (b, t, h), lanes over the keys of one mask word.
 // dk/dv: one wave per (b, s, h), lanes over 64 queries at a time (t >= s),
 //        reading bit (s % 64) of each query's word s / 64.
+// Keys may be compressed blocks ("Add Flash Attention Support to Deepseek v4",
+// Description): Sk keys of `ratio` tokens, key s visible to t when
+// ratio*s + ratio - 1 <= t; mask rows are ceil(Sk / 64) words. ratio 1 and
+// Sk = S is token-level DSA.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ D,
-    const uint64_t* __restrict__ bits, int B, int S, int H, int Dqk, int Dv, float scale,
+    const uint64_t* __restrict__ bits, int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale,
     T* __restrict__ dq) {
   __shared__ float qs[4][256], os[4][256], dss[4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -82,7 +86,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
   const int h = (int)(row % H);
   const int t = (int)((row / H) % S);
   const int b = (int)(row / ((size_t)H * S));
-  const int W = (S + 63) / 64;
+  const int W = (Sk + 63) / 64;
+  const int tk = (t + 1) / ratio - 1;  // last visible key
   for (int d = lane; d < Dqk; d += 64) qs[wid][d] = Elem<T>::load(q + row * Dqk + d);
   for (int d = lane; d < Dv; d += 64) os[wid][d] = Elem<T>::load(dout + row * Dv + d);
   __builtin_amdgcn_wave_barrier();
@@ -90,14 +95,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
   const float Dt = D[((size_t)b * H + h) * S + t];
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const uint64_t* brow = bits + ((size_t)b * S + t) * W;
-  for (int w = 0; w <= t / 64; ++w) {
+  for (int w = 0; w < (tk + 64) / 64; ++w) {
     const uint64_t word = brow[w];
     if (word == 0ull) continue;
     const int s = 64 * w + lane;
     float dsv = 0.f;
     if ((word >> lane) & 1ull) {
-      const T* krow = k + (((size_t)b * S + s) * H + h) * Dqk;
-      const T* vrow = v + (((size_t)b * S + s) * H + h) * Dv;
+      const T* krow = k + (((size_t)b * Sk + s) * H + h) * Dqk;
+      const T* vrow = v + (((size_t)b * Sk + s) * H + h) * Dv;
       float dot = 0.f, dp = 0.f;
       for (int d = 0; d < Dqk; ++d) dot = fmaf(qs[wid][d], Elem<T>::load(krow + d), dot);
       for (int e = 0; e < Dv; ++e) dp = fmaf(os[wid][e], Elem<T>::load(vrow + e), dp);
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_plain_kernel(
     for (int jj = 0; jj < 64; ++jj) {
       if (!((word >> jj) & 1ull)) continue;
       const float g = dss[wid][jj];
-      const T* krow = k + (((size_t)b * S + 64 * w + jj) * H + h) * Dqk;
+      const T* krow = k + (((size_t)b * Sk + 64 * w + jj) * H + h) * Dqk;
       for (int j = 0; j < 4; ++j) {
         const int d = lane + 64 * j;
         if (d < Dqk) acc[j] = fmaf(g, Elem<T>::load(krow + d), acc[j]);
@@ -127,20 +132,20 @@ template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_plain_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ D, const uint64_t* __restrict__ bits, int B,
-    int S, int H, int Dqk, int Dv, float scale, T* __restrict__ dk, T* __restrict__ dv) {
+    int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale, T* __restrict__ dk, T* __restrict__ dv) {
   __shared__ float ks_[4][256], vs_[4][256], ps[4][64], dss[4][64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const size_t row = (size_t)blockIdx.x * 4 + wid;  // (b, s, h)
-  if (row >= (size_t)B * S * H) return;
+  const size_t row = (size_t)blockIdx.x * 4 + wid;  // (b, s, h), s one of the Sk keys
+  if (row >= (size_t)B * Sk * H) return;
   const int h = (int)(row % H);
-  const int s = (int)((row / H) % S);
-  const int b = (int)(row / ((size_t)H * S));
-  const int W = (S + 63) / 64;
+  const int s = (int)((row / H) % Sk);
+  const int b = (int)(row / ((size_t)H * Sk));
+  const int W = (Sk + 63) / 64;
   for (int d = lane; d < Dqk; d += 64) ks_[wid][d] = Elem<T>::load(k + row * Dqk + d);
   for (int d = lane; d < Dv; d += 64) vs_[wid][d] = Elem<T>::load(v + row * Dv + d);
   __builtin_amdgcn_wave_barrier();
   float ak[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = s; t0 < S; t0 += 64) {
+  for (int t0 = ratio * s + ratio - 1; t0 < S; t0 += 64) {  // the first query that sees key s
     const int t = t0 + lane;
     float p = 0.f, dsv = 0.f;
     bool kept = false;
@@ -179,33 +184,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_plain_kernel(
 
 hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,
                                     const void* dout, const float* lse, const float* D, const uint64_t* bits,
-                                    int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
-                                    void* dq, hipStream_t st) {
+                                    int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale,
+                                    bool bf16, void* dq, hipStream_t st) {
   const size_t nblk = ((size_t)B * S * H + 3) / 4;
   if (bf16)
     hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                       (const uint16_t*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale, (uint16_t*)dq);
+                       (const uint16_t*)dout, lse, D, bits, B, S, Sk, ratio, H, Dqk, Dv, scale, (uint16_t*)dq);
   else
     hipLaunchKernelGGL(attn_bwd_dq_plain_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
                        (const float*)q, (const float*)k, (const float*)v,
-                       (const float*)dout, lse, D, bits, B, S, H, Dqk, Dv, scale, (float*)dq);
+                       (const float*)dout, lse, D, bits, B, S, Sk, ratio, H, Dqk, Dv, scale, (float*)dq);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* v, const void* dout,
                                       const float* lse, const float* D, const uint64_t* bits, int B,
-                                      int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dk,
-                                      void* dv, hipStream_t st) {
-  const size_t nblk = ((size_t)B * S * H + 3) / 4;
+                                      int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale, bool bf16,
+                                      void* dk, void* dv, hipStream_t st) {
+  const size_t nblk = ((size_t)B * Sk * H + 3) / 4;
   if (bf16)
     hipLaunchKernelGGL(attn_bwd_dkdv_plain_kernel<uint16_t>, dim3((unsigned)nblk), dim3(256), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout,
-                       lse, D, bits, B, S, H, Dqk, Dv, scale, (uint16_t*)dk, (uint16_t*)dv);
+                       lse, D, bits, B, S, Sk, ratio, H, Dqk, Dv, scale, (uint16_t*)dk, (uint16_t*)dv);
   else
     hipLaunchKernelGGL(attn_bwd_dkdv_plain_kernel<float>, dim3((unsigned)nblk), dim3(256), 0, st,
                        (const float*)q, (const float*)k, (const float*)v, (const float*)dout, lse, D,
-                       bits, B, S, H, Dqk, Dv, scale, (float*)dk, (float*)dv);
+                       bits, B, S, Sk, ratio, H, Dqk, Dv, scale, (float*)dk, (float*)dv);
   return hipGetLastError();
 }
 

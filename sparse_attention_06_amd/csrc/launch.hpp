@@ -60,8 +60,8 @@ hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v
                                      int H, float scale, void* dk, void* dv, void* dsf, hipStream_t st);
 hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* v, const void* dout,
                                       const float* lse, const float* D, const uint64_t* bits, int B,
-                                      int S, int H, int Dqk, int Dv, float scale, bool bf16, void* dk,
-                                      void* dv, hipStream_t st);
+                                      int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale, bool bf16,
+                                      void* dk, void* dv, hipStream_t st);
 // backward, query-major: dq from the dS^T fragments of the key-major kernel
 // (which then gets a non-null dsf), or with dS recomputed from q, k, v, dout
 // and the workspace's D and base-2 LSE (key-major kernel given dsf = nullptr)
@@ -72,8 +72,8 @@ hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t
                                    float scale, void* dq, hipStream_t st);
 hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,
                                     const void* dout, const float* lse, const float* D, const uint64_t* bits,
-                                    int B, int S, int H, int Dqk, int Dv, float scale, bool bf16,
-                                    void* dq, hipStream_t st);
+                                    int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale,
+                                    bool bf16, void* dq, hipStream_t st);
 
 // indexer KL auxiliary loss: teacher [B,S,K] (bf16 q, k with Dqk in {64, 128,
 // 192}); student softmax, KL per row, loss2 = {loss, N} and the dense score

@@ -25,6 +25,7 @@ EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "ds
            "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
            "dsa_indexer_teacher", "dsa_indexer_kl", "dsa_indexer_bwd",
            "dsa_csa_mask_bytes", "dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd",
+           "dsa_csa_sparse_attn_bwd",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -76,7 +77,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_csa_build_mask.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp]
         L.dsa_csa_sparse_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp,
                                               vp]
-        for f in ("dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd"):
+        L.dsa_csa_sparse_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                              i32, vp, vp, vp, vp, sz, vp]
+        for f in ("dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd",
+                  "dsa_csa_sparse_attn_bwd"):
             getattr(L, f).restype = i32
         L.dsa_csa_mask_bytes.argtypes = [i32, i32, i32]
         L.dsa_csa_mask_bytes.restype = sz
@@ -240,6 +244,16 @@ def dsa_csa_sparse_attn_fwd(q, k, v, mask, ratio: int, softmax_scale: float, o, 
     _check("dsa_csa_sparse_attn_fwd", lib().dsa_csa_sparse_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(mask), B, S, Sk, ratio, H, Dqk, Dv, float(softmax_scale), _dt(q), _ptr(o),
         _ptr(lse), _stream(stream)))
+
+
+def dsa_csa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, ratio: int, softmax_scale: float, dq, dk, dv, workspace,
+                            stream=None) -> None:
+    B, S, H, Dqk = q.shape
+    Sk, Dv = k.shape[1], v.shape[-1]
+    _check("dsa_csa_sparse_attn_bwd", lib().dsa_csa_sparse_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(mask), B, S, Sk, ratio, H, Dqk, Dv,
+        float(softmax_scale), _dt(q), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def dsa_sparse_attn_bwd(q, k, v, o, dout, lse, mask, softmax_scale: float, dq, dk, dv, workspace,

@@ -219,3 +219,18 @@ def test_csa_sizes_and_rejects():
     assert fwd(P, P, P, P, 1, 128, 32, 4, 2, 192, 128, -1.0, 0, P, P, S_) == 1     # scale
     assert fwd(P, P, P, MIS, 1, 128, 32, 4, 2, 192, 128, 0.1, 0, P, P, S_) == 1    # misaligned mask
     assert fwd(P, P, P, P, 1, 128, 32, 4, 2, 512, 128, 0.1, 0, P, P, S_) == 2      # head dim above 256
+
+
+def test_csa_backward_rejects_before_any_launch():
+    bwd = dsa.lib().dsa_csa_sparse_attn_bwd
+    need = dsa.dsa_bwd_workspace_min_bytes(1, 128, 2)
+    args = lambda **kw: [kw.get(n, d) for n, d in (
+        ("q", P), ("k", P), ("v", P), ("o", P), ("dout", P), ("lse", P), ("mask", P), ("B", 1), ("S", 128),
+        ("Sk", 32), ("r", 4), ("H", 2), ("Dqk", 192), ("Dv", 128), ("scale", 0.1), ("dt", 0), ("dq", P), ("dk", P),
+        ("dv", P), ("ws", P), ("wsb", need), ("st", S_))]
+    assert bwd(*args(r=0)) == 1
+    assert bwd(*args(Sk=33)) == 1
+    assert bwd(*args(dk=NUL)) == 1
+    assert bwd(*args(mask=MIS)) == 1
+    assert bwd(*args(wsb=need - 1)) == 3      # DSA_ERR_WORKSPACE
+    assert bwd(*args(Dqk=300)) == 2

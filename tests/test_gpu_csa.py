@@ -249,3 +249,36 @@ def test_csa_workload_fullsize():
             check_close(f"O[{b},{t}]", f64(o[b, t]), Ot, True)
             np.testing.assert_allclose(lse[b, :, t].cpu().numpy(), Lt, rtol=0, atol=1e-4)
     assert n_dec >= 0.75 * 2 * rows.size
+
+
+# ------------------------------------------------------------------ backward
+@pytest.mark.parametrize("ratio,dims,dtype", [(4, (192, 128), "bf16"), (3, (64, 64), "fp32"),
+                                              (5, (64, 32), "bf16")])
+def test_csa_attention_bwd(ratio, dims, dtype):
+    """dq, dk, dv of the compressed keys, element by element, on mapped random
+    sets (visible entries, incomplete blocks, duplicates, past-the-end
+    entries), after the forward on the same mask."""
+    cfg = _cfg(ratio=ratio, Dqk=dims[0], Dv=dims[1], dtype=dtype, K=24, backward=True)
+    x, d = _make(cfg)
+    B, S, Sk, H = cfg.B, cfg.S, cfg.Sk, cfg.H
+    sets = _entry_sets(cfg)
+    mask = torch.empty(dsa.dsa_csa_mask_bytes(B, S, Sk), dtype=torch.uint8, device=DEV)
+    dsa.dsa_csa_build_mask(torch.from_numpy(sets).to(DEV), Sk, ratio, mask)
+    o = torch.empty((B, S, H, cfg.Dv), dtype=d["q"].dtype, device=DEV)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    dsa.dsa_csa_sparse_attn_fwd(d["q"], d["k"], d["v"], mask, ratio, cfg.softmax_scale, o, lse)
+    dq = torch.full_like(d["q"], float("nan"))
+    dk = torch.full_like(d["k"], float("nan"))
+    dv = torch.full_like(d["v"], float("nan"))
+    ws = torch.full((dsa.dsa_bwd_workspace_min_bytes(B, S, H),), 0x7F, dtype=torch.uint8, device=DEV)
+    dsa.dsa_csa_sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, mask, ratio, cfg.softmax_scale, dq, dk,
+                                dv, ws)
+    torch.cuda.synchronize()
+    want_dq, want_dk, want_dv = ref.csa_attention_bwd(f64(x["q"]), f64(x["k"]), f64(x["v"]), f64(x["dout"]), sets,
+                                                      ratio, cfg.softmax_scale)
+    bf16 = dtype == "bf16"
+    rel = 2e-2 if bf16 else None
+    check_close("dq", f64(dq), want_dq, bf16, rel)
+    check_close("dk", f64(dk), want_dk, bf16, rel)
+    check_close("dv", f64(dv), want_dv, bf16, rel)
+    assert np.all(f64(dq)[:, : ratio - 1] == 0)   # rows that see no entry
