@@ -255,11 +255,15 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  * kernels (MFMA or plain) as in those calls.
  * dsa_csa_sparse_attn_bwd: gradients of sum(O * dout) w.r.t. q, k, v with the
  * forward's o, lse and mask; dq [B,S,H,Dqk], dk [B,Sk,H,Dqk], dv [B,Sk,H,Dv];
- * workspace >= dsa_bwd_workspace_min_bytes(B,S,H) (D and LSE only: it runs the
- * prologue and the plain key-major and query-major kernels, any dims up to 256,
- * bf16 or fp32). The token-level backward calls take ratio-1 masks only.
+ * workspace >= dsa_bwd_workspace_min_bytes(B,S,H). It runs the prologue and the
+ * key-major and query-major kernels: MFMA for bf16 192/128, with the dS handoff
+ * when workspace_bytes >= dsa_csa_bwd_workspace_bytes(...) (each 32-query chunk
+ * then holds all ceil(Sk/64) key tiles, 4 KB each, per (b, h); capped like the
+ * token-level one), plain kernels otherwise (any dims up to 256, bf16 or fp32).
+ * The token-level backward calls take ratio-1 masks only.
  * ------------------------------------------------------------------------- */
 size_t dsa_csa_mask_bytes(int B, int S, int Sk);
+size_t dsa_csa_bwd_workspace_bytes(int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, dsa_dtype dtype);
 dsa_status dsa_csa_index_scores(const void* q_idx, const void* k_idx, const void* w, int B, int S, int Sk,
                                 int ratio, int Hi, int Di, dsa_dtype in_dtype, int row0, int nrows,
                                 void* scores, dsa_dtype score_dtype, int64_t ld, void* stream);

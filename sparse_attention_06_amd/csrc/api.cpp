@@ -79,6 +79,11 @@ static bool bwd_handoff(int B, int S, int H, int Dqk, int Dv, dsa_dtype dtype, s
   return attn_mfma(Dqk, Dv, dtype) && workspace_bytes >= bwd_frag_offset(B, S, H) + bwd_handoff_bytes(B, S, H);
 }
 
+// the dS handoff over Sk compressed keys: every 32-query chunk holds all key tiles
+static size_t csa_handoff_bytes(int B, int S, int Sk, int H, int ratio) {
+  return (size_t)B * H * dsa::dsf_base((S + 31) / 32, ratio, dsa::n_ktiles(Sk)) * 4096;
+}
+
 size_t dsa_bwd_workspace_min_bytes(int B, int S, int H) {
   if (B < 1 || S < 1 || H < 1) return 0;
   return bwd_frag_offset(B, S, H);
@@ -88,6 +93,13 @@ size_t dsa_bwd_workspace_bytes(int B, int S, int H, int Dqk, int Dv, dsa_dtype d
   if (B < 1 || S < 1 || H < 1) return 0;
   if (attn_mfma(Dqk, Dv, dtype) && bwd_handoff_bytes(B, S, H) <= (size_t)DSA_BWD_HANDOFF_MAX_BYTES)
     return bwd_frag_offset(B, S, H) + bwd_handoff_bytes(B, S, H);
+  return bwd_frag_offset(B, S, H);
+}
+
+size_t dsa_csa_bwd_workspace_bytes(int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, dsa_dtype dtype) {
+  if (B < 1 || S < 1 || Sk < 1 || ratio < 1 || H < 1) return 0;
+  const size_t hb = csa_handoff_bytes(B, S, Sk, H, ratio);
+  if (attn_mfma(Dqk, Dv, dtype) && hb <= (size_t)DSA_BWD_HANDOFF_MAX_BYTES) return bwd_frag_offset(B, S, H) + hb;
   return bwd_frag_offset(B, S, H);
 }
 
@@ -422,7 +434,7 @@ dsa_status dsa_sparse_attn_bwd_dkdv(const void* q, const void* k, const void* v,
   if (attn_mfma(Dqk, Dv, dtype)) {
     void* dsf = bwd_handoff(B, S, H, Dqk, Dv, dtype, workspace_bytes)
                     ? (void*)((char*)workspace + bwd_frag_offset(B, S, H)) : nullptr;
-    return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
+    return hip_status(dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, S, 1, H,
                                                      softmax_scale, dk, dv, dsf, st),
                       "dsa_sparse_attn_bwd_dkdv");
   }
@@ -444,7 +456,7 @@ dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, c
   const float* ws = (const float*)workspace;
   if (bwd_handoff(B, S, H, Dqk, Dv, dtype, workspace_bytes))
     return hip_status(dsa::launch_attn_bwd_dq_mfma(k, (const char*)workspace + bwd_frag_offset(B, S, H),
-                                                   cls_of(m, B, S), B, S, H, softmax_scale, dq, st),
+                                                   cls_of(m, B, S), B, S, S, 1, H, softmax_scale, dq, st),
                       "dsa_sparse_attn_bwd_dq");
   if (attn_mfma(Dqk, Dv, dtype))
     return hip_status(dsa::launch_attn_bwd_dq_recompute(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
@@ -477,9 +489,9 @@ dsa_status dsa_sparse_attn_bwd(const void* q, const void* k, const void* v, cons
 }
 
 
-// compressed keys: the prologue, then the plain key-major and query-major
-// kernels over the Sk entries (the MFMA dK/dV grid and its dS handoff layout
-// follow token causality)
+// compressed keys: the prologue, then the key-major and query-major kernels
+// over the Sk entries (MFMA for bf16 192/128, with the dS handoff when the
+// workspace holds it; plain otherwise)
 dsa_status dsa_csa_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                    const float* lse, const void* mask, int B, int S, int Sk, int ratio, int H,
                                    int Dqk, int Dv, float softmax_scale, dsa_dtype dtype, void* dq, void* dk,
@@ -503,9 +515,24 @@ dsa_status dsa_csa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
   REQ(workspace_bytes >= need, DSA_ERR_WORKSPACE, "workspace %zu bytes < %zu", workspace_bytes, need);
   hipStream_t st = (hipStream_t)stream;
   const bool bf16 = dtype == DSA_BF16;
-  const uint64_t* bits = bits_of(const_cast<void*>(mask));
+  void* m = const_cast<void*>(mask);
+  const uint64_t* bits = bits_of(m);
   float* ws = (float*)workspace;
   hipError_t e = dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, bf16, ws, st);
+  if (attn_mfma(Dqk, Dv, dtype)) {
+    // the MFMA key-major kernel, handing dS to the MFMA dQ kernel when the
+    // workspace holds it (else dQ takes the plain kernel)
+    const bool handoff = workspace_bytes >= bwd_frag_offset(B, S, H) + csa_handoff_bytes(B, S, Sk, H, ratio);
+    void* dsf = handoff ? (void*)((char*)workspace + bwd_frag_offset(B, S, H)) : nullptr;
+    if (e == hipSuccess)
+      e = dsa::launch_attn_bwd_dkdv_mfma(q, k, v, dout, ws, bits, cls_of(m, B, S, Sk), B, S, Sk, ratio, H,
+                                         softmax_scale, dk, dv, dsf, st);
+    if (e == hipSuccess)
+      e = handoff ? dsa::launch_attn_bwd_dq_mfma(k, dsf, cls_of(m, B, S, Sk), B, S, Sk, ratio, H, softmax_scale, dq, st)
+                  : dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits, B, S, Sk, ratio, H, Dqk, Dv,
+                                                  softmax_scale, bf16, dq, st);
+    return hip_status(e, "dsa_csa_sparse_attn_bwd");
+  }
   if (e == hipSuccess)
     e = dsa::launch_attn_bwd_dkdv_plain(q, k, v, dout, lse, ws, bits, B, S, Sk, ratio, H, Dqk, Dv, softmax_scale,
                                         bf16, dk, dv, st);

@@ -97,7 +97,7 @@ template <bool HANDOFF>
 __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws, const uint64_t* __restrict__ bits,
-    const uint8_t* __restrict__ cls, int B, int S, int H, float scale, float scale_log2,
+    const uint8_t* __restrict__ cls, int B, int S, int Sk, int ratio, int H, float scale, float scale_log2,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, u32x4* __restrict__ dsf) {
   using namespace bwd;
   using dkv::NW;
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   const int half = lane >> 5, col = lane & 31;
   const bool roleA = wid < 4;
   const int kw = wid & 3;
-  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
-  const int nkb = (S + 127) / 128;
+  const int W = (Sk + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int nkb = (Sk + 127) / 128;
   const int L = xcd_remap((int)blockIdx.x, (int)gridDim.x);  // a (b, h)'s key blocks share an XCD
   const int kblk = L % nkb;
   const int bh = L / nkb;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   const int kb0 = kblk * 128;
   const int s0 = kb0 + kw * 32;   // this wave pair's first key
   const int sk = s0 + col;        // this lane's key
-  const bool kvalid = sk < S;
+  const bool kvalid = sk < Sk;
   const int kt_lo = kb0 / 64;     // workgroup's first key tile
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
   const uint16_t* qbase = q + (size_t)b * S * rs_qk + (size_t)h * DQK;
@@ -150,7 +150,8 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   __syncthreads();  // class column staged
   if (wid == 0) {   // compact the non-empty chunks from the diagonal on
     int cnt = 0;
-    for (int base = kb0 / QC; base < nchunks; base += 64) {
+    // from the chunk of the first query that sees the workgroup's first key
+    for (int base = (ratio * kb0 + ratio - 1) / QC; base < nchunks; base += 64) {
       const int qc = base + lane;
       int fl = 0;
       if (qc < nchunks) fl = (scls[0][qc * QC / 128] != 0) | ((scls[1][qc * QC / 128] != 0) << 1);
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
   // this wave pair's keys take part in the chunk: its key tile is non-empty
   // there and the chunk reaches the pair's first key (causal)
   auto active = [&](int e) __attribute__((always_inline)) {
-    return ((e >> (14 + (kw >> 1))) & 1) != 0 && s0 <= (e & 0x3FFF) * QC + QC - 1;
+    return ((e >> (14 + (kw >> 1))) & 1) != 0 && ratio * s0 + ratio - 1 <= (e & 0x3FFF) * QC + QC - 1;
   };
 
   // source offsets (elements from the chunk's first row) of this lane's Q / dO
@@ -265,13 +266,13 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int ks = 0; ks < DQK / 16; ++ks) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      if (kvalid) z = *(const u32x4*)(k + ((size_t)b * S + sk) * rs_qk + (size_t)h * DQK + ks * 16 + 8 * half);
+      if (kvalid) z = *(const u32x4*)(k + ((size_t)b * Sk + sk) * rs_qk + (size_t)h * DQK + ks * 16 + 8 * half);
       kf[ks] = z;
     }
 #pragma unroll
     for (int ks = 0; ks < DV / 16; ++ks) {
       u32x4 z = {0u, 0u, 0u, 0u};
-      if (kvalid) z = *(const u32x4*)(v + ((size_t)b * S + sk) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
+      if (kvalid) z = *(const u32x4*)(v + ((size_t)b * Sk + sk) * rs_v + (size_t)h * DV + ks * 16 + 8 * half);
       vf[ks] = z;
     }
     wait_vmem();  // once: the loop's waits then only concern chunk copies
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
         // tiles have every in-range bit set.
         const float Lq = smLD[bi][col], Dq = smLD[bi][QC + col];
         const uint32_t Wq = smW[bi][wsel][hsel][col] >> (4 * half);
-        u32x4* fr = dsf + (((size_t)bh * dsf_tile_base(nchunks) + dsf_tile_base(qc) + kt_lo + (kw >> 1)) * 4 +
+        u32x4* fr = dsf + (((size_t)bh * dsf_base(nchunks, ratio, NK) + dsf_base(qc, ratio, NK) + kt_lo + (kw >> 1)) * 4 +
                            2 * (kw & 1)) * 64 + lane;
         // P and dS. On a chunk of a FULL tile every pair is kept and the mask
         // select is skipped; not on a ragged last chunk, whose rows past S (kept
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
       // the A waves of key block j took part in chunk e: their key tile is
       // non-empty there and the chunk reaches the block's first key
       auto act = [&](int e, int j) __attribute__((always_inline)) {
-        return ((e >> (14 + kh)) & 1) != 0 && sb + 32 * j <= (e & 0x3FFF) * QC + QC - 1;
+        return ((e >> (14 + kh)) & 1) != 0 && ratio * (sb + 32 * j) + ratio - 1 <= (e & 0x3FFF) * QC + QC - 1;
       };
       bool prev = false, prev2 = false;
       int it = 0;
@@ -496,9 +497,9 @@ __global__ __launch_bounds__(dkv::NW * 64) void attn_bwd_dkdv_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int s = sb + 32 * j + col;
-        if (s >= S) continue;
-        uint16_t* dkrow = dk + ((size_t)b * S + s) * rs_qk + (size_t)h * DQK;
-        uint16_t* dvrow = dv + ((size_t)b * S + s) * rs_v + (size_t)h * DV;
+        if (s >= Sk) continue;
+        uint16_t* dkrow = dk + ((size_t)b * Sk + s) * rs_qk + (size_t)h * DQK;
+        uint16_t* dvrow = dv + ((size_t)b * Sk + s) * rs_v + (size_t)h * DV;
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
           // role 0: dK^T block i; role 1: dK^T block 5 (i == 0), dV^T block i-1
@@ -549,7 +550,7 @@ static_assert(KSL * 8 == bwd::QP, "pitch");
 
 __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ k, const u32x4* __restrict__ dsf, const uint8_t* __restrict__ cls, int B,
-    int S, int H, float scale, uint16_t* __restrict__ dq) {
+    int S, int Sk, int ratio, int H, float scale, uint16_t* __restrict__ dq) {
   using namespace bwd;
   using dqk::NW;
   using dqk::QW;
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
   const int half = lane >> 5, col = lane & 31;
-  const int NQ = (S + 127) / 128, NK = (S + 63) / 64;
+  const int NQ = (S + 127) / 128, NK = (Sk + 63) / 64;
   const int NQW = (S + QW - 1) / QW;
   const int nchunks = (S + QC - 1) / QC;
   // the query blocks of a (b, h) on one XCD (they share K), costliest first
@@ -573,10 +574,11 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   const int qt_w = min(NQ - 1, qc * QC / 128);
   const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
   const size_t rs_qk = (size_t)H * DQK;
-  const uint16_t* kbase = uniform_ptr(k + (size_t)b * S * rs_qk + (size_t)h * DQK);
+  const uint16_t* kbase = uniform_ptr(k + (size_t)b * Sk * rs_qk + (size_t)h * DQK);
   // this (b, h)'s fragment tiles, and this chunk's: key tile kt at + 256 * kt (u32x4 units)
-  const u32x4* fbh = uniform_ptr(dsf + (size_t)bh * dsf_tile_base(nchunks) * 256);
-  const u32x4* fch = uniform_ptr(fbh + dsf_tile_base(wvalid ? qc : 0) * 256);
+  const u32x4* fbh = uniform_ptr(dsf + (size_t)bh * dsf_base(nchunks, ratio, NK) * 256);
+  const u32x4* fch = uniform_ptr(fbh + dsf_base(wvalid ? qc : 0, ratio, NK) * 256);
+  const int kl_q = (qc * QC + QC) / ratio - 1;  // last key this chunk's last query sees
 
   f32x16 dqacc[DQK / 32];
 #pragma unroll
@@ -584,7 +586,9 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqacc[i][j] = 0.f;
 
-  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  // last key tile any of the workgroup's queries sees (-1: none)
+  const int kl_last = (min(S - 1, qw * QW + QW - 1) + 1) / ratio - 1;
+  const int kt_last = kl_last < 0 ? -1 : kl_last / TK;
   stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
   stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
   const uint8_t* cls0 = scls[0];
@@ -606,7 +610,7 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   }
   auto issue_k = [&](int kt, int buf) {
     const uint16_t* tb = kbase + (size_t)kt * TK * rs_qk;
-    const int lim = S - 1 - kt * TK;  // last in-range row of the tile
+    const int lim = Sk - 1 - kt * TK;  // last in-range row of the tile
 #pragma unroll
     for (int i = 0; i < dqk::KI; ++i)
       if (wid + i * NW < dqk::KBLK) {
@@ -617,7 +621,7 @@ __global__ __launch_bounds__(dqk::NW * 64) void attn_bwd_dq_kernel(
   // 32-key halves of tile kt this wave takes: 0, 1 or 2 (causal at 32 keys)
   auto halves = [&](int kt) -> int {
     if (kt > kt_last || !wvalid || clsw[kt] == 0) return 0;
-    return max(0, min(2, qc - 2 * kt + 1));
+    return (64 * kt <= kl_q) + (64 * kt + 32 <= kl_q);
   };
   // the four fragment blocks of tile kt into ring slot f; k steps the wave
   // does not take copy this (b, h)'s first block instead
@@ -868,27 +872,29 @@ hipError_t launch_attn_bwd_dq_recompute(const void* q, const void* k, const void
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int H,
-                                   float scale, void* dq, hipStream_t st) {
+hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int Sk,
+                                   int ratio, int H, float scale, void* dq, hipStream_t st) {
   const size_t nq = (size_t)((S + dqk::QW - 1) / dqk::QW) * B * H;
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)nq), dim3(dqk::NW * 64), 0, st, (const uint16_t*)k,
-                     (const u32x4*)dsf, cls, B, S, H, scale, (uint16_t*)dq);
+                     (const u32x4*)dsf, cls, B, S, Sk, ratio, H, scale, (uint16_t*)dq);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout,
                                      const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
-                                     int H, float scale, void* dk, void* dv, void* dsf, hipStream_t st) {
-  const size_t nkv = (size_t)((S + 127) / 128) * B * H;
+                                     int Sk, int ratio, int H, float scale, void* dk, void* dv, void* dsf,
+                                     hipStream_t st) {
+  const size_t nkv = (size_t)((Sk + 127) / 128) * B * H;
   if (dsf)
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits,
-                       cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv,
+                       cls, B, S, Sk, ratio, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv,
                        (u32x4*)dsf);
   else
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, dim3((unsigned)nkv), dim3(dkv::NW * 64), 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits,
-                       cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv, nullptr);
+                       cls, B, S, Sk, ratio, H, scale, scale * 1.4426950408889634f, (uint16_t*)dk, (uint16_t*)dv,
+                       nullptr);
   return hipGetLastError();
 }
 

@@ -57,7 +57,8 @@ hipError_t launch_attn_bwd_prep(const void* o, const void* dout, const float* ls
 // and the dS^T fragments (dsf) for the dQ kernel
 hipError_t launch_attn_bwd_dkdv_mfma(const void* q, const void* k, const void* v, const void* dout,
                                      const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
-                                     int H, float scale, void* dk, void* dv, void* dsf, hipStream_t st);
+                                     int Sk, int ratio, int H, float scale, void* dk, void* dv, void* dsf,
+                                     hipStream_t st);
 hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* v, const void* dout,
                                       const float* lse, const float* D, const uint64_t* bits, int B,
                                       int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale, bool bf16,
@@ -68,8 +69,8 @@ hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* 
 hipError_t launch_attn_bwd_dq_recompute(const void* q, const void* k, const void* v, const void* dout,
                                         const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
                                         int H, float scale, void* dq, hipStream_t st);
-hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int H,
-                                   float scale, void* dq, hipStream_t st);
+hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int Sk,
+                                   int ratio, int H, float scale, void* dq, hipStream_t st);
 hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,
                                     const void* dout, const float* lse, const float* D, const uint64_t* bits,
                                     int B, int S, int Sk, int ratio, int H, int Dqk, int Dv, float scale,
@@ -95,6 +96,11 @@ hipError_t launch_indexer_bwd(const void* q_idx, const void* k_idx, const void* 
 __host__ __device__ inline size_t dsf_tile_base(int qc) {
   const size_t m = (size_t)(qc >> 1);
   return (qc & 1) ? (m + 1) * (m + 1) : m * (m + 1);
+}
+// The same for any key axis: token keys (ratio 1) use the causal layout above;
+// compressed keys give every chunk all nkt key tiles of its (b, h).
+__host__ __device__ inline size_t dsf_base(int qc, int ratio, int nkt) {
+  return ratio == 1 ? dsf_tile_base(qc) : (size_t)qc * nkt;
 }
 
 // layout helpers shared by the host side

@@ -25,7 +25,7 @@ EXPORTS = ("dsa_index_scores", "dsa_index_scores_fp8", "dsa_quant_fp8_rows", "ds
            "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_noalloc", "dsa_sparse_attn_bwd_prep", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_bwd_dkdv", "dsa_mask_bytes", "dsa_bwd_workspace_bytes", "dsa_bwd_workspace_min_bytes",
            "dsa_indexer_teacher", "dsa_indexer_kl", "dsa_indexer_bwd",
            "dsa_csa_mask_bytes", "dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd",
-           "dsa_csa_sparse_attn_bwd",
+           "dsa_csa_sparse_attn_bwd", "dsa_csa_bwd_workspace_bytes",
            "dsa_status_string", "dsa_last_error", "dsa_version")
 
 
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         for f in ("dsa_csa_index_scores", "dsa_csa_topk", "dsa_csa_build_mask", "dsa_csa_sparse_attn_fwd",
                   "dsa_csa_sparse_attn_bwd"):
             getattr(L, f).restype = i32
+        L.dsa_csa_bwd_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+        L.dsa_csa_bwd_workspace_bytes.restype = sz
         L.dsa_csa_mask_bytes.argtypes = [i32, i32, i32]
         L.dsa_csa_mask_bytes.restype = sz
         L.dsa_mask_bytes.argtypes = [i32, i32]
@@ -144,6 +146,11 @@ def dsa_bwd_workspace_min_bytes(B: int, S: int, H: int) -> int:
 
 def dsa_csa_mask_bytes(B: int, S: int, Sk: int) -> int:
     return int(lib().dsa_csa_mask_bytes(B, S, Sk))
+
+
+def dsa_csa_bwd_workspace_bytes(B: int, S: int, Sk: int, ratio: int, H: int, Dqk: int, Dv: int,
+                                dtype=torch.bfloat16) -> int:
+    return int(lib().dsa_csa_bwd_workspace_bytes(B, S, Sk, ratio, H, Dqk, Dv, _dt(dtype)))
 
 
 def mask_views(mask: torch.Tensor, B: int, S: int, Sk: Optional[int] = None):

@@ -234,3 +234,13 @@ def test_csa_backward_rejects_before_any_launch():
     assert bwd(*args(mask=MIS)) == 1
     assert bwd(*args(wsb=need - 1)) == 3      # DSA_ERR_WORKSPACE
     assert bwd(*args(Dqk=300)) == 2
+
+
+def test_csa_backward_workspace_sizes():
+    B, S, Sk, r, H = 2, 1000, 250, 4, 3
+    base = dsa.dsa_bwd_workspace_min_bytes(B, S, H)
+    nch, nkt = (S + 31) // 32, (Sk + 63) // 64
+    assert dsa.dsa_csa_bwd_workspace_bytes(B, S, Sk, r, H, 192, 128) == base + B * H * nch * nkt * 4096
+    assert dsa.dsa_csa_bwd_workspace_bytes(B, S, Sk, r, H, 64, 64) == base                 # plain kernels
+    assert dsa.dsa_csa_bwd_workspace_bytes(B, S, S, 1, H, 192, 128) == dsa.dsa_bwd_workspace_bytes(B, S, H, 192, 128)
+    assert dsa.dsa_csa_bwd_workspace_bytes(B, S, 0, r, H, 192, 128) == 0

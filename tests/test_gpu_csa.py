@@ -252,12 +252,15 @@ def test_csa_workload_fullsize():
 
 
 # ------------------------------------------------------------------ backward
-@pytest.mark.parametrize("ratio,dims,dtype", [(4, (192, 128), "bf16"), (3, (64, 64), "fp32"),
-                                              (5, (64, 32), "bf16")])
-def test_csa_attention_bwd(ratio, dims, dtype):
+@pytest.mark.parametrize("ratio,dims,dtype,handoff", [(4, (192, 128), "bf16", True), (4, (192, 128), "bf16", False),
+                                                      (3, (192, 128), "bf16", True), (3, (64, 64), "fp32", False),
+                                                      (5, (64, 32), "bf16", False)])
+def test_csa_attention_bwd(ratio, dims, dtype, handoff):
     """dq, dk, dv of the compressed keys, element by element, on mapped random
     sets (visible entries, incomplete blocks, duplicates, past-the-end
-    entries), after the forward on the same mask."""
+    entries), after the forward on the same mask. bf16 192/128 takes the MFMA
+    kernels, with the dS handoff (workspace of dsa_csa_bwd_workspace_bytes) or
+    without it (the minimum workspace: dQ from the plain kernel)."""
     cfg = _cfg(ratio=ratio, Dqk=dims[0], Dv=dims[1], dtype=dtype, K=24, backward=True)
     x, d = _make(cfg)
     B, S, Sk, H = cfg.B, cfg.S, cfg.Sk, cfg.H
@@ -270,7 +273,9 @@ def test_csa_attention_bwd(ratio, dims, dtype):
     dq = torch.full_like(d["q"], float("nan"))
     dk = torch.full_like(d["k"], float("nan"))
     dv = torch.full_like(d["v"], float("nan"))
-    ws = torch.full((dsa.dsa_bwd_workspace_min_bytes(B, S, H),), 0x7F, dtype=torch.uint8, device=DEV)
+    nws = (dsa.dsa_csa_bwd_workspace_bytes(B, S, Sk, ratio, H, cfg.Dqk, cfg.Dv, d["q"].dtype) if handoff
+           else dsa.dsa_bwd_workspace_min_bytes(B, S, H))
+    ws = torch.full((nws,), 0x7F, dtype=torch.uint8, device=DEV)
     dsa.dsa_csa_sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, mask, ratio, cfg.softmax_scale, dq, dk,
                                 dv, ws)
     torch.cuda.synchronize()
@@ -282,3 +287,88 @@ def test_csa_attention_bwd(ratio, dims, dtype):
     check_close("dk", f64(dk), want_dk, bf16, rel)
     check_close("dv", f64(dv), want_dv, bf16, rel)
     assert np.all(f64(dq)[:, : ratio - 1] == 0)   # rows that see no entry
+
+
+def test_csa_bwd_ratio_one_is_dsa_bit_for_bit():
+    """The compressed-key backward with ratio 1 (MFMA, dS handoff) gives the
+    token-level backward's bits."""
+    cfg = inputs.CONFIGS["c2"].replace(B=2, S=333, H=3, K=64)
+    x, d = _make(cfg)
+    B, S, H, K = cfg.B, cfg.S, cfg.H, cfg.K
+    sets = torch.from_numpy(inputs.random_index_sets(B, S, K, None, seed=2)).to(DEV)
+    mask = torch.empty(dsa.dsa_mask_bytes(B, S), dtype=torch.uint8, device=DEV)
+    dsa.dsa_build_mask(sets, None, mask)
+    o = torch.empty((B, S, H, cfg.Dv), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    dsa.dsa_sparse_attn_fwd(d["q"], d["k"], d["v"], mask, cfg.softmax_scale, o, lse)
+    nws = dsa.dsa_bwd_workspace_bytes(B, S, H, cfg.Dqk, cfg.Dv)
+    assert nws == dsa.dsa_csa_bwd_workspace_bytes(B, S, S, 1, H, cfg.Dqk, cfg.Dv)
+    outs = []
+    for csa in (False, True):
+        g = [torch.empty_like(d[n]) for n in ("q", "k", "v")]
+        ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+        if csa:
+            dsa.dsa_csa_sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, mask, 1, cfg.softmax_scale, *g, ws)
+        else:
+            dsa.dsa_sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, mask, cfg.softmax_scale, *g, ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in g])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_csa_bwd_fullsize():
+    """The CSA workload's backward (MFMA, dS handoff) on the selection the
+    forward path makes: sampled dQ rows, every element of dK/dV for the last
+    64 entries of one head (only rows t >= S - 256 see them), and the sum
+    rules over all entries."""
+    cfg = inputs.CSA_CONFIGS["csa"].replace(backward=True)
+    x = inputs.make(cfg, device=DEV)
+    B, S, Sk, K, H, r = cfg.B, cfg.S, cfg.Sk, cfg.K, cfg.H, cfg.ratio
+    sc = torch.empty((B, S, Sk), dtype=torch.float32, device=DEV)
+    idx = torch.empty((B, S, K), dtype=torch.int32, device=DEV)
+    mask = torch.empty(dsa.dsa_csa_mask_bytes(B, S, Sk), dtype=torch.uint8, device=DEV)
+    o = torch.empty((B, S, H, cfg.Dv), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    dsa.dsa_csa_index_scores(x["q_idx"], x["k_idx"], x["w"], r, 0, S, sc)
+    dsa.dsa_csa_topk(sc, B, S, Sk, r, K, 0, S, idx, mask)
+    dsa.dsa_csa_sparse_attn_fwd(x["q"], x["k"], x["v"], mask, r, cfg.softmax_scale, o, lse)
+    dq, dk, dv = (torch.empty_like(x[n]) for n in ("q", "k", "v"))
+    ws = torch.empty(dsa.dsa_csa_bwd_workspace_bytes(B, S, Sk, r, H, cfg.Dqk, cfg.Dv), dtype=torch.uint8, device=DEV)
+    dsa.dsa_csa_sparse_attn_bwd(x["q"], x["k"], x["v"], o, x["dout"], lse, mask, r, cfg.softmax_scale, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    b = B - 1
+    gidx = idx[b].cpu().numpy()
+    rng = np.random.default_rng(9)
+    for t in np.unique(np.concatenate([[0, 3, 4, 2047, 2051, S - 1], rng.integers(0, S, 24)])):
+        t = int(t)
+        sel = gidx[t][gidx[t] >= 0].astype(np.int64)
+        if sel.size == 0:
+            assert np.all(f64(dq[b, t]) == 0)
+            continue
+        g = lambda n: f64(x[n][b, torch.from_numpy(sel).to(DEV)])
+        dq_t, _, _ = ref.attention_bwd_row(f64(x["q"][b, t]), g("k"), g("v"), f64(x["dout"][b, t]), cfg.softmax_scale)
+        check_close(f"dq[{b},{t}]", f64(dq[b, t]), dq_t, True, 2e-2)
+    # the last 64 entries of head h: rows t >= r * (Sk - 64) + r - 1 see them
+    h, c0 = H // 2, Sk - 64
+    rows = np.arange(r * c0 + r - 1, S)
+    sl = slice(h, h + 1)
+    want_dk = np.zeros((64, cfg.Dqk))
+    want_dv = np.zeros((64, cfg.Dv))
+    qh, doh = f64(x["q"][b, :, sl]), f64(x["dout"][b, :, sl])
+    kh, vh = f64(x["k"][b, :, sl]), f64(x["v"][b, :, sl])
+    for t in rows:
+        sel = gidx[t][gidx[t] >= 0].astype(np.int64)
+        _, dks, dvs = ref.attention_bwd_row(qh[t], kh[sel], vh[sel], doh[t], cfg.softmax_scale)
+        late = sel >= c0
+        want_dk[sel[late] - c0] += dks[late, 0]
+        want_dv[sel[late] - c0] += dvs[late, 0]
+    check_close("dk tail", f64(dk[b, c0:, h]), want_dk, True, 2e-2)
+    check_close("dv tail", f64(dv[b, c0:, h]), want_dv, True, 2e-2)
+    # sum rules: sum_c dK(c) = 0; sum_c dV(c) = sum of dO over the rows that keep an entry
+    dks = dk.float().sum(dim=1)
+    assert torch.all(dks.abs() <= 1e-2 * dk.float().abs().sum(dim=1) + 1e-3)
+    live = torch.from_numpy(np.arange(S) >= r - 1).to(DEV)
+    dvs = dv.float().sum(dim=1)
+    do = (x["dout"].float() * live[None, :, None, None]).sum(dim=1)
+    assert torch.all((dvs - do).abs() <= 1e-2 * dv.float().abs().sum(dim=1) + 1e-2)
