@@ -293,13 +293,14 @@ def long_workload(key, reps=2, attention=True):
 
 
 def csa_workload(reps=5):
-    """The compressed-key (CSA) forward path at its workload: indexer over the
-    Sk = S / ratio compressed entries, top-k and the attention forward, one
-    warm-up pass then `reps` timed passes, HIP events on the launch stream.
+    """The compressed-key (CSA) path at its workload: indexer over the
+    Sk = S / ratio compressed entries, top-k, the attention forward and its
+    backward (dS handoff route), one warm-up pass then `reps` timed passes,
+    HIP events on the launch stream.
     Useful work counts the entries visible to each row, (t + 1) // ratio."""
     import torch
     from sparse_attention_06_amd import dsa, inputs
-    cfg = inputs.CSA_CONFIGS["csa"]
+    cfg = inputs.CSA_CONFIGS["csa"].replace(backward=True)
     B, S, Sk, K, H, r = cfg.B, cfg.S, cfg.Sk, cfg.K, cfg.H, cfg.ratio
     x = inputs.make(cfg, device="cuda")
     scores = torch.empty((B, S, Sk), dtype=torch.float32, device="cuda")
@@ -307,9 +308,13 @@ def csa_workload(reps=5):
     mask = torch.empty(dsa.dsa_csa_mask_bytes(B, S, Sk), dtype=torch.uint8, device="cuda")
     o = torch.empty((B, S, H, cfg.Dv), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+    dout = x["dout"]
+    dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+    ws = torch.empty(dsa.dsa_csa_bwd_workspace_bytes(B, S, Sk, r, H, cfg.Dqk, cfg.Dv), dtype=torch.uint8,
+                     device="cuda")
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    t = {"index_scores": [], "topk": [], "attn_fwd": []}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    t = {"index_scores": [], "topk": [], "attn_fwd": [], "attn_bwd": []}
     for i in range(reps + 1):
         ev[0].record(stream)
         dsa.dsa_csa_index_scores(x["q_idx"], x["k_idx"], x["w"], r, 0, S, scores)
@@ -318,6 +323,9 @@ def csa_workload(reps=5):
         ev[2].record(stream)
         dsa.dsa_csa_sparse_attn_fwd(x["q"], x["k"], x["v"], mask, r, cfg.softmax_scale, o, lse)
         ev[3].record(stream)
+        dsa.dsa_csa_sparse_attn_bwd(x["q"], x["k"], x["v"], o, dout, lse, mask, r, cfg.softmax_scale,
+                                    dq, dk, dv, ws)
+        ev[4].record(stream)
         torch.cuda.synchronize()
         if i:
             for j, c in enumerate(t):
@@ -327,6 +335,7 @@ def csa_workload(reps=5):
     W = (Sk + 63) // 64
     flops_idx = int(nv.sum()) * cfg.Hi * 2 * cfg.Di
     flops_fwd = int(sel.sum()) * H * 2 * (cfg.Dqk + cfg.Dv)
+    flops_bwd = 2 * flops_fwd  # dP, dV, dQ, dK: 4 (Dqk + Dv) flop per kept pair and head
     topk_bytes = int(nv[nv > K].sum()) * 4 + B * S * K * 4 + B * S * W * 8
     _, cls = dsa.mask_views(mask, B, S, Sk)
     cls_np = cls.cpu().numpy()
@@ -341,15 +350,18 @@ def csa_workload(reps=5):
                      "unit": "TFLOP/s", "bound": "mfma", "algorithmic": flops_fwd,
                      "executed_tile_tflops": executed / (ms["attn_fwd"] * 1e-3) / 1e12,
                      "useful_over_executed": flops_fwd / executed},
+        "attn_bwd": {"ms": ms["attn_bwd"], "achieved": flops_bwd / (ms["attn_bwd"] * 1e-3) / 1e12,
+                     "unit": "TFLOP/s", "bound": "mfma", "algorithmic": flops_bwd,
+                     "passes": "attn_bwd_prep+attn_bwd_dkdv+attn_bwd_dq", "handoff": True},
     }
     for c, k in kern.items():
         k["frac"] = k["achieved"] / (PEAK_HBM_GBS if k["bound"] == "hbm" else PEAK_BF16_TFLOPS)
         k["ms_stats"] = stats(t[c])
     total = sum(ms.values())
-    del x, scores, idx, mask, o, lse
+    del x, scores, idx, mask, o, lse, dout, dq, dk, dv, ws
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "ratio": r, "S": S, "Sk": Sk, "K": K, "heads": H, "passes": "+".join(t),
-            "ms_per_pass": total, "useful_tflops": (flops_idx + flops_fwd) / (total * 1e-3) / 1e12,
+            "ms_per_pass": total, "useful_tflops": (flops_idx + flops_fwd + flops_bwd) / (total * 1e-3) / 1e12,
             "indexer_topk_ms": ms["index_scores"] + ms["topk"], "kernels": kern}
 
 
@@ -549,7 +561,7 @@ def main():
     ap.add_argument("--no-c1", action="store_true", help="skip the tiny workload's latency")
     ap.add_argument("--no-scrub", action="store_true", help="do not overwrite 512 MB before each timed step")
     ap.add_argument("--no-kl", action="store_true", help="skip timing the indexer KL auxiliary loss")
-    ap.add_argument("--no-csa", action="store_true", help="skip the compressed-key (CSA) forward workload")
+    ap.add_argument("--no-csa", action="store_true", help="skip the compressed-key (CSA) workload")
     ap.add_argument("--long-only", action="store_true",
                     help="only the 32K and 128K workloads (one JSON line)")
     ap.add_argument("--copy-mib", type=int, default=0,

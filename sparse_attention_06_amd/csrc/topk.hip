@@ -28,6 +28,8 @@
 // are taken, lowest positions first. |valid| <= K takes every valid key; a
 // causal-only row with L <= K never reads its scores. Each kernel emits the
 // ascending index list and the row's u64 mask words together.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -378,7 +380,7 @@ template <int NW> __device__ __forceinline__ void block_minmax_u(uint32_t& mn, u
 // Largest bin b of hist[0..kNB) with count(bins >= b) >= need, for NT threads;
 // writes b and count(bins > b). Needs count(all bins) >= need >= 1.
 template <int NT>
-__device__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t& found_bin,
+__device__ __forceinline__ void find_bin_n(const uint32_t* hist, uint32_t need, uint32_t* red, uint32_t& found_bin,
                            uint32_t& found_above, uint32_t* total = nullptr) {
   constexpr int PER = kNB / NT, NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -683,8 +685,8 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
 // A strided sample of the row (32 runs of 64 consecutive keys) gives a lower
 // bound lo on the threshold, chosen so that about 2K of the row's keys are at
 // or above it. One pass over the row (16-byte loads, every score read once)
-// lists each valid key >= lo as (position << 11 | bin), with a 2048-bin
-// histogram over [lo, sampled max]; every other key costs two compares. Any
+// lists each key >= lo; every other key costs one compare. A 2048-bin
+// histogram over [lo, sampled max] is then built from the list. Any
 // lo for which at least K keys are listed gives the exact result: every key
 // in a bin above the K-th largest's bin is listed, and so are the largest
 // keys of that bin. The K-th largest key T is then found by ranking the
@@ -694,11 +696,12 @@ __global__ __launch_bounds__(64 * NW) void topk_long_kernel(const ST* __restrict
 // thread. A row whose list comes out short, or longer than the LDS list
 // holds, is finished by the multi-pass selection in the same workgroup.
 //
-// In the pass, each lane holds kSU 16-byte blocks per stage in VGPRs, with the
-// next two stages in flight. Each wave lists into its own region of the list,
-// at slots from a wave-wide prefix of the lanes' counts: no atomics on the
+// In the pass, each lane reads kSU 16-byte blocks per stage, with the next
+// stage in flight (two register buffers in turn). Each wave lists into its own region of
+// the list, at slots from the ballot of each score slot: no atomics on the
 // list, and no waits inside the pass.
-constexpr int kStash = 6144;     // listed keys
+constexpr int kStash = 6656;     // list slots (kStash / NW per wave)
+constexpr int kStashUse = 6144;  // listed keys a row can rely on: kStash minus 64 per wave of 8
 constexpr int kChunks = 32;      // sample: runs of 64 consecutive keys
 constexpr int kSB = 256;         // sample histogram bins
 constexpr int kSU = 2;           // 16-byte blocks per lane and stage (two stages in flight)
@@ -734,11 +737,10 @@ static size_t stash_lds_bytes(int nw_max, bool seg) {
   return stash_list_bytes(nw_max) + (seg ? (size_t)nw_max * 8 : 0);
 }
 
-// fp32 rows without segments are held to 64 VGPRs, so that four workgroups
-// (eight waves per SIMD) share a CU: 10% faster at 32K. The bf16 and
-// segment-aware instances gain nothing or spill at that budget.
+// Held to 64 VGPRs, so that four workgroups (eight waves per SIMD) share a
+// CU. Only the multi-pass fallback, an out-of-line call, spills at that budget.
 template <typename ST, bool SEG>
-constexpr int stash_waves_per_simd() { return (sizeof(ST) == 4 && !SEG) ? 8 : 1; }
+constexpr int stash_waves_per_simd() { return 8; }
 
 template <typename ST, bool SEG, int NW>
 __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void topk_stash_kernel(const ST* __restrict__ scores, int64_t ld,
@@ -812,16 +814,18 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
   // derived from the row pointer, so the loads stay global (flat loads would
   // also count against the LDS wait counter)
   const u32x4* blk = (const u32x4*)((const char*)row - (rs - ra));
-  auto load_stage = [&](int i0, u32x4 (&v)[kSU]) {
+  // Stage st reads blocks [st * kSU * NT, (st + 1) * kSU * NT): wave w takes
+  // block (st * kSU + u) * NT + 64 * w + lane, u < kSU. A score's index in
+  // its wave's own sequence, ((st * kSU + u) * 64 + lane) * EPB + e, stays
+  // below 2^16. Loads past the row re-read its last block.
+  const int nstage = (nblk + kSU * NT - 1) / (kSU * NT);
+  auto load_stage = [&](int st, u32x4 (&v)[kSU]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kSU; ++u) {
-      const int i = i0 + u * NT;
-      if (i < nblk) v[u] = blk[i];
-    }
+    for (int u = 0; u < kSU; ++u) v[u] = blk[min((st * kSU + u) * NT + tid, nblk - 1)];
   };
   float sx[CPW];
   bool sv[CPW];
-  u32x4 vcur[kSU], vnxt[kSU];  // stages st + 1 and st + 2 while stage st is scanned
+  u32x4 vb0[kSU], vb1[kSU];  // stages st and st + 1 (two in turn)
   if (!take_all) {
     // sample: run c starts at c * (L - 64) / (kChunks - 1)
 #pragma unroll
@@ -831,8 +835,7 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
       sv[j] = valid_pos(p);
       sx[j] = sv[j] ? ScoreLoad<ST>::get(row, p) : 0.f;
     }
-    load_stage(tid, vcur);
-    load_stage(tid + kSU * NT, vnxt);
+    load_stage(0, vb0);
   }
 
   bool fail = false;
@@ -867,6 +870,11 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
       mx = fmaxf(mx, sh.red_f[NW + i]);
       nvs += sh.samp_n[i];
     }
+    // the same in every lane (read from LDS): readfirstlane keeps them, the
+    // branches on them and the pass's list counts in scalar registers
+    mn = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mn)));
+    mx = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mx)));
+    nvs = __builtin_amdgcn_readfirstlane(nvs);
     float lo = mn;
     if (nvs < 64) {
       fail = true;  // uniform: too few valid keys sampled
@@ -900,84 +908,105 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
         }
       }
       __syncthreads();
-      lo = mn + (float)sh.found_bin / inv_s;
+      lo = mn + (float)__builtin_amdgcn_readfirstlane(sh.found_bin) / inv_s;
     }
     if (!fail) {
       // bins: fp32 scores, linear in the value over [lo, max]; bf16 scores,
       // one bin per value from the largest bf16 value below lo (exact while
       // the listed values span fewer than 2047 of them)
-      const float inv = mx > lo ? (float)kNB / (mx - lo) : 1e30f;
+      // The pass lists this wave's scores >= lo in its region of the list.
+      // An entry is (position << 11) | bin for fp32 scores; for bf16 it is the
+      // score's 16-bit key in the high half (its raw bits when lo > 0, since
+      // then every listed score is positive) and its index in the wave's own
+      // sequence in the low half. Per score slot: one compare, whose ballot is
+      // the slot's listing mask, a lane prefix from mbcnt, and the entry.
+      // Bins, segment validity and the histogram are taken afterwards from the
+      // list, so their cost follows the list, not the row. A row whose wave
+      // listed more than its region holds less 64 is finished by the
+      // multi-pass selection.
+      const bool posk = sizeof(ST) == 2 && lo > 0.f;
+      const float inv = mx > lo ? fminf((float)kNB / (mx - lo), 1e30f) : 1.f;
       const uint32_t klo16 = bkey16(__float_as_uint(lo) >> 16);
       const uint32_t kb16 = klo16 > 0 ? klo16 - 1 : 0;
-      auto bin_of = [&](float x) -> int {
-        if constexpr (sizeof(ST) == 2) return (int)min(bkey16(__float_as_uint(x) >> 16) - kb16, (uint32_t)(kNB - 1));
-        else return (int)fminf(fmaxf((x - lo) * inv, 0.f), (float)(kNB - 1));
-      };
-      // the pass: list this wave's valid scores >= lo in its region of the list
-      uint32_t* wst = stash + wid * kCapW;
-      uint32_t listed = 0;  // this wave's slots so far (uniform)
-      const int nstage = (nblk + kSU * NT - 1) / (kSU * NT);
-      for (int st = 0; st < nstage; ++st) {
-        const int i0 = tid + st * kSU * NT;
-        u32x4 v[kSU];
+      uint32_t listed = 0;  // this wave's listed scores so far (uniform)
+      static_assert(kSU == 2, "the stage scan takes two blocks per lane");
+      auto scan = [&](auto chk, auto pos, int st, u32x4 v0, u32x4 v1) __attribute__((always_inline)) {
+        constexpr bool CHK = decltype(chk)::value, POS = decltype(pos)::value;
 #pragma unroll
         for (int u = 0; u < kSU; ++u) {
-          v[u] = vcur[u];
-          vcur[u] = vnxt[u];
-        }
-        load_stage(i0 + 2 * kSU * NT, vnxt);  // two stages ahead
-        uint32_t msk = 0;  // bit u * EPB + e: score e of block u is listed
-#pragma unroll
-        for (int u = 0; u < kSU; ++u) {
-          const int i = i0 + u * NT;
-          const uint32_t pb = (uint32_t)(p_ra + i * EPB);
+          const u32x4 vu = u ? v1 : v0;
+          const uint32_t r = (uint32_t)(((st * kSU + u) * 64 + lane) * EPB);  // index in the wave's sequence
+          const int pb = p_ra + ((st * kSU + u) * NT + tid) * EPB;             // position of the block
+          const uint32_t pr11 = (uint32_t)pb << 11;
 #pragma unroll
           for (int e = 0; e < EPB; ++e) {
-            float x;
-            if constexpr (sizeof(ST) == 4) x = __uint_as_float(v[u][e]);
-            else x = __uint_as_float((e & 1) ? (v[u][e >> 1] & 0xffff0000u) : (v[u][e >> 1] << 16));
-            if (i < nblk && pb + e < (uint32_t)L && x >= lo) msk |= 1u << (u * EPB + e);
-          }
-        }
-        const uint32_t cnt = __popc(msk);
-        const uint32_t incl = wave_incl_scan(cnt);
-        uint32_t slot = listed + incl - cnt;
-        // the listed scores, in a static walk over the stage (each write is
-        // masked to the lanes that list that score)
-#pragma unroll
-        for (int u = 0; u < kSU; ++u) {
-#pragma unroll
-          for (int e = 0; e < EPB; ++e) {
-            if ((msk >> (u * EPB + e)) & 1u) {
-              float x;
-              if constexpr (sizeof(ST) == 4) x = __uint_as_float(v[u][e]);
-              else x = __uint_as_float((e & 1) ? (v[u][e >> 1] & 0xffff0000u) : (v[u][e >> 1] << 16));
-              const int p = p_ra + (i0 + u * NT) * EPB + e;
-              uint32_t ent = kHole;
-              if (valid_pos(p)) {
-                const int bn = bin_of(x);
-                atomicAdd(&sh.hist[bn], 1u);
-                ent = ((uint32_t)p << 11) | (uint32_t)bn;
-              }
-              if (slot < (uint32_t)kCapW) wst[slot] = ent;
-              ++slot;
+            uint32_t xb;  // the score's bits as a float (bf16 in the high half)
+            if constexpr (sizeof(ST) == 4) xb = vu[e];
+            else xb = (e & 1) ? (vu[e >> 1] & 0xffff0000u) : (vu[e >> 1] << 16);
+            const float x = __uint_as_float(xb);
+            bool c = x >= lo;
+            if constexpr (CHK) c = c && (uint32_t)(pb + e) < (uint32_t)L;
+            const uint64_t m = __ballot(c);
+            uint32_t ent;
+            if constexpr (sizeof(ST) == 4) {
+              ent = pr11 + ((uint32_t)e << 11) +
+                    (uint32_t)__builtin_amdgcn_fmed3f((x - lo) * inv, 0.f, (float)(kNB - 1));
+            } else {
+              uint32_t xk = xb;  // POS: the bits are the key (sign bit clear)
+              if constexpr (!POS) xk = x < 0.f ? (xb ^ 0xffff0000u) : (xb | 0x80000000u);  // -0 as +0
+              ent = xk + r + (uint32_t)e;
             }
+            // past kCapW - 64 listed keys the slots repeat the region's last
+            // 64; such a wave sends its row to the multi-pass selection
+            const uint32_t base = wid * kCapW + min(listed, (uint32_t)(kCapW - 64));
+            if (c) stash[base + lanes_below(m)] = ent;
+            listed = __builtin_amdgcn_readfirstlane(listed + popc64(m));  // uniform: keep it scalar
           }
         }
-        listed += __builtin_amdgcn_readlane(incl, 63);
-      }
+      };
+      auto scan_stage = [&](auto pos, int st, u32x4 v0, u32x4 v1) __attribute__((always_inline)) {
+        if (st >= nstage) return;  // wave-uniform
+        const int pa = p_ra + st * kSU * NT * EPB;  // the stage's first position
+        if (pa < 0 || pa + kSU * NT * EPB > L) scan(std::true_type{}, pos, st, v0, v1);
+        else scan(std::false_type{}, pos, st, v0, v1);
+      };
+      // loads one stage ahead; past the last stage they re-read the last block
+      auto pass = [&](auto pos) __attribute__((always_inline)) {
+        for (int st = 0; st < nstage; st += 2) {
+          load_stage(st + 1, vb1);
+          scan_stage(pos, st, vb0[0], vb0[1]);
+          load_stage(st + 2, vb0);
+          scan_stage(pos, st + 1, vb1[0], vb1[1]);
+        }
+      };
+      if (posk) pass(std::true_type{});
+      else pass(std::false_type{});
       if (lane == 0) sh.wave_g[wid] = listed;
-      __syncthreads();  // the list and its histogram are complete
+      __syncthreads();  // the list is complete
       bool over = false;
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) over |= sh.wave_g[w2] > (uint32_t)kCapW;
-      // this thread's list slots j = tid + NT * q (slot j % kCapW of wave j / kCapW)
+      for (int w2 = 0; w2 < NW; ++w2) over |= sh.wave_g[w2] > (uint32_t)(kCapW - 64);
+      // this thread's list slots j = tid + NT * q (slot j % kCapW of wave j / kCapW),
+      // as (position << 11) | bin; keys of other segments become holes, the
+      // rest count into the histogram. bf16 bins: bkey16 of the score minus
+      // kb16, one bin per bf16 value.
       uint32_t ent[kSPT];
 #pragma unroll
       for (int q = 0; q < kSPT; ++q) {
-        const int j = tid + NT * q;
-        ent[q] = !over && (uint32_t)(j % kCapW) < sh.wave_g[j / kCapW] ? stash[j] : kHole;
+        const int j = tid + NT * q, wq = j / kCapW;
+        ent[q] = !over && (uint32_t)(j % kCapW) < sh.wave_g[wq] ? stash[j] : kHole;
+        if (ent[q] != kHole) {
+          if constexpr (sizeof(ST) == 2) {
+            const uint32_t k16 = posk ? (ent[q] >> 16) | 0x8000u : ent[q] >> 16;
+            const uint32_t r = ent[q] & 0xffffu, g = r / EPB;  // (st * kSU + u) * 64 + lane
+            const uint32_t pq = (uint32_t)(p_ra + (int)(((g >> 6) * NT + wq * 64 + (g & 63)) * EPB + r % EPB));
+            ent[q] = (pq << 11) | min(k16 - kb16, (uint32_t)(kNB - 1));
+          }
+          if (SEG && !valid_pos((int)(ent[q] >> 11))) ent[q] = kHole;
+          else atomicAdd(&sh.hist[ent[q] & (kNB - 1)], 1u);
+        }
       }
+      __syncthreads();  // the histogram is complete
       uint32_t nst = 0;  // valid listed keys: the histogram's total
       find_bin_n<NT>(sh.hist, (uint32_t)K, sh.red_u, sh.found_bin, sh.found_above, &nst);
       if (over || nst < (uint32_t)K) {
@@ -1184,7 +1213,7 @@ template <typename ST, bool SEG>
 static hipError_t launch_long_rows(const ST* scores, int64_t ld, const int32_t* seg, int B, int S, int Sk, int ratio,
                                    int K, int row0, int nrows, int rbeg, int rcount, int32_t* idx, uint64_t* bits,
                                    hipStream_t st) {
-  if (2 * K > kStash)  // the listed keys could not hold the selection: multi-pass only
+  if (2 * K > kStashUse)  // the listed keys could not hold the selection: multi-pass only
     return launch_multipass<ST, SEG, 16>(scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, rbeg, rcount, idx, bits,
                                          st);
   return launch_stash<ST, SEG, 8>(scores, ld, seg, B, S, Sk, ratio, K, row0, nrows, rbeg, rcount, idx, bits, st);

@@ -91,7 +91,8 @@ CONFIGS = {
 
 # Compressed sparse attention (DeepSeek-V4 CSA, compression ratio 4) on the 2B
 # shape: 1024 compressed entries per row of 4096 tokens; top-k scaled by the
-# ratio (2048 / 4). Forward only. Not one of the five metric workloads.
+# ratio (2048 / 4). Forward by default (`.replace(backward=True)` adds dO).
+# Not one of the five metric workloads.
 CSA_CONFIGS = {
     "csa": Config("csa_r4_b12_s4k", 12, 4096, 64, 128, 512, 16, 192, 128, "bf16", True, ratio=4),
 }
