@@ -220,6 +220,38 @@ def test_topk_long_rows(score_dtype, segments, K):
         assert np.array_equal(bits[:, row0:row0 + n].cpu().numpy(), wb), row0
 
 
+@pytest.mark.parametrize("score_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", ["shifted", "median"])
+def test_topk_long_rows_threshold_at_or_below_zero(score_dtype, case):
+    """Rows longer than 4096 keys whose K-th largest score is negative or
+    zero, so the single-read kernel lists keys of both signs (for bf16 the
+    entries then carry the signed order key): "shifted" scores N(0,1) - 3 with
+    K = 300, "median" scores rounded to 1/16 with signed zeros and K = 2048,
+    about half of a row just past 4096 keys, so ties and -0 / +0 sit at the
+    threshold. Bit-exact index lists and mask rows."""
+    B, S = 2, 8192
+    K = 300 if case == "shifted" else 2048
+    idx = torch.full((B, S, K), -7, dtype=torch.int32, device=DEV)
+    mask = torch.zeros(dsa.dsa_mask_bytes(B, S), dtype=torch.uint8, device=DEV)
+    bits, _ = dsa.mask_views(mask, B, S)
+    for i, (row0, n) in enumerate([(4096, 256), (8064, 128)]):
+        g = torch.Generator().manual_seed(500 + i)
+        v = torch.randn((B, n, S), generator=g)
+        if case == "shifted":
+            v -= 3.0
+        else:
+            v = torch.round(v * 16) / 16
+            v[torch.rand((B, n, S), generator=g) < 0.05] = -0.0
+        sc = v.to(score_dtype)
+        dsa.dsa_topk(sc.to(DEV).contiguous(), None, B, S, K, row0, n, idx, mask)
+        torch.cuda.synchronize()
+        want = ref.topk(sc.double().numpy(), None, np.arange(row0, row0 + n), K, S)
+        got = idx[:, row0:row0 + n].cpu().numpy()
+        assert np.array_equal(got, want), row0
+        wb = ref.pack_bits(ref.selection_matrix(want, S)).view(np.int64)
+        assert np.array_equal(bits[:, row0:row0 + n].cpu().numpy(), wb), row0
+
+
 # --------------------------------------------------------------- attention
 def _sets(cfg, x):
     return inputs.random_index_sets(cfg.B, cfg.S, cfg.K, _seg_np(x), seed=cfg.seed + 1)
