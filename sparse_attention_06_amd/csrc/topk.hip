@@ -986,24 +986,32 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
       bool over = false;
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) over |= sh.wave_g[w2] > (uint32_t)(kCapW - 64);
-      // this thread's list slots j = tid + NT * q (slot j % kCapW of wave j / kCapW),
-      // as (position << 11) | bin; keys of other segments become holes, the
-      // rest count into the histogram. bf16 bins: bkey16 of the score minus
-      // kb16, one bin per bf16 value.
+      // Each wave takes its own region back: slot lane + 64 * q of it, up to
+      // its own count (listed, still in a scalar register), as (position <<
+      // 11) | bin; keys of other segments become holes, the rest count into
+      // the histogram. bf16 bins: bkey16 of the score minus kb16, one bin per
+      // bf16 value.
+      static_assert(kSPT * 64 == kCapW, "a wave's region is kSPT slots per lane");
       uint32_t ent[kSPT];
 #pragma unroll
       for (int q = 0; q < kSPT; ++q) {
-        const int j = tid + NT * q, wq = j / kCapW;
-        ent[q] = !over && (uint32_t)(j % kCapW) < sh.wave_g[wq] ? stash[j] : kHole;
-        if (ent[q] != kHole) {
+        ent[q] = kHole;
+        if (over || (uint32_t)(64 * q) >= listed) continue;  // uniform
+        const uint32_t jr = (uint32_t)(lane + 64 * q);
+        if (jr < listed) {
+          uint32_t e = stash[wid * kCapW + jr];
           if constexpr (sizeof(ST) == 2) {
-            const uint32_t k16 = posk ? (ent[q] >> 16) | 0x8000u : ent[q] >> 16;
-            const uint32_t r = ent[q] & 0xffffu, g = r / EPB;  // (st * kSU + u) * 64 + lane
-            const uint32_t pq = (uint32_t)(p_ra + (int)(((g >> 6) * NT + wq * 64 + (g & 63)) * EPB + r % EPB));
-            ent[q] = (pq << 11) | min(k16 - kb16, (uint32_t)(kNB - 1));
+            const uint32_t k16 = posk ? (e >> 16) | 0x8000u : e >> 16;
+            const uint32_t r = e & 0xffffu, g = r / EPB;  // (st * kSU + u) * 64 + lane
+            const uint32_t pq = (uint32_t)(p_ra + (int)(((g >> 6) * NT + wid * 64 + (g & 63)) * EPB + r % EPB));
+            e = (pq << 11) | min(k16 - kb16, (uint32_t)(kNB - 1));
           }
-          if (SEG && !valid_pos((int)(ent[q] >> 11))) ent[q] = kHole;
-          else atomicAdd(&sh.hist[ent[q] & (kNB - 1)], 1u);
+          if (SEG && !valid_pos((int)(e >> 11))) {
+            e = kHole;
+          } else {
+            atomicAdd(&sh.hist[e & (kNB - 1)], 1u);
+          }
+          ent[q] = e;
         }
       }
       __syncthreads();  // the histogram is complete
@@ -1016,10 +1024,11 @@ __global__ __launch_bounds__(64 * NW, (stash_waves_per_simd<ST, SEG>())) void to
         // the mask takes over the list's LDS
         for (int w = tid; w < nw; w += NT) selw[w] = 0ull;
         __syncthreads();
-        const uint32_t bstar = sh.found_bin;
-        const uint32_t need = (uint32_t)K - sh.found_above;
+        const uint32_t bstar = __builtin_amdgcn_readfirstlane(sh.found_bin);
+        const uint32_t need = (uint32_t)K - __builtin_amdgcn_readfirstlane(sh.found_above);
 #pragma unroll
         for (int q = 0; q < kSPT; ++q) {
+          if ((uint32_t)(64 * q) >= listed) continue;  // uniform: past the wave's listed keys
           if (ent[q] == kHole) continue;
           const uint32_t bn = ent[q] & (kNB - 1), p = ent[q] >> 11;
           if (bn == bstar) {
