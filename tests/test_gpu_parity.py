@@ -252,6 +252,27 @@ def test_topk_long_rows_threshold_at_or_below_zero(score_dtype, case):
         assert np.array_equal(bits[:, row0:row0 + n].cpu().numpy(), wb), row0
 
 
+@pytest.mark.parametrize("score_dtype,S", [(torch.float32, 5003), (torch.bfloat16, 5005)])
+def test_topk_long_rows_unaligned(score_dtype, S):
+    """Rows longer than 4096 keys whose starts are not 16-byte aligned (a
+    row of S scores is not a whole number of 16-byte blocks), so the
+    single-read kernel's first and last stages hold positions outside the
+    row: bit-exact index lists and mask rows against the oracle."""
+    B, K = 2, 700
+    idx = torch.full((B, S, K), -7, dtype=torch.int32, device=DEV)
+    mask = torch.zeros(dsa.dsa_mask_bytes(B, S), dtype=torch.uint8, device=DEV)
+    bits, _ = dsa.mask_views(mask, B, S)
+    for i, (row0, n) in enumerate([(4096, 128), (4992, S - 4992)]):
+        sc = _long_rows(B, n, S, row0, score_dtype, seed=700 + i)
+        dsa.dsa_topk(sc.to(DEV).contiguous(), None, B, S, K, row0, n, idx, mask)
+        torch.cuda.synchronize()
+        want = ref.topk(sc.double().numpy(), None, np.arange(row0, row0 + n), K, S)
+        got = idx[:, row0:row0 + n].cpu().numpy()
+        assert np.array_equal(got, want), row0
+        wb = ref.pack_bits(ref.selection_matrix(want, S)).view(np.int64)
+        assert np.array_equal(bits[:, row0:row0 + n].cpu().numpy(), wb), row0
+
+
 # --------------------------------------------------------------- attention
 def _sets(cfg, x):
     return inputs.random_index_sets(cfg.B, cfg.S, cfg.K, _seg_np(x), seed=cfg.seed + 1)
