@@ -259,7 +259,8 @@ dsa_status dsa_sparse_attn_fwd(const void* q, const void* k, const void* v, cons
  * key-major and query-major kernels: MFMA for bf16 192/128, with the dS handoff
  * when workspace_bytes >= dsa_csa_bwd_workspace_bytes(...) (each 32-query chunk
  * then holds all ceil(Sk/64) key tiles, 4 KB each, per (b, h); capped like the
- * token-level one), plain kernels otherwise (any dims up to 256, bf16 or fp32).
+ * token-level one) and otherwise a dQ kernel that recomputes dS (the same
+ * bits); plain kernels for other dims (up to 256) and for fp32.
  * The token-level backward calls take ratio-1 masks only.
  * ------------------------------------------------------------------------- */
 size_t dsa_csa_mask_bytes(int B, int S, int Sk);

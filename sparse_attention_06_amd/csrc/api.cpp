@@ -459,8 +459,8 @@ dsa_status dsa_sparse_attn_bwd_dq(const void* q, const void* k, const void* v, c
                                                    cls_of(m, B, S), B, S, S, 1, H, softmax_scale, dq, st),
                       "dsa_sparse_attn_bwd_dq");
   if (attn_mfma(Dqk, Dv, dtype))
-    return hip_status(dsa::launch_attn_bwd_dq_recompute(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, H,
-                                                        softmax_scale, dq, st),
+    return hip_status(dsa::launch_attn_bwd_dq_recompute(q, k, v, dout, ws, bits_of(m), cls_of(m, B, S), B, S, S,
+                                                        1, H, softmax_scale, dq, st),
                       "dsa_sparse_attn_bwd_dq");
   return hip_status(dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits_of(m), B, S, S, 1, H, Dqk, Dv,
                                                   softmax_scale, dtype == DSA_BF16, dq, st),
@@ -521,7 +521,7 @@ dsa_status dsa_csa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
   hipError_t e = dsa::launch_attn_bwd_prep(o, dout, lse, B, S, H, Dv, bf16, ws, st);
   if (attn_mfma(Dqk, Dv, dtype)) {
     // the MFMA key-major kernel, handing dS to the MFMA dQ kernel when the
-    // workspace holds it (else dQ takes the plain kernel)
+    // workspace holds it (else the MFMA dQ kernel that recomputes dS)
     const bool handoff = workspace_bytes >= bwd_frag_offset(B, S, H) + csa_handoff_bytes(B, S, Sk, H, ratio);
     void* dsf = handoff ? (void*)((char*)workspace + bwd_frag_offset(B, S, H)) : nullptr;
     if (e == hipSuccess)
@@ -529,8 +529,8 @@ dsa_status dsa_csa_sparse_attn_bwd(const void* q, const void* k, const void* v, 
                                          softmax_scale, dk, dv, dsf, st);
     if (e == hipSuccess)
       e = handoff ? dsa::launch_attn_bwd_dq_mfma(k, dsf, cls_of(m, B, S, Sk), B, S, Sk, ratio, H, softmax_scale, dq, st)
-                  : dsa::launch_attn_bwd_dq_plain(q, k, v, dout, lse, ws, bits, B, S, Sk, ratio, H, Dqk, Dv,
-                                                  softmax_scale, bf16, dq, st);
+                  : dsa::launch_attn_bwd_dq_recompute(q, k, v, dout, ws, bits, cls_of(m, B, S, Sk), B, S, Sk, ratio,
+                                                      H, softmax_scale, dq, st);
     return hip_status(e, "dsa_csa_sparse_attn_bwd");
   }
   if (e == hipSuccess)

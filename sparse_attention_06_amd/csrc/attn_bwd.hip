@@ -709,7 +709,7 @@ static_assert(bwd::TK * KSL % 64 == 0 && bwd::TK * VSL % 64 == 0, "tiles must be
 __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ ws, const uint64_t* __restrict__ bits,
-    const uint8_t* __restrict__ cls, int B, int S, int H, float scale, float scale_log2,
+    const uint8_t* __restrict__ cls, int B, int S, int Sk, int ratio, int H, float scale, float scale_log2,
     uint16_t* __restrict__ dq) {
   using namespace bwd;
   using dqr::NW;
@@ -721,7 +721,7 @@ __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so per-wave data is scalar
   const int half = lane >> 5, col = lane & 31;
-  const int W = (S + 63) / 64, NQ = (S + 127) / 128, NK = W;
+  const int W = (Sk + 63) / 64, NQ = (S + 127) / 128, NK = W;
   const int NQW = (S + QW - 1) / QW;
   int bh, qw;
   grouped_order(xcd_remap((int)blockIdx.x, (int)gridDim.x), NQW, B * H, bh, qw);
@@ -731,8 +731,8 @@ __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
   const int qt_w = min(NQ - 1, (qw * QW + wid * 32) / 128);
   const int qt0 = qw * QW / 128, qt1 = min(NQ - 1, qt0 + 1);
   const size_t rs_qk = (size_t)H * DQK, rs_v = (size_t)H * DV;
-  const uint16_t* kbase = k + (size_t)b * S * rs_qk + (size_t)h * DQK;
-  const uint16_t* vbase = v + (size_t)b * S * rs_v + (size_t)h * DV;
+  const uint16_t* kbase = k + (size_t)b * Sk * rs_qk + (size_t)h * DQK;
+  const uint16_t* vbase = v + (size_t)b * Sk * rs_v + (size_t)h * DV;
 
   u32x4 qf[DQK / 16], of[DV / 16];
 #pragma unroll
@@ -758,7 +758,10 @@ __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
 #pragma unroll
     for (int j = 0; j < 16; ++j) dqacc[i][j] = 0.f;
 
-  const int kt_last = min(S - 1, qw * QW + QW - 1) / TK;
+  // last key tile any of the workgroup's queries sees (-1: none); key s is
+  // visible to query t when ratio * s + ratio - 1 <= t
+  const int kl_last = (min(S - 1, qw * QW + QW - 1) + 1) / ratio - 1;
+  const int kt_last = kl_last < 0 ? -1 : kl_last / TK;
   stage_bytes(scls[0], cls + ((size_t)b * NQ + qt0) * NK, kt_last + 1);
   stage_bytes(scls[1], cls + ((size_t)b * NQ + qt1) * NK, kt_last + 1);
   const uint8_t* cls0 = scls[0];
@@ -771,14 +774,14 @@ __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
     return n;
   };
   // this wave's 1 KB blocks of a tile; pad slots copy a harmless chunk and rows
-  // past S copy row S-1
+  // past the last key copy row Sk-1
   auto issue = [&](int kt, int buf) {
 #pragma unroll
     for (int i = 0; i < dqr::KI; ++i) {
       const int j = wid + i * NW;
       if (j < dqr::KBLK) {
         const int slot = j * 64 + lane, row = slot / dqr::KSL, c = min(slot % dqr::KSL, dqr::KSL - 2);
-        const int s = min(kt * TK + row, S - 1);
+        const int s = min(kt * TK + row, Sk - 1);
         g2lds16(kbase + (size_t)s * rs_qk + c * 8, (char*)smK[buf] + j * 1024);
       }
     }
@@ -787,7 +790,7 @@ __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
       const int j = wid + i * NW;
       if (j < dqr::VBLK) {
         const int slot = j * 64 + lane, row = slot / dqr::VSL, c = min(slot % dqr::VSL, dqr::VSL - 2);
-        const int s = min(kt * TK + row, S - 1);
+        const int s = min(kt * TK + row, Sk - 1);
         g2lds16(vbase + (size_t)s * rs_v + c * 8, (char*)smV[buf] + j * 1024);
       }
     }
@@ -864,11 +867,11 @@ __global__ __launch_bounds__(dqr::NW * 64) void attn_bwd_dq_recompute_kernel(
 
 hipError_t launch_attn_bwd_dq_recompute(const void* q, const void* k, const void* v, const void* dout,
                                         const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
-                                        int H, float scale, void* dq, hipStream_t st) {
+                                        int Sk, int ratio, int H, float scale, void* dq, hipStream_t st) {
   const size_t nq = (size_t)((S + dqr::QW - 1) / dqr::QW) * B * H;
   hipLaunchKernelGGL(attn_bwd_dq_recompute_kernel, dim3((unsigned)nq), dim3(dqr::NW * 64), 0, st,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, ws, bits,
-                     cls, B, S, H, scale, scale * 1.4426950408889634f, (uint16_t*)dq);
+                     cls, B, S, Sk, ratio, H, scale, scale * 1.4426950408889634f, (uint16_t*)dq);
   return hipGetLastError();
 }
 

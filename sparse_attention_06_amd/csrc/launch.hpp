@@ -68,7 +68,7 @@ hipError_t launch_attn_bwd_dkdv_plain(const void* q, const void* k, const void* 
 // and the workspace's D and base-2 LSE (key-major kernel given dsf = nullptr)
 hipError_t launch_attn_bwd_dq_recompute(const void* q, const void* k, const void* v, const void* dout,
                                         const float* ws, const uint64_t* bits, const uint8_t* cls, int B, int S,
-                                        int H, float scale, void* dq, hipStream_t st);
+                                        int Sk, int ratio, int H, float scale, void* dq, hipStream_t st);
 hipError_t launch_attn_bwd_dq_mfma(const void* k, const void* dsf, const uint8_t* cls, int B, int S, int Sk,
                                    int ratio, int H, float scale, void* dq, hipStream_t st);
 hipError_t launch_attn_bwd_dq_plain(const void* q, const void* k, const void* v,

@@ -260,7 +260,8 @@ def test_csa_attention_bwd(ratio, dims, dtype, handoff):
     sets (visible entries, incomplete blocks, duplicates, past-the-end
     entries), after the forward on the same mask. bf16 192/128 takes the MFMA
     kernels, with the dS handoff (workspace of dsa_csa_bwd_workspace_bytes) or
-    without it (the minimum workspace: dQ from the plain kernel)."""
+    without it (the minimum workspace: dQ from the MFMA kernel that recomputes
+    dS)."""
     cfg = _cfg(ratio=ratio, Dqk=dims[0], Dv=dims[1], dtype=dtype, K=24, backward=True)
     x, d = _make(cfg)
     B, S, Sk, H = cfg.B, cfg.S, cfg.Sk, cfg.H
@@ -287,6 +288,33 @@ def test_csa_attention_bwd(ratio, dims, dtype, handoff):
     check_close("dk", f64(dk), want_dk, bf16, rel)
     check_close("dv", f64(dv), want_dv, bf16, rel)
     assert np.all(f64(dq)[:, : ratio - 1] == 0)   # rows that see no entry
+
+
+@pytest.mark.parametrize("ratio,S", [(4, 333), (3, 700)])
+def test_csa_bwd_recompute_route_matches_handoff(ratio, S):
+    """Over compressed keys the two dQ routes of the MFMA backward (dS handed
+    over by the key-major kernel, or recomputed by the query-major one) give
+    the same bits, and dK/dV do not depend on the route."""
+    cfg = _cfg(ratio=ratio, S=S, K=40, backward=True)
+    x, d = _make(cfg)
+    B, Sk, H = cfg.B, cfg.Sk, cfg.H
+    sets = _entry_sets(cfg)
+    mask = torch.empty(dsa.dsa_csa_mask_bytes(B, S, Sk), dtype=torch.uint8, device=DEV)
+    dsa.dsa_csa_build_mask(torch.from_numpy(sets).to(DEV), Sk, ratio, mask)
+    o = torch.empty((B, S, H, cfg.Dv), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=DEV)
+    dsa.dsa_csa_sparse_attn_fwd(d["q"], d["k"], d["v"], mask, ratio, cfg.softmax_scale, o, lse)
+    outs = []
+    for nws in (dsa.dsa_csa_bwd_workspace_bytes(B, S, Sk, ratio, H, cfg.Dqk, cfg.Dv),
+                dsa.dsa_bwd_workspace_min_bytes(B, S, H)):
+        g = [torch.full_like(d[n], float("nan")) for n in ("q", "k", "v")]
+        ws = torch.full((nws,), 0x7F, dtype=torch.uint8, device=DEV)
+        dsa.dsa_csa_sparse_attn_bwd(d["q"], d["k"], d["v"], o, d["dout"], lse, mask, ratio, cfg.softmax_scale,
+                                    *g, ws)
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in g])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint16), b.view(torch.uint16))
 
 
 def test_csa_bwd_ratio_one_is_dsa_bit_for_bit():
