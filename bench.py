@@ -357,6 +357,21 @@ def csa_workload(reps=5):
     for c, k in kern.items():
         k["frac"] = k["achieved"] / (PEAK_HBM_GBS if k["bound"] == "hbm" else PEAK_BF16_TFLOPS)
         k["ms_stats"] = stats(t[c])
+    # the backward's other route: the minimum workspace, dQ recomputing dS
+    ws_min = torch.empty(dsa.dsa_bwd_workspace_min_bytes(B, S, H), dtype=torch.uint8, device="cuda")
+    t_rc = []
+    for i in range(reps + 1):
+        ev[0].record(stream)
+        dsa.dsa_csa_sparse_attn_bwd(x["q"], x["k"], x["v"], o, dout, lse, mask, r, cfg.softmax_scale,
+                                    dq, dk, dv, ws_min)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        if i:
+            t_rc.append(ev[0].elapsed_time(ev[1]))
+    m_rc = float(np.median(t_rc))
+    kern["attn_bwd"]["recompute_route"] = {"ms": m_rc, "achieved": flops_bwd / (m_rc * 1e-3) / 1e12,
+                                           "unit": "TFLOP/s", "ms_stats": stats(t_rc)}
+    del ws_min
     total = sum(ms.values())
     del x, scores, idx, mask, o, lse, dout, dq, dk, dv, ws
     torch.cuda.empty_cache()
